@@ -1,0 +1,422 @@
+"""Oracle for one Qwen-style GQA decoder layer -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, float64 numpy implementation of what the layer computes.  Only
+the tests, the smoke check and the benchmark's CPU-baseline leg may import it;
+the product (the HIP library and its Python binding) never does.  It shares no
+code with the HIP path; both take their inputs from ``synth``.
+
+Page abbreviations used in the citations below (the four source pages):
+
+* [QWEN] "从零实现 C++ LLM 推理引擎：加载 Qwen2.5-7B 并跑通单层 Forward Pass"
+* [TFF]  "十年 C++ 后端 GAP 六个月，写了一个近 3 万行的LLM-TFFInfer推理框架项目解析"
+* [HET]  the devpress article on a C++-native heterogeneous inference engine
+         ("为什么要做一套 C++ 原生的异构推理引擎")
+
+Every step is written from the definition it cites.  Where the pages are
+silent or garbled the plainest reading is taken and named in the docstring.
+
+Parity status of each function (what pins it, see tests/test_oracle_*.py):
+  round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, kv_calibrate,
+  kv_quantize, kv_dequantize, attention, attention_online, PagedCache,
+  layer_forward -- all pinned (worked examples, closed forms, brute force,
+  special cases).  The pages' own printed layer output (Qwen2.5-7B-Instruct
+  weights, [QWEN] section "运行结果") cannot be reproduced without those
+  weights: that end-to-end value is parity unpinned.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+BLOCK_SIZE = 16
+
+
+# --------------------------------------------------------------------------
+# Number formats
+# --------------------------------------------------------------------------
+
+def round_bf16(x) -> np.ndarray:
+    """Round real values to the nearest bf16 value, ties to even.
+
+    bf16 keeps 8 significant bits (1 implicit + 7 stored) and fp32's exponent
+    range.  For a value m * 2**e with m in [0.5, 1) (``np.frexp``), the bf16
+    quantum is 2**(e-8); below the normal range (|x| < 2**-126) it is fixed at
+    2**-133.  ``np.rint`` rounds halves to even.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    quantum_exp = np.maximum(e - 8, -133)
+    q = np.ldexp(np.ones_like(x), quantum_exp)
+    out = np.rint(x / q) * q
+    assert np.all(np.isfinite(out[np.isfinite(x)])) and np.all(np.abs(out) < 3.4e38), \
+        "value outside bf16 range"
+    return out
+
+
+def q80_expand(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Q8_0 weights to real values: blocks of 32 int8 codes along the input
+    (K) dimension of each output row share one fp16 scale,
+    W[n, k] = scale[n, k // 32] * code[n, k].
+
+    The format is named on [TFF] section 1.1 (Qwen3-8B Q8_0) and its
+    block-strided rows on [TFF] section 3.4 (Tensor block size); the 32-code +
+    fp16 block is the Q8_0 definition.  The product of an 11-bit significand
+    and a 7-bit integer is exact in float64.
+    """
+    n, k = codes.shape
+    assert k % 32 == 0 and scales.shape == (n, k // 32)
+    s = np.repeat(scales.astype(np.float64), 32, axis=1)
+    return s * codes.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Layer building blocks
+# --------------------------------------------------------------------------
+
+def rms_norm(x, g, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: x * g / sqrt(mean(x**2) + eps).
+
+    [QWEN] section "2. 自定义 CUDA Kernels" (the rms_norm kernel: one row, sum of
+    squares divided by the row length, eps inside the reciprocal square root,
+    then times the weight).  The page's snippet is garbled (no row offset on
+    the output); the reading is the textbook RMSNorm: mean over the full row
+    length H (not H-1), eps added before the square root.
+    """
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, np.float64)
+
+
+def rope_neox(x, pos, theta: float) -> np.ndarray:
+    """Rotary position embedding, half-split ("NeoX") pairing.
+
+    x has shape [..., D]; ``pos`` broadcasts against x[..., 0].  For
+    i < D/2 the pair (x_i, x_{i+D/2}) is rotated by a = pos * theta**(-2i/D):
+    (x_i cos a - x_{i+D/2} sin a,  x_i sin a + x_{i+D/2} cos a).
+
+    [TFF] section 3.7.2 item 4 rotates pairs by a cos/sin table; [QWEN]
+    section "2. 自定义 CUDA Kernels" applies RoPE to Q and K heads.  Neither
+    fixes the pairing: the half-split pairing is the reading taken because the
+    layer is Qwen-style.  Positions are absolute and 0-based; the frequency
+    scale is 1.  Angles are formed in float64.
+    """
+    x = np.asarray(x, np.float64)
+    D = x.shape[-1]
+    half = D // 2
+    i = np.arange(half, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / D)
+    a = np.asarray(pos, np.float64)[..., None] * inv_freq
+    c, s = np.cos(a), np.sin(a)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def rope_interleaved(x, pos, theta: float) -> np.ndarray:
+    """Adjacent-pair variant ((x_{2i}, x_{2i+1}) as one complex number), as
+    [TFF] section 3.7.2 item 4 draws it.  Kept only so tests can tell the two
+    pairings apart; the layer uses ``rope_neox``."""
+    x = np.asarray(x, np.float64)
+    D = x.shape[-1]
+    i = np.arange(D // 2, dtype=np.float64)
+    a = np.asarray(pos, np.float64)[..., None] * theta ** (-2.0 * i / D)
+    c, s = np.cos(a), np.sin(a)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out
+
+
+def linear(x, w, b=None) -> np.ndarray:
+    """Y = X W^T (+ b) with W in [out, in] row-major layout.
+
+    [QWEN] section "4. cuBLAS Row-Major 陷阱": out[M,N] = input[M,K] @ W[N,K]^T.
+    """
+    y = np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+    if b is not None:
+        y = y + np.asarray(b, np.float64)
+    return y
+
+
+def silu(z) -> np.ndarray:
+    """SiLU(z) = z / (1 + exp(-z))."""
+    z = np.asarray(z, np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(gate, up) -> np.ndarray:
+    """SwiGLU combination silu(gate) * up ([TFF] section 3.7.1 operator list
+    "Unary (SwiGLU)"; [QWEN] architecture overview "SwiGLU MLP").  The gate
+    branch is the one that goes through SiLU."""
+    return silu(gate) * np.asarray(up, np.float64)
+
+
+# --------------------------------------------------------------------------
+# int8 asymmetric per-channel KV quantisation
+# --------------------------------------------------------------------------
+
+def kv_calibrate(values: np.ndarray):
+    """Per-channel asymmetric parameters from [HET] section 2.6 (量化公式):
+    scale_c = (max_c - min_c) / 255, zero_point_c = round(-min_c / scale_c).
+
+    ``values`` is [n_tokens, n_kv_heads, head_dim] float32; a channel is one
+    (kv_head, d) pair, reduced over all tokens.  Reading taken: the arithmetic
+    is IEEE float32 (the precision the kernel quantises in); round() is
+    round-half-to-even; zero_point stays an unclamped int32; a flat channel
+    (max == min) gets scale 1.
+    """
+    v = np.asarray(values, np.float32)
+    assert v.ndim == 3 and v.shape[0] > 0
+    mx = v.max(axis=0)
+    mn = v.min(axis=0)
+    scale = (mx - mn) / np.float32(255.0)
+    scale = np.where(scale == 0, np.float32(1.0), scale).astype(np.float32)
+    zp = np.rint(-mn / scale).astype(np.int32)
+    return scale, zp
+
+
+def kv_quantize(x, scale, zp) -> np.ndarray:
+    """Q_c = clamp(round(x / scale_c) + zero_point_c, 0, 255) ([HET] section
+    2.6), in float32 with a correctly rounded divide and round-half-to-even;
+    stored as uint8 (the page calls the codes int8 but clamps to 0..255)."""
+    x32 = np.asarray(x, np.float32)
+    q = np.rint(x32 / scale).astype(np.int64) + zp.astype(np.int64)
+    return np.clip(q, 0, 255).astype(np.uint8)
+
+
+def kv_dequantize(codes, scale, zp) -> np.ndarray:
+    """x ~ (Q_c - zero_point_c) * scale_c ([HET] section 2.6)."""
+    return (np.asarray(codes, np.float64) - zp.astype(np.float64)) * scale.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Paged KV cache
+# --------------------------------------------------------------------------
+
+class PagedCache:
+    """Logical model of the block-paged KV cache.
+
+    Physical storage is a pool of fixed-size blocks; a sequence's block table
+    maps logical block t // B to a physical block, and token t lives at
+    offset t % B of it ([TFF] section 3.6.4, get_location; [HET] section 4.3
+    with 16-token blocks).  ``dtype`` is "bf16" (values rounded to bf16 when
+    written) or "u8" (codes + per-channel scale/zero point).  Keys/values are
+    held per (block, kv_head, offset, d); the physical byte layout of the GPU
+    pool is not modelled here.
+    """
+
+    def __init__(self, n_blocks: int, n_kv_heads: int, head_dim: int, dtype: str,
+                 k_params=None, v_params=None):
+        assert dtype in ("bf16", "u8")
+        self.dtype = dtype
+        self.n_blocks, self.n_kv_heads, self.head_dim = n_blocks, n_kv_heads, head_dim
+        shape = (n_blocks, n_kv_heads, BLOCK_SIZE, head_dim)
+        if dtype == "bf16":
+            self.k = np.full(shape, np.nan)
+            self.v = np.full(shape, np.nan)
+        else:
+            assert k_params is not None and v_params is not None
+            self.k_scale, self.k_zp = k_params
+            self.v_scale, self.v_zp = v_params
+            self.k = np.zeros(shape, np.uint8)
+            self.v = np.zeros(shape, np.uint8)
+            self.written = np.zeros(shape[:1] + shape[2:3], bool)
+
+    @staticmethod
+    def location(table_row: np.ndarray, t: int):
+        """(physical block, offset) of token t ([TFF] section 3.6.4)."""
+        blk = int(table_row[t // BLOCK_SIZE])
+        assert blk >= 0, "token beyond the sequence's allocated blocks"
+        return blk, t % BLOCK_SIZE
+
+    def write(self, table_row, t: int, k, v):
+        """Store token t's K and V ([n_kv_heads, head_dim] real values),
+        rounded to the cache dtype."""
+        blk, off = self.location(table_row, t)
+        if self.dtype == "bf16":
+            self.k[blk, :, off, :] = round_bf16(k)
+            self.v[blk, :, off, :] = round_bf16(v)
+        else:
+            self.k[blk, :, off, :] = kv_quantize(k, self.k_scale, self.k_zp)
+            self.v[blk, :, off, :] = kv_quantize(v, self.v_scale, self.v_zp)
+            self.written[blk, off] = True
+
+    def read(self, table_row, n_tokens: int):
+        """Keys and values of tokens 0..n_tokens-1, [n_tokens, n_kv_heads, D],
+        as real numbers (u8 codes dequantised)."""
+        K = np.empty((n_tokens, self.n_kv_heads, self.head_dim))
+        V = np.empty_like(K)
+        for t in range(n_tokens):
+            blk, off = self.location(table_row, t)
+            if self.dtype == "bf16":
+                K[t], V[t] = self.k[blk, :, off, :], self.v[blk, :, off, :]
+            else:
+                assert self.written[blk, off], "reading a slot never written"
+                K[t] = kv_dequantize(self.k[blk, :, off, :], self.k_scale, self.k_zp)
+                V[t] = kv_dequantize(self.v[blk, :, off, :], self.v_scale, self.v_zp)
+        assert np.all(np.isfinite(K)) and np.all(np.isfinite(V)), "reading a slot never written"
+        return K, V
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+
+def attention(q, q_pos, K, V) -> np.ndarray:
+    """Causal grouped-query attention, exact two-pass softmax.
+
+    q: [Tq, Hq, D] queries at absolute positions q_pos [Tq];
+    K, V: [Tk, Hkv, D], key j sitting at position j.
+    Query head h reads KV head h // (Hq / Hkv) -- consecutive query heads
+    share a KV head ([QWEN] section "3. GQA": 28 Q heads share 4 KV heads,
+    7:1; the order of the expansion is the reading taken).
+    Scores are q.k / sqrt(D) ([HET] section 4.3 kernel comment); a query at
+    position p sees keys 0..p (causal mask including the diagonal, [QWEN]
+    architecture overview "Causal mask + softmax").  Masked keys are left out.
+    """
+    q = np.asarray(q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    Tq, Hq, D = q.shape
+    Hkv = K.shape[1]
+    n_rep = Hq // Hkv
+    out = np.empty((Tq, Hq, D))
+    for i in range(Tq):
+        n_vis = int(q_pos[i]) + 1
+        assert n_vis <= K.shape[0]
+        for h in range(Hq):
+            g = h // n_rep
+            s = K[:n_vis, g, :] @ q[i, h] / math.sqrt(D)
+            m = s.max()
+            e = np.exp(s - m)
+            out[i, h] = (e @ V[:n_vis, g, :]) / e.sum()
+    return out
+
+
+def attention_online(q, q_pos, K, V, tile: int) -> np.ndarray:
+    """The same attention, computed tile by tile with a running max m,
+    running denominator l and rescaled accumulator ([TFF] section 3.7.2
+    item 5, online softmax).  The page's update adds one exp term per tile,
+    which is only right for one score at a time; the reading used is
+    m' = max(m, max s), l' = l e^(m-m') + sum e^(s-m'),
+    acc' = acc e^(m-m') + sum e^(s-m') v, o = acc / l."""
+    q = np.asarray(q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    Tq, Hq, D = q.shape
+    n_rep = Hq // K.shape[1]
+    out = np.empty((Tq, Hq, D))
+    for i in range(Tq):
+        n_vis = int(q_pos[i]) + 1
+        for h in range(Hq):
+            g = h // n_rep
+            m, l, acc = -np.inf, 0.0, np.zeros(D)
+            for j0 in range(0, n_vis, tile):
+                j1 = min(j0 + tile, n_vis)
+                s = K[j0:j1, g, :] @ q[i, h] / math.sqrt(D)
+                m_new = max(m, s.max())
+                alpha = math.exp(m - m_new) if np.isfinite(m) else 0.0
+                p = np.exp(s - m_new)
+                l = l * alpha + p.sum()
+                acc = acc * alpha + p @ V[j0:j1, g, :]
+                m = m_new
+            out[i, h] = acc / l
+    return out
+
+
+# --------------------------------------------------------------------------
+# The layer
+# --------------------------------------------------------------------------
+
+def expand_weights(shape, w: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    """float64 copies of the weights; Q8_0 matrices expanded exactly."""
+    out = {}
+    for name, a in w.items():
+        if name.endswith("_scale"):
+            continue
+        if shape.weight_dtype == "q80" and name + "_scale" in w:
+            out[name] = q80_expand(a, w[name + "_scale"])
+        else:
+            out[name] = np.asarray(a, np.float64)
+    return out
+
+
+def layer_forward(shape, w: Dict[str, np.ndarray], x: np.ndarray, q_start, q_len, ctx_len,
+                  table: Optional[np.ndarray], cache: Optional[PagedCache],
+                  want_stages: bool = False):
+    """Forward pass of one pre-norm Qwen-style GQA decoder layer over a batch
+    of sequences.
+
+    Sequence i owns rows q_start[i] .. q_start[i]+q_len[i]-1 of x [rows, H];
+    its new tokens sit at positions ctx_len[i] + 0..q_len[i]-1 and its first
+    ctx_len[i] tokens are already in ``cache``.  With ``cache`` None (no KV
+    cache) each sequence must have ctx_len 0 and attends over its own exact
+    keys.  Steps ([QWEN] architecture overview; [TFF] section 4.1 decode
+    flow; weights already expanded by ``expand_weights``):
+
+      1. xn = RMSNorm(x, ln1)
+      2. q, k, v = xn Wq^T (+bq), xn Wk^T (+bk), xn Wv^T (+bv)
+      3. (Qwen3) per-head RMSNorm of q and k over head_dim, gains q_norm/k_norm,
+         before RoPE (reading: same eps; gains shared by all heads)
+      4. RoPE (half-split) on q and k at each token's position
+      5. k, v of new tokens written to the cache (rounded to its dtype), then
+         every key/value is read back from the cache ([TFF] 3.6.4; decode
+         appends the token at position ctx_len first)
+      6. o = causal GQA attention
+      7. h = x + o Wo^T                      (residual)
+      8. hn = RMSNorm(h, ln2)
+      9. a = silu(hn Wg^T) * (hn Wu^T)
+     10. y = h + a Wd^T                      (second residual; reading: the
+         standard pre-norm layer with two residual adds)
+    """
+    H, D = shape.hidden, shape.head_dim
+    Hq, Hkv = shape.n_q_heads, shape.n_kv_heads
+    x = np.asarray(x, np.float64)
+    rows = x.shape[0]
+    xn = rms_norm(x, w["ln1"], shape.rms_eps)
+    q = linear(xn, w["wq"], w.get("bq")).reshape(rows, Hq, D)
+    k = linear(xn, w["wk"], w.get("bk")).reshape(rows, Hkv, D)
+    v = linear(xn, w["wv"], w.get("bv")).reshape(rows, Hkv, D)
+    if shape.qk_norm:
+        q = rms_norm(q, w["q_norm"], shape.rms_eps)
+        k = rms_norm(k, w["k_norm"], shape.rms_eps)
+    pos = np.empty(rows, np.int64)
+    for i in range(len(q_len)):
+        r0 = int(q_start[i])
+        pos[r0:r0 + int(q_len[i])] = int(ctx_len[i]) + np.arange(int(q_len[i]))
+    q = rope_neox(q, pos[:, None], shape.rope_theta)
+    k = rope_neox(k, pos[:, None], shape.rope_theta)
+    o = np.empty((rows, Hq, D))
+    for i in range(len(q_len)):
+        r0, n, c = int(q_start[i]), int(q_len[i]), int(ctx_len[i])
+        if n == 0:
+            continue
+        if cache is None:
+            assert c == 0, "prior context needs a KV cache"
+            Ks, Vs = k[r0:r0 + n], v[r0:r0 + n]
+        else:
+            for t in range(n):
+                cache.write(table[i], c + t, k[r0 + t], v[r0 + t])
+            Ks, Vs = cache.read(table[i], c + n)
+        o[r0:r0 + n] = attention(q[r0:r0 + n], pos[r0:r0 + n], Ks, Vs)
+    o2 = o.reshape(rows, Hq * D)
+    h = x + linear(o2, w["wo"])
+    hn = rms_norm(h, w["ln2"], shape.rms_eps)
+    a = swiglu(linear(hn, w["wg"]), linear(hn, w["wu"]))
+    y = h + linear(a, w["wd"])
+    if want_stages:
+        return y, dict(xn=xn, q=q, k=k, v=v, o=o2, h=h, hn=hn, a=a, pos=pos)
+    return y
+
+
+def fill_cache(cache: PagedCache, table: np.ndarray, ctx_len, cache_k, cache_v):
+    """Write the already-cached tokens: sequence i's positions 0..ctx_len[i]-1
+    come from consecutive rows of cache_k / cache_v ([n, Hkv, D])."""
+    r = 0
+    for i, c in enumerate(ctx_len):
+        for t in range(int(c)):
+            cache.write(table[i], t, cache_k[r], cache_v[r])
+            r += 1
+    assert r == (0 if cache_k is None else cache_k.shape[0])

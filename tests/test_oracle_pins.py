@@ -1,0 +1,378 @@
+"""Pins of the oracle to facts other than itself: worked examples printed in
+tests/golden (each with its citation), closed forms, invariants, library
+routines for special cases, and brute force on tiny inputs.
+
+Each test names the plausible mistake it would catch."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- bf16 ----
+
+def test_round_bf16_matches_torch_cast():
+    # special case reducing to a library routine: torch's fp32 -> bf16 cast
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 20000),
+                        np.float32([0.0, -0.0, 1.0, 1e-40, 3e38])]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_round_bf16_ties_to_even():
+    # 1 + 2^-8 lies exactly between 1 and 1 + 2^-7: even mantissa is 1.0
+    assert oracle.round_bf16(1 + 2 ** -8) == 1.0
+    assert oracle.round_bf16(1 + 3 * 2 ** -8) == 1 + 2 ** -6
+    assert oracle.round_bf16(-(1 + 2 ** -8 + 2 ** -30)) == -(1 + 2 ** -7)
+
+
+# ------------------------------------------------------------- RMSNorm ----
+
+def test_rmsnorm_worked_example():
+    g = load("rmsnorm_worked.json")
+    y = oracle.rms_norm(np.array([g["x"]]), g["g"], g["eps"])[0]
+    np.testing.assert_allclose(y, g["y"], atol=g["atol"])
+
+
+def test_rmsnorm_constant_row_and_gain():
+    # constant row c -> c / sqrt(c^2 + eps) * g (catches eps outside the sqrt,
+    # mean over H-1, dropped gain)
+    c, eps = 3.0, 1e-6
+    gains = np.linspace(0.5, 1.5, 8)
+    y = oracle.rms_norm(np.full((1, 8), c), gains, eps)[0]
+    np.testing.assert_allclose(y, c / math.sqrt(c * c + eps) * gains, rtol=1e-15)
+    # large eps makes its placement visible: mean(x^2) = 1, eps = 3 -> 1/2
+    y = oracle.rms_norm(np.ones((1, 4)), np.ones(4), 3.0)[0]
+    np.testing.assert_allclose(y, 0.5, rtol=1e-15)
+
+
+def test_rmsnorm_scale_invariance_and_unit_rms():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((5, 64))
+    y = oracle.rms_norm(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(oracle.rms_norm(7.5 * x, np.ones(64), 0.0), y, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- RoPE ----
+
+def test_rope_worked_example_both_pairings():
+    g = load("rope_worked.json")
+    x = np.array(g["x"])
+    np.testing.assert_allclose(oracle.rope_neox(x, g["pos"], g["theta"]), g["neox"], atol=g["atol"])
+    np.testing.assert_allclose(oracle.rope_interleaved(x, g["pos"], g["theta"]), g["interleaved"],
+                               atol=g["atol"])
+
+
+def test_rope_identity_norm_and_relative_position():
+    rng = np.random.default_rng(3)
+    D, theta = 128, 1e6
+    x = rng.standard_normal((6, D))
+    np.testing.assert_allclose(oracle.rope_neox(x, np.zeros(6), theta), x, rtol=0, atol=0)
+    y = oracle.rope_neox(x, np.arange(6) * 977, theta)
+    pair_norm = lambda a: a[..., :D // 2] ** 2 + a[..., D // 2:] ** 2
+    np.testing.assert_allclose(pair_norm(y), pair_norm(x), rtol=1e-12)
+    # <R_p q, R_p' k> depends only on p - p'
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    d1 = oracle.rope_neox(q, 1000, theta) @ oracle.rope_neox(k, 990, theta)
+    d2 = oracle.rope_neox(q, 4011, theta) @ oracle.rope_neox(k, 4001, theta)
+    assert abs(d1 - d2) < 1e-10
+    d3 = oracle.rope_neox(q, 4012, theta) @ oracle.rope_neox(k, 4001, theta)
+    assert abs(d1 - d3) > 1e-6
+
+
+def test_rope_frequency_per_pair():
+    # a unit vector in pair i at position p rotates by exactly p * theta^(-2i/D)
+    D, theta, p = 16, 1e4, 37
+    for i in range(D // 2):
+        x = np.zeros(D)
+        x[i] = 1.0
+        y = oracle.rope_neox(x, p, theta)
+        ang = math.atan2(y[i + D // 2], y[i])
+        want = math.remainder(p * theta ** (-2 * i / D), 2 * math.pi)
+        assert abs(ang - want) < 1e-12
+
+
+# ------------------------------------------------------------- linear -----
+
+def test_linear_layout_against_loops_and_torch():
+    # W is [out, in]: Y[m, n] = sum_k X[m, k] W[n, k] (catches a transposed W)
+    rng = np.random.default_rng(4)
+    X, W, b = rng.standard_normal((3, 7)), rng.standard_normal((5, 7)), rng.standard_normal(5)
+    Y = oracle.linear(X, W, b)
+    for m in range(3):
+        for n in range(5):
+            assert abs(Y[m, n] - (sum(X[m, k] * W[n, k] for k in range(7)) + b[n])) < 1e-12
+    X, W = rng.standard_normal((32, 688)), rng.standard_normal((256, 688))
+    ref = torch.nn.functional.linear(torch.from_numpy(X), torch.from_numpy(W)).numpy()
+    np.testing.assert_allclose(oracle.linear(X, W), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_silu_values():
+    g = load("silu_values.json")
+    np.testing.assert_allclose(oracle.silu(g["z"]), g["silu"], atol=g["atol"])
+    # swiglu: silu on the gate, not on up (catches swapped branches)
+    assert oracle.swiglu(1.0, 2.0) == pytest.approx(2 * 0.7310585786)
+    assert oracle.swiglu(2.0, 1.0) == pytest.approx(2.0 / (1 + math.exp(-2.0)))
+
+
+def test_q80_expand_exact():
+    rng = np.random.default_rng(5)
+    codes = rng.integers(-127, 128, (4, 96), dtype=np.int8)
+    scales = np.abs(rng.standard_normal((4, 3)) * 0.002).astype(np.float16)
+    W = oracle.q80_expand(codes, scales)
+    for n in range(4):
+        for k in range(96):
+            assert W[n, k] == float(scales[n, k // 32]) * int(codes[n, k])
+    # the block index runs along the input dimension (catches [n, k % 3])
+    s = np.array([[1, 2, 4]], np.float16)
+    c = np.ones((1, 96), np.int8)
+    assert list(oracle.q80_expand(c, s)[0, ::32]) == [1.0, 2.0, 4.0]
+
+
+# ------------------------------------------------- int8 KV quantisation ---
+
+def test_kv_quant_worked_examples():
+    g = load("kv_quant_worked.json")
+    for case in g["cases"]:
+        x = np.array(case["x"], np.float32).reshape(4, 1, 1)
+        scale, zp = oracle.kv_calibrate(x)
+        assert float(scale[0, 0]) == float.fromhex(case["scale_hex"])
+        assert int(zp[0, 0]) == case["zp"]
+        codes = oracle.kv_quantize(x, scale, zp)
+        assert codes.ravel().tolist() == case["codes"]
+
+
+def test_kv_quant_invariants_and_error_bound():
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((500, 3, 8)) * rng.uniform(0.1, 5, (1, 3, 8))
+         + rng.uniform(-2, 2, (1, 3, 8))).astype(np.float32)
+    scale, zp = oracle.kv_calibrate(x)
+    codes = oracle.kv_quantize(x, scale, zp)
+    amin, amax = x.argmin(axis=0), x.argmax(axis=0)
+    for h in range(3):
+        for d in range(8):
+            assert codes[amin[h, d], h, d] == 0
+            assert codes[amax[h, d], h, d] in (254, 255)
+    deq = oracle.kv_dequantize(codes, scale, zp)
+    bound = scale / 2 + 2.0 ** -23 * np.maximum(np.abs(x.min(0)), np.abs(x.max(0))) * 4
+    assert np.all(np.abs(deq - x) <= bound[None] * (1 + 1e-6))
+    # per-channel: a channel's parameters ignore the other channels
+    x2 = x.copy()
+    x2[:, 0, 0] *= 100
+    s2, z2 = oracle.kv_calibrate(x2)
+    assert np.array_equal(s2[1:], scale[1:]) and np.array_equal(z2[:, 1:], zp[:, 1:])
+    # values outside the calibrated range clamp
+    assert oracle.kv_quantize(np.float32([[[1e6]]]), scale[:1, :1], zp[:1, :1])[0, 0, 0] == 255
+    # a flat channel gets scale 1
+    s, z = oracle.kv_calibrate(np.full((4, 1, 1), 2.5, np.float32))
+    assert s[0, 0] == 1.0 and z[0, 0] == -2
+
+
+# ------------------------------------------------------------ attention ---
+
+def brute_force_attention(q, q_pos, K, V):
+    """Full-matrix attention with an explicit repeat_kv and an explicit mask
+    matrix (a different construction from the oracle's per-row loop)."""
+    Tq, Hq, D = q.shape
+    n_rep = Hq // K.shape[1]
+    Kr = np.repeat(K, n_rep, axis=1)          # [Tk, Hq, D]
+    Vr = np.repeat(V, n_rep, axis=1)
+    S = np.einsum("qhd,khd->hqk", q, Kr) / math.sqrt(D)
+    mask = np.arange(K.shape[0])[None, :] <= np.asarray(q_pos)[:, None]
+    S = np.where(mask[None], S, -np.inf)
+    P = np.exp(S - S.max(axis=-1, keepdims=True))
+    P /= P.sum(axis=-1, keepdims=True)
+    return np.einsum("hqk,khd->qhd", P, Vr)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,Tq,Tk", [(4, 2, 64, 32, 32), (6, 2, 16, 5, 9), (7, 1, 8, 3, 20),
+                                            (3, 3, 4, 4, 4)])
+def test_attention_brute_force(Hq, Hkv, D, Tq, Tk):
+    rng = np.random.default_rng(Hq * 100 + Tk)
+    q = rng.standard_normal((Tq, Hq, D))
+    K, V = rng.standard_normal((Tk, Hkv, D)), rng.standard_normal((Tk, Hkv, D))
+    q_pos = np.arange(Tk - Tq, Tk)
+    np.testing.assert_allclose(oracle.attention(q, q_pos, K, V),
+                               brute_force_attention(q, q_pos, K, V), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_against_torch_sdpa_gqa():
+    # library routine: torch SDPA (fp64 CPU, causal, enable_gqa -> query head h
+    # reads KV head h // n_rep)
+    rng = np.random.default_rng(7)
+    T, Hq, Hkv, D = 12, 6, 2, 16
+    q, K, V = rng.standard_normal((T, Hq, D)), rng.standard_normal((T, Hkv, D)), rng.standard_normal((T, Hkv, D))
+    t = lambda a: torch.from_numpy(a).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(K), t(V), is_causal=True,
+                                                           enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(oracle.attention(q, np.arange(T), K, V), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(8)
+    K, V = rng.standard_normal((10, 2, 8)), rng.standard_normal((10, 2, 8))
+    q = rng.standard_normal((1, 4, 8))
+    # one visible key: the output is that key's value, for every head of the group
+    o = oracle.attention(q, [0], K, V)
+    for h in range(4):
+        np.testing.assert_allclose(o[0, h], V[0, h // 2], rtol=1e-14)
+    # all keys equal: uniform weights, the mean of the visible values
+    Ke = np.repeat(K[:1], 10, axis=0)
+    o = oracle.attention(q, [6], Ke, V)
+    for h in range(4):
+        np.testing.assert_allclose(o[0, h], V[:7, h // 2].mean(axis=0), rtol=1e-12)
+
+
+@pytest.mark.parametrize("tile", [1, 5, 16])
+def test_online_softmax_equals_two_pass(tile):
+    rng = np.random.default_rng(9)
+    q, K, V = rng.standard_normal((6, 4, 16)) * 3, rng.standard_normal((40, 2, 16)), rng.standard_normal((40, 2, 16))
+    pos = np.array([0, 1, 15, 16, 17, 39])
+    np.testing.assert_allclose(oracle.attention_online(q, pos, K, V, tile), oracle.attention(q, pos, K, V),
+                               rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------ paged KV ----
+
+def test_paged_equals_contiguous_bit_exact():
+    rng = np.random.default_rng(10)
+    Hkv, D, n = 2, 8, 70
+    K = synth.to_bf16_values(rng.standard_normal((n, Hkv, D)).astype(np.float32)).astype(np.float64)
+    V = synth.to_bf16_values(rng.standard_normal((n, Hkv, D)).astype(np.float32)).astype(np.float64)
+    table = synth.random_tables(rng, [n], n_blocks=9)
+    cache = oracle.PagedCache(9, Hkv, D, "bf16")
+    for t in range(n):
+        cache.write(table[0], t, K[t], V[t])
+    Kp, Vp = cache.read(table[0], n)
+    assert np.array_equal(Kp, K) and np.array_equal(Vp, V)
+    q = rng.standard_normal((3, 4, D))
+    pos = np.array([5, 40, 69])
+    assert np.array_equal(oracle.attention(q, pos, Kp, Vp), oracle.attention(q, pos, K, V))
+    # slot addressing: token t at (table[t // 16], t % 16)
+    blk, off = cache.location(table[0], 37)
+    assert blk == table[0][2] and off == 5
+    assert np.array_equal(cache.k[blk, :, off, :], K[37])
+
+
+def test_paged_u8_roundtrip():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((40, 2, 8)).astype(np.float32)
+    params = oracle.kv_calibrate(x)
+    cache = oracle.PagedCache(4, 2, 8, "u8", params, params)
+    table = np.array([[3, 0, 2]], np.int32)
+    for t in range(40):
+        cache.write(table[0], t, x[t], x[t])
+    Kp, _ = cache.read(table[0], 40)
+    np.testing.assert_allclose(Kp, oracle.kv_dequantize(oracle.kv_quantize(x, *params), *params), rtol=0)
+    assert np.all(np.abs(Kp - x) <= params[0][None] * 0.5001)
+
+
+# ---------------------------------------------------------------- layer ---
+
+def tiny_shape(**kw):
+    base = dict(name="t", hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=8, intermediate=40,
+                rms_eps=1e-6, rope_theta=1e4, qkv_bias=True, qk_norm=False, weight_dtype="f32")
+    base.update(kw)
+    return synth.LayerShape(**base)
+
+
+def run_prefill(shape, w, x, cache=None, start=0, table=None):
+    T = x.shape[0]
+    return oracle.layer_forward(shape, oracle.expand_weights(shape, w), x, [0], [T], [start],
+                                table, cache, want_stages=True)
+
+
+def test_layer_single_token_closed_form():
+    # T = 1: attention returns v itself, so the layer reduces to plain matrix
+    # algebra (catches a wrong residual source, a missing bias, swapped MLP
+    # branches, or the wrong KV head for a query head)
+    shape = tiny_shape()
+    w = synth.make_weights(shape, seed=1, random_gains=True)
+    x = np.random.default_rng(2).standard_normal((1, 32))
+    y, _ = run_prefill(shape, w, x)
+    W = {k: np.asarray(v, np.float64) for k, v in w.items()}
+    r = lambda a, g: a / np.sqrt(np.mean(a * a) + 1e-6) * g
+    xn = r(x[0], W["ln1"])
+    v = (W["wv"] @ xn + W["bv"]).reshape(2, 8)
+    o = np.concatenate([v[h // 2] for h in range(4)])
+    h = x[0] + W["wo"] @ o
+    hn = r(h, W["ln2"])
+    gte, up = W["wg"] @ hn, W["wu"] @ hn
+    want = h + W["wd"] @ (gte / (1 + np.exp(-gte)) * up)
+    np.testing.assert_allclose(y[0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_zero_branches():
+    shape = tiny_shape()
+    w = synth.make_weights(shape, seed=3)
+    x = np.random.default_rng(4).standard_normal((5, 32))
+    w0 = dict(w, wo=np.zeros_like(w["wo"]), wd=np.zeros_like(w["wd"]))
+    y, _ = run_prefill(shape, w0, x)
+    assert np.array_equal(y, x)
+    w1 = dict(w, wd=np.zeros_like(w["wd"]))
+    y, st = run_prefill(shape, w1, x)
+    assert np.array_equal(y, st["h"])
+
+
+def test_layer_qk_norm_step():
+    # with qk_norm each head of q and k has unit RMS (gains 1) before RoPE; RoPE
+    # preserves pair norms, so the stage output still has unit RMS per head
+    shape = tiny_shape(qkv_bias=False, qk_norm=True, rms_eps=1e-12)
+    w = synth.make_weights(shape, seed=5)
+    x = np.random.default_rng(6).standard_normal((3, 32)) * 4
+    _, st = run_prefill(shape, w, x)
+    np.testing.assert_allclose(np.sqrt(np.mean(st["q"] ** 2, -1)), 1.0, rtol=1e-5)
+    np.testing.assert_allclose(np.sqrt(np.mean(st["k"] ** 2, -1)), 1.0, rtol=1e-5)
+
+
+def test_prefill_decode_consistency():
+    # the last row of prefill over S+1 tokens equals a decode step at context S
+    shape = tiny_shape()
+    w = synth.make_weights(shape, seed=7)
+    W = oracle.expand_weights(shape, w)
+    S = 21
+    x = synth.to_bf16_values(np.random.default_rng(8).standard_normal((S + 1, 32)).astype(np.float32))
+    table = np.array([[4, 1]], np.int32)
+    c1 = oracle.PagedCache(6, 2, 8, "bf16")
+    y_full = oracle.layer_forward(shape, W, x, [0], [S + 1], [0], table, c1)
+    c2 = oracle.PagedCache(6, 2, 8, "bf16")
+    oracle.layer_forward(shape, W, x[:S], [0], [S], [0], table, c2)
+    y_dec = oracle.layer_forward(shape, W, x[S:], [0], [1], [S], table, c2)
+    np.testing.assert_allclose(y_dec[0], y_full[S], rtol=1e-13, atol=1e-13)
+    # chunked prefill (two chunks) equals the one-shot rows
+    c3 = oracle.PagedCache(6, 2, 8, "bf16")
+    y_a = oracle.layer_forward(shape, W, x[:9], [0], [9], [0], table, c3)
+    y_b = oracle.layer_forward(shape, W, x[9:], [0], [S + 1 - 9], [9], table, c3)
+    np.testing.assert_allclose(np.concatenate([y_a, y_b]), y_full, rtol=1e-13, atol=1e-13)
+
+
+def test_batch_rows_independent():
+    # a mixed batch gives each sequence the result it gets alone
+    shape = tiny_shape()
+    W = oracle.expand_weights(shape, synth.make_weights(shape, seed=9))
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((7, 32))
+    table = np.array([[0, 1, -1], [2, 3, 4]], np.int32)
+    cache = oracle.PagedCache(5, 2, 8, "bf16")
+    kv = rng.standard_normal((40, 2, 8))
+    oracle.fill_cache(cache, table, [0, 40], kv, kv)
+    import copy
+    c_alone = copy.deepcopy(cache)
+    y = oracle.layer_forward(shape, W, x, [0, 6], [6, 1], [0, 40], table, cache)
+    y1 = oracle.layer_forward(shape, W, x[6:], [0], [1], [40], table[1:], c_alone)
+    np.testing.assert_allclose(y[6], y1[0], rtol=1e-13)
