@@ -1,0 +1,277 @@
+/*
+ * tdl.h -- C ABI of an MI355X (gfx950) implementation of one Qwen-style
+ * grouped-query-attention decoder layer: RMSNorm -> Q/K/V projection (+bias)
+ * -> (optional per-head Q/K RMSNorm) -> RoPE -> causal GQA attention ->
+ * output projection + residual -> RMSNorm -> SwiGLU MLP + residual.
+ *
+ * Sources of the operations (pages the design follows):
+ *  [QWEN] "从零实现 C++ LLM 推理引擎：加载 Qwen2.5-7B 并跑通单层 Forward Pass":
+ *         architecture overview (the op sequence of one layer), section 2
+ *         (RMSNorm, RoPE over Q and K heads in one kernel), section 3 (GQA,
+ *         28 Q heads over 4 KV heads), section 4 (row-major Y = X W^T with W
+ *         stored [out, in]), section 5 (owning handles free their memory).
+ *  [TFF]  "十年 C++ 后端 GAP 六个月 ... LLM-TFFInfer推理框架项目解析": section
+ *         3.6.4 (paged KV cache: LIFO free list, allocate fails when empty,
+ *         page table, get_location(t) = (table[t / page], t % page)),
+ *         section 3.7.2 (flash attention: tiled K/V, online softmax), the
+ *         layer hyper-parameter set of its graph context (section 3.5).
+ *  [HET]  devpress article on a C++-native heterogeneous inference engine:
+ *         section 2.3 / 4.3 (paged attention, 16-token blocks, a kernel that
+ *         walks the block table), section 2.6 (int8 asymmetric per-channel
+ *         formula), section 2.2 (prefill and decode mixed in one step,
+ *         chunked prefill), the C-ABI as its cross-language surface.
+ *
+ * Conventions for every call:
+ *  - Every function returns tdl_status; nothing throws across the ABI.  On an
+ *    error, tdl_last_error() (thread-local) holds a message.
+ *  - All host-side argument checks happen before anything is enqueued, so a
+ *    call that fails leaves no partial work behind.
+ *  - "device pointer" = memory on the current HIP device (e.g. a torch CUDA
+ *    tensor's data_ptr()); "host pointer" = ordinary host memory.  The
+ *    library never dereferences a device pointer on the host.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *    is asynchronous: inputs must stay valid and outputs untouched until the
+ *    stream reaches that point.  No call synchronises the stream, except
+ *    layer_create / kv_cache_alloc at set-up.
+ *  - bf16 means IEEE bfloat16 (16-bit, 8-bit exponent); every fp32 -> bf16
+ *    conversion rounds to nearest, ties to even.
+ *  - A layer handle and a KV handle each serve one host thread at a time.
+ */
+#ifndef TDL_H
+#define TDL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TDL_OK = 0,
+  TDL_E_INVALID = 1,      /* bad argument (null pointer, size out of range, ...) */
+  TDL_E_UNSUPPORTED = 2,  /* valid request this build does not implement        */
+  TDL_E_CAPACITY = 3,     /* a size limit fixed at create time, or no free blocks */
+  TDL_E_NOMEM = 4,        /* device allocation failed                            */
+  TDL_E_HIP = 5           /* a HIP runtime call or kernel launch failed          */
+} tdl_status;
+
+typedef enum {
+  TDL_BF16 = 0,
+  TDL_F32 = 1,
+  TDL_Q8_0 = 2,    /* 32 int8 codes + one fp16 scale per block along K          */
+  TDL_U8_ASYM = 3  /* uint8 codes + per-channel fp32 scale and int32 zero point */
+} tdl_dtype;
+
+typedef void* tdl_stream; /* hipStream_t */
+typedef struct tdl_layer tdl_layer;
+typedef struct tdl_kv_cache tdl_kv_cache;
+
+/* Layer hyper-parameters ([TFF] 3.5 graph context: heads, kv heads, head
+ * size, rope base, rms eps; [QWEN] "运行结果" config line). */
+typedef struct {
+  int32_t hidden;         /* H                                              */
+  int32_t n_q_heads;      /* Hq                                             */
+  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0, Hq / Hkv <= 16             */
+  int32_t head_dim;       /* D: 64 or 128                                   */
+  int32_t intermediate;   /* I of the SwiGLU MLP                            */
+  float rms_eps;
+  float rope_theta;       /* RoPE base; half-split pairs (i, i + D/2)       */
+  int32_t qkv_bias;       /* 1: Q/K/V projections have a bias               */
+  int32_t qk_norm;        /* 1: per-head RMSNorm on q and k before RoPE     */
+  int32_t weight_dtype;   /* TDL_F32, TDL_BF16 or TDL_Q8_0                  */
+  int32_t max_tokens;     /* most rows (new tokens) in one call             */
+  int32_t max_seqs;       /* most sequences in one call                     */
+  int32_t max_position;   /* positions 0 .. max_position-1 can be rotated   */
+} tdl_layer_config;
+
+/* Weights, device pointers in PyTorch Linear layout ([out, in], row-major).
+ * Matrices wq [Hq*D, H], wk/wv [Hkv*D, H], wo [H, Hq*D], wg/wu [I, H],
+ * wd [H, I] hold weight_dtype elements: float32, bf16, or for Q8_0 the int8
+ * codes, with the fp16 scales in w*_scale [out, in/32].  Biases bq/bk/bv
+ * (if qkv_bias) and gains ln1/ln2 [H], q_norm/k_norm [D] (if qk_norm) are
+ * float32.  Unused pointers may be NULL.  layer_create copies (and repacks)
+ * everything into library-owned memory; the caller may free its copies once
+ * layer_create has returned. */
+typedef struct {
+  const void *ln1, *wq, *bq, *wk, *bk, *wv, *bv, *wo, *ln2, *wg, *wu, *wd, *q_norm, *k_norm;
+  const void *wq_scale, *wk_scale, *wv_scale, *wo_scale, *wg_scale, *wu_scale, *wd_scale;
+} tdl_layer_weights;
+
+/* Paged KV cache ([TFF] 3.6.4 KVConfig; [HET] 4.3 BlockManager). */
+typedef struct {
+  int32_t n_blocks;       /* physical blocks in the pool                    */
+  int32_t block_size;     /* tokens per block; must be 16                   */
+  int32_t n_kv_heads;
+  int32_t head_dim;       /* 64 or 128                                      */
+  int32_t kv_dtype;       /* TDL_BF16 or TDL_U8_ASYM                        */
+  uint64_t free_list_seed;/* 0: blocks handed out 0,1,2,...; otherwise the
+                             free list is a seeded random permutation       */
+} tdl_kv_config;
+
+/* Where a cache's bytes live.  Element (block b, kv head g, token slot s,
+ * channel d) of K is at k_pool[b*k_strides[0] + g*k_strides[1] +
+ * s*k_strides[2] + d*k_strides[3]] (strides in elements; same for V).  K is
+ * stored [block][head][slot][d]; V is stored [block][head][d][slot] so that
+ * the 16 tokens of one channel are contiguous.  For TDL_U8_ASYM the four
+ * parameter arrays hold [n_kv_heads * head_dim] entries; otherwise NULL. */
+typedef struct {
+  void* k_pool;
+  void* v_pool;
+  int64_t k_strides[4];
+  int64_t v_strides[4];
+  int32_t elem_bytes;
+  float* k_scale;
+  int32_t* k_zero_point;
+  float* v_scale;
+  int32_t* v_zero_point;
+} tdl_kv_view;
+
+/* A batch of sequences for layer_step ([HET] 2.2, 4.2: prefill chunks and
+ * decode tokens mixed in one step).  Sequence i owns rows q_start[i] ..
+ * q_start[i]+q_len[i]-1 of x and y; its new tokens take positions
+ * ctx_len[i] .. ctx_len[i]+q_len[i]-1; its first ctx_len[i] tokens are in the
+ * cache already.  Sequences 0 .. n_prefill_seqs-1 may have any q_len >= 1;
+ * sequences n_prefill_seqs .. n_seqs-1 must have q_len == 1 (decode).
+ * q_start/q_len/ctx_len/block_tables are device int32 arrays (block_tables
+ * [n_seqs, max_blocks]); the host bounds size the launch grids and must hold:
+ * n_rows == sum q_len, max_q_len >= every prefill q_len, max_ctx_len >=
+ * every ctx_len + q_len. */
+typedef struct {
+  int32_t n_seqs;
+  int32_t n_prefill_seqs;
+  int32_t n_rows;
+  int32_t max_q_len;
+  int32_t max_ctx_len;
+  int32_t max_blocks;
+  const int32_t* q_start;
+  const int32_t* q_len;
+  const int32_t* ctx_len;
+  const int32_t* block_tables;
+} tdl_batch;
+
+/* Device pointers to a layer's intermediate buffers, valid after a call has
+ * completed on its stream, for stage-by-stage checks.  Row r of each holds
+ * the call's row r.  xn [rows, H] fp16 (RMSNorm-1 output); qkv [rows,
+ * (Hq+2Hkv)*D] float32 (projections + bias, before RoPE); q [rows, Hq, D]
+ * float32 (after Q-norm and RoPE); o [rows, Hq*D] fp16 (attention output);
+ * h [rows, H] float32 (first residual); hn [rows, H] fp16 (RMSNorm-2
+ * output); a [rows, I] bf16 (silu(gate) * up).
+ * The projections take fp16 operands where their input is bounded (xn, o,
+ * hn: weights converted to fp16 at layer_create, which refuses weights
+ * beyond +-65504) and bf16 for the down projection (a is unbounded). */
+typedef struct {
+  const void *xn, *qkv, *q, *o, *h, *hn, *a;
+} tdl_workspace_view;
+
+/* ---------------------------------------------------------------- layer */
+
+/* Validates the configuration, allocates the library-owned weight copies and
+ * workspace (sized by max_tokens / max_seqs), converts f32 weights to bf16
+ * and interleaves gate/up rows for the fused SiLU-gate epilogue.
+ * Synchronises `stream` before returning.  *out is NULL on failure. */
+tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_weights* w,
+                        tdl_stream stream, tdl_layer** out);
+
+/* Frees everything the handle owns.  Work still queued on a stream that uses
+ * the handle must have finished.  NULL is accepted. */
+tdl_status layer_destroy(tdl_layer* layer);
+
+/* Prompt prefill of one sequence ([QWEN] architecture overview): x, y are
+ * [n_tokens, H] bf16 device arrays (y must not overlap x); the new tokens
+ * take positions start_pos .. start_pos+n_tokens-1.  With kv != NULL their
+ * K/V are written into the cache through block_table (device int32, at least
+ * ceil((start_pos+n_tokens)/16) valid entries) and attention also reads
+ * the start_pos tokens already cached (chunked prefill).  With kv == NULL,
+ * start_pos must be 0 and K/V live only for the call.
+ * 1 <= n_tokens <= max_tokens; start_pos + n_tokens <= max_position. */
+tdl_status layer_prefill(tdl_layer* layer, tdl_stream stream, const void* x, void* y,
+                         int32_t n_tokens, int32_t start_pos, tdl_kv_cache* kv,
+                         const int32_t* block_table);
+
+/* One decode step of `batch` sequences, one new token each ([HET] 4.3;
+ * [TFF] 3.6.4 append_token): x, y [batch, H] bf16.  ctx_lens (device int32
+ * [batch]) counts the tokens already cached; the new token's K/V goes to
+ * position ctx_lens[b] first, then attention covers ctx_lens[b]+1 keys read
+ * through block_tables (device int32 [batch, max_blocks]).  max_ctx_len is a
+ * host bound >= every ctx_lens[b]+1 and <= max_blocks*16 (it sizes the grid).
+ * The device arrays are trusted; TDL_DEBUG=1 in the environment copies them
+ * back and checks them (and synchronises) before enqueuing. */
+tdl_status layer_decode_paged(tdl_layer* layer, tdl_stream stream, const void* x, void* y,
+                              int32_t batch, const int32_t* ctx_lens,
+                              const int32_t* block_tables, int32_t max_blocks,
+                              int32_t max_ctx_len, tdl_kv_cache* kv);
+
+/* A mixed step over a tdl_batch: all rows go through the projections and the
+ * MLP together; prefill sequences use the flash prefill attention kernel and
+ * decode sequences the paged decode kernel.  x, y [n_rows, H] bf16. */
+tdl_status layer_step(tdl_layer* layer, tdl_stream stream, const tdl_batch* batch,
+                      const void* x, void* y, tdl_kv_cache* kv);
+
+/* Pointers to the intermediate buffers (see tdl_workspace_view). */
+tdl_status layer_workspace_view(const tdl_layer* layer, tdl_workspace_view* out);
+
+/* ------------------------------------------------------------- KV cache */
+
+/* Bytes of device memory a cache with this configuration needs (pools plus,
+ * for TDL_U8_ASYM, the per-channel parameters).  0 for an invalid config. */
+size_t kv_cache_bytes(const tdl_kv_config* cfg);
+
+/* Creates a cache handle.  dev_mem == NULL: the library allocates
+ * kv_cache_bytes(cfg) device bytes (zeroed) and frees them in kv_cache_free;
+ * otherwise dev_mem (caller-owned, >= kv_cache_bytes, 256-byte aligned) is
+ * used as is and never touched by the host.  The host-side free list
+ * ([TFF] 3.6.4 PageManager) always lives in the handle. */
+tdl_status kv_cache_alloc(const tdl_kv_config* cfg, void* dev_mem, tdl_kv_cache** out);
+
+/* Frees the handle (and the device memory if the library allocated it).
+ * NULL is accepted. */
+tdl_status kv_cache_free(tdl_kv_cache* kv);
+
+tdl_status kv_cache_view(const tdl_kv_cache* kv, tdl_kv_view* out);
+
+/* Block tables on the host ([TFF] 3.6.4 append_token / allocate; [HET] 4.3
+ * acquire).  table (host int32 [n_seqs, max_blocks]) is read and updated:
+ * for sequence i, entries 0 .. ceil(n_tokens[i]/16)-1 that are < 0 receive a
+ * block popped from the free list; entries already >= 0 are kept; entries
+ * from ceil(n_tokens[i]/16) on are left alone.  All or nothing: if the free
+ * list is too short (TDL_E_CAPACITY) or any n_tokens[i] needs more than
+ * max_blocks blocks (TDL_E_INVALID), nothing changes. */
+tdl_status kv_block_table(tdl_kv_cache* kv, int32_t n_seqs, const int32_t* n_tokens,
+                          int32_t max_blocks, int32_t* table);
+
+/* Returns blocks to the free list ([HET] 4.3 release).  A block that is out
+ * of range or already free fails the whole call with TDL_E_INVALID and
+ * nothing is released. */
+tdl_status kv_block_release(tdl_kv_cache* kv, const int32_t* blocks, int32_t n);
+
+/* Number of blocks on the free list. */
+int32_t kv_free_blocks(const tdl_kv_cache* kv);
+
+/* TDL_U8_ASYM only: sets the per-channel (kv head, d) parameters of K and of
+ * V from n_tokens float32 rows k, v [n_tokens, Hkv, D] (device):
+ * scale = (max - min) / 255, zero_point = round_half_even(-min / scale),
+ * scale 1 for a flat channel ([HET] 2.6).  Later writes use them. */
+tdl_status kv_cache_calibrate(tdl_kv_cache* kv, tdl_stream stream, const float* k,
+                              const float* v, int64_t n_tokens);
+
+/* Writes K/V rows into the cache: rows cu_rows[i] .. cu_rows[i+1]-1 of k, v
+ * ([rows, Hkv, D], src_dtype TDL_F32 or TDL_BF16, device) belong to sequence
+ * i and go to positions start_pos[i] + 0, 1, ... through block_tables
+ * (device int32 [n_seqs, max_blocks]).  cu_rows, start_pos: device int32.
+ * bf16 caches round to nearest even; u8 caches quantise with
+ * clamp(round_half_even(x / scale) + zero_point, 0, 255). */
+tdl_status kv_cache_write(tdl_kv_cache* kv, tdl_stream stream, int32_t n_seqs,
+                          const int32_t* cu_rows, const int32_t* start_pos,
+                          const int32_t* block_tables, int32_t max_blocks, int32_t src_dtype,
+                          const void* k, const void* v, int32_t n_rows);
+
+/* --------------------------------------------------------------- errors */
+
+const char* tdl_status_string(tdl_status s);
+const char* tdl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TDL_H */

@@ -345,7 +345,7 @@ def expand_weights(shape, w: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
 
 def layer_forward(shape, w: Dict[str, np.ndarray], x: np.ndarray, q_start, q_len, ctx_len,
                   table: Optional[np.ndarray], cache: Optional[PagedCache],
-                  want_stages: bool = False):
+                  want_stages: bool = False, rows_out=None):
     """Forward pass of one pre-norm Qwen-style GQA decoder layer over a batch
     of sequences.
 
@@ -370,13 +370,19 @@ def layer_forward(shape, w: Dict[str, np.ndarray], x: np.ndarray, q_start, q_len
       9. a = silu(hn Wg^T) * (hn Wu^T)
      10. y = h + a Wd^T                      (second residual; reading: the
          standard pre-norm layer with two residual adds)
+
+    ``rows_out`` (optional, sorted row indices) restricts steps 6-10 to those
+    rows -- every row's k and v still reach the cache -- so long prompts can
+    be checked on a sample of rows.  The result then has one row per entry.
     """
     H, D = shape.hidden, shape.head_dim
     Hq, Hkv = shape.n_q_heads, shape.n_kv_heads
     x = np.asarray(x, np.float64)
     rows = x.shape[0]
+    sel = np.arange(rows) if rows_out is None else np.asarray(rows_out)
     xn = rms_norm(x, w["ln1"], shape.rms_eps)
-    q = linear(xn, w["wq"], w.get("bq")).reshape(rows, Hq, D)
+    q = np.zeros((rows, Hq, D))
+    q[sel] = linear(xn[sel], w["wq"], w.get("bq")).reshape(len(sel), Hq, D)
     k = linear(xn, w["wk"], w.get("bk")).reshape(rows, Hkv, D)
     v = linear(xn, w["wv"], w.get("bv")).reshape(rows, Hkv, D)
     if shape.qk_norm:
@@ -388,7 +394,9 @@ def layer_forward(shape, w: Dict[str, np.ndarray], x: np.ndarray, q_start, q_len
         pos[r0:r0 + int(q_len[i])] = int(ctx_len[i]) + np.arange(int(q_len[i]))
     q = rope_neox(q, pos[:, None], shape.rope_theta)
     k = rope_neox(k, pos[:, None], shape.rope_theta)
-    o = np.empty((rows, Hq, D))
+    o = np.zeros((rows, Hq, D))
+    in_sel = np.zeros(rows, bool)
+    in_sel[sel] = True
     for i in range(len(q_len)):
         r0, n, c = int(q_start[i]), int(q_len[i]), int(ctx_len[i])
         if n == 0:
@@ -400,14 +408,16 @@ def layer_forward(shape, w: Dict[str, np.ndarray], x: np.ndarray, q_start, q_len
             for t in range(n):
                 cache.write(table[i], c + t, k[r0 + t], v[r0 + t])
             Ks, Vs = cache.read(table[i], c + n)
-        o[r0:r0 + n] = attention(q[r0:r0 + n], pos[r0:r0 + n], Ks, Vs)
-    o2 = o.reshape(rows, Hq * D)
-    h = x + linear(o2, w["wo"])
+        mine = np.arange(r0, r0 + n)[in_sel[r0:r0 + n]]
+        if len(mine):
+            o[mine] = attention(q[mine], pos[mine], Ks, Vs)
+    o2 = o[sel].reshape(len(sel), Hq * D)
+    h = x[sel] + linear(o2, w["wo"])
     hn = rms_norm(h, w["ln2"], shape.rms_eps)
     a = swiglu(linear(hn, w["wg"]), linear(hn, w["wu"]))
     y = h + linear(a, w["wd"])
     if want_stages:
-        return y, dict(xn=xn, q=q, k=k, v=v, o=o2, h=h, hn=hn, a=a, pos=pos)
+        return y, dict(xn=xn[sel], q=q[sel], k=k, v=v, o=o2, h=h, hn=hn, a=a, pos=pos[sel])
     return y
 
 

@@ -1,0 +1,157 @@
+"""GPU parity of the whole layer through the C-ABI, stage by stage, against
+the oracle on the same seeded inputs.  Float stages meet the bf16 tolerance
+(harness.compare); cache slots and u8 codes are checked bit for bit."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from harness import compare, gpu_call, gpu_setup, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+TINY_Q3 = dataclasses.replace(synth.TINY, name="tiny-qwen3", qkv_bias=False, qk_norm=True,
+                              weight_dtype="bf16", rope_theta=1e6)
+TINY_Q80 = dataclasses.replace(TINY_Q3, name="tiny-q8_0", intermediate=704, weight_dtype="q80")
+TINY_D128 = dataclasses.replace(synth.TINY, name="tiny-d128", hidden=512, n_q_heads=7, n_kv_heads=1,
+                                head_dim=128, intermediate=1024, weight_dtype="bf16", rope_theta=1e6)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_decoder_layer_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_stages(layer, t, rows, shape):
+    import torch
+    import transformer_decoder_layer_amd as tdl
+    ws = layer.workspace()
+    n = int(t["x"].shape[0])
+    H, D, Hq, I = shape.hidden, shape.head_dim, shape.n_q_heads, shape.intermediate
+    get = lambda p, cols, dt: tdl.device_tensor(p, (n, cols), dt)[rows].float().cpu().numpy()
+    return dict(xn=get(ws.xn, H, torch.float16), q=get(ws.q, Hq * D, torch.float32),
+                o=get(ws.o, Hq * D, torch.float16), h=get(ws.h, H, torch.float32),
+                a=get(ws.a, I, torch.bfloat16))
+
+
+def check_layer(inp, seqs=None, what="", stages=True):
+    import torch
+    shape = inp.workload.shape
+    log(f"[{what}] gpu setup")
+    layer, kv, t = gpu_setup(inp)
+    log(f"[{what}] gpu call")
+    gpu_call(inp, layer, kv, t)
+    torch.cuda.synchronize()
+    log(f"[{what}] oracle")
+    rows, (ref, st), cache = run_oracle(inp, seqs, want_stages=True)
+    y = t["y"].float().cpu().numpy()[rows]
+    x_gpu = t["x"].float().cpu().numpy()[rows]
+    x = inp.x[rows].astype(np.float64)
+    errs = {"y": compare(y, ref)}
+    if stages:
+        g = gpu_stages(layer, t, rows, shape)
+        errs["xn"] = compare(g["xn"], st["xn"])
+        errs["q"] = compare(g["q"], st["q"].reshape(len(rows), -1))
+        errs["o"] = compare(g["o"], st["o"])
+        errs["h-x"] = compare(g["h"] - x_gpu, st["h"] - x)
+        errs["a"] = compare(g["a"], st["a"])
+    for k, e in errs.items():
+        log(f"[{what}] {k}: {e}")
+    bad = [k for k, e in errs.items() if not e.ok]
+    assert not bad, f"{what}: stages out of tolerance: {bad}"
+    return layer, kv, t, cache, rows
+
+
+def check_cache_rows(inp, kv, cache, seqs):
+    """New tokens' K/V in the GPU pool: bf16 values within tolerance of the
+    oracle's (both round their own projections), u8 codes within one code."""
+    import torch
+    b = inp.batch
+    kt, vt = kv.tensors()[:2]
+    kg, vg, kr, vr = [], [], [], []
+    for i in seqs:
+        for p in range(int(b.ctx_len[i]), int(b.ctx_len[i] + b.q_len[i])):
+            blk, off = oracle.PagedCache.location(b.table[i], p)
+            kg.append(kt[blk, :, off, :].float().cpu().numpy())
+            vg.append(vt[blk, :, :, off].float().cpu().numpy())
+            kr.append(cache.k[blk, :, off, :].astype(np.float64))
+            vr.append(cache.v[blk, :, off, :].astype(np.float64))
+    kg, vg, kr, vr = map(np.array, (kg, vg, kr, vr))
+    if cache.dtype == "u8":
+        assert np.abs(kg - kr).max() <= 1 and np.abs(vg - vr).max() <= 1
+        assert (kg != kr).mean() < 0.05 and (vg != vr).mean() < 0.05
+    else:
+        ek, ev = compare(kg, kr), compare(vg, vr)
+        log(f"new K {ek}\nnew V {ev}")
+        assert ek.ok and ev.ok
+
+
+# ----------------------------------------------------------------- tiny ---
+
+def test_tiny_prefill_no_cache():
+    inp = synth.make_inputs(synth.WORKLOADS["tiny_prefill_32"])
+    check_layer(inp, what="tiny prefill 32")
+
+
+@pytest.mark.parametrize("T", [1, 45, 130])
+def test_tiny_prefill_paged(T):
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], kv_dtype="bf16")
+    inp = synth.make_inputs(wl, seed=T, prefill_len=T, spare_blocks=3)
+    layer, kv, t, cache, rows = check_layer(inp, what=f"tiny paged prefill {T}")
+    check_cache_rows(inp, kv, cache, [0])
+
+
+def test_tiny_chunked_prefill_start_pos():
+    # a second chunk attends to the cached first chunk
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=TINY_Q3, kv_dtype="bf16")
+    inp = synth.make_inputs(wl, seed=5, prefill_len=37, prefill_start=83, spare_blocks=2)
+    layer, kv, t, cache, rows = check_layer(inp, what="tiny chunk start 83")
+    check_cache_rows(inp, kv, cache, [0])
+
+
+@pytest.mark.parametrize("shape", [synth.TINY, TINY_Q3, TINY_D128], ids=lambda s: s.name)
+def test_tiny_decode_bf16(shape):
+    wl = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=shape)
+    ctx = [0, 1, 15, 16, 17, 31, 100, 250, 511, 1000]
+    inp = synth.make_inputs(wl, seed=3, decode_batch=len(ctx), decode_ctx=ctx)
+    layer, kv, t, cache, rows = check_layer(inp, what=f"decode bf16 {shape.name}")
+    check_cache_rows(inp, kv, cache, range(len(ctx)))
+
+
+def test_tiny_decode_u8():
+    wl = dataclasses.replace(synth.WORKLOADS["qwen3_decode_u8_b128"], shape=TINY_Q3)
+    ctx = [1, 15, 16, 17, 64, 300, 777, 2048]
+    inp = synth.make_inputs(wl, seed=4, decode_batch=len(ctx), decode_ctx=ctx)
+    layer, kv, t, cache, rows = check_layer(inp, what="decode u8 tiny")
+    check_cache_rows(inp, kv, cache, range(len(ctx)))
+
+
+def test_tiny_mixed_q80():
+    wl = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=TINY_Q80)
+    inp = synth.make_inputs(wl, seed=6, prefill_len=77, decode_batch=5, decode_ctx=[3, 16, 40, 129, 500])
+    layer, kv, t, cache, rows = check_layer(inp, what="mixed q80 tiny")
+    check_cache_rows(inp, kv, cache, range(6))
+
+
+# ------------------------------------------------------ full-size shapes ---
+
+def test_qwen25_prefill_512():
+    inp = synth.make_inputs(synth.WORKLOADS["qwen25_prefill_512"])
+    check_layer(inp, what="qwen2.5 prefill 512")
+
+
+def test_qwen25_decode_b64():
+    inp = synth.make_inputs(synth.WORKLOADS["qwen25_decode_b64"])
+    layer, kv, t, cache, rows = check_layer(inp, what="qwen2.5 decode b64")
+    check_cache_rows(inp, kv, cache, range(64))

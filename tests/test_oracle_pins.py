@@ -376,3 +376,16 @@ def test_batch_rows_independent():
     y = oracle.layer_forward(shape, W, x, [0, 6], [6, 1], [0, 40], table, cache)
     y1 = oracle.layer_forward(shape, W, x[6:], [0], [1], [40], table[1:], c_alone)
     np.testing.assert_allclose(y[6], y1[0], rtol=1e-13)
+
+
+def test_sampled_rows_equal_full_rows():
+    # restricting the output rows changes nothing in the rows that are kept
+    shape = tiny_shape()
+    W = oracle.expand_weights(shape, synth.make_weights(shape, seed=11))
+    x = np.random.default_rng(12).standard_normal((20, 32))
+    table = np.array([[2, 0]], np.int32)
+    y_all = oracle.layer_forward(shape, W, x, [0], [20], [0], table, oracle.PagedCache(3, 2, 8, "bf16"))
+    sel = np.array([0, 7, 19])
+    y_sel = oracle.layer_forward(shape, W, x, [0], [20], [0], table, oracle.PagedCache(3, 2, 8, "bf16"),
+                                 rows_out=sel)
+    assert np.array_equal(y_sel, y_all[sel])

@@ -1,0 +1,780 @@
+// C-ABI entry points of libtdl: argument checks, handle ownership, the host
+// free list of KV blocks, and the per-call launch sequence of the layer.
+//
+// Launch sequence of one call (the op order of the Qwen2.5-7B single-layer
+// page's architecture overview, each step a gfx950 kernel):
+//   rmsnorm(x) -> gemm_qkv(+bias) -> rope/q-k norm/kv write -> attention
+//   (prefill and/or paged decode) -> gemm_o(+x) -> rmsnorm(h) ->
+//   gemm_gate_up(silu gate) -> gemm_down(+h)
+
+#include "../../include/tdl.h"
+#include "kernels.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace tdl;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tdl_status fail(tdl_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(TDL_E_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, \
+                  __LINE__);                                                            \
+  } while (0)
+
+bool debug_checks() {
+  const char* e = std::getenv("TDL_DEBUG");
+  return e && e[0] == '1';
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+}  // namespace
+
+// ------------------------------------------------------------------ types
+
+struct tdl_kv_cache {
+  tdl_kv_config cfg;
+  void* mem = nullptr;
+  bool owned = false;
+  void* k = nullptr;
+  void* v = nullptr;
+  float* k_scale = nullptr;
+  int32_t* k_zp = nullptr;
+  float* v_scale = nullptr;
+  int32_t* v_zp = nullptr;
+  std::vector<int32_t> free_list;  // LIFO: back() is handed out next
+  std::vector<uint8_t> is_free;
+};
+
+struct tdl_layer {
+  tdl_layer_config cfg;
+  bool q80 = false;
+  int Nqkv = 0;
+  // weights (library-owned)
+  void* wqkv = nullptr;
+  __half* wqkv_s = nullptr;
+  float* bqkv = nullptr;
+  void* wo = nullptr;
+  __half* wo_s = nullptr;
+  void* wgu = nullptr;
+  __half* wgu_s = nullptr;
+  void* wd = nullptr;
+  __half* wd_s = nullptr;
+  float *ln1 = nullptr, *ln2 = nullptr, *qn = nullptr, *kn = nullptr;
+  float2* rope = nullptr;
+  // workspace
+  void *xn = nullptr, *qkv = nullptr, *q = nullptr, *o = nullptr, *hn = nullptr, *a = nullptr;
+  float* h = nullptr;
+  float* gemm_ws = nullptr;
+  size_t gemm_ws_floats = 0;
+  int* gemm_cnt = nullptr;
+  int gemm_cnt_n = 0;
+  float* dec_part = nullptr;
+  size_t dec_part_floats = 0;
+  int* dec_cnt = nullptr;
+  int dec_cnt_n = 0;
+  void* priv_k = nullptr;  // bf16 pool for calls without a KV cache
+  void* priv_v = nullptr;
+  std::vector<void*> allocs;
+
+  ~tdl_layer() {
+    for (void* p : allocs) (void)hipFree(p);
+  }
+};
+
+namespace {
+
+template <typename T>
+tdl_status dalloc(tdl_layer* L, T** out, size_t bytes) {
+  void* p = nullptr;
+  if (bytes == 0) bytes = 256;
+  if (hipMalloc(&p, bytes) != hipSuccess)
+    return fail(TDL_E_NOMEM, "hipMalloc of %zu bytes failed", bytes);
+  L->allocs.push_back(p);
+  *out = (T*)p;
+  return TDL_OK;
+}
+
+#define TRY(expr)                   \
+  do {                              \
+    tdl_status s_ = (expr);         \
+    if (s_ != TDL_OK) return s_;    \
+  } while (0)
+
+tdl_status check_config(const tdl_layer_config* c) {
+  if (!c) return fail(TDL_E_INVALID, "config is NULL");
+  if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->intermediate <= 0)
+    return fail(TDL_E_INVALID, "non-positive layer dimension");
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(TDL_E_INVALID, "n_q_heads (%d) not a multiple of n_kv_heads (%d)", c->n_q_heads,
+                c->n_kv_heads);
+  const int n_rep = c->n_q_heads / c->n_kv_heads;
+  if (!(n_rep == 1 || n_rep == 2 || n_rep == 4 || n_rep == 7 || n_rep == 8))
+    return fail(TDL_E_UNSUPPORTED, "query heads per KV head must be 1, 2, 4, 7 or 8 (got %d)", n_rep);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(TDL_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
+  if (c->hidden % 64)
+    return fail(TDL_E_UNSUPPORTED, "hidden must be a multiple of 64 (got %d)", c->hidden);
+  if (c->intermediate % 16)
+    return fail(TDL_E_UNSUPPORTED, "intermediate must be a multiple of 16 (got %d)", c->intermediate);
+  if (c->weight_dtype != TDL_F32 && c->weight_dtype != TDL_BF16 && c->weight_dtype != TDL_Q8_0)
+    return fail(TDL_E_INVALID, "weight_dtype must be TDL_F32, TDL_BF16 or TDL_Q8_0");
+  if (c->weight_dtype == TDL_Q8_0 && (c->hidden % 32 || c->intermediate % 32 ||
+                                      (c->n_q_heads * c->head_dim) % 32))
+    return fail(TDL_E_INVALID, "Q8_0 needs every input dimension to be a multiple of 32");
+  if (c->max_tokens <= 0 || c->max_seqs <= 0 || c->max_position <= 0)
+    return fail(TDL_E_INVALID, "max_tokens, max_seqs and max_position must be positive");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f))
+    return fail(TDL_E_INVALID, "rms_eps must be >= 0 and rope_theta > 0");
+  return TDL_OK;
+}
+
+struct GemmShapes {
+  int Nqkv, H, Hq_D, I;
+};
+
+// Largest split-K workspace / counter count over every row count a call may use.
+void gemm_ws_need(const tdl_layer_config& c, int Nqkv, bool q80, size_t* ws, int* cnt) {
+  const int H = c.hidden, QD = c.n_q_heads * c.head_dim, I = c.intermediate;
+  const int shapes[4][3] = {{Nqkv, H, EPI_BIAS_F32}, {H, QD, EPI_RESID_F32},
+                            {2 * I, H, EPI_SILU_GATE}, {H, I, EPI_RESID_BF16}};
+  size_t w = 0;
+  int n = 0;
+  for (int M = 1; M <= c.max_tokens; ++M)
+    for (auto& s : shapes) {
+      const GemmPlan p = gemm_plan(M, s[0], s[1], q80, s[2]);
+      w = std::max(w, p.ws_floats);
+      n = std::max(n, p.n_counters);
+    }
+  *ws = w;
+  *cnt = n;
+}
+
+size_t decode_part_need(const tdl_layer_config& c, int batch) {
+  const int Hkv = c.n_kv_heads;
+  const int want = std::max(1, (2048 + batch * Hkv - 1) / (batch * Hkv));
+  return (size_t)batch * Hkv * (want + 1) * (16 * c.head_dim + 32);
+}
+
+KvPool pool_of(const tdl_layer* L, const tdl_kv_cache* kv) {
+  KvPool p{};
+  if (kv) {
+    p.k = kv->k;
+    p.v = kv->v;
+    p.u8 = kv->cfg.kv_dtype == TDL_U8_ASYM;
+    p.k_scale = kv->k_scale;
+    p.k_zp = kv->k_zp;
+    p.v_scale = kv->v_scale;
+    p.v_zp = kv->v_zp;
+  } else {
+    p.k = L->priv_k;
+    p.v = L->priv_v;
+  }
+  return p;
+}
+
+tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const void* A, const void* B,
+                    const __half* Bs, int epi, const float* bias, const void* resid, int ldr,
+                    void* C, int ldc) {
+  const GemmPlan pl = gemm_plan(M, N, K, L->q80, epi);
+  if (pl.ws_floats > L->gemm_ws_floats || pl.n_counters > L->gemm_cnt_n)
+    return fail(TDL_E_CAPACITY, "GEMM workspace too small for M=%d N=%d K=%d", M, N, K);
+  GemmArgs a{};
+  a.A = A;
+  a.lda = K;
+  a.B = B;
+  a.ldb = K;
+  a.B_scale = Bs;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.bias = bias;
+  a.resid = resid;
+  a.ldr = ldr;
+  a.C = C;
+  a.ldc = ldc;
+  a.ws = L->gemm_ws;
+  a.counters = L->gemm_cnt;
+  HIP_TRY(gemm_launch(pl, a, L->q80, epi, st));
+  return TDL_OK;
+}
+
+// The whole layer over `rows` rows.  Sequences 0..n_prefill-1 of `seq` use the
+// prefill attention kernel, decode sequences dec_first .. dec_first+n_dec-1
+// the paged decode kernel.
+tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int rows, SeqInfo seq,
+                     KvPool pool, int n_prefill, int max_q_len, int dec_first, int n_dec,
+                     int max_ctx_len) {
+  const tdl_layer_config& c = L->cfg;
+  const int H = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, I = c.intermediate;
+  DecodePlan dp{};
+  if (n_dec) {
+    dp = decode_plan(n_dec, Hq, Hkv, D, max_ctx_len);
+    if (dp.part_floats > L->dec_part_floats || dp.n_counters > L->dec_cnt_n)
+      return fail(TDL_E_CAPACITY, "decode workspace too small (batch %d, max_ctx_len %d)", n_dec,
+                  max_ctx_len);
+  }
+  HIP_TRY(rmsnorm_bf16in(x, L->ln1, L->xn, rows, H, c.rms_eps, st));
+  TRY(run_gemm(L, st, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, EPI_BIAS_F32, L->bqkv, nullptr, 0,
+               L->qkv, L->Nqkv));
+  HIP_TRY(rope_kv_write(L->qkv, rows, Hq, Hkv, D, L->rope, c.qk_norm ? L->qn : nullptr,
+                        c.qk_norm ? L->kn : nullptr, c.rms_eps, L->q, seq, pool, st));
+  if (n_prefill) HIP_TRY(attn_prefill(L->q, pool, seq, n_prefill, max_q_len, Hq, Hkv, D, L->o, st));
+  if (n_dec)
+    HIP_TRY(attn_decode(dp, L->q, pool, seq, dec_first, 0, n_dec, Hq, Hkv, D, L->o, L->dec_part,
+                        L->dec_cnt, st));
+  TRY(run_gemm(L, st, rows, H, Hq * D, L->o, L->wo, L->wo_s, EPI_RESID_F32, nullptr, x, H, L->h, H));
+  HIP_TRY(rmsnorm_f32in(L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
+  TRY(run_gemm(L, st, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, EPI_SILU_GATE, nullptr, nullptr, 0,
+               L->a, I));
+  TRY(run_gemm(L, st, rows, H, I, L->a, L->wd, L->wd_s, EPI_RESID_BF16, nullptr, L->h, H, y, H));
+  return TDL_OK;
+}
+
+tdl_status check_kv_matches(const tdl_layer* L, const tdl_kv_cache* kv) {
+  if (!kv) return TDL_OK;
+  if (kv->cfg.n_kv_heads != L->cfg.n_kv_heads || kv->cfg.head_dim != L->cfg.head_dim)
+    return fail(TDL_E_INVALID, "KV cache heads/head_dim do not match the layer");
+  return TDL_OK;
+}
+
+// TDL_DEBUG=1: copy device tables back and check every entry a call will read.
+tdl_status debug_check_tables(const int32_t* ctx_dev, const int32_t* qlen_dev, int n, int extra,
+                              const int32_t* tables_dev, int max_blocks, int n_blocks,
+                              int max_ctx_len, hipStream_t st) {
+  std::vector<int32_t> ctx(n), qlen(n, extra), tab((size_t)n * max_blocks);
+  HIP_TRY(hipStreamSynchronize(st));
+  HIP_TRY(hipMemcpy(ctx.data(), ctx_dev, n * sizeof(int32_t), hipMemcpyDeviceToHost));
+  if (qlen_dev) HIP_TRY(hipMemcpy(qlen.data(), qlen_dev, n * sizeof(int32_t), hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(tab.data(), tables_dev, tab.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
+  for (int i = 0; i < n; ++i) {
+    const int total = ctx[i] + qlen[i];
+    if (ctx[i] < 0 || total > max_ctx_len)
+      return fail(TDL_E_INVALID, "sequence %d: ctx_len %d + %d exceeds max_ctx_len %d", i, ctx[i],
+                  qlen[i], max_ctx_len);
+    for (int b = 0; b < (total + 15) / 16; ++b) {
+      const int blk = tab[(size_t)i * max_blocks + b];
+      if (blk < 0 || blk >= n_blocks)
+        return fail(TDL_E_INVALID, "sequence %d: block table entry %d = %d out of range", i, b, blk);
+    }
+  }
+  return TDL_OK;
+}
+
+uint64_t splitmix64(uint64_t& s) {
+  uint64_t z = (s += 0x9e3779b97f4a7c15ull);
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+
+}  // namespace
+
+// ================================================================ layer
+
+extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_weights* w,
+                                   tdl_stream stream, tdl_layer** out) {
+  if (!out) return fail(TDL_E_INVALID, "out is NULL");
+  *out = nullptr;
+  TRY(check_config(cfg));
+  if (!w) return fail(TDL_E_INVALID, "weights are NULL");
+  const tdl_layer_config& c = *cfg;
+  const bool q80 = c.weight_dtype == TDL_Q8_0;
+  if (!w->ln1 || !w->wq || !w->wk || !w->wv || !w->wo || !w->ln2 || !w->wg || !w->wu || !w->wd)
+    return fail(TDL_E_INVALID, "a required weight pointer is NULL");
+  if (c.qkv_bias && (!w->bq || !w->bk || !w->bv))
+    return fail(TDL_E_INVALID, "qkv_bias set but a bias pointer is NULL");
+  if (c.qk_norm && (!w->q_norm || !w->k_norm))
+    return fail(TDL_E_INVALID, "qk_norm set but q_norm/k_norm is NULL");
+  if (q80 && (!w->wq_scale || !w->wk_scale || !w->wv_scale || !w->wo_scale || !w->wg_scale ||
+              !w->wu_scale || !w->wd_scale))
+    return fail(TDL_E_INVALID, "Q8_0 weights need every *_scale pointer");
+
+  hipStream_t st = (hipStream_t)stream;
+  tdl_layer* L = new tdl_layer();
+  L->cfg = c;
+  L->q80 = q80;
+  const int H = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, I = c.intermediate;
+  const int QD = Hq * D, KD = Hkv * D;
+  L->Nqkv = QD + 2 * KD;
+  const int T = c.max_tokens;
+  auto bail = [&](tdl_status s) {
+    delete L;
+    return s;
+  };
+#define CTRY(expr)                        \
+  do {                                    \
+    tdl_status s2_ = (expr);              \
+    if (s2_ != TDL_OK) return bail(s2_);  \
+  } while (0)
+#define CHIP(expr)                                                                            \
+  do {                                                                                        \
+    hipError_t e2_ = (expr);                                                                  \
+    if (e2_ != hipSuccess)                                                                    \
+      return bail(fail(TDL_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e2_)));          \
+  } while (0)
+
+  // ---- weights: bf16 copies (f32 rounded to nearest even), or Q8_0 codes
+  const size_t wel = q80 ? 1 : 2;  // bytes per stored weight element
+  CTRY(dalloc(L, &L->wqkv, (size_t)L->Nqkv * H * wel));
+  CTRY(dalloc(L, &L->wo, (size_t)H * QD * wel));
+  CTRY(dalloc(L, &L->wgu, (size_t)2 * I * H * wel));
+  CTRY(dalloc(L, &L->wd, (size_t)H * I * wel));
+  // fp16 copies for the projections whose activation input is bounded (QKV,
+  // output, gate/up); bf16 for the down projection.  Saturated fp16 values
+  // are counted and refused below.
+  int* n_sat = nullptr;
+  CTRY(dalloc(L, &n_sat, 4));
+  CHIP(hipMemsetAsync(n_sat, 0, 4, st));
+  auto put = [&](const void* src, void* dst, int64_t n, int to_f16) -> tdl_status {
+    const hipError_t e = q80 ? hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, st)
+                             : convert_weights(src, c.weight_dtype == TDL_F32, dst, to_f16, n,
+                                               n_sat, st);
+    if (e != hipSuccess) return fail(TDL_E_HIP, "weight copy failed: %s", hipGetErrorString(e));
+    return TDL_OK;
+  };
+  char* qkv = (char*)L->wqkv;
+  CTRY(put(w->wq, qkv, (int64_t)QD * H, 1));
+  CTRY(put(w->wk, qkv + (size_t)QD * H * wel, (int64_t)KD * H, 1));
+  CTRY(put(w->wv, qkv + (size_t)(QD + KD) * H * wel, (int64_t)KD * H, 1));
+  CTRY(put(w->wo, L->wo, (int64_t)H * QD, 1));
+  CTRY(put(w->wd, L->wd, (int64_t)H * I, 0));
+  {
+    // gate/up: convert to the stored type, then interleave 16-row groups
+    void* g16 = nullptr;
+    void* u16 = nullptr;
+    CTRY(dalloc(L, &g16, (size_t)I * H * wel));
+    CTRY(dalloc(L, &u16, (size_t)I * H * wel));
+    CTRY(put(w->wg, g16, (int64_t)I * H, 1));
+    CTRY(put(w->wu, u16, (int64_t)I * H, 1));
+    CHIP(interleave_gate_up(g16, u16, (int)(H * wel), I, L->wgu, st));
+    CHIP(hipStreamSynchronize(st));
+    for (void* p : {g16, u16}) {
+      L->allocs.erase(std::find(L->allocs.begin(), L->allocs.end(), p));
+      (void)hipFree(p);
+    }
+  }
+  if (q80) {
+    CTRY(dalloc(L, &L->wqkv_s, (size_t)L->Nqkv * (H / 32) * 2));
+    CTRY(dalloc(L, &L->wo_s, (size_t)H * (QD / 32) * 2));
+    CTRY(dalloc(L, &L->wgu_s, (size_t)2 * I * (H / 32) * 2));
+    CTRY(dalloc(L, &L->wd_s, (size_t)H * (I / 32) * 2));
+    char* s = (char*)L->wqkv_s;
+    const size_t rs = (size_t)(H / 32) * 2;
+    CHIP(hipMemcpyAsync(s, w->wq_scale, QD * rs, hipMemcpyDeviceToDevice, st));
+    CHIP(hipMemcpyAsync(s + QD * rs, w->wk_scale, KD * rs, hipMemcpyDeviceToDevice, st));
+    CHIP(hipMemcpyAsync(s + (QD + KD) * rs, w->wv_scale, KD * rs, hipMemcpyDeviceToDevice, st));
+    CHIP(hipMemcpyAsync(L->wo_s, w->wo_scale, (size_t)H * (QD / 32) * 2, hipMemcpyDeviceToDevice, st));
+    CHIP(hipMemcpyAsync(L->wd_s, w->wd_scale, (size_t)H * (I / 32) * 2, hipMemcpyDeviceToDevice, st));
+    CHIP(interleave_gate_up(w->wg_scale, w->wu_scale, (int)rs, I, L->wgu_s, st));
+  }
+  if (c.qkv_bias) {
+    CTRY(dalloc(L, &L->bqkv, (size_t)L->Nqkv * 4));
+    CHIP(copy_f32((const float*)w->bq, L->bqkv, QD, st));
+    CHIP(copy_f32((const float*)w->bk, L->bqkv + QD, KD, st));
+    CHIP(copy_f32((const float*)w->bv, L->bqkv + QD + KD, KD, st));
+  }
+  CTRY(dalloc(L, &L->ln1, (size_t)H * 4));
+  CTRY(dalloc(L, &L->ln2, (size_t)H * 4));
+  CHIP(copy_f32((const float*)w->ln1, L->ln1, H, st));
+  CHIP(copy_f32((const float*)w->ln2, L->ln2, H, st));
+  if (c.qk_norm) {
+    CTRY(dalloc(L, &L->qn, (size_t)D * 4));
+    CTRY(dalloc(L, &L->kn, (size_t)D * 4));
+    CHIP(copy_f32((const float*)w->q_norm, L->qn, D, st));
+    CHIP(copy_f32((const float*)w->k_norm, L->kn, D, st));
+  }
+  CTRY(dalloc(L, &L->rope, (size_t)c.max_position * (D / 2) * sizeof(float2)));
+  CHIP(rope_table_build(L->rope, c.max_position, D, (double)c.rope_theta, st));
+
+  // ---- workspace
+  CTRY(dalloc(L, &L->xn, (size_t)T * H * 2));
+  CTRY(dalloc(L, &L->qkv, (size_t)T * L->Nqkv * 4));
+  CTRY(dalloc(L, &L->q, (size_t)T * QD * 4));
+  CTRY(dalloc(L, &L->o, (size_t)T * QD * 2));
+  CTRY(dalloc(L, &L->h, (size_t)T * H * 4));
+  CTRY(dalloc(L, &L->hn, (size_t)T * H * 2));
+  CTRY(dalloc(L, &L->a, (size_t)T * I * 2));
+  gemm_ws_need(c, L->Nqkv, q80, &L->gemm_ws_floats, &L->gemm_cnt_n);
+  CTRY(dalloc(L, &L->gemm_ws, L->gemm_ws_floats * 4));
+  CTRY(dalloc(L, &L->gemm_cnt, (size_t)std::max(1, L->gemm_cnt_n) * 4));
+  CHIP(hipMemsetAsync(L->gemm_cnt, 0, (size_t)std::max(1, L->gemm_cnt_n) * 4, st));
+  const int max_dec = std::min(c.max_seqs, c.max_tokens);
+  L->dec_part_floats = decode_part_need(c, max_dec);
+  L->dec_cnt_n = max_dec * Hkv;
+  CTRY(dalloc(L, &L->dec_part, L->dec_part_floats * 4));
+  CTRY(dalloc(L, &L->dec_cnt, (size_t)L->dec_cnt_n * 4));
+  CHIP(hipMemsetAsync(L->dec_cnt, 0, (size_t)L->dec_cnt_n * 4, st));
+  const size_t priv_blocks = (size_t)(T + 15) / 16;
+  CTRY(dalloc(L, &L->priv_k, priv_blocks * KD * 16 * 2));
+  CTRY(dalloc(L, &L->priv_v, priv_blocks * KD * 16 * 2));
+  CHIP(hipStreamSynchronize(st));
+  int sat = 0;
+  CHIP(hipMemcpy(&sat, n_sat, 4, hipMemcpyDeviceToHost));
+  if (sat)
+    return bail(fail(TDL_E_UNSUPPORTED, "%d weights exceed the fp16 range (|w| > 65504)", sat));
+  *out = L;
+  return TDL_OK;
+#undef CTRY
+#undef CHIP
+}
+
+extern "C" tdl_status layer_destroy(tdl_layer* layer) {
+  delete layer;
+  return TDL_OK;
+}
+
+extern "C" tdl_status layer_prefill(tdl_layer* L, tdl_stream stream, const void* x, void* y,
+                                    int32_t n_tokens, int32_t start_pos, tdl_kv_cache* kv,
+                                    const int32_t* block_table) {
+  if (!L) return fail(TDL_E_INVALID, "layer is NULL");
+  if (!x || !y) return fail(TDL_E_INVALID, "x or y is NULL");
+  if (x == y) return fail(TDL_E_INVALID, "y must not alias x");
+  if (n_tokens < 1 || n_tokens > L->cfg.max_tokens)
+    return fail(n_tokens < 1 ? TDL_E_INVALID : TDL_E_CAPACITY,
+                "n_tokens %d outside [1, max_tokens=%d]", n_tokens, L->cfg.max_tokens);
+  if (start_pos < 0) return fail(TDL_E_INVALID, "start_pos < 0");
+  if ((int64_t)start_pos + n_tokens > L->cfg.max_position)
+    return fail(TDL_E_CAPACITY, "positions up to %d exceed max_position %d",
+                start_pos + n_tokens - 1, L->cfg.max_position);
+  if (!kv && start_pos != 0) return fail(TDL_E_INVALID, "start_pos > 0 needs a KV cache");
+  if (kv && !block_table) return fail(TDL_E_INVALID, "a KV cache needs a block table");
+  TRY(check_kv_matches(L, kv));
+  if (kv && kv->cfg.kv_dtype == TDL_U8_ASYM)
+    return fail(TDL_E_UNSUPPORTED, "prefill attention over a u8 cache is not implemented");
+  const int total = start_pos + n_tokens;
+  if (kv && total > kv->cfg.n_blocks * 16)
+    return fail(TDL_E_CAPACITY, "sequence longer than the cache pool");
+  hipStream_t st = (hipStream_t)stream;
+  if (kv && debug_checks()) {
+    int32_t ctx_h = start_pos;
+    (void)ctx_h;
+    std::vector<int32_t> tab((total + 15) / 16);
+    HIP_TRY(hipStreamSynchronize(st));
+    HIP_TRY(hipMemcpy(tab.data(), block_table, tab.size() * 4, hipMemcpyDeviceToHost));
+    for (size_t b = 0; b < tab.size(); ++b)
+      if (tab[b] < 0 || tab[b] >= kv->cfg.n_blocks)
+        return fail(TDL_E_INVALID, "block table entry %zu = %d out of range", b, tab[b]);
+  }
+  SeqInfo seq{};
+  seq.n_seqs = 1;
+  seq.q_len0 = n_tokens;
+  seq.ctx0 = start_pos;
+  seq.tables = kv ? block_table : nullptr;
+  seq.max_blocks = 0;
+  return run_layer(L, st, x, y, n_tokens, seq, pool_of(L, kv), 1, n_tokens, 0, 0, 0);
+}
+
+extern "C" tdl_status layer_decode_paged(tdl_layer* L, tdl_stream stream, const void* x, void* y,
+                                         int32_t batch, const int32_t* ctx_lens,
+                                         const int32_t* block_tables, int32_t max_blocks,
+                                         int32_t max_ctx_len, tdl_kv_cache* kv) {
+  if (!L) return fail(TDL_E_INVALID, "layer is NULL");
+  if (!x || !y || !ctx_lens || !block_tables || !kv)
+    return fail(TDL_E_INVALID, "x, y, ctx_lens, block_tables and kv are required");
+  if (x == y) return fail(TDL_E_INVALID, "y must not alias x");
+  if (batch < 1) return fail(TDL_E_INVALID, "batch < 1");
+  if (batch > L->cfg.max_seqs || batch > L->cfg.max_tokens)
+    return fail(TDL_E_CAPACITY, "batch %d exceeds max_seqs/max_tokens", batch);
+  if (max_blocks < 1) return fail(TDL_E_INVALID, "max_blocks < 1");
+  if (max_ctx_len < 1 || max_ctx_len > max_blocks * 16)
+    return fail(TDL_E_INVALID, "max_ctx_len %d outside [1, max_blocks*16]", max_ctx_len);
+  if (max_ctx_len > L->cfg.max_position)
+    return fail(TDL_E_CAPACITY, "max_ctx_len %d exceeds max_position %d", max_ctx_len,
+                L->cfg.max_position);
+  TRY(check_kv_matches(L, kv));
+  hipStream_t st = (hipStream_t)stream;
+  if (debug_checks())
+    TRY(debug_check_tables(ctx_lens, nullptr, batch, 1, block_tables, max_blocks, kv->cfg.n_blocks,
+                           max_ctx_len, st));
+  SeqInfo seq{};
+  seq.ctx_len = ctx_lens;
+  seq.n_seqs = batch;
+  seq.tables = block_tables;
+  seq.max_blocks = max_blocks;
+  seq.rows_are_seqs = 1;
+  return run_layer(L, st, x, y, batch, seq, pool_of(L, kv), 0, 0, 0, batch, max_ctx_len);
+}
+
+extern "C" tdl_status layer_step(tdl_layer* L, tdl_stream stream, const tdl_batch* b, const void* x,
+                                 void* y, tdl_kv_cache* kv) {
+  if (!L) return fail(TDL_E_INVALID, "layer is NULL");
+  if (!b || !x || !y || !kv) return fail(TDL_E_INVALID, "batch, x, y and kv are required");
+  if (x == y) return fail(TDL_E_INVALID, "y must not alias x");
+  if (!b->q_start || !b->q_len || !b->ctx_len || !b->block_tables)
+    return fail(TDL_E_INVALID, "batch arrays are required");
+  if (b->n_seqs < 1 || b->n_prefill_seqs < 0 || b->n_prefill_seqs > b->n_seqs)
+    return fail(TDL_E_INVALID, "need 0 <= n_prefill_seqs <= n_seqs, n_seqs >= 1");
+  const int n_dec = b->n_seqs - b->n_prefill_seqs;
+  if (b->n_rows < b->n_seqs || b->n_rows > L->cfg.max_tokens)
+    return fail(b->n_rows < b->n_seqs ? TDL_E_INVALID : TDL_E_CAPACITY,
+                "n_rows %d outside [n_seqs, max_tokens=%d]", b->n_rows, L->cfg.max_tokens);
+  if (b->n_seqs > L->cfg.max_seqs) return fail(TDL_E_CAPACITY, "n_seqs exceeds max_seqs");
+  if (b->n_prefill_seqs > 0 && b->max_q_len < 1)
+    return fail(TDL_E_INVALID, "max_q_len must be >= 1 with prefill sequences");
+  if (b->max_blocks < 1 || b->max_ctx_len < 1 || b->max_ctx_len > b->max_blocks * 16)
+    return fail(TDL_E_INVALID, "max_ctx_len must be in [1, max_blocks*16]");
+  if (b->max_ctx_len > L->cfg.max_position)
+    return fail(TDL_E_CAPACITY, "max_ctx_len exceeds max_position");
+  TRY(check_kv_matches(L, kv));
+  if (kv->cfg.kv_dtype == TDL_U8_ASYM && b->n_prefill_seqs > 0)
+    return fail(TDL_E_UNSUPPORTED, "prefill attention over a u8 cache is not implemented");
+  hipStream_t st = (hipStream_t)stream;
+  if (debug_checks())
+    TRY(debug_check_tables(b->ctx_len, b->q_len, b->n_seqs, 1, b->block_tables, b->max_blocks,
+                           kv->cfg.n_blocks, b->max_ctx_len, st));
+  SeqInfo seq{};
+  seq.q_start = b->q_start;
+  seq.q_len = b->q_len;
+  seq.ctx_len = b->ctx_len;
+  seq.n_seqs = b->n_seqs;
+  seq.tables = b->block_tables;
+  seq.max_blocks = b->max_blocks;
+  return run_layer(L, st, x, y, b->n_rows, seq, pool_of(L, kv), b->n_prefill_seqs, b->max_q_len,
+                   b->n_prefill_seqs, n_dec, b->max_ctx_len);
+}
+
+extern "C" tdl_status layer_workspace_view(const tdl_layer* L, tdl_workspace_view* out) {
+  if (!L || !out) return fail(TDL_E_INVALID, "NULL argument");
+  out->xn = L->xn;
+  out->qkv = L->qkv;
+  out->q = L->q;
+  out->o = L->o;
+  out->h = L->h;
+  out->hn = L->hn;
+  out->a = L->a;
+  return TDL_OK;
+}
+
+// ============================================================= KV cache
+
+namespace {
+bool kv_config_ok(const tdl_kv_config* c) {
+  return c && c->n_blocks > 0 && c->block_size == 16 && c->n_kv_heads > 0 &&
+         (c->head_dim == 64 || c->head_dim == 128) &&
+         (c->kv_dtype == TDL_BF16 || c->kv_dtype == TDL_U8_ASYM);
+}
+size_t pool_bytes(const tdl_kv_config* c) {
+  const size_t esz = c->kv_dtype == TDL_U8_ASYM ? 1 : 2;
+  return align256((size_t)c->n_blocks * c->n_kv_heads * 16 * c->head_dim * esz);
+}
+size_t param_bytes(const tdl_kv_config* c) {
+  return c->kv_dtype == TDL_U8_ASYM ? 4 * align256((size_t)c->n_kv_heads * c->head_dim * 4) : 0;
+}
+}  // namespace
+
+extern "C" size_t kv_cache_bytes(const tdl_kv_config* cfg) {
+  if (!kv_config_ok(cfg)) return 0;
+  return 2 * pool_bytes(cfg) + param_bytes(cfg);
+}
+
+extern "C" tdl_status kv_cache_alloc(const tdl_kv_config* cfg, void* dev_mem, tdl_kv_cache** out) {
+  if (!out) return fail(TDL_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!cfg) return fail(TDL_E_INVALID, "config is NULL");
+  if (cfg->block_size != 16) return fail(TDL_E_UNSUPPORTED, "block_size must be 16");
+  if (!kv_config_ok(cfg)) return fail(TDL_E_INVALID, "invalid KV cache configuration");
+  if (dev_mem && ((uintptr_t)dev_mem & 255))
+    return fail(TDL_E_INVALID, "dev_mem must be 256-byte aligned");
+  const size_t bytes = kv_cache_bytes(cfg);
+  tdl_kv_cache* kv = new tdl_kv_cache();
+  kv->cfg = *cfg;
+  if (dev_mem) {
+    kv->mem = dev_mem;
+  } else {
+    if (hipMalloc(&kv->mem, bytes) != hipSuccess) {
+      delete kv;
+      return fail(TDL_E_NOMEM, "hipMalloc of %zu bytes failed", bytes);
+    }
+    kv->owned = true;
+    hipError_t e = hipMemset(kv->mem, 0, bytes);
+    if (e != hipSuccess) {
+      (void)hipFree(kv->mem);
+      delete kv;
+      return fail(TDL_E_HIP, "hipMemset failed: %s", hipGetErrorString(e));
+    }
+  }
+  char* base = (char*)kv->mem;
+  kv->k = base;
+  kv->v = base + pool_bytes(cfg);
+  if (cfg->kv_dtype == TDL_U8_ASYM) {
+    char* pb = base + 2 * pool_bytes(cfg);
+    const size_t ps = align256((size_t)cfg->n_kv_heads * cfg->head_dim * 4);
+    kv->k_scale = (float*)pb;
+    kv->k_zp = (int32_t*)(pb + ps);
+    kv->v_scale = (float*)(pb + 2 * ps);
+    kv->v_zp = (int32_t*)(pb + 3 * ps);
+  }
+  // free list: LIFO; blocks come out as 0, 1, 2, ... or in a seeded order
+  std::vector<int32_t> order(cfg->n_blocks);
+  for (int i = 0; i < cfg->n_blocks; ++i) order[i] = i;
+  if (cfg->free_list_seed) {
+    uint64_t s = cfg->free_list_seed;
+    for (int i = cfg->n_blocks - 1; i > 0; --i) {
+      const int j = (int)(splitmix64(s) % (uint64_t)(i + 1));
+      std::swap(order[i], order[j]);
+    }
+  }
+  kv->free_list.assign(order.rbegin(), order.rend());
+  kv->is_free.assign(cfg->n_blocks, 1);
+  *out = kv;
+  return TDL_OK;
+}
+
+extern "C" tdl_status kv_cache_free(tdl_kv_cache* kv) {
+  if (!kv) return TDL_OK;
+  if (kv->owned) (void)hipFree(kv->mem);
+  delete kv;
+  return TDL_OK;
+}
+
+extern "C" tdl_status kv_cache_view(const tdl_kv_cache* kv, tdl_kv_view* out) {
+  if (!kv || !out) return fail(TDL_E_INVALID, "NULL argument");
+  const int64_t D = kv->cfg.head_dim, Hkv = kv->cfg.n_kv_heads;
+  out->k_pool = kv->k;
+  out->v_pool = kv->v;
+  out->k_strides[0] = Hkv * 16 * D;
+  out->k_strides[1] = 16 * D;
+  out->k_strides[2] = D;
+  out->k_strides[3] = 1;
+  out->v_strides[0] = Hkv * 16 * D;
+  out->v_strides[1] = 16 * D;
+  out->v_strides[2] = 1;
+  out->v_strides[3] = 16;
+  out->elem_bytes = kv->cfg.kv_dtype == TDL_U8_ASYM ? 1 : 2;
+  out->k_scale = kv->k_scale;
+  out->k_zero_point = kv->k_zp;
+  out->v_scale = kv->v_scale;
+  out->v_zero_point = kv->v_zp;
+  return TDL_OK;
+}
+
+extern "C" tdl_status kv_block_table(tdl_kv_cache* kv, int32_t n_seqs, const int32_t* n_tokens,
+                                     int32_t max_blocks, int32_t* table) {
+  if (!kv || !n_tokens || !table) return fail(TDL_E_INVALID, "NULL argument");
+  if (n_seqs < 0 || max_blocks < 1) return fail(TDL_E_INVALID, "n_seqs < 0 or max_blocks < 1");
+  size_t need = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    if (n_tokens[i] < 0) return fail(TDL_E_INVALID, "n_tokens[%d] < 0", i);
+    const int nb = (n_tokens[i] + 15) / 16;
+    if (nb > max_blocks)
+      return fail(TDL_E_INVALID, "sequence %d needs %d blocks > max_blocks %d", i, nb, max_blocks);
+    for (int b = 0; b < nb; ++b) {
+      const int32_t e = table[(size_t)i * max_blocks + b];
+      if (e < 0) ++need;
+      else if (e >= kv->cfg.n_blocks || kv->is_free[e])
+        return fail(TDL_E_INVALID, "sequence %d entry %d holds block %d that is not allocated", i,
+                    b, e);
+    }
+  }
+  if (need > kv->free_list.size())
+    return fail(TDL_E_CAPACITY, "need %zu free blocks, %zu left", need, kv->free_list.size());
+  for (int i = 0; i < n_seqs; ++i) {
+    const int nb = (n_tokens[i] + 15) / 16;
+    for (int b = 0; b < nb; ++b) {
+      int32_t& e = table[(size_t)i * max_blocks + b];
+      if (e >= 0) continue;
+      e = kv->free_list.back();
+      kv->free_list.pop_back();
+      kv->is_free[e] = 0;
+    }
+  }
+  return TDL_OK;
+}
+
+extern "C" tdl_status kv_block_release(tdl_kv_cache* kv, const int32_t* blocks, int32_t n) {
+  if (!kv || (!blocks && n > 0)) return fail(TDL_E_INVALID, "NULL argument");
+  if (n < 0) return fail(TDL_E_INVALID, "n < 0");
+  std::vector<uint8_t> seen(kv->cfg.n_blocks, 0);
+  for (int i = 0; i < n; ++i) {
+    const int32_t b = blocks[i];
+    if (b < 0 || b >= kv->cfg.n_blocks) return fail(TDL_E_INVALID, "block %d out of range", b);
+    if (kv->is_free[b] || seen[b]) return fail(TDL_E_INVALID, "block %d is already free", b);
+    seen[b] = 1;
+  }
+  for (int i = 0; i < n; ++i) {
+    kv->is_free[blocks[i]] = 1;
+    kv->free_list.push_back(blocks[i]);
+  }
+  return TDL_OK;
+}
+
+extern "C" int32_t kv_free_blocks(const tdl_kv_cache* kv) {
+  return kv ? (int32_t)kv->free_list.size() : 0;
+}
+
+extern "C" tdl_status kv_cache_calibrate(tdl_kv_cache* kv, tdl_stream stream, const float* k,
+                                         const float* v, int64_t n_tokens) {
+  if (!kv || !k || !v) return fail(TDL_E_INVALID, "NULL argument");
+  if (kv->cfg.kv_dtype != TDL_U8_ASYM) return fail(TDL_E_INVALID, "cache is not TDL_U8_ASYM");
+  if (n_tokens < 1) return fail(TDL_E_INVALID, "n_tokens < 1");
+  hipStream_t st = (hipStream_t)stream;
+  const int C = kv->cfg.n_kv_heads * kv->cfg.head_dim;
+  HIP_TRY(tdl::kv_calibrate(k, n_tokens, C, kv->k_scale, kv->k_zp, st));
+  HIP_TRY(tdl::kv_calibrate(v, n_tokens, C, kv->v_scale, kv->v_zp, st));
+  return TDL_OK;
+}
+
+extern "C" tdl_status kv_cache_write(tdl_kv_cache* kv, tdl_stream stream, int32_t n_seqs,
+                                     const int32_t* cu_rows, const int32_t* start_pos,
+                                     const int32_t* block_tables, int32_t max_blocks,
+                                     int32_t src_dtype, const void* k, const void* v,
+                                     int32_t n_rows) {
+  if (!kv || !cu_rows || !start_pos || !block_tables || !k || !v)
+    return fail(TDL_E_INVALID, "NULL argument");
+  if (n_seqs < 1 || max_blocks < 1 || n_rows < 0)
+    return fail(TDL_E_INVALID, "n_seqs and max_blocks must be >= 1, n_rows >= 0");
+  if (src_dtype != TDL_F32 && src_dtype != TDL_BF16)
+    return fail(TDL_E_INVALID, "src_dtype must be TDL_F32 or TDL_BF16");
+  hipStream_t st = (hipStream_t)stream;
+  SeqInfo seq{};
+  seq.q_start = cu_rows;
+  seq.q_len = nullptr;
+  seq.ctx_len = start_pos;
+  seq.n_seqs = n_seqs;
+  seq.tables = block_tables;
+  seq.max_blocks = max_blocks;
+  KvPool pool = pool_of(nullptr, kv);
+  HIP_TRY(kv_write_rows(k, v, src_dtype == TDL_F32, n_rows, kv->cfg.n_kv_heads, kv->cfg.head_dim,
+                        seq, pool, st));
+  return TDL_OK;
+}
+
+// =============================================================== errors
+
+extern "C" const char* tdl_status_string(tdl_status s) {
+  switch (s) {
+    case TDL_OK: return "ok";
+    case TDL_E_INVALID: return "invalid argument";
+    case TDL_E_UNSUPPORTED: return "unsupported";
+    case TDL_E_CAPACITY: return "capacity exceeded";
+    case TDL_E_NOMEM: return "out of device memory";
+    case TDL_E_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* tdl_last_error(void) { return g_last_error.c_str(); }

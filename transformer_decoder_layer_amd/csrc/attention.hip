@@ -1,0 +1,592 @@
+// Causal grouped-query attention over the block-paged KV cache.
+//
+// KV pool layout (elements): K [block][kv_head][slot 0..15][d] -- one head's
+// block is one contiguous tile (the per-block base address of the paged
+// kernel on the devpress engine page, section 4.3); V [block][kv_head][d]
+// [slot], so that the 16 tokens of a channel are contiguous and feed the
+// key-dimension of the P*V matrix product directly.
+//
+// Both kernels compute S^T = K * Q^T on the MFMA units (keys as rows), so
+// the softmax of one query row lives in one lane (plus its partner lanes),
+// and O^T = V^T * P^T, whose B operand is exactly the register layout the
+// first product leaves P in -- P never goes through LDS.  Scores are scaled
+// by log2(e)/sqrt(D) so exp2 gives e^(s - m); softmax is the online form
+// (running max m, denominator l, rescaled accumulator) of the TFFInfer page,
+// section 3.7.2 item 5, with the per-tile update written in full.
+//
+// Prefill: a workgroup owns one KV head and 32 query positions of one
+// sequence, with one wave per query head of the group: each 64-key K/V tile
+// is read from HBM once into LDS and used by every head that shares it (no
+// repeat_kv copy, cf. the Qwen2.5-7B page, section 3).
+//
+// Decode: a workgroup owns (sequence, KV head, context partition); its four
+// waves walk the partition's blocks through the block table, one 16-token
+// block per step, with the whole query-head group packed into the 16 columns
+// of one MFMA tile.  u8 caches are dequantised in registers: codes convert
+// exactly to bf16; the K scale is folded into q and the zero point into a
+// per-head constant, the V scale and zero point are applied once at the end.
+// The last workgroup of a (sequence, KV head) to finish merges the
+// partitions' (m, l, acc) triples in partition order.
+
+#include "common.h"
+#include "kernels.h"
+
+#include <algorithm>
+
+namespace tdl {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// bf16 / fp32 -> fp16, saturating at the fp16 range.  A bf16 value inside the
+// range converts exactly (8 significant bits fit in 11).
+__device__ __forceinline__ f16 to_f16(float v) { return f32_to_f16_sat(v); }
+__device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t w) {
+  const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+  const f16 a = to_f16(lo), b = to_f16(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ int seq_row(const SeqInfo& s, int sidx) {
+  if (s.rows_are_seqs) return sidx;
+  return s.q_start ? s.q_start[sidx] : 0;
+}
+__device__ __forceinline__ int seq_qlen(const SeqInfo& s, int sidx) {
+  if (s.rows_are_seqs) return 1;
+  return s.q_start ? s.q_len[sidx] : s.q_len0;
+}
+__device__ __forceinline__ int seq_ctx(const SeqInfo& s, int sidx) {
+  if (s.rows_are_seqs || s.q_start) return s.ctx_len[sidx];
+  return s.ctx0;
+}
+__device__ __forceinline__ int seq_block(const SeqInfo& s, int sidx, int lblk) {
+  if (!s.tables) return lblk;
+  return s.tables[(size_t)sidx * s.max_blocks + lblk];
+}
+
+// ================================================================ prefill
+constexpr int PQ = 32;   // query positions per workgroup
+constexpr int PK = 64;   // keys per tile
+
+// K and V tiles are held in LDS as fp16 (converted exactly from the bf16
+// cache): with fp16 query and probability operands the MFMA inputs carry 11
+// significant bits instead of bf16's 8, at the same MFMA rate.
+template <int D>
+struct PrefillSmem {
+  f16 k[2][PK * D];      // [key][d], 16-byte chunks XOR-swizzled by key
+  f16 vt[2][D * PK];     // [d][key], 8-byte units XOR-swizzled by d
+};
+
+template <int D>
+__device__ __forceinline__ int k_off(int key, int chunk) {  // chunk of 8 bf16
+  return key * D + ((chunk ^ (key & (D / 8 - 1))) << 3);
+}
+__device__ __forceinline__ int vt_off(int d, int unit) {  // unit of 4 bf16
+  return d * PK + ((unit ^ (d & 15)) << 2);
+}
+
+template <int D, int NREP>
+__global__ __launch_bounds__(NREP * 64) void attn_prefill_kernel(const float* __restrict__ q,
+                                                                 KvPool pool, SeqInfo seq, int Hq,
+                                                                 int Hkv, int n_qtiles,
+                                                                 f16* __restrict__ o) {
+  __shared__ __attribute__((aligned(16))) PrefillSmem<D> sm;
+  constexpr int n_rep = NREP;
+  constexpr int nthreads = NREP * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qt = n_qtiles - 1 - blockIdx.x;  // longest tiles first
+  const int g = blockIdx.y;
+  const int sidx = blockIdx.z;
+  const int q_len = seq_qlen(seq, sidx);
+  if (qt * PQ >= q_len) return;
+  const int ctx = seq_ctx(seq, sidx);
+  const int row0 = seq_row(seq, sidx) + qt * PQ;
+  const int n_keys = ctx + q_len;                                   // keys in the cache
+  const int last_q = ctx + min(qt * PQ + PQ, q_len) - 1;            // last query position
+  const int n_tiles = cdiv(last_q + 1, PK);
+  const int first_q = ctx + qt * PQ;
+  const int h = g * n_rep + wave;
+  const int ql = lane & 31, G = lane >> 5;
+
+  // Q fragments: B operand of S^T = K Q^T; lane supplies q[ql][16s + 8G .. +7]
+  f16x8 qf[D / 16];
+  {
+    const bool valid = qt * PQ + ql < q_len;
+    const float* qp = q + ((size_t)(row0 + ql) * Hq + h) * D + 8 * G;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      f16x8 v{};
+      if (valid) {
+        const float4 a = *(const float4*)(qp + 16 * s), b = *(const float4*)(qp + 16 * s + 4);
+        v[0] = to_f16(a.x); v[1] = to_f16(a.y); v[2] = to_f16(a.z); v[3] = to_f16(a.w);
+        v[4] = to_f16(b.x); v[5] = to_f16(b.y); v[6] = to_f16(b.z); v[7] = to_f16(b.w);
+      }
+      qf[s] = v;
+    }
+  }
+
+  // tile loader: K blocks (4 KB each for D=128) and V blocks into LDS
+  constexpr int K_CHUNKS = PK * D / 8;   // 16-byte chunks of K per tile
+  constexpr int V_CHUNKS = D * PK / 8;
+  constexpr int MAX_PER_T = (K_CHUNKS + V_CHUNKS + nthreads - 1) / nthreads;
+  uint4 rk[MAX_PER_T];
+  const bf16* kpool = (const bf16*)pool.k;
+  const bf16* vpool = (const bf16*)pool.v;
+  const size_t head_elems = (size_t)kBlockTokens * D;
+
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < MAX_PER_T; ++i) {
+      const int c = tid + i * nthreads;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (c < K_CHUNKS + V_CHUNKS) {
+        const bool isk = c < K_CHUNKS;
+        const int cc = isk ? c : c - K_CHUNKS;
+        // both pools: 16-token block = kBlockTokens*D elements; chunk cc covers
+        // elements [8cc, 8cc+8) of the tile's 4 consecutive logical blocks
+        const int lb = cc / (int)(head_elems / 8);
+        const int within = cc % (int)(head_elems / 8);
+        const int lblk = t * (PK / kBlockTokens) + lb;
+        if (lblk * kBlockTokens < n_keys) {
+          const int phys = seq_block(seq, sidx, lblk);
+          const bf16* src = (isk ? kpool : vpool) + ((size_t)phys * Hkv + g) * head_elems + within * 8;
+          val = *(const uint4*)src;
+          // zero keys past the end of the sequence (unwritten slots)
+          const int base_key = lblk * kBlockTokens;
+          if (base_key + kBlockTokens > n_keys) {
+            uint32_t w[4] = {val.x, val.y, val.z, val.w};
+            if (isk) {
+              const int key = base_key + (within * 8) / D;
+              if (key >= n_keys) w[0] = w[1] = w[2] = w[3] = 0;
+            } else {
+              const int key0 = base_key + (within * 8) % kBlockTokens;  // 8 keys of one d
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (key0 + e >= n_keys) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            }
+            val = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      }
+      rk[i] = val;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < MAX_PER_T; ++i) {
+      const int c = tid + i * nthreads;
+      if (c < K_CHUNKS) {
+        const int lb = c / (int)(head_elems / 8);
+        const int within = c % (int)(head_elems / 8);
+        const int key = lb * kBlockTokens + (within * 8) / D;
+        const int chunk = ((within * 8) % D) / 8;
+        const uint4 w = rk[i];
+        *(uint4*)(&sm.k[buf][k_off<D>(key, chunk)]) =
+            make_uint4(bf16pair_to_f16pair(w.x), bf16pair_to_f16pair(w.y),
+                       bf16pair_to_f16pair(w.z), bf16pair_to_f16pair(w.w));
+      } else if (c < K_CHUNKS + V_CHUNKS) {
+        const int cc = c - K_CHUNKS;
+        const int lb = cc / (int)(head_elems / 8);
+        const int within = cc % (int)(head_elems / 8);
+        const int d = (within * 8) / kBlockTokens;
+        const int key0 = lb * kBlockTokens + (within * 8) % kBlockTokens;
+        const int unit = key0 / 4;  // even
+        *(u32x2*)(&sm.vt[buf][vt_off(d, unit)]) =
+            u32x2{bf16pair_to_f16pair(rk[i].x), bf16pair_to_f16pair(rk[i].y)};
+        *(u32x2*)(&sm.vt[buf][vt_off(d, unit + 1)]) =
+            u32x2{bf16pair_to_f16pair(rk[i].z), bf16pair_to_f16pair(rk[i].w)};
+      }
+    }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = kLog2e * rsqrtf((float)D);
+  const int my_q = first_q + ql;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int cur = t & 1;
+    const bool more = t + 1 < n_tiles;
+    if (more) load_tile(t + 1);
+
+    // S^T for 64 keys x 32 queries: two 32-key halves
+    f32x16 st[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      st[kh] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const f16x8 kf = *(const f16x8*)(&sm.k[cur][k_off<D>(kh * 32 + ql, 2 * s + G)]);
+        st[kh] = mfma32x32x16(kf, qf[s], st[kh]);
+      }
+    }
+    // lane holds keys kh*32 + 8(r/4) + 4G + r%4 of query ql
+    const int key_base = t * PK;
+    const bool need_mask = key_base + PK - 1 > first_q || key_base + PK > n_keys;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = st[kh][r] * sc;
+        if (need_mask) {
+          const int key = key_base + kh * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
+          if (key > my_q || key >= n_keys) v = -INFINITY;
+        }
+        st[kh][r] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    f16x8 pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const f16 pv = (f16)exp2f(st[kh][r] - m_new);
+        psum += (float)pv;
+        pb[kh * 2 + (r >> 3)][r & 7] = pv;
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int t2 = 0; t2 < D / 32; ++t2) acc[t2] *= alpha;
+    // O^T += V^T P^T, 16 keys per MFMA: chunk kc covers keys kc*16 .. +15;
+    // lane supplies keys kc*16 + 4G + 0..3 and kc*16 + 8 + 4G + 0..3
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int t2 = 0; t2 < D / 32; ++t2) {
+        const int d = 32 * t2 + ql;
+        const u32x2 lo = *(const u32x2*)(&sm.vt[cur][vt_off(d, kc * 4 + G)]);
+        const u32x2 hi = *(const u32x2*)(&sm.vt[cur][vt_off(d, kc * 4 + 2 + G)]);
+        const uint4 w = make_uint4(lo[0], lo[1], hi[0], hi[1]);
+        acc[t2] = mfma32x32x16(__builtin_bit_cast(f16x8, w), pb[kc], acc[t2]);
+      }
+    }
+    if (more) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (qt * PQ + ql < q_len) {
+    const float inv = 1.f / l_run;
+    f16* op = o + (size_t)(row0 + ql) * Hq * D + (size_t)h * D;
+#pragma unroll
+    for (int t2 = 0; t2 < D / 32; ++t2)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = to_f16(acc[t2][4 * a + e] * inv);
+        *(f16x4*)(op + 32 * t2 + 8 * a + 4 * G) = v4;
+      }
+  }
+}
+
+// ================================================================= decode
+struct DecArgs {
+  const float* q;
+  KvPool pool;
+  SeqInfo seq;
+  int first_seq;
+  int Hq, Hkv;
+  int part_blocks, max_parts;
+  float* part;
+  int* counters;
+  f16* o;
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 load_k_frag(const void* base, bool u8, int off) {
+  if (!u8) return *(const bf16x8*)((const bf16*)base + off);
+  const uint2 w = *(const uint2*)((const uint8_t*)base + off);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (bf16)(float)((w.x >> (8 * e)) & 0xff);
+    r[4 + e] = (bf16)(float)((w.y >> (8 * e)) & 0xff);
+  }
+  return r;
+}
+
+template <int D, bool U8>
+__global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
+  constexpr int NT = D / 16;  // 16-channel tiles of the output
+  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ float sm_o[4][D][16];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int sidx = a.first_seq + b;
+  const int n_rep = a.Hq / a.Hkv;
+  const int ctx = seq_ctx(a.seq, sidx);
+  const int n_keys = ctx + 1;
+  const int n_blk = cdiv(n_keys, kBlockTokens);
+  const int n_parts = cdiv(n_blk, a.part_blocks);
+  if (p >= n_parts) return;
+  const int row = seq_row(a.seq, sidx);
+  const int blk0 = p * a.part_blocks;
+  const int blk1 = min(n_blk, blk0 + a.part_blocks);
+  const int col = lane & 15, grp = lane >> 4;
+  const bool head_ok = col < n_rep;
+
+  // query fragments (B operand of S^T = K Q^T): q[head col][32s + 8grp .. +7],
+  // carried as a bf16 pair hi + lo so the fp32 query keeps its precision
+  // (MFMA time is free here: the kernel is bound by HBM).  u8: q' = q *
+  // k_scale folds the K scale in; the zero point enters through
+  // corr = sum_d q'[d] * zp[d] in fp32.
+  bf16x8 qf[D / 32];
+  bf16x8 qlo[D / 32];
+  float corr = 0.f;
+  {
+    const float* qp = a.q + ((size_t)row * a.Hq + g * n_rep + col) * D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (head_ok) {
+        const float4 x0 = *(const float4*)(qp + 32 * s), x1 = *(const float4*)(qp + 32 * s + 4);
+        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+      }
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float qs = v[e];
+        if constexpr (U8) {
+          const int ch = g * D + 32 * s + 8 * grp + e;
+          qs *= a.pool.k_scale[ch];
+          corr += qs * (float)a.pool.k_zp[ch];
+        }
+        hi[e] = f32_to_bf16(qs);
+        lo[e] = f32_to_bf16(qs - (float)hi[e]);
+      }
+      qf[s] = hi;
+      qlo[s] = lo;
+    }
+    if constexpr (U8) {
+      corr += __shfl_xor(corr, 16, 64);
+      corr += __shfl_xor(corr, 32, 64);
+    }
+  }
+
+  const float sc = kLog2e * rsqrtf((float)D);
+  const int esz = U8 ? 1 : 2;
+  const size_t head_elems = (size_t)kBlockTokens * D;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int blk = blk0 + wave; blk < blk1; blk += 4) {
+    const int phys = seq_block(a.seq, sidx, blk);
+    const size_t hb = ((size_t)phys * a.Hkv + g) * head_elems;
+    const char* kb = (const char*)a.pool.k + hb * esz;
+    const char* vb = (const char*)a.pool.v + hb * esz;
+    // S^T[key][head]: A = K rows (key = lane%16), B = Q^T
+    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      const bf16x8 kf = load_k_frag<D>(kb, U8, col * D + 32 * s + 8 * grp);
+      st = mfma16x16x32(kf, qf[s], st);
+      st = mfma16x16x32(kf, qlo[s], st);
+    }
+    // V^T fragments: channel d = 16t + col, keys 4grp .. 4grp+3
+    bf16x4 vf[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int off = (16 * t + col) * kBlockTokens + 4 * grp;
+      if constexpr (U8) {
+        const uint32_t w = *(const uint32_t*)(vb + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vf[t][e] = (bf16)(float)((w >> (8 * e)) & 0xff);
+      } else {
+        vf[t] = *(const bf16x4*)((const bf16*)vb + off);
+      }
+    }
+    // lane holds S[head col][key 4grp + r]
+    const int key0 = blk * kBlockTokens + 4 * grp;
+    float sv[4];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = (st[r] - corr) * sc;
+      if (key0 + r >= n_keys) v = -INFINITY;
+      sv[r] = v;
+      mb = fmaxf(mb, v);
+    }
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float m_new = fmaxf(m_run, mb);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    // P as a bf16 pair hi + lo: the weights keep fp32 precision
+    bf16x4 pf, pl;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pv = exp2f(sv[r] - m_new);
+      pf[r] = f32_to_bf16(pv);
+      pl[r] = f32_to_bf16(pv - (float)pf[r]);
+      psum += pv;
+    }
+    l_run = l_run * alpha + psum;
+    if (key0 + 3 >= n_keys) {  // unwritten slots of the last block: zero V
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (key0 + r >= n_keys) vf[t][r] = (bf16)0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      acc[t] = mfma16x16x16(vf[t], pf, acc[t] * alpha);
+      acc[t] = mfma16x16x16(vf[t], pl, acc[t]);
+    }
+  }
+
+  // ---- merge the four waves: acc[t][r] = O^T[16t + 4grp + r][head col]
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (lane < 16) {
+    sm_m[wave][lane] = m_run;
+    sm_l[wave][lane] = l_run;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm_o[wave][16 * t + 4 * grp + r][col] = acc[t][r];
+  __syncthreads();
+
+  // each thread: (head hh, channels) -- 16 heads x D channels
+  const size_t pbase_stride = (size_t)16 * D + 32;
+  float* part_bg = a.part + ((size_t)b * a.Hkv + g) * a.max_parts * pbase_stride;
+  for (int e = tid; e < 16 * D; e += 256) {
+    const int hh = e / D, d = e % D;
+    if (hh >= n_rep) continue;
+    float M = sm_m[0][hh];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][hh]);
+    float O = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = exp2f(sm_m[w][hh] - M);  // 0 for a wave with no blocks
+      O += sm_o[w][d][hh] * f;
+      L += sm_l[w][hh] * f;
+    }
+    if constexpr (U8) {
+      const int ch = g * D + d;
+      O = a.pool.v_scale[ch] * (O - (float)a.pool.v_zp[ch] * L);
+    }
+    if (n_parts == 1) {
+      a.o[(size_t)row * a.Hq * D + (size_t)(g * n_rep + hh) * D + d] = to_f16(O / L);
+    } else {
+      float* pp = part_bg + (size_t)p * pbase_stride;
+      pp[hh * D + d] = O;
+      if (d == 0) {
+        pp[16 * D + 2 * hh] = M;
+        pp[16 * D + 2 * hh + 1] = L;
+      }
+    }
+  }
+  if (n_parts == 1) return;
+
+  // ---- last partition to arrive merges all partitions in order
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int cidx = b * a.Hkv + g;
+    const int prev = atomicAdd(&a.counters[cidx], 1);
+    s_last = prev == n_parts - 1;
+    if (s_last) a.counters[cidx] = 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int e = tid; e < 16 * D; e += 256) {
+    const int hh = e / D, d = e % D;
+    if (hh >= n_rep) continue;
+    float M = -INFINITY;
+    for (int pp = 0; pp < n_parts; ++pp) M = fmaxf(M, part_bg[pp * pbase_stride + 16 * D + 2 * hh]);
+    float O = 0.f, L = 0.f;
+    for (int pp = 0; pp < n_parts; ++pp) {
+      const float* q2 = part_bg + pp * pbase_stride;
+      const float f = exp2f(q2[16 * D + 2 * hh] - M);
+      O += q2[hh * D + d] * f;
+      L += q2[16 * D + 2 * hh + 1] * f;
+    }
+    a.o[(size_t)row * a.Hq * D + (size_t)(g * n_rep + hh) * D + d] = to_f16(O / L);
+  }
+}
+
+}  // namespace
+
+hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, int n_prefill, int max_q_len,
+                        int Hq, int Hkv, int D, void* o, hipStream_t s) {
+  if (n_prefill == 0 || max_q_len == 0) return hipSuccess;
+  const int n_qtiles = cdiv(max_q_len, PQ);
+  dim3 grid(n_qtiles, Hkv, n_prefill);
+  const int n_rep = Hq / Hkv;
+#define TDL_PREFILL_CASE(DD, NR)                                                               \
+  if (D == DD && n_rep == NR) {                                                                \
+    attn_prefill_kernel<DD, NR><<<grid, NR * 64, 0, s>>>((const float*)q, pool, seq, Hq, Hkv,  \
+                                                        n_qtiles, (f16*)o);                   \
+    return hipGetLastError();                                                                  \
+  }
+  TDL_PREFILL_CASE(128, 1) TDL_PREFILL_CASE(128, 2) TDL_PREFILL_CASE(128, 4)
+  TDL_PREFILL_CASE(128, 7) TDL_PREFILL_CASE(128, 8)
+  TDL_PREFILL_CASE(64, 1) TDL_PREFILL_CASE(64, 2) TDL_PREFILL_CASE(64, 4)
+  TDL_PREFILL_CASE(64, 7) TDL_PREFILL_CASE(64, 8)
+#undef TDL_PREFILL_CASE
+  return hipErrorInvalidValue;
+}
+
+DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len) {
+  (void)Hq;
+  DecodePlan pl{};
+  const int max_blk = cdiv(max_ctx_len, kBlockTokens);
+  // aim for ~2048 workgroups over the longest context
+  const int want_parts = std::max(1, cdiv(2048, std::max(1, batch * Hkv)));
+  int pb = cdiv(max_blk, want_parts);
+  pb = std::max(8, cdiv(pb, 4) * 4);
+  pl.part_blocks = pb;
+  pl.max_parts = cdiv(max_blk, pb);
+  pl.part_floats = (size_t)batch * Hkv * pl.max_parts * (16 * D + 32);
+  pl.n_counters = batch * Hkv;
+  return pl;
+}
+
+hipError_t attn_decode(const DecodePlan& pl, const void* q, KvPool pool, SeqInfo seq, int first_seq,
+                       int row0, int batch, int Hq, int Hkv, int D, void* o, float* part,
+                       int* counters, hipStream_t s) {
+  (void)row0;
+  if (batch == 0) return hipSuccess;
+  DecArgs a{(const float*)q, pool, seq, first_seq, Hq, Hkv, pl.part_blocks, pl.max_parts, part,
+            counters, (f16*)o};
+  dim3 grid(pl.max_parts, Hkv, batch);
+  if (D == 128) {
+    if (pool.u8) attn_decode_kernel<128, true><<<grid, 256, 0, s>>>(a);
+    else attn_decode_kernel<128, false><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (pool.u8) attn_decode_kernel<64, true><<<grid, 256, 0, s>>>(a);
+    else attn_decode_kernel<64, false><<<grid, 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tdl

@@ -1,0 +1,81 @@
+// Shared device-side types and helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tdl {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+typedef _Float16 f16;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+
+constexpr int kWave = 64;
+constexpr float kF16Max = 65504.f;
+
+// fp32 -> fp16, round to nearest even, saturating at +-65504.
+__device__ __forceinline__ f16 f32_to_f16_sat(float v) {
+  return (f16)fminf(fmaxf(v, -kF16Max), kF16Max);
+}
+
+// Element type of an MFMA operand: bf16 or fp16 (same rate on gfx950; fp16
+// keeps 11 significant bits, bf16 8).
+template <typename T> struct Mfma;
+template <> struct Mfma<bf16> {
+  typedef bf16x8 v8;
+  __device__ static f32x4 mma(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static bf16 from_f32(float v) { return (bf16)v; }
+};
+template <> struct Mfma<f16> {
+  typedef f16x8 v8;
+  __device__ static f32x4 mma(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static f16 from_f32(float v) { return f32_to_f16_sat(v); }
+};
+constexpr int kBlockTokens = 16;
+
+__device__ __forceinline__ float bf16_to_f32(bf16 v) { return (float)v; }
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ bf16 f32_to_bf16(float v) { return (bf16)v; }
+
+__device__ __forceinline__ uint16_t bf16_bits(bf16 v) { return __builtin_bit_cast(uint16_t, v); }
+__device__ __forceinline__ bf16 bits_bf16(uint16_t v) { return __builtin_bit_cast(bf16, v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// 16x16x32 bf16 MFMA: D = A(16x32) * B(32x16) + C.  Lane l supplies 8 values
+// of row l%16 of A and of column l%16 of B; both use the same k order, so any
+// pairing that loads A and B alike contracts correctly.  D: lane l holds
+// rows 4*(l/16)+0..3 of column l%16.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x16 bf16 MFMA: lane l supplies A[l%16][4*(l/16)+0..3] and
+// B[4*(l/16)+0..3][l%16]; D as above.
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace tdl

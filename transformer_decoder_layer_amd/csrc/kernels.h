@@ -1,0 +1,136 @@
+// Launch interface of the gfx950 kernels (internal to libtdl).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace tdl {
+
+// ----------------------------------------------------------------- GEMM
+// C = epilogue(A[M,K] * B[N,K]^T), row-major, B either of A's element type or
+// Q8_0 (int8 codes [N,K] + fp16 scales [N,K/32]).  The epilogue fixes the
+// operand type: fp16 for the first three, bf16 for EPI_RESID_BF16.
+enum GemmEpilogue {
+  EPI_BIAS_F32 = 0,    // fp16 operands; C f32  = acc + bias[n] (bias may be null)
+  EPI_RESID_F32 = 1,   // fp16 operands; C f32  = acc + resid_bf16[m, n]
+  EPI_RESID_BF16 = 2,  // bf16 operands; C bf16 = acc + resid_f32[m, n]
+  EPI_SILU_GATE = 3    // fp16 operands; C bf16 [M, N/2] = silu(gate) * up,
+                       // gate/up in alternating 16-column groups of B
+};
+
+struct GemmArgs {
+  const void* A;
+  int lda;
+  const void* B;
+  int ldb;
+  const __half* B_scale;  // Q8_0 only, [N, K/32]
+  int M, N, K;
+  const float* bias;
+  const void* resid;
+  int ldr;
+  void* C;
+  int ldc;
+  float* ws;         // split-K partial tiles
+  int* counters;     // split-K arrival counters (zero between calls)
+  int splits;
+  int k_tiles_per_split;
+};
+
+// Picks a tile configuration and split count for (M, N, K) and returns the
+// workspace floats / counters it needs (for sizing at create time).
+struct GemmPlan {
+  int cfg;          // tile configuration id
+  int splits;
+  int k_tiles_per_split;
+  int grid;
+  size_t ws_floats;
+  int n_counters;
+};
+GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi);
+hipError_t gemm_launch(const GemmPlan& plan, GemmArgs a, bool q80, int epi, hipStream_t s);
+
+// -------------------------------------------------------- element-wise
+// y[r] = fp16(x[r] * rsqrt(mean(x[r]^2) + eps) * g), x bf16 or f32.
+hipError_t rmsnorm_bf16in(const void* x, const float* g, void* y, int rows, int H, float eps,
+                          hipStream_t s);
+hipError_t rmsnorm_f32in(const float* x, const float* g, void* y, int rows, int H, float eps,
+                         hipStream_t s);
+
+// Per-call sequence description shared by the row-wise and attention
+// kernels.  Arrays are device int32.  Three forms: rows_are_seqs (decode:
+// row r = sequence r, q_len 1, ctx_len[r]); q_start null (one sequence,
+// q_len0 rows from position ctx0); otherwise the general q_start / q_len /
+// ctx_len arrays.
+struct SeqInfo {
+  const int* q_start;
+  const int* q_len;
+  const int* ctx_len;
+  int n_seqs;
+  int q_len0;
+  int ctx0;
+  const int* tables;  // [n_seqs, max_blocks]; null = identity (block = pos/16)
+  int max_blocks;
+  int rows_are_seqs;  // 1: row r is sequence r with one new token at ctx_len[r]
+};
+
+struct KvPool {
+  void* k;          // [blocks][Hkv][16][D]
+  void* v;          // [blocks][Hkv][D][16]
+  int u8;           // 0: bf16 elements, 1: uint8 codes
+  const float* k_scale;
+  const int* k_zp;
+  const float* v_scale;
+  const int* v_zp;
+};
+
+// Per row of qkv (float32 [rows][(Hq+2Hkv)*D]): optional per-head RMSNorm of
+// q and k, RoPE of q and k (half-split pairs, cos/sin table [max_pos][D/2]),
+// q -> q_out [rows][Hq][D] float32, k and v -> the pool slot of the row's
+// position (rounded once, from fp32).
+hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D,
+                         const float2* rope_tab, const float* q_norm, const float* k_norm,
+                         float eps, void* q_out, SeqInfo seq, KvPool pool, hipStream_t s);
+
+// Writes caller K/V rows into the pool (kv_cache_write).
+hipError_t kv_write_rows(const void* k, const void* v, int src_f32, int rows, int Hkv, int D,
+                         SeqInfo seq, KvPool pool, hipStream_t s);
+// Per-channel min/max -> scale / zero point (kv_cache_calibrate).
+hipError_t kv_calibrate(const float* x, int64_t n_tokens, int channels, float* scale, int* zp,
+                        hipStream_t s);
+
+// cos/sin table of RoPE angles pos * theta^(-2i/D), formed in float64.
+hipError_t rope_table_build(float2* tab, int max_pos, int D, double theta, hipStream_t s);
+
+// Weight conversion of n elements from f32 or bf16 to bf16 (dst_f16 = 0) or
+// to fp16 (dst_f16 = 1; values beyond +-65504 saturate and are counted in
+// *n_saturated, a device int).
+hipError_t convert_weights(const void* src, int src_f32, void* dst, int dst_f16, int64_t n,
+                           int* n_saturated, hipStream_t s);
+// gate/up interleave: dst row (32*(j/16) + j%16) = gate row j, (+16) = up row j.
+hipError_t interleave_gate_up(const void* gate, const void* up, int elem_bytes_row, int I,
+                              void* dst, hipStream_t s);
+hipError_t copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+
+// ------------------------------------------------------------- attention
+// Flash prefill attention over sequences 0..n_prefill-1 of `seq`; K/V read
+// from the (bf16) pool through the tables.  q [rows][Hq][D] f32; o
+// [rows][Hq*D] fp16 (saturating).
+hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, int n_prefill, int max_q_len,
+                        int Hq, int Hkv, int D, void* o, hipStream_t s);
+
+// Paged decode attention for decode sequences first_seq .. first_seq+batch-1
+// (one query row each, rows row0 + b).  part_* is the split-context
+// workspace; counters zero between calls.
+struct DecodePlan {
+  int part_blocks;
+  int max_parts;
+  size_t part_floats;
+  int n_counters;
+};
+DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len);
+hipError_t attn_decode(const DecodePlan& plan, const void* q, KvPool pool, SeqInfo seq,
+                       int first_seq, int row0, int batch, int Hq, int Hkv, int D, void* o,
+                       float* part, int* counters, hipStream_t s);
+
+}  // namespace tdl

@@ -1,0 +1,343 @@
+// Row-wise kernels: RMSNorm, Q/K-norm + RoPE + KV-slot write, KV-cache
+// writes and per-channel int8 calibration, weight conversion, RoPE table.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace tdl {
+
+namespace {
+
+// ------------------------------------------------------------- RMSNorm
+// One workgroup per row (the "one block per row" layout of the RMSNorm kernel
+// on the Qwen2.5-7B single-layer page, section 2): fp32 sum of squares over
+// 16-byte vector loads, reduced within each wave by lane shuffles and across
+// the four waves through LDS; y = x * rsqrt(sum/H + eps) * g.
+
+__device__ __forceinline__ void load8(const bf16* p, float* v) {
+  const bf16x8 t = *(const bf16x8*)p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (float)t[e];
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const TIn* __restrict__ x,
+                                                      const float* __restrict__ g,
+                                                      f16* __restrict__ y, int H, float eps) {
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const TIn* xr = x + (size_t)row * H;
+  f16* yr = y + (size_t)row * H;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    float v[8];
+    load8(xr + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float inv = rsqrtf(tot / (float)H + eps);
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    float v[8];
+    load8(xr + c, v);
+    const float4 g0 = *(const float4*)(g + c), g1 = *(const float4*)(g + c + 4);
+    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = f32_to_f16_sat(v[e] * inv * gg[e]);
+    *(f16x8*)(yr + c) = o;
+  }
+}
+
+// ---------------------------------------------------- sequence lookups
+__device__ __forceinline__ int find_seq(const SeqInfo& s, int row) {
+  if (s.rows_are_seqs) return row;
+  if (!s.q_start) return 0;
+  int lo = 0, hi = s.n_seqs - 1;
+  while (lo < hi) {  // last sequence whose q_start <= row
+    const int mid = (lo + hi + 1) >> 1;
+    if (s.q_start[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+__device__ __forceinline__ int row_position(const SeqInfo& s, int seq, int row) {
+  if (s.rows_are_seqs) return s.ctx_len[row];
+  if (!s.q_start) return s.ctx0 + row;
+  return s.ctx_len[seq] + row - s.q_start[seq];
+}
+// Physical block of token `pos` of sequence `seq` (the page table lookup,
+// get_location of the TFFInfer page section 3.6.4).
+__device__ __forceinline__ int block_of(const SeqInfo& s, int seq, int pos) {
+  if (!s.tables) return pos / kBlockTokens;
+  return s.tables[(size_t)seq * s.max_blocks + pos / kBlockTokens];
+}
+
+// Quantise one value: clamp(round_half_even(x / scale) + zp, 0, 255), with a
+// correctly rounded fp32 divide.
+__device__ __forceinline__ uint8_t quant_u8(float x, float scale, int zp) {
+  const float q = __builtin_rintf(__fdiv_rn(x, scale));
+  int c = (int)q + zp;
+  c = c < 0 ? 0 : (c > 255 ? 255 : c);
+  return (uint8_t)c;
+}
+
+__device__ __forceinline__ void store_kv(const KvPool& pool, int blk, int g, int Hkv, int D, int slot,
+                                         int d, float kval, float vval) {
+  const size_t head = ((size_t)blk * Hkv + g) * kBlockTokens * D;
+  const size_t kidx = head + (size_t)slot * D + d;   // K: [blk][g][slot][d]
+  const size_t vidx = head + (size_t)d * kBlockTokens + slot;  // V: [blk][g][d][slot]
+  if (pool.u8) {
+    const int ch = g * D + d;
+    ((uint8_t*)pool.k)[kidx] = quant_u8(kval, pool.k_scale[ch], pool.k_zp[ch]);
+    ((uint8_t*)pool.v)[vidx] = quant_u8(vval, pool.v_scale[ch], pool.v_zp[ch]);
+  } else {
+    ((bf16*)pool.k)[kidx] = f32_to_bf16(kval);
+    ((bf16*)pool.v)[vidx] = f32_to_bf16(vval);
+  }
+}
+
+// ------------------------------------------------ Q/K-norm + RoPE + KV
+// One workgroup (4 waves) per row; each wave takes one head at a time: the
+// Q heads, then the K heads (RoPE and, for K, the cache write together with
+// the matching V head).  Q and K heads share the launch, as the RoPE kernel
+// of the Qwen2.5-7B page (section 2) does with its unified head indexing.
+// Half-split pairs (i, i + D/2): lane i < D/2 owns pair i.
+__global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ qkv, int Hq, int Hkv,
+                                                      int D, const float2* __restrict__ tab,
+                                                      const float* __restrict__ qn,
+                                                      const float* __restrict__ kn, float eps,
+                                                      float* __restrict__ q_out, SeqInfo seq,
+                                                      KvPool pool) {
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = D >> 1;
+  const int sidx = find_seq(seq, row);
+  const int pos = row_position(seq, sidx, row);
+  const int ldq = (Hq + 2 * Hkv) * D;
+  const float* src = qkv + (size_t)row * ldq;
+  const bool act = lane < half;
+  float2 cs = make_float2(1.f, 0.f);
+  if (act) cs = tab[(size_t)pos * half + lane];
+  const int blk = block_of(seq, sidx, pos);
+  const int slot = pos % kBlockTokens;
+
+  for (int h = wave; h < Hq + Hkv; h += 4) {
+    const bool is_q = h < Hq;
+    const float* hp = src + (size_t)h * D;  // q heads then k heads are contiguous
+    float x1 = 0.f, x2 = 0.f;
+    if (act) {
+      x1 = hp[lane];
+      x2 = hp[lane + half];
+    }
+    const float* gn = is_q ? qn : kn;
+    if (gn) {  // per-head RMSNorm over D
+      const float ss = wave_sum(x1 * x1 + x2 * x2);
+      const float inv = rsqrtf(ss / (float)D + eps);
+      if (act) {
+        x1 = x1 * inv * gn[lane];
+        x2 = x2 * inv * gn[lane + half];
+      }
+    }
+    const float r1 = x1 * cs.x - x2 * cs.y;
+    const float r2 = x1 * cs.y + x2 * cs.x;
+    if (!act) continue;
+    if (is_q) {
+      float* qo = q_out + ((size_t)row * Hq + h) * D;
+      qo[lane] = r1;
+      qo[lane + half] = r2;
+    } else {
+      const int g = h - Hq;
+      const float* vp = src + (size_t)(Hq + Hkv + g) * D;
+      const float v1 = vp[lane], v2 = vp[lane + half];
+      store_kv(pool, blk, g, Hkv, D, slot, lane, r1, v1);
+      store_kv(pool, blk, g, Hkv, D, slot, lane + half, r2, v2);
+    }
+  }
+}
+
+// ---------------------------------------------------- cache writes
+__global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ k,
+                                                       const void* __restrict__ v, int src_f32,
+                                                       int Hkv, int D, SeqInfo seq, KvPool pool) {
+  const int row = blockIdx.x;
+  const int sidx = find_seq(seq, row);
+  const int pos = row_position(seq, sidx, row);
+  const int blk = block_of(seq, sidx, pos);
+  const int slot = pos % kBlockTokens;
+  for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
+    const size_t idx = (size_t)row * Hkv * D + e;
+    const float kv = src_f32 ? ((const float*)k)[idx] : (float)((const bf16*)k)[idx];
+    const float vv = src_f32 ? ((const float*)v)[idx] : (float)((const bf16*)v)[idx];
+    store_kv(pool, blk, e / D, Hkv, D, slot, e % D, kv, vv);
+  }
+}
+
+// Per-channel min / max over n tokens: one thread per channel walks the
+// tokens of its slice; partial results merge with atomics on ordered ints.
+__device__ __forceinline__ int f2ord(float f) {
+  const int i = __float_as_int(f);
+  return i >= 0 ? i : i ^ 0x7fffffff;
+}
+__device__ __forceinline__ float ord2f(int i) { return __int_as_float(i >= 0 ? i : i ^ 0x7fffffff); }
+
+__global__ void minmax_kernel(const float* __restrict__ x, int64_t n, int C, int rows_per_block,
+                              int* __restrict__ mn, int* __restrict__ mx) {
+  const int c = blockIdx.y * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t r1 = min(n, r0 + rows_per_block);
+  float lo = INFINITY, hi = -INFINITY;
+  for (int64_t r = r0; r < r1; ++r) {
+    const float v = x[r * C + c];
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  if (r0 < r1) {
+    atomicMin(&mn[c], f2ord(lo));
+    atomicMax(&mx[c], f2ord(hi));
+  }
+}
+__global__ void minmax_init(int* mn, int* mx, int C) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c < C) {
+    mn[c] = 0x7fffffff;
+    mx[c] = (int)0x80000000;
+  }
+}
+// scale = (max - min) / 255 (1 for a flat channel); zp = rint(-min / scale)
+// -- the per-channel formula of the devpress engine page, section 2.6.
+__global__ void calib_finish(const int* mn, const int* mx, int C, float* scale, int* zp) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  const float lo = ord2f(mn[c]), hi = ord2f(mx[c]);
+  float s = __fdiv_rn(hi - lo, 255.0f);
+  if (s == 0.f) s = 1.0f;
+  scale[c] = s;
+  zp[c] = (int)__builtin_rintf(__fdiv_rn(-lo, s));
+}
+
+// ----------------------------------------------------- weight set-up
+__global__ void convert_kernel(const void* __restrict__ src, int src_f32, void* __restrict__ dst,
+                               int dst_f16, int64_t n, int* __restrict__ n_sat) {
+  int sat = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float v = src_f32 ? ((const float*)src)[i] : (float)((const bf16*)src)[i];
+    if (dst_f16) {
+      sat += fabsf(v) > kF16Max;
+      ((f16*)dst)[i] = f32_to_f16_sat(v);
+    } else {
+      ((bf16*)dst)[i] = f32_to_bf16(v);
+    }
+  }
+  if (sat) atomicAdd(n_sat, sat);
+}
+__global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+// dst row 32*(j/16) + j%16 <- gate row j; dst row 32*(j/16) + 16 + j%16 <- up row j
+__global__ void interleave_kernel(const uint8_t* __restrict__ gate, const uint8_t* __restrict__ up,
+                                  int row_bytes, int I, uint8_t* __restrict__ dst) {
+  const int drow = blockIdx.x;  // 0 .. 2I-1
+  const int grp = drow / 32, w = drow % 32;
+  const int j = grp * 16 + (w % 16);
+  const uint8_t* s = (w < 16 ? gate : up) + (size_t)j * row_bytes;
+  uint8_t* d = dst + (size_t)drow * row_bytes;
+  for (int b = threadIdx.x * 4; b < row_bytes; b += blockDim.x * 4)
+    *(uint32_t*)(d + b) = *(const uint32_t*)(s + b);
+}
+
+__global__ void rope_table_kernel(float2* tab, int max_pos, int D, double theta) {
+  const int half = D / 2;
+  const int64_t n = (int64_t)max_pos * half;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int pos = (int)(idx / half), i = (int)(idx % half);
+    const double a = (double)pos * pow(theta, -2.0 * i / D);
+    double sn, cn;
+    sincos(a, &sn, &cn);
+    tab[idx] = make_float2((float)cn, (float)sn);
+  }
+}
+
+}  // namespace
+
+hipError_t rmsnorm_bf16in(const void* x, const float* g, void* y, int rows, int H, float eps,
+                          hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  rmsnorm_kernel<bf16><<<rows, 256, 0, s>>>((const bf16*)x, g, (f16*)y, H, eps);
+  return hipGetLastError();
+}
+hipError_t rmsnorm_f32in(const float* x, const float* g, void* y, int rows, int H, float eps,
+                         hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  rmsnorm_kernel<float><<<rows, 256, 0, s>>>(x, g, (f16*)y, H, eps);
+  return hipGetLastError();
+}
+
+hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, const float2* tab,
+                         const float* q_norm, const float* k_norm, float eps, void* q_out,
+                         SeqInfo seq, KvPool pool, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  rope_kv_kernel<<<rows, 256, 0, s>>>((const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps,
+                                      (float*)q_out, seq, pool);
+  return hipGetLastError();
+}
+
+hipError_t kv_write_rows(const void* k, const void* v, int src_f32, int rows, int Hkv, int D,
+                         SeqInfo seq, KvPool pool, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  kv_write_kernel<<<rows, 256, 0, s>>>(k, v, src_f32, Hkv, D, seq, pool);
+  return hipGetLastError();
+}
+
+hipError_t kv_calibrate(const float* x, int64_t n, int C, float* scale, int* zp, hipStream_t s) {
+  // min/max scratch lives in the zero-point array (int) and the scale array
+  // reinterpreted as int until calib_finish overwrites both.
+  int* mn = zp;
+  int* mx = (int*)scale;
+  minmax_init<<<cdiv(C, 256), 256, 0, s>>>(mn, mx, C);
+  const int rows_per_block = 256;
+  const int64_t nb = (n + rows_per_block - 1) / rows_per_block;
+  if (nb > 0) {
+    dim3 grid((unsigned)nb, cdiv(C, 256));
+    minmax_kernel<<<grid, 256, 0, s>>>(x, n, C, rows_per_block, mn, mx);
+  }
+  calib_finish<<<cdiv(C, 256), 256, 0, s>>>(mn, mx, C, scale, zp);
+  return hipGetLastError();
+}
+
+hipError_t rope_table_build(float2* tab, int max_pos, int D, double theta, hipStream_t s) {
+  rope_table_kernel<<<1024, 256, 0, s>>>(tab, max_pos, D, theta);
+  return hipGetLastError();
+}
+
+hipError_t convert_weights(const void* src, int src_f32, void* dst, int dst_f16, int64_t n,
+                           int* n_saturated, hipStream_t s) {
+  convert_kernel<<<2048, 256, 0, s>>>(src, src_f32, dst, dst_f16, n, n_saturated);
+  return hipGetLastError();
+}
+
+hipError_t interleave_gate_up(const void* gate, const void* up, int row_bytes, int I, void* dst,
+                              hipStream_t s) {
+  interleave_kernel<<<2 * I, 256, 0, s>>>((const uint8_t*)gate, (const uint8_t*)up, row_bytes, I,
+                                          (uint8_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
+  copy_f32_kernel<<<256, 256, 0, s>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace tdl
