@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the decoder layer on one MI355X.
+
+Headline: prompt prefill of the Qwen2.5-7B-shaped layer (hidden 3584, 28 Q /
+4 KV heads, head_dim 128, SwiGLU 18944, QKV bias) over 4096 tokens, batch 1,
+writing K/V into a bf16 block-paged cache -- one layer_prefill call per step,
+inputs resident in HBM.  value = tokens/s.
+
+Also reported (same JSON line): the paged decode step of the same layer (batch
+64, contexts U[128, 4096], bf16 cache, random block permutation) in us/step
+with its HBM fraction; the dominant kernel's roofline (per-kernel HIP-event
+durations recorded by the library on the call's stream over the timed
+region); and the oracle's CPU throughput on a bounded sample of the prefill.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=30)
+    ap.add_argument("--prefill-len", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="prompt tokens the oracle runs for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+def linear_flops_per_token(s):
+    D = s.head_dim
+    n = (s.n_q_heads + 2 * s.n_kv_heads) * D * s.hidden + s.hidden * s.n_q_heads * D \
+        + 2 * s.intermediate * s.hidden + s.hidden * s.intermediate
+    return 2 * n
+
+
+def weight_bytes(s):
+    return linear_flops_per_token(s) // 2 * 2   # 2-byte weights
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import transformer_decoder_layer_amd as tdl
+
+    torch.cuda.set_device(0)
+    shape = synth.QWEN25_7B
+    H, D, Hq, Hkv, I = shape.hidden, shape.head_dim, shape.n_q_heads, shape.n_kv_heads, shape.intermediate
+    T = args.prefill_len
+    stream = torch.cuda.current_stream()
+
+    log("generating weights")
+    w = synth.torch_weights(shape, seed=0)
+    cfg = tdl.make_config(shape, max_tokens=T, max_seqs=64, max_position=8192)
+    layer = tdl.Layer(cfg, w)
+
+    # ------------------------------------------------------------ prefill
+    x = synth.torch_normal((T, H), seed=1, dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    rng = np.random.default_rng(2)
+    n_blk = math.ceil(T / 16)
+    table = torch.from_numpy(synth.random_tables(rng, [T], n_blocks=n_blk)[0]).cuda()
+    kv = tdl.KvCache(n_blk, Hkv, D, "bf16")
+    log(f"prefill T={T}: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        layer.prefill(x, y, 0, kv, table)
+    torch.cuda.synchronize()
+    layer.profile_enable(True)
+    log(f"prefill: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.prefill(x, y, 0, kv, table)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = layer.profile_read()
+    layer.profile_enable(False)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    tok_s = T * args.steps / (t1 - t0)
+    stage_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in prof.items()}
+    log("prefill stages (ms/launch): " + ", ".join(f"{k}={v:.3f}" for k, v in stage_ms.items() if v))
+    assert torch.isfinite(y.float()).all(), "non-finite prefill output"
+
+    lin_flops = linear_flops_per_token(shape) * T
+    attn_flops = 2 * D * Hq * T * (T + 1)
+    step_flops = lin_flops + attn_flops
+    gu_flops = 2 * T * (2 * I) * H
+    gu_ms = stage_ms["gate_up"]
+    gu_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "gate_up GEMM + SiLU-gate (fp16 operands)",
+                "achieved": round(gu_tflops, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gu_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 4)}
+    layer_tflops = step_flops / (ms_step * 1e-3) / 1e12
+    stage_report = {k: round(v, 4) for k, v in stage_ms.items() if v}
+
+    # ------------------------------------------------------------- decode
+    decode = None
+    if not args.no_decode:
+        wl = synth.WORKLOADS["qwen25_decode_b64"]
+        B = wl.decode_batch
+        ctx = synth.context_lengths(np.random.default_rng(0), wl)
+        totals = (ctx + 1).tolist()
+        nb = int(sum(math.ceil(t / 16) for t in totals))
+        tab_np = synth.random_tables(np.random.default_rng(3), totals, n_blocks=nb)
+        dkv = tdl.KvCache(nb, Hkv, D, "bf16")
+        n_cached = int(ctx.sum())
+        log(f"decode: filling cache with {n_cached} tokens")
+        ck = synth.torch_normal((n_cached, Hkv, D), seed=4, dtype=torch.bfloat16)
+        cv = synth.torch_normal((n_cached, Hkv, D), seed=5, dtype=torch.bfloat16)
+        tab = torch.from_numpy(tab_np).cuda()
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)).cuda()
+        dkv.write(cu, torch.zeros(B, dtype=torch.int32, device="cuda"), tab, ck, cv)
+        del ck, cv
+        ctx_d = torch.from_numpy(ctx).cuda()
+        xd = synth.torch_normal((B, H), seed=6, dtype=torch.bfloat16)
+        yd = torch.empty_like(xd)
+        max_ctx = int(ctx.max()) + 1
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB > L2 + MALL
+        for _ in range(3):
+            layer.decode_paged(xd, yd, ctx_d, tab, max_ctx, dkv)
+        torch.cuda.synchronize()
+        layer.profile_enable(True)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.decode_steps)]
+        for e0, e1 in ev:
+            flush.fill_(1.0)
+            e0.record(stream)
+            layer.decode_paged(xd, yd, ctx_d, tab, max_ctx, dkv)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        dprof = layer.profile_read()
+        layer.profile_enable(False)
+        times = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        us = 1e3 * float(np.median(times))
+        kv_bytes = int(sum(totals)) * Hkv * D * 2 * 2
+        step_bytes = weight_bytes(shape) + kv_bytes + 2 * B * H * 2
+        dstage = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in dprof.items()}
+        attn_ms = dstage["attn_decode"]
+        decode = {"workload": "qwen2.5-7b layer paged decode, batch 64, ctx U[128,4096], bf16 KV, "
+                              "block 16, random block permutation; L2/MALL flushed between steps",
+                  "us_per_step": round(us, 2), "us_p10": round(1e3 * times[len(times) // 10], 2),
+                  "us_p90": round(1e3 * times[(9 * len(times)) // 10], 2),
+                  "algorithmic_bytes": step_bytes,
+                  "hbm_gbs": round(step_bytes / (us * 1e-6) / 1e9, 1),
+                  "hbm_frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                  "attn_kernel": {"bound": "hbm", "avg_launch_ms": round(attn_ms, 4),
+                                  "achieved": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(kv_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                  "stages_ms": {k: round(v, 4) for k, v in dstage.items() if v}}
+        log(f"decode: {us:.1f} us/step, {decode['hbm_gbs']} GB/s")
+        assert torch.isfinite(yd.float()).all(), "non-finite decode output"
+        del flush
+
+    # --------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        n = min(args.cpu_tokens, T)
+        log(f"cpu baseline: oracle on {n} prompt tokens")
+        wh = {k: v.float().cpu().numpy() for k, v in w.items()}
+        W = oracle.expand_weights(shape, wh)
+        xh = x[:n].float().cpu().numpy()
+        tab_h = table.cpu().numpy()[None, :]
+        cache = oracle.PagedCache(n_blk, Hkv, D, "bf16")
+        c0 = time.perf_counter()
+        oracle.layer_forward(shape, W, xh, [0], [n], [0], tab_h, cache)
+        c1 = time.perf_counter()
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        cpu = {"value": round(n / (c1 - c0), 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"float64 numpy oracle, one {n}-token causal prefill of the same layer and "
+                         f"weights ({c1 - c0:.1f} s)"}
+        log(f"cpu baseline: {cpu['value']} tokens/s on {threads} threads")
+
+    out = {
+        "metric": "layer prefill tokens/s + paged decode us/step; % of MFMA / HBM roofline",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16/bf16 MFMA operands, fp32 accumulate; bf16 KV cache",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations)",
+        "config": {"workload": f"qwen2.5-7b-shaped decoder layer, causal prefill seq {T}, batch 1, "
+                               "QKV bias, bf16 paged KV cache written",
+                   "global_batch": 1, "seq_len": T},
+        "roofline": roofline,
+        "layer_mfma": {"flops_per_step": step_flops, "achieved_tflops": round(layer_tflops, 1),
+                       "frac": round(layer_tflops / PEAK_MFMA_TFLOPS, 4)},
+        "stages_ms": stage_report,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

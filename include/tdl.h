@@ -211,6 +211,30 @@ tdl_status layer_step(tdl_layer* layer, tdl_stream stream, const tdl_batch* batc
 /* Pointers to the intermediate buffers (see tdl_workspace_view). */
 tdl_status layer_workspace_view(const tdl_layer* layer, tdl_workspace_view* out);
 
+/* Per-stage timing.  While enabled, every call records a pair of hipEvents
+ * around each of its kernels on the call's stream (a few microseconds per
+ * call).  layer_profile_read synchronises those events, adds their elapsed
+ * times to the totals and returns the totals since the last enable. */
+enum {
+  TDL_STAGE_RMSNORM1 = 0,  /* x -> xn                         */
+  TDL_STAGE_QKV = 1,       /* xn W_qkv^T + b                   */
+  TDL_STAGE_ROPE_KV = 2,   /* q/k norm, RoPE, KV slot write     */
+  TDL_STAGE_ATTN_PREFILL = 3,
+  TDL_STAGE_ATTN_DECODE = 4,
+  TDL_STAGE_O_PROJ = 5,    /* h = x + o W_o^T                  */
+  TDL_STAGE_RMSNORM2 = 6,  /* h -> hn                          */
+  TDL_STAGE_GATE_UP = 7,   /* a = silu(hn W_g^T) * (hn W_u^T)  */
+  TDL_STAGE_DOWN = 8,      /* y = h + a W_d^T                  */
+  TDL_N_STAGES = 9
+};
+typedef struct {
+  double ms[TDL_N_STAGES];        /* summed kernel time per stage          */
+  int64_t launches[TDL_N_STAGES]; /* kernel launches counted per stage     */
+} tdl_profile;
+
+tdl_status layer_profile_enable(tdl_layer* layer, int enable);
+tdl_status layer_profile_read(tdl_layer* layer, tdl_profile* out);
+
 /* ------------------------------------------------------------- KV cache */
 
 /* Bytes of device memory a cache with this configuration needs (pools plus,

@@ -282,3 +282,43 @@ def make_inputs(wl: Workload, seed: int = 0, shape: Optional[LayerShape] = None,
                        bf16=(wl.kv_dtype == "bf16"))
         cache_k, cache_v = kv["k"], kv["v"]
     return LayerInputs(wl, weights, x, batch, cache_k, cache_v)
+
+
+# ------------------------------------------------------------------------
+# Device-side generation for benchmarks: the same distributions drawn with
+# torch's generator on the GPU (fast for ~10^8 values; not bitwise equal to
+# the numpy draws above).
+# ------------------------------------------------------------------------
+
+def torch_weights(shape: LayerShape, seed: int = 0, device: str = "cuda"):
+    """Weights as device tensors in the dtypes the C ABI takes: linear weights
+    bf16 (or Q8_0 int8 codes + fp16 scales), biases and gains float32."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    H, D, I = shape.hidden, shape.head_dim, shape.intermediate
+    nq, nkv = shape.n_q_heads * D, shape.n_kv_heads * D
+    dims = {"wq": (nq, H), "wk": (nkv, H), "wv": (nkv, H), "wo": (H, nq),
+            "wg": (I, H), "wu": (I, H), "wd": (H, I)}
+    w = {"ln1": torch.ones(H, device=device), "ln2": torch.ones(H, device=device)}
+    for name, (o, i) in dims.items():
+        if shape.weight_dtype == "q80":
+            w[name] = torch.randint(-127, 128, (o, i), generator=g, device=device, dtype=torch.int8)
+            w[name + "_scale"] = (torch.randn(o, i // 32, generator=g, device=device).abs() * 0.002).half()
+        else:
+            w[name] = (torch.randn(o, i, generator=g, device=device) * 0.02).to(torch.bfloat16)
+    if shape.qkv_bias:
+        for name, n in (("bq", nq), ("bk", nkv), ("bv", nkv)):
+            w[name] = (torch.randn(n, generator=g, device=device) * 0.02).to(torch.bfloat16).float()
+    if shape.qk_norm:
+        w["q_norm"] = torch.ones(D, device=device)
+        w["k_norm"] = torch.ones(D, device=device)
+    return w
+
+
+def torch_normal(shape, seed: int, dtype=None, device: str = "cuda"):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(*shape, generator=g, device=device)
+    return t.to(dtype) if dtype is not None else t

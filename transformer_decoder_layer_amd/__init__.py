@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the layer runs in the library's HIP
 kernels.  PyTorch supplies device memory (tensors) and streams.  Importing
 fails loudly if the library has not been built
-(``python -m transformer_decoder_layer_amd.build``).
+(``python transformer_decoder_layer_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libtdl.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m transformer_decoder_layer_amd.build` (hipcc, gfx950)")
+                      "`python transformer_decoder_layer_amd/build.py` (hipcc, gfx950)")
 _lib = ctypes.CDLL(LIB_PATH)
 
 TDL_OK, TDL_E_INVALID, TDL_E_UNSUPPORTED, TDL_E_CAPACITY, TDL_E_NOMEM, TDL_E_HIP = range(6)
@@ -29,7 +29,7 @@ c_i32, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctyp
 P_i32 = ctypes.POINTER(ctypes.c_int32)
 
 EXPORTS = ["layer_create", "layer_destroy", "layer_prefill", "layer_decode_paged", "layer_step",
-           "layer_workspace_view", "kv_cache_bytes", "kv_cache_alloc", "kv_cache_free",
+           "layer_workspace_view", "layer_profile_enable", "layer_profile_read", "kv_cache_bytes", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_view", "kv_block_table", "kv_block_release", "kv_free_blocks",
            "kv_cache_calibrate", "kv_cache_write", "tdl_status_string", "tdl_last_error"]
 
@@ -68,6 +68,14 @@ class Batch(ctypes.Structure):
                 ("q_start", c_vp), ("q_len", c_vp), ("ctx_len", c_vp), ("block_tables", c_vp)]
 
 
+STAGES = ["rmsnorm1", "qkv", "rope_kv", "attn_prefill", "attn_decode", "o_proj", "rmsnorm2",
+          "gate_up", "down"]
+
+
+class Profile(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * len(STAGES)), ("launches", ctypes.c_int64 * len(STAGES))]
+
+
 class WorkspaceView(ctypes.Structure):
     _fields_ = [(n, c_vp) for n in ["xn", "qkv", "q", "o", "h", "hn", "a"]]
 
@@ -87,6 +95,8 @@ _layer_decode = _sig("layer_decode_paged", c_i32, c_vp, c_vp, c_vp, c_vp, c_i32,
                      c_i32, c_vp)
 _layer_step = _sig("layer_step", c_i32, c_vp, c_vp, ctypes.POINTER(Batch), c_vp, c_vp, c_vp)
 _layer_ws = _sig("layer_workspace_view", c_i32, c_vp, ctypes.POINTER(WorkspaceView))
+_layer_prof_enable = _sig("layer_profile_enable", c_i32, c_vp, c_i32)
+_layer_prof_read = _sig("layer_profile_read", c_i32, c_vp, ctypes.POINTER(Profile))
 _kv_bytes = _sig("kv_cache_bytes", c_sz, ctypes.POINTER(KvConfig))
 _kv_alloc = _sig("kv_cache_alloc", c_i32, ctypes.POINTER(KvConfig), c_vp, ctypes.POINTER(c_vp))
 _kv_free = _sig("kv_cache_free", c_i32, c_vp)
@@ -297,6 +307,15 @@ class Layer:
                   block_tables.shape[1], _ptr(q_start), _ptr(q_len), _ptr(ctx_len), _ptr(block_tables))
         _check("layer_step", _layer_step(self._h, _stream(stream), ctypes.byref(b), _ptr(x), _ptr(y),
                                          kv.handle))
+
+    def profile_enable(self, enable: bool = True):
+        _check("layer_profile_enable", _layer_prof_enable(self._h, int(enable)))
+
+    def profile_read(self) -> Dict[str, tuple]:
+        # {stage: (total_ms, launches)} since the last profile_enable
+        p = Profile()
+        _check("layer_profile_read", _layer_prof_read(self._h, ctypes.byref(p)))
+        return {name: (p.ms[i], p.launches[i]) for i, name in enumerate(STAGES)}
 
     def workspace(self) -> WorkspaceView:
         v = WorkspaceView()

@@ -1,6 +1,6 @@
 """Builds libtdl.so (the HIP kernels and the C-ABI) for gfx950 with hipcc.
 
-    python -m transformer_decoder_layer_amd.build
+    python transformer_decoder_layer_amd/build.py
 
 Objects go to transformer_decoder_layer_amd/_build/, the library next to
 this file.  Always recompiles every source.

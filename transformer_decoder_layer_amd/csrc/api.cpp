@@ -99,8 +99,23 @@ struct tdl_layer {
   void* priv_k = nullptr;  // bf16 pool for calls without a KV cache
   void* priv_v = nullptr;
   std::vector<void*> allocs;
+  // per-stage timing (layer_profile_enable)
+  bool prof_on = false;
+  struct Mark {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<Mark> prof_pending;
+  std::vector<hipEvent_t> prof_free;
+  double prof_ms[TDL_N_STAGES] = {};
+  int64_t prof_n[TDL_N_STAGES] = {};
 
   ~tdl_layer() {
+    for (auto& m : prof_pending) {
+      (void)hipEventDestroy(m.a);
+      (void)hipEventDestroy(m.b);
+    }
+    for (auto e : prof_free) (void)hipEventDestroy(e);
     for (void* p : allocs) (void)hipFree(p);
   }
 };
@@ -222,6 +237,36 @@ tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const voi
   return TDL_OK;
 }
 
+// Per-stage timing: a StageTimer records an event pair around one stage's
+// kernels on the call's stream while profiling is on.
+hipEvent_t take_event(tdl_layer* L) {
+  if (!L->prof_free.empty()) {
+    hipEvent_t e = L->prof_free.back();
+    L->prof_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+int prof_begin(tdl_layer* L, int stage, hipStream_t st) {
+  if (!L->prof_on) return -1;
+  tdl_layer::Mark m{stage, take_event(L), take_event(L)};
+  if (!m.a || !m.b) return -1;
+  (void)hipEventRecord(m.a, st);
+  L->prof_pending.push_back(m);
+  return (int)L->prof_pending.size() - 1;
+}
+struct StageTimer {
+  tdl_layer* L;
+  hipStream_t st;
+  int mark;
+  StageTimer(tdl_layer* l, int stage, hipStream_t s) : L(l), st(s), mark(prof_begin(l, stage, s)) {}
+  ~StageTimer() {
+    if (mark >= 0) (void)hipEventRecord(L->prof_pending[mark].b, st);
+  }
+};
+
 // The whole layer over `rows` rows.  Sequences 0..n_prefill-1 of `seq` use the
 // prefill attention kernel, decode sequences dec_first .. dec_first+n_dec-1
 // the paged decode kernel.
@@ -237,20 +282,47 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
       return fail(TDL_E_CAPACITY, "decode workspace too small (batch %d, max_ctx_len %d)", n_dec,
                   max_ctx_len);
   }
-  HIP_TRY(rmsnorm_bf16in(x, L->ln1, L->xn, rows, H, c.rms_eps, st));
-  TRY(run_gemm(L, st, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, EPI_BIAS_F32, L->bqkv, nullptr, 0,
-               L->qkv, L->Nqkv));
-  HIP_TRY(rope_kv_write(L->qkv, rows, Hq, Hkv, D, L->rope, c.qk_norm ? L->qn : nullptr,
-                        c.qk_norm ? L->kn : nullptr, c.rms_eps, L->q, seq, pool, st));
-  if (n_prefill) HIP_TRY(attn_prefill(L->q, pool, seq, n_prefill, max_q_len, Hq, Hkv, D, L->o, st));
-  if (n_dec)
+  {
+    StageTimer t(L, TDL_STAGE_RMSNORM1, st);
+    HIP_TRY(rmsnorm_bf16in(x, L->ln1, L->xn, rows, H, c.rms_eps, st));
+  }
+  {
+    StageTimer t(L, TDL_STAGE_QKV, st);
+    TRY(run_gemm(L, st, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, EPI_BIAS_F32, L->bqkv, nullptr,
+                 0, L->qkv, L->Nqkv));
+  }
+  {
+    StageTimer t(L, TDL_STAGE_ROPE_KV, st);
+    HIP_TRY(rope_kv_write(L->qkv, rows, Hq, Hkv, D, L->rope, c.qk_norm ? L->qn : nullptr,
+                          c.qk_norm ? L->kn : nullptr, c.rms_eps, L->q, seq, pool, st));
+  }
+  if (n_prefill) {
+    StageTimer t(L, TDL_STAGE_ATTN_PREFILL, st);
+    HIP_TRY(attn_prefill(L->q, pool, seq, n_prefill, max_q_len, Hq, Hkv, D, L->o, st));
+  }
+  if (n_dec) {
+    StageTimer t(L, TDL_STAGE_ATTN_DECODE, st);
     HIP_TRY(attn_decode(dp, L->q, pool, seq, dec_first, 0, n_dec, Hq, Hkv, D, L->o, L->dec_part,
                         L->dec_cnt, st));
-  TRY(run_gemm(L, st, rows, H, Hq * D, L->o, L->wo, L->wo_s, EPI_RESID_F32, nullptr, x, H, L->h, H));
-  HIP_TRY(rmsnorm_f32in(L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
-  TRY(run_gemm(L, st, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, EPI_SILU_GATE, nullptr, nullptr, 0,
-               L->a, I));
-  TRY(run_gemm(L, st, rows, H, I, L->a, L->wd, L->wd_s, EPI_RESID_BF16, nullptr, L->h, H, y, H));
+  }
+  {
+    StageTimer t(L, TDL_STAGE_O_PROJ, st);
+    TRY(run_gemm(L, st, rows, H, Hq * D, L->o, L->wo, L->wo_s, EPI_RESID_F32, nullptr, x, H, L->h,
+                 H));
+  }
+  {
+    StageTimer t(L, TDL_STAGE_RMSNORM2, st);
+    HIP_TRY(rmsnorm_f32in(L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
+  }
+  {
+    StageTimer t(L, TDL_STAGE_GATE_UP, st);
+    TRY(run_gemm(L, st, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, EPI_SILU_GATE, nullptr, nullptr, 0,
+                 L->a, I));
+  }
+  {
+    StageTimer t(L, TDL_STAGE_DOWN, st);
+    TRY(run_gemm(L, st, rows, H, I, L->a, L->wd, L->wd_s, EPI_RESID_BF16, nullptr, L->h, H, y, H));
+  }
   return TDL_OK;
 }
 
@@ -566,6 +638,41 @@ extern "C" tdl_status layer_workspace_view(const tdl_layer* L, tdl_workspace_vie
   out->h = L->h;
   out->hn = L->hn;
   out->a = L->a;
+  return TDL_OK;
+}
+
+extern "C" tdl_status layer_profile_enable(tdl_layer* L, int enable) {
+  if (!L) return fail(TDL_E_INVALID, "layer is NULL");
+  for (auto& m : L->prof_pending) {
+    (void)hipEventSynchronize(m.b);
+    L->prof_free.push_back(m.a);
+    L->prof_free.push_back(m.b);
+  }
+  L->prof_pending.clear();
+  for (int i = 0; i < TDL_N_STAGES; ++i) {
+    L->prof_ms[i] = 0;
+    L->prof_n[i] = 0;
+  }
+  L->prof_on = enable != 0;
+  return TDL_OK;
+}
+
+extern "C" tdl_status layer_profile_read(tdl_layer* L, tdl_profile* out) {
+  if (!L || !out) return fail(TDL_E_INVALID, "NULL argument");
+  for (auto& m : L->prof_pending) {
+    HIP_TRY(hipEventSynchronize(m.b));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, m.a, m.b));
+    L->prof_ms[m.stage] += ms;
+    L->prof_n[m.stage] += 1;
+    L->prof_free.push_back(m.a);
+    L->prof_free.push_back(m.b);
+  }
+  L->prof_pending.clear();
+  for (int i = 0; i < TDL_N_STAGES; ++i) {
+    out->ms[i] = L->prof_ms[i];
+    out->launches[i] = L->prof_n[i];
+  }
   return TDL_OK;
 }
 
