@@ -90,12 +90,8 @@ struct tdl_layer {
   float* h = nullptr;
   float* gemm_ws = nullptr;
   size_t gemm_ws_floats = 0;
-  int* gemm_cnt = nullptr;
-  int gemm_cnt_n = 0;
   float* dec_part = nullptr;
   size_t dec_part_floats = 0;
-  int* dec_cnt = nullptr;
-  int dec_cnt_n = 0;
   void* priv_k = nullptr;  // bf16 pool for calls without a KV cache
   void* priv_v = nullptr;
   std::vector<void*> allocs;
@@ -171,27 +167,25 @@ struct GemmShapes {
   int Nqkv, H, Hq_D, I;
 };
 
-// Largest split-K workspace / counter count over every row count a call may use.
-void gemm_ws_need(const tdl_layer_config& c, int Nqkv, bool q80, size_t* ws, int* cnt) {
+// Largest split-K workspace over every row count a call may use.
+void gemm_ws_need(const tdl_layer_config& c, int Nqkv, bool q80, size_t* ws) {
   const int H = c.hidden, QD = c.n_q_heads * c.head_dim, I = c.intermediate;
   const int shapes[4][3] = {{Nqkv, H, EPI_BIAS_F32}, {H, QD, EPI_RESID_F32},
                             {2 * I, H, EPI_SILU_GATE}, {H, I, EPI_RESID_BF16}};
   size_t w = 0;
-  int n = 0;
   for (int M = 1; M <= c.max_tokens; ++M)
-    for (auto& s : shapes) {
-      const GemmPlan p = gemm_plan(M, s[0], s[1], q80, s[2]);
-      w = std::max(w, p.ws_floats);
-      n = std::max(n, p.n_counters);
-    }
+    for (auto& s : shapes) w = std::max(w, gemm_plan(M, s[0], s[1], q80, s[2]).ws_floats);
   *ws = w;
-  *cnt = n;
 }
 
-size_t decode_part_need(const tdl_layer_config& c, int batch) {
-  const int Hkv = c.n_kv_heads;
-  const int want = std::max(1, (2048 + batch * Hkv - 1) / (batch * Hkv));
-  return (size_t)batch * Hkv * (want + 1) * (16 * c.head_dim + 32);
+// Largest decode partition workspace over every batch size and context bound.
+size_t decode_part_need(const tdl_layer_config& c, int max_batch) {
+  size_t w = 0;
+  const int max_blk = (c.max_position + 15) / 16;
+  for (int b = 1; b <= max_batch; ++b)
+    for (int nb = 1; nb <= max_blk; ++nb)
+      w = std::max(w, decode_plan(b, c.n_q_heads, c.n_kv_heads, c.head_dim, nb * 16).part_floats);
+  return w;
 }
 
 KvPool pool_of(const tdl_layer* L, const tdl_kv_cache* kv) {
@@ -215,7 +209,7 @@ tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const voi
                     const __half* Bs, int epi, const float* bias, const void* resid, int ldr,
                     void* C, int ldc) {
   const GemmPlan pl = gemm_plan(M, N, K, L->q80, epi);
-  if (pl.ws_floats > L->gemm_ws_floats || pl.n_counters > L->gemm_cnt_n)
+  if (pl.ws_floats > L->gemm_ws_floats)
     return fail(TDL_E_CAPACITY, "GEMM workspace too small for M=%d N=%d K=%d", M, N, K);
   GemmArgs a{};
   a.A = A;
@@ -232,7 +226,6 @@ tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const voi
   a.C = C;
   a.ldc = ldc;
   a.ws = L->gemm_ws;
-  a.counters = L->gemm_cnt;
   HIP_TRY(gemm_launch(pl, a, L->q80, epi, st));
   return TDL_OK;
 }
@@ -278,7 +271,7 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   DecodePlan dp{};
   if (n_dec) {
     dp = decode_plan(n_dec, Hq, Hkv, D, max_ctx_len);
-    if (dp.part_floats > L->dec_part_floats || dp.n_counters > L->dec_cnt_n)
+    if (dp.part_floats > L->dec_part_floats)
       return fail(TDL_E_CAPACITY, "decode workspace too small (batch %d, max_ctx_len %d)", n_dec,
                   max_ctx_len);
   }
@@ -302,8 +295,7 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   }
   if (n_dec) {
     StageTimer t(L, TDL_STAGE_ATTN_DECODE, st);
-    HIP_TRY(attn_decode(dp, L->q, pool, seq, dec_first, 0, n_dec, Hq, Hkv, D, L->o, L->dec_part,
-                        L->dec_cnt, st));
+    HIP_TRY(attn_decode(dp, L->q, pool, seq, dec_first, n_dec, Hq, Hkv, D, L->o, L->dec_part, st));
   }
   {
     StageTimer t(L, TDL_STAGE_O_PROJ, st);
@@ -490,16 +482,11 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   CTRY(dalloc(L, &L->h, (size_t)T * H * 4));
   CTRY(dalloc(L, &L->hn, (size_t)T * H * 2));
   CTRY(dalloc(L, &L->a, (size_t)T * I * 2));
-  gemm_ws_need(c, L->Nqkv, q80, &L->gemm_ws_floats, &L->gemm_cnt_n);
+  gemm_ws_need(c, L->Nqkv, q80, &L->gemm_ws_floats);
   CTRY(dalloc(L, &L->gemm_ws, L->gemm_ws_floats * 4));
-  CTRY(dalloc(L, &L->gemm_cnt, (size_t)std::max(1, L->gemm_cnt_n) * 4));
-  CHIP(hipMemsetAsync(L->gemm_cnt, 0, (size_t)std::max(1, L->gemm_cnt_n) * 4, st));
   const int max_dec = std::min(c.max_seqs, c.max_tokens);
   L->dec_part_floats = decode_part_need(c, max_dec);
-  L->dec_cnt_n = max_dec * Hkv;
   CTRY(dalloc(L, &L->dec_part, L->dec_part_floats * 4));
-  CTRY(dalloc(L, &L->dec_cnt, (size_t)L->dec_cnt_n * 4));
-  CHIP(hipMemsetAsync(L->dec_cnt, 0, (size_t)L->dec_cnt_n * 4, st));
   const size_t priv_blocks = (size_t)(T + 15) / 16;
   CTRY(dalloc(L, &L->priv_k, priv_blocks * KD * 16 * 2));
   CTRY(dalloc(L, &L->priv_v, priv_blocks * KD * 16 * 2));

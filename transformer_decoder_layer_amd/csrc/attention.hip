@@ -32,6 +32,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace tdl {
 
@@ -306,15 +307,44 @@ struct DecArgs {
   int first_seq;
   int Hq, Hkv;
   int part_blocks, max_parts;
-  float* part;
-  int* counters;
+  float* part;  // [batch][Hkv][max_parts][16*D + 32]: unnormalised O, then (m, l)
   f16* o;
 };
 
-template <int D>
-__device__ __forceinline__ bf16x8 load_k_frag(const void* base, bool u8, int off) {
-  if (!u8) return *(const bf16x8*)((const bf16*)base + off);
-  const uint2 w = *(const uint2*)((const uint8_t*)base + off);
+constexpr int kPartStride(int D) { return 16 * D + 32; }
+
+template <int D, bool U8>
+struct DecFrags {
+  // K rows (A operand): key lane%16, channels 32s + 8*(lane/16) .. +7
+  typename std::conditional<U8, uint2, bf16x8>::type k[D / 32];
+  // V^T rows (A operand): channel 16t + lane%16, keys 4*(lane/16) .. +3
+  typename std::conditional<U8, uint32_t, bf16x4>::type v[D / 16];
+};
+
+template <int D, bool U8>
+__device__ __forceinline__ void dec_load(DecFrags<D, U8>& f, const DecArgs& a, int phys, int g,
+                                         int col, int grp) {
+  const size_t hb = ((size_t)phys * a.Hkv + g) * (kBlockTokens * D);
+  if constexpr (U8) {
+    const uint8_t* kb = (const uint8_t*)a.pool.k + hb;
+    const uint8_t* vb = (const uint8_t*)a.pool.v + hb;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) f.k[s] = *(const uint2*)(kb + col * D + 32 * s + 8 * grp);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      f.v[t] = *(const uint32_t*)(vb + (16 * t + col) * kBlockTokens + 4 * grp);
+  } else {
+    const bf16* kb = (const bf16*)a.pool.k + hb;
+    const bf16* vb = (const bf16*)a.pool.v + hb;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) f.k[s] = *(const bf16x8*)(kb + col * D + 32 * s + 8 * grp);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      f.v[t] = *(const bf16x4*)(vb + (16 * t + col) * kBlockTokens + 4 * grp);
+  }
+}
+
+__device__ __forceinline__ bf16x8 u8x8_to_bf16(uint2 w) {
   bf16x8 r;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -323,13 +353,18 @@ __device__ __forceinline__ bf16x8 load_k_frag(const void* base, bool u8, int off
   }
   return r;
 }
+__device__ __forceinline__ bf16x4 u8x4_to_bf16(uint32_t w) {
+  bf16x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = (bf16)(float)((w >> (8 * e)) & 0xff);
+  return r;
+}
 
 template <int D, bool U8>
 __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   constexpr int NT = D / 16;  // 16-channel tiles of the output
   __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][D][16];
-  __shared__ int s_last;
+  __shared__ float sm_o[4][D][17];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -386,38 +421,27 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   }
 
   const float sc = kLog2e * rsqrtf((float)D);
-  const int esz = U8 ? 1 : 2;
-  const size_t head_elems = (size_t)kBlockTokens * D;
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int blk = blk0 + wave; blk < blk1; blk += 4) {
-    const int phys = seq_block(a.seq, sidx, blk);
-    const size_t hb = ((size_t)phys * a.Hkv + g) * head_elems;
-    const char* kb = (const char*)a.pool.k + hb * esz;
-    const char* vb = (const char*)a.pool.v + hb * esz;
-    // S^T[key][head]: A = K rows (key = lane%16), B = Q^T
+  // this wave's blocks: blk0 + wave + 4i; the table entries come in one load
+  const int cnt = blk1 - blk0 > wave ? cdiv(blk1 - blk0 - wave, 4) : 0;
+  int my_phys = 0;
+  if (lane < cnt) my_phys = seq_block(a.seq, sidx, blk0 + wave + 4 * lane);
+
+  auto compute = [&](const DecFrags<D, U8>& f, int i) {
+    const int blk = blk0 + wave + 4 * i;
+    // S^T[key][head]: A = K rows (key = lane%16), B = Q^T (hi + lo)
     f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      const bf16x8 kf = load_k_frag<D>(kb, U8, col * D + 32 * s + 8 * grp);
+      bf16x8 kf;
+      if constexpr (U8) kf = u8x8_to_bf16(f.k[s]);
+      else kf = f.k[s];
       st = mfma16x16x32(kf, qf[s], st);
       st = mfma16x16x32(kf, qlo[s], st);
-    }
-    // V^T fragments: channel d = 16t + col, keys 4grp .. 4grp+3
-    bf16x4 vf[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int off = (16 * t + col) * kBlockTokens + 4 * grp;
-      if constexpr (U8) {
-        const uint32_t w = *(const uint32_t*)(vb + off);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vf[t][e] = (bf16)(float)((w >> (8 * e)) & 0xff);
-      } else {
-        vf[t] = *(const bf16x4*)((const bf16*)vb + off);
-      }
     }
     // lane holds S[head col][key 4grp + r]
     const int key0 = blk * kBlockTokens + 4 * grp;
@@ -446,17 +470,31 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       psum += pv;
     }
     l_run = l_run * alpha + psum;
-    if (key0 + 3 >= n_keys) {  // unwritten slots of the last block: zero V
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (key0 + r >= n_keys) vf[t][r] = (bf16)0.f;
-    }
+    const bool tail = key0 + 3 >= n_keys;  // unwritten slots of the last block: zero V
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      acc[t] = mfma16x16x16(vf[t], pf, acc[t] * alpha);
-      acc[t] = mfma16x16x16(vf[t], pl, acc[t]);
+      bf16x4 vf;
+      if constexpr (U8) vf = u8x4_to_bf16(f.v[t]);
+      else vf = f.v[t];
+      if (tail) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (key0 + r >= n_keys) vf[r] = (bf16)0.f;
+      }
+      acc[t] = mfma16x16x16(vf, pf, acc[t] * alpha);
+      acc[t] = mfma16x16x16(vf, pl, acc[t]);
+    }
+  };
+
+  // ping-pong: the next block's loads are in flight while this one computes
+  DecFrags<D, U8> fa, fb;
+  if (cnt > 0) dec_load<D, U8>(fa, a, __shfl(my_phys, 0, 64), g, col, grp);
+  for (int i = 0; i < cnt; i += 2) {
+    if (i + 1 < cnt) dec_load<D, U8>(fb, a, __shfl(my_phys, i + 1, 64), g, col, grp);
+    compute(fa, i);
+    if (i + 1 < cnt) {
+      if (i + 2 < cnt) dec_load<D, U8>(fa, a, __shfl(my_phys, i + 2, 64), g, col, grp);
+      compute(fb, i + 1);
     }
   }
 
@@ -473,9 +511,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     for (int r = 0; r < 4; ++r) sm_o[wave][16 * t + 4 * grp + r][col] = acc[t][r];
   __syncthreads();
 
-  // each thread: (head hh, channels) -- 16 heads x D channels
-  const size_t pbase_stride = (size_t)16 * D + 32;
-  float* part_bg = a.part + ((size_t)b * a.Hkv + g) * a.max_parts * pbase_stride;
+  float* pp = a.part + (((size_t)b * a.Hkv + g) * a.max_parts + p) * kPartStride(D);
   for (int e = tid; e < 16 * D; e += 256) {
     const int hh = e / D, d = e % D;
     if (hh >= n_rep) continue;
@@ -496,7 +532,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     if (n_parts == 1) {
       a.o[(size_t)row * a.Hq * D + (size_t)(g * n_rep + hh) * D + d] = to_f16(O / L);
     } else {
-      float* pp = part_bg + (size_t)p * pbase_stride;
       pp[hh * D + d] = O;
       if (d == 0) {
         pp[16 * D + 2 * hh] = M;
@@ -504,31 +539,30 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       }
     }
   }
-  if (n_parts == 1) return;
+}
 
-  // ---- last partition to arrive merges all partitions in order
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int cidx = b * a.Hkv + g;
-    const int prev = atomicAdd(&a.counters[cidx], 1);
-    s_last = prev == n_parts - 1;
-    if (s_last) a.counters[cidx] = 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int e = tid; e < 16 * D; e += 256) {
+// Merges the context partitions of sequences with more than one: one
+// workgroup per (sequence, KV head), partitions combined in order.
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_merge_kernel(DecArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int sidx = a.first_seq + b;
+  const int n_rep = a.Hq / a.Hkv;
+  const int n_blk = cdiv(seq_ctx(a.seq, sidx) + 1, kBlockTokens);
+  const int n_parts = cdiv(n_blk, a.part_blocks);
+  if (n_parts <= 1) return;
+  const int row = seq_row(a.seq, sidx);
+  const float* base = a.part + ((size_t)b * a.Hkv + g) * a.max_parts * kPartStride(D);
+  for (int e = threadIdx.x; e < n_rep * D; e += 256) {
     const int hh = e / D, d = e % D;
-    if (hh >= n_rep) continue;
     float M = -INFINITY;
-    for (int pp = 0; pp < n_parts; ++pp) M = fmaxf(M, part_bg[pp * pbase_stride + 16 * D + 2 * hh]);
+    for (int q = 0; q < n_parts; ++q) M = fmaxf(M, base[q * kPartStride(D) + 16 * D + 2 * hh]);
     float O = 0.f, L = 0.f;
-    for (int pp = 0; pp < n_parts; ++pp) {
-      const float* q2 = part_bg + pp * pbase_stride;
-      const float f = exp2f(q2[16 * D + 2 * hh] - M);
-      O += q2[hh * D + d] * f;
-      L += q2[16 * D + 2 * hh + 1] * f;
+    for (int q = 0; q < n_parts; ++q) {
+      const float* pq = base + q * kPartStride(D);
+      const float f = exp2f(pq[16 * D + 2 * hh] - M);
+      O += pq[hh * D + d] * f;
+      L += pq[16 * D + 2 * hh + 1] * f;
     }
     a.o[(size_t)row * a.Hq * D + (size_t)(g * n_rep + hh) * D + d] = to_f16(O / L);
   }
@@ -560,24 +594,22 @@ DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len) {
   (void)Hq;
   DecodePlan pl{};
   const int max_blk = cdiv(max_ctx_len, kBlockTokens);
-  // aim for ~2048 workgroups over the longest context
-  const int want_parts = std::max(1, cdiv(2048, std::max(1, batch * Hkv)));
-  int pb = cdiv(max_blk, want_parts);
-  pb = std::max(8, cdiv(pb, 4) * 4);
+  // partitions of 16 blocks (256 tokens): ~4 blocks per wave, and enough
+  // workgroups to fill the chip when contexts are long; short batches split
+  // finer so that there are still a few hundred workgroups
+  int pb = 16;
+  while (pb > 4 && (long)batch * Hkv * cdiv(max_blk, pb) < 1024) pb /= 2;
   pl.part_blocks = pb;
   pl.max_parts = cdiv(max_blk, pb);
-  pl.part_floats = (size_t)batch * Hkv * pl.max_parts * (16 * D + 32);
-  pl.n_counters = batch * Hkv;
+  pl.part_floats = (size_t)batch * Hkv * pl.max_parts * kPartStride(D);
   return pl;
 }
 
 hipError_t attn_decode(const DecodePlan& pl, const void* q, KvPool pool, SeqInfo seq, int first_seq,
-                       int row0, int batch, int Hq, int Hkv, int D, void* o, float* part,
-                       int* counters, hipStream_t s) {
-  (void)row0;
+                       int batch, int Hq, int Hkv, int D, void* o, float* part, hipStream_t s) {
   if (batch == 0) return hipSuccess;
   DecArgs a{(const float*)q, pool, seq, first_seq, Hq, Hkv, pl.part_blocks, pl.max_parts, part,
-            counters, (f16*)o};
+            (f16*)o};
   dim3 grid(pl.max_parts, Hkv, batch);
   if (D == 128) {
     if (pool.u8) attn_decode_kernel<128, true><<<grid, 256, 0, s>>>(a);
@@ -586,6 +618,11 @@ hipError_t attn_decode(const DecodePlan& pl, const void* q, KvPool pool, SeqInfo
     if (pool.u8) attn_decode_kernel<64, true><<<grid, 256, 0, s>>>(a);
     else attn_decode_kernel<64, false><<<grid, 256, 0, s>>>(a);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.max_parts == 1) return e;
+  dim3 mgrid(Hkv, batch);
+  if (D == 128) attn_decode_merge_kernel<128><<<mgrid, 256, 0, s>>>(a);
+  else attn_decode_merge_kernel<64><<<mgrid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

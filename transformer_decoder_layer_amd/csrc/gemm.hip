@@ -21,8 +21,7 @@
 // fp32 rounding (no activation quantisation).
 //
 // Split-K: the K range is cut into `splits` slices; each workgroup writes its
-// fp32 partial tile, and the last workgroup to arrive on a tile (an arrival
-// counter, reset by that workgroup) sums the partials in slice order --
+// fp32 partial tile and a reduction kernel sums the slices in order --
 // deterministic -- and runs the epilogue.
 //
 // Epilogues: bias (QKV projection), residual add (output and down
@@ -37,6 +36,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <cmath>
+
 namespace tdl {
 
 namespace {
@@ -49,31 +50,47 @@ __device__ __forceinline__ int swz(int row, int chunk) {  // offset in bf16 elem
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
-template <int BM, int BN, int WM, int WN, bool Q80, int EPI, typename T>
+typedef __attribute__((address_space(3))) void lds_void;
+
+// DIRECT: operand tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4, no staging registers); each lane fetches the
+// 16-byte chunk that belongs at its fixed LDS slot, so the XOR swizzle is
+// applied on the source side.  Needs K % 64 == 0 and bf16/fp16 weights.
+template <int BM, int BN, int WM, int WN, bool Q80, int EPI, typename T, bool DIRECT>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   typedef typename Mfma<T>::v8 T8;
+  static_assert(!(DIRECT && Q80), "direct loads carry bf16/fp16 weights only");
+  constexpr int NW = WM * WN;
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int A_CHUNKS = BM * BK / 8;            // 16-byte chunks per A tile
   constexpr int B_CHUNKS = Q80 ? BN * BK / 16 : BN * BK / 8;  // global chunks
-  constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
-  constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
+  constexpr int A_PER_T = DIRECT ? 1 : (A_CHUNKS + NT - 1) / NT;
+  constexpr int B_PER_T = DIRECT ? 1 : (B_CHUNKS + NT - 1) / NT;
   static_assert(FM >= 1 && FN >= 1, "wave tile");
   static_assert(EPI != EPI_SILU_GATE || (WTN % 32) == 0, "SiLU-gate needs 32-column wave tiles");
 
   __shared__ __attribute__((aligned(16))) T As[2][BM * BK];
   __shared__ __attribute__((aligned(16))) T Bs[2][BN * BK];
   __shared__ float Ss[Q80 ? 2 : 1][Q80 ? BN * 2 : 1];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
+  const int col_l = lane & 15;
 
-  // ---- tile coordinates: grouped ordering (8 M-tiles share B panels)
+  // ---- tile coordinates.  Workgroups are dispatched round-robin over the 8
+  // XCDs (each with its own L2); remap so that consecutive logical ids run on
+  // one XCD, then walk tiles in groups of 8 M-tiles sharing a B panel.
   const int tiles_m = cdiv(p.M, BM), tiles_n = cdiv(p.N, BN);
-  const int split = blockIdx.x % p.splits;
-  const int tile = blockIdx.x / p.splits;
+  int bid = blockIdx.x;
+  {
+    const int nwg = gridDim.x, per = nwg / 8, rem = nwg % 8;
+    const int xcd = bid % 8, slot = bid / 8;
+    bid = xcd * per + min(xcd, rem) + slot;
+  }
+  const int split = bid % p.splits;
+  const int tile = bid / p.splits;
   constexpr int GROUP = 8;
   const int group_size = GROUP * tiles_n;
   const int gidx = tile / group_size;
@@ -147,6 +164,28 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
     }
   };
 
+  // direct path: instruction i of a tile fills LDS rows 8i .. 8i+7 (1 KB);
+  // lane L lands at row 8i + L/8, physical chunk L%8 = logical chunk ^ (row&7)
+  auto issue_tile = [&](int kt, int buf) {
+    const int k0 = kt * BK;
+    const int r8 = lane >> 3, pc = lane & 7;
+#pragma unroll
+    for (int i = wave; i < BM / 8; i += NW) {
+      const int row = i * 8 + r8;
+      const int grow = min(m0 + row, p.M - 1);  // rows past M are computed, never stored
+      const T* src = A + (size_t)grow * p.lda + k0 + ((pc ^ (row & 7)) << 3);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&As[buf][i * 512], 16, 0, 0);
+    }
+    const T* __restrict__ B = (const T*)p.B;
+#pragma unroll
+    for (int i = wave; i < BN / 8; i += NW) {
+      const int row = i * 8 + r8;
+      const int grow = min(n0 + row, p.N - 1);
+      const T* src = B + (size_t)grow * p.ldb + k0 + ((pc ^ (row & 7)) << 3);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&Bs[buf][i * 512], 16, 0, 0);
+    }
+  };
+
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
@@ -197,158 +236,221 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (kt0 < kt1) {
-    load_tile(kt0);
-    store_tile(0);
+    if constexpr (DIRECT) {
+      issue_tile(kt0, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      load_tile(kt0);
+      store_tile(0);
+    }
   }
   __syncthreads();
 
   for (int kt = kt0; kt < kt1; ++kt) {
     const int cur = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
-    if (more) load_tile(kt + 1);
+    if constexpr (DIRECT) {
+      if (more) issue_tile(kt + 1, cur ^ 1);
+    } else {
+      if (more) load_tile(kt + 1);
+    }
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
-      T8 af[FM], bfr[FN];
+      // all A fragments of the wave tile, then one B fragment at a time
+      T8 af[FM];
       const int ch = kk * 4 + (lane >> 4);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
         af[i] = *(const T8*)(&As[cur][swz(wm * WTM + i * 16 + (lane & 15), ch)]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *(const T8*)(&Bs[cur][swz(wn * WTN + j * 16 + (lane & 15), ch)]);
-      if constexpr (!Q80) {
+      for (int j = 0; j < FN; ++j) {
+        const T8 bfr = *(const T8*)(&Bs[cur][swz(wn * WTN + j * 16 + (lane & 15), ch)]);
+        if constexpr (!Q80) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<T>::mma(af[i], bfr[j], acc[i][j]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
+          for (int i = 0; i < FM; ++i) acc[i][j] = Mfma<T>::mma(af[i], bfr, acc[i][j]);
+        } else {
           const float sc = Ss[cur][(wn * WTN + j * 16 + (lane & 15)) * 2 + kk];
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
-            const f32x4 t = Mfma<T>::mma(af[i], bfr[j], f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 t = Mfma<T>::mma(af[i], bfr, f32x4{0.f, 0.f, 0.f, 0.f});
             acc[i][j] += t * sc;
           }
         }
       }
     }
-    if (more) store_tile(cur ^ 1);
+    if constexpr (DIRECT) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS fills of the next tile
+    } else {
+      if (more) store_tile(cur ^ 1);
+    }
     __syncthreads();
   }
 
-  // ---- split-K: publish the partial tile; the last arrival reduces
-  if (p.splits > 1) {
-    constexpr int ACC = FM * FN * 4;
-    const int tile_id = tm * tiles_n + tn;
-    float* base = p.ws + (size_t)tile_id * p.splits * ACC * NT;
-    {
-      float* mine = base + (size_t)split * ACC * NT;
+  // ---- epilogue.  v[i][j][r] = C[m0 + wm*WTM + i*16 + 4*(lane/16) + r]
+  //                                [n0 + wn*WTN + j*16 + lane%16]
+  auto epilogue = [&](const f32x4 (&v)[FM][FN]) {
+    const int col = lane & 15;
+    const int rbase = m0 + wm * WTM + 4 * (lane >> 4);
+    if constexpr (EPI == EPI_SILU_GATE) {
+      bf16* __restrict__ C = (bf16*)p.C;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int jp = 0; jp < FN / 2; ++jp) {
+        const int ng = n0 + wn * WTN + jp * 32;  // first gate column of the pair
+        const int jcol = ng / 2 + col;           // output column
+        if (ng + col >= p.N) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mine[((i * FN + j) * 4 + r) * NT + tid] = acc[i][j][r];
+          for (int r = 0; r < 4; ++r) {
+            const int m = rbase + i * 16 + r;
+            if (m < p.M) {
+              const float g = v[i][2 * jp][r], u = v[i][2 * jp + 1][r];
+              C[(size_t)m * p.ldc + jcol] = f32_to_bf16(silu_f(g) * u);
+            }
+          }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * WTN + j * 16 + col;
+        if (n >= p.N) continue;
+        float bias = 0.f;
+        if constexpr (EPI == EPI_BIAS_F32)
+          if (p.bias) bias = p.bias[n];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = rbase + i * 16 + r;
+            if (m >= p.M) continue;
+            const float val = v[i][j][r];
+            if constexpr (EPI == EPI_BIAS_F32) {
+              ((float*)p.C)[(size_t)m * p.ldc + n] = val + bias;
+            } else if constexpr (EPI == EPI_RESID_F32) {
+              const float res = bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
+              ((float*)p.C)[(size_t)m * p.ldc + n] = val + res;
+            } else {
+              const float res = ((const float*)p.resid)[(size_t)m * p.ldr + n];
+              ((bf16*)p.C)[(size_t)m * p.ldc + n] = f32_to_bf16(val + res);
+            }
+          }
+      }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int prev = atomicAdd(&p.counters[tile_id], 1);
-      s_last = (prev == p.splits - 1);
-      if (s_last) p.counters[tile_id] = 0;  // ready for the next call
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+  };
+
+  if (p.splits == 1) {
+    epilogue(acc);
+    return;
+  }
+  // ---- split-K: this slice's fp32 partial tile goes to ws[split][M][N]; a
+  // second kernel sums the slices in order and applies the epilogue (no
+  // cross-workgroup handshake, which would need device-wide L2 write-backs
+  // on a multi-XCD part).
+  float* part = p.ws + (size_t)split * p.M * p.N;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + wn * WTN + j * 16 + col_l;
+    if (n >= p.N) continue;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.splits; ++s) {
-      const float* part = base + (size_t)s * ACC * NT;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] += part[((i * FN + j) * 4 + r) * NT + tid];
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + r;
+        if (m < p.M) part[(size_t)m * p.N + n] = acc[i][j][r];
+      }
   }
+}
 
-  // ---- epilogue.  acc[i][j][r] = C[m0 + wm*WTM + i*16 + 4*(lane/16) + r]
-  //                                  [n0 + wn*WTN + j*16 + lane%16]
-  const int col = lane & 15;
-  const int rbase = m0 + wm * WTM + 4 * (lane >> 4);
+// Sum of the split-K slices in slice order, then the epilogue; one thread per
+// 4 consecutive output columns (per gate/up pair for the SiLU-gate form).
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
+  const int Nout = EPI == EPI_SILU_GATE ? p.N / 2 : p.N;
+  const int cols4 = Nout / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.M * cols4) return;
+  const int m = (int)(idx / cols4), c = (int)(idx % cols4) * 4;
+  const size_t slice = (size_t)p.M * p.N;
+  float out[4];
   if constexpr (EPI == EPI_SILU_GATE) {
-    bf16* __restrict__ C = (bf16*)p.C;
-#pragma unroll
-    for (int jp = 0; jp < FN / 2; ++jp) {
-      const int ng = n0 + wn * WTN + jp * 32;  // first gate column of the pair
-      const int jcol = ng / 2 + col;           // output column
-      if (ng + col >= p.N) continue;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = rbase + i * 16 + r;
-          if (m < p.M) {
-            const float g = acc[i][2 * jp][r], u = acc[i][2 * jp + 1][r];
-            C[(size_t)m * p.ldc + jcol] = f32_to_bf16(silu_f(g) * u);
-          }
-        }
+    // output column j -> gate column 32*(j/16) + j%16, up column +16
+    const int ng = 32 * (c / 16) + (c % 16);
+    float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.splits; ++s) {
+      const float4 a = *(const float4*)(p.ws + s * slice + (size_t)m * p.N + ng);
+      const float4 b = *(const float4*)(p.ws + s * slice + (size_t)m * p.N + ng + 16);
+      g[0] += a.x; g[1] += a.y; g[2] += a.z; g[3] += a.w;
+      u[0] += b.x; u[1] += b.y; u[2] += b.z; u[3] += b.w;
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = silu_f(g[e]) * u[e];
+    bf16* C = (bf16*)p.C + (size_t)m * p.ldc + c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) C[e] = f32_to_bf16(out[e]);
   } else {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.splits; ++s) {
+      const float4 a = *(const float4*)(p.ws + s * slice + (size_t)m * p.N + c);
+      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * WTN + j * 16 + col;
-      if (n >= p.N) continue;
-      float bias = 0.f;
-      if constexpr (EPI == EPI_BIAS_F32)
-        if (p.bias) bias = p.bias[n];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = rbase + i * 16 + r;
-          if (m >= p.M) continue;
-          const float v = acc[i][j][r];
-          if constexpr (EPI == EPI_BIAS_F32) {
-            ((float*)p.C)[(size_t)m * p.ldc + n] = v + bias;
-          } else if constexpr (EPI == EPI_RESID_F32) {
-            const float res = bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
-            ((float*)p.C)[(size_t)m * p.ldc + n] = v + res;
-          } else {
-            const float res = ((const float*)p.resid)[(size_t)m * p.ldr + n];
-            ((bf16*)p.C)[(size_t)m * p.ldc + n] = f32_to_bf16(v + res);
-          }
-        }
+    for (int e = 0; e < 4; ++e) {
+      const int n = c + e;
+      if constexpr (EPI == EPI_BIAS_F32) {
+        ((float*)p.C)[(size_t)m * p.ldc + n] = v[e] + (p.bias ? p.bias[n] : 0.f);
+      } else if constexpr (EPI == EPI_RESID_F32) {
+        ((float*)p.C)[(size_t)m * p.ldc + n] =
+            v[e] + bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
+      } else {
+        ((bf16*)p.C)[(size_t)m * p.ldc + n] =
+            f32_to_bf16(v[e] + ((const float*)p.resid)[(size_t)m * p.ldr + n]);
+      }
     }
   }
 }
 
 struct Cfg {
-  int BM, BN, NT;
+  int BM, BN;
+  float eff;  // relative per-tile efficiency, for the planner
 };
-// cfg 0: 128x128 (2x2 waves of 64x64) for many rows;
-// cfg 1: 64x128 (1x4 waves of 64x32) for decode-sized M;
-// cfg 2: 128x128 (1x4 waves of 128x32) for M in (64, 128].
-constexpr Cfg kCfgs[3] = {{128, 128, 256}, {64, 128, 256}, {128, 128, 256}};
+// cfg 0: 256x256 (2x4 waves of 128x64);  cfg 1: 256x224 (4x2 waves of
+// 64x112: N = 3584 splits into 16 tiles);  cfg 2: 128x128 (2x2 waves of
+// 64x64);  cfg 3: 64x128 (1x4 waves of 64x32) and cfg 4: 128x128 (1x4 waves
+// of 128x32) for decode-sized M.  Eight-wave tiles keep two waves per SIMD,
+// each with at most 128 accumulators (AGPRs).
+constexpr int kNumCfgs = 5;
+constexpr Cfg kCfgs[kNumCfgs] = {{256, 256, 1.0f}, {256, 224, 0.97f}, {128, 128, 0.55f},
+                                 {64, 128, 0.35f}, {128, 128, 0.5f}};
 
-template <bool Q80, int EPI, typename T>
-hipError_t launch_cfg(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
+template <bool Q80, int EPI, typename T, bool DIRECT>
+hipError_t launch_cfg2(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
   switch (cfg) {
     case 0:
-      gemm_kernel<128, 128, 2, 2, Q80, EPI, T><<<grid, 256, 0, s>>>(a);
+      gemm_kernel<256, 256, 2, 4, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
       break;
     case 1:
-      gemm_kernel<64, 128, 1, 4, Q80, EPI, T><<<grid, 256, 0, s>>>(a);
+      if constexpr (EPI != EPI_SILU_GATE)
+        gemm_kernel<256, 224, 4, 2, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
+      break;
+    case 2:
+      gemm_kernel<128, 128, 2, 2, Q80, EPI, T, DIRECT><<<grid, 256, 0, s>>>(a);
+      break;
+    case 3:
+      gemm_kernel<64, 128, 1, 4, Q80, EPI, T, DIRECT><<<grid, 256, 0, s>>>(a);
       break;
     default:
-      gemm_kernel<128, 128, 1, 4, Q80, EPI, T><<<grid, 256, 0, s>>>(a);
+      gemm_kernel<128, 128, 1, 4, Q80, EPI, T, DIRECT><<<grid, 256, 0, s>>>(a);
       break;
   }
   return hipGetLastError();
+}
+
+template <bool Q80, int EPI, typename T>
+hipError_t launch_cfg(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
+  if constexpr (!Q80) {
+    if (a.K % BK == 0) return launch_cfg2<Q80, EPI, T, true>(cfg, grid, a, s);
+  }
+  return launch_cfg2<Q80, EPI, T, false>(cfg, grid, a, s);
 }
 
 // The operand type follows the epilogue: the down projection (residual into
@@ -365,30 +467,60 @@ hipError_t launch_epi(int cfg, int grid, int epi, const GemmArgs& a, hipStream_t
 
 }  // namespace
 
+// Chooses the tile configuration and split-K factor with the lowest estimated
+// time: rounds of workgroups over the 256 CUs times the per-workgroup work,
+// divided by the configuration's relative efficiency.
 GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
-  (void)q80;
-  (void)epi;
-  GemmPlan pl{};
-  pl.cfg = M <= 64 ? 1 : (M <= 128 ? 2 : 0);
-  const Cfg c = kCfgs[pl.cfg];
-  const int tiles = cdiv(M, c.BM) * cdiv(N, c.BN);
+  constexpr int kCUs = 256;
   const int KT = cdiv(K, BK);
-  // enough workgroups to cover the 256 CUs about twice, each slice >= 4 k-tiles
-  int splits = 1;
-  while (tiles * splits < 512 && KT / (splits * 2) >= 4) splits *= 2;
-  pl.k_tiles_per_split = cdiv(KT, splits);
-  pl.splits = cdiv(KT, pl.k_tiles_per_split);
-  pl.grid = tiles * pl.splits;
-  pl.ws_floats = pl.splits > 1 ? (size_t)tiles * pl.splits * c.BM * c.BN : 0;
-  pl.n_counters = pl.splits > 1 ? tiles : 0;
-  return pl;
+  GemmPlan best{};
+  double best_cost = 1e300;
+  for (int cfg = 0; cfg < kNumCfgs; ++cfg) {
+    const Cfg c = kCfgs[cfg];
+    if (cfg == 1 && (epi == EPI_SILU_GATE || N % 224 != 0)) continue;
+    if (q80 && cfg <= 1) continue;        // Q8_0 staging needs the register path
+    if (cfg >= 3 && M > 128) continue;   // the decode shapes only
+    if (cfg == 3 && M > 64) continue;
+    const int tiles = cdiv(M, c.BM) * cdiv(N, c.BN);
+    for (int splits = 1; splits <= 16; splits *= 2) {
+      if (splits > 1 && KT / splits < 4) break;
+      const int kps = cdiv(KT, splits);
+      const int sp = cdiv(KT, kps);
+      const int wgs = tiles * sp;
+      const double rounds = std::ceil((double)wgs / kCUs);
+      double cost = rounds * (double)c.BM * c.BN * kps / c.eff;
+      // split-K: the partial slices make a round trip through memory and the
+      // reduction is a second launch (expressed in the same MAC-time units)
+      if (sp > 1) cost += 2.0 * sp * (double)M * N * 4.0 * 40.0 / kCUs + 4.0e5;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best.cfg = cfg;
+        best.splits = sp;
+        best.k_tiles_per_split = kps;
+        best.grid = wgs;
+        best.ws_floats = sp > 1 ? (size_t)sp * M * N : 0;
+      }
+    }
+  }
+  return best;
 }
 
 hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, bool q80, int epi, hipStream_t s) {
   a.splits = pl.splits;
   a.k_tiles_per_split = pl.k_tiles_per_split;
-  if (q80) return launch_epi<true>(pl.cfg, pl.grid, epi, a, s);
-  return launch_epi<false>(pl.cfg, pl.grid, epi, a, s);
+  const hipError_t e = q80 ? launch_epi<true>(pl.cfg, pl.grid, epi, a, s)
+                           : launch_epi<false>(pl.cfg, pl.grid, epi, a, s);
+  if (e != hipSuccess || pl.splits == 1) return e;
+  const int Nout = epi == EPI_SILU_GATE ? a.N / 2 : a.N;
+  const int64_t threads = (int64_t)a.M * (Nout / 4);
+  const int blocks = (int)((threads + 255) / 256);
+  switch (epi) {
+    case EPI_BIAS_F32: splitk_reduce_kernel<EPI_BIAS_F32><<<blocks, 256, 0, s>>>(a); break;
+    case EPI_RESID_F32: splitk_reduce_kernel<EPI_RESID_F32><<<blocks, 256, 0, s>>>(a); break;
+    case EPI_RESID_BF16: splitk_reduce_kernel<EPI_RESID_BF16><<<blocks, 256, 0, s>>>(a); break;
+    default: splitk_reduce_kernel<EPI_SILU_GATE><<<blocks, 256, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace tdl

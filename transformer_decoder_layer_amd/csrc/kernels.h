@@ -31,21 +31,20 @@ struct GemmArgs {
   int ldr;
   void* C;
   int ldc;
-  float* ws;         // split-K partial tiles
-  int* counters;     // split-K arrival counters (zero between calls)
+  float* ws;         // split-K partial slices [splits][M][N] fp32
   int splits;
   int k_tiles_per_split;
 };
 
 // Picks a tile configuration and split count for (M, N, K) and returns the
-// workspace floats / counters it needs (for sizing at create time).
+// workspace floats it needs (for sizing at create time).  With splits > 1 a
+// reduction kernel follows the GEMM.
 struct GemmPlan {
   int cfg;          // tile configuration id
   int splits;
   int k_tiles_per_split;
   int grid;
   size_t ws_floats;
-  int n_counters;
 };
 GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi);
 hipError_t gemm_launch(const GemmPlan& plan, GemmArgs a, bool q80, int epi, hipStream_t s);
@@ -120,17 +119,17 @@ hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, int n_prefill, 
                         int Hq, int Hkv, int D, void* o, hipStream_t s);
 
 // Paged decode attention for decode sequences first_seq .. first_seq+batch-1
-// (one query row each, rows row0 + b).  part_* is the split-context
-// workspace; counters zero between calls.
+// (one query row each).  Each sequence's context is cut into partitions of
+// part_blocks blocks; `part` holds the partitions' (O, m, l) and a merge
+// kernel combines them.
 struct DecodePlan {
   int part_blocks;
   int max_parts;
   size_t part_floats;
-  int n_counters;
 };
 DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len);
 hipError_t attn_decode(const DecodePlan& plan, const void* q, KvPool pool, SeqInfo seq,
-                       int first_seq, int row0, int batch, int Hq, int Hkv, int D, void* o,
-                       float* part, int* counters, hipStream_t s);
+                       int first_seq, int batch, int Hq, int Hkv, int D, void* o, float* part,
+                       hipStream_t s);
 
 }  // namespace tdl
