@@ -1,10 +1,12 @@
 """Test harness: runs one workload call through the C-ABI (GPU) and through
 the oracle (CPU) on the same seeded inputs, and measures the difference.
 
-Tolerance (bf16 path): max |y - r| <= 2e-2 * max |r| and
-sum |y - r| / sum |r| <= 5e-3, applied to the layer output y and to the
-branch delta y - x (the residual would otherwise hide errors in the
-attention and MLP branches)."""
+Tolerance (the bf16 bar): max |y - r| <= 2e-2 * max |r| and
+sum |y - r| / sum |r| <= 5e-3 (a normalised L1; a per-element ratio is
+ill-conditioned near zero).  The GPU tests apply it to the layer output y and
+to the stage buffers (RMSNorm output, rotated q, attention output, the
+attention branch h - x, the SwiGLU product), so a residual add cannot hide an
+error in a branch."""
 from __future__ import annotations
 
 import dataclasses
@@ -46,7 +48,9 @@ def compare(y, ref) -> Err:
 
 # ------------------------------------------------------------------ oracle
 
-def oracle_cache(inp: synth.LayerInputs) -> Optional[oracle.PagedCache]:
+def oracle_cache(inp: synth.LayerInputs, seqs=None) -> Optional[oracle.PagedCache]:
+    """The oracle's cache holding the already-cached tokens of the chosen
+    sequences (all by default).  u8 parameters come from every cached token."""
     wl, shape, b = inp.workload, inp.workload.shape, inp.batch
     if wl.kv_dtype == "none":
         return None
@@ -57,22 +61,34 @@ def oracle_cache(inp: synth.LayerInputs) -> Optional[oracle.PagedCache]:
         vp = oracle.kv_calibrate(inp.cache_v)
         cache = oracle.PagedCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, "u8", kp, vp)
     if inp.cache_k is not None:
-        oracle.fill_cache(cache, b.table, b.ctx_len, inp.cache_k, inp.cache_v)
+        seqs = range(b.n_seqs) if seqs is None else seqs
+        off = np.concatenate([[0], np.cumsum(b.ctx_len)])
+        for i in seqs:
+            for t in range(int(b.ctx_len[i])):
+                cache.write(b.table[i], t, inp.cache_k[off[i] + t], inp.cache_v[off[i] + t])
     return cache
 
 
-def run_oracle(inp: synth.LayerInputs, seqs: Optional[List[int]] = None, want_stages=False):
+def run_oracle(inp: synth.LayerInputs, seqs: Optional[List[int]] = None, want_stages=False,
+               rows_out=None):
     """Oracle output rows of the chosen sequences (all by default), in row
-    order, with their row indices."""
+    order, with their row indices.  ``rows_out`` (absolute row indices within
+    the chosen sequences) restricts the outputs to a sample of rows."""
     shape, b = inp.workload.shape, inp.batch
     W = oracle.expand_weights(shape, inp.weights)
-    cache = oracle_cache(inp)
     seqs = list(range(b.n_seqs)) if seqs is None else list(seqs)
+    cache = oracle_cache(inp, seqs)
     rows = np.concatenate([np.arange(b.q_start[i], b.q_start[i] + b.q_len[i]) for i in seqs])
     q_len = b.q_len[seqs]
     q_start = np.concatenate([[0], np.cumsum(q_len)[:-1]])
+    sel = None
+    if rows_out is not None:
+        pos_of = {int(r): k for k, r in enumerate(rows)}
+        sel = np.array(sorted(pos_of[int(r)] for r in rows_out))
     out = oracle.layer_forward(shape, W, inp.x[rows], q_start, q_len, b.ctx_len[seqs],
-                               b.table[seqs], cache, want_stages=want_stages)
+                               b.table[seqs], cache, want_stages=want_stages, rows_out=sel)
+    if sel is not None:
+        rows = rows[sel]
     return rows, out, cache
 
 
@@ -154,11 +170,3 @@ def run_gpu(inp: synth.LayerInputs, **kw) -> GpuRun:
     torch.cuda.synchronize()
     y = t["y"].float().cpu().numpy()
     return GpuRun(y, layer, kv, t)
-
-
-def assert_close(y, ref, x, what=""):
-    e = compare(y, ref)
-    ed = compare(np.asarray(y, np.float64) - x, np.asarray(ref, np.float64) - x)
-    assert e.ok, f"{what} output: {e}"
-    assert ed.ok, f"{what} branch delta y-x: {ed}"
-    return e, ed

@@ -1,0 +1,157 @@
+"""Bit-exact GPU checks through the C-ABI: cache slot placement, u8
+calibration and codes against the oracle's quantiser on identical fp32
+inputs, paged-table independence, and run-to-run determinism."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from harness import gpu_call, gpu_setup
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _write_setup(dtype, n_blocks=12, Hkv=2, D=64, lens=(20, 33), starts=(0, 5), seed=0):
+    import torch
+    import transformer_decoder_layer_amd as tdl
+    rng = np.random.default_rng(seed)
+    totals = [s + n for s, n in zip(starts, lens)]
+    table = synth.random_tables(rng, totals, n_blocks=n_blocks)
+    n = sum(lens)
+    k = (rng.standard_normal((n, Hkv, D)) * rng.uniform(0.2, 3, (1, Hkv, D))).astype(np.float32)
+    v = (rng.standard_normal((n, Hkv, D)) * rng.uniform(0.2, 3, (1, Hkv, D)) + 0.5).astype(np.float32)
+    kv = tdl.KvCache(n_blocks, Hkv, D, dtype)
+    kv.memory.fill_(0x5A)                      # sentinel in every byte
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    cu = dev(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    st = dev(np.array(starts, np.int32))
+    return kv, dev, cu, st, dev(table), table, k, v
+
+
+def _slots(table, lens, starts):
+    out = []
+    for i, (n, s0) in enumerate(zip(lens, starts)):
+        for t in range(n):
+            out.append(oracle.PagedCache.location(table[i], s0 + t))
+    return out
+
+
+def test_bf16_slot_writes_exact_and_nothing_else_changes():
+    import torch
+    lens, starts = (20, 33), (0, 5)
+    kv, dev, cu, st, table_d, table, k, v = _write_setup("bf16", lens=lens, starts=starts)
+    before = kv.memory.clone()
+    kv.write(cu, st, table_d, dev(k), dev(v))
+    torch.cuda.synchronize()
+    kt, vt = kv.tensors()
+    kb = kt.view(torch.int16).cpu().numpy()
+    vb = vt.view(torch.int16).cpu().numpy()
+    # expected: the oracle's bf16 rounding of each value, at (table[p/16], p%16)
+    want_k = np.zeros(kb.shape, np.int64)
+    want_v = np.zeros(vb.shape, np.int64)
+    sel_k = np.zeros(kb.shape, bool)
+    sel_v = np.zeros(vb.shape, bool)
+    bits = lambda a: (torch.from_numpy(oracle.round_bf16(a).astype(np.float32)).view(torch.int32).numpy()
+                      >> 16) & 0xffff
+    for r, (blk, off) in enumerate(_slots(table, lens, starts)):
+        want_k[blk, :, off, :] = bits(k[r])
+        want_v[blk, :, :, off] = bits(v[r])
+        sel_k[blk, :, off, :] = True
+        sel_v[blk, :, :, off] = True
+    assert np.array_equal(kb[sel_k].astype(np.int64) & 0xffff, want_k[sel_k])
+    assert np.array_equal(vb[sel_v].astype(np.int64) & 0xffff, want_v[sel_v])
+    # every byte outside the written slots is still the sentinel
+    mem = kv.memory.cpu().numpy()
+    ref = before.cpu().numpy()
+    view = kv.view()
+    base = kv.memory.data_ptr()
+    touched = np.zeros(mem.shape, bool)
+    ks, vs = list(view.k_strides), list(view.v_strides)
+    # strides are given for (block, head, slot, d); the V tensor's axes are
+    # (block, head, d, slot)
+    for arr, sel, ptr, strides in ((kb, sel_k, view.k_pool, ks),
+                                   (vb, sel_v, view.v_pool, [vs[0], vs[1], vs[3], vs[2]])):
+        idx = np.argwhere(sel)
+        off = (idx * np.array(strides)).sum(1) * 2 + (ptr - base)
+        touched[off] = touched[off + 1] = True
+    assert np.array_equal(mem[~touched], ref[~touched])
+    assert touched.sum() == 2 * 2 * sum(lens) * 2 * 64
+
+
+def test_u8_calibration_and_codes_match_oracle_quantiser():
+    import torch
+    lens, starts = (300, 477), (0, 0)
+    kv, dev, cu, st, table_d, table, k, v = _write_setup("u8", n_blocks=60, lens=lens, starts=starts,
+                                                         seed=3)
+    kv.calibrate(dev(k), dev(v))
+    kv.write(cu, st, table_d, dev(k), dev(v))
+    torch.cuda.synchronize()
+    kt, vt, ks, kz, vs, vz = kv.tensors()
+    sk, zk = oracle.kv_calibrate(k)
+    sv, zv = oracle.kv_calibrate(v)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), sk.reshape(-1).view(np.uint32))
+    assert np.array_equal(kz.cpu().numpy(), zk.reshape(-1))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), sv.reshape(-1).view(np.uint32))
+    assert np.array_equal(vz.cpu().numpy(), zv.reshape(-1))
+    kc, vc = kt.cpu().numpy(), vt.cpu().numpy()
+    qk, qv = oracle.kv_quantize(k, sk, zk), oracle.kv_quantize(v, sv, zv)
+    for r, (blk, off) in enumerate(_slots(table, lens, starts)):
+        assert np.array_equal(kc[blk, :, off, :], qk[r]), r
+        assert np.array_equal(vc[blk, :, :, off], qv[r]), r
+
+
+def _tiny_decode_inputs(kv_dtype, seed, table_seed):
+    shape = dataclasses.replace(synth.TINY, qkv_bias=False, qk_norm=True, weight_dtype="bf16")
+    wl = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=shape, kv_dtype=kv_dtype)
+    inp = synth.make_inputs(wl, seed=seed, decode_batch=6, decode_ctx=[5, 16, 17, 90, 300, 1025])
+    # the same logical cache under another physical placement
+    rng = np.random.default_rng(table_seed)
+    totals = (inp.batch.ctx_len + 1).tolist()
+    b = dataclasses.replace(inp.batch, table=synth.random_tables(rng, totals, n_blocks=inp.batch.n_blocks))
+    ident = dataclasses.replace(inp.batch, table=synth.random_tables(
+        np.random.default_rng(0), totals, n_blocks=inp.batch.n_blocks))
+    ident.table[:] = -1
+    pos = 0
+    for i, t in enumerate(totals):
+        nb = -(-t // 16)
+        ident.table[i, :nb] = np.arange(pos, pos + nb)
+        pos += nb
+    return dataclasses.replace(inp, batch=b), dataclasses.replace(inp, batch=ident)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "u8"])
+def test_paged_decode_independent_of_block_placement(kv_dtype):
+    import torch
+    a, b = _tiny_decode_inputs(kv_dtype, seed=7, table_seed=11)
+    ys = []
+    for inp in (a, b):
+        layer, kv, t = gpu_setup(inp)
+        gpu_call(inp, layer, kv, t)
+        torch.cuda.synchronize()
+        ys.append(t["y"].view(torch.int16).cpu().numpy())
+    assert np.array_equal(ys[0], ys[1])
+
+
+def test_run_to_run_determinism():
+    # the Qwen2.5 shape at 512 rows uses split-K reductions; decode uses
+    # context partitions and their merge
+    import torch
+    for wl, kw in ((synth.WORKLOADS["qwen25_prefill_512"], {}),
+                   (synth.WORKLOADS["qwen25_decode_b64"], dict(decode_batch=16))):
+        inp = synth.make_inputs(wl, seed=1, **kw)
+        layer, kv, t = gpu_setup(inp)
+        outs = []
+        for _ in range(3):
+            gpu_call(inp, layer, kv, t)
+            torch.cuda.synchronize()
+            outs.append(t["y"].view(torch.int16).cpu().numpy().copy())
+        assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2]), wl.name

@@ -472,6 +472,10 @@ hipError_t launch_epi(int cfg, int grid, int epi, const GemmArgs& a, hipStream_t
 // divided by the configuration's relative efficiency.
 GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
   constexpr int kCUs = 256;
+  {
+    GemmPlan sk{};
+    if (skinny_plan(M, N, K, &sk)) return sk;
+  }
   const int KT = cdiv(K, BK);
   GemmPlan best{};
   double best_cost = 1e300;
@@ -508,8 +512,9 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
 hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, bool q80, int epi, hipStream_t s) {
   a.splits = pl.splits;
   a.k_tiles_per_split = pl.k_tiles_per_split;
-  const hipError_t e = q80 ? launch_epi<true>(pl.cfg, pl.grid, epi, a, s)
-                           : launch_epi<false>(pl.cfg, pl.grid, epi, a, s);
+  const hipError_t e = pl.cfg >= 10 ? gemm_skinny_launch(pl, a, q80, epi, s)
+                       : q80          ? launch_epi<true>(pl.cfg, pl.grid, epi, a, s)
+                                      : launch_epi<false>(pl.cfg, pl.grid, epi, a, s);
   if (e != hipSuccess || pl.splits == 1) return e;
   const int Nout = epi == EPI_SILU_GATE ? a.N / 2 : a.N;
   const int64_t threads = (int64_t)a.M * (Nout / 4);
