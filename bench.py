@@ -47,6 +47,9 @@ def parse():
                     help="prompt tokens the oracle runs for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 512 MiB device-to-device copy (a known byte count that "
+                         "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -201,6 +204,13 @@ def main():
                "sample": f"float64 numpy oracle, one {n}-token causal prefill of the same layer and "
                          f"weights ({c1 - c0:.1f} s)"}
         log(f"cpu baseline: {cpu['value']} tokens/s on {threads} threads")
+
+    if args.copy_probe:
+        src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 536870912 bytes read and written")
 
     out = {
         "metric": "layer prefill tokens/s + paged decode us/step; % of MFMA / HBM roofline",

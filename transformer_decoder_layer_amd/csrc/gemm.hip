@@ -71,8 +71,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   static_assert(FM >= 1 && FN >= 1, "wave tile");
   static_assert(EPI != EPI_SILU_GATE || (WTN % 32) == 0, "SiLU-gate needs 32-column wave tiles");
 
-  __shared__ __attribute__((aligned(16))) T As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) T Bs[2][BN * BK];
+  // two LDS stages as separate arrays: the direct path selects them
+  // statically, so the compiler can tell an in-flight LDS fill of one stage
+  // from reads of the other and does not wait for the fill
+  __shared__ __attribute__((aligned(16))) T As0[BM * BK];
+  __shared__ __attribute__((aligned(16))) T As1[BM * BK];
+  __shared__ __attribute__((aligned(16))) T Bs0[BN * BK];
+  __shared__ __attribute__((aligned(16))) T Bs1[BN * BK];
   __shared__ float Ss[Q80 ? 2 : 1][Q80 ? BN * 2 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
 
   // direct path: instruction i of a tile fills LDS rows 8i .. 8i+7 (1 KB);
   // lane L lands at row 8i + L/8, physical chunk L%8 = logical chunk ^ (row&7)
-  auto issue_tile = [&](int kt, int buf) {
+  auto issue_tile = [&](int kt, T* Ad, T* Bd) {
     const int k0 = kt * BK;
     const int r8 = lane >> 3, pc = lane & 7;
 #pragma unroll
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
       const int row = i * 8 + r8;
       const int grow = min(m0 + row, p.M - 1);  // rows past M are computed, never stored
       const T* src = A + (size_t)grow * p.lda + k0 + ((pc ^ (row & 7)) << 3);
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&As[buf][i * 512], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&Ad[i * 512], 16, 0, 0);
     }
     const T* __restrict__ B = (const T*)p.B;
 #pragma unroll
@@ -182,17 +187,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
       const int row = i * 8 + r8;
       const int grow = min(n0 + row, p.N - 1);
       const T* src = B + (size_t)grow * p.ldb + k0 + ((pc ^ (row & 7)) << 3);
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&Bs[buf][i * 512], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&Bd[i * 512], 16, 0, 0);
     }
   };
 
   auto store_tile = [&](int buf) {
+    T* Ab = buf ? As1 : As0;
+    T* Bb = buf ? Bs1 : Bs0;
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
       const int c = tid + i * NT;
       if (c < A_CHUNKS) {
         const int r = c / (BK / 8), ch = c % (BK / 8);
-        *(uint4*)(&As[buf][swz(r, ch)]) = ra[i];
+        *(uint4*)(&Ab[swz(r, ch)]) = ra[i];
       }
     }
     if constexpr (!Q80) {
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
         const int c = tid + i * NT;
         if (c < B_CHUNKS) {
           const int r = c / (BK / 8), ch = c % (BK / 8);
-          *(uint4*)(&Bs[buf][swz(r, ch)]) = rb[i];
+          *(uint4*)(&Bb[swz(r, ch)]) = rb[i];
         }
       }
     } else {
@@ -217,8 +224,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
             lo[e] = (T)(float)(int8_t)(w[e >> 2] >> ((e & 3) * 8));
             hi[e] = (T)(float)(int8_t)(w[2 + (e >> 2)] >> ((e & 3) * 8));
           }
-          *(T8*)(&Bs[buf][swz(r, ch)]) = lo;
-          *(T8*)(&Bs[buf][swz(r, ch + 1)]) = hi;
+          *(T8*)(&Bb[swz(r, ch)]) = lo;
+          *(T8*)(&Bb[swz(r, ch + 1)]) = hi;
         }
       }
 #pragma unroll
@@ -235,25 +242,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (kt0 < kt1) {
-    if constexpr (DIRECT) {
-      issue_tile(kt0, 0);
-      __builtin_amdgcn_s_waitcnt(0);
-    } else {
-      load_tile(kt0);
-      store_tile(0);
-    }
-  }
-  __syncthreads();
-
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int cur = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if constexpr (DIRECT) {
-      if (more) issue_tile(kt + 1, cur ^ 1);
-    } else {
-      if (more) load_tile(kt + 1);
-    }
+  // one k-tile of MFMAs from the given LDS stage
+  auto compute = [&](const T* Ab, const T* Bb, int sbuf) {
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       // all A fragments of the wave tile, then one B fragment at a time
@@ -261,15 +251,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
       const int ch = kk * 4 + (lane >> 4);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = *(const T8*)(&As[cur][swz(wm * WTM + i * 16 + (lane & 15), ch)]);
+        af[i] = *(const T8*)(&Ab[swz(wm * WTM + i * 16 + (lane & 15), ch)]);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const T8 bfr = *(const T8*)(&Bs[cur][swz(wn * WTN + j * 16 + (lane & 15), ch)]);
+        const T8 bfr = *(const T8*)(&Bb[swz(wn * WTN + j * 16 + (lane & 15), ch)]);
         if constexpr (!Q80) {
 #pragma unroll
           for (int i = 0; i < FM; ++i) acc[i][j] = Mfma<T>::mma(af[i], bfr, acc[i][j]);
         } else {
-          const float sc = Ss[cur][(wn * WTN + j * 16 + (lane & 15)) * 2 + kk];
+          const float sc = Ss[sbuf][(wn * WTN + j * 16 + (lane & 15)) * 2 + kk];
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
             const f32x4 t = Mfma<T>::mma(af[i], bfr, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -278,12 +268,40 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
         }
       }
     }
-    if constexpr (DIRECT) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS fills of the next tile
-    } else {
-      if (more) store_tile(cur ^ 1);
+  };
+
+  if constexpr (DIRECT) {
+    // stage 0 holds tile kt, stage 1 tile kt+1; the fill of the next tile
+    // runs while this one feeds the MFMAs
+    if (kt0 < kt1) issue_tile(kt0, As0, Bs0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      if (kt + 1 < kt1) issue_tile(kt + 1, As1, Bs1);
+      compute(As0, Bs0, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kt + 1 < kt1) {
+        if (kt + 2 < kt1) issue_tile(kt + 2, As0, Bs0);
+        compute(As1, Bs1, 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  } else {
+    if (kt0 < kt1) {
+      load_tile(kt0);
+      store_tile(0);
     }
     __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int cur = (kt - kt0) & 1;
+      const bool more = kt + 1 < kt1;
+      if (more) load_tile(kt + 1);
+      compute(cur ? As1 : As0, cur ? Bs1 : Bs0, cur);
+      if (more) store_tile(cur ^ 1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue.  v[i][j][r] = C[m0 + wm*WTM + i*16 + 4*(lane/16) + r]
