@@ -94,6 +94,7 @@ struct tdl_layer {
   size_t dec_part_floats = 0;
   void* priv_k = nullptr;  // bf16 pool for calls without a KV cache
   void* priv_v = nullptr;
+  int32_t* priv_table = nullptr;  // identity block table of the private pool
   std::vector<void*> allocs;
   // per-stage timing (layer_profile_enable)
   bool prof_on = false;
@@ -490,6 +491,12 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   const size_t priv_blocks = (size_t)(T + 15) / 16;
   CTRY(dalloc(L, &L->priv_k, priv_blocks * KD * 16 * 2));
   CTRY(dalloc(L, &L->priv_v, priv_blocks * KD * 16 * 2));
+  CTRY(dalloc(L, &L->priv_table, priv_blocks * sizeof(int32_t)));
+  {
+    std::vector<int32_t> ident(priv_blocks);
+    for (size_t b = 0; b < priv_blocks; ++b) ident[b] = (int32_t)b;
+    CHIP(hipMemcpy(L->priv_table, ident.data(), priv_blocks * sizeof(int32_t), hipMemcpyHostToDevice));
+  }
   CHIP(hipStreamSynchronize(st));
   int sat = 0;
   CHIP(hipMemcpy(&sat, n_sat, 4, hipMemcpyDeviceToHost));
@@ -542,7 +549,7 @@ extern "C" tdl_status layer_prefill(tdl_layer* L, tdl_stream stream, const void*
   seq.n_seqs = 1;
   seq.q_len0 = n_tokens;
   seq.ctx0 = start_pos;
-  seq.tables = kv ? block_table : nullptr;
+  seq.tables = kv ? block_table : L->priv_table;
   seq.max_blocks = 0;
   return run_layer(L, st, x, y, n_tokens, seq, pool_of(L, kv), 1, n_tokens, 0, 0, 0);
 }

@@ -96,206 +96,221 @@ __device__ __forceinline__ int vt_off(int d, int unit) {  // unit of 4 bf16
 template <int D, int NREP>
 __global__ __launch_bounds__(NREP * 64) void attn_prefill_kernel(const float* __restrict__ q,
                                                                  KvPool pool, SeqInfo seq, int Hq,
-                                                                 int Hkv, int n_qtiles,
+                                                                 int Hkv, int n_qtiles, int paired,
                                                                  f16* __restrict__ o) {
   __shared__ __attribute__((aligned(16))) PrefillSmem<D> sm;
   constexpr int n_rep = NREP;
   constexpr int nthreads = NREP * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qt = n_qtiles - 1 - blockIdx.x;  // longest tiles first
   const int g = blockIdx.y;
   const int sidx = blockIdx.z;
   const int q_len = seq_qlen(seq, sidx);
-  if (qt * PQ >= q_len) return;
   const int ctx = seq_ctx(seq, sidx);
-  const int row0 = seq_row(seq, sidx) + qt * PQ;
-  const int n_keys = ctx + q_len;                                   // keys in the cache
-  const int last_q = ctx + min(qt * PQ + PQ, q_len) - 1;            // last query position
-  const int n_tiles = cdiv(last_q + 1, PK);
-  const int first_q = ctx + qt * PQ;
+  const int n_keys = ctx + q_len;  // keys in the cache
   const int h = g * n_rep + wave;
   const int ql = lane & 31, G = lane >> 5;
-
-  // Q fragments: B operand of S^T = K Q^T; lane supplies q[ql][16s + 8G .. +7]
-  f16x8 qf[D / 16];
-  {
-    const bool valid = qt * PQ + ql < q_len;
-    const float* qp = q + ((size_t)(row0 + ql) * Hq + h) * D + 8 * G;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      f16x8 v{};
-      if (valid) {
-        const float4 a = *(const float4*)(qp + 16 * s), b = *(const float4*)(qp + 16 * s + 4);
-        v[0] = to_f16(a.x); v[1] = to_f16(a.y); v[2] = to_f16(a.z); v[3] = to_f16(a.w);
-        v[4] = to_f16(b.x); v[5] = to_f16(b.y); v[6] = to_f16(b.z); v[7] = to_f16(b.w);
-      }
-      qf[s] = v;
-    }
-  }
-
-  // tile loader: K blocks (4 KB each for D=128) and V blocks into LDS
-  constexpr int K_CHUNKS = PK * D / 8;   // 16-byte chunks of K per tile
-  constexpr int V_CHUNKS = D * PK / 8;
-  constexpr int MAX_PER_T = (K_CHUNKS + V_CHUNKS + nthreads - 1) / nthreads;
-  uint4 rk[MAX_PER_T];
+  const int nq_seq = cdiv(q_len, PQ);  // this sequence's query tiles
   const bf16* kpool = (const bf16*)pool.k;
   const bf16* vpool = (const bf16*)pool.v;
-  const size_t head_elems = (size_t)kBlockTokens * D;
-
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < MAX_PER_T; ++i) {
-      const int c = tid + i * nthreads;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (c < K_CHUNKS + V_CHUNKS) {
-        const bool isk = c < K_CHUNKS;
-        const int cc = isk ? c : c - K_CHUNKS;
-        // both pools: 16-token block = kBlockTokens*D elements; chunk cc covers
-        // elements [8cc, 8cc+8) of the tile's 4 consecutive logical blocks
-        const int lb = cc / (int)(head_elems / 8);
-        const int within = cc % (int)(head_elems / 8);
-        const int lblk = t * (PK / kBlockTokens) + lb;
-        if (lblk * kBlockTokens < n_keys) {
-          const int phys = seq_block(seq, sidx, lblk);
-          const bf16* src = (isk ? kpool : vpool) + ((size_t)phys * Hkv + g) * head_elems + within * 8;
-          val = *(const uint4*)src;
-          // zero keys past the end of the sequence (unwritten slots)
-          const int base_key = lblk * kBlockTokens;
-          if (base_key + kBlockTokens > n_keys) {
-            uint32_t w[4] = {val.x, val.y, val.z, val.w};
-            if (isk) {
-              const int key = base_key + (within * 8) / D;
-              if (key >= n_keys) w[0] = w[1] = w[2] = w[3] = 0;
-            } else {
-              const int key0 = base_key + (within * 8) % kBlockTokens;  // 8 keys of one d
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (key0 + e >= n_keys) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-            }
-            val = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        }
-      }
-      rk[i] = val;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < MAX_PER_T; ++i) {
-      const int c = tid + i * nthreads;
-      if (c < K_CHUNKS) {
-        const int lb = c / (int)(head_elems / 8);
-        const int within = c % (int)(head_elems / 8);
-        const int key = lb * kBlockTokens + (within * 8) / D;
-        const int chunk = ((within * 8) % D) / 8;
-        const uint4 w = rk[i];
-        *(uint4*)(&sm.k[buf][k_off<D>(key, chunk)]) =
-            make_uint4(bf16pair_to_f16pair(w.x), bf16pair_to_f16pair(w.y),
-                       bf16pair_to_f16pair(w.z), bf16pair_to_f16pair(w.w));
-      } else if (c < K_CHUNKS + V_CHUNKS) {
-        const int cc = c - K_CHUNKS;
-        const int lb = cc / (int)(head_elems / 8);
-        const int within = cc % (int)(head_elems / 8);
-        const int d = (within * 8) / kBlockTokens;
-        const int key0 = lb * kBlockTokens + (within * 8) % kBlockTokens;
-        const int unit = key0 / 4;  // even
-        *(u32x2*)(&sm.vt[buf][vt_off(d, unit)]) =
-            u32x2{bf16pair_to_f16pair(rk[i].x), bf16pair_to_f16pair(rk[i].y)};
-        *(u32x2*)(&sm.vt[buf][vt_off(d, unit + 1)]) =
-            u32x2{bf16pair_to_f16pair(rk[i].z), bf16pair_to_f16pair(rk[i].w)};
-      }
-    }
-  };
-
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  constexpr int head_elems = kBlockTokens * D;
+  constexpr int K_CHUNKS = PK * D / 8;  // 16-byte chunks of K per tile
+  constexpr int V_CHUNKS = D * PK / 8;
+  constexpr int CHUNKS_PER_BLOCK = head_elems / 8;
+  constexpr int MAX_PER_T = (K_CHUNKS + V_CHUNKS + nthreads - 1) / nthreads;
   const float sc = kLog2e * rsqrtf((float)D);
-  const int my_q = first_q + ql;
+  const int* tab = seq.tables + (size_t)sidx * seq.max_blocks;  // never null here
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int cur = t & 1;
-    const bool more = t + 1 < n_tiles;
-    if (more) load_tile(t + 1);
+  // paired mode: workgroup x takes query tiles x and n_qtiles-1-x (equal
+  // causal work per workgroup); otherwise the tiles in longest-first order
+  const int n_items = paired ? 2 : 1;
+  for (int item = 0; item < n_items; ++item) {
+    int qt;
+    if (paired) {
+      qt = item == 0 ? (int)blockIdx.x : n_qtiles - 1 - (int)blockIdx.x;
+      if (item == 1 && qt == (int)blockIdx.x) break;   // odd count: middle tile once
+    } else {
+      qt = n_qtiles - 1 - (int)blockIdx.x;
+    }
+    if (qt >= nq_seq) continue;  // uniform over the workgroup
+    const int row0 = seq_row(seq, sidx) + qt * PQ;
+    const int last_q = ctx + min(qt * PQ + PQ, q_len) - 1;  // last query position
+    const int n_tiles = cdiv(last_q + 1, PK);
+    const int first_q = ctx + qt * PQ;
+    const int my_q = first_q + ql;
 
-    // S^T for 64 keys x 32 queries: two 32-key halves
-    f32x16 st[2];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      st[kh] = f32x16{};
+    // Q fragments: B operand of S^T = K Q^T; lane supplies q[ql][16s + 8G .. +7]
+    f16x8 qf[D / 16];
+    {
+      const bool valid = qt * PQ + ql < q_len;
+      const float* qp = q + ((size_t)(row0 + ql) * Hq + h) * D + 8 * G;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const f16x8 kf = *(const f16x8*)(&sm.k[cur][k_off<D>(kh * 32 + ql, 2 * s + G)]);
-        st[kh] = mfma32x32x16(kf, qf[s], st[kh]);
-      }
-    }
-    // lane holds keys kh*32 + 8(r/4) + 4G + r%4 of query ql
-    const int key_base = t * PK;
-    const bool need_mask = key_base + PK - 1 > first_q || key_base + PK > n_keys;
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = st[kh][r] * sc;
-        if (need_mask) {
-          const int key = key_base + kh * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
-          if (key > my_q || key >= n_keys) v = -INFINITY;
+        f16x8 v{};
+        if (valid) {
+          const float4 a = *(const float4*)(qp + 16 * s), b = *(const float4*)(qp + 16 * s + 4);
+          v[0] = to_f16(a.x * sc); v[1] = to_f16(a.y * sc); v[2] = to_f16(a.z * sc);
+          v[3] = to_f16(a.w * sc); v[4] = to_f16(b.x * sc); v[5] = to_f16(b.y * sc);
+          v[6] = to_f16(b.z * sc); v[7] = to_f16(b.w * sc);
         }
-        st[kh][r] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    f16x8 pb[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const f16 pv = (f16)exp2f(st[kh][r] - m_new);
-        psum += (float)pv;
-        pb[kh * 2 + (r >> 3)][r & 7] = pv;
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int t2 = 0; t2 < D / 32; ++t2) acc[t2] *= alpha;
-    // O^T += V^T P^T, 16 keys per MFMA: chunk kc covers keys kc*16 .. +15;
-    // lane supplies keys kc*16 + 4G + 0..3 and kc*16 + 8 + 4G + 0..3
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int t2 = 0; t2 < D / 32; ++t2) {
-        const int d = 32 * t2 + ql;
-        const u32x2 lo = *(const u32x2*)(&sm.vt[cur][vt_off(d, kc * 4 + G)]);
-        const u32x2 hi = *(const u32x2*)(&sm.vt[cur][vt_off(d, kc * 4 + 2 + G)]);
-        const uint4 w = make_uint4(lo[0], lo[1], hi[0], hi[1]);
-        acc[t2] = mfma32x32x16(__builtin_bit_cast(f16x8, w), pb[kc], acc[t2]);
+        qf[s] = v;
       }
     }
-    if (more) store_tile(cur ^ 1);
-    __syncthreads();
-  }
 
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (qt * PQ + ql < q_len) {
-    const float inv = 1.f / l_run;
-    f16* op = o + (size_t)(row0 + ql) * Hq * D + (size_t)h * D;
+    // tile loader: the tile's four block-table entries are uniform loads;
+    // every chunk load is then unconditional (blocks past the sequence read
+    // block 0 and are zeroed when stored), so all loads are in flight at once
+    uint4 rk[MAX_PER_T];
+    int phys[PK / kBlockTokens];  // physical blocks of the tile to load next
+    // (loaded one tile ahead and not touched until the tile is fetched, so
+    // no wait on the table sits between the K/V loads and the MFMAs)
+    auto load_table = [&](int t) {
 #pragma unroll
-    for (int t2 = 0; t2 < D / 32; ++t2)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        f16x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = to_f16(acc[t2][4 * a + e] * inv);
-        *(f16x4*)(op + 32 * t2 + 8 * a + 4 * G) = v4;
+      for (int b = 0; b < PK / kBlockTokens; ++b) {
+        const int lblk = t * (PK / kBlockTokens) + b;
+        phys[b] = tab[lblk * kBlockTokens < n_keys ? lblk : 0];
       }
+    };
+    auto load_tile = [&](int t) {
+#pragma unroll
+      for (int i = 0; i < MAX_PER_T; ++i) {
+        const int c = tid + i * nthreads;
+        if (c < K_CHUNKS + V_CHUNKS) {
+          const bool isk = c < K_CHUNKS;
+          const int cc = isk ? c : c - K_CHUNKS;
+          const int lb = cc / CHUNKS_PER_BLOCK, within = cc % CHUNKS_PER_BLOCK;
+          const bf16* src = (isk ? kpool : vpool) + ((size_t)phys[lb] * Hkv + g) * head_elems + within * 8;
+          rk[i] = *(const uint4*)src;
+        }
+      }
+    };
+    // convert to fp16 (keys past the end of the sequence become zero) and store
+    auto store_tile = [&](int t, int buf) {
+#pragma unroll
+      for (int i = 0; i < MAX_PER_T; ++i) {
+        const int c = tid + i * nthreads;
+        if (c >= K_CHUNKS + V_CHUNKS) continue;
+        const bool isk = c < K_CHUNKS;
+        const int cc = isk ? c : c - K_CHUNKS;
+        const int lb = cc / CHUNKS_PER_BLOCK, within = cc % CHUNKS_PER_BLOCK;
+        const int base_key = (t * (PK / kBlockTokens) + lb) * kBlockTokens;
+        uint32_t w[4] = {rk[i].x, rk[i].y, rk[i].z, rk[i].w};
+        if (isk) {
+          if (base_key + (within * 8) / D >= n_keys) w[0] = w[1] = w[2] = w[3] = 0;
+          const int key = lb * kBlockTokens + (within * 8) / D;
+          const int chunk = ((within * 8) % D) / 8;
+          *(uint4*)(&sm.k[buf][k_off<D>(key, chunk)]) =
+              make_uint4(bf16pair_to_f16pair(w[0]), bf16pair_to_f16pair(w[1]),
+                         bf16pair_to_f16pair(w[2]), bf16pair_to_f16pair(w[3]));
+        } else {
+          const int key0 = (within * 8) % kBlockTokens;  // 8 keys of one channel
+          if (base_key + kBlockTokens > n_keys) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (base_key + key0 + e >= n_keys) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+          const int d = (within * 8) / kBlockTokens;
+          const int unit = (lb * kBlockTokens + key0) / 4;  // even
+          *(u32x2*)(&sm.vt[buf][vt_off(d, unit)]) =
+              u32x2{bf16pair_to_f16pair(w[0]), bf16pair_to_f16pair(w[1])};
+          *(u32x2*)(&sm.vt[buf][vt_off(d, unit + 1)]) =
+              u32x2{bf16pair_to_f16pair(w[2]), bf16pair_to_f16pair(w[3])};
+        }
+      }
+    };
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    __syncthreads();  // the previous item's last tile may still be read
+    load_table(0);
+    load_tile(0);
+    load_table(1);
+    store_tile(0, 0);
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      const int cur = t & 1;
+      const bool more = t + 1 < n_tiles;
+      // unconditional (a tile past the end reads valid blocks and is never
+      // stored), so no loaded register is merged across a branch
+      load_tile(t + 1);
+      load_table(t + 2);
+
+      // S^T for 64 keys x 32 queries: two independent 32-key halves
+      f32x16 st[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const f16x8 k0 = *(const f16x8*)(&sm.k[cur][k_off<D>(ql, 2 * s + G)]);
+        const f16x8 k1 = *(const f16x8*)(&sm.k[cur][k_off<D>(32 + ql, 2 * s + G)]);
+        st[0] = mfma32x32x16(k0, qf[s], st[0]);
+        st[1] = mfma32x32x16(k1, qf[s], st[1]);
+      }
+      // lane holds keys kh*32 + 8(r/4) + 4G + r%4 of query ql; keys past
+      // min(own position, last cached key) are masked (only near the
+      // diagonal and in the sequence's last tile)
+      const int key_base = t * PK;
+      if (key_base + PK - 1 > first_q || key_base + PK > n_keys) {
+        const int lim = min(my_q, n_keys - 1) - key_base - 4 * G;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            st[kh][r] = kh * 32 + 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : st[kh][r];
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, st[kh][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      f16x8 pb[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const f16 pv = (f16)exp2f(st[kh][r] - m_new);
+          psum += (float)pv;
+          pb[kh * 2 + (r >> 3)][r & 7] = pv;
+        }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int t2 = 0; t2 < D / 32; ++t2) acc[t2] *= alpha;
+      // O^T += V^T P^T, 16 keys per MFMA: chunk kc covers keys kc*16 .. +15;
+      // lane supplies keys kc*16 + 4G + 0..3 and kc*16 + 8 + 4G + 0..3
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int t2 = 0; t2 < D / 32; ++t2) {
+          const int d = 32 * t2 + ql;
+          const u32x2 lo = *(const u32x2*)(&sm.vt[cur][vt_off(d, kc * 4 + G)]);
+          const u32x2 hi = *(const u32x2*)(&sm.vt[cur][vt_off(d, kc * 4 + 2 + G)]);
+          const uint4 w = make_uint4(lo[0], lo[1], hi[0], hi[1]);
+          acc[t2] = mfma32x32x16(__builtin_bit_cast(f16x8, w), pb[kc], acc[t2]);
+        }
+      }
+      if (more) store_tile(t + 1, cur ^ 1);
+      __syncthreads();
+    }
+
+    l_run += __shfl_xor(l_run, 32, 64);
+    if (qt * PQ + ql < q_len) {
+      const float inv = 1.f / l_run;
+      f16* op = o + (size_t)(row0 + ql) * Hq * D + (size_t)h * D;
+#pragma unroll
+      for (int t2 = 0; t2 < D / 32; ++t2)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          f16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = to_f16(acc[t2][4 * a + e] * inv);
+          *(f16x4*)(op + 32 * t2 + 8 * a + 4 * G) = v4;
+        }
+    }
   }
 }
 
@@ -574,12 +589,14 @@ hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, int n_prefill, 
                         int Hq, int Hkv, int D, void* o, hipStream_t s) {
   if (n_prefill == 0 || max_q_len == 0) return hipSuccess;
   const int n_qtiles = cdiv(max_q_len, PQ);
-  dim3 grid(n_qtiles, Hkv, n_prefill);
+  // pair tiles (x, n-1-x) when that still leaves a workgroup for every CU
+  const int paired = (long)cdiv(n_qtiles, 2) * Hkv * n_prefill >= 256 ? 1 : 0;
+  dim3 grid(paired ? cdiv(n_qtiles, 2) : n_qtiles, Hkv, n_prefill);
   const int n_rep = Hq / Hkv;
 #define TDL_PREFILL_CASE(DD, NR)                                                               \
   if (D == DD && n_rep == NR) {                                                                \
     attn_prefill_kernel<DD, NR><<<grid, NR * 64, 0, s>>>((const float*)q, pool, seq, Hq, Hkv,  \
-                                                        n_qtiles, (f16*)o);                   \
+                                                        n_qtiles, paired, (f16*)o);           \
     return hipGetLastError();                                                                  \
   }
   TDL_PREFILL_CASE(128, 1) TDL_PREFILL_CASE(128, 2) TDL_PREFILL_CASE(128, 4)
