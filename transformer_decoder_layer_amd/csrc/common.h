@@ -18,6 +18,9 @@ typedef _Float16 f16;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
 
+// LDS (address space 3) pointer, the destination type of direct-to-LDS loads
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int kWave = 64;
 constexpr float kF16Max = 65504.f;
 

@@ -50,7 +50,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {  // offset in bf16 elem
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // DIRECT: operand tiles go from global memory straight into LDS
 // (global_load_lds_dwordx4, no staging registers); each lane fetches the
@@ -492,7 +491,7 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
   constexpr int kCUs = 256;
   {
     GemmPlan sk{};
-    if (skinny_plan(M, N, K, &sk)) return sk;
+    if (skinny_plan(M, N, K, epi, &sk)) return sk;
   }
   const int KT = cdiv(K, BK);
   GemmPlan best{};

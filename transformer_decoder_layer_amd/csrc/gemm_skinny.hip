@@ -2,22 +2,31 @@
 // where the weight matrix B is streamed from HBM exactly once.
 //
 // With few rows every weight element is used only M times, so the kernel is
-// bound by HBM bandwidth, not by the matrix cores.  The design therefore
-// keeps as many weight bytes in flight as possible and touches no LDS on the
-// streaming path: each lane loads its MFMA operand fragments straight from
-// global memory (16 bytes = 8 consecutive k of one row), for the weights
-// from HBM and for the activations from L2, where the small A matrix stays
-// resident.  A workgroup owns 64 weight rows; its four waves take contiguous
-// quarters of the workgroup's K range, so each wave streams 64 rows x its
-// quarter, with the loads of the next k32-steps in flight while the
-// current ones feed the MFMAs.  The four
-// partial sums meet in LDS; when the K range is also split across
-// workgroups (long K, few rows of N) the slices go to memory and the shared
-// split-K reduction kernel finishes them.
+// bound by HBM bandwidth; what matters is keeping enough weight bytes in
+// flight on every CU and never draining that stream.  Layout of the work:
 //
-// Q8_0 weights: lane loads 8 int8 codes (one 32-code block per k32 step
-// across the four lane groups), converts them exactly, and the block's fp16
-// scale multiplies that MFMA's partial product.
+//  * A workgroup owns 64 weight rows and a K range.  Its waves form KW
+//    k-slices of four row waves; a row wave streams its 16 rows over its
+//    slice's part of the K range.  (With the SiLU-gate epilogue the gate
+//    and up rows of an output column sit in neighbouring row waves and meet
+//    in LDS at the end.)
+//  * Weights go straight from HBM into MFMA operand registers (16 bytes =
+//    8 consecutive k of one row per lane), in kStages rotating register
+//    sets: the loads of stage s + kStages - 1 are issued before the MFMAs of
+//    stage s, so kStages - 1 stages of every wave are always in flight.
+//  * The activations of a stage (all M rows x 64 k) are shared by the four
+//    row waves of a slice: they go from global memory (L2-resident) into an
+//    LDS ring of kStages buffers with direct-to-LDS loads, each of the four
+//    waves fetching a quarter.  One wait on the load counter plus one
+//    barrier per stage covers both the register and the LDS data (loads
+//    complete in issue order).
+//  * k-slices meet in LDS at the end; splits of K across workgroups (only
+//    where the row count alone cannot fill the GPU) go through the shared
+//    split-K reduction kernel.
+//
+// Q8_0 weights: a lane loads 8 int8 codes of its row per 32-k step plus the
+// block's fp16 scale; the codes convert exactly to fp16 and the scale
+// multiplies that step's MFMA product in fp32.
 
 #include "common.h"
 #include "kernels.h"
@@ -26,218 +35,319 @@ namespace tdl {
 
 namespace {
 
-constexpr int kU = 2;  // k32 steps per load group
+constexpr int kRowWaves = 4;  // row waves per k-slice
+constexpr int kStages = 4;    // pipeline depth: LDS ring buffers = register sets
+constexpr int kStageK = 64;   // k per stage (two 32-k MFMA steps)
 
-template <typename T, bool Q80, int MT, int EPI>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p) {
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding and leaves the other counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+template <bool Q80, typename T> struct BFrag;
+template <typename T> struct BFrag<false, T> { typename Mfma<T>::v8 v; };
+template <typename T> struct BFrag<true, T> { uint2 codes; uint32_t scale; };
+
+// (at most 128 registers up to 64 rows of A: four waves per SIMD, i.e. two
+// 8-wave workgroups per CU, so that every workgroup of a launch is resident
+// at once; 128 rows of A need more and run two waves per SIMD)
+template <typename T, bool Q80, int MT, int KW, int EPI>
+__global__ __launch_bounds__(64 * kRowWaves * KW) __attribute__((amdgpu_waves_per_eu(MT == 8 ? 2 : 4)))
+void gemm_stream_kernel(GemmArgs p) {
   typedef typename Mfma<T>::v8 T8;
-  constexpr int FN = 4;  // 64 weight rows per workgroup, 16 per MFMA tile
-  __shared__ f32x4 red[3][MT][FN][64];
+  constexpr int FN = 1;                              // 16-row fragments per wave
+  constexpr int ROWS = 16 * FN * kRowWaves;
+  constexpr int AE = MT * 16 * kStageK;              // A elements per slice and stage
+  constexpr int A_PER_WAVE = MT / 2;                 // 1 KB direct loads per wave and stage
+  constexpr int LOADS = A_PER_WAVE + FN * 2 * (Q80 ? 2 : 1);  // vector-memory ops per stage
+  // four separate arrays (not one indexed array): the compiler can then tell
+  // that reading one buffer does not depend on the loads still filling another
+  __shared__ __attribute__((aligned(16))) T ring0[KW * AE];
+  __shared__ __attribute__((aligned(16))) T ring1[KW * AE];
+  __shared__ __attribute__((aligned(16))) T ring2[KW * AE];
+  __shared__ __attribute__((aligned(16))) T ring3[KW * AE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_tiles = cdiv(p.N, 64);
+  const int wr = wave % kRowWaves, wk = wave / kRowWaves;
+  const int n_tiles = cdiv(p.N, ROWS);
   const int split = blockIdx.x / n_tiles;
-  const int n0 = (blockIdx.x % n_tiles) * 64;
-  const int KS = p.K / 32;                          // k32 steps
-  const int s0 = split * p.k_tiles_per_split;       // this workgroup's steps
-  const int s1 = min(s0 + p.k_tiles_per_split, KS);
-  const int per_wave = cdiv(s1 - s0, 4);
-  const int w0 = s0 + wave * per_wave;
-  const int w1 = min(w0 + per_wave, s1);
-  const int r16 = lane & 15, g8 = (lane >> 4) * 8;
+  const int n0 = (blockIdx.x % n_tiles) * ROWS;
+  const int KS32 = p.K / 32;
+  const int KS = cdiv(KS32, 2);                       // stages over the whole K
+  const int ks0 = split * p.k_tiles_per_split;        // this split's stages
+  const int ks1 = min(ks0 + p.k_tiles_per_split, KS);
+  const int per_slice = cdiv(max(ks1 - ks0, 0), KW);  // stages per slice (all slices alike)
+  const int my0 = ks0 + wk * per_slice;               // this slice's stages: [my0, my1)
+  const int my1 = min(my0 + per_slice, ks1);
+  const int last = max(my1 - 1, 0);                   // loads past the end repeat the last stage
+  const int n_iter = cdiv(per_slice, kStages) * kStages;
 
   const T* __restrict__ A = (const T*)p.A;
-  const T* arow[MT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) arow[i] = A + (size_t)min(16 * i + r16, p.M - 1) * p.lda + g8;
-  size_t brow[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) brow[j] = (size_t)min(n0 + 16 * j + r16, p.N - 1);
+  const int r16 = lane & 15, g8 = (lane >> 4) * 8;
 
+  // this wave's direct-load rows of A: tokens 8*(wr*A_PER_WAVE + q) + lane/8,
+  // 16-byte chunk position lane%8 holding source chunk (lane%8) ^ (token%8)
+  const T* a_src[A_PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < A_PER_WAVE; ++q) {
+    const int t = 8 * (wr * A_PER_WAVE + q) + (lane >> 3);
+    a_src[q] = A + (size_t)min(t, p.M - 1) * p.lda + (((lane & 7) ^ (t & 7)) << 3);
+  }
+  const int a_c8 = ((lane & 7) ^ ((lane >> 3) & 7)) << 3;     // that chunk's first k
+  const int a_dst = wk * AE + 8 * wr * A_PER_WAVE * kStageK;  // + q * 8 tokens * 64 k
+
+  // weight rows of this lane (clamped; rows past N are computed, never stored)
+  size_t b_row[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) b_row[f] = (size_t)min(n0 + 16 * (wr * FN + f) + r16, p.N - 1);
+
+  BFrag<Q80, T> breg[kStages][FN][2];
   f32x4 acc[MT][FN];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < FN; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one k32 step of operands: 4 weight fragments (+ Q8_0 scales), MT
-  // activation fragments.  Steps past the wave's range load from a clamped
-  // (valid) address and zero their activation fragments, so the loop below
-  // needs no branches and the compiler can count outstanding loads exactly.
-  struct Step {
-    T8 b[FN];
-    T8 a[MT];
-    float sc[Q80 ? FN : 1];
-    bool valid;
-  };
-  auto load = [&](Step& st, int step) {
-    st.valid = step < w1;
-    const int k = min(step, KS - 1) * 32;
+  auto issue = [&](int it, T* ring, BFrag<Q80, T> (&b)[FN][2]) {
+    const int st = min(my0 + it, last);
+    const int k0 = st * kStageK;
+    // A: the whole stage chunk; a k past K (a half stage at the end) reads
+    // the row's first chunk instead, multiplied by zeroed weights
+    const int a_off = k0 + a_c8 < p.K ? k0 : -a_c8;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (Q80) {
-        const uint2 c = *(const uint2*)((const int8_t*)p.B + brow[j] * p.ldb + k + g8);
-        T8 v;
+    for (int q = 0; q < A_PER_WAVE; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + a_off),
+                                       (lds_void*)&ring[a_dst + q * 8 * kStageK], 16, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = (T)(float)(int8_t)(c.x >> (8 * e));
-          v[4 + e] = (T)(float)(int8_t)(c.y >> (8 * e));
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ks = min(2 * st + u, KS32 - 1);
+        const int k = ks * 32 + g8;
+        if constexpr (Q80) {
+          b[f][u].codes = *(const uint2*)((const int8_t*)p.B + b_row[f] * p.ldb + k);
+          b[f][u].scale = *(const uint16_t*)(p.B_scale + b_row[f] * (p.ldb / 32) + ks);
+        } else {
+          b[f][u].v = *(const T8*)((const T*)p.B + b_row[f] * p.ldb + k);
         }
-        st.b[j] = v;
-        st.sc[j] = __half2float(p.B_scale[brow[j] * (p.ldb / 32) + (k >> 5)]);
-      } else {
-        st.b[j] = *(const T8*)((const T*)p.B + brow[j] * p.ldb + k + g8);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < MT; ++i) st.a[i] = *(const T8*)(arow[i] + k);
   };
-  auto mma = [&](const Step& st) {
-    T8 a[MT];
+
+  auto compute = [&](int it, const T* ring, const BFrag<Q80, T> (&b)[FN][2]) {
+    const int st = my0 + it;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) a[i] = st.valid ? st.a[i] : T8{};
+    for (int u = 0; u < 2; ++u) {
+      const bool valid = st < my1 && 2 * st + u < KS32;
+      T8 bv[FN];
+      float sc[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int f = 0; f < FN; ++f) {
+        if constexpr (Q80) {
+          T8 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = (T)(float)(int8_t)(b[f][u].codes.x >> (8 * e));
+            v[4 + e] = (T)(float)(int8_t)(b[f][u].codes.y >> (8 * e));
+          }
+          bv[f] = v;
+          sc[f] = valid ? __half2float(__ushort_as_half((unsigned short)b[f][u].scale)) : 0.f;
+        } else {
+          bv[f] = valid ? b[f][u].v : T8{};
+        }
+      }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        if constexpr (Q80) {
-          const f32x4 t = Mfma<T>::mma(a[i], st.b[j], f32x4{0.f, 0.f, 0.f, 0.f});
-          acc[i][j] += t * st.sc[j];
-        } else {
-          acc[i][j] = Mfma<T>::mma(a[i], st.b[j], acc[i][j]);
+        // token 16i + r16, chunk 4u + lane/16, swizzled by token % 8 = lane % 8
+        const T8 a = *(const T8*)&ring[wk * AE + (16 * i + r16) * kStageK +
+                                       (((4 * u + (lane >> 4)) ^ (lane & 7)) << 3)];
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          if constexpr (Q80) {
+            const f32x4 t = Mfma<T>::mma(a, bv[f], f32x4{0.f, 0.f, 0.f, 0.f});
+            acc[i][f] += t * sc[f];
+          } else {
+            acc[i][f] = Mfma<T>::mma(a, bv[f], acc[i][f]);
+          }
         }
       }
+    }
   };
 
-  // groups of kU steps: the next group's loads are issued before this
-  // group's MFMAs, so a group's worth of weight bytes is always in flight
-  // (two register sets used alternately: no copies between iterations,
-  // whose reads of freshly loaded registers would force a wait)
-  const int n_groups = w1 > w0 ? cdiv(w1 - w0, kU) : 0;
-  Step sa[kU], sb[kU];
-#pragma unroll
-  for (int u = 0; u < kU; ++u) load(sa[u], w0 + u);
-  for (int gi = 0; gi < n_groups; gi += 2) {
-#pragma unroll
-    for (int u = 0; u < kU; ++u) load(sb[u], w0 + (gi + 1) * kU + u);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) mma(sa[u]);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) load(sa[u], w0 + (gi + 2) * kU + u);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) mma(sb[u]);
+  // one pipeline step: wait for stage it (kStages - 2 later stages may stay
+  // in flight), barrier (every wave's share of the A chunk has landed and
+  // every wave is done with the buffer refilled next), refill, compute
+  // (scheduling barriers keep the compiler from moving register reads of a
+  // stage's loads, or the loads themselves, across these points: the wait
+  // counts assume program order)
+#define TDL_STREAM_STEP(J, RING, RING_PREV)                                   \
+  {                                                                           \
+    __builtin_amdgcn_sched_barrier(0);                                        \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * LOADS));             \
+    asm volatile("s_barrier" ::: "memory");                                   \
+    __builtin_amdgcn_sched_barrier(0);                                        \
+    issue(it + J + kStages - 1, RING_PREV, breg[(J + kStages - 1) % kStages]); \
+    __builtin_amdgcn_sched_barrier(0);                                        \
+    compute(it + J, RING, breg[J]);                                           \
   }
 
-  // ---- the four waves' partial sums meet in LDS (fixed order: 0+1+2+3)
-  if (wave > 0) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) red[wave - 1][i][j][lane] = acc[i][j];
+  issue(0, ring0, breg[0]);
+  issue(1, ring1, breg[1]);
+  issue(2, ring2, breg[2]);
+  for (int it = 0; it < n_iter; it += kStages) {
+    TDL_STREAM_STEP(0, ring0, ring3)
+    TDL_STREAM_STEP(1, ring1, ring0)
+    TDL_STREAM_STEP(2, ring2, ring1)
+    TDL_STREAM_STEP(3, ring3, ring2)
   }
-  __syncthreads();
-  if (wave > 0) return;
-#pragma unroll
-  for (int w = 0; w < 3; ++w)
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] += red[w][i][j][lane];
+#undef TDL_STREAM_STEP
+  // the last refills are still landing in the ring: drain them before the
+  // ring is reused or the workgroup exits
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // acc[i][j][r] = C[16i + 4*(lane/16) + r][n0 + 16j + lane%16]
-  const int col = lane & 15;
+  // ---- k-slices meet in LDS, summed in a fixed order
+  if constexpr (KW > 1) {
+    f32x4* red = (f32x4*)ring0;  // (KW-1) x 4 waves x MT x 64 lanes x 16 B <= ring0
+    static_assert((KW - 1) * kRowWaves * MT * 64 * 16 <= KW * AE * (int)sizeof(T), "ring0 too small");
+    __syncthreads();
+    if (wk > 0) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) red[(((wk - 1) * kRowWaves + wr) * MT + i) * 64 + lane] = acc[i][0];
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int w = 1; w < KW; ++w)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i][0] += red[(((w - 1) * kRowWaves + wr) * MT + i) * 64 + lane];
+    }
+  }
+
+  // from here on slice 0 holds the sums: acc[i][0][r] =
+  // C[16i + 4*(lane/16) + r][n0 + 16*wr + lane%16]
   const int rb = 4 * (lane >> 4);
+  const int n = n0 + 16 * wr + r16;
   if (p.splits > 1) {
+    if (wk > 0 || n >= p.N) return;
     float* part = p.ws + (size_t)split * p.M * p.N;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + 16 * j + col;
-      if (n >= p.N) continue;
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 16 * i + rb + r;
-          if (m < p.M) part[(size_t)m * p.N + n] = acc[i][j][r];
-        }
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * i + rb + r;
+        if (m < p.M) part[(size_t)m * p.N + n] = acc[i][0][r];
+      }
     return;
   }
   if constexpr (EPI == EPI_SILU_GATE) {
+    // row waves 2j hold gate rows n0 + 32j + [0,16), waves 2j+1 the matching
+    // up rows: the up waves hand their sums over through LDS
+    f32x4* xch = (f32x4*)ring1;
+    static_assert(2 * MT * 64 * 16 <= KW * AE * (int)sizeof(T), "ring1 too small");
+    __syncthreads();  // every wave is done reading ring1
+    if (wk == 0 && (wr & 1)) {
 #pragma unroll
-    for (int jp = 0; jp < FN / 2; ++jp) {
-      const int ng = n0 + 32 * jp;
-      if (ng + col >= p.N) continue;
-      const int jcol = ng / 2 + col;
+      for (int i = 0; i < MT; ++i) xch[((wr >> 1) * MT + i) * 64 + lane] = acc[i][0];
+    }
+    __syncthreads();
+    if (wk > 0 || (wr & 1) || n >= p.N) return;
+    const int jcol = (n0 + 16 * wr) / 2 + r16;
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i) {
+      const f32x4 up = xch[((wr >> 1) * MT + i) * 64 + lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 16 * i + rb + r;
-          if (m < p.M) {
-            const float g = acc[i][2 * jp][r], u = acc[i][2 * jp + 1][r];
-            ((bf16*)p.C)[(size_t)m * p.ldc + jcol] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
-          }
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * i + rb + r;
+        if (m < p.M) {
+          const float g = acc[i][0][r];
+          ((bf16*)p.C)[(size_t)m * p.ldc + jcol] = f32_to_bf16(g / (1.0f + __expf(-g)) * up[r]);
         }
+      }
     }
   } else {
+    if (wk > 0 || n >= p.N) return;
+    const float bias = (EPI == EPI_BIAS_F32 && p.bias) ? p.bias[n] : 0.f;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + 16 * j + col;
-      if (n >= p.N) continue;
-      const float bias = (EPI == EPI_BIAS_F32 && p.bias) ? p.bias[n] : 0.f;
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 16 * i + rb + r;
-          if (m >= p.M) continue;
-          const float v = acc[i][j][r];
-          if constexpr (EPI == EPI_BIAS_F32) {
-            ((float*)p.C)[(size_t)m * p.ldc + n] = v + bias;
-          } else if constexpr (EPI == EPI_RESID_F32) {
-            ((float*)p.C)[(size_t)m * p.ldc + n] =
-                v + bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
-          } else {
-            ((bf16*)p.C)[(size_t)m * p.ldc + n] =
-                f32_to_bf16(v + ((const float*)p.resid)[(size_t)m * p.ldr + n]);
-          }
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * i + rb + r;
+        if (m >= p.M) continue;
+        const float v = acc[i][0][r];
+        if constexpr (EPI == EPI_BIAS_F32) {
+          ((float*)p.C)[(size_t)m * p.ldc + n] = v + bias;
+        } else if constexpr (EPI == EPI_RESID_F32) {
+          ((float*)p.C)[(size_t)m * p.ldc + n] =
+              v + bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
+        } else {
+          ((bf16*)p.C)[(size_t)m * p.ldc + n] =
+              f32_to_bf16(v + ((const float*)p.resid)[(size_t)m * p.ldr + n]);
         }
-    }
+      }
   }
 }
 
-template <bool Q80, int MT>
-hipError_t launch_mt(int grid, int epi, const GemmArgs& a, hipStream_t s) {
+template <bool Q80, int MT, int KW>
+hipError_t launch_stream(int grid, int epi, const GemmArgs& a, hipStream_t s) {
+  constexpr int threads = 64 * kRowWaves * KW;
   switch (epi) {
     case EPI_BIAS_F32:
-      gemm_skinny_kernel<f16, Q80, MT, EPI_BIAS_F32><<<grid, 256, 0, s>>>(a);
+      gemm_stream_kernel<f16, Q80, MT, KW, EPI_BIAS_F32><<<grid, threads, 0, s>>>(a);
       break;
     case EPI_RESID_F32:
-      gemm_skinny_kernel<f16, Q80, MT, EPI_RESID_F32><<<grid, 256, 0, s>>>(a);
+      gemm_stream_kernel<f16, Q80, MT, KW, EPI_RESID_F32><<<grid, threads, 0, s>>>(a);
       break;
     case EPI_RESID_BF16:
-      gemm_skinny_kernel<bf16, Q80, MT, EPI_RESID_BF16><<<grid, 256, 0, s>>>(a);
+      gemm_stream_kernel<bf16, Q80, MT, KW, EPI_RESID_BF16><<<grid, threads, 0, s>>>(a);
       break;
     default:
-      gemm_skinny_kernel<f16, Q80, MT, EPI_SILU_GATE><<<grid, 256, 0, s>>>(a);
+      gemm_stream_kernel<f16, Q80, MT, KW, EPI_SILU_GATE><<<grid, threads, 0, s>>>(a);
       break;
   }
   return hipGetLastError();
 }
 
+template <bool Q80, int MT>
+hipError_t launch_mt(int kw, int grid, int epi, const GemmArgs& a, hipStream_t s) {
+  if constexpr (MT == 8) return launch_stream<Q80, 8, 1>(grid, epi, a, s);  // LDS: one slice only
+  else return kw == 1 ? launch_stream<Q80, MT, 1>(grid, epi, a, s) : launch_stream<Q80, MT, 2>(grid, epi, a, s);
+}
+
 }  // namespace
 
-bool skinny_plan(int M, int N, int K, GemmPlan* pl) {
+// cfg = 100 + 10 * MT + KW.  Picks the fewest K splits (each costs a round
+// trip of M x N fp32 partials) that still give every CU a workgroup and
+// at least six waves (enough weight bytes in flight to cover HBM latency),
+// preferring two k-slices per workgroup over a split.
+bool skinny_plan(int M, int N, int K, int epi, GemmPlan* pl) {
   if (M > 128 || K % 32 != 0) return false;
-  const int n_tiles = cdiv(N, 64);
-  const int KS = K / 32;
-  // split K across workgroups until there are ~2 per CU, keeping >= 16 k32
-  // steps (4 per wave) per workgroup
-  int splits = 1;
-  while (n_tiles * splits < 480 && KS / (splits * 2) >= 16) splits *= 2;
-  pl->cfg = M <= 64 ? 10 : 11;
-  pl->k_tiles_per_split = cdiv(KS, splits);
+  constexpr int kCUs = 256;
+  const int MT = M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  const int rows = 16 * kRowWaves;
+  const int n_tiles = cdiv(N, rows);
+  const int KS = cdiv(K / 32, 2);
+  int best_s = 1, best_kw = 1;
+  long best_waves = -1;
+  bool found = false;
+  for (int s = 1; s <= 32 && !found; s *= 2) {
+    for (int kw = 1; kw <= (MT == 8 ? 1 : 2); ++kw) {
+      const int per_split = cdiv(KS, s);
+      if (s > 1 && per_split / kw < 4) continue;   // too short to fill the pipeline
+      const long wgs = (long)n_tiles * cdiv(KS, per_split);
+      const long waves = wgs * kRowWaves * kw;
+      if (wgs >= kCUs && waves >= 6 * kCUs) {
+        best_s = s;
+        best_kw = kw;
+        found = true;
+        break;
+      }
+      if (waves > best_waves) {
+        best_waves = waves;
+        best_s = s;
+        best_kw = kw;
+      }
+    }
+  }
+  pl->cfg = 100 + 10 * MT + best_kw;
+  pl->k_tiles_per_split = cdiv(KS, best_s);
   pl->splits = cdiv(KS, pl->k_tiles_per_split);
   pl->grid = n_tiles * pl->splits;
   pl->ws_floats = pl->splits > 1 ? (size_t)pl->splits * M * N : 0;
@@ -246,8 +356,10 @@ bool skinny_plan(int M, int N, int K, GemmPlan* pl) {
 
 hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, bool q80, int epi,
                               hipStream_t s) {
-  if (pl.cfg == 10) return q80 ? launch_mt<true, 4>(pl.grid, epi, a, s) : launch_mt<false, 4>(pl.grid, epi, a, s);
-  return q80 ? launch_mt<true, 8>(pl.grid, epi, a, s) : launch_mt<false, 8>(pl.grid, epi, a, s);
+  const int MT = (pl.cfg - 100) / 10, kw = pl.cfg % 10;
+  if (MT == 2) return q80 ? launch_mt<true, 2>(kw, pl.grid, epi, a, s) : launch_mt<false, 2>(kw, pl.grid, epi, a, s);
+  if (MT == 4) return q80 ? launch_mt<true, 4>(kw, pl.grid, epi, a, s) : launch_mt<false, 4>(kw, pl.grid, epi, a, s);
+  return q80 ? launch_mt<true, 8>(1, pl.grid, epi, a, s) : launch_mt<false, 8>(1, pl.grid, epi, a, s);
 }
 
 }  // namespace tdl

@@ -48,8 +48,8 @@ struct GemmPlan {
 };
 GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi);
 // Decode-sized M (<= 128, K % 32 == 0): weights streamed straight from HBM
-// into MFMA operands (cfg 10 / 11).
-bool skinny_plan(int M, int N, int K, GemmPlan* pl);
+// into MFMA operands, activations shared through LDS (cfg >= 100).
+bool skinny_plan(int M, int N, int K, int epi, GemmPlan* pl);
 hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, bool q80, int epi,
                               hipStream_t s);
 hipError_t gemm_launch(const GemmPlan& plan, GemmArgs a, bool q80, int epi, hipStream_t s);
