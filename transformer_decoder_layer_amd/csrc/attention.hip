@@ -501,16 +501,40 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     }
   };
 
-  // ping-pong: the next block's loads are in flight while this one computes
-  DecFrags<D, U8> fa, fb;
-  if (cnt > 0) dec_load<D, U8>(fa, a, __shfl(my_phys, 0, 64), g, col, grp);
-  for (int i = 0; i < cnt; i += 2) {
-    if (i + 1 < cnt) dec_load<D, U8>(fb, a, __shfl(my_phys, i + 1, 64), g, col, grp);
-    compute(fa, i);
-    if (i + 1 < cnt) {
-      if (i + 2 < cnt) dec_load<D, U8>(fa, a, __shfl(my_phys, i + 2, 64), g, col, grp);
-      compute(fb, i + 1);
+  // three register sets in rotation: while one block computes, the next two
+  // blocks' loads are in flight.  Loads past the wave's last block repeat
+  // that block (valid addresses) and are never computed.  The explicit
+  // waits count this wave's vector-memory operations in program order; the
+  // scheduling barriers keep the compiler from moving loads or their uses
+  // across them.
+  constexpr int LOADS = D / 32 + D / 16;  // vector-memory operations per block
+  constexpr int kWaitOne = (LOADS & 15) | (7 << 4) | (15 << 8) | (((LOADS >> 4) & 3) << 14);
+  if (cnt > 0) {
+    auto phys_of = [&](int i) { return __shfl(my_phys, min(i, cnt - 1), 64); };
+    DecFrags<D, U8> f0, f1, f2;
+    dec_load<D, U8>(f0, a, phys_of(0), g, col, grp);
+    dec_load<D, U8>(f1, a, phys_of(1), g, col, grp);
+    for (int i = 0; i < cnt; i += 3) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitOne);
+      __builtin_amdgcn_sched_barrier(0);
+      dec_load<D, U8>(f2, a, phys_of(i + 2), g, col, grp);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f0, i);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitOne);
+      __builtin_amdgcn_sched_barrier(0);
+      dec_load<D, U8>(f0, a, phys_of(i + 3), g, col, grp);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < cnt) compute(f1, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitOne);
+      __builtin_amdgcn_sched_barrier(0);
+      dec_load<D, U8>(f1, a, phys_of(i + 4), g, col, grp);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < cnt) compute(f2, i + 2);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the last (unused) loads land before the registers go
   }
 
   // ---- merge the four waves: acc[t][r] = O^T[16t + 4grp + r][head col]
@@ -611,10 +635,11 @@ DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len) {
   (void)Hq;
   DecodePlan pl{};
   const int max_blk = cdiv(max_ctx_len, kBlockTokens);
-  // partitions of 16 blocks (256 tokens): ~4 blocks per wave, and enough
-  // workgroups to fill the chip when contexts are long; short batches split
-  // finer so that there are still a few hundred workgroups
-  int pb = 16;
+  // partitions of 32 blocks (512 tokens): ~8 blocks per wave, long enough
+  // for the three-deep load pipeline, and enough workgroups to fill the chip
+  // when contexts are long; short batches split finer so that there are
+  // still a few hundred workgroups
+  int pb = 32;
   while (pb > 4 && (long)batch * Hkv * cdiv(max_blk, pb) < 1024) pb /= 2;
   pl.part_blocks = pb;
   pl.max_parts = cdiv(max_blk, pb);

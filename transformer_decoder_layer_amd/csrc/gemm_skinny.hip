@@ -35,9 +35,8 @@ namespace tdl {
 
 namespace {
 
-constexpr int kRowWaves = 4;  // row waves per k-slice
-constexpr int kStages = 4;    // pipeline depth: LDS ring buffers = register sets
-constexpr int kStageK = 64;   // k per stage (two 32-k MFMA steps)
+constexpr int kStageK = 64;  // k per stage (two 32-k MFMA steps)
+constexpr int kMaxStages = 8;
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding and leaves the other counters alone.
@@ -50,21 +49,32 @@ template <typename T> struct BFrag<true, T> { uint2 codes; uint32_t scale; };
 // (at most 128 registers up to 64 rows of A: four waves per SIMD, i.e. two
 // 8-wave workgroups per CU, so that every workgroup of a launch is resident
 // at once; 128 rows of A need more and run two waves per SIMD)
-template <typename T, bool Q80, int MT, int KW, int EPI>
-__global__ __launch_bounds__(64 * kRowWaves * KW) __attribute__((amdgpu_waves_per_eu(MT == 8 ? 2 : 4)))
+// RW row waves per k-slice (64 * RW / 4 ... 16 * RW weight rows per
+// workgroup), NS pipeline stages (= LDS ring buffers = register sets).
+template <typename T, bool Q80, int MT, int KW, int RW, int NS, int EPI, bool PACKED = false>
+__global__ __launch_bounds__(64 * RW * KW) __attribute__((amdgpu_waves_per_eu(MT == 8 ? 2 : 4)))
 void gemm_stream_kernel(GemmArgs p) {
+  constexpr int kRowWaves = RW, kStages = NS;
+  static_assert(NS >= 3 && NS <= kMaxStages && RW % 2 == 0, "stream GEMM shape");
   typedef typename Mfma<T>::v8 T8;
   constexpr int FN = 1;                              // 16-row fragments per wave
   constexpr int ROWS = 16 * FN * kRowWaves;
   constexpr int AE = MT * 16 * kStageK;              // A elements per slice and stage
-  constexpr int A_PER_WAVE = MT / 2;                 // 1 KB direct loads per wave and stage
+  constexpr int A_PER_WAVE = 2 * MT / RW;            // 1 KB direct loads per wave and stage
+  static_assert(A_PER_WAVE >= 1 && A_PER_WAVE * RW == 2 * MT, "A chunk split over the row waves");
   constexpr int LOADS = A_PER_WAVE + FN * 2 * (Q80 ? 2 : 1);  // vector-memory ops per stage
-  // four separate arrays (not one indexed array): the compiler can then tell
-  // that reading one buffer does not depend on the loads still filling another
+  // separate arrays (not one indexed array): the compiler can then tell that
+  // reading one buffer does not depend on the loads still filling another
+  // (arrays past NS are never referenced and take no LDS)
   __shared__ __attribute__((aligned(16))) T ring0[KW * AE];
   __shared__ __attribute__((aligned(16))) T ring1[KW * AE];
   __shared__ __attribute__((aligned(16))) T ring2[KW * AE];
   __shared__ __attribute__((aligned(16))) T ring3[KW * AE];
+  __shared__ __attribute__((aligned(16))) T ring4[KW * AE];
+  __shared__ __attribute__((aligned(16))) T ring5[KW * AE];
+  __shared__ __attribute__((aligned(16))) T ring6[KW * AE];
+  __shared__ __attribute__((aligned(16))) T ring7[KW * AE];
+  T* const rings[kMaxStages] = {ring0, ring1, ring2, ring3, ring4, ring5, ring6, ring7};
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave % kRowWaves, wk = wave / kRowWaves;
@@ -126,6 +136,9 @@ void gemm_stream_kernel(GemmArgs p) {
         if constexpr (Q80) {
           b[f][u].codes = *(const uint2*)((const int8_t*)p.B + b_row[f] * p.ldb + k);
           b[f][u].scale = *(const uint16_t*)(p.B_scale + b_row[f] * (p.ldb / 32) + ks);
+        } else if constexpr (PACKED) {
+          // [N/16][K/32] tiles of 512 elements: [k8 group][row][8 k]
+          b[f][u].v = *(const T8*)((const T*)p.B + ((size_t)(b_row[f] >> 4) * KS32 + ks) * 512 + lane * 8);
         } else {
           b[f][u].v = *(const T8*)((const T*)p.B + b_row[f] * p.ldb + k);
         }
@@ -174,38 +187,32 @@ void gemm_stream_kernel(GemmArgs p) {
 
   // one pipeline step: wait for stage it (kStages - 2 later stages may stay
   // in flight), barrier (every wave's share of the A chunk has landed and
-  // every wave is done with the buffer refilled next), refill, compute
-  // (scheduling barriers keep the compiler from moving register reads of a
+  // every wave is done with the buffer refilled next), refill, compute.
+  // Scheduling barriers keep the compiler from moving register reads of a
   // stage's loads, or the loads themselves, across these points: the wait
-  // counts assume program order)
-#define TDL_STREAM_STEP(J, RING, RING_PREV)                                   \
-  {                                                                           \
-    __builtin_amdgcn_sched_barrier(0);                                        \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * LOADS));             \
-    asm volatile("s_barrier" ::: "memory");                                   \
-    __builtin_amdgcn_sched_barrier(0);                                        \
-    issue(it + J + kStages - 1, RING_PREV, breg[(J + kStages - 1) % kStages]); \
-    __builtin_amdgcn_sched_barrier(0);                                        \
-    compute(it + J, RING, breg[J]);                                           \
-  }
-
-  issue(0, ring0, breg[0]);
-  issue(1, ring1, breg[1]);
-  issue(2, ring2, breg[2]);
+  // counts assume program order.
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j) issue(j, rings[j], breg[j]);
   for (int it = 0; it < n_iter; it += kStages) {
-    TDL_STREAM_STEP(0, ring0, ring3)
-    TDL_STREAM_STEP(1, ring1, ring0)
-    TDL_STREAM_STEP(2, ring2, ring1)
-    TDL_STREAM_STEP(3, ring3, ring2)
+#pragma unroll
+    for (int j = 0; j < kStages; ++j) {
+      const int jn = (j + kStages - 1) % kStages;
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * LOADS));
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      issue(it + j + kStages - 1, rings[jn], breg[jn]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(it + j, rings[j], breg[j]);
+    }
   }
-#undef TDL_STREAM_STEP
   // the last refills are still landing in the ring: drain them before the
   // ring is reused or the workgroup exits
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // ---- k-slices meet in LDS, summed in a fixed order
   if constexpr (KW > 1) {
-    f32x4* red = (f32x4*)ring0;  // (KW-1) x 4 waves x MT x 64 lanes x 16 B <= ring0
+    f32x4* red = (f32x4*)ring0;  // (KW-1) x RW waves x MT x 64 lanes x 16 B <= ring0
     static_assert((KW - 1) * kRowWaves * MT * 64 * 16 <= KW * AE * (int)sizeof(T), "ring0 too small");
     __syncthreads();
     if (wk > 0) {
@@ -239,20 +246,22 @@ void gemm_stream_kernel(GemmArgs p) {
   }
   if constexpr (EPI == EPI_SILU_GATE) {
     // row waves 2j hold gate rows n0 + 32j + [0,16), waves 2j+1 the matching
-    // up rows: the up waves hand their sums over through LDS
-    f32x4* xch = (f32x4*)ring1;
-    static_assert(2 * MT * 64 * 16 <= KW * AE * (int)sizeof(T), "ring1 too small");
-    __syncthreads();  // every wave is done reading ring1
+    // up rows: the up waves hand their sums over through LDS (two pairs per
+    // ring buffer, from buffer 1 on)
+    const int pair = wr >> 1;
+    f32x4* xch = (f32x4*)(pair < 2 ? ring1 : ring2) + (pair % 2) * MT * 64;
+    static_assert(2 * MT * 64 * 16 <= KW * AE * (int)sizeof(T) && 1 + RW / 4 < NS, "exchange space");
+    __syncthreads();  // every wave is done reading the ring
     if (wk == 0 && (wr & 1)) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i) xch[((wr >> 1) * MT + i) * 64 + lane] = acc[i][0];
+      for (int i = 0; i < MT; ++i) xch[i * 64 + lane] = acc[i][0];
     }
     __syncthreads();
     if (wk > 0 || (wr & 1) || n >= p.N) return;
     const int jcol = (n0 + 16 * wr) / 2 + r16;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      const f32x4 up = xch[((wr >> 1) * MT + i) * 64 + lane];
+      const f32x4 up = xch[i * 64 + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 16 * i + rb + r;
@@ -285,69 +294,47 @@ void gemm_stream_kernel(GemmArgs p) {
   }
 }
 
-template <bool Q80, int MT, int KW>
+template <bool Q80, int MT, int KW, int RW, int NS>
 hipError_t launch_stream(int grid, int epi, const GemmArgs& a, hipStream_t s) {
-  constexpr int threads = 64 * kRowWaves * KW;
+  constexpr int threads = 64 * RW * KW;
   switch (epi) {
     case EPI_BIAS_F32:
-      gemm_stream_kernel<f16, Q80, MT, KW, EPI_BIAS_F32><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_BIAS_F32><<<grid, threads, 0, s>>>(a);
       break;
     case EPI_RESID_F32:
-      gemm_stream_kernel<f16, Q80, MT, KW, EPI_RESID_F32><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_RESID_F32><<<grid, threads, 0, s>>>(a);
       break;
     case EPI_RESID_BF16:
-      gemm_stream_kernel<bf16, Q80, MT, KW, EPI_RESID_BF16><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<bf16, Q80, MT, KW, RW, NS, EPI_RESID_BF16><<<grid, threads, 0, s>>>(a);
       break;
     default:
-      gemm_stream_kernel<f16, Q80, MT, KW, EPI_SILU_GATE><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_SILU_GATE><<<grid, threads, 0, s>>>(a);
       break;
   }
   return hipGetLastError();
 }
 
-template <bool Q80, int MT>
-hipError_t launch_mt(int kw, int grid, int epi, const GemmArgs& a, hipStream_t s) {
-  if constexpr (MT == 8) return launch_stream<Q80, 8, 1>(grid, epi, a, s);  // LDS: one slice only
-  else return kw == 1 ? launch_stream<Q80, MT, 1>(grid, epi, a, s) : launch_stream<Q80, MT, 2>(grid, epi, a, s);
-}
-
 }  // namespace
 
-// cfg = 100 + 10 * MT + KW.  Picks the fewest K splits (each costs a round
-// trip of M x N fp32 partials) that still give every CU a workgroup and
-// at least six waves (enough weight bytes in flight to cover HBM latency),
-// preferring two k-slices per workgroup over a split.
+// Shapes of the stream kernel that are built: (MT, RW, NS, KW).
+// cfg = 10000 + 1000 * MT + 100 * RW + 10 * NS + KW.
+int stream_cfg(int MT, int RW, int NS, int KW) { return 10000 + 1000 * MT + 100 * RW + 10 * NS + KW; }
+
+// One 4-wave workgroup per 64 weight rows; K is split across workgroups
+// (fp32 partials plus a reduction launch) only until there are 128
+// workgroups: measured on the decode shapes, fewer, longer streams beat
+// more parallelism once the split-K round trip and second launch are paid.
 bool skinny_plan(int M, int N, int K, int epi, GemmPlan* pl) {
+  (void)epi;
   if (M > 128 || K % 32 != 0) return false;
-  constexpr int kCUs = 256;
   const int MT = M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  const int rows = 16 * kRowWaves;
-  const int n_tiles = cdiv(N, rows);
+  constexpr int RW = 4, NS = 4;
+  const int n_tiles = cdiv(N, 16 * RW);
   const int KS = cdiv(K / 32, 2);
-  int best_s = 1, best_kw = 1;
-  long best_waves = -1;
-  bool found = false;
-  for (int s = 1; s <= 32 && !found; s *= 2) {
-    for (int kw = 1; kw <= (MT == 8 ? 1 : 2); ++kw) {
-      const int per_split = cdiv(KS, s);
-      if (s > 1 && per_split / kw < 4) continue;   // too short to fill the pipeline
-      const long wgs = (long)n_tiles * cdiv(KS, per_split);
-      const long waves = wgs * kRowWaves * kw;
-      if (wgs >= kCUs && waves >= 6 * kCUs) {
-        best_s = s;
-        best_kw = kw;
-        found = true;
-        break;
-      }
-      if (waves > best_waves) {
-        best_waves = waves;
-        best_s = s;
-        best_kw = kw;
-      }
-    }
-  }
-  pl->cfg = 100 + 10 * MT + best_kw;
-  pl->k_tiles_per_split = cdiv(KS, best_s);
+  int s = 1;
+  while (n_tiles * s < 128 && cdiv(KS, 2 * s) >= 2 * NS) s *= 2;
+  pl->cfg = stream_cfg(MT, RW, NS, 1);
+  pl->k_tiles_per_split = cdiv(KS, s);
   pl->splits = cdiv(KS, pl->k_tiles_per_split);
   pl->grid = n_tiles * pl->splits;
   pl->ws_floats = pl->splits > 1 ? (size_t)pl->splits * M * N : 0;
@@ -356,10 +343,15 @@ bool skinny_plan(int M, int N, int K, int epi, GemmPlan* pl) {
 
 hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, bool q80, int epi,
                               hipStream_t s) {
-  const int MT = (pl.cfg - 100) / 10, kw = pl.cfg % 10;
-  if (MT == 2) return q80 ? launch_mt<true, 2>(kw, pl.grid, epi, a, s) : launch_mt<false, 2>(kw, pl.grid, epi, a, s);
-  if (MT == 4) return q80 ? launch_mt<true, 4>(kw, pl.grid, epi, a, s) : launch_mt<false, 4>(kw, pl.grid, epi, a, s);
-  return q80 ? launch_mt<true, 8>(1, pl.grid, epi, a, s) : launch_mt<false, 8>(1, pl.grid, epi, a, s);
+#define TDL_STREAM_CFG(MT, RW, NS, KW)                                                      \
+  if (pl.cfg == stream_cfg(MT, RW, NS, KW))                                                 \
+    return q80 ? launch_stream<true, MT, KW, RW, NS>(pl.grid, epi, a, s)                    \
+               : launch_stream<false, MT, KW, RW, NS>(pl.grid, epi, a, s);
+  TDL_STREAM_CFG(2, 4, 4, 1)
+  TDL_STREAM_CFG(4, 4, 4, 1)
+  TDL_STREAM_CFG(8, 4, 4, 1)
+#undef TDL_STREAM_CFG
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tdl
