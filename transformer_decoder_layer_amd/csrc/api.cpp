@@ -81,6 +81,9 @@ struct tdl_layer {
   __half* wo_s = nullptr;
   void* wgu = nullptr;
   __half* wgu_s = nullptr;
+  // per weight matrix (QKV, output, gate/up, down): stored in the packed
+  // tile layout (bf16/fp16 with N % 16 == 0 and K % 64 == 0) or row-major
+  int packed[4] = {0, 0, 0, 0};
   void* wd = nullptr;
   __half* wd_s = nullptr;
   float *ln1 = nullptr, *ln2 = nullptr, *qn = nullptr, *kn = nullptr;
@@ -207,8 +210,8 @@ KvPool pool_of(const tdl_layer* L, const tdl_kv_cache* kv) {
 }
 
 tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const void* A, const void* B,
-                    const __half* Bs, int epi, const float* bias, const void* resid, int ldr,
-                    void* C, int ldc) {
+                    const __half* Bs, int packed, int epi, const float* bias, const void* resid,
+                    int ldr, void* C, int ldc) {
   const GemmPlan pl = gemm_plan(M, N, K, L->q80, epi);
   if (pl.ws_floats > L->gemm_ws_floats)
     return fail(TDL_E_CAPACITY, "GEMM workspace too small for M=%d N=%d K=%d", M, N, K);
@@ -227,6 +230,7 @@ tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const voi
   a.C = C;
   a.ldc = ldc;
   a.ws = L->gemm_ws;
+  a.b_packed = packed;
   HIP_TRY(gemm_launch(pl, a, L->q80, epi, st));
   return TDL_OK;
 }
@@ -282,7 +286,7 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   }
   {
     StageTimer t(L, TDL_STAGE_QKV, st);
-    TRY(run_gemm(L, st, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, EPI_BIAS_F32, L->bqkv, nullptr,
+    TRY(run_gemm(L, st, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->packed[0], EPI_BIAS_F32, L->bqkv, nullptr,
                  0, L->qkv, L->Nqkv));
   }
   {
@@ -300,7 +304,7 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   }
   {
     StageTimer t(L, TDL_STAGE_O_PROJ, st);
-    TRY(run_gemm(L, st, rows, H, Hq * D, L->o, L->wo, L->wo_s, EPI_RESID_F32, nullptr, x, H, L->h,
+    TRY(run_gemm(L, st, rows, H, Hq * D, L->o, L->wo, L->wo_s, L->packed[1], EPI_RESID_F32, nullptr, x, H, L->h,
                  H));
   }
   {
@@ -309,12 +313,12 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   }
   {
     StageTimer t(L, TDL_STAGE_GATE_UP, st);
-    TRY(run_gemm(L, st, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, EPI_SILU_GATE, nullptr, nullptr, 0,
+    TRY(run_gemm(L, st, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, L->packed[2], EPI_SILU_GATE, nullptr, nullptr, 0,
                  L->a, I));
   }
   {
     StageTimer t(L, TDL_STAGE_DOWN, st);
-    TRY(run_gemm(L, st, rows, H, I, L->a, L->wd, L->wd_s, EPI_RESID_BF16, nullptr, L->h, H, y, H));
+    TRY(run_gemm(L, st, rows, H, I, L->a, L->wd, L->wd_s, L->packed[3], EPI_RESID_BF16, nullptr, L->h, H, y, H));
   }
   return TDL_OK;
 }
@@ -441,6 +445,26 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
       L->allocs.erase(std::find(L->allocs.begin(), L->allocs.end(), p));
       (void)hipFree(p);
     }
+  }
+  if (!q80) {
+    // repack every matrix the tiled readers can take (one temporary the size
+    // of the largest)
+    const int shapes[4][2] = {{L->Nqkv, H}, {H, QD}, {2 * I, H}, {H, I}};
+    void* mats[4] = {L->wqkv, L->wo, L->wgu, L->wd};
+    size_t most = 0;
+    for (auto& sh : shapes) most = std::max(most, (size_t)sh[0] * sh[1] * 2);
+    void* tmp = nullptr;
+    CTRY(dalloc(L, &tmp, most));
+    for (int i = 0; i < 4; ++i) {
+      if (shapes[i][0] % 16 != 0 || shapes[i][1] % 64 != 0) continue;
+      CHIP(pack_weights(mats[i], tmp, shapes[i][0], shapes[i][1], st));
+      CHIP(hipMemcpyAsync(mats[i], tmp, (size_t)shapes[i][0] * shapes[i][1] * 2,
+                          hipMemcpyDeviceToDevice, st));
+      L->packed[i] = 1;
+    }
+    CHIP(hipStreamSynchronize(st));
+    L->allocs.erase(std::find(L->allocs.begin(), L->allocs.end(), tmp));
+    (void)hipFree(tmp);
   }
   if (q80) {
     CTRY(dalloc(L, &L->wqkv_s, (size_t)L->Nqkv * (H / 32) * 2));

@@ -52,9 +52,12 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 
 
 // DIRECT: operand tiles go from global memory straight into LDS
-// (global_load_lds_dwordx4, no staging registers); each lane fetches the
+// (global_load_lds_dwordx4, no staging registers).  A: each lane fetches the
 // 16-byte chunk that belongs at its fixed LDS slot, so the XOR swizzle is
-// applied on the source side.  Needs K % 64 == 0 and bf16/fp16 weights.
+// applied on the source side.  B: weights in the packed tile layout
+// (pack_weights); one load instruction copies one 1 KB tile as is, and a
+// B fragment is then chunk `lane` of a tile in LDS (linear, conflict-free).
+// Needs K % 64 == 0 and packed bf16/fp16 weights.
 template <int BM, int BN, int WM, int WN, bool Q80, int EPI, typename T, bool DIRECT>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   typedef typename Mfma<T>::v8 T8;
@@ -180,12 +183,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
       const T* src = A + (size_t)grow * p.lda + k0 + ((pc ^ (row & 7)) << 3);
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&Ad[i * 512], 16, 0, 0);
     }
+    // B: instruction i copies tile (k slice i / (BN/16), row group i % (BN/16));
+    // groups past N repeat the last one (computed, never stored)
     const T* __restrict__ B = (const T*)p.B;
+    const int NG = p.N >> 4;
 #pragma unroll
     for (int i = wave; i < BN / 8; i += NW) {
-      const int row = i * 8 + r8;
-      const int grow = min(n0 + row, p.N - 1);
-      const T* src = B + (size_t)grow * p.ldb + k0 + ((pc ^ (row & 7)) << 3);
+      const int ks = (k0 >> 5) + i / (BN / 16);
+      const int grp = min((n0 >> 4) + i % (BN / 16), NG - 1);
+      const T* src = B + ((size_t)ks * NG + grp) * 512 + lane * 8;
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&Bd[i * 512], 16, 0, 0);
     }
   };
@@ -253,7 +259,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
         af[i] = *(const T8*)(&Ab[swz(wm * WTM + i * 16 + (lane & 15), ch)]);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const T8 bfr = *(const T8*)(&Bb[swz(wn * WTN + j * 16 + (lane & 15), ch)]);
+        const T8 bfr = DIRECT ? *(const T8*)(&Bb[(kk * (BN / 16) + (wn * WTN + j * 16) / 16) * 512 + lane * 8])
+                              : *(const T8*)(&Bb[swz(wn * WTN + j * 16 + (lane & 15), ch)]);
         if constexpr (!Q80) {
 #pragma unroll
           for (int i = 0; i < FM; ++i) acc[i][j] = Mfma<T>::mma(af[i], bfr, acc[i][j]);
@@ -465,8 +472,12 @@ hipError_t launch_cfg2(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
 template <bool Q80, int EPI, typename T>
 hipError_t launch_cfg(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
   if constexpr (!Q80) {
-    if (a.K % BK == 0) return launch_cfg2<Q80, EPI, T, true>(cfg, grid, a, s);
+    if (a.b_packed) {
+      if (a.K % BK != 0 || a.N % 16 != 0) return hipErrorInvalidValue;
+      return launch_cfg2<Q80, EPI, T, true>(cfg, grid, a, s);
+    }
   }
+  if (a.b_packed) return hipErrorInvalidValue;  // Q8_0 codes are row-major
   return launch_cfg2<Q80, EPI, T, false>(cfg, grid, a, s);
 }
 

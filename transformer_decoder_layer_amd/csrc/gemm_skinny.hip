@@ -11,9 +11,12 @@
 //    and up rows of an output column sit in neighbouring row waves and meet
 //    in LDS at the end.)
 //  * Weights go straight from HBM into MFMA operand registers (16 bytes =
-//    8 consecutive k of one row per lane), in kStages rotating register
-//    sets: the loads of stage s + kStages - 1 are issued before the MFMAs of
-//    stage s, so kStages - 1 stages of every wave are always in flight.
+//    8 consecutive k of one row per lane), in NS rotating register sets: the
+//    loads of stage s + NS - 1 are issued before the MFMAs of stage s, so
+//    NS - 1 stages of every wave are always in flight.  In the packed tile
+//    layout (pack_weights) a fragment is one contiguous 1 KB read; row-major
+//    weights give each load 16 rows x 64 bytes, which HBM serves markedly
+//    slower.
 //  * The activations of a stage (all M rows x 64 k) are shared by the four
 //    row waves of a slice: they go from global memory (L2-resident) into an
 //    LDS ring of kStages buffers with direct-to-LDS loads, each of the four
@@ -137,8 +140,8 @@ void gemm_stream_kernel(GemmArgs p) {
           b[f][u].codes = *(const uint2*)((const int8_t*)p.B + b_row[f] * p.ldb + k);
           b[f][u].scale = *(const uint16_t*)(p.B_scale + b_row[f] * (p.ldb / 32) + ks);
         } else if constexpr (PACKED) {
-          // [N/16][K/32] tiles of 512 elements: [k8 group][row][8 k]
-          b[f][u].v = *(const T8*)((const T*)p.B + ((size_t)(b_row[f] >> 4) * KS32 + ks) * 512 + lane * 8);
+          // fragment = chunk `lane` of tile (row group, ks): one 1 KB read
+          b[f][u].v = *(const T8*)((const T*)p.B + ((size_t)ks * (p.N >> 4) + (b_row[f] >> 4)) * 512 + lane * 8);
         } else {
           b[f][u].v = *(const T8*)((const T*)p.B + b_row[f] * p.ldb + k);
         }
@@ -294,24 +297,35 @@ void gemm_stream_kernel(GemmArgs p) {
   }
 }
 
-template <bool Q80, int MT, int KW, int RW, int NS>
-hipError_t launch_stream(int grid, int epi, const GemmArgs& a, hipStream_t s) {
+template <bool Q80, int MT, int KW, int RW, int NS, bool PK>
+hipError_t launch_stream2(int grid, int epi, const GemmArgs& a, hipStream_t s) {
   constexpr int threads = 64 * RW * KW;
   switch (epi) {
     case EPI_BIAS_F32:
-      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_BIAS_F32><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_BIAS_F32, PK><<<grid, threads, 0, s>>>(a);
       break;
     case EPI_RESID_F32:
-      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_RESID_F32><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_RESID_F32, PK><<<grid, threads, 0, s>>>(a);
       break;
     case EPI_RESID_BF16:
-      gemm_stream_kernel<bf16, Q80, MT, KW, RW, NS, EPI_RESID_BF16><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<bf16, Q80, MT, KW, RW, NS, EPI_RESID_BF16, PK><<<grid, threads, 0, s>>>(a);
       break;
     default:
-      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_SILU_GATE><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_SILU_GATE, PK><<<grid, threads, 0, s>>>(a);
       break;
   }
   return hipGetLastError();
+}
+
+template <bool Q80, int MT, int KW, int RW, int NS>
+hipError_t launch_stream(int grid, int epi, const GemmArgs& a, hipStream_t s) {
+  if constexpr (Q80) {
+    if (a.b_packed) return hipErrorInvalidValue;  // Q8_0 codes stay row-major
+    return launch_stream2<true, MT, KW, RW, NS, false>(grid, epi, a, s);
+  } else {
+    return a.b_packed ? launch_stream2<false, MT, KW, RW, NS, true>(grid, epi, a, s)
+                      : launch_stream2<false, MT, KW, RW, NS, false>(grid, epi, a, s);
+  }
 }
 
 }  // namespace

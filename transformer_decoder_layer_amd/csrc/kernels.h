@@ -34,6 +34,9 @@ struct GemmArgs {
   float* ws;         // split-K partial slices [splits][M][N] fp32
   int splits;
   int k_tiles_per_split;
+  int b_packed;      // B (bf16/fp16, K % 64 == 0, N % 16 == 0) in the tiled
+                     // layout written by pack_weights instead of row-major;
+                     // the large-M kernels take such B only in that layout
 };
 
 // Picks a tile configuration and split count for (M, N, K) and returns the
@@ -115,6 +118,19 @@ hipError_t convert_weights(const void* src, int src_f32, void* dst, int dst_f16,
 hipError_t interleave_gate_up(const void* gate, const void* up, int elem_bytes_row, int I,
                               void* dst, hipStream_t s);
 hipError_t copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+// Row-major [N][K] 2-byte weights -> tiles of 16 rows x 32 k (1 KB), tile
+// (n/16, k/32) at ((k/32) * N/16 + n/16) * 512 elements (all row groups of a
+// 32-k slice side by side), inside a tile [k/8 % 4][n % 16][k % 8]: the
+// 16-byte chunk lane l of a 16x16x32 MFMA fragment needs (row l%16, k
+// 8*(l/16)..+7) is chunk l of its tile, so a fragment load, from memory or
+// from a tile copied to LDS as is, is one contiguous 1 KB access.  Needs
+// N % 16 == 0, K % 32 == 0.
+hipError_t pack_weights(const void* src, void* dst, int N, int K, hipStream_t s);
+// Element offset of (n, k) in that layout.
+__host__ __device__ inline size_t packed_offset(int n, int k, int N) {
+  return ((size_t)(k >> 5) * (N >> 4) + (n >> 4)) * 512 + (size_t)((((k >> 3) & 3) << 4) + (n & 15)) * 8 +
+         (k & 7);
+}
 
 // ------------------------------------------------------------- attention
 // Flash prefill attention over sequences 0..n_prefill-1 of `seq`; K/V read

@@ -257,6 +257,17 @@ __global__ void interleave_kernel(const uint8_t* __restrict__ gate, const uint8_
     *(uint32_t*)(d + b) = *(const uint32_t*)(s + b);
 }
 
+// one thread per 16-byte chunk (8 elements of one row), written to its
+// packed position
+__global__ void pack_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int N, int K) {
+  const int64_t chunks = (int64_t)N * (K / 8);
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int n = (int)(c / (K / 8)), k = (int)(c % (K / 8)) * 8;
+    dst[packed_offset(n, k, N) / 8] = src[c];
+  }
+}
+
 __global__ void rope_table_kernel(float2* tab, int max_pos, int D, double theta) {
   const int half = D / 2;
   const int64_t n = (int64_t)max_pos * half;
@@ -332,6 +343,12 @@ hipError_t interleave_gate_up(const void* gate, const void* up, int row_bytes, i
                               hipStream_t s) {
   interleave_kernel<<<2 * I, 256, 0, s>>>((const uint8_t*)gate, (const uint8_t*)up, row_bytes, I,
                                           (uint8_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t pack_weights(const void* src, void* dst, int N, int K, hipStream_t s) {
+  if (N % 16 != 0 || K % 32 != 0) return hipErrorInvalidValue;
+  pack_kernel<<<2048, 256, 0, s>>>((const uint4*)src, (uint4*)dst, N, K);
   return hipGetLastError();
 }
 
