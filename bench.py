@@ -53,6 +53,29 @@ def parse():
     return ap.parse_args()
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_qwen25_prefill4096_hbm_traffic.txt")
+GEMM_SOURCES = ["gemm.hip", "common.h", "kernels.h"]
+
+
+def measured_traffic():
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by the copy-kernel
+    calibration), or None when the GEMM sources changed since it was taken."""
+    import hashlib
+    try:
+        line = [l for l in open(TRAFFIC_FILE) if l.startswith("TRAFFIC ")][-1]
+    except (OSError, IndexError):
+        return None
+    meta = json.loads(line[len("TRAFFIC "):])
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "transformer_decoder_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != meta.get("kernel_source_sha256"):
+        return None
+    return meta.get("traffic_bytes_per_launch")
+
+
 def linear_flops_per_token(s):
     D = s.head_dim
     n = (s.n_q_heads + 2 * s.n_kv_heads) * D * s.hidden + s.hidden * s.n_q_heads * D \
@@ -120,7 +143,8 @@ def main():
     gu_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "gate_up GEMM + SiLU-gate (fp16 operands)",
                 "achieved": round(gu_tflops, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gu_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                "frac": round(gu_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": measured_traffic(),
+                "algorithmic_bytes": 2 * (T * H + 2 * I * H + T * I),
                 "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 4)}
     layer_tflops = step_flops / (ms_step * 1e-3) / 1e12
     stage_report = {k: round(v, 4) for k, v in stage_ms.items() if v}
