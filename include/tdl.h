@@ -153,7 +153,9 @@ typedef struct {
 /* Device pointers to a layer's intermediate buffers, valid after a call has
  * completed on its stream, for stage-by-stage checks.  Row r of each holds
  * the call's row r.  xn [rows, H] fp16 (RMSNorm-1 output); qkv [rows,
- * (Hq+2Hkv)*D] float32 (projections + bias, before RoPE); q [rows, Hq, D]
+ * (Hq+2Hkv)*D] float32 (projections + bias, before RoPE; not written when a
+ * decode-sized projection is split over K: the RoPE kernel then sums the
+ * split partial products itself); q [rows, Hq, D]
  * float32 (after Q-norm and RoPE); o [rows, Hq*D] fp16 (attention output);
  * h [rows, H] float32 (first residual); hn [rows, H] fp16 (RMSNorm-2
  * output); a [rows, I] bf16 (silu(gate) * up).

@@ -209,10 +209,13 @@ KvPool pool_of(const tdl_layer* L, const tdl_kv_cache* kv) {
   return p;
 }
 
+// defer: a split-K plan leaves its fp32 partials in the GEMM workspace for
+// the next kernel to sum (*splits_out tells how many; 1 = C was written).
 tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const void* A, const void* B,
                     const __half* Bs, int packed, int epi, const float* bias, const void* resid,
-                    int ldr, void* C, int ldc) {
+                    int ldr, void* C, int ldc, bool defer = false, int* splits_out = nullptr) {
   const GemmPlan pl = gemm_plan(M, N, K, L->q80, epi);
+  if (splits_out) *splits_out = defer ? pl.splits : 1;
   if (pl.ws_floats > L->gemm_ws_floats)
     return fail(TDL_E_CAPACITY, "GEMM workspace too small for M=%d N=%d K=%d", M, N, K);
   GemmArgs a{};
@@ -231,7 +234,7 @@ tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const voi
   a.ldc = ldc;
   a.ws = L->gemm_ws;
   a.b_packed = packed;
-  HIP_TRY(gemm_launch(pl, a, L->q80, epi, st));
+  HIP_TRY(gemm_launch(pl, a, L->q80, epi, st, !defer));
   return TDL_OK;
 }
 
@@ -268,6 +271,8 @@ struct StageTimer {
 // The whole layer over `rows` rows.  Sequences 0..n_prefill-1 of `seq` use the
 // prefill attention kernel, decode sequences dec_first .. dec_first+n_dec-1
 // the paged decode kernel.
+constexpr int kFusedNormMaxH = 8192;  // hidden sizes the fused split-sum RMSNorm takes
+
 tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int rows, SeqInfo seq,
                      KvPool pool, int n_prefill, int max_q_len, int dec_first, int n_dec,
                      int max_ctx_len) {
@@ -284,15 +289,21 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
     StageTimer t(L, TDL_STAGE_RMSNORM1, st);
     HIP_TRY(rmsnorm_bf16in(x, L->ln1, L->xn, rows, H, c.rms_eps, st));
   }
+  // a split QKV projection is summed (with its bias) by the RoPE kernel, and
+  // a split output projection (with the residual) by RMSNorm-2: two fewer
+  // launches and no second round trip of the sums
+  int qkv_splits = 1;
   {
     StageTimer t(L, TDL_STAGE_QKV, st);
     TRY(run_gemm(L, st, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->packed[0], EPI_BIAS_F32, L->bqkv, nullptr,
-                 0, L->qkv, L->Nqkv));
+                 0, L->qkv, L->Nqkv, true, &qkv_splits));
   }
   {
     StageTimer t(L, TDL_STAGE_ROPE_KV, st);
-    HIP_TRY(rope_kv_write(L->qkv, rows, Hq, Hkv, D, L->rope, c.qk_norm ? L->qn : nullptr,
-                          c.qk_norm ? L->kn : nullptr, c.rms_eps, L->q, seq, pool, st));
+    HIP_TRY(rope_kv_write(qkv_splits > 1 ? (const void*)L->gemm_ws : (const void*)L->qkv, rows, Hq, Hkv,
+                          D, L->rope, c.qk_norm ? L->qn : nullptr, c.qk_norm ? L->kn : nullptr,
+                          c.rms_eps, L->q, seq, pool, st, qkv_splits,
+                          qkv_splits > 1 ? L->bqkv : nullptr));
   }
   if (n_prefill) {
     StageTimer t(L, TDL_STAGE_ATTN_PREFILL, st);
@@ -302,14 +313,18 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
     StageTimer t(L, TDL_STAGE_ATTN_DECODE, st);
     HIP_TRY(attn_decode(dp, L->q, pool, seq, dec_first, n_dec, Hq, Hkv, D, L->o, L->dec_part, st));
   }
+  int o_splits = 1;
   {
     StageTimer t(L, TDL_STAGE_O_PROJ, st);
     TRY(run_gemm(L, st, rows, H, Hq * D, L->o, L->wo, L->wo_s, L->packed[1], EPI_RESID_F32, nullptr, x, H, L->h,
-                 H));
+                 H, H <= kFusedNormMaxH, &o_splits));
   }
   {
     StageTimer t(L, TDL_STAGE_RMSNORM2, st);
-    HIP_TRY(rmsnorm_f32in(L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
+    if (o_splits > 1)
+      HIP_TRY(rmsnorm_splits_resid(L->gemm_ws, o_splits, x, L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
+    else
+      HIP_TRY(rmsnorm_f32in(L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
   }
   {
     StageTimer t(L, TDL_STAGE_GATE_UP, st);

@@ -581,9 +581,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 }
 
 // Merges the context partitions of sequences with more than one: one
-// workgroup per (sequence, KV head), partitions combined in order.
+// workgroup per (sequence, KV head).  The per-(partition, head) weights
+// exp2(m_p - M) / L come first (LDS), then every output element sums its
+// partitions with independent loads.
+constexpr int kMaxDecodeParts = 256;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_merge_kernel(DecArgs a) {
+  __shared__ float sw[kMaxDecodeParts][16];  // m, then the partition weight
+  __shared__ float sl[kMaxDecodeParts][16];
   const int g = blockIdx.x, b = blockIdx.y;
   const int sidx = a.first_seq + b;
   const int n_rep = a.Hq / a.Hkv;
@@ -592,18 +598,38 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(DecArgs a) {
   if (n_parts <= 1) return;
   const int row = seq_row(a.seq, sidx);
   const float* base = a.part + ((size_t)b * a.Hkv + g) * a.max_parts * kPartStride(D);
-  for (int e = threadIdx.x; e < n_rep * D; e += 256) {
-    const int hh = e / D, d = e % D;
-    float M = -INFINITY;
-    for (int q = 0; q < n_parts; ++q) M = fmaxf(M, base[q * kPartStride(D) + 16 * D + 2 * hh]);
-    float O = 0.f, L = 0.f;
-    for (int q = 0; q < n_parts; ++q) {
-      const float* pq = base + q * kPartStride(D);
-      const float f = exp2f(pq[16 * D + 2 * hh] - M);
-      O += pq[hh * D + d] * f;
-      L += pq[16 * D + 2 * hh + 1] * f;
+  for (int e = threadIdx.x; e < n_parts * 16; e += 256) {
+    const int q = e / 16, hh = e % 16;
+    if (hh < n_rep) {
+      sw[q][hh] = base[q * kPartStride(D) + 16 * D + 2 * hh];
+      sl[q][hh] = base[q * kPartStride(D) + 16 * D + 2 * hh + 1];
     }
-    a.o[(size_t)row * a.Hq * D + (size_t)(g * n_rep + hh) * D + d] = to_f16(O / L);
+  }
+  __syncthreads();
+  if (threadIdx.x < n_rep) {
+    const int hh = threadIdx.x;
+    float M = -INFINITY;
+    for (int q = 0; q < n_parts; ++q) M = fmaxf(M, sw[q][hh]);
+    float L = 0.f;
+    for (int q = 0; q < n_parts; ++q) L += sl[q][hh] * exp2f(sw[q][hh] - M);
+    const float inv = 1.f / L;
+    for (int q = 0; q < n_parts; ++q) sw[q][hh] = exp2f(sw[q][hh] - M) * inv;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n_rep * D; e += 256) {
+    const int hh = e / D;
+    float O = 0.f;
+    int q = 0;
+    for (; q + 4 <= n_parts; q += 4) {
+      const float o0 = base[(q + 0) * kPartStride(D) + e], o1 = base[(q + 1) * kPartStride(D) + e];
+      const float o2 = base[(q + 2) * kPartStride(D) + e], o3 = base[(q + 3) * kPartStride(D) + e];
+      O += o0 * sw[q][hh];
+      O += o1 * sw[q + 1][hh];
+      O += o2 * sw[q + 2][hh];
+      O += o3 * sw[q + 3][hh];
+    }
+    for (; q < n_parts; ++q) O += base[q * kPartStride(D) + e] * sw[q][hh];
+    a.o[(size_t)row * a.Hq * D + (size_t)g * n_rep * D + e] = to_f16(O);
   }
 }
 
@@ -641,6 +667,7 @@ DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len) {
   // still a few hundred workgroups
   int pb = 32;
   while (pb > 4 && (long)batch * Hkv * cdiv(max_blk, pb) < 1024) pb /= 2;
+  while (cdiv(max_blk, pb) > kMaxDecodeParts) pb *= 2;  // the merge kernel's LDS bound
   pl.part_blocks = pb;
   pl.max_parts = cdiv(max_blk, pb);
   pl.part_floats = (size_t)batch * Hkv * pl.max_parts * kPartStride(D);

@@ -51,6 +51,103 @@ __device__ __forceinline__ int swz(int row, int chunk) {  // offset in bf16 elem
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 
+// Result of one wave's FM x FN accumulator block whose top-left output
+// element is (mw, nw): v[i][j][r] = C[mw + i*16 + 4*(lane/16) + r][nw + j*16 +
+// lane%16].  One split: the epilogue; several: the fp32 partial tile goes to
+// ws[split][M][N] and a second kernel sums the slices in order and applies
+// the epilogue (no cross-workgroup handshake, which would need device-wide
+// L2 write-backs on a multi-XCD part).
+template <int EPI, int FM, int FN>
+__device__ __forceinline__ void gemm_store(const GemmArgs& p, const f32x4 (&v)[FM][FN], int mw, int nw,
+                                           int split, int lane) {
+  const int col = lane & 15;
+  const int rbase = mw + 4 * (lane >> 4);
+  if (p.splits > 1) {
+    float* part = p.ws + (size_t)split * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = nw + j * 16 + col;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = rbase + i * 16 + r;
+          if (m < p.M) part[(size_t)m * p.N + n] = v[i][j][r];
+        }
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_SILU_GATE) {
+    bf16* __restrict__ C = (bf16*)p.C;
+#pragma unroll
+    for (int jp = 0; jp < FN / 2; ++jp) {
+      const int ng = nw + jp * 32;   // first gate column of the pair
+      const int jcol = ng / 2 + col;  // output column
+      if (ng + col >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = rbase + i * 16 + r;
+          if (m < p.M) {
+            const float g = v[i][2 * jp][r], u = v[i][2 * jp + 1][r];
+            C[(size_t)m * p.ldc + jcol] = f32_to_bf16(silu_f(g) * u);
+          }
+        }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = nw + j * 16 + col;
+      if (n >= p.N) continue;
+      float bias = 0.f;
+      if constexpr (EPI == EPI_BIAS_F32)
+        if (p.bias) bias = p.bias[n];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = rbase + i * 16 + r;
+          if (m >= p.M) continue;
+          const float val = v[i][j][r];
+          if constexpr (EPI == EPI_BIAS_F32) {
+            ((float*)p.C)[(size_t)m * p.ldc + n] = val + bias;
+          } else if constexpr (EPI == EPI_RESID_F32) {
+            const float res = bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
+            ((float*)p.C)[(size_t)m * p.ldc + n] = val + res;
+          } else {
+            const float res = ((const float*)p.resid)[(size_t)m * p.ldr + n];
+            ((bf16*)p.C)[(size_t)m * p.ldc + n] = f32_to_bf16(val + res);
+          }
+        }
+    }
+  }
+}
+
+// Tile of a workgroup.  Workgroups are dispatched round-robin over the 8
+// XCDs (each with its own L2); remap so that consecutive logical ids run on
+// one XCD, then walk tiles in groups of 8 M-tiles sharing a B panel.
+template <int BM, int BN>
+__device__ __forceinline__ void tile_of(const GemmArgs& p, int* m0, int* n0, int* split) {
+  const int tiles_m = cdiv(p.M, BM), tiles_n = cdiv(p.N, BN);
+  int bid = blockIdx.x;
+  {
+    const int nwg = gridDim.x, per = nwg / 8, rem = nwg % 8;
+    const int xcd = bid % 8, slot = bid / 8;
+    bid = xcd * per + min(xcd, rem) + slot;
+  }
+  *split = bid % p.splits;
+  const int tile = bid / p.splits;
+  constexpr int GROUP = 8;
+  const int group_size = GROUP * tiles_n;
+  const int gidx = tile / group_size;
+  const int first_m = gidx * GROUP;
+  const int gm = min(tiles_m - first_m, GROUP);
+  *m0 = (first_m + (tile % group_size) % gm) * BM;
+  *n0 = ((tile % group_size) / gm) * BN;
+}
+
 // DIRECT: operand tiles go from global memory straight into LDS
 // (global_load_lds_dwordx4, no staging registers).  A: each lane fetches the
 // 16-byte chunk that belongs at its fixed LDS slot, so the XOR swizzle is
@@ -86,26 +183,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   const int wm = wave / WN, wn = wave % WN;
   const int col_l = lane & 15;
 
-  // ---- tile coordinates.  Workgroups are dispatched round-robin over the 8
-  // XCDs (each with its own L2); remap so that consecutive logical ids run on
-  // one XCD, then walk tiles in groups of 8 M-tiles sharing a B panel.
-  const int tiles_m = cdiv(p.M, BM), tiles_n = cdiv(p.N, BN);
-  int bid = blockIdx.x;
-  {
-    const int nwg = gridDim.x, per = nwg / 8, rem = nwg % 8;
-    const int xcd = bid % 8, slot = bid / 8;
-    bid = xcd * per + min(xcd, rem) + slot;
-  }
-  const int split = bid % p.splits;
-  const int tile = bid / p.splits;
-  constexpr int GROUP = 8;
-  const int group_size = GROUP * tiles_n;
-  const int gidx = tile / group_size;
-  const int first_m = gidx * GROUP;
-  const int gm = min(tiles_m - first_m, GROUP);
-  const int tm = first_m + (tile % group_size) % gm;
-  const int tn = (tile % group_size) / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
+  int m0, n0, split;
+  tile_of<BM, BN>(p, &m0, &n0, &split);
 
   const int KT = cdiv(p.K, BK);
   const int kt0 = split * p.k_tiles_per_split;
@@ -310,79 +389,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
     }
   }
 
-  // ---- epilogue.  v[i][j][r] = C[m0 + wm*WTM + i*16 + 4*(lane/16) + r]
-  //                                [n0 + wn*WTN + j*16 + lane%16]
-  auto epilogue = [&](const f32x4 (&v)[FM][FN]) {
-    const int col = lane & 15;
-    const int rbase = m0 + wm * WTM + 4 * (lane >> 4);
-    if constexpr (EPI == EPI_SILU_GATE) {
-      bf16* __restrict__ C = (bf16*)p.C;
-#pragma unroll
-      for (int jp = 0; jp < FN / 2; ++jp) {
-        const int ng = n0 + wn * WTN + jp * 32;  // first gate column of the pair
-        const int jcol = ng / 2 + col;           // output column
-        if (ng + col >= p.N) continue;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = rbase + i * 16 + r;
-            if (m < p.M) {
-              const float g = v[i][2 * jp][r], u = v[i][2 * jp + 1][r];
-              C[(size_t)m * p.ldc + jcol] = f32_to_bf16(silu_f(g) * u);
-            }
-          }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * WTN + j * 16 + col;
-        if (n >= p.N) continue;
-        float bias = 0.f;
-        if constexpr (EPI == EPI_BIAS_F32)
-          if (p.bias) bias = p.bias[n];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = rbase + i * 16 + r;
-            if (m >= p.M) continue;
-            const float val = v[i][j][r];
-            if constexpr (EPI == EPI_BIAS_F32) {
-              ((float*)p.C)[(size_t)m * p.ldc + n] = val + bias;
-            } else if constexpr (EPI == EPI_RESID_F32) {
-              const float res = bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
-              ((float*)p.C)[(size_t)m * p.ldc + n] = val + res;
-            } else {
-              const float res = ((const float*)p.resid)[(size_t)m * p.ldr + n];
-              ((bf16*)p.C)[(size_t)m * p.ldc + n] = f32_to_bf16(val + res);
-            }
-          }
-      }
-    }
-  };
-
-  if (p.splits == 1) {
-    epilogue(acc);
-    return;
-  }
-  // ---- split-K: this slice's fp32 partial tile goes to ws[split][M][N]; a
-  // second kernel sums the slices in order and applies the epilogue (no
-  // cross-workgroup handshake, which would need device-wide L2 write-backs
-  // on a multi-XCD part).
-  float* part = p.ws + (size_t)split * p.M * p.N;
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int n = n0 + wn * WTN + j * 16 + col_l;
-    if (n >= p.N) continue;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + r;
-        if (m < p.M) part[(size_t)m * p.N + n] = acc[i][j][r];
-      }
-  }
+  gemm_store<EPI, FM, FN>(p, acc, m0 + wm * WTM, n0 + wn * WTN, split, lane);
 }
 
 // Sum of the split-K slices in slice order, then the epilogue; one thread per
@@ -537,13 +544,13 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
   return best;
 }
 
-hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, bool q80, int epi, hipStream_t s) {
+hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, bool q80, int epi, hipStream_t s, bool reduce) {
   a.splits = pl.splits;
   a.k_tiles_per_split = pl.k_tiles_per_split;
   const hipError_t e = pl.cfg >= 10 ? gemm_skinny_launch(pl, a, q80, epi, s)
                        : q80          ? launch_epi<true>(pl.cfg, pl.grid, epi, a, s)
                                       : launch_epi<false>(pl.cfg, pl.grid, epi, a, s);
-  if (e != hipSuccess || pl.splits == 1) return e;
+  if (e != hipSuccess || pl.splits == 1 || !reduce) return e;
   const int Nout = epi == EPI_SILU_GATE ? a.N / 2 : a.N;
   const int64_t threads = (int64_t)a.M * (Nout / 4);
   const int blocks = (int)((threads + 255) / 256);

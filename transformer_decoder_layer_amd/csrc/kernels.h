@@ -55,7 +55,10 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi);
 bool skinny_plan(int M, int N, int K, int epi, GemmPlan* pl);
 hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, bool q80, int epi,
                               hipStream_t s);
-hipError_t gemm_launch(const GemmPlan& plan, GemmArgs a, bool q80, int epi, hipStream_t s);
+// reduce = false leaves split-K partials in a.ws for a consumer that sums them
+// (only meaningful when plan.splits > 1).
+hipError_t gemm_launch(const GemmPlan& plan, GemmArgs a, bool q80, int epi, hipStream_t s,
+                       bool reduce = true);
 
 // -------------------------------------------------------- element-wise
 // y[r] = fp16(x[r] * rsqrt(mean(x[r]^2) + eps) * g), x bf16 or f32.
@@ -63,6 +66,11 @@ hipError_t rmsnorm_bf16in(const void* x, const float* g, void* y, int rows, int 
                           hipStream_t s);
 hipError_t rmsnorm_f32in(const float* x, const float* g, void* y, int rows, int H, float eps,
                          hipStream_t s);
+// h = sum of `splits` fp32 partial slices [splits][rows][H] + resid (bf16),
+// written to h (fp32), and y = fp16(RMSNorm(h) * g): the split-K reduction of
+// the output projection fused with its residual and the second RMSNorm.
+hipError_t rmsnorm_splits_resid(const float* ws, int splits, const void* resid, float* h,
+                                const float* g, void* y, int rows, int H, float eps, hipStream_t s);
 
 // Per-call sequence description shared by the row-wise and attention
 // kernels.  Arrays are device int32.  Three forms: rows_are_seqs (decode:
@@ -94,10 +102,13 @@ struct KvPool {
 // Per row of qkv (float32 [rows][(Hq+2Hkv)*D]): optional per-head RMSNorm of
 // q and k, RoPE of q and k (half-split pairs, cos/sin table [max_pos][D/2]),
 // q -> q_out [rows][Hq][D] float32, k and v -> the pool slot of the row's
-// position (rounded once, from fp32).
-hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D,
-                         const float2* rope_tab, const float* q_norm, const float* k_norm,
-                         float eps, void* q_out, SeqInfo seq, KvPool pool, hipStream_t s);
+// position (rounded once, from fp32).  splits > 1: qkv holds that many fp32
+// partial slices [splits][rows][(Hq+2Hkv)*D] of the projection, summed here
+// in slice order, plus bias (may be null).
+hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, const float2* tab,
+                         const float* q_norm, const float* k_norm, float eps, void* q_out,
+                         SeqInfo seq, KvPool pool, hipStream_t s, int splits = 1,
+                         const float* bias = nullptr);
 
 // Writes caller K/V rows into the pool (kv_cache_write).
 hipError_t kv_write_rows(const void* k, const void* v, int src_f32, int rows, int Hkv, int D,

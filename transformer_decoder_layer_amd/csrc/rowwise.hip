@@ -115,27 +115,36 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
                                                       const float* __restrict__ qn,
                                                       const float* __restrict__ kn, float eps,
                                                       float* __restrict__ q_out, SeqInfo seq,
-                                                      KvPool pool) {
+                                                      KvPool pool, int splits,
+                                                      const float* __restrict__ bias) {
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = D >> 1;
   const int sidx = find_seq(seq, row);
   const int pos = row_position(seq, sidx, row);
   const int ldq = (Hq + 2 * Hkv) * D;
+  const size_t slice = (size_t)gridDim.x * ldq;
   const float* src = qkv + (size_t)row * ldq;
+  // element c of this row's projection: the partial slices in order (+ bias)
+  auto val = [&](int c) {
+    float v = src[c];
+    for (int sp = 1; sp < splits; ++sp) v += src[sp * slice + c];
+    return bias ? v + bias[c] : v;
+  };
   const bool act = lane < half;
   float2 cs = make_float2(1.f, 0.f);
   if (act) cs = tab[(size_t)pos * half + lane];
   const int blk = block_of(seq, sidx, pos);
   const int slot = pos % kBlockTokens;
 
-  for (int h = wave; h < Hq + Hkv; h += 4) {
+  // one wave per head: workgroup (row, y) takes heads 4y .. 4y+3
+  for (int h = 4 * blockIdx.y + wave; h < min(Hq + Hkv, 4 * (int)blockIdx.y + 4); h += 4) {
     const bool is_q = h < Hq;
-    const float* hp = src + (size_t)h * D;  // q heads then k heads are contiguous
+    const int hc = h * D;  // q heads then k heads are contiguous
     float x1 = 0.f, x2 = 0.f;
     if (act) {
-      x1 = hp[lane];
-      x2 = hp[lane + half];
+      x1 = val(hc + lane);
+      x2 = val(hc + lane + half);
     }
     const float* gn = is_q ? qn : kn;
     if (gn) {  // per-head RMSNorm over D
@@ -155,11 +164,62 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
       qo[lane + half] = r2;
     } else {
       const int g = h - Hq;
-      const float* vp = src + (size_t)(Hq + Hkv + g) * D;
-      const float v1 = vp[lane], v2 = vp[lane + half];
+      const int vc = (Hq + Hkv + g) * D;
+      const float v1 = val(vc + lane), v2 = val(vc + lane + half);
       store_kv(pool, blk, g, Hkv, D, slot, lane, r1, v1);
       store_kv(pool, blk, g, Hkv, D, slot, lane + half, r2, v2);
     }
+  }
+}
+
+// h = sum of the split slices (in order) + residual, kept in registers (up to
+// 256 * 8 * kSplitRowChunks columns), written once; then y = RMSNorm(h) * g.
+constexpr int kSplitRowChunks = 4;
+__global__ __launch_bounds__(256) void rmsnorm_splits_kernel(const float* __restrict__ ws, int splits,
+                                                             const bf16* __restrict__ resid,
+                                                             float* __restrict__ h,
+                                                             const float* __restrict__ g,
+                                                             f16* __restrict__ y, int H, float eps) {
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const size_t slice = (size_t)gridDim.x * H;
+  float v[kSplitRowChunks][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kSplitRowChunks; ++j) {
+    const int c = (threadIdx.x + 256 * j) * 8;
+    if (c >= H) break;
+    const size_t o = (size_t)row * H + c;
+    const bf16x8 r = *(const bf16x8*)(resid + o);
+    float4 a = *(const float4*)(ws + o), b = *(const float4*)(ws + o + 4);
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 a2 = *(const float4*)(ws + sp * slice + o), b2 = *(const float4*)(ws + sp * slice + o + 4);
+      a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+      b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+    }
+    const float p[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[j][e] = p[e] + (float)r[e];
+      ss += v[j][e] * v[j][e];
+    }
+    *(float4*)(h + o) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+    *(float4*)(h + o + 4) = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+#pragma unroll
+  for (int j = 0; j < kSplitRowChunks; ++j) {
+    const int c = (threadIdx.x + 256 * j) * 8;
+    if (c >= H) break;
+    const float4 g0 = *(const float4*)(g + c), g1 = *(const float4*)(g + c + 4);
+    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = f32_to_f16_sat(v[j][e] * inv * gg[e]);
+    *(f16x8*)(y + (size_t)row * H + c) = o;
   }
 }
 
@@ -283,6 +343,14 @@ __global__ void rope_table_kernel(float2* tab, int max_pos, int D, double theta)
 
 }  // namespace
 
+hipError_t rmsnorm_splits_resid(const float* ws, int splits, const void* resid, float* h,
+                                const float* g, void* y, int rows, int H, float eps, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (H % 8 != 0 || H > 256 * 8 * kSplitRowChunks) return hipErrorInvalidValue;
+  rmsnorm_splits_kernel<<<rows, 256, 0, s>>>(ws, splits, (const bf16*)resid, h, g, (f16*)y, H, eps);
+  return hipGetLastError();
+}
+
 hipError_t rmsnorm_bf16in(const void* x, const float* g, void* y, int rows, int H, float eps,
                           hipStream_t s) {
   if (rows == 0) return hipSuccess;
@@ -298,10 +366,10 @@ hipError_t rmsnorm_f32in(const float* x, const float* g, void* y, int rows, int 
 
 hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, const float2* tab,
                          const float* q_norm, const float* k_norm, float eps, void* q_out,
-                         SeqInfo seq, KvPool pool, hipStream_t s) {
+                         SeqInfo seq, KvPool pool, hipStream_t s, int splits, const float* bias) {
   if (rows == 0) return hipSuccess;
-  rope_kv_kernel<<<rows, 256, 0, s>>>((const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps,
-                                      (float*)q_out, seq, pool);
+  rope_kv_kernel<<<dim3(rows, cdiv(Hq + Hkv, 4)), 256, 0, s>>>(
+      (const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps, (float*)q_out, seq, pool, splits, bias);
   return hipGetLastError();
 }
 
