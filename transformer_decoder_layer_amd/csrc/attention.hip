@@ -39,6 +39,7 @@ namespace tdl {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f;  // prefill softmax: slack of the running maximum (log2 units)
 
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
@@ -49,10 +50,15 @@ __device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
 // bf16 / fp32 -> fp16, saturating at the fp16 range.  A bf16 value inside the
 // range converts exactly (8 significant bits fit in 11).
 __device__ __forceinline__ f16 to_f16(float v) { return f32_to_f16_sat(v); }
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+// one packed convert (round to nearest even) and a packed clamp to the fp16
+// range for two bf16 values
 __device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t w) {
-  const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
-  const f16 a = to_f16(lo), b = to_f16(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2v v = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  f16x2v h = __builtin_convertvector(v, f16x2v);
+  h = __builtin_elementwise_min(__builtin_elementwise_max(h, (f16x2v)(-kF16Max)), (f16x2v)(kF16Max));
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ int seq_row(const SeqInfo& s, int sidx) {
@@ -264,22 +270,30 @@ __global__ __launch_bounds__(NREP * 64) void attn_prefill_kernel(const float* __
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, st[kh][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
+      // the reference point m_run of the exponentials moves only when a row's
+      // maximum exceeds it by more than kLazy (log2 units): softmax does not
+      // depend on it, P stays <= 2^kLazy (exact in fp16), and the rescale of
+      // the accumulators is skipped for the wave in most tiles
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int t2 = 0; t2 < D / 32; ++t2) acc[t2] *= alpha;
+      }
       f16x8 pb[4];
       float psum = 0.f;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const f16 pv = (f16)exp2f(st[kh][r] - m_new);
-          psum += (float)pv;
-          pb[kh * 2 + (r >> 3)][r & 7] = pv;
+          // masked keys are -inf: exp2 gives 0
+          const float pv = __builtin_amdgcn_exp2f(st[kh][r] - m_run);
+          psum += pv;
+          pb[kh * 2 + (r >> 3)][r & 7] = (f16)pv;
         }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int t2 = 0; t2 < D / 32; ++t2) acc[t2] *= alpha;
+      l_run += psum;
       // O^T += V^T P^T, 16 keys per MFMA: chunk kc covers keys kc*16 .. +15;
       // lane supplies keys kc*16 + 4G + 0..3 and kc*16 + 8 + 4G + 0..3
 #pragma unroll

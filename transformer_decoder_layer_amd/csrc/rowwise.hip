@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
                                                       const float* __restrict__ kn, float eps,
                                                       float* __restrict__ q_out, SeqInfo seq,
                                                       KvPool pool, int splits,
-                                                      const float* __restrict__ bias) {
+                                                      const float* __restrict__ bias, int hpw) {
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = D >> 1;
@@ -137,8 +137,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
   const int blk = block_of(seq, sidx, pos);
   const int slot = pos % kBlockTokens;
 
-  // one wave per head: workgroup (row, y) takes heads 4y .. 4y+3
-  for (int h = 4 * blockIdx.y + wave; h < min(Hq + Hkv, 4 * (int)blockIdx.y + 4); h += 4) {
+  // one wave per head: workgroup (row, y) takes heads hpw*y .. hpw*y + hpw-1
+  for (int h = hpw * blockIdx.y + wave; h < min(Hq + Hkv, hpw * ((int)blockIdx.y + 1)); h += 4) {
     const bool is_q = h < Hq;
     const int hc = h * D;  // q heads then k heads are contiguous
     float x1 = 0.f, x2 = 0.f;
@@ -368,8 +368,12 @@ hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, cons
                          const float* q_norm, const float* k_norm, float eps, void* q_out,
                          SeqInfo seq, KvPool pool, hipStream_t s, int splits, const float* bias) {
   if (rows == 0) return hipSuccess;
-  rope_kv_kernel<<<dim3(rows, cdiv(Hq + Hkv, 4)), 256, 0, s>>>(
-      (const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps, (float*)q_out, seq, pool, splits, bias);
+  // few rows (decode): four heads per workgroup for parallelism; many rows
+  // (prefill): all heads of a row in one workgroup
+  const int hpw = rows >= 1024 ? Hq + Hkv : 4;
+  rope_kv_kernel<<<dim3(rows, cdiv(Hq + Hkv, hpw)), 256, 0, s>>>(
+      (const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps, (float*)q_out, seq, pool, splits, bias,
+      hpw);
   return hipGetLastError();
 }
 
