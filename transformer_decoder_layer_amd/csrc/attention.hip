@@ -675,12 +675,13 @@ DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len) {
   (void)Hq;
   DecodePlan pl{};
   const int max_blk = cdiv(max_ctx_len, kBlockTokens);
-  // partitions of 32 blocks (512 tokens): ~8 blocks per wave, long enough
-  // for the three-deep load pipeline, and enough workgroups to fill the chip
-  // when contexts are long; short batches split finer so that there are
-  // still a few hundred workgroups
-  int pb = 32;
-  while (pb > 4 && (long)batch * Hkv * cdiv(max_blk, pb) < 1024) pb /= 2;
+  // the longest partitions that still give ~2 workgroups per CU (each
+  // workgroup pays a fixed cost -- query conversion, filling the load
+  // pipeline, the four-wave merge and the partial write -- which measured as
+  // large as the streaming itself for 4-8 blocks per wave): up to 256 blocks
+  // (64 per wave), down to 4 for short batches
+  int pb = 256;
+  while (pb > 4 && (long)batch * Hkv * cdiv(max_blk, pb) < 512) pb /= 2;
   while (cdiv(max_blk, pb) > kMaxDecodeParts) pb *= 2;  // the merge kernel's LDS bound
   pl.part_blocks = pb;
   pl.max_parts = cdiv(max_blk, pb);
