@@ -1,0 +1,102 @@
+"""GPU parity at the edges of the supported shapes and sizes: every
+query-group ratio and head dimension the attention kernels are built for,
+Q8_0 weights on the decode-sized GEMM, a reduction dimension that ends in a
+half 64-k stage, calls exactly at max_tokens / max_position, and mixed steps
+with only decode or only prefill rows.  Same tolerance as the other layer
+tests (stage by stage, cache rows checked)."""
+import dataclasses
+
+import pytest
+
+import synth
+from test_gpu_layer import TINY_Q80, check_cache_rows, check_layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_decoder_layer_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _shape(name, hidden, hq, hkv, d, inter, **kw):
+    return dataclasses.replace(synth.TINY, name=name, hidden=hidden, n_q_heads=hq, n_kv_heads=hkv,
+                               head_dim=d, intermediate=inter, weight_dtype="bf16", rope_theta=1e6, **kw)
+
+
+# one shape per (head_dim, query heads per KV head) the kernels instantiate
+GQA_SHAPES = [
+    _shape("mha-d64", 256, 4, 4, 64, 512),                 # 1:1
+    _shape("gqa4-d64", 512, 8, 2, 64, 768),                # 4:1
+    _shape("gqa8-d128", 1024, 8, 1, 128, 1536),            # 8:1
+    _shape("mha-d128", 512, 4, 4, 128, 1024, qk_norm=True, qkv_bias=False),
+]
+
+
+@pytest.mark.parametrize("shape", GQA_SHAPES, ids=lambda s: s.name)
+def test_gqa_ratios_prefill_and_decode(shape):
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=shape, kv_dtype="bf16")
+    inp = synth.make_inputs(wl, seed=21, prefill_len=70, prefill_start=19, spare_blocks=2)
+    layer, kv, t, cache, rows = check_layer(inp, what=f"prefill {shape.name}")
+    check_cache_rows(inp, kv, cache, [0])
+    for kvd in ("bf16", "u8"):
+        wd = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=shape, kv_dtype=kvd)
+        ctx = [0, 9, 33, 255, 700]
+        inp = synth.make_inputs(wd, seed=22, decode_batch=len(ctx), decode_ctx=ctx)
+        layer, kv, t, cache, rows = check_layer(inp, what=f"decode {kvd} {shape.name}")
+        check_cache_rows(inp, kv, cache, range(len(ctx)))
+
+
+def test_q80_decode_stream_gemm():
+    wl = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=TINY_Q80)
+    ctx = [1, 16, 47, 300, 1023, 64, 5]
+    inp = synth.make_inputs(wl, seed=23, decode_batch=len(ctx), decode_ctx=ctx)
+    layer, kv, t, cache, rows = check_layer(inp, what="decode q80")
+    check_cache_rows(inp, kv, cache, range(len(ctx)))
+
+
+def test_half_stage_reduction_dim():
+    # intermediate 736: the down projection's K = 23 steps of 32, so the decode
+    # GEMM's last 64-k stage is half empty; the prefill GEMM takes K % 64 != 0
+    shape = _shape("k736", 256, 4, 2, 64, 736)
+    wd = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=shape)
+    ctx = [3, 40, 129, 600, 17, 2]
+    inp = synth.make_inputs(wd, seed=24, decode_batch=len(ctx), decode_ctx=ctx)
+    check_layer(inp, what="decode k736")
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=shape, kv_dtype="bf16")
+    inp = synth.make_inputs(wl, seed=25, prefill_len=150, spare_blocks=1)
+    check_layer(inp, what="prefill k736")
+
+
+def test_calls_at_capacity_limits():
+    # prefill of exactly max_tokens rows ending exactly at max_position
+    T, start = 96, 160
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], kv_dtype="bf16")
+    inp = synth.make_inputs(wl, seed=26, prefill_len=T, prefill_start=start)
+    layer, kv, t, cache, rows = check_layer(inp, what="prefill at max_tokens/max_position",
+                                            max_tokens=T, max_position=start + T)
+    check_cache_rows(inp, kv, cache, [0])
+    # decode tokens landing on the last position, max_position - 1
+    wd = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=synth.TINY)
+    ctx = [511, 511, 100]
+    inp = synth.make_inputs(wd, seed=27, decode_batch=len(ctx), decode_ctx=ctx)
+    layer, kv, t, cache, rows = check_layer(inp, what="decode at max_position - 1",
+                                            max_tokens=len(ctx), max_position=512)
+    check_cache_rows(inp, kv, cache, range(len(ctx)))
+
+
+@pytest.mark.parametrize("what", ["decode_only", "prefill_only"])
+def test_mixed_step_one_sided(what):
+    wl = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=TINY_Q80)
+    if what == "decode_only":
+        ctx = [0, 31, 200, 513]
+        inp = synth.make_inputs(wl, seed=28, prefill_len=0, decode_batch=len(ctx), decode_ctx=ctx)
+        rows = range(len(ctx))
+    else:
+        inp = synth.make_inputs(wl, seed=29, prefill_len=61, prefill_start=35, decode_batch=0)
+        rows = [0]
+    layer, kv, t, cache, _ = check_layer(inp, what=f"mixed {what}")
+    check_cache_rows(inp, kv, cache, rows)

@@ -45,11 +45,11 @@ def gpu_stages(layer, t, rows, shape):
                 a=get(ws.a, I, torch.bfloat16))
 
 
-def check_layer(inp, seqs=None, what="", stages=True):
+def check_layer(inp, seqs=None, what="", stages=True, **setup):
     import torch
     shape = inp.workload.shape
     log(f"[{what}] gpu setup")
-    layer, kv, t = gpu_setup(inp)
+    layer, kv, t = gpu_setup(inp, **setup)
     log(f"[{what}] gpu call")
     gpu_call(inp, layer, kv, t)
     torch.cuda.synchronize()
