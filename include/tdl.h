@@ -33,6 +33,9 @@
  *    is asynchronous: inputs must stay valid and outputs untouched until the
  *    stream reaches that point.  No call synchronises the stream, except
  *    layer_create / kv_cache_alloc at set-up.
+ *  - Activation arrays (x, y of the layer calls) must be 16-byte aligned
+ *    (the kernels move them in 16-byte chunks); a misaligned one is
+ *    TDL_E_INVALID.  torch allocations are 256-byte aligned.
  *  - bf16 means IEEE bfloat16 (16-bit, 8-bit exponent); every fp32 -> bf16
  *    conversion rounds to nearest, ties to even.
  *  - A layer handle and a KV handle each serve one host thread at a time.

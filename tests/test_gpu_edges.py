@@ -2,13 +2,15 @@
 query-group ratio and head dimension the attention kernels are built for,
 Q8_0 weights on the decode-sized GEMM, a reduction dimension that ends in a
 half 64-k stage, calls exactly at max_tokens / max_position, and mixed steps
-with only decode or only prefill rows.  Same tolerance as the other layer
+with only decode or only prefill rows, and the rejection of misaligned
+activation pointers.  Same tolerance as the other layer
 tests (stage by stage, cache rows checked)."""
 import dataclasses
 
 import pytest
 
 import synth
+from harness import gpu_setup
 from test_gpu_layer import TINY_Q80, check_cache_rows, check_layer
 
 pytestmark = pytest.mark.gpu
@@ -100,3 +102,23 @@ def test_mixed_step_one_sided(what):
         rows = [0]
     layer, kv, t, cache, _ = check_layer(inp, what=f"mixed {what}")
     check_cache_rows(inp, kv, cache, rows)
+
+
+def test_misaligned_activations_rejected():
+    # x and y move in 16-byte chunks: a pointer off that grid is an argument
+    # error raised before anything is enqueued
+    import torch
+    import transformer_decoder_layer_amd as tdl
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], kv_dtype="none")
+    inp = synth.make_inputs(wl, seed=30, prefill_len=8)
+    layer, kv, t = gpu_setup(inp)
+    T, H = t["x"].shape
+    buf = torch.zeros(T * H + 8, dtype=torch.bfloat16, device="cuda")
+    x_off = buf[1:1 + T * H].view(T, H)
+    assert x_off.data_ptr() % 16 == 2
+    with pytest.raises(tdl.TdlError):
+        layer.prefill(x_off, t["y"], 0, None, None)
+    y_off = torch.zeros(T * H + 8, dtype=torch.bfloat16, device="cuda")[4:4 + T * H].view(T, H)
+    with pytest.raises(tdl.TdlError):
+        layer.prefill(t["x"], y_off, 0, None, None)
+    torch.cuda.synchronize()

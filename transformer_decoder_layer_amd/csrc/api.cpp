@@ -558,6 +558,7 @@ extern "C" tdl_status layer_prefill(tdl_layer* L, tdl_stream stream, const void*
   if (!L) return fail(TDL_E_INVALID, "layer is NULL");
   if (!x || !y) return fail(TDL_E_INVALID, "x or y is NULL");
   if (x == y) return fail(TDL_E_INVALID, "y must not alias x");
+  if (((uintptr_t)x | (uintptr_t)y) & 15) return fail(TDL_E_INVALID, "x and y must be 16-byte aligned");
   if (n_tokens < 1 || n_tokens > L->cfg.max_tokens)
     return fail(n_tokens < 1 ? TDL_E_INVALID : TDL_E_CAPACITY,
                 "n_tokens %d outside [1, max_tokens=%d]", n_tokens, L->cfg.max_tokens);
@@ -601,6 +602,7 @@ extern "C" tdl_status layer_decode_paged(tdl_layer* L, tdl_stream stream, const 
   if (!x || !y || !ctx_lens || !block_tables || !kv)
     return fail(TDL_E_INVALID, "x, y, ctx_lens, block_tables and kv are required");
   if (x == y) return fail(TDL_E_INVALID, "y must not alias x");
+  if (((uintptr_t)x | (uintptr_t)y) & 15) return fail(TDL_E_INVALID, "x and y must be 16-byte aligned");
   if (batch < 1) return fail(TDL_E_INVALID, "batch < 1");
   if (batch > L->cfg.max_seqs || batch > L->cfg.max_tokens)
     return fail(TDL_E_CAPACITY, "batch %d exceeds max_seqs/max_tokens", batch);
@@ -629,6 +631,7 @@ extern "C" tdl_status layer_step(tdl_layer* L, tdl_stream stream, const tdl_batc
   if (!L) return fail(TDL_E_INVALID, "layer is NULL");
   if (!b || !x || !y || !kv) return fail(TDL_E_INVALID, "batch, x, y and kv are required");
   if (x == y) return fail(TDL_E_INVALID, "y must not alias x");
+  if (((uintptr_t)x | (uintptr_t)y) & 15) return fail(TDL_E_INVALID, "x and y must be 16-byte aligned");
   if (!b->q_start || !b->q_len || !b->ctx_len || !b->block_tables)
     return fail(TDL_E_INVALID, "batch arrays are required");
   if (b->n_seqs < 1 || b->n_prefill_seqs < 0 || b->n_prefill_seqs > b->n_seqs)

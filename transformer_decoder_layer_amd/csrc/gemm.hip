@@ -57,23 +57,30 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 // ws[split][M][N] and a second kernel sums the slices in order and applies
 // the epilogue (no cross-workgroup handshake, which would need device-wide
 // L2 write-backs on a multi-XCD part).
-template <int EPI, int FM, int FN>
-__device__ __forceinline__ void gemm_store(const GemmArgs& p, const f32x4 (&v)[FM][FN], int mw, int nw,
-                                           int split, int lane) {
+//
+// GUARD = false for a wave block that lies inside the output (the common
+// case): no per-element branches.  A guarded store is a branch, and the
+// compiler waits (vmcnt(0), which counts earlier stores too) for a loaded
+// bias inside every such branch, one memory round trip per element; the
+// bias loads are unconditional from clamped addresses for the same reason.
+// Residual epilogues normally go through LDS (resid_epilogue).
+template <int EPI, int FM, int FN, bool GUARD>
+__device__ __forceinline__ void gemm_store_block(const GemmArgs& p, const f32x4 (&v)[FM][FN], int mw,
+                                                 int nw, int split, int lane) {
   const int col = lane & 15;
   const int rbase = mw + 4 * (lane >> 4);
+  auto in_range = [&](int m, int n) { return !GUARD || (m < p.M && n < p.N); };
   if (p.splits > 1) {
     float* part = p.ws + (size_t)split * p.M * p.N;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = nw + j * 16 + col;
-      if (n >= p.N) continue;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = rbase + i * 16 + r;
-          if (m < p.M) part[(size_t)m * p.N + n] = v[i][j][r];
+          if (in_range(m, n)) part[(size_t)m * p.N + n] = v[i][j][r];
         }
     }
     return;
@@ -84,45 +91,130 @@ __device__ __forceinline__ void gemm_store(const GemmArgs& p, const f32x4 (&v)[F
     for (int jp = 0; jp < FN / 2; ++jp) {
       const int ng = nw + jp * 32;   // first gate column of the pair
       const int jcol = ng / 2 + col;  // output column
-      if (ng + col >= p.N) continue;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = rbase + i * 16 + r;
-          if (m < p.M) {
+          if (in_range(m, ng + col)) {
             const float g = v[i][2 * jp][r], u = v[i][2 * jp + 1][r];
             C[(size_t)m * p.ldc + jcol] = f32_to_bf16(silu_f(g) * u);
           }
         }
     }
-  } else {
+  } else if constexpr (EPI == EPI_BIAS_F32) {
+    float* __restrict__ Cf = (float*)p.C;
+    float bias[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bias[j] = p.bias ? p.bias[min(nw + j * 16 + col, p.N - 1)] : 0.f;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = nw + j * 16 + col;
-      if (n >= p.N) continue;
-      float bias = 0.f;
-      if constexpr (EPI == EPI_BIAS_F32)
-        if (p.bias) bias = p.bias[n];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = rbase + i * 16 + r;
-          if (m >= p.M) continue;
-          const float val = v[i][j][r];
-          if constexpr (EPI == EPI_BIAS_F32) {
-            ((float*)p.C)[(size_t)m * p.ldc + n] = val + bias;
-          } else if constexpr (EPI == EPI_RESID_F32) {
-            const float res = bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
-            ((float*)p.C)[(size_t)m * p.ldc + n] = val + res;
-          } else {
-            const float res = ((const float*)p.resid)[(size_t)m * p.ldr + n];
-            ((bf16*)p.C)[(size_t)m * p.ldc + n] = f32_to_bf16(val + res);
-          }
+          if (in_range(m, n)) Cf[(size_t)m * p.ldc + n] = v[i][j][r] + bias[j];
+        }
+    }
+  } else {
+    // residual epilogue without LDS: only for residual rows that are not
+    // 16-byte aligned (resid_epilogue serves the rest), element by element
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = nw + j * 16 + col;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = rbase + i * 16 + r;
+          if (!in_range(m, n)) continue;
+          if constexpr (EPI == EPI_RESID_F32)
+            ((float*)p.C)[(size_t)m * p.ldc + n] =
+                v[i][j][r] + bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
+          else
+            ((bf16*)p.C)[(size_t)m * p.ldc + n] =
+                f32_to_bf16(v[i][j][r] + ((const float*)p.resid)[(size_t)m * p.ldr + n]);
         }
     }
   }
+}
+
+template <int EPI, int FM, int FN>
+__device__ __forceinline__ void gemm_store(const GemmArgs& p, const f32x4 (&v)[FM][FN], int mw, int nw,
+                                           int split, int lane) {
+  // wave-uniform: the whole FM*16 x FN*16 block inside the output
+  if (mw + FM * 16 <= p.M && nw + FN * 16 <= p.N)
+    gemm_store_block<EPI, FM, FN, false>(p, v, mw, nw, split, lane);
+  else
+    gemm_store_block<EPI, FM, FN, true>(p, v, mw, nw, split, lane);
+}
+
+// Residual epilogue through LDS, after the main loop (whose last barrier
+// leaves the stage buffers free).  Each wave copies the residual rows of its
+// block into its own LDS slice with 16-byte direct-to-LDS loads -- one
+// coalesced round trip, no registers held -- then adds them element by
+// element from LDS and stores.  FMP 16-row fragments per pass (fp32
+// residuals take two passes in the eight-wave tiles).  Rows past M and
+// chunks past N are clamped to valid addresses and never stored.
+template <int EPI, int FM, int FN, int FMP>
+__device__ __forceinline__ void resid_epilogue(const GemmArgs& p, const f32x4 (&v)[FM][FN], int mw,
+                                               int nw, int lane, char* slice) {
+  typedef typename std::conditional<EPI == EPI_RESID_F32, bf16, float>::type R;
+  constexpr int WTN = FN * 16;
+  constexpr int EPC = 16 / (int)sizeof(R);  // elements per 16-byte chunk
+  constexpr int CPR = WTN / EPC;            // chunks per row
+  constexpr int INSTS = FMP * 16 * CPR / 64;
+  static_assert(WTN % EPC == 0 && (FMP * 16 * CPR) % 64 == 0 && FM % FMP == 0, "residual slice");
+  const R* __restrict__ Rp = (const R*)p.resid;
+  const bool full = mw + FM * 16 <= p.M && nw + WTN <= p.N;
+  const int col = lane & 15, g4 = 4 * (lane >> 4);
+  const R* sl = (const R*)slice;
+#pragma unroll
+  for (int i0 = 0; i0 < FM; i0 += FMP) {
+#pragma unroll
+    for (int t = 0; t < INSTS; ++t) {
+      const int c = t * 64 + lane;
+      const int gm = min(mw + i0 * 16 + c / CPR, p.M - 1);
+      const int gn = min(nw + (c % CPR) * EPC, p.N - EPC);
+      __builtin_amdgcn_global_load_lds((const void*)(Rp + (size_t)gm * p.ldr + gn),
+                                       (lds_void*)(slice + t * 1024), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int ii = 0; ii < FMP; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = nw + j * 16 + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mw + (i0 + ii) * 16 + g4 + r;
+          float res;
+          if constexpr (EPI == EPI_RESID_F32) res = bf16_to_f32(sl[(ii * 16 + g4 + r) * WTN + j * 16 + col]);
+          else res = sl[(ii * 16 + g4 + r) * WTN + j * 16 + col];
+          if (full || (m < p.M && n < p.N)) {
+            const float val = v[i0 + ii][j][r] + res;
+            if constexpr (EPI == EPI_RESID_BF16) ((bf16*)p.C)[(size_t)m * p.ldc + n] = f32_to_bf16(val);
+            else ((float*)p.C)[(size_t)m * p.ldc + n] = val;
+          }
+        }
+        // one column group's LDS reads at a time (register bound)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    // the next pass refills the slice: this wave's LDS reads must be done
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Largest divisor of FM whose pass (FMP x 16 rows x BYTES_PER_ROW) fits CAP.
+template <int FM, int BYTES_PER_I, int CAP>
+constexpr int resid_fmp() {
+  for (int f = FM; f >= 1; --f)
+    if (FM % f == 0 && f * BYTES_PER_I <= CAP) return f;
+  return 0;
 }
 
 // Tile of a workgroup.  Workgroups are dispatched round-robin over the 8
@@ -389,6 +481,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
     }
   }
 
+  if constexpr (EPI == EPI_RESID_F32 || EPI == EPI_RESID_BF16) {
+    // residual through LDS when its rows are 16-byte aligned (the main
+    // loop's last barrier has left the stage buffers free)
+    constexpr int RB = EPI == EPI_RESID_F32 ? 2 : 4;
+    constexpr int SPA = NW / 4;  // wave slices per stage array
+    static_assert(NW == 4 || NW == 8, "four stage arrays shared by the waves");
+    constexpr int CAP = (int)(sizeof(As0) < sizeof(Bs0) ? sizeof(As0) : sizeof(Bs0)) / SPA;
+    constexpr int FMP = resid_fmp<FM, 16 * WTN * RB, CAP>();
+    static_assert(FMP >= 1, "residual slice does not fit");
+    const int epc = 16 / RB;
+    if (p.splits == 1 && ((uintptr_t)p.resid & 15) == 0 && p.ldr % epc == 0 && p.N % epc == 0) {
+      const int arr = wave / SPA;
+      T* base = arr == 0 ? As0 : arr == 1 ? As1 : arr == 2 ? Bs0 : Bs1;
+      char* slice = (char*)base + (wave % SPA) * CAP;
+      resid_epilogue<EPI, FM, FN, FMP>(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane, slice);
+      return;
+    }
+  }
   gemm_store<EPI, FM, FN>(p, acc, m0 + wm * WTM, n0 + wn * WTN, split, lane);
 }
 
@@ -424,18 +534,22 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
       const float4 a = *(const float4*)(p.ws + s * slice + (size_t)m * p.N + c);
       v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
     }
+    // the residual is never the output: its loads all issue before the stores
+    const bf16* __restrict__ Rb = (const bf16*)p.resid;
+    const float* __restrict__ Rf = (const float*)p.resid;
+    float add[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int n = c + e;
-      if constexpr (EPI == EPI_BIAS_F32) {
-        ((float*)p.C)[(size_t)m * p.ldc + n] = v[e] + (p.bias ? p.bias[n] : 0.f);
-      } else if constexpr (EPI == EPI_RESID_F32) {
-        ((float*)p.C)[(size_t)m * p.ldc + n] =
-            v[e] + bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
-      } else {
-        ((bf16*)p.C)[(size_t)m * p.ldc + n] =
-            f32_to_bf16(v[e] + ((const float*)p.resid)[(size_t)m * p.ldr + n]);
-      }
+      if constexpr (EPI == EPI_BIAS_F32) add[e] = p.bias ? p.bias[n] : 0.f;
+      else if constexpr (EPI == EPI_RESID_F32) add[e] = bf16_to_f32(Rb[(size_t)m * p.ldr + n]);
+      else add[e] = Rf[(size_t)m * p.ldr + n];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int n = c + e;
+      if constexpr (EPI == EPI_RESID_BF16) ((bf16*)p.C)[(size_t)m * p.ldc + n] = f32_to_bf16(v[e] + add[e]);
+      else ((float*)p.C)[(size_t)m * p.ldc + n] = v[e] + add[e];
     }
   }
 }
@@ -456,12 +570,14 @@ constexpr Cfg kCfgs[kNumCfgs] = {{256, 256, 1.0f}, {256, 224, 0.97f}, {128, 128,
 template <bool Q80, int EPI, typename T, bool DIRECT>
 hipError_t launch_cfg2(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
   switch (cfg) {
-    case 0:
-      gemm_kernel<256, 256, 2, 4, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
+    case 0:  // the planner gives the eight-wave tiles bf16/fp16 weights only
+      if constexpr (!Q80) gemm_kernel<256, 256, 2, 4, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
+      else return hipErrorInvalidValue;
       break;
     case 1:
-      if constexpr (EPI != EPI_SILU_GATE)
+      if constexpr (!Q80 && EPI != EPI_SILU_GATE)
         gemm_kernel<256, 224, 4, 2, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
+      else return hipErrorInvalidValue;
       break;
     case 2:
       gemm_kernel<128, 128, 2, 2, Q80, EPI, T, DIRECT><<<grid, 256, 0, s>>>(a);

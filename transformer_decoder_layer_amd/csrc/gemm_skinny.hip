@@ -276,23 +276,31 @@ void gemm_stream_kernel(GemmArgs p) {
     }
   } else {
     if (wk > 0 || n >= p.N) return;
+    // the residual is never the output: its loads all issue before the
+    // stores, unconditionally from clamped addresses (a guarded load would
+    // be a branch that waits for its own result)
+    const bf16* __restrict__ Rb = (const bf16*)p.resid;
+    const float* __restrict__ Rf = (const float*)p.resid;
     const float bias = (EPI == EPI_BIAS_F32 && p.bias) ? p.bias[n] : 0.f;
+    float add[MT][4];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const size_t off = (size_t)min(16 * i + rb + r, p.M - 1) * p.ldr + n;
+        if constexpr (EPI == EPI_BIAS_F32) add[i][r] = bias;
+        else if constexpr (EPI == EPI_RESID_F32) add[i][r] = bf16_to_f32(Rb[off]);
+        else add[i][r] = Rf[off];
+      }
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 16 * i + rb + r;
         if (m >= p.M) continue;
-        const float v = acc[i][0][r];
-        if constexpr (EPI == EPI_BIAS_F32) {
-          ((float*)p.C)[(size_t)m * p.ldc + n] = v + bias;
-        } else if constexpr (EPI == EPI_RESID_F32) {
-          ((float*)p.C)[(size_t)m * p.ldc + n] =
-              v + bf16_to_f32(((const bf16*)p.resid)[(size_t)m * p.ldr + n]);
-        } else {
-          ((bf16*)p.C)[(size_t)m * p.ldc + n] =
-              f32_to_bf16(v + ((const float*)p.resid)[(size_t)m * p.ldr + n]);
-        }
+        const float v = acc[i][0][r] + add[i][r];
+        if constexpr (EPI == EPI_RESID_BF16) ((bf16*)p.C)[(size_t)m * p.ldc + n] = f32_to_bf16(v);
+        else ((float*)p.C)[(size_t)m * p.ldc + n] = v;
       }
   }
 }
