@@ -561,11 +561,12 @@ struct Cfg {
 // cfg 0: 256x256 (2x4 waves of 128x64);  cfg 1: 256x224 (4x2 waves of
 // 64x112: N = 3584 splits into 16 tiles);  cfg 2: 128x128 (2x2 waves of
 // 64x64);  cfg 3: 64x128 (1x4 waves of 64x32) and cfg 4: 128x128 (1x4 waves
-// of 128x32) for decode-sized M.  Eight-wave tiles keep two waves per SIMD,
-// each with at most 128 accumulators (AGPRs).
-constexpr int kNumCfgs = 5;
-constexpr Cfg kCfgs[kNumCfgs] = {{256, 256, 1.0f}, {256, 224, 0.97f}, {128, 128, 0.55f},
-                                 {64, 128, 0.35f}, {128, 128, 0.5f}};
+// of 128x32) for decode-sized M;  cfg 5: 256x288 (4x2 waves of 64x144: N =
+// 4608 splits into 16 tiles, so 4096 rows make one tile per CU).  Eight-wave
+// tiles keep two waves per SIMD.
+constexpr int kNumCfgs = 6;
+constexpr Cfg kCfgs[kNumCfgs] = {{256, 256, 1.0f}, {256, 224, 0.96f}, {128, 128, 0.55f},
+                                 {64, 128, 0.35f},  {128, 128, 0.5f},  {256, 288, 0.98f}};
 
 template <bool Q80, int EPI, typename T, bool DIRECT>
 hipError_t launch_cfg2(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
@@ -581,6 +582,11 @@ hipError_t launch_cfg2(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
       break;
     case 2:
       gemm_kernel<128, 128, 2, 2, Q80, EPI, T, DIRECT><<<grid, 256, 0, s>>>(a);
+      break;
+    case 5:
+      if constexpr (!Q80 && EPI != EPI_SILU_GATE)
+        gemm_kernel<256, 288, 4, 2, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
+      else return hipErrorInvalidValue;
       break;
     case 3:
       gemm_kernel<64, 128, 1, 4, Q80, EPI, T, DIRECT><<<grid, 256, 0, s>>>(a);
@@ -633,8 +639,9 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
   for (int cfg = 0; cfg < kNumCfgs; ++cfg) {
     const Cfg c = kCfgs[cfg];
     if (cfg == 1 && (epi == EPI_SILU_GATE || N % 224 != 0)) continue;
-    if (q80 && cfg <= 1) continue;        // Q8_0 staging needs the register path
-    if (cfg >= 3 && M > 128) continue;   // the decode shapes only
+    if (cfg == 5 && (epi == EPI_SILU_GATE || N % 288 != 0)) continue;
+    if (q80 && (cfg <= 1 || cfg == 5)) continue;  // Q8_0 staging needs the register path
+    if ((cfg == 3 || cfg == 4) && M > 128) continue;  // the decode shapes only
     if (cfg == 3 && M > 64) continue;
     const int tiles = cdiv(M, c.BM) * cdiv(N, c.BN);
     for (int splits = 1; splits <= 16; splits *= 2) {
