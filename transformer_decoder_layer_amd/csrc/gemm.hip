@@ -217,20 +217,11 @@ constexpr int resid_fmp() {
   return 0;
 }
 
-// Tile of a workgroup.  Workgroups are dispatched round-robin over the 8
-// XCDs (each with its own L2); remap so that consecutive logical ids run on
-// one XCD, then walk tiles in groups of 8 M-tiles sharing a B panel.
+// Output tile `tile` in the walk order: groups of 8 M-tiles sharing a B
+// panel.
 template <int BM, int BN>
-__device__ __forceinline__ void tile_of(const GemmArgs& p, int* m0, int* n0, int* split) {
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int tile, int* m0, int* n0) {
   const int tiles_m = cdiv(p.M, BM), tiles_n = cdiv(p.N, BN);
-  int bid = blockIdx.x;
-  {
-    const int nwg = gridDim.x, per = nwg / 8, rem = nwg % 8;
-    const int xcd = bid % 8, slot = bid / 8;
-    bid = xcd * per + min(xcd, rem) + slot;
-  }
-  *split = bid % p.splits;
-  const int tile = bid / p.splits;
   constexpr int GROUP = 8;
   const int group_size = GROUP * tiles_n;
   const int gidx = tile / group_size;
@@ -238,6 +229,39 @@ __device__ __forceinline__ void tile_of(const GemmArgs& p, int* m0, int* n0, int
   const int gm = min(tiles_m - first_m, GROUP);
   *m0 = (first_m + (tile % group_size) % gm) * BM;
   *n0 = ((tile % group_size) / gm) * BN;
+}
+
+// Tile of a workgroup.  Workgroups are dispatched round-robin over the 8
+// XCDs (each with its own L2); remap so that consecutive logical ids run on
+// one XCD.  With a split tail, the workgroups past full_tiles (dispatched
+// last) are (tail tile, K slice) pairs: *tail >= 0.
+template <int BM, int BN>
+__device__ __forceinline__ void tile_of(const GemmArgs& p, int* m0, int* n0, int* split, int* tail) {
+  int bid = blockIdx.x;
+  int tile;
+  *tail = -1;
+  if (p.tail_splits > 1 && bid >= p.full_tiles) {
+    const int tb = bid - p.full_tiles;
+    *tail = tb / p.tail_splits;
+    *split = tb % p.tail_splits;
+    tile = p.full_tiles + *tail;
+  } else {
+    const int nwg = p.tail_splits > 1 ? p.full_tiles : (int)gridDim.x;
+    const int per = nwg / 8, rem = nwg % 8;
+    const int xcd = bid % 8, slot = bid / 8;
+    bid = xcd * per + min(xcd, rem) + slot;
+    *split = bid % p.splits;
+    tile = bid / p.splits;
+  }
+  tile_coords<BM, BN>(p, tile, m0, n0);
+}
+
+// Split-tail partials: [tail tile][split][i][j][thread] of f32x4, i.e. each
+// thread's accumulator registers as they are (16-byte coalesced stores).
+template <int FM, int FN, int NT>
+__device__ __forceinline__ size_t tail_offset(const GemmArgs& p, int tail, int split, int i, int j,
+                                              int tid) {
+  return ((((size_t)tail * p.tail_splits + split) * FM + i) * FN + j) * NT + tid;
 }
 
 // DIRECT: operand tiles go from global memory straight into LDS
@@ -275,12 +299,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   const int wm = wave / WN, wn = wave % WN;
   const int col_l = lane & 15;
 
-  int m0, n0, split;
-  tile_of<BM, BN>(p, &m0, &n0, &split);
+  int m0, n0, split, tail;
+  tile_of<BM, BN>(p, &m0, &n0, &split, &tail);
 
   const int KT = cdiv(p.K, BK);
-  const int kt0 = split * p.k_tiles_per_split;
-  const int kt1 = min(kt0 + p.k_tiles_per_split, KT);
+  const int kps = tail >= 0 ? p.tail_kps : p.k_tiles_per_split;
+  const int kt0 = split * kps;
+  const int kt1 = min(kt0 + kps, KT);
 
   const T* __restrict__ A = (const T*)p.A;
 
@@ -481,6 +506,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
     }
   }
 
+  if (tail >= 0) {  // a K slice of a tail tile: the partial, as the registers hold it
+    f32x4* ws = (f32x4*)p.tail_ws;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) ws[tail_offset<FM, FN, NT>(p, tail, split, i, j, tid)] = acc[i][j];
+    return;
+  }
   if constexpr (EPI == EPI_RESID_F32 || EPI == EPI_RESID_BF16) {
     // residual through LDS when its rows are 16-byte aligned (the main
     // loop's last barrier has left the stage buffers free)
@@ -554,6 +587,34 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   }
 }
 
+// Sums the K slices of the split-tail tiles in slice order (deterministic)
+// and applies the epilogue: one 64-thread workgroup per (wave block, tail
+// tile), grid (NW, tail tiles).  Bias and SiLU-gate epilogues only.
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64) void tail_reduce_kernel(GemmArgs p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  static_assert(EPI == EPI_BIAS_F32 || EPI == EPI_SILU_GATE, "split tail: no residual epilogues");
+  const int wave = blockIdx.x, tail = blockIdx.y, lane = threadIdx.x;
+  const int tid = wave * 64 + lane;
+  const int wm = wave / WN, wn = wave % WN;
+  int m0, n0;
+  tile_coords<BM, BN>(p, p.full_tiles + tail, &m0, &n0);
+  const f32x4* ws = (const f32x4*)p.tail_ws;
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = ws[tail_offset<FM, FN, NT>(p, tail, 0, i, j, tid)];
+  for (int sp = 1; sp < p.tail_splits; ++sp)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] += ws[tail_offset<FM, FN, NT>(p, tail, sp, i, j, tid)];
+  gemm_store<EPI, FM, FN>(p, acc, m0 + wm * WTM, n0 + wn * WTN, 0, lane);
+}
+
 struct Cfg {
   int BM, BN;
   float eff;  // relative per-tile efficiency, for the planner
@@ -622,6 +683,30 @@ hipError_t launch_epi(int cfg, int grid, int epi, const GemmArgs& a, hipStream_t
   }
 }
 
+hipError_t tail_reduce(const GemmPlan& pl, const GemmArgs& a, int epi, hipStream_t s) {
+  const int tail = (pl.grid - pl.full_tiles) / pl.tail_splits;
+#define TDL_TAIL_CASE(CFG, BM, BN, WM, WN)                                                     \
+  if (pl.cfg == CFG) {                                                                       \
+    const dim3 grid(WM * WN, tail);                                                          \
+    if (epi == EPI_SILU_GATE) tail_reduce_kernel<BM, BN, WM, WN, EPI_SILU_GATE><<<grid, 64, 0, s>>>(a); \
+    else if (epi == EPI_BIAS_F32) tail_reduce_kernel<BM, BN, WM, WN, EPI_BIAS_F32><<<grid, 64, 0, s>>>(a); \
+    else return hipErrorInvalidValue;                                                        \
+    return hipGetLastError();                                                                \
+  }
+  TDL_TAIL_CASE(0, 256, 256, 2, 4)
+  TDL_TAIL_CASE(2, 128, 128, 2, 2)
+#undef TDL_TAIL_CASE
+  if (pl.cfg == 1 && epi == EPI_BIAS_F32) {
+    tail_reduce_kernel<256, 224, 4, 2, EPI_BIAS_F32><<<dim3(8, tail), 64, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  if (pl.cfg == 5 && epi == EPI_BIAS_F32) {
+    tail_reduce_kernel<256, 288, 4, 2, EPI_BIAS_F32><<<dim3(8, tail), 64, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 // Chooses the tile configuration and split-K factor with the lowest estimated
@@ -656,11 +741,40 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
       if (sp > 1) cost += 2.0 * sp * (double)M * N * 4.0 * 40.0 / kCUs + 4.0e5;
       if (cost < best_cost) {
         best_cost = cost;
+        best = GemmPlan{};
         best.cfg = cfg;
         best.splits = sp;
         best.k_tiles_per_split = kps;
         best.grid = wgs;
         best.ws_floats = sp > 1 ? (size_t)sp * M * N : 0;
+      }
+    }
+    // split tail: when the last round of whole tiles would be at most half
+    // full, its tiles are cut along K into enough slices to fill the chip;
+    // their fp32 partials make a round trip through memory (about 0.01 cost
+    // units per byte, plus a second launch)
+    const int full = tiles / kCUs * kCUs, tail = tiles - full;
+    if (full > 0 && tail > 0 && 2 * tail <= kCUs && (epi == EPI_BIAS_F32 || epi == EPI_SILU_GATE) &&
+        cfg != 3 && cfg != 4) {
+      const int ts = std::min(kCUs / tail, KT / 8);
+      if (ts >= 2) {
+        const int tkps = cdiv(KT, ts);
+        const int tsp = cdiv(KT, tkps);
+        const double bytes = 2.0 * tail * tsp * (double)c.BM * c.BN * 4.0;
+        const double cost = (double)(full / kCUs) * c.BM * c.BN * KT / c.eff +
+                            (double)c.BM * c.BN * tkps / c.eff + 0.01 * bytes + 2.4e5;
+        if (cost < best_cost) {
+          best_cost = cost;
+          best = GemmPlan{};
+          best.cfg = cfg;
+          best.splits = 1;
+          best.k_tiles_per_split = KT;
+          best.full_tiles = full;
+          best.tail_splits = tsp;
+          best.tail_kps = tkps;
+          best.grid = full + tail * tsp;
+          best.ws_floats = (size_t)tail * tsp * c.BM * c.BN;
+        }
       }
     }
   }
@@ -670,10 +784,17 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
 hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, bool q80, int epi, hipStream_t s, bool reduce) {
   a.splits = pl.splits;
   a.k_tiles_per_split = pl.k_tiles_per_split;
+  a.full_tiles = pl.full_tiles;
+  a.tail_splits = pl.tail_splits;
+  a.tail_kps = pl.tail_kps;
+  a.tail_ws = pl.tail_splits > 1 ? a.ws : nullptr;
+  if (pl.tail_splits > 1 && (!a.ws || pl.splits != 1)) return hipErrorInvalidValue;
   const hipError_t e = pl.cfg >= 10 ? gemm_skinny_launch(pl, a, q80, epi, s)
                        : q80          ? launch_epi<true>(pl.cfg, pl.grid, epi, a, s)
                                       : launch_epi<false>(pl.cfg, pl.grid, epi, a, s);
-  if (e != hipSuccess || pl.splits == 1 || !reduce) return e;
+  if (e != hipSuccess) return e;
+  if (pl.tail_splits > 1) return tail_reduce(pl, a, epi, s);
+  if (pl.splits == 1 || !reduce) return e;
   const int Nout = epi == EPI_SILU_GATE ? a.N / 2 : a.N;
   const int64_t threads = (int64_t)a.M * (Nout / 4);
   const int blocks = (int)((threads + 255) / 256);

@@ -37,6 +37,14 @@ struct GemmArgs {
   int b_packed;      // B (bf16/fp16, K % 64 == 0, N % 16 == 0) in the tiled
                      // layout written by pack_weights instead of row-major;
                      // the large-M kernels take such B only in that layout
+  // Split tail (large-M kernels, splits == 1): workgroups past full_tiles
+  // each take 1/tail_splits of the K range (tail_kps k-tiles) of one of the
+  // remaining tiles and write an fp32 partial to tail_ws; a reduction kernel
+  // sums them and applies the epilogue.  tail_splits == 0: off.
+  int full_tiles;
+  int tail_splits;
+  int tail_kps;
+  float* tail_ws;
 };
 
 // Picks a tile configuration and split count for (M, N, K) and returns the
@@ -47,7 +55,10 @@ struct GemmPlan {
   int splits;
   int k_tiles_per_split;
   int grid;
-  size_t ws_floats;
+  size_t ws_floats;   // workspace: split-K slices or split-tail partials
+  int full_tiles;     // split tail: tiles computed whole (the rest are split)
+  int tail_splits;    // 0 = no split tail
+  int tail_kps;
 };
 GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi);
 // Decode-sized M (<= 128, K % 32 == 0): weights streamed straight from HBM
