@@ -550,11 +550,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
     // output column j -> gate column 32*(j/16) + j%16, up column +16
     const int ng = 32 * (c / 16) + (c % 16);
     float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.splits; ++s) {
-      const float4 a = *(const float4*)(p.ws + s * slice + (size_t)m * p.N + ng);
-      const float4 b = *(const float4*)(p.ws + s * slice + (size_t)m * p.N + ng + 16);
-      g[0] += a.x; g[1] += a.y; g[2] += a.z; g[3] += a.w;
-      u[0] += b.x; u[1] += b.y; u[2] += b.z; u[3] += b.w;
+    for (int s0 = 0; s0 < p.splits; s0 += 4) {  // four slices of independent loads per batch
+      float4 a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float* src = p.ws + min(s0 + q, p.splits - 1) * slice + (size_t)m * p.N + ng;
+        a[q] = *(const float4*)src;
+        b[q] = *(const float4*)(src + 16);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (s0 + q >= p.splits) break;
+        g[0] += a[q].x; g[1] += a[q].y; g[2] += a[q].z; g[3] += a[q].w;
+        u[0] += b[q].x; u[1] += b[q].y; u[2] += b[q].z; u[3] += b[q].w;
+      }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[e] = silu_f(g[e]) * u[e];
@@ -563,9 +572,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
     for (int e = 0; e < 4; ++e) C[e] = f32_to_bf16(out[e]);
   } else {
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.splits; ++s) {
-      const float4 a = *(const float4*)(p.ws + s * slice + (size_t)m * p.N + c);
-      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    for (int s0 = 0; s0 < p.splits; s0 += 4) {  // four slices of independent loads per batch
+      float4 a[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[q] = *(const float4*)(p.ws + min(s0 + q, p.splits - 1) * slice + (size_t)m * p.N + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (s0 + q >= p.splits) break;
+        v[0] += a[q].x; v[1] += a[q].y; v[2] += a[q].z; v[3] += a[q].w;
+      }
     }
     // the residual is never the output: its loads all issue before the stores
     const bf16* __restrict__ Rb = (const bf16*)p.resid;
@@ -716,7 +731,7 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
   constexpr int kCUs = 256;
   {
     GemmPlan sk{};
-    if (skinny_plan(M, N, K, epi, &sk)) return sk;
+    if (skinny_plan(M, N, K, q80, epi, &sk)) return sk;
   }
   const int KT = cdiv(K, BK);
   GemmPlan best{};
@@ -788,6 +803,7 @@ hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, bool q80, int epi, hipStr
   a.tail_splits = pl.tail_splits;
   a.tail_kps = pl.tail_kps;
   a.tail_ws = pl.tail_splits > 1 ? a.ws : nullptr;
+  a.rng_count = pl.rng_count;
   if (pl.tail_splits > 1 && (!a.ws || pl.splits != 1)) return hipErrorInvalidValue;
   const hipError_t e = pl.cfg >= 10 ? gemm_skinny_launch(pl, a, q80, epi, s)
                        : q80          ? launch_epi<true>(pl.cfg, pl.grid, epi, a, s)

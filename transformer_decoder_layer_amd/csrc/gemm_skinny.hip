@@ -5,11 +5,16 @@
 // bound by HBM bandwidth; what matters is keeping enough weight bytes in
 // flight on every CU and never draining that stream.  Layout of the work:
 //
-//  * A workgroup owns 64 weight rows and a K range.  Its waves form KW
-//    k-slices of four row waves; a row wave streams its 16 rows over its
-//    slice's part of the K range.  (With the SiLU-gate epilogue the gate
-//    and up rows of an output column sit in neighbouring row waves and meet
-//    in LDS at the end.)
+//  * A workgroup owns a range of 16-row groups and a K range.  The N/16
+//    groups are dealt out as evenly as possible over the row ranges (so
+//    that, with one workgroup per CU, every CU streams the same bytes: the
+//    busiest CU sets the time); a range has at most RW groups.  Its waves
+//    form KW k-slices of RW row waves; a row wave streams its 16 rows over
+//    its slice's part of the K range.  Spare row waves (range shorter than
+//    RW) repeat the last live wave's loads -- cache hits -- so that every
+//    wave issues the same loads, and store nothing.  (With the SiLU-gate
+//    epilogue the gate and up rows of an output column sit in neighbouring
+//    row waves, ranges hold whole pairs, and the two meet in LDS at the end.)
 //  * Weights go straight from HBM into MFMA operand registers (16 bytes =
 //    8 consecutive k of one row per lane), in NS rotating register sets: the
 //    loads of stage s + NS - 1 are issued before the MFMAs of stage s, so
@@ -33,6 +38,8 @@
 
 #include "common.h"
 #include "kernels.h"
+
+#include <algorithm>
 
 namespace tdl {
 
@@ -61,10 +68,9 @@ void gemm_stream_kernel(GemmArgs p) {
   static_assert(NS >= 3 && NS <= kMaxStages && RW % 2 == 0, "stream GEMM shape");
   typedef typename Mfma<T>::v8 T8;
   constexpr int FN = 1;                              // 16-row fragments per wave
-  constexpr int ROWS = 16 * FN * kRowWaves;
   constexpr int AE = MT * 16 * kStageK;              // A elements per slice and stage
-  constexpr int A_PER_WAVE = 2 * MT / RW;            // 1 KB direct loads per wave and stage
-  static_assert(A_PER_WAVE >= 1 && A_PER_WAVE * RW == 2 * MT, "A chunk split over the row waves");
+  constexpr int A_CHUNKS = 2 * MT;                   // 1 KB direct loads per slice and stage
+  constexpr int A_PER_WAVE = (A_CHUNKS + RW - 1) / RW;  // per wave (the last chunk repeats)
   constexpr int LOADS = A_PER_WAVE + FN * 2 * (Q80 ? 2 : 1);  // vector-memory ops per stage
   // separate arrays (not one indexed array): the compiler can then tell that
   // reading one buffer does not depend on the loads still filling another
@@ -81,9 +87,15 @@ void gemm_stream_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave % kRowWaves, wk = wave / kRowWaves;
-  const int n_tiles = cdiv(p.N, ROWS);
-  const int split = blockIdx.x / n_tiles;
-  const int n0 = (blockIdx.x % n_tiles) * ROWS;
+  // this workgroup's row range (ng <= RW groups from row n0) and K split
+  constexpr int PG = EPI == EPI_SILU_GATE ? 2 : 1;  // groups per unit dealt out
+  const int units = cdiv(p.N, 16) / PG;
+  const int rng = blockIdx.x % p.rng_count;
+  const int split = blockIdx.x / p.rng_count;
+  const int g0 = (int)((long)rng * units / p.rng_count) * PG;
+  const int ng = (int)((long)(rng + 1) * units / p.rng_count) * PG - g0;
+  const int n0 = g0 * 16;
+  const bool live = wr < ng;
   const int KS32 = p.K / 32;
   const int KS = cdiv(KS32, 2);                       // stages over the whole K
   const int ks0 = split * p.k_tiles_per_split;        // this split's stages
@@ -97,21 +109,26 @@ void gemm_stream_kernel(GemmArgs p) {
   const T* __restrict__ A = (const T*)p.A;
   const int r16 = lane & 15, g8 = (lane >> 4) * 8;
 
-  // this wave's direct-load rows of A: tokens 8*(wr*A_PER_WAVE + q) + lane/8,
-  // 16-byte chunk position lane%8 holding source chunk (lane%8) ^ (token%8)
+  // this wave's direct-load chunks of A: chunk c = tokens 8c .. 8c+7, lane
+  // L loads token 8c + L/8 into 16-byte position L%8, holding source chunk
+  // (L%8) ^ (token%8); chunks past the stage repeat the last one (the same
+  // bytes to the same place)
   const T* a_src[A_PER_WAVE];
+  int a_dst[A_PER_WAVE];
 #pragma unroll
   for (int q = 0; q < A_PER_WAVE; ++q) {
-    const int t = 8 * (wr * A_PER_WAVE + q) + (lane >> 3);
+    const int c = min(wr * A_PER_WAVE + q, A_CHUNKS - 1);
+    const int t = 8 * c + (lane >> 3);
     a_src[q] = A + (size_t)min(t, p.M - 1) * p.lda + (((lane & 7) ^ (t & 7)) << 3);
+    a_dst[q] = wk * AE + 8 * c * kStageK;
   }
-  const int a_c8 = ((lane & 7) ^ ((lane >> 3) & 7)) << 3;     // that chunk's first k
-  const int a_dst = wk * AE + 8 * wr * A_PER_WAVE * kStageK;  // + q * 8 tokens * 64 k
+  const int a_c8 = ((lane & 7) ^ ((lane >> 3) & 7)) << 3;  // that chunk's first k
 
-  // weight rows of this lane (clamped; rows past N are computed, never stored)
+  // weight rows of this lane: spare waves repeat the last live wave's rows;
+  // rows past N are clamped (computed, never stored)
   size_t b_row[FN];
 #pragma unroll
-  for (int f = 0; f < FN; ++f) b_row[f] = (size_t)min(n0 + 16 * (wr * FN + f) + r16, p.N - 1);
+  for (int f = 0; f < FN; ++f) b_row[f] = (size_t)min(n0 + 16 * (min(wr, ng - 1) * FN + f) + r16, p.N - 1);
 
   BFrag<Q80, T> breg[kStages][FN][2];
   f32x4 acc[MT][FN];
@@ -128,8 +145,8 @@ void gemm_stream_kernel(GemmArgs p) {
     const int a_off = k0 + a_c8 < p.K ? k0 : -a_c8;
 #pragma unroll
     for (int q = 0; q < A_PER_WAVE; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + a_off),
-                                       (lds_void*)&ring[a_dst + q * 8 * kStageK], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + a_off), (lds_void*)&ring[a_dst[q]], 16, 0,
+                                       0);
 #pragma unroll
     for (int f = 0; f < FN; ++f)
 #pragma unroll
@@ -236,7 +253,7 @@ void gemm_stream_kernel(GemmArgs p) {
   const int rb = 4 * (lane >> 4);
   const int n = n0 + 16 * wr + r16;
   if (p.splits > 1) {
-    if (wk > 0 || n >= p.N) return;
+    if (wk > 0 || !live || n >= p.N) return;
     float* part = p.ws + (size_t)split * p.M * p.N;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -252,15 +269,16 @@ void gemm_stream_kernel(GemmArgs p) {
     // up rows: the up waves hand their sums over through LDS (two pairs per
     // ring buffer, from buffer 1 on)
     const int pair = wr >> 1;
-    f32x4* xch = (f32x4*)(pair < 2 ? ring1 : ring2) + (pair % 2) * MT * 64;
-    static_assert(2 * MT * 64 * 16 <= KW * AE * (int)sizeof(T) && 1 + RW / 4 < NS, "exchange space");
+    f32x4* xch = (f32x4*)(pair < 2 ? ring1 : pair < 4 ? ring2 : ring3) + (pair % 2) * MT * 64;
+    static_assert(2 * MT * 64 * 16 <= KW * AE * (int)sizeof(T) && 1 + (RW / 2 - 1) / 2 < NS && RW <= 12,
+                  "exchange space");
     __syncthreads();  // every wave is done reading the ring
     if (wk == 0 && (wr & 1)) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) xch[i * 64 + lane] = acc[i][0];
     }
     __syncthreads();
-    if (wk > 0 || (wr & 1) || n >= p.N) return;
+    if (wk > 0 || (wr & 1) || !live || n >= p.N) return;
     const int jcol = (n0 + 16 * wr) / 2 + r16;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -275,7 +293,7 @@ void gemm_stream_kernel(GemmArgs p) {
       }
     }
   } else {
-    if (wk > 0 || n >= p.N) return;
+    if (wk > 0 || !live || n >= p.N) return;
     // the residual is never the output: its loads all issue before the
     // stores, unconditionally from clamped addresses (a guarded load would
     // be a branch that waits for its own result)
@@ -342,25 +360,58 @@ hipError_t launch_stream(int grid, int epi, const GemmArgs& a, hipStream_t s) {
 // cfg = 10000 + 1000 * MT + 100 * RW + 10 * NS + KW.
 int stream_cfg(int MT, int RW, int NS, int KW) { return 10000 + 1000 * MT + 100 * RW + 10 * NS + KW; }
 
-// One 4-wave workgroup per 64 weight rows; K is split across workgroups
-// (fp32 partials plus a reduction launch) only until there are 128
-// workgroups: measured on the decode shapes, fewer, longer streams beat
-// more parallelism once the split-K round trip and second launch are paid.
-bool skinny_plan(int M, int N, int K, int epi, GemmPlan* pl) {
-  (void)epi;
+// Row waves per workgroup that are built (RW), and the pipeline depth.
+constexpr int kStreamRW[3] = {4, 8, 10};
+constexpr int kStreamNS = 4;
+
+// Chooses (RW, row ranges, K splits) by a model of the decode-sized stream,
+// fitted to measurements on the Qwen2.5-7B decode shapes: a CU streams its
+// weight bytes at ~1.5 us latency with (NS-1) stages of 2 KB in flight per
+// live row wave, up to ~22 GB/s, and the GPU at ~5.5 TB/s; the busiest CU
+// sets the time.  K splits add streams (and fp32 partials that are written
+// and read once more).
+bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl) {
   if (M > 128 || K % 32 != 0) return false;
+  constexpr int kCUs = 256;
   const int MT = M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  constexpr int RW = 4, NS = 4;
-  const int n_tiles = cdiv(N, 16 * RW);
+  const int PG = epi == EPI_SILU_GATE ? 2 : 1;
+  const int units = cdiv(N, 16) / PG;
+  if (units < 1) return false;
   const int KS = cdiv(K / 32, 2);
-  int s = 1;
-  while (n_tiles * s < 128 && cdiv(KS, 2 * s) >= 2 * NS) s *= 2;
-  pl->cfg = stream_cfg(MT, RW, NS, 1);
-  pl->k_tiles_per_split = cdiv(KS, s);
-  pl->splits = cdiv(KS, pl->k_tiles_per_split);
-  pl->grid = n_tiles * pl->splits;
-  pl->ws_floats = pl->splits > 1 ? (size_t)pl->splits * M * N : 0;
-  return true;
+  const double wb = q80 ? 1.0625 : 2.0;  // weight bytes per element (Q8_0: + fp16 scale per 32)
+  const double total = (double)N * K * wb;
+  double best = 1e300;
+  for (int RW : kStreamRW) {
+    const int per = RW / PG;  // units per range at most
+    const int rmin = cdiv(units, per);
+    for (int s = 1; s <= 16; ++s) {
+      const int kps = cdiv(KS, s), sp = cdiv(KS, kps);
+      if (sp != s || (sp > 1 && kps < 2 * kStreamNS)) continue;
+      const int cands[3] = {rmin, kCUs / sp, 2 * kCUs / sp};
+      for (int R : cands) {
+        if (R < rmin || R > units || R < 1) continue;
+        const int W = R * sp;
+        const int wg_per_cu = cdiv(W, kCUs);
+        const int groups = cdiv(units, R) * PG;          // live row waves of the largest range
+        const double wg_bytes = (double)groups * 16 * kps * 64 * wb;
+        const double rate = std::min(22e9, wg_per_cu * groups * (kStreamNS - 1) * 2048.0 / 1.5e-6);
+        double t = std::max(wg_per_cu * wg_bytes / rate, total / 5.5e12);
+        if (sp > 1) t += 2.0 * sp * (double)M * N * 4.0 / 5.0e12;
+        t += 1e-9 * RW;  // ties: fewer waves
+        if (t < best) {
+          best = t;
+          *pl = GemmPlan{};
+          pl->cfg = stream_cfg(MT, RW, kStreamNS, 1);
+          pl->rng_count = R;
+          pl->splits = sp;
+          pl->k_tiles_per_split = kps;
+          pl->grid = W;
+          pl->ws_floats = sp > 1 ? (size_t)sp * M * N : 0;
+        }
+      }
+    }
+  }
+  return best < 1e300;
 }
 
 hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, bool q80, int epi,
@@ -369,9 +420,9 @@ hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, bool q80, i
   if (pl.cfg == stream_cfg(MT, RW, NS, KW))                                                 \
     return q80 ? launch_stream<true, MT, KW, RW, NS>(pl.grid, epi, a, s)                    \
                : launch_stream<false, MT, KW, RW, NS>(pl.grid, epi, a, s);
-  TDL_STREAM_CFG(2, 4, 4, 1)
-  TDL_STREAM_CFG(4, 4, 4, 1)
-  TDL_STREAM_CFG(8, 4, 4, 1)
+  TDL_STREAM_CFG(2, 4, 4, 1) TDL_STREAM_CFG(2, 8, 4, 1) TDL_STREAM_CFG(2, 10, 4, 1)
+  TDL_STREAM_CFG(4, 4, 4, 1) TDL_STREAM_CFG(4, 8, 4, 1) TDL_STREAM_CFG(4, 10, 4, 1)
+  TDL_STREAM_CFG(8, 4, 4, 1) TDL_STREAM_CFG(8, 8, 4, 1) TDL_STREAM_CFG(8, 10, 4, 1)
 #undef TDL_STREAM_CFG
   return hipErrorInvalidValue;
 }

@@ -45,6 +45,10 @@ struct GemmArgs {
   int tail_splits;
   int tail_kps;
   float* tail_ws;
+  // Decode-sized kernel: the N/16 row groups (pairs of groups with the
+  // SiLU-gate epilogue) are dealt out evenly over rng_count row ranges;
+  // workgroup b takes range b % rng_count and K split b / rng_count.
+  int rng_count;
 };
 
 // Picks a tile configuration and split count for (M, N, K) and returns the
@@ -59,11 +63,12 @@ struct GemmPlan {
   int full_tiles;     // split tail: tiles computed whole (the rest are split)
   int tail_splits;    // 0 = no split tail
   int tail_kps;
+  int rng_count;      // decode-sized kernel: row ranges
 };
 GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi);
 // Decode-sized M (<= 128, K % 32 == 0): weights streamed straight from HBM
 // into MFMA operands, activations shared through LDS (cfg >= 100).
-bool skinny_plan(int M, int N, int K, int epi, GemmPlan* pl);
+bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl);
 hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, bool q80, int epi,
                               hipStream_t s);
 // reduce = false leaves split-K partials in a.ws for a consumer that sums them

@@ -125,13 +125,23 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
   const int ldq = (Hq + 2 * Hkv) * D;
   const size_t slice = (size_t)gridDim.x * ldq;
   const float* src = qkv + (size_t)row * ldq;
-  // element c of this row's projection: the partial slices in order (+ bias)
+  // element c of this row's projection: the partial slices in order (+
+  // bias).  Four slices per batch of independent loads (slice indices past
+  // the last repeat it and add nothing): a load per round trip otherwise.
   auto val = [&](int c) {
-    float v = src[c];
-    for (int sp = 1; sp < splits; ++sp) v += src[sp * slice + c];
+    if (splits == 1) return bias ? src[c] + bias[c] : src[c];
+    float v = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += 4) {
+      float t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t[u] = src[(size_t)min(s0 + u, splits - 1) * slice + c];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v += s0 + u < splits ? t[u] : 0.f;
+    }
     return bias ? v + bias[c] : v;
   };
   const bool act = lane < half;
+  const int ln = act ? lane : 0;  // lanes past D/2 load a valid element and store nothing
   float2 cs = make_float2(1.f, 0.f);
   if (act) cs = tab[(size_t)pos * half + lane];
   const int blk = block_of(seq, sidx, pos);
@@ -141,11 +151,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
   for (int h = hpw * blockIdx.y + wave; h < min(Hq + Hkv, hpw * ((int)blockIdx.y + 1)); h += 4) {
     const bool is_q = h < Hq;
     const int hc = h * D;  // q heads then k heads are contiguous
-    float x1 = 0.f, x2 = 0.f;
-    if (act) {
-      x1 = val(hc + lane);
-      x2 = val(hc + lane + half);
-    }
+    float x1 = val(hc + ln), x2 = val(hc + ln + half);
+    if (!act) x1 = x2 = 0.f;
     const float* gn = is_q ? qn : kn;
     if (gn) {  // per-head RMSNorm over D
       const float ss = wave_sum(x1 * x1 + x2 * x2);
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     } else {
       const int g = h - Hq;
       const int vc = (Hq + Hkv + g) * D;
-      const float v1 = val(vc + lane), v2 = val(vc + lane + half);
+      const float v1 = val(vc + ln), v2 = val(vc + ln + half);
       store_kv(pool, blk, g, Hkv, D, slot, lane, r1, v1);
       store_kv(pool, blk, g, Hkv, D, slot, lane + half, r2, v2);
     }
@@ -183,28 +190,42 @@ __global__ __launch_bounds__(256) void rmsnorm_splits_kernel(const float* __rest
   __shared__ float red[4];
   const int row = blockIdx.x;
   const size_t slice = (size_t)gridDim.x * H;
-  float v[kSplitRowChunks][8];
+  // first pass: loads only (slices four at a time, chunks past H clamped to
+  // a valid address and zeroed), so that they all pipeline; second pass:
+  // the stores of h and y
+  float v[kSplitRowChunks][8], gg[kSplitRowChunks][8];
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < kSplitRowChunks; ++j) {
+    if (256 * 8 * j >= H) break;  // uniform: chunks wholly past the row
     const int c = (threadIdx.x + 256 * j) * 8;
-    if (c >= H) break;
-    const size_t o = (size_t)row * H + c;
+    const bool ok = c < H;
+    const size_t o = (size_t)row * H + (ok ? c : 0);
     const bf16x8 r = *(const bf16x8*)(resid + o);
-    float4 a = *(const float4*)(ws + o), b = *(const float4*)(ws + o + 4);
-    for (int sp = 1; sp < splits; ++sp) {
-      const float4 a2 = *(const float4*)(ws + sp * slice + o), b2 = *(const float4*)(ws + sp * slice + o + 4);
-      a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
-      b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+    const float4 g0 = *(const float4*)(g + (ok ? c : 0)), g1 = *(const float4*)(g + (ok ? c : 0) + 4);
+    gg[j][0] = g0.x; gg[j][1] = g0.y; gg[j][2] = g0.z; gg[j][3] = g0.w;
+    gg[j][4] = g1.x; gg[j][5] = g1.y; gg[j][6] = g1.z; gg[j][7] = g1.w;
+    float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += 4) {
+      float4 a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* src = ws + (size_t)min(s0 + u, splits - 1) * slice + o;
+        a[u] = *(const float4*)src;
+        b[u] = *(const float4*)(src + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (s0 + u >= splits) break;
+        p[0] += a[u].x; p[1] += a[u].y; p[2] += a[u].z; p[3] += a[u].w;
+        p[4] += b[u].x; p[5] += b[u].y; p[6] += b[u].z; p[7] += b[u].w;
+      }
     }
-    const float p[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      v[j][e] = p[e] + (float)r[e];
+      v[j][e] = ok ? p[e] + (float)r[e] : 0.f;
       ss += v[j][e] * v[j][e];
     }
-    *(float4*)(h + o) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
-    *(float4*)(h + o + 4) = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -214,12 +235,13 @@ __global__ __launch_bounds__(256) void rmsnorm_splits_kernel(const float* __rest
   for (int j = 0; j < kSplitRowChunks; ++j) {
     const int c = (threadIdx.x + 256 * j) * 8;
     if (c >= H) break;
-    const float4 g0 = *(const float4*)(g + c), g1 = *(const float4*)(g + c + 4);
-    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    f16x8 o;
+    const size_t o = (size_t)row * H + c;
+    *(float4*)(h + o) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+    *(float4*)(h + o + 4) = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
+    f16x8 o8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = f32_to_f16_sat(v[j][e] * inv * gg[e]);
-    *(f16x8*)(y + (size_t)row * H + c) = o;
+    for (int e = 0; e < 8; ++e) o8[e] = f32_to_f16_sat(v[j][e] * inv * gg[j][e]);
+    *(f16x8*)(y + o) = o8;
   }
 }
 
