@@ -174,7 +174,9 @@ typedef struct {
 /* Validates the configuration, allocates the library-owned weight copies and
  * workspace (sized by max_tokens / max_seqs), converts f32 weights to bf16
  * and interleaves gate/up rows for the fused SiLU-gate epilogue.
- * Synchronises `stream` before returning.  *out is NULL on failure. */
+ * Synchronises `stream` before returning.  *out is NULL on failure.
+ * TDL_E_UNSUPPORTED when min(max_seqs, max_tokens) > 2048 (decode sequences
+ * in one call) or max_position > 131072. */
 tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_weights* w,
                         tdl_stream stream, tdl_layer** out);
 

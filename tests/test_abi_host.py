@@ -49,6 +49,7 @@ def cfg_ok(tdl, **kw):
     (dict(head_dim=96), 2), (dict(n_q_heads=6, n_kv_heads=4), 1), (dict(n_q_heads=12, n_kv_heads=4), 2),
     (dict(hidden=200), 2), (dict(intermediate=100), 2), (dict(weight_dtype=3), 1),
     (dict(max_tokens=0), 1), (dict(rope_theta=0.0), 1), (dict(weight_dtype=2, intermediate=688), 1),
+    (dict(max_seqs=4096, max_tokens=4096), 2), (dict(max_position=300000), 2),
 ])
 def test_layer_create_rejects_bad_config(kw, status):
     import transformer_decoder_layer_amd as tdl

@@ -162,6 +162,9 @@ tdl_status check_config(const tdl_layer_config* c) {
     return fail(TDL_E_INVALID, "Q8_0 needs every input dimension to be a multiple of 32");
   if (c->max_tokens <= 0 || c->max_seqs <= 0 || c->max_position <= 0)
     return fail(TDL_E_INVALID, "max_tokens, max_seqs and max_position must be positive");
+  if (std::min(c->max_seqs, c->max_tokens) > kMaxDecodeSeqs || c->max_position > kMaxDecodePosition)
+    return fail(TDL_E_UNSUPPORTED, "decode batches above %d sequences or contexts above %d tokens",
+                kMaxDecodeSeqs, kMaxDecodePosition);
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f))
     return fail(TDL_E_INVALID, "rms_eps must be >= 0 and rope_theta > 0");
   return TDL_OK;

@@ -170,6 +170,8 @@ hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, int n_prefill, 
 // (one query row each).  Each sequence's context is cut into partitions of
 // part_blocks blocks; `part` holds the partitions' (O, m, l) and a merge
 // kernel combines them.
+constexpr int kMaxDecodeSeqs = 2048;        // sequences in one decode launch
+constexpr int kMaxDecodePosition = 131072;  // longest context (keys) per sequence
 struct DecodePlan {
   int part_blocks;
   int max_parts;
