@@ -146,7 +146,7 @@ def main():
     gu_flops = 2 * T * (2 * I) * H
     gu_ms = stage_ms["gate_up"]
     gu_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "gate_up GEMM + SiLU-gate (fp16 operands)",
+    roofline = {"bound": "mfma", "kernel": "gate_up GEMM + SiLU-gate (fp16 operands; with its split-tail reduction)",
                 "achieved": round(gu_tflops, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gu_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": measured_traffic(),
                 "algorithmic_bytes": 2 * (T * H + 2 * I * H + T * I),
