@@ -10,7 +10,10 @@ Also reported (same JSON line): the paged decode step of the same layer (batch
 64, contexts U[128, 4096], bf16 cache, random block permutation) in us/step
 with its HBM fraction; the dominant kernel's roofline (per-kernel HIP-event
 durations recorded by the library on the call's stream over the timed
-region); and the oracle's CPU throughput on a bounded sample of the prefill.
+region); the other configurations (the 512-token prefill, the Qwen3-8B
+decode over a u8 cache at batch 128, the Qwen3-8B Q8_0 mixed step), each with
+its roofline fraction; and the oracle's CPU throughput on a bounded sample of
+the prefill.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -47,6 +50,8 @@ def parse():
                     help="prompt tokens the oracle runs for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the other workloads (512-token prefill, Qwen3 u8 decode, Q8_0 mixed step)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 512 MiB device-to-device copy (a known byte count that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -85,6 +90,145 @@ def linear_flops_per_token(s):
 
 def weight_bytes(s):
     return linear_flops_per_token(s) // 2 * 2   # 2-byte weights
+
+
+def timed_steps(torch, stream, step_fn, n, flush=None, sink=None):
+    """Per-step HIP-event times (ms, sorted) of n calls on `stream`; with
+    `flush`, a 1 GiB read evicts L2 and the MALL before each call."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        if flush is not None:
+            torch.sum(flush, dim=0, out=sink)
+        e0.record(stream)
+        step_fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+
+
+def attention_flops(D, Hq, n_pairs):
+    return 4 * D * Hq * n_pairs  # Q.K and P.V: 2 FLOP x D per (query, key) pair and head
+
+
+def other_workloads(args, torch, synth, tdl, stream, layer512):
+    """The other configurations of the layer, measured the same way (synthetic
+    inputs, resident in HBM): the 512-token prefill of the same Qwen2.5-7B
+    layer, the Qwen3-8B decode over a u8 cache (batch 128), and the Qwen3-8B
+    Q8_0 mixed step (a 2048-token chunk + 64 decode rows)."""
+    out = {}
+    n_steps = max(5, args.steps)
+    # ---- Qwen2.5-7B prefill of 512 tokens
+    layer, shape = layer512
+    T = 512
+    x = synth.torch_normal((T, shape.hidden), seed=21, dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    nb = T // 16
+    tab = torch.from_numpy(synth.random_tables(np.random.default_rng(22), [T], n_blocks=nb)[0]).cuda()
+    kv = tdl.KvCache(nb, shape.n_kv_heads, shape.head_dim, "bf16")
+    for _ in range(3):
+        layer.prefill(x, y, 0, kv, tab)
+    times = timed_steps(torch, stream, lambda: layer.prefill(x, y, 0, kv, tab), n_steps)
+    ms = float(np.median(times))
+    fl = linear_flops_per_token(shape) * T + attention_flops(shape.head_dim, shape.n_q_heads, T * (T + 1) // 2)
+    out["qwen25_prefill_512"] = {
+        "workload": "qwen2.5-7b-shaped layer, causal prefill seq 512, batch 1, bf16 paged KV cache written",
+        "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 1), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}}
+    log(f"prefill 512: {ms * 1e3:.1f} us/step")
+    kv.close()
+    del x, y, kv
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    # ---- Qwen3-8B decode, batch 128, ctx U[512, 8192], u8 cache
+    wl = synth.WORKLOADS["qwen3_decode_u8_b128"]
+    shape = wl.shape
+    Hkv, D, H = shape.n_kv_heads, shape.head_dim, shape.hidden
+    B = wl.decode_batch
+    ctx = synth.context_lengths(np.random.default_rng(30), wl)
+    totals = (ctx + 1).tolist()
+    nb = int(sum(math.ceil(t / 16) for t in totals))
+    tab_np = synth.random_tables(np.random.default_rng(31), totals, n_blocks=nb)
+    tab = torch.from_numpy(tab_np).cuda()
+    log(f"qwen3 u8 decode: weights, cache of {int(ctx.sum())} tokens")
+    layer = tdl.Layer(tdl.make_config(shape, max_tokens=B, max_seqs=B, max_position=8448),
+                      synth.torch_weights(shape, seed=32))
+    kv = tdl.KvCache(nb, Hkv, D, "u8")
+    # per-channel parameters from a sample of the same N(0,1) distribution,
+    # then the cached tokens, 16 sequences at a time
+    kv.calibrate(synth.torch_normal((1 << 16, Hkv, D), seed=33), synth.torch_normal((1 << 16, Hkv, D), seed=34))
+    for s0 in range(0, B, 16):
+        c = ctx[s0:s0 + 16]
+        n = int(c.sum())
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(c)]).astype(np.int32)).cuda()
+        kv.write(cu, torch.zeros(len(c), dtype=torch.int32, device="cuda"), tab[s0:s0 + 16].contiguous(),
+                 synth.torch_normal((n, Hkv, D), seed=100 + s0), synth.torch_normal((n, Hkv, D), seed=200 + s0))
+    ctx_d = torch.from_numpy(ctx).cuda()
+    x = synth.torch_normal((B, H), seed=35, dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    max_ctx = int(ctx.max()) + 1
+    for _ in range(3):
+        layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv)
+    times = timed_steps(torch, stream, lambda: layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv),
+                        args.decode_steps, flush, sink)
+    us = 1e3 * float(np.median(times))
+    kv_bytes = int(sum(totals)) * Hkv * D * 2  # u8 K and V
+    step_bytes = weight_bytes(shape) + kv_bytes + 2 * B * H * 2
+    assert torch.isfinite(y.float()).all(), "non-finite u8 decode output"
+    out["qwen3_decode_u8_b128"] = {
+        "workload": "qwen3-8b-shaped layer (Q/K RMSNorm) paged decode, batch 128, ctx U[512,8192], "
+                    "u8 per-channel asymmetric KV, block 16, random block permutation; L2/MALL flushed between steps",
+        "us_per_step": round(us, 2), "algorithmic_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(step_bytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}}
+    log(f"qwen3 u8 decode: {us:.1f} us/step")
+    layer.close()
+    kv.close()
+    del x, y, kv, tab, ctx_d
+
+    # ---- Qwen3-8B Q8_0 mixed step: one 2048-token chunk + 64 decode rows at ctx 2048
+    wl = synth.WORKLOADS["qwen3_q80_mixed"]
+    shape = wl.shape
+    Hq, Hkv, D, H = shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.hidden
+    Tc, B, c0 = wl.prefill_len, wl.decode_batch, wl.ctx_fixed
+    totals = [Tc] + [c0 + 1] * B
+    nb = int(sum(math.ceil(t / 16) for t in totals))
+    tab = torch.from_numpy(synth.random_tables(np.random.default_rng(40), totals, n_blocks=nb)).cuda()
+    log("q8_0 mixed: weights, cache")
+    layer = tdl.Layer(tdl.make_config(shape, max_tokens=Tc + B, max_seqs=B + 1, max_position=4096),
+                      synth.torch_weights(shape, seed=41))
+    kv = tdl.KvCache(nb, Hkv, D, "bf16")
+    cu = torch.from_numpy(np.arange(B + 1, dtype=np.int32) * c0).cuda()
+    kv.write(cu, torch.zeros(B, dtype=torch.int32, device="cuda"), tab[1:].contiguous(),
+             synth.torch_normal((B * c0, Hkv, D), seed=42, dtype=torch.bfloat16),
+             synth.torch_normal((B * c0, Hkv, D), seed=43, dtype=torch.bfloat16))
+    rows = Tc + B
+    q_start = torch.from_numpy(np.array([0] + [Tc + i for i in range(B)], np.int32)).cuda()
+    q_len = torch.from_numpy(np.array([Tc] + [1] * B, np.int32)).cuda()
+    ctx_len = torch.from_numpy(np.array([0] + [c0] * B, np.int32)).cuda()
+    x = synth.torch_normal((rows, H), seed=44, dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    step = lambda: layer.step(x, y, q_start, q_len, ctx_len, tab, 1, Tc, c0 + 1, kv)
+    for _ in range(3):
+        step()
+    times = timed_steps(torch, stream, step, n_steps)
+    ms = float(np.median(times))
+    fl = linear_flops_per_token(shape) * rows + attention_flops(D, Hq, Tc * (Tc + 1) // 2 + B * (c0 + 1))
+    assert torch.isfinite(y.float()).all(), "non-finite mixed-step output"
+    out["qwen3_q80_mixed"] = {
+        "workload": "qwen3-8b-shaped layer with Q8_0 weights, mixed step: 2048-token chunked prefill + "
+                    "64 decode rows at ctx 2048, bf16 paged KV cache (Q8_0 codes convert exactly to fp16 "
+                    "MFMA operands, so the fp16 peak applies)",
+        "ms_per_step": round(ms, 4), "rows_per_s": round(rows / (ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 1), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}}
+    log(f"q8_0 mixed: {ms * 1e3:.1f} us/step")
+    layer.close()
+    kv.close()
+    del flush
+    return out
 
 
 def main():
@@ -237,6 +381,11 @@ def main():
         assert torch.isfinite(yd.float()).all(), "non-finite decode output"
         del flush
 
+    # ----------------------------------------------- the other workloads
+    others = None
+    if not args.no_other:
+        others = other_workloads(args, torch, synth, tdl, stream, (layer, shape))
+
     # --------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -286,6 +435,7 @@ def main():
                        "frac": round(layer_tflops / PEAK_MFMA_TFLOPS, 4)},
         "stages_ms": stage_report,
         "decode": decode,
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

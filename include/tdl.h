@@ -173,7 +173,11 @@ typedef struct {
 
 /* Validates the configuration, allocates the library-owned weight copies and
  * workspace (sized by max_tokens / max_seqs), converts f32 weights to bf16
- * and interleaves gate/up rows for the fused SiLU-gate epilogue.
+ * and interleaves gate/up rows for the fused SiLU-gate epilogue.  A Q8_0
+ * layer with max_tokens > 128 also keeps each matrix expanded (code x scale
+ * rounded once to fp16, bf16 for the down projection: about twice the
+ * codes' memory) for calls of more than 128 rows, whose GEMMs are bound by
+ * MFMA throughput; calls of up to 128 rows stream the 1-byte codes.
  * Synchronises `stream` before returning.  *out is NULL on failure.
  * TDL_E_UNSUPPORTED when min(max_seqs, max_tokens) > 2048 (decode sequences
  * in one call) or max_position > 131072. */

@@ -2,9 +2,9 @@
 query-group ratio and head dimension the attention kernels are built for,
 Q8_0 weights on the decode-sized GEMM, a reduction dimension that ends in a
 half 64-k stage, calls exactly at max_tokens / max_position, and mixed steps
-with only decode or only prefill rows, and the rejection of misaligned
-activation pointers.  Same tolerance as the other layer
-tests (stage by stage, cache rows checked)."""
+with only decode or only prefill rows, Q8_0 layers above 128 rows (expanded
+weight copies), and the rejection of misaligned activation pointers.  Same
+tolerance as the other layer tests (stage by stage, cache rows checked)."""
 import dataclasses
 
 import pytest
@@ -122,3 +122,14 @@ def test_misaligned_activations_rejected():
     with pytest.raises(tdl.TdlError):
         layer.prefill(t["x"], y_off, 0, None, None)
     torch.cuda.synchronize()
+
+
+def test_q80_over_128_rows_expanded_weights():
+    # more than 128 rows: the Q8_0 layer's GEMMs run on its fp16/bf16
+    # expanded copies (codes x scales rounded once) instead of the codes
+    wl = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=TINY_Q80)
+    ctx = [5, 130, 301]
+    inp = synth.make_inputs(wl, seed=31, prefill_len=200, prefill_start=40, decode_batch=len(ctx),
+                            decode_ctx=ctx)
+    layer, kv, t, cache, rows = check_layer(inp, what="mixed q80 203 rows")
+    check_cache_rows(inp, kv, cache, range(1 + len(ctx)))

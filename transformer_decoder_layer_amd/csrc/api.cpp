@@ -84,6 +84,10 @@ struct tdl_layer {
   // per weight matrix (QKV, output, gate/up, down): stored in the packed
   // tile layout (bf16/fp16 with N % 16 == 0 and K % 64 == 0) or row-major
   int packed[4] = {0, 0, 0, 0};
+  // Q8_0 layers that take more than 128 rows: the four matrices expanded to
+  // fp16 (bf16 for the down projection) in the packed tile layout, for the
+  // compute-bound GEMMs (the decode-sized ones stream the 1-byte codes)
+  void* wexp[4] = {nullptr, nullptr, nullptr, nullptr};
   void* wd = nullptr;
   __half* wd_s = nullptr;
   float *ln1 = nullptr, *ln2 = nullptr, *qn = nullptr, *kn = nullptr;
@@ -175,13 +179,17 @@ struct GemmShapes {
 };
 
 // Largest split-K workspace over every row count a call may use.
-void gemm_ws_need(const tdl_layer_config& c, int Nqkv, bool q80, size_t* ws) {
+// (Q8_0 layers with expanded copies plan rows > kQ80CodeRows on those.)
+constexpr int kQ80CodeRows = 128;
+void gemm_ws_need(const tdl_layer_config& c, int Nqkv, bool q80, bool expanded, size_t* ws) {
   const int H = c.hidden, QD = c.n_q_heads * c.head_dim, I = c.intermediate;
   const int shapes[4][3] = {{Nqkv, H, EPI_BIAS_F32}, {H, QD, EPI_RESID_F32},
                             {2 * I, H, EPI_SILU_GATE}, {H, I, EPI_RESID_BF16}};
   size_t w = 0;
-  for (int M = 1; M <= c.max_tokens; ++M)
-    for (auto& s : shapes) w = std::max(w, gemm_plan(M, s[0], s[1], q80, s[2]).ws_floats);
+  for (int M = 1; M <= c.max_tokens; ++M) {
+    const bool codes = q80 && !(expanded && M > kQ80CodeRows);
+    for (auto& s : shapes) w = std::max(w, gemm_plan(M, s[0], s[1], codes, s[2]).ws_floats);
+  }
   *ws = w;
 }
 
@@ -215,9 +223,18 @@ KvPool pool_of(const tdl_layer* L, const tdl_kv_cache* kv) {
 // defer: a split-K plan leaves its fp32 partials in the GEMM workspace for
 // the next kernel to sum (*splits_out tells how many; 1 = C was written).
 tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const void* A, const void* B,
-                    const __half* Bs, int packed, int epi, const float* bias, const void* resid,
-                    int ldr, void* C, int ldc, bool defer = false, int* splits_out = nullptr) {
-  const GemmPlan pl = gemm_plan(M, N, K, L->q80, epi);
+                    const __half* Bs, int packed, const void* Bexp, int epi, const float* bias,
+                    const void* resid, int ldr, void* C, int ldc, bool defer = false,
+                    int* splits_out = nullptr) {
+  // Q8_0: more than kQ80CodeRows rows take the expanded (packed) copy
+  bool q80 = L->q80;
+  if (q80 && M > kQ80CodeRows && Bexp) {
+    q80 = false;
+    B = Bexp;
+    Bs = nullptr;
+    packed = 1;
+  }
+  const GemmPlan pl = gemm_plan(M, N, K, q80, epi);
   if (splits_out) *splits_out = defer ? pl.splits : 1;
   if (pl.ws_floats > L->gemm_ws_floats)
     return fail(TDL_E_CAPACITY, "GEMM workspace too small for M=%d N=%d K=%d", M, N, K);
@@ -237,7 +254,7 @@ tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const voi
   a.ldc = ldc;
   a.ws = L->gemm_ws;
   a.b_packed = packed;
-  HIP_TRY(gemm_launch(pl, a, L->q80, epi, st, !defer));
+  HIP_TRY(gemm_launch(pl, a, q80, epi, st, !defer));
   return TDL_OK;
 }
 
@@ -298,7 +315,7 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   int qkv_splits = 1;
   {
     StageTimer t(L, TDL_STAGE_QKV, st);
-    TRY(run_gemm(L, st, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->packed[0], EPI_BIAS_F32, L->bqkv, nullptr,
+    TRY(run_gemm(L, st, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->packed[0], L->wexp[0], EPI_BIAS_F32, L->bqkv, nullptr,
                  0, L->qkv, L->Nqkv, true, &qkv_splits));
   }
   {
@@ -319,7 +336,7 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   int o_splits = 1;
   {
     StageTimer t(L, TDL_STAGE_O_PROJ, st);
-    TRY(run_gemm(L, st, rows, H, Hq * D, L->o, L->wo, L->wo_s, L->packed[1], EPI_RESID_F32, nullptr, x, H, L->h,
+    TRY(run_gemm(L, st, rows, H, Hq * D, L->o, L->wo, L->wo_s, L->packed[1], L->wexp[1], EPI_RESID_F32, nullptr, x, H, L->h,
                  H, H <= kFusedNormMaxH, &o_splits));
   }
   {
@@ -331,12 +348,12 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   }
   {
     StageTimer t(L, TDL_STAGE_GATE_UP, st);
-    TRY(run_gemm(L, st, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, L->packed[2], EPI_SILU_GATE, nullptr, nullptr, 0,
+    TRY(run_gemm(L, st, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, L->packed[2], L->wexp[2], EPI_SILU_GATE, nullptr, nullptr, 0,
                  L->a, I));
   }
   {
     StageTimer t(L, TDL_STAGE_DOWN, st);
-    TRY(run_gemm(L, st, rows, H, I, L->a, L->wd, L->wd_s, L->packed[3], EPI_RESID_BF16, nullptr, L->h, H, y, H));
+    TRY(run_gemm(L, st, rows, H, I, L->a, L->wd, L->wd_s, L->packed[3], L->wexp[3], EPI_RESID_BF16, nullptr, L->h, H, y, H));
   }
   return TDL_OK;
 }
@@ -497,6 +514,30 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
     CHIP(hipMemcpyAsync(L->wo_s, w->wo_scale, (size_t)H * (QD / 32) * 2, hipMemcpyDeviceToDevice, st));
     CHIP(hipMemcpyAsync(L->wd_s, w->wd_scale, (size_t)H * (I / 32) * 2, hipMemcpyDeviceToDevice, st));
     CHIP(interleave_gate_up(w->wg_scale, w->wu_scale, (int)rs, I, L->wgu_s, st));
+    if (c.max_tokens > kQ80CodeRows) {
+      // expanded copies for the compute-bound GEMMs (one packing temporary)
+      const int shapes[4][2] = {{L->Nqkv, H}, {H, QD}, {2 * I, H}, {H, I}};
+      const void* codes[4] = {L->wqkv, L->wo, L->wgu, L->wd};
+      const void* scales[4] = {L->wqkv_s, L->wo_s, L->wgu_s, L->wd_s};
+      bool ok = true;
+      size_t most = 0;
+      for (auto& sh : shapes) {
+        ok = ok && sh[0] % 16 == 0 && sh[1] % 64 == 0;
+        most = std::max(most, (size_t)sh[0] * sh[1] * 2);
+      }
+      if (ok) {
+        void* tmp = nullptr;
+        CTRY(dalloc(L, &tmp, most));
+        for (int i = 0; i < 4; ++i) {
+          CTRY(dalloc(L, &L->wexp[i], (size_t)shapes[i][0] * shapes[i][1] * 2));
+          CHIP(expand_q80(codes[i], scales[i], shapes[i][0], shapes[i][1], tmp, i != 3, st));
+          CHIP(pack_weights(tmp, L->wexp[i], shapes[i][0], shapes[i][1], st));
+        }
+        CHIP(hipStreamSynchronize(st));
+        L->allocs.erase(std::find(L->allocs.begin(), L->allocs.end(), tmp));
+        (void)hipFree(tmp);
+      }
+    }
   }
   if (c.qkv_bias) {
     CTRY(dalloc(L, &L->bqkv, (size_t)L->Nqkv * 4));
@@ -525,7 +566,7 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   CTRY(dalloc(L, &L->h, (size_t)T * H * 4));
   CTRY(dalloc(L, &L->hn, (size_t)T * H * 2));
   CTRY(dalloc(L, &L->a, (size_t)T * I * 2));
-  gemm_ws_need(c, L->Nqkv, q80, &L->gemm_ws_floats);
+  gemm_ws_need(c, L->Nqkv, q80, L->wexp[0] != nullptr, &L->gemm_ws_floats);
   CTRY(dalloc(L, &L->gemm_ws, L->gemm_ws_floats * 4));
   const int max_dec = std::min(c.max_seqs, c.max_tokens);
   L->dec_part_floats = decode_part_need(c, max_dec);

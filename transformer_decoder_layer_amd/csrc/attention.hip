@@ -52,13 +52,13 @@ __device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
 __device__ __forceinline__ f16 to_f16(float v) { return f32_to_f16_sat(v); }
 typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));
-// one packed convert (round to nearest even) and a packed clamp to the fp16
-// range for two bf16 values
+// one packed convert of two bf16 cache values to fp16: exact inside the fp16
+// range, which is the prefill kernel's domain for K and V (|K|, |V| <=
+// 65504; no clamp -- it would cost the tile conversion 40% of its work and
+// would not make values outside the range correct either)
 __device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t w) {
   const f32x2v v = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
-  f16x2v h = __builtin_convertvector(v, f16x2v);
-  h = __builtin_elementwise_min(__builtin_elementwise_max(h, (f16x2v)(-kF16Max)), (f16x2v)(kF16Max));
-  return __builtin_bit_cast(uint32_t, h);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
 }
 
 __device__ __forceinline__ int seq_row(const SeqInfo& s, int sidx) {
@@ -237,7 +237,6 @@ __global__ __launch_bounds__(NREP * 64) void attn_prefill_kernel(const float* __
     __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
       const int cur = t & 1;
-      const bool more = t + 1 < n_tiles;
       // unconditional (a tile past the end reads valid blocks and is never
       // stored), so no loaded register is merged across a branch
       load_tile(t + 1);
@@ -307,7 +306,10 @@ __global__ __launch_bounds__(NREP * 64) void attn_prefill_kernel(const float* __
           acc[t2] = mfma32x32x16(__builtin_bit_cast(f16x8, w), pb[kc], acc[t2]);
         }
       }
-      if (more) store_tile(t + 1, cur ^ 1);
+      // unconditional, so that its conversions can interleave with the PV
+      // MFMAs above: past the last tile it fills the idle buffer from valid
+      // blocks (the next query tile reloads both buffers after a barrier)
+      store_tile(t + 1, cur ^ 1);
       __syncthreads();
     }
 

@@ -152,6 +152,10 @@ hipError_t copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 // 8*(l/16)..+7) is chunk l of its tile, so a fragment load, from memory or
 // from a tile copied to LDS as is, is one contiguous 1 KB access.  Needs
 // N % 16 == 0, K % 32 == 0.
+// Q8_0 codes [N][K] int8 and scales [N][K/32] fp16 -> dst [N][K] fp16
+// (dst_f16 = 1, saturating) or bf16: code * scale rounded to nearest even.
+hipError_t expand_q80(const void* codes, const void* scales, int N, int K, void* dst, int dst_f16,
+                      hipStream_t s);
 hipError_t pack_weights(const void* src, void* dst, int N, int K, hipStream_t s);
 // Element offset of (n, k) in that layout.
 __host__ __device__ inline size_t packed_offset(int n, int k, int N) {

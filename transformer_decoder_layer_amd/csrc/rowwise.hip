@@ -322,6 +322,34 @@ __global__ void convert_kernel(const void* __restrict__ src, int src_f32, void* 
   }
   if (sat) atomicAdd(n_sat, sat);
 }
+// Q8_0 -> fp16 or bf16 weights: w[n][k] = code[n][k] * scale[n][k/32], the
+// product (exact in fp32) rounded to nearest even, fp16 saturating.  One
+// thread per 8 codes.
+__global__ void expand_q80_kernel(const int8_t* __restrict__ codes, const __half* __restrict__ scales,
+                                  int N, int K, void* __restrict__ dst, int dst_f16) {
+  const int64_t n8 = (int64_t)N * (K / 8);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int n = (int)(i / (K / 8)), k = (int)(i % (K / 8)) * 8;
+    const float sc = __half2float(scales[(size_t)n * (K / 32) + k / 32]);
+    const uint2 c = *(const uint2*)(codes + (size_t)n * K + k);
+    const uint32_t w[2] = {c.x, c.y};
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)(int8_t)(w[e >> 2] >> (8 * (e & 3))) * sc;
+    if (dst_f16) {
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = f32_to_f16_sat(v[e]);
+      *(f16x8*)((f16*)dst + (size_t)n * K + k) = o;
+    } else {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16(v[e]);
+      *(bf16x8*)((bf16*)dst + (size_t)n * K + k) = o;
+    }
+  }
+}
 __global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -430,6 +458,13 @@ hipError_t rope_table_build(float2* tab, int max_pos, int D, double theta, hipSt
 hipError_t convert_weights(const void* src, int src_f32, void* dst, int dst_f16, int64_t n,
                            int* n_saturated, hipStream_t s) {
   convert_kernel<<<2048, 256, 0, s>>>(src, src_f32, dst, dst_f16, n, n_saturated);
+  return hipGetLastError();
+}
+
+hipError_t expand_q80(const void* codes, const void* scales, int N, int K, void* dst, int dst_f16,
+                      hipStream_t s) {
+  if (K % 32 != 0) return hipErrorInvalidValue;
+  expand_q80_kernel<<<2048, 256, 0, s>>>((const int8_t*)codes, (const __half*)scales, N, K, dst, dst_f16);
   return hipGetLastError();
 }
 
