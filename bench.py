@@ -106,6 +106,20 @@ def timed_steps(torch, stream, step_fn, n, flush=None, sink=None):
     return sorted(e0.elapsed_time(e1) for e0, e1 in ev)
 
 
+def stage_profile(layer, step_fn, n, before=None):
+    """ms per launch of each stage over n calls, from the library's HIP events."""
+    import torch
+    layer.profile_enable(True)
+    for _ in range(n):
+        if before is not None:
+            before()
+        step_fn()
+    torch.cuda.synchronize()
+    prof = layer.profile_read()
+    layer.profile_enable(False)
+    return {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]}
+
+
 def attention_flops(D, Hq, n_pairs):
     return 4 * D * Hq * n_pairs  # Q.K and P.V: 2 FLOP x D per (query, key) pair and head
 
@@ -134,7 +148,8 @@ def other_workloads(args, torch, synth, tdl, stream, layer512):
         "workload": "qwen2.5-7b-shaped layer, causal prefill seq 512, batch 1, bf16 paged KV cache written",
         "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 1), "peak": PEAK_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}}
+                     "unit": "TFLOP/s", "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)},
+        "stages_ms": stage_profile(layer, lambda: layer.prefill(x, y, 0, kv, tab), 5)}
     log(f"prefill 512: {ms * 1e3:.1f} us/step")
     kv.close()
     del x, y, kv
@@ -182,7 +197,9 @@ def other_workloads(args, torch, synth, tdl, stream, layer512):
                     "u8 per-channel asymmetric KV, block 16, random block permutation; L2/MALL flushed between steps",
         "us_per_step": round(us, 2), "algorithmic_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(step_bytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}}
+                     "unit": "GB/s", "frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "stages_ms": stage_profile(layer, lambda: layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv), 5,
+                                   lambda: torch.sum(flush, dim=0, out=sink))}
     log(f"qwen3 u8 decode: {us:.1f} us/step")
     layer.close()
     kv.close()
@@ -223,7 +240,8 @@ def other_workloads(args, torch, synth, tdl, stream, layer512):
                     "MFMA operands, so the fp16 peak applies)",
         "ms_per_step": round(ms, 4), "rows_per_s": round(rows / (ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 1), "peak": PEAK_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}}
+                     "unit": "TFLOP/s", "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)},
+        "stages_ms": stage_profile(layer, step, 5)}
     log(f"q8_0 mixed: {ms * 1e3:.1f} us/step")
     layer.close()
     kv.close()

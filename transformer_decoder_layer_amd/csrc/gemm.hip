@@ -641,7 +641,7 @@ struct Cfg {
 // 4608 splits into 16 tiles, so 4096 rows make one tile per CU).  Eight-wave
 // tiles keep two waves per SIMD.
 constexpr int kNumCfgs = 6;
-constexpr Cfg kCfgs[kNumCfgs] = {{256, 256, 1.0f}, {256, 224, 0.96f}, {128, 128, 0.55f},
+constexpr Cfg kCfgs[kNumCfgs] = {{256, 256, 1.0f}, {256, 224, 0.96f}, {128, 128, 0.4f},
                                  {64, 128, 0.35f},  {128, 128, 0.5f},  {256, 288, 0.98f}};
 
 template <bool Q80, int EPI, typename T, bool DIRECT>
@@ -751,9 +751,10 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
       const int wgs = tiles * sp;
       const double rounds = std::ceil((double)wgs / kCUs);
       double cost = rounds * (double)c.BM * c.BN * kps / c.eff;
-      // split-K: the partial slices make a round trip through memory and the
-      // reduction is a second launch (expressed in the same MAC-time units)
-      if (sp > 1) cost += 2.0 * sp * (double)M * N * 4.0 * 40.0 / kCUs + 4.0e5;
+      // split-K: the fp32 partial slices make a round trip through memory
+      // (about 0.01 cost units per byte: a unit is ~25 ps of a CU, a byte
+      // ~0.25 ps of the chip) and the reduction is a second launch
+      if (sp > 1) cost += 0.01 * 2.0 * sp * (double)M * N * 4.0 + 2.4e5;
       if (cost < best_cost) {
         best_cost = cost;
         best = GemmPlan{};
