@@ -25,8 +25,8 @@
 // of one MFMA tile.  u8 caches are dequantised in registers: codes convert
 // exactly to bf16; the K scale is folded into q and the zero point into a
 // per-head constant, the V scale and zero point are applied once at the end.
-// The last workgroup of a (sequence, KV head) to finish merges the
-// partitions' (m, l, acc) triples in partition order.
+// A second kernel merges the partitions' (m, l, acc) triples of each
+// (sequence, KV head) in partition order.
 
 #include "common.h"
 #include "kernels.h"
@@ -346,33 +346,63 @@ constexpr int kPartStride(int D) { return 16 * D + 32; }
 
 template <int D, bool U8>
 struct DecFrags {
-  // K rows (A operand): key lane%16, channels 32s + 8*(lane/16) .. +7
-  typename std::conditional<U8, uint2, bf16x8>::type k[D / 32];
+  // K rows (A operand): key lane%16; bf16: channels 32s + 8*(lane/16) .. +7
+  // of product s; u8: 16 channels 64h + 16*(lane/16) .. +15 per load, the
+  // first 8 for product 2h, the last 8 for product 2h + 1 (dec_kchan)
+  typename std::conditional<U8, uint4, bf16x8>::type k[U8 ? D / 64 : D / 32];
   // V^T rows (A operand): channel 16t + lane%16, keys 4*(lane/16) .. +3
   typename std::conditional<U8, uint32_t, bf16x4>::type v[D / 16];
 };
 
+// First of the 8 channels lane group grp feeds to k-slots 8grp .. 8grp+7
+// of the key-query product s (any channel order gives the same dot product,
+// as long as K and q use the same one).  u8: a lane takes one 16-byte chunk
+// (16 channels) of its key row per pair of products.
+template <bool U8>
+__device__ __forceinline__ int dec_kchan(int s, int grp) {
+  return U8 ? 64 * (s >> 1) + 16 * grp + 8 * (s & 1) : 32 * s + 8 * grp;
+}
+
+// LDS staging of one u8 block-head: K (16 keys x D codes) then V^T (D
+// channels x 16 codes), 16-byte chunks.  K chunk c of key r sits at slot
+// r * CPR + (c ^ x(r)): the 8 lanes that read a 128-byte LDS row together
+// (same chunk, keys r..r+7) then hit 8 different bank quads.  Each copy
+// instruction still reads 1 KB of whole key rows.
+template <int D>
+struct DecStage {
+  static constexpr int kHalf = kBlockTokens * D;   // bytes of K (= of V)
+  static constexpr int kBytes = 2 * kHalf;
+  static constexpr int kInst = kHalf / 1024;       // copy instructions per half
+  static constexpr int CPR = D / 16;               // chunks per key row
+  __device__ static int x(int r) { return (r / (8 / CPR)) & (CPR - 1); }
+  __device__ static int k_slot(int r, int c) { return r * CPR + (c ^ x(r)); }
+  // source byte offset of the chunk that goes to slot s
+  __device__ static int k_src(int s) {
+    const int r = s / CPR;
+    return r * D + 16 * ((s % CPR) ^ x(r));
+  }
+};
+constexpr int kDecStages = 3;  // u8 blocks per wave in LDS (one read, two in flight)
+template <int D, bool U8>
+constexpr int dec_stage_array_bytes() {
+  constexpr int o = 2 * D * 16 * 4;  // two waves' O^T tiles
+  constexpr int st = U8 ? 4 * DecStage<D>::kBytes : 0;
+  return o > st ? o : st;
+}
+
+// bf16 blocks: fragments straight from the pool into registers
 template <int D, bool U8>
 __device__ __forceinline__ void dec_load(DecFrags<D, U8>& f, const DecArgs& a, int phys, int g,
                                          int col, int grp) {
+  static_assert(!U8, "u8 blocks are staged through LDS (DecStage)");
   const size_t hb = ((size_t)phys * a.Hkv + g) * (kBlockTokens * D);
-  if constexpr (U8) {
-    const uint8_t* kb = (const uint8_t*)a.pool.k + hb;
-    const uint8_t* vb = (const uint8_t*)a.pool.v + hb;
+  const bf16* kb = (const bf16*)a.pool.k + hb;
+  const bf16* vb = (const bf16*)a.pool.v + hb;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) f.k[s] = *(const uint2*)(kb + col * D + 32 * s + 8 * grp);
+  for (int s = 0; s < D / 32; ++s) f.k[s] = *(const bf16x8*)(kb + col * D + 32 * s + 8 * grp);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      f.v[t] = *(const uint32_t*)(vb + (16 * t + col) * kBlockTokens + 4 * grp);
-  } else {
-    const bf16* kb = (const bf16*)a.pool.k + hb;
-    const bf16* vb = (const bf16*)a.pool.v + hb;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) f.k[s] = *(const bf16x8*)(kb + col * D + 32 * s + 8 * grp);
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      f.v[t] = *(const bf16x4*)(vb + (16 * t + col) * kBlockTokens + 4 * grp);
-  }
+  for (int t = 0; t < D / 16; ++t)
+    f.v[t] = *(const bf16x4*)(vb + (16 * t + col) * kBlockTokens + 4 * grp);
 }
 
 __device__ __forceinline__ bf16x8 u8x8_to_bf16(uint2 w) {
@@ -395,7 +425,17 @@ template <int D, bool U8>
 __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   constexpr int NT = D / 16;  // 16-channel tiles of the output
   __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][D][17];
+  // u8: stage j of every wave's block rotation lives in its own array, so
+  // the compiler can tell a wave's reads of one stage from the copies still
+  // landing in the others (one array would make every read wait for all
+  // copies).  After the loop st0 / st1 hold the four waves' accumulators.
+  constexpr int SZ = dec_stage_array_bytes<D, U8>();
+  __shared__ __attribute__((aligned(16))) uint8_t st0[SZ];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[SZ];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[U8 ? SZ : 16];
+  // wave w's O^T tile [D][16] floats, columns XOR-swizzled by row
+  auto o_tile = [&](int w) { return (float*)(w < 2 ? st0 : st1) + (w & 1) * D * 16; };
+  auto o_idx = [](int d, int hh) { return d * 16 + (hh ^ (d & 15)); };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -421,12 +461,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   bf16x8 qlo[D / 32];
   float corr = 0.f;
   {
-    const float* qp = a.q + ((size_t)row * a.Hq + g * n_rep + col) * D + 8 * grp;
+    const float* qp = a.q + ((size_t)row * a.Hq + g * n_rep + col) * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       if (head_ok) {
-        const float4 x0 = *(const float4*)(qp + 32 * s), x1 = *(const float4*)(qp + 32 * s + 4);
+        const float* qs = qp + dec_kchan<U8>(s, grp);
+        const float4 x0 = *(const float4*)qs, x1 = *(const float4*)(qs + 4);
         v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
         v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
       }
@@ -435,7 +476,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       for (int e = 0; e < 8; ++e) {
         float qs = v[e];
         if constexpr (U8) {
-          const int ch = g * D + 32 * s + 8 * grp + e;
+          const int ch = g * D + dec_kchan<U8>(s, grp) + e;
           qs *= a.pool.k_scale[ch];
           corr += qs * (float)a.pool.k_zp[ch];
         }
@@ -469,88 +510,157 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       bf16x8 kf;
-      if constexpr (U8) kf = u8x8_to_bf16(f.k[s]);
+      if constexpr (U8) {
+        const uint4 w = f.k[s >> 1];
+        kf = u8x8_to_bf16((s & 1) ? uint2{w.z, w.w} : uint2{w.x, w.y});
+      }
       else kf = f.k[s];
       st = mfma16x16x32(kf, qf[s], st);
       st = mfma16x16x32(kf, qlo[s], st);
     }
-    // lane holds S[head col][key 4grp + r]
+    // lane holds S[head col][key 4grp + r]; only the sequence's last block
+    // has unwritten slots (wave-uniform test)
     const int key0 = blk * kBlockTokens + 4 * grp;
+    const bool partial = (blk + 1) * kBlockTokens > n_keys;
     float sv[4];
     float mb = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float v = (st[r] - corr) * sc;
-      if (key0 + r >= n_keys) v = -INFINITY;
-      sv[r] = v;
-      mb = fmaxf(mb, v);
+      sv[r] = (st[r] - corr) * sc;
+      mb = fmaxf(mb, sv[r]);
+    }
+    if (partial) {
+      mb = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (key0 + r >= n_keys) sv[r] = -INFINITY;
+        mb = fmaxf(mb, sv[r]);
+      }
     }
     mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
+    // the reference point of the exponentials moves (and the accumulators
+    // are rescaled) only when a block's maximum exceeds it by more than
+    // kLazy: P <= 2^kLazy keeps its hi + lo bf16 pair exact enough, softmax
+    // does not depend on the reference point
+    if (__builtin_amdgcn_ballot_w64(mb > m_run + kLazy) != 0) {
+      const float m_new = fmaxf(m_run, mb);
+      const float alpha = exp2f(m_run - m_new);  // 0 on the first block
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+    }
     // P as a bf16 pair hi + lo: the weights keep fp32 precision
     bf16x4 pf, pl;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float pv = exp2f(sv[r] - m_new);
+      const float pv = exp2f(sv[r] - m_run);
       pf[r] = f32_to_bf16(pv);
       pl[r] = f32_to_bf16(pv - (float)pf[r]);
       psum += pv;
     }
-    l_run = l_run * alpha + psum;
-    const bool tail = key0 + 3 >= n_keys;  // unwritten slots of the last block: zero V
+    l_run += psum;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       bf16x4 vf;
       if constexpr (U8) vf = u8x4_to_bf16(f.v[t]);
       else vf = f.v[t];
-      if (tail) {
+      if (partial) {  // unwritten slots of the last block: zero V
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (key0 + r >= n_keys) vf[r] = (bf16)0.f;
       }
-      acc[t] = mfma16x16x16(vf, pf, acc[t] * alpha);
+      acc[t] = mfma16x16x16(vf, pf, acc[t]);
       acc[t] = mfma16x16x16(vf, pl, acc[t]);
     }
   };
 
-  // three register sets in rotation: while one block computes, the next two
-  // blocks' loads are in flight.  Loads past the wave's last block repeat
-  // that block (valid addresses) and are never computed.  The explicit
-  // waits count this wave's vector-memory operations in program order; the
-  // scheduling barriers keep the compiler from moving loads or their uses
-  // across them.
-  constexpr int LOADS = D / 32 + D / 16;  // vector-memory operations per block
-  constexpr int kWaitOne = (LOADS & 15) | (7 << 4) | (15 << 8) | (((LOADS >> 4) & 3) << 14);
-  if (cnt > 0) {
-    auto phys_of = [&](int i) { return __shfl(my_phys, min(i, cnt - 1), 64); };
-    DecFrags<D, U8> f0, f1, f2;
-    dec_load<D, U8>(f0, a, phys_of(0), g, col, grp);
-    dec_load<D, U8>(f1, a, phys_of(1), g, col, grp);
-    for (int i = 0; i < cnt; i += 3) {
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(kWaitOne);
-      __builtin_amdgcn_sched_barrier(0);
-      dec_load<D, U8>(f2, a, phys_of(i + 2), g, col, grp);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(f0, i);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(kWaitOne);
-      __builtin_amdgcn_sched_barrier(0);
-      dec_load<D, U8>(f0, a, phys_of(i + 3), g, col, grp);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < cnt) compute(f1, i + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(kWaitOne);
-      __builtin_amdgcn_sched_barrier(0);
-      dec_load<D, U8>(f1, a, phys_of(i + 4), g, col, grp);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 2 < cnt) compute(f2, i + 2);
+  // Loads past the wave's last block repeat that block (valid addresses)
+  // and are never computed.  The explicit waits count this wave's
+  // vector-memory operations in program order; the scheduling barriers keep
+  // the compiler from moving loads or their uses across them.
+  if constexpr (U8) {
+    // u8: whole cache lines go straight to LDS (16 bytes per lane, 1 KB per
+    // instruction; kDecStages blocks per wave in rotation), fragments are
+    // read back from there.  Read in place as register fragments, a block
+    // would cost 3x the cache-line requests (each key row is 128 bytes, a
+    // fragment load takes 16-64 of them), which bounds this kernel.
+    using St = DecStage<D>;
+    constexpr int NB = kDecStages;
+    constexpr int LOADS = 2 * St::kInst;
+    constexpr int kWaitIn = (NB - 2) * LOADS;
+    constexpr int kWait = (kWaitIn & 15) | (7 << 4) | (15 << 8) | (((kWaitIn >> 4) & 3) << 14);
+    static_assert(NB == 3, "one LDS array per stage");
+    auto stage = [&](int j) { return (j == 0 ? st0 : j == 1 ? st1 : st2) + wave * St::kBytes; };
+    if (cnt > 0) {
+      auto phys_of = [&](int i) { return __shfl(my_phys, min(i, cnt - 1), 64); };
+      auto issue = [&](int i, int buf) {
+        const size_t hb = ((size_t)phys_of(i) * a.Hkv + g) * (kBlockTokens * D);
+        const uint8_t* kb = (const uint8_t*)a.pool.k + hb;
+        const uint8_t* vb = (const uint8_t*)a.pool.v + hb;
+        uint8_t* kd = stage(buf);
+#pragma unroll
+        for (int j = 0; j < St::kInst; ++j)
+          __builtin_amdgcn_global_load_lds((const void*)(kb + St::k_src(64 * j + lane)),
+                                           (lds_void*)(kd + 1024 * j), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < St::kInst; ++j)
+          __builtin_amdgcn_global_load_lds((const void*)(vb + 1024 * j + 16 * lane),
+                                           (lds_void*)(kd + St::kHalf + 1024 * j), 16, 0, 0);
+      };
+#pragma unroll
+      for (int j = 0; j < NB - 1; ++j) issue(j, j);
+      for (int i = 0; i < cnt; i += NB) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(kWait);
+          __builtin_amdgcn_sched_barrier(0);
+          issue(i + j + NB - 1, (j + NB - 1) % NB);
+          __builtin_amdgcn_sched_barrier(0);
+          if (j == 0 || i + j < cnt) {
+            const uint8_t* kd = stage(j);
+            DecFrags<D, U8> f;
+#pragma unroll
+            for (int h = 0; h < D / 64; ++h)
+              f.k[h] = *(const uint4*)(kd + St::k_slot(col, 4 * h + grp) * 16);
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t)
+              f.v[t] = *(const uint32_t*)(kd + St::kHalf + (16 * t + col) * 16 + 4 * grp);
+            compute(f, i + j);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // the last (unused) copies land before the merge reuses LDS
     }
-    __builtin_amdgcn_s_waitcnt(0);  // the last (unused) loads land before the registers go
+    __syncthreads();  // every wave is done with its stages before they take the accumulators
+  } else {
+    // bf16: fragments load straight into registers, three sets in rotation
+    // (one computing, two in flight)
+    constexpr int NSETS = 3;
+    constexpr int LOADS = D / 32 + D / 16;  // vector-memory operations per block
+    constexpr int kWaitIn = (NSETS - 2) * LOADS;  // blocks i+1 .. i+NSETS-2 may be in flight
+    constexpr int kWait = (kWaitIn & 15) | (7 << 4) | (15 << 8) | (((kWaitIn >> 4) & 3) << 14);
+    if (cnt > 0) {
+      auto phys_of = [&](int i) { return __shfl(my_phys, min(i, cnt - 1), 64); };
+      DecFrags<D, U8> f[NSETS];
+#pragma unroll
+      for (int j = 0; j < NSETS - 1; ++j) dec_load<D, U8>(f[j], a, phys_of(j), g, col, grp);
+      for (int i = 0; i < cnt; i += NSETS) {
+#pragma unroll
+        for (int j = 0; j < NSETS; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(kWait);
+          __builtin_amdgcn_sched_barrier(0);
+          dec_load<D, U8>(f[(j + NSETS - 1) % NSETS], a, phys_of(i + j + NSETS - 1), g, col, grp);
+          __builtin_amdgcn_sched_barrier(0);
+          if (j == 0 || i + j < cnt) compute(f[j], i + j);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // the last (unused) loads land before the registers go
+    }
   }
 
   // ---- merge the four waves: acc[t][r] = O^T[16t + 4grp + r][head col]
@@ -563,7 +673,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm_o[wave][16 * t + 4 * grp + r][col] = acc[t][r];
+    for (int r = 0; r < 4; ++r) o_tile(wave)[o_idx(16 * t + 4 * grp + r, col)] = acc[t][r];
   __syncthreads();
 
   float* pp = a.part + (((size_t)b * a.Hkv + g) * a.max_parts + p) * kPartStride(D);
@@ -577,7 +687,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float f = exp2f(sm_m[w][hh] - M);  // 0 for a wave with no blocks
-      O += sm_o[w][d][hh] * f;
+      O += o_tile(w)[o_idx(d, hh)] * f;
       L += sm_l[w][hh] * f;
     }
     if constexpr (U8) {
