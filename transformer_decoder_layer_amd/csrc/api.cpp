@@ -198,8 +198,8 @@ size_t decode_part_need(const tdl_layer_config& c, int max_batch) {
   size_t w = 0;
   const int max_blk = (c.max_position + 15) / 16;
   for (int b = 1; b <= max_batch; ++b)
-    for (int nb = 1; nb <= max_blk; ++nb)
-      w = std::max(w, decode_plan(b, c.n_q_heads, c.n_kv_heads, c.head_dim, nb * 16).part_floats);
+    for (int u8 = 0; u8 < 2; ++u8)
+      w = std::max(w, decode_plan(b, c.n_q_heads, c.n_kv_heads, c.head_dim, max_blk * 16, u8).part_floats_bound);
   return w;
 }
 
@@ -300,7 +300,7 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   const int H = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, I = c.intermediate;
   DecodePlan dp{};
   if (n_dec) {
-    dp = decode_plan(n_dec, Hq, Hkv, D, max_ctx_len);
+    dp = decode_plan(n_dec, Hq, Hkv, D, max_ctx_len, pool.u8 != 0);
     if (dp.part_floats > L->dec_part_floats)
       return fail(TDL_E_CAPACITY, "decode workspace too small (batch %d, max_ctx_len %d)", n_dec,
                   max_ctx_len);

@@ -346,10 +346,12 @@ constexpr int kPartStride(int D) { return 16 * D + 32; }
 
 template <int D, bool U8>
 struct DecFrags {
-  // K rows (A operand): key lane%16; bf16: channels 32s + 8*(lane/16) .. +7
-  // of product s; u8: 16 channels 64h + 16*(lane/16) .. +15 per load, the
-  // first 8 for product 2h, the last 8 for product 2h + 1 (dec_kchan)
-  typename std::conditional<U8, uint4, bf16x8>::type k[U8 ? D / 64 : D / 32];
+  // K rows (A operand): key lane%16, one 16-byte chunk per entry; bf16:
+  // channels 32s + 8*(lane/16) .. +7 of product s; u8: channels 64h +
+  // 16*(lane/16) .. +15, the first 8 for product 2h, the last 8 for product
+  // 2h + 1 (dec_kchan)
+  using KT = typename std::conditional<U8, uint4, bf16x8>::type;
+  KT k[U8 ? D / 64 : D / 32];
   // V^T rows (A operand): channel 16t + lane%16, keys 4*(lane/16) .. +3
   typename std::conditional<U8, uint32_t, bf16x4>::type v[D / 16];
 };
@@ -363,43 +365,46 @@ __device__ __forceinline__ int dec_kchan(int s, int grp) {
   return U8 ? 64 * (s >> 1) + 16 * grp + 8 * (s & 1) : 32 * s + 8 * grp;
 }
 
-// LDS staging of one u8 block-head: K (16 keys x D codes) then V^T (D
-// channels x 16 codes), 16-byte chunks.  K chunk c of key r sits at slot
-// r * CPR + (c ^ x(r)): the 8 lanes that read a 128-byte LDS row together
-// (same chunk, keys r..r+7) then hit 8 different bank quads.  Each copy
-// instruction still reads 1 KB of whole key rows.
-template <int D>
+// LDS staging of one block-head: K (16 keys x D elements), then for u8
+// V^T (D channels x 16 codes); bf16 V^T fragments load straight into
+// registers (each of their loads already reads whole cache lines).  16-byte
+// chunks; K chunk c of key r sits at slot r * CPR + (c ^ x(r)), so the 8
+// lanes that read a 128-byte LDS row together (same chunk, keys r..r+7) hit
+// 8 different bank quads, while each copy instruction still reads 1 KB of
+// whole key rows.
+template <int D, bool U8>
 struct DecStage {
-  static constexpr int kHalf = kBlockTokens * D;   // bytes of K (= of V)
-  static constexpr int kBytes = 2 * kHalf;
-  static constexpr int kInst = kHalf / 1024;       // copy instructions per half
-  static constexpr int CPR = D / 16;               // chunks per key row
-  __device__ static int x(int r) { return (r / (8 / CPR)) & (CPR - 1); }
+  static constexpr int kRow = D * (U8 ? 1 : 2);    // bytes per key row
+  static constexpr int kK = kBlockTokens * kRow;   // K bytes
+  static constexpr int kV = U8 ? kBlockTokens * D : 0;
+  static constexpr int kBytes = kK + kV;
+  static constexpr int kInstK = kK / 1024;         // copy instructions
+  static constexpr int kInstV = kV / 1024;
+  static constexpr int CPR = kRow / 16;            // chunks per key row
+  static_assert(CPR >= 4 && kK % 1024 == 0, "head dim");
+  __device__ static int x(int r) { return CPR >= 8 ? (r & 7) : ((r >> 1) & 3); }
   __device__ static int k_slot(int r, int c) { return r * CPR + (c ^ x(r)); }
   // source byte offset of the chunk that goes to slot s
   __device__ static int k_src(int s) {
     const int r = s / CPR;
-    return r * D + 16 * ((s % CPR) ^ x(r));
+    return r * kRow + 16 * ((s % CPR) ^ x(r));
   }
 };
-constexpr int kDecStages = 3;  // u8 blocks per wave in LDS (one read, two in flight)
+constexpr int kDecStages = 3;  // blocks per wave in rotation (one read, two in flight)
 template <int D, bool U8>
 constexpr int dec_stage_array_bytes() {
   constexpr int o = 2 * D * 16 * 4;  // two waves' O^T tiles
-  constexpr int st = U8 ? 4 * DecStage<D>::kBytes : 0;
+  constexpr int st = 4 * DecStage<D, U8>::kBytes;
   return o > st ? o : st;
 }
 
-// bf16 blocks: fragments straight from the pool into registers
+// bf16 V^T fragments straight from the pool into registers
 template <int D, bool U8>
-__device__ __forceinline__ void dec_load(DecFrags<D, U8>& f, const DecArgs& a, int phys, int g,
-                                         int col, int grp) {
-  static_assert(!U8, "u8 blocks are staged through LDS (DecStage)");
+__device__ __forceinline__ void dec_load_v(DecFrags<D, U8>& f, const DecArgs& a, int phys, int g,
+                                           int col, int grp) {
+  static_assert(!U8, "u8 blocks are staged through LDS whole");
   const size_t hb = ((size_t)phys * a.Hkv + g) * (kBlockTokens * D);
-  const bf16* kb = (const bf16*)a.pool.k + hb;
   const bf16* vb = (const bf16*)a.pool.v + hb;
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s) f.k[s] = *(const bf16x8*)(kb + col * D + 32 * s + 8 * grp);
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
     f.v[t] = *(const bf16x4*)(vb + (16 * t + col) * kBlockTokens + 4 * grp);
@@ -425,32 +430,31 @@ template <int D, bool U8>
 __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   constexpr int NT = D / 16;  // 16-channel tiles of the output
   __shared__ float sm_m[4][16], sm_l[4][16];
-  // u8: stage j of every wave's block rotation lives in its own array, so
+  // Stage j of every wave's block rotation lives in its own array, so
   // the compiler can tell a wave's reads of one stage from the copies still
   // landing in the others (one array would make every read wait for all
   // copies).  After the loop st0 / st1 hold the four waves' accumulators.
   constexpr int SZ = dec_stage_array_bytes<D, U8>();
   __shared__ __attribute__((aligned(16))) uint8_t st0[SZ];
   __shared__ __attribute__((aligned(16))) uint8_t st1[SZ];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[U8 ? SZ : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[SZ];
   // wave w's O^T tile [D][16] floats, columns XOR-swizzled by row
   auto o_tile = [&](int w) { return (float*)(w < 2 ? st0 : st1) + (w & 1) * D * 16; };
   auto o_idx = [](int d, int hh) { return d * 16 + (hh ^ (d & 15)); };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // partition index slowest: consecutive workgroups (which the dispatcher
+  // deals round-robin to the 8 XCDs) are different (sequence, KV head)
+  // pairs, so the first partitions -- the only ones short sequences have --
+  // spread over every XCD instead of piling onto those whose index
+  // matches a multiple of the partition count
+  const int g = blockIdx.x, b = blockIdx.y, p = blockIdx.z;
   const int sidx = a.first_seq + b;
   const int n_rep = a.Hq / a.Hkv;
-  const int ctx = seq_ctx(a.seq, sidx);
-  const int n_keys = ctx + 1;
-  const int n_blk = cdiv(n_keys, kBlockTokens);
-  const int n_parts = cdiv(n_blk, a.part_blocks);
-  if (p >= n_parts) return;
-  const int row = seq_row(a.seq, sidx);
-  const int blk0 = p * a.part_blocks;
-  const int blk1 = min(n_blk, blk0 + a.part_blocks);
   const int col = lane & 15, grp = lane >> 4;
   const bool head_ok = col < n_rep;
+  const int ctx = seq_ctx(a.seq, sidx);
+  const int row = seq_row(a.seq, sidx);
 
   // query fragments (B operand of S^T = K Q^T): q[head col][32s + 8grp .. +7],
   // carried as a bf16 pair hi + lo so the fp32 query keeps its precision
@@ -492,21 +496,35 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     }
   }
 
+  // the sequence's context is cut into n_parts partitions of (nearly) equal
+  // size, at most part_blocks blocks each
+  const int n_keys = ctx + 1;
+  const int n_blk = cdiv(n_keys, kBlockTokens);
+  const int n_parts = cdiv(n_blk, a.part_blocks);
+  if (p >= n_parts) return;
+  const int part_size = cdiv(n_blk, n_parts);
+  const int blk0 = p * part_size;
+  const int blk1 = min(n_blk, blk0 + part_size);
+
   const float sc = kLog2e * rsqrtf((float)D);
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // this wave's blocks: blk0 + wave + 4i; the table entries come in one load
+  // this wave's blocks: blk0 + wave + 4i, i < cnt <= 128; the table
+  // entries come in two loads (entry i in lane i % 64 of my_phys[i / 64])
   const int cnt = blk1 - blk0 > wave ? cdiv(blk1 - blk0 - wave, 4) : 0;
-  int my_phys = 0;
-  if (lane < cnt) my_phys = seq_block(a.seq, sidx, blk0 + wave + 4 * lane);
+  int my_phys[2] = {0, 0};
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (64 * h + lane < cnt) my_phys[h] = seq_block(a.seq, sidx, blk0 + wave + 4 * (64 * h + lane));
 
   auto compute = [&](const DecFrags<D, U8>& f, int i) {
     const int blk = blk0 + wave + 4 * i;
-    // S^T[key][head]: A = K rows (key = lane%16), B = Q^T (hi + lo)
-    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+    // S^T[key][head]: A = K rows (key = lane%16), B = Q^T (hi + lo, two
+    // independent accumulation chains)
+    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f}, st_lo = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       bf16x8 kf;
@@ -516,8 +534,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       }
       else kf = f.k[s];
       st = mfma16x16x32(kf, qf[s], st);
-      st = mfma16x16x32(kf, qlo[s], st);
+      st_lo = mfma16x16x32(kf, qlo[s], st_lo);
     }
+    st += st_lo;
     // lane holds S[head col][key 4grp + r]; only the sequence's last block
     // has unwritten slots (wave-uniform test)
     const int key0 = blk * kBlockTokens + 4 * grp;
@@ -581,34 +600,44 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   // and are never computed.  The explicit waits count this wave's
   // vector-memory operations in program order; the scheduling barriers keep
   // the compiler from moving loads or their uses across them.
-  if constexpr (U8) {
-    // u8: whole cache lines go straight to LDS (16 bytes per lane, 1 KB per
-    // instruction; kDecStages blocks per wave in rotation), fragments are
-    // read back from there.  Read in place as register fragments, a block
-    // would cost 3x the cache-line requests (each key row is 128 bytes, a
-    // fragment load takes 16-64 of them), which bounds this kernel.
-    using St = DecStage<D>;
+  {
+    // K (and u8 V) blocks go to LDS as whole cache lines (16 bytes per lane,
+    // 1 KB per instruction; kDecStages blocks per wave in rotation) and the
+    // fragments are read back from there.  Read in place as register
+    // fragments, K would cost 2-4x the cache-line requests (a fragment load
+    // takes 32-64 bytes of each of 16 key rows), and requests, not bytes,
+    // bound this kernel.
+    using St = DecStage<D, U8>;
     constexpr int NB = kDecStages;
-    constexpr int LOADS = 2 * St::kInst;
-    constexpr int kWaitIn = (NB - 2) * LOADS;
+    constexpr int LOADS = St::kInstK + (U8 ? St::kInstV : D / 16);
+    constexpr int kWaitIn = (NB - 2) * LOADS;  // blocks i+1 .. i+NB-2 may be in flight
     constexpr int kWait = (kWaitIn & 15) | (7 << 4) | (15 << 8) | (((kWaitIn >> 4) & 3) << 14);
     static_assert(NB == 3, "one LDS array per stage");
     auto stage = [&](int j) { return (j == 0 ? st0 : j == 1 ? st1 : st2) + wave * St::kBytes; };
+    DecFrags<D, U8> fv[U8 ? 1 : NB];  // bf16: V^T register sets in rotation
     if (cnt > 0) {
-      auto phys_of = [&](int i) { return __shfl(my_phys, min(i, cnt - 1), 64); };
+      auto phys_of = [&](int i) {
+        i = min(i, cnt - 1);  // wave-uniform
+        return __shfl(i < 64 ? my_phys[0] : my_phys[1], i & 63, 64);
+      };
       auto issue = [&](int i, int buf) {
-        const size_t hb = ((size_t)phys_of(i) * a.Hkv + g) * (kBlockTokens * D);
+        const int phys = phys_of(i);
+        const size_t hb = ((size_t)phys * a.Hkv + g) * (kBlockTokens * St::kRow);
         const uint8_t* kb = (const uint8_t*)a.pool.k + hb;
-        const uint8_t* vb = (const uint8_t*)a.pool.v + hb;
         uint8_t* kd = stage(buf);
 #pragma unroll
-        for (int j = 0; j < St::kInst; ++j)
+        for (int j = 0; j < St::kInstK; ++j)
           __builtin_amdgcn_global_load_lds((const void*)(kb + St::k_src(64 * j + lane)),
                                            (lds_void*)(kd + 1024 * j), 16, 0, 0);
+        if constexpr (U8) {
+          const uint8_t* vb = (const uint8_t*)a.pool.v + hb;
 #pragma unroll
-        for (int j = 0; j < St::kInst; ++j)
-          __builtin_amdgcn_global_load_lds((const void*)(vb + 1024 * j + 16 * lane),
-                                           (lds_void*)(kd + St::kHalf + 1024 * j), 16, 0, 0);
+          for (int j = 0; j < St::kInstV; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(vb + 1024 * j + 16 * lane),
+                                             (lds_void*)(kd + St::kK + 1024 * j), 16, 0, 0);
+        } else {
+          dec_load_v<D, U8>(fv[buf], a, phys, g, col, grp);
+        }
       };
 #pragma unroll
       for (int j = 0; j < NB - 1; ++j) issue(j, j);
@@ -624,43 +653,23 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
             const uint8_t* kd = stage(j);
             DecFrags<D, U8> f;
 #pragma unroll
-            for (int h = 0; h < D / 64; ++h)
-              f.k[h] = *(const uint4*)(kd + St::k_slot(col, 4 * h + grp) * 16);
+            for (int h = 0; h < St::kRow / 64; ++h)
+              f.k[h] = *(const typename DecFrags<D, U8>::KT*)(kd + St::k_slot(col, 4 * h + grp) * 16);
+            if constexpr (U8) {
 #pragma unroll
-            for (int t = 0; t < D / 16; ++t)
-              f.v[t] = *(const uint32_t*)(kd + St::kHalf + (16 * t + col) * 16 + 4 * grp);
+              for (int t = 0; t < D / 16; ++t)
+                f.v[t] = *(const uint32_t*)(kd + St::kK + (16 * t + col) * 16 + 4 * grp);
+            } else {
+#pragma unroll
+              for (int t = 0; t < D / 16; ++t) f.v[t] = fv[j].v[t];
+            }
             compute(f, i + j);
           }
         }
       }
-      __builtin_amdgcn_s_waitcnt(0);  // the last (unused) copies land before the merge reuses LDS
+      __builtin_amdgcn_s_waitcnt(0);  // the last (unused) copies land before LDS is reused
     }
     __syncthreads();  // every wave is done with its stages before they take the accumulators
-  } else {
-    // bf16: fragments load straight into registers, three sets in rotation
-    // (one computing, two in flight)
-    constexpr int NSETS = 3;
-    constexpr int LOADS = D / 32 + D / 16;  // vector-memory operations per block
-    constexpr int kWaitIn = (NSETS - 2) * LOADS;  // blocks i+1 .. i+NSETS-2 may be in flight
-    constexpr int kWait = (kWaitIn & 15) | (7 << 4) | (15 << 8) | (((kWaitIn >> 4) & 3) << 14);
-    if (cnt > 0) {
-      auto phys_of = [&](int i) { return __shfl(my_phys, min(i, cnt - 1), 64); };
-      DecFrags<D, U8> f[NSETS];
-#pragma unroll
-      for (int j = 0; j < NSETS - 1; ++j) dec_load<D, U8>(f[j], a, phys_of(j), g, col, grp);
-      for (int i = 0; i < cnt; i += NSETS) {
-#pragma unroll
-        for (int j = 0; j < NSETS; ++j) {
-          __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_s_waitcnt(kWait);
-          __builtin_amdgcn_sched_barrier(0);
-          dec_load<D, U8>(f[(j + NSETS - 1) % NSETS], a, phys_of(i + j + NSETS - 1), g, col, grp);
-          __builtin_amdgcn_sched_barrier(0);
-          if (j == 0 || i + j < cnt) compute(f[j], i + j);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0);  // the last (unused) loads land before the registers go
-    }
   }
 
   // ---- merge the four waves: acc[t][r] = O^T[16t + 4grp + r][head col]
@@ -711,6 +720,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 // exp2(m_p - M) / L come first (LDS), then every output element sums its
 // partitions with independent loads.
 constexpr int kMaxDecodeParts = 256;
+constexpr int kMaxPartBlocks = 512;  // two block-table entries per lane and wave
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_merge_kernel(DecArgs a) {
@@ -783,30 +793,38 @@ hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, int n_prefill, 
   return hipErrorInvalidValue;
 }
 
-DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len) {
+DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len, bool u8) {
   (void)Hq;
   DecodePlan pl{};
   const int max_blk = cdiv(max_ctx_len, kBlockTokens);
-  // the longest partitions that still give ~2 workgroups per CU (each
-  // workgroup pays a fixed cost -- query conversion, filling the load
-  // pipeline, the four-wave merge and the partial write -- which measured as
-  // large as the streaming itself for 4-8 blocks per wave): up to 256 blocks
-  // (64 per wave), down to 4 for short batches
-  int pb = 256;
-  while (pb > 4 && (long)batch * Hkv * cdiv(max_blk, pb) < 512) pb /= 2;
-  while (cdiv(max_blk, pb) > kMaxDecodeParts) pb *= 2;  // the merge kernel's LDS bound
+  // Parts per sequence (for the longest one; each sequence is cut into
+  // near-equal parts of at most part_blocks blocks).  Measured on ragged
+  // batches: enough (sequence, KV head) pairs x parts for one workgroup per
+  // CU, and no part above ~2 MB of cache (257 bf16 / 171 u8 blocks of a
+  // 128-wide head; u8 blocks cost more compute per byte); more, shorter
+  // parts only add workgroup start-up, partial writes and the merge.
+  const int pairs = batch * Hkv;
+  const int cap = std::min(kMaxPartBlocks, (u8 ? 171 : 257) * 128 / D);
+  int parts = std::max(cdiv(256, pairs), cdiv(max_blk, cap));
+  parts = std::max(1, std::min(parts, max_blk));
+  int pb = cdiv(max_blk, parts);
+  while (cdiv(max_blk, pb) > kMaxDecodeParts) ++pb;  // the merge kernel's LDS bound
   pl.part_blocks = pb;
   pl.max_parts = cdiv(max_blk, pb);
-  pl.part_floats = (size_t)batch * Hkv * pl.max_parts * kPartStride(D);
+  pl.part_floats = pl.max_parts > 1 ? (size_t)batch * Hkv * pl.max_parts * kPartStride(D) : 0;
+  // parts never falls as max_ctx_len grows and max_parts <= parts: this
+  // bounds part_floats for every shorter context at this batch size
+  pl.part_floats_bound = (size_t)batch * Hkv * parts * kPartStride(D);
   return pl;
 }
 
 hipError_t attn_decode(const DecodePlan& pl, const void* q, KvPool pool, SeqInfo seq, int first_seq,
                        int batch, int Hq, int Hkv, int D, void* o, float* part, hipStream_t s) {
   if (batch == 0) return hipSuccess;
+  if (pl.part_blocks > kMaxPartBlocks) return hipErrorInvalidValue;
   DecArgs a{(const float*)q, pool, seq, first_seq, Hq, Hkv, pl.part_blocks, pl.max_parts, part,
             (f16*)o};
-  dim3 grid(pl.max_parts, Hkv, batch);
+  dim3 grid(Hkv, batch, pl.max_parts);
   if (D == 128) {
     if (pool.u8) attn_decode_kernel<128, true><<<grid, 256, 0, s>>>(a);
     else attn_decode_kernel<128, false><<<grid, 256, 0, s>>>(a);

@@ -179,9 +179,10 @@ constexpr int kMaxDecodePosition = 131072;  // longest context (keys) per sequen
 struct DecodePlan {
   int part_blocks;
   int max_parts;
-  size_t part_floats;
+  size_t part_floats;        // partial-result workspace of this launch
+  size_t part_floats_bound;  // >= part_floats of any max_ctx_len up to this one
 };
-DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len);
+DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len, bool u8);
 hipError_t attn_decode(const DecodePlan& plan, const void* q, KvPool pool, SeqInfo seq,
                        int first_seq, int batch, int Hq, int Hkv, int D, void* o, float* part,
                        hipStream_t s);
