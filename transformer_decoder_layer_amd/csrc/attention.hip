@@ -22,9 +22,10 @@
 // Decode: a workgroup owns (sequence, KV head, context partition); its four
 // waves walk the partition's blocks through the block table, one 16-token
 // block per step, with the whole query-head group packed into the 16 columns
-// of one MFMA tile.  u8 caches are dequantised in registers: codes convert
-// exactly to bf16; the K scale is folded into q and the zero point into a
-// per-head constant, the V scale and zero point are applied once at the end.
+// of one MFMA tile.  u8 caches are dequantised in registers: a code c
+// becomes the fp16 value 1024 + c exactly (one byte permute per two codes);
+// the K scale is folded into q and the zero point and bias into a per-head
+// constant, the V scale, zero point and bias are applied once at the end.
 // A second kernel merges the partitions' (m, l, acc) triples of each
 // (sequence, KV head) in partition order.
 
@@ -410,20 +411,23 @@ __device__ __forceinline__ void dec_load_v(DecFrags<D, U8>& f, const DecArgs& a,
     f.v[t] = *(const bf16x4*)(vb + (16 * t + col) * kBlockTokens + 4 * grp);
 }
 
-__device__ __forceinline__ bf16x8 u8x8_to_bf16(uint2 w) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = (bf16)(float)((w.x >> (8 * e)) & 0xff);
-    r[4 + e] = (bf16)(float)((w.y >> (8 * e)) & 0xff);
-  }
-  return r;
+// u8 codes as fp16 operands: the fp16 value with bit pattern 0x6400 | c is
+// exactly 1024 + c for a code c in 0..255 (unit spacing in [1024, 2048)), so
+// one byte permute turns two codes into two biased fp16 values; the bias
+// 1024 goes into the zero points.
+constexpr float kU8Bias = 1024.f;
+__device__ __forceinline__ uint32_t u8x2_biased(uint32_t w, uint32_t sel) {
+  return __builtin_amdgcn_perm(0x64646464u, w, sel);  // selectors 4..7: the 0x64 bytes
 }
-__device__ __forceinline__ bf16x4 u8x4_to_bf16(uint32_t w) {
-  bf16x4 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = (bf16)(float)((w >> (8 * e)) & 0xff);
-  return r;
+__device__ __forceinline__ f16x8 u8x8_to_f16_biased(uint32_t w0, uint32_t w1) {
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4v;
+  const u32x4v r = {u8x2_biased(w0, 0x04010400u), u8x2_biased(w0, 0x04030402u),
+                    u8x2_biased(w1, 0x04010400u), u8x2_biased(w1, 0x04030402u)};
+  return __builtin_bit_cast(f16x8, r);
+}
+__device__ __forceinline__ f16x4 u8x4_to_f16_biased(uint32_t w) {
+  const u32x2 r = {u8x2_biased(w, 0x04010400u), u8x2_biased(w, 0x04030402u)};
+  return __builtin_bit_cast(f16x4, r);
 }
 
 template <int D, bool U8>
@@ -456,36 +460,65 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   const int ctx = seq_ctx(a.seq, sidx);
   const int row = seq_row(a.seq, sidx);
 
-  // query fragments (B operand of S^T = K Q^T): q[head col][32s + 8grp .. +7],
-  // carried as a bf16 pair hi + lo so the fp32 query keeps its precision
-  // (MFMA time is free here: the kernel is bound by HBM).  u8: q' = q *
-  // k_scale folds the K scale in; the zero point enters through
-  // corr = sum_d q'[d] * zp[d] in fp32.
-  bf16x8 qf[D / 32];
-  bf16x8 qlo[D / 32];
+  // query fragments (B operand of S^T = K Q^T): q[head col][channels of
+  // dec_kchan], carried as a pair hi + lo so the fp32 query keeps its
+  // precision (MFMA time is free here).  bf16 cache: bf16 pairs.  u8 cache:
+  // fp16 pairs of q' = q * k_scale * 2^e (the K scale folded in, 2^e puts
+  // the head's largest |q'| in [128, 256) and comes back out through the
+  // score scale); the codes enter as 1024 + c, so the zero point and bias
+  // enter through corr = sum_d q'[d] * (1024 + zp[d]) in fp32.
+  using QT = typename std::conditional<U8, f16x8, bf16x8>::type;
+  using PT = typename std::conditional<U8, f16x4, bf16x4>::type;
+  QT qf[D / 32];
+  QT qlo[D / 32];
   float corr = 0.f;
+  float sc = kLog2e * rsqrtf((float)D);
   {
     const float* qp = a.q + ((size_t)row * a.Hq + g * n_rep + col) * D;
+    float qv[D / 32][8];
+    float amax = 0.f;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[s][e] = 0.f;
       if (head_ok) {
         const float* qs = qp + dec_kchan<U8>(s, grp);
         const float4 x0 = *(const float4*)qs, x1 = *(const float4*)(qs + 4);
-        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+        qv[s][0] = x0.x; qv[s][1] = x0.y; qv[s][2] = x0.z; qv[s][3] = x0.w;
+        qv[s][4] = x1.x; qv[s][5] = x1.y; qv[s][6] = x1.z; qv[s][7] = x1.w;
       }
-      bf16x8 hi, lo;
+      if constexpr (U8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qv[s][e] *= a.pool.k_scale[g * D + dec_kchan<U8>(s, grp) + e];
+          amax = fmaxf(amax, fabsf(qv[s][e]));
+        }
+      }
+    }
+    float qscale = 1.f;
+    if constexpr (U8) {
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      int ex = 0;
+      frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1); ex = 0 for amax 0
+      const int sh = min(100, max(-100, 8 - ex));
+      qscale = ldexpf(1.f, sh);
+      sc = ldexpf(sc, -sh);
+    }
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      QT hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float qs = v[e];
+        const float qs = qv[s][e] * qscale;
         if constexpr (U8) {
-          const int ch = g * D + dec_kchan<U8>(s, grp) + e;
-          qs *= a.pool.k_scale[ch];
-          corr += qs * (float)a.pool.k_zp[ch];
+          corr += qs * (kU8Bias + (float)a.pool.k_zp[g * D + dec_kchan<U8>(s, grp) + e]);
+          hi[e] = (_Float16)qs;
+          lo[e] = (_Float16)(qs - (float)hi[e]);
+        } else {
+          hi[e] = f32_to_bf16(qs);
+          lo[e] = f32_to_bf16(qs - (float)hi[e]);
         }
-        hi[e] = f32_to_bf16(qs);
-        lo[e] = f32_to_bf16(qs - (float)hi[e]);
       }
       qf[s] = hi;
       qlo[s] = lo;
@@ -506,7 +539,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   const int blk0 = p * part_size;
   const int blk1 = min(n_blk, blk0 + part_size);
 
-  const float sc = kLog2e * rsqrtf((float)D);
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -527,12 +559,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f}, st_lo = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      bf16x8 kf;
+      QT kf;
       if constexpr (U8) {
         const uint4 w = f.k[s >> 1];
-        kf = u8x8_to_bf16((s & 1) ? uint2{w.z, w.w} : uint2{w.x, w.y});
+        kf = (s & 1) ? u8x8_to_f16_biased(w.z, w.w) : u8x8_to_f16_biased(w.x, w.y);
+      } else {
+        kf = f.k[s];
       }
-      else kf = f.k[s];
       st = mfma16x16x32(kf, qf[s], st);
       st_lo = mfma16x16x32(kf, qlo[s], st_lo);
     }
@@ -560,7 +593,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
     // the reference point of the exponentials moves (and the accumulators
     // are rescaled) only when a block's maximum exceeds it by more than
-    // kLazy: P <= 2^kLazy keeps its hi + lo bf16 pair exact enough, softmax
+    // kLazy: P <= 2^kLazy keeps its hi + lo pair exact enough, softmax
     // does not depend on the reference point
     if (__builtin_amdgcn_ballot_w64(mb > m_run + kLazy) != 0) {
       const float m_new = fmaxf(m_run, mb);
@@ -570,26 +603,35 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] *= alpha;
     }
-    // P as a bf16 pair hi + lo: the weights keep fp32 precision
-    bf16x4 pf, pl;
+    // P as a pair hi + lo (bf16 or fp16, the operand type of V): the
+    // weights keep fp32 precision
+    PT pf, pl;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float pv = exp2f(sv[r] - m_run);
-      pf[r] = f32_to_bf16(pv);
-      pl[r] = f32_to_bf16(pv - (float)pf[r]);
+      if constexpr (U8) {
+        pf[r] = (_Float16)pv;
+        pl[r] = (_Float16)(pv - (float)pf[r]);
+      } else {
+        pf[r] = f32_to_bf16(pv);
+        pl[r] = f32_to_bf16(pv - (float)pf[r]);
+      }
       psum += pv;
     }
     l_run += psum;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      bf16x4 vf;
-      if constexpr (U8) vf = u8x4_to_bf16(f.v[t]);
-      else vf = f.v[t];
-      if (partial) {  // unwritten slots of the last block: zero V
+      PT vf;
+      if constexpr (U8) {
+        vf = u8x4_to_f16_biased(f.v[t]);  // finite, so P = 0 cancels unwritten slots
+      } else {
+        vf = f.v[t];
+        if (partial) {  // unwritten slots of the last block may hold any bits: zero V
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (key0 + r >= n_keys) vf[r] = (bf16)0.f;
+          for (int r = 0; r < 4; ++r)
+            if (key0 + r >= n_keys) vf[r] = (bf16)0.f;
+        }
       }
       acc[t] = mfma16x16x16(vf, pf, acc[t]);
       acc[t] = mfma16x16x16(vf, pl, acc[t]);
@@ -701,7 +743,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     }
     if constexpr (U8) {
       const int ch = g * D + d;
-      O = a.pool.v_scale[ch] * (O - (float)a.pool.v_zp[ch] * L);
+      O = a.pool.v_scale[ch] * (O - (kU8Bias + (float)a.pool.v_zp[ch]) * L);
     }
     if (n_parts == 1) {
       a.o[(size_t)row * a.Hq * D + (size_t)(g * n_rep + hh) * D + d] = to_f16(O / L);
