@@ -380,16 +380,18 @@ bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl) {
   const int KS = cdiv(K / 32, 2);
   const double wb = q80 ? 1.0625 : 2.0;  // weight bytes per element (Q8_0: + fp16 scale per 32)
   const double total = (double)N * K * wb;
-  // 128 rows of A (MT 8): each weight byte costs twice the MFMA and LDS
-  // work, so a live row wave streams slower (measured on the Qwen3-8B
-  // shapes: ~2.7 GB/s against ~4 at 64 rows), spare row waves, which repeat
-  // that work, slow the live ones (rate x live/RW), and 4-wave workgroups
-  // (two per CU, each loading the A chunk) lose to 8-wave ones
+  // Spare row waves (a range shorter than RW), which repeat a live wave's
+  // loads and MFMAs, slow the live ones: rate x live/RW.  4-wave
+  // workgroups (two per CU, each loading its own A chunks) measured slower
+  // than 8-wave ones on every decode shape.  128 rows of A (MT 8): each
+  // weight byte costs twice the MFMA and LDS work, so a live row wave
+  // streams slower (measured on the Qwen3-8B shapes: ~2.7 GB/s against ~4
+  // at 64 rows).
   const bool big = MT == 8;
   const double wave_lat = big ? 2.3e-6 : 1.5e-6;
   double best = 1e300;
   for (int RW : kStreamRW) {
-    if (big && RW < 8) continue;
+    if (RW < 8 && units > 16) continue;  // (tiny N: too few row groups for 8 waves)
     const int per = RW / PG;  // units per range at most
     const int rmin = cdiv(units, per);
     for (int s = 1; s <= 16; ++s) {
@@ -403,7 +405,7 @@ bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl) {
         const int groups = cdiv(units, R) * PG;          // live row waves of the largest range
         const double wg_bytes = (double)groups * 16 * kps * 64 * wb;
         double rate = std::min(22e9, wg_per_cu * groups * (kStreamNS - 1) * 2048.0 / wave_lat);
-        if (big) rate *= (double)groups / RW;
+        rate *= (double)groups / RW;
         double t = std::max(wg_per_cu * wg_bytes / rate, total / 5.5e12);
         if (sp > 1) t += 2.0 * sp * (double)M * N * 4.0 / 5.0e12;
         t += 1e-9 * RW;  // ties: fewer waves
