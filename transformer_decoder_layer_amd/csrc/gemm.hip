@@ -744,10 +744,11 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
     if ((cfg == 3 || cfg == 4) && M > 128) continue;  // the decode shapes only
     if (cfg == 3 && M > 64) continue;
     const int tiles = cdiv(M, c.BM) * cdiv(N, c.BN);
-    for (int splits = 1; splits <= 16; splits *= 2) {
+    for (int splits = 1; splits <= 16; ++splits) {
       if (splits > 1 && KT / splits < 4) break;
       const int kps = cdiv(KT, splits);
       const int sp = cdiv(KT, kps);
+      if (sp != splits) continue;  // the same plan as a smaller count
       const int wgs = tiles * sp;
       const double rounds = std::ceil((double)wgs / kCUs);
       double cost = rounds * (double)c.BM * c.BN * kps / c.eff;
