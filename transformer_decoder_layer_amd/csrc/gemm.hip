@@ -638,11 +638,13 @@ struct Cfg {
 // 64x112: N = 3584 splits into 16 tiles);  cfg 2: 128x128 (2x2 waves of
 // 64x64);  cfg 3: 64x128 (1x4 waves of 64x32) and cfg 4: 128x128 (1x4 waves
 // of 128x32) for decode-sized M;  cfg 5: 256x288 (4x2 waves of 64x144: N =
-// 4608 splits into 16 tiles, so 4096 rows make one tile per CU).  Eight-wave
-// tiles keep two waves per SIMD.
-constexpr int kNumCfgs = 6;
+// 4608 splits into 16 tiles, so 4096 rows make one tile per CU);  cfg 6:
+// 192x256 (2x4 waves of 96x64: 2112 = 11 x 192 rows without a mostly empty
+// last row of tiles).  Eight-wave tiles keep two waves per SIMD.
+constexpr int kNumCfgs = 7;
 constexpr Cfg kCfgs[kNumCfgs] = {{256, 256, 1.0f}, {256, 224, 0.96f}, {128, 128, 0.4f},
-                                 {64, 128, 0.35f},  {128, 128, 0.5f},  {256, 288, 0.98f}};
+                                 {64, 128, 0.35f},  {128, 128, 0.5f},  {256, 288, 0.98f},
+                                 {192, 256, 0.78f}};
 
 template <bool Q80, int EPI, typename T, bool DIRECT>
 hipError_t launch_cfg2(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
@@ -662,6 +664,10 @@ hipError_t launch_cfg2(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
     case 5:
       if constexpr (!Q80 && EPI != EPI_SILU_GATE)
         gemm_kernel<256, 288, 4, 2, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
+      else return hipErrorInvalidValue;
+      break;
+    case 6:
+      if constexpr (!Q80) gemm_kernel<192, 256, 2, 4, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
       else return hipErrorInvalidValue;
       break;
     case 3:
@@ -710,6 +716,7 @@ hipError_t tail_reduce(const GemmPlan& pl, const GemmArgs& a, int epi, hipStream
   }
   TDL_TAIL_CASE(0, 256, 256, 2, 4)
   TDL_TAIL_CASE(2, 128, 128, 2, 2)
+  TDL_TAIL_CASE(6, 192, 256, 2, 4)
 #undef TDL_TAIL_CASE
   if (pl.cfg == 1 && epi == EPI_BIAS_F32) {
     tail_reduce_kernel<256, 224, 4, 2, EPI_BIAS_F32><<<dim3(8, tail), 64, 0, s>>>(a);
@@ -740,7 +747,7 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
     const Cfg c = kCfgs[cfg];
     if (cfg == 1 && (epi == EPI_SILU_GATE || N % 224 != 0)) continue;
     if (cfg == 5 && (epi == EPI_SILU_GATE || N % 288 != 0)) continue;
-    if (q80 && (cfg <= 1 || cfg == 5)) continue;  // Q8_0 staging needs the register path
+    if (q80 && (cfg <= 1 || cfg >= 5)) continue;  // Q8_0 staging needs the register path
     if ((cfg == 3 || cfg == 4) && M > 128) continue;  // the decode shapes only
     if (cfg == 3 && M > 64) continue;
     const int tiles = cdiv(M, c.BM) * cdiv(N, c.BN);
