@@ -59,3 +59,14 @@ def test_qwen3_q80_mixed_sampled():
     rows = [0, 1, 700, 2046, 2047, 2048, 2049, 2100, 2111]
     seqs = [0, 1, 2, 53, 64]
     _check(inp, seqs, rows_out=rows, what="qwen3 q8_0 mixed")
+
+
+def test_qwen25_decode_b64_longest_partition():
+    # one sequence at ctx 4096 (4097 keys = 257 blocks) with 64 x 4 (sequence,
+    # KV head) pairs: a single 257-block partition, so one wave walks 65
+    # blocks and takes its last block-table entry from the second table load
+    wl = synth.WORKLOADS["qwen25_decode_b64"]
+    ctx = [int(c) for c in synth.context_lengths(np.random.default_rng(7), wl)]
+    ctx[5], ctx[40] = 4096, 4095
+    inp = synth.make_inputs(wl, seed=8, decode_ctx=ctx)
+    _check(inp, [0, 5, 40, 63], what="qwen2.5 decode b64, ctx 4096")
