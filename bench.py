@@ -127,8 +127,9 @@ def attention_flops(D, Hq, n_pairs):
 def other_workloads(args, torch, synth, tdl, stream, layer512):
     """The other configurations of the layer, measured the same way (synthetic
     inputs, resident in HBM): the 512-token prefill of the same Qwen2.5-7B
-    layer, the Qwen3-8B decode over a u8 cache (batch 128), and the Qwen3-8B
-    Q8_0 mixed step (a 2048-token chunk + 64 decode rows)."""
+    layer, the Qwen3-8B decode over a u8 cache (batch 128), the Qwen3-8B
+    Q8_0 mixed step (a 2048-token chunk + 64 decode rows), and a 28-layer
+    stack of the Qwen2.5-7B layer decoding batch 64."""
     out = {}
     n_steps = max(5, args.steps)
     # ---- Qwen2.5-7B prefill of 512 tokens
@@ -245,6 +246,64 @@ def other_workloads(args, torch, synth, tdl, stream, layer512):
     log(f"q8_0 mixed: {ms * 1e3:.1f} us/step")
     layer.close()
     kv.close()
+    del x, y, kv, tab
+
+    # ---- a 28-layer stack of Qwen2.5-7B-shaped layers (each with its own
+    # weights and bf16 cache), decode batch 64: one token of every sequence
+    # through every layer per step, eager and as a replayed HIP graph
+    wl = synth.WORKLOADS["qwen25_decode_b64"]
+    shape = wl.shape
+    Hkv, D, H = shape.n_kv_heads, shape.head_dim, shape.hidden
+    B, n_layers = wl.decode_batch, 28
+    ctx = synth.context_lengths(np.random.default_rng(50), wl)
+    totals = (ctx + 1).tolist()
+    nb = int(sum(math.ceil(t / 16) for t in totals))
+    tab = torch.from_numpy(synth.random_tables(np.random.default_rng(51), totals, n_blocks=nb)).cuda()
+    n_cached = int(ctx.sum())
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)).cuda()
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    log(f"stack of {n_layers} layers: weights and caches")
+    layers, kvs = [], []
+    for l in range(n_layers):
+        layers.append(tdl.Layer(tdl.make_config(shape, max_tokens=B, max_seqs=B, max_position=4224),
+                                synth.torch_weights(shape, seed=500 + l)))
+        kv = tdl.KvCache(nb, Hkv, D, "bf16")
+        kv.write(cu, zero, tab, synth.torch_normal((n_cached, Hkv, D), seed=600 + l, dtype=torch.bfloat16),
+                 synth.torch_normal((n_cached, Hkv, D), seed=700 + l, dtype=torch.bfloat16))
+        kvs.append(kv)
+    stack = tdl.Stack(layers)
+    ctx_d = torch.from_numpy(ctx).cuda()
+    x = synth.torch_normal((B, H), seed=52, dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    max_ctx = int(ctx.max()) + 1
+    step = lambda: stack.decode_paged(x, y, ctx_d, tab, max_ctx, kvs)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    us = 1e3 * float(np.median(timed_steps(torch, stream, step, n_steps, flush, sink)))
+    y_eager = y.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    us_graph = 1e3 * float(np.median(timed_steps(torch, stream, graph.replay, n_steps, flush, sink)))
+    assert torch.equal(y, y_eager), "graph replay of the stack differs from the eager step"
+    assert torch.isfinite(y.float()).all(), "non-finite stack output"
+    del graph
+    step_bytes = n_layers * (weight_bytes(shape) + int(sum(totals)) * Hkv * D * 2 * 2) + 2 * B * H * 2
+    out["qwen25_stack28_decode_b64"] = {
+        "workload": "28 qwen2.5-7b-shaped layers (own weights and bf16 paged cache each), decode batch 64, "
+                    "ctx U[128,4096], random block permutation: one token per sequence through the stack",
+        "us_per_step": round(us, 1), "tokens_per_s": round(B / (us * 1e-6), 1),
+        "graph_us_per_step": round(us_graph, 1), "algorithmic_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(step_bytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}}
+    log(f"stack of {n_layers}: {us:.1f} us/step eager, {us_graph:.1f} us/step graph")
+    stack.close()
+    for l in layers:
+        l.close()
+    for k in kvs:
+        k.close()
     del flush
     return out
 

@@ -69,6 +69,7 @@ typedef enum {
 typedef void* tdl_stream; /* hipStream_t */
 typedef struct tdl_layer tdl_layer;
 typedef struct tdl_kv_cache tdl_kv_cache;
+typedef struct tdl_stack tdl_stack;
 
 /* Layer hyper-parameters ([TFF] 3.5 graph context: heads, kv heads, head
  * size, rope base, rms eps; [QWEN] "运行结果" config line). */
@@ -245,6 +246,33 @@ typedef struct {
 
 tdl_status layer_profile_enable(tdl_layer* layer, int enable);
 tdl_status layer_profile_read(tdl_layer* layer, tdl_profile* out);
+
+/* ---------------------------------------------------------------- stack */
+
+/* A stack of layers applied in order, as one decode step of a whole model
+ * ([TFF] 3.6.1: the runtime's decode loop runs every layer per generated
+ * token; 3.6.2: a captured graph replays such a step).  The layers stay
+ * caller-owned and must outlive the stack; they must share `hidden`.  The
+ * stack owns two bf16 activation buffers of min(max_seqs, max_tokens) rows
+ * (over its layers) x hidden, allocated here.  *out is NULL on failure. */
+tdl_status stack_create(tdl_layer* const* layers, int32_t n_layers, tdl_stack** out);
+
+/* Frees the activation buffers (not the layers).  Work still queued on a
+ * stream that uses the stack must have finished.  NULL is accepted. */
+tdl_status stack_destroy(tdl_stack* stack);
+
+/* One decode step through every layer: layer 0 reads x, layer i>0 reads
+ * layer i-1's output, the last layer writes y (x, y [batch, hidden] bf16;
+ * y must not alias x).  kvs[i] (n_layers handles) is layer i's cache; all
+ * caches use the same block_tables and ctx_lens (the same sequences), with
+ * the arguments of layer_decode_paged.  Every layer's arguments are checked
+ * before the first layer is enqueued; a failure there enqueues nothing.  No
+ * allocation and, unless TDL_DEBUG=1, no synchronisation: a graph capture
+ * records the whole step. */
+tdl_status stack_decode_paged(tdl_stack* stack, tdl_stream stream, const void* x, void* y,
+                              int32_t batch, const int32_t* ctx_lens,
+                              const int32_t* block_tables, int32_t max_blocks,
+                              int32_t max_ctx_len, tdl_kv_cache* const* kvs);
 
 /* ------------------------------------------------------------- KV cache */
 

@@ -78,6 +78,18 @@ def test_null_handles_are_invalid():
     assert tdl._kv_free(None) == tdl.TDL_OK
 
 
+def test_stack_argument_checks():
+    import transformer_decoder_layer_amd as tdl
+    h = ctypes.c_void_p(123)
+    assert tdl._stack_create(None, 2, ctypes.byref(h)) == tdl.TDL_E_INVALID
+    assert not h.value                           # *out cleared on failure
+    null_layers = (ctypes.c_void_p * 2)(None, None)
+    assert tdl._stack_create(null_layers, 2, ctypes.byref(h)) == tdl.TDL_E_INVALID
+    assert tdl._stack_create(null_layers, 0, ctypes.byref(h)) == tdl.TDL_E_INVALID
+    assert tdl._stack_decode(None, None, 1, 2, 4, 3, 5, 1, 16, None) == tdl.TDL_E_INVALID
+    assert tdl._stack_destroy(None) == tdl.TDL_OK
+
+
 def test_kv_cache_bytes():
     import transformer_decoder_layer_amd as tdl
     c = tdl.KvConfig(100, 16, 4, 128, tdl.TDL_BF16, 0)

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Dict, Optional, Sequence
+from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
@@ -29,7 +29,8 @@ c_i32, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctyp
 P_i32 = ctypes.POINTER(ctypes.c_int32)
 
 EXPORTS = ["layer_create", "layer_destroy", "layer_prefill", "layer_decode_paged", "layer_step",
-           "layer_workspace_view", "layer_profile_enable", "layer_profile_read", "kv_cache_bytes", "kv_cache_alloc", "kv_cache_free",
+           "layer_workspace_view", "layer_profile_enable", "layer_profile_read", "stack_create",
+           "stack_destroy", "stack_decode_paged", "kv_cache_bytes", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_view", "kv_block_table", "kv_block_release", "kv_free_blocks",
            "kv_cache_calibrate", "kv_cache_write", "tdl_status_string", "tdl_last_error"]
 
@@ -107,6 +108,10 @@ _kv_free_blocks = _sig("kv_free_blocks", c_i32, c_vp)
 _kv_calibrate = _sig("kv_cache_calibrate", c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_int64)
 _kv_write = _sig("kv_cache_write", c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp,
                  c_vp, c_i32)
+_stack_create = _sig("stack_create", c_i32, ctypes.POINTER(c_vp), c_i32, ctypes.POINTER(c_vp))
+_stack_destroy = _sig("stack_destroy", c_i32, c_vp)
+_stack_decode = _sig("stack_decode_paged", c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32,
+                     c_i32, ctypes.POINTER(c_vp))
 _status_string = _sig("tdl_status_string", ctypes.c_char_p, c_i32)
 _last_error = _sig("tdl_last_error", ctypes.c_char_p)
 
@@ -321,6 +326,36 @@ class Layer:
         v = WorkspaceView()
         _check("layer_workspace_view", _layer_ws(self._h, ctypes.byref(v)))
         return v
+
+
+class Stack:
+    """Layers applied in order as one decode step (stack_decode_paged).  The
+    layers (and their caches) must outlive the stack."""
+
+    def __init__(self, layers: List[Layer]):
+        hs = (c_vp * len(layers))(*[l._h.value for l in layers])
+        h = c_vp()
+        _check("stack_create", _stack_create(hs, len(layers), ctypes.byref(h)))
+        self._h = h
+        self.layers = list(layers)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _stack_destroy(self._h)
+            self._h = c_vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def decode_paged(self, x, y, ctx_lens, block_tables, max_ctx_len: int, kvs: List[KvCache],
+                     stream=None):
+        ks = (c_vp * len(kvs))(*[k.handle.value if k is not None else None for k in kvs])
+        _check("stack_decode_paged", _stack_decode(self._h, _stream(stream), _ptr(x), _ptr(y), x.shape[0],
+                                                   _ptr(ctx_lens), _ptr(block_tables),
+                                                   block_tables.shape[1], max_ctx_len, ks))
 
 
 def device_tensor(ptr: int, shape, dtype):

@@ -17,6 +17,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <limits>
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -638,10 +640,10 @@ extern "C" tdl_status layer_prefill(tdl_layer* L, tdl_stream stream, const void*
   return run_layer(L, st, x, y, n_tokens, seq, pool_of(L, kv), 1, n_tokens, 0, 0, 0);
 }
 
-extern "C" tdl_status layer_decode_paged(tdl_layer* L, tdl_stream stream, const void* x, void* y,
-                                         int32_t batch, const int32_t* ctx_lens,
-                                         const int32_t* block_tables, int32_t max_blocks,
-                                         int32_t max_ctx_len, tdl_kv_cache* kv) {
+// Host-side checks of a decode step (nothing is enqueued).
+tdl_status check_decode(const tdl_layer* L, const void* x, const void* y, int32_t batch,
+                        const int32_t* ctx_lens, const int32_t* block_tables, int32_t max_blocks,
+                        int32_t max_ctx_len, const tdl_kv_cache* kv) {
   if (!L) return fail(TDL_E_INVALID, "layer is NULL");
   if (!x || !y || !ctx_lens || !block_tables || !kv)
     return fail(TDL_E_INVALID, "x, y, ctx_lens, block_tables and kv are required");
@@ -656,8 +658,12 @@ extern "C" tdl_status layer_decode_paged(tdl_layer* L, tdl_stream stream, const 
   if (max_ctx_len > L->cfg.max_position)
     return fail(TDL_E_CAPACITY, "max_ctx_len %d exceeds max_position %d", max_ctx_len,
                 L->cfg.max_position);
-  TRY(check_kv_matches(L, kv));
-  hipStream_t st = (hipStream_t)stream;
+  return check_kv_matches(L, kv);
+}
+
+tdl_status enqueue_decode(tdl_layer* L, hipStream_t st, const void* x, void* y, int32_t batch,
+                          const int32_t* ctx_lens, const int32_t* block_tables, int32_t max_blocks,
+                          int32_t max_ctx_len, tdl_kv_cache* kv) {
   if (debug_checks())
     TRY(debug_check_tables(ctx_lens, nullptr, batch, 1, block_tables, max_blocks, kv->cfg.n_blocks,
                            max_ctx_len, st));
@@ -668,6 +674,87 @@ extern "C" tdl_status layer_decode_paged(tdl_layer* L, tdl_stream stream, const 
   seq.max_blocks = max_blocks;
   seq.rows_are_seqs = 1;
   return run_layer(L, st, x, y, batch, seq, pool_of(L, kv), 0, 0, 0, batch, max_ctx_len);
+}
+
+extern "C" tdl_status layer_decode_paged(tdl_layer* L, tdl_stream stream, const void* x, void* y,
+                                         int32_t batch, const int32_t* ctx_lens,
+                                         const int32_t* block_tables, int32_t max_blocks,
+                                         int32_t max_ctx_len, tdl_kv_cache* kv) {
+  TRY(check_decode(L, x, y, batch, ctx_lens, block_tables, max_blocks, max_ctx_len, kv));
+  return enqueue_decode(L, (hipStream_t)stream, x, y, batch, ctx_lens, block_tables, max_blocks,
+                        max_ctx_len, kv);
+}
+
+// ---------------------------------------------------------------- stack
+
+struct tdl_stack {
+  std::vector<tdl_layer*> layers;  // not owned
+  int H = 0;
+  int max_rows = 0;
+  void* buf[2] = {nullptr, nullptr};  // bf16 [max_rows, H]: activations between layers
+  ~tdl_stack() {
+    for (void* p : buf)
+      if (p) (void)hipFree(p);
+  }
+};
+
+extern "C" tdl_status stack_create(tdl_layer* const* layers, int32_t n_layers, tdl_stack** out) {
+  if (!out) return fail(TDL_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!layers || n_layers < 1) return fail(TDL_E_INVALID, "need n_layers >= 1 layers");
+  for (int i = 0; i < n_layers; ++i)
+    if (!layers[i]) return fail(TDL_E_INVALID, "layer %d is NULL", i);
+  std::unique_ptr<tdl_stack> S(new (std::nothrow) tdl_stack);
+  if (!S) return fail(TDL_E_NOMEM, "host allocation failed");
+  S->H = layers[0]->cfg.hidden;
+  S->max_rows = std::numeric_limits<int>::max();
+  for (int i = 0; i < n_layers; ++i) {
+    if (layers[i]->cfg.hidden != S->H)
+      return fail(TDL_E_INVALID, "layer %d: hidden %d differs from layer 0's %d", i,
+                  layers[i]->cfg.hidden, S->H);
+    S->max_rows = std::min({S->max_rows, layers[i]->cfg.max_seqs, layers[i]->cfg.max_tokens});
+    S->layers.push_back(layers[i]);
+  }
+  if (n_layers > 1) {
+    const size_t bytes = (size_t)S->max_rows * S->H * 2;
+    for (void*& p : S->buf)
+      if (hipMalloc(&p, bytes) != hipSuccess) {
+        p = nullptr;
+        (void)hipGetLastError();
+        return fail(TDL_E_NOMEM, "hipMalloc of %zu bytes failed", bytes);
+      }
+  }
+  *out = S.release();
+  return TDL_OK;
+}
+
+extern "C" tdl_status stack_destroy(tdl_stack* stack) {
+  delete stack;
+  return TDL_OK;
+}
+
+extern "C" tdl_status stack_decode_paged(tdl_stack* S, tdl_stream stream, const void* x, void* y,
+                                         int32_t batch, const int32_t* ctx_lens,
+                                         const int32_t* block_tables, int32_t max_blocks,
+                                         int32_t max_ctx_len, tdl_kv_cache* const* kvs) {
+  if (!S) return fail(TDL_E_INVALID, "stack is NULL");
+  if (!kvs) return fail(TDL_E_INVALID, "kvs is NULL");
+  if (batch > S->max_rows)
+    return fail(TDL_E_CAPACITY, "batch %d exceeds the stack's %d rows", batch, S->max_rows);
+  const int n = (int)S->layers.size();
+  auto in_of = [&](int i) { return i == 0 ? x : (const void*)S->buf[(i - 1) & 1]; };
+  auto out_of = [&](int i) { return i == n - 1 ? y : S->buf[i & 1]; };
+  if (x && y && n > 1 && (x == y)) return fail(TDL_E_INVALID, "y must not alias x");
+  // every layer's arguments are checked before the first layer is enqueued
+  for (int i = 0; i < n; ++i) {
+    const tdl_status st = check_decode(S->layers[i], in_of(i), out_of(i), batch, ctx_lens,
+                                       block_tables, max_blocks, max_ctx_len, kvs[i]);
+    if (st != TDL_OK) return st;
+  }
+  for (int i = 0; i < n; ++i)
+    TRY(enqueue_decode(S->layers[i], (hipStream_t)stream, in_of(i), out_of(i), batch, ctx_lens,
+                       block_tables, max_blocks, max_ctx_len, kvs[i]));
+  return TDL_OK;
 }
 
 extern "C" tdl_status layer_step(tdl_layer* L, tdl_stream stream, const tdl_batch* b, const void* x,
