@@ -16,8 +16,8 @@ Every step is written from the definition it cites.  Where the pages are
 silent or garbled the plainest reading is taken and named in the docstring.
 
 Parity status of each function (what pins it, see tests/test_oracle_*.py):
-  round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, kv_calibrate,
-  kv_quantize, kv_dequantize, attention, attention_online, PagedCache,
+  round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, kv_levels,
+  kv_calibrate, kv_quantize, kv_dequantize, attention, attention_online, PagedCache,
   layer_forward -- all pinned (worked examples, closed forms, brute force,
   special cases).  The pages' own printed layer output (Qwen2.5-7B-Instruct
   weights, [QWEN] section "运行结果") cannot be reproduced without those
@@ -154,12 +154,22 @@ def swiglu(gate, up) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# int8 asymmetric per-channel KV quantisation
+# int8 / uint4 asymmetric per-channel KV quantisation
 # --------------------------------------------------------------------------
 
-def kv_calibrate(values: np.ndarray):
+def kv_levels(n_bits: int) -> int:
+    """Largest code of an n-bit cache: 255 for int8 ([HET] section 2.6),
+    15 for uint4.  The pages list uint4 KV caches ([HET] sections 2.4, 2.6)
+    but give the formula only for 8 bits; the reading taken is the same
+    asymmetric formula with 2^4 - 1 in place of 255."""
+    assert n_bits in (8, 4)
+    return (1 << n_bits) - 1
+
+
+def kv_calibrate(values: np.ndarray, n_bits: int = 8):
     """Per-channel asymmetric parameters from [HET] section 2.6 (量化公式):
-    scale_c = (max_c - min_c) / 255, zero_point_c = round(-min_c / scale_c).
+    scale_c = (max_c - min_c) / L, zero_point_c = round(-min_c / scale_c),
+    with L = 2^n_bits - 1 (255 for the page's int8, 15 for uint4).
 
     ``values`` is [n_tokens, n_kv_heads, head_dim] float32; a channel is one
     (kv_head, d) pair, reduced over all tokens.  Reading taken: the arithmetic
@@ -171,19 +181,20 @@ def kv_calibrate(values: np.ndarray):
     assert v.ndim == 3 and v.shape[0] > 0
     mx = v.max(axis=0)
     mn = v.min(axis=0)
-    scale = (mx - mn) / np.float32(255.0)
+    scale = (mx - mn) / np.float32(kv_levels(n_bits))
     scale = np.where(scale == 0, np.float32(1.0), scale).astype(np.float32)
     zp = np.rint(-mn / scale).astype(np.int32)
     return scale, zp
 
 
-def kv_quantize(x, scale, zp) -> np.ndarray:
-    """Q_c = clamp(round(x / scale_c) + zero_point_c, 0, 255) ([HET] section
-    2.6), in float32 with a correctly rounded divide and round-half-to-even;
-    stored as uint8 (the page calls the codes int8 but clamps to 0..255)."""
+def kv_quantize(x, scale, zp, n_bits: int = 8) -> np.ndarray:
+    """Q_c = clamp(round(x / scale_c) + zero_point_c, 0, L) ([HET] section
+    2.6, L = 2^n_bits - 1), in float32 with a correctly rounded divide and
+    round-half-to-even; stored one code per uint8 element (the page calls
+    the 8-bit codes int8 but clamps them to 0..255)."""
     x32 = np.asarray(x, np.float32)
     q = np.rint(x32 / scale).astype(np.int64) + zp.astype(np.int64)
-    return np.clip(q, 0, 255).astype(np.uint8)
+    return np.clip(q, 0, kv_levels(n_bits)).astype(np.uint8)
 
 
 def kv_dequantize(codes, scale, zp) -> np.ndarray:
@@ -202,15 +213,16 @@ class PagedCache:
     maps logical block t // B to a physical block, and token t lives at
     offset t % B of it ([TFF] section 3.6.4, get_location; [HET] section 4.3
     with 16-token blocks).  ``dtype`` is "bf16" (values rounded to bf16 when
-    written) or "u8" (codes + per-channel scale/zero point).  Keys/values are
-    held per (block, kv_head, offset, d); the physical byte layout of the GPU
-    pool is not modelled here.
+    written), "u8" or "u4" (8- or 4-bit codes + per-channel scale/zero point,
+    one code per element here).  Keys/values are held per (block, kv_head,
+    offset, d); the physical byte layout of the GPU pool is not modelled here.
     """
 
     def __init__(self, n_blocks: int, n_kv_heads: int, head_dim: int, dtype: str,
                  k_params=None, v_params=None):
-        assert dtype in ("bf16", "u8")
+        assert dtype in ("bf16", "u8", "u4")
         self.dtype = dtype
+        self.n_bits = 4 if dtype == "u4" else 8
         self.n_blocks, self.n_kv_heads, self.head_dim = n_blocks, n_kv_heads, head_dim
         shape = (n_blocks, n_kv_heads, BLOCK_SIZE, head_dim)
         if dtype == "bf16":
@@ -239,13 +251,13 @@ class PagedCache:
             self.k[blk, :, off, :] = round_bf16(k)
             self.v[blk, :, off, :] = round_bf16(v)
         else:
-            self.k[blk, :, off, :] = kv_quantize(k, self.k_scale, self.k_zp)
-            self.v[blk, :, off, :] = kv_quantize(v, self.v_scale, self.v_zp)
+            self.k[blk, :, off, :] = kv_quantize(k, self.k_scale, self.k_zp, self.n_bits)
+            self.v[blk, :, off, :] = kv_quantize(v, self.v_scale, self.v_zp, self.n_bits)
             self.written[blk, off] = True
 
     def read(self, table_row, n_tokens: int):
         """Keys and values of tokens 0..n_tokens-1, [n_tokens, n_kv_heads, D],
-        as real numbers (u8 codes dequantised)."""
+        as real numbers (codes dequantised)."""
         K = np.empty((n_tokens, self.n_kv_heads, self.head_dim))
         V = np.empty_like(K)
         for t in range(n_tokens):

@@ -183,6 +183,49 @@ def test_kv_quant_invariants_and_error_bound():
     assert s[0, 0] == 1.0 and z[0, 0] == -2
 
 
+def test_kv_quant_u4_worked_examples():
+    g = load("kv_quant_u4_worked.json")
+    assert oracle.kv_levels(g["n_bits"]) == 15 and oracle.kv_levels(8) == 255
+    for case in g["cases"]:
+        x = np.array(case["x"], np.float32).reshape(4, 1, 1)
+        scale, zp = oracle.kv_calibrate(x, 4)
+        assert float(scale[0, 0]) == float.fromhex(case["scale_hex"])
+        assert int(zp[0, 0]) == case["zp"]
+        codes = oracle.kv_quantize(x, scale, zp, 4)
+        assert codes.ravel().tolist() == case["codes"]
+
+
+def test_kv_quant_u4_invariants_and_error_bound():
+    rng = np.random.default_rng(16)
+    x = (rng.standard_normal((300, 2, 8)) * rng.uniform(0.1, 5, (1, 2, 8))
+         + rng.uniform(-2, 2, (1, 2, 8))).astype(np.float32)
+    scale, zp = oracle.kv_calibrate(x, 4)
+    # 15 steps span each channel's range (a 255-step scale would be 17x finer)
+    rng_c = x.max(0).astype(np.float64) - x.min(0)
+    np.testing.assert_allclose(scale, rng_c / 15, rtol=2 ** -22)
+    codes = oracle.kv_quantize(x, scale, zp, 4)
+    assert codes.max() <= 15
+    amin, amax = x.argmin(axis=0), x.argmax(axis=0)
+    for h in range(2):
+        for d in range(8):
+            assert codes[amin[h, d], h, d] == 0
+            assert codes[amax[h, d], h, d] in (14, 15)
+            # every level in between is reachable: 300 spread values hit most
+            assert len(np.unique(codes[:, h, d])) >= 12
+    deq = oracle.kv_dequantize(codes, scale, zp)
+    bound = scale / 2 + 2.0 ** -23 * np.maximum(np.abs(x.min(0)), np.abs(x.max(0))) * 4
+    assert np.all(np.abs(deq - x) <= bound[None] * (1 + 1e-6))
+    # a channel of exactly 16 equally spaced values (step a power of two)
+    # takes the codes 0..15 in order
+    lv = (np.arange(16, dtype=np.float32) * np.float32(0.125) - np.float32(1)).reshape(16, 1, 1)
+    s, z = oracle.kv_calibrate(lv, 4)
+    assert s[0, 0] == 0.125 and z[0, 0] == 8
+    assert oracle.kv_quantize(lv, s, z, 4).ravel().tolist() == list(range(16))
+    # values outside the calibrated range clamp at both ends
+    assert oracle.kv_quantize(np.float32([[[1e6]]]), s, z, 4)[0, 0, 0] == 15
+    assert oracle.kv_quantize(np.float32([[[-1e6]]]), s, z, 4)[0, 0, 0] == 0
+
+
 # ------------------------------------------------------------ attention ---
 
 def brute_force_attention(q, q_pos, K, V):
@@ -280,6 +323,23 @@ def test_paged_u8_roundtrip():
     Kp, _ = cache.read(table[0], 40)
     np.testing.assert_allclose(Kp, oracle.kv_dequantize(oracle.kv_quantize(x, *params), *params), rtol=0)
     assert np.all(np.abs(Kp - x) <= params[0][None] * 0.5001)
+
+
+def test_paged_u4_roundtrip():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((40, 2, 8)).astype(np.float32)
+    params = oracle.kv_calibrate(x, 4)
+    cache = oracle.PagedCache(4, 2, 8, "u4", params, params)
+    table = np.array([[1, 3, 0]], np.int32)
+    for t in range(40):
+        cache.write(table[0], t, x[t], -x[t])
+    Kp, Vp = cache.read(table[0], 40)
+    assert cache.k.max() <= 15
+    np.testing.assert_allclose(Kp, oracle.kv_dequantize(oracle.kv_quantize(x, *params, 4), *params),
+                               rtol=0)
+    assert np.all(np.abs(Kp - x) <= params[0][None] * 0.5001)
+    # the negated values fall outside the range on one side and clamp there
+    assert np.all(Vp >= oracle.kv_dequantize(np.zeros((1, 2, 8)), *params) - 1e-12)
 
 
 # ---------------------------------------------------------------- layer ---
