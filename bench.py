@@ -11,7 +11,8 @@ Also reported (same JSON line): the paged decode step of the same layer (batch
 with its HBM fraction; the dominant kernel's roofline (per-kernel HIP-event
 durations recorded by the library on the call's stream over the timed
 region); the other configurations (the 512-token prefill, the Qwen3-8B
-decode over a u8 cache at batch 128, the Qwen3-8B Q8_0 mixed step), each with
+decode over u8 and u4 caches at batch 128, the Qwen3-8B Q8_0 mixed step, a
+28-layer decode stack), each with
 its roofline fraction; and the oracle's CPU throughput on a bounded sample of
 the prefill.
 
@@ -51,7 +52,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-other", action="store_true",
-                    help="skip the other workloads (512-token prefill, Qwen3 u8 decode, Q8_0 mixed step)")
+                    help="skip the other workloads (512-token prefill, Qwen3 u8 / u4 decode, Q8_0 mixed step, layer stack)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 512 MiB device-to-device copy (a known byte count that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -124,10 +125,62 @@ def attention_flops(D, Hq, n_pairs):
     return 4 * D * Hq * n_pairs  # Q.K and P.V: 2 FLOP x D per (query, key) pair and head
 
 
+def quantised_decode(args, torch, synth, tdl, stream, kvd, flush, sink):
+    """Qwen3-8B-shaped decode at batch 128 over a u8 or u4 (per-channel
+    asymmetric) cache; contexts and block placement as for the bf16 decode."""
+    wl = synth.WORKLOADS[f"qwen3_decode_{kvd}_b128"]
+    shape = wl.shape
+    Hkv, D, H = shape.n_kv_heads, shape.head_dim, shape.hidden
+    B = wl.decode_batch
+    ctx = synth.context_lengths(np.random.default_rng(30), wl)
+    totals = (ctx + 1).tolist()
+    nb = int(sum(math.ceil(t / 16) for t in totals))
+    tab_np = synth.random_tables(np.random.default_rng(31), totals, n_blocks=nb)
+    tab = torch.from_numpy(tab_np).cuda()
+    log(f"qwen3 {kvd} decode: weights, cache of {int(ctx.sum())} tokens")
+    layer = tdl.Layer(tdl.make_config(shape, max_tokens=B, max_seqs=B, max_position=8448),
+                      synth.torch_weights(shape, seed=32))
+    kv = tdl.KvCache(nb, Hkv, D, kvd)
+    # per-channel parameters from a sample of the same N(0,1) distribution,
+    # then the cached tokens, 16 sequences at a time
+    kv.calibrate(synth.torch_normal((1 << 16, Hkv, D), seed=33), synth.torch_normal((1 << 16, Hkv, D), seed=34))
+    for s0 in range(0, B, 16):
+        c = ctx[s0:s0 + 16]
+        n = int(c.sum())
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(c)]).astype(np.int32)).cuda()
+        kv.write(cu, torch.zeros(len(c), dtype=torch.int32, device="cuda"), tab[s0:s0 + 16].contiguous(),
+                 synth.torch_normal((n, Hkv, D), seed=100 + s0), synth.torch_normal((n, Hkv, D), seed=200 + s0))
+    ctx_d = torch.from_numpy(ctx).cuda()
+    x = synth.torch_normal((B, H), seed=35, dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    max_ctx = int(ctx.max()) + 1
+    for _ in range(3):
+        layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv)
+    times = timed_steps(torch, stream, lambda: layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv),
+                        args.decode_steps, flush, sink)
+    us = 1e3 * float(np.median(times))
+    bits = 8 if kvd == "u8" else 4
+    kv_bytes = int(sum(totals)) * Hkv * D * 2 * bits // 8  # K and V codes
+    step_bytes = weight_bytes(shape) + kv_bytes + 2 * B * H * 2
+    assert torch.isfinite(y.float()).all(), f"non-finite {kvd} decode output"
+    res = {f"qwen3_decode_{kvd}_b128": {
+        "workload": "qwen3-8b-shaped layer (Q/K RMSNorm) paged decode, batch 128, ctx U[512,8192], "
+                    f"{kvd} per-channel asymmetric KV, block 16, random block permutation; L2/MALL flushed between steps",
+        "us_per_step": round(us, 2), "algorithmic_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(step_bytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "stages_ms": stage_profile(layer, lambda: layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv), 5,
+                                   lambda: torch.sum(flush, dim=0, out=sink))}}
+    log(f"qwen3 {kvd} decode: {us:.1f} us/step")
+    layer.close()
+    kv.close()
+    return res
+
+
 def other_workloads(args, torch, synth, tdl, stream, layer512):
     """The other configurations of the layer, measured the same way (synthetic
     inputs, resident in HBM): the 512-token prefill of the same Qwen2.5-7B
-    layer, the Qwen3-8B decode over a u8 cache (batch 128), the Qwen3-8B
+    layer, the Qwen3-8B decode over a u8 and over a u4 cache (batch 128), the Qwen3-8B
     Q8_0 mixed step (a 2048-token chunk + 64 decode rows), and a 28-layer
     stack of the Qwen2.5-7B layer decoding batch 64."""
     out = {}
@@ -158,53 +211,9 @@ def other_workloads(args, torch, synth, tdl, stream, layer512):
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
 
-    # ---- Qwen3-8B decode, batch 128, ctx U[512, 8192], u8 cache
-    wl = synth.WORKLOADS["qwen3_decode_u8_b128"]
-    shape = wl.shape
-    Hkv, D, H = shape.n_kv_heads, shape.head_dim, shape.hidden
-    B = wl.decode_batch
-    ctx = synth.context_lengths(np.random.default_rng(30), wl)
-    totals = (ctx + 1).tolist()
-    nb = int(sum(math.ceil(t / 16) for t in totals))
-    tab_np = synth.random_tables(np.random.default_rng(31), totals, n_blocks=nb)
-    tab = torch.from_numpy(tab_np).cuda()
-    log(f"qwen3 u8 decode: weights, cache of {int(ctx.sum())} tokens")
-    layer = tdl.Layer(tdl.make_config(shape, max_tokens=B, max_seqs=B, max_position=8448),
-                      synth.torch_weights(shape, seed=32))
-    kv = tdl.KvCache(nb, Hkv, D, "u8")
-    # per-channel parameters from a sample of the same N(0,1) distribution,
-    # then the cached tokens, 16 sequences at a time
-    kv.calibrate(synth.torch_normal((1 << 16, Hkv, D), seed=33), synth.torch_normal((1 << 16, Hkv, D), seed=34))
-    for s0 in range(0, B, 16):
-        c = ctx[s0:s0 + 16]
-        n = int(c.sum())
-        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(c)]).astype(np.int32)).cuda()
-        kv.write(cu, torch.zeros(len(c), dtype=torch.int32, device="cuda"), tab[s0:s0 + 16].contiguous(),
-                 synth.torch_normal((n, Hkv, D), seed=100 + s0), synth.torch_normal((n, Hkv, D), seed=200 + s0))
-    ctx_d = torch.from_numpy(ctx).cuda()
-    x = synth.torch_normal((B, H), seed=35, dtype=torch.bfloat16)
-    y = torch.empty_like(x)
-    max_ctx = int(ctx.max()) + 1
-    for _ in range(3):
-        layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv)
-    times = timed_steps(torch, stream, lambda: layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv),
-                        args.decode_steps, flush, sink)
-    us = 1e3 * float(np.median(times))
-    kv_bytes = int(sum(totals)) * Hkv * D * 2  # u8 K and V
-    step_bytes = weight_bytes(shape) + kv_bytes + 2 * B * H * 2
-    assert torch.isfinite(y.float()).all(), "non-finite u8 decode output"
-    out["qwen3_decode_u8_b128"] = {
-        "workload": "qwen3-8b-shaped layer (Q/K RMSNorm) paged decode, batch 128, ctx U[512,8192], "
-                    "u8 per-channel asymmetric KV, block 16, random block permutation; L2/MALL flushed between steps",
-        "us_per_step": round(us, 2), "algorithmic_bytes": step_bytes,
-        "roofline": {"bound": "hbm", "achieved": round(step_bytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
-        "stages_ms": stage_profile(layer, lambda: layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv), 5,
-                                   lambda: torch.sum(flush, dim=0, out=sink))}
-    log(f"qwen3 u8 decode: {us:.1f} us/step")
-    layer.close()
-    kv.close()
-    del x, y, kv, tab, ctx_d
+    # ---- Qwen3-8B decode, batch 128, ctx U[512, 8192], u8 and u4 caches
+    for kvd in ("u8", "u4"):
+        out.update(quantised_decode(args, torch, synth, tdl, stream, kvd, flush, sink))
 
     # ---- Qwen3-8B Q8_0 mixed step: one 2048-token chunk + 64 decode rows at ctx 2048
     wl = synth.WORKLOADS["qwen3_q80_mixed"]

@@ -63,7 +63,8 @@ typedef enum {
   TDL_BF16 = 0,
   TDL_F32 = 1,
   TDL_Q8_0 = 2,    /* 32 int8 codes + one fp16 scale per block along K          */
-  TDL_U8_ASYM = 3  /* uint8 codes + per-channel fp32 scale and int32 zero point */
+  TDL_U8_ASYM = 3, /* uint8 codes + per-channel fp32 scale and int32 zero point */
+  TDL_U4_ASYM = 4  /* uint4 codes, two per byte, + the same per-channel parameters */
 } tdl_dtype;
 
 typedef void* tdl_stream; /* hipStream_t */
@@ -108,7 +109,7 @@ typedef struct {
   int32_t block_size;     /* tokens per block; must be 16                   */
   int32_t n_kv_heads;
   int32_t head_dim;       /* 64 or 128                                      */
-  int32_t kv_dtype;       /* TDL_BF16 or TDL_U8_ASYM                        */
+  int32_t kv_dtype;       /* TDL_BF16, TDL_U8_ASYM or TDL_U4_ASYM ([HET] 2.4) */
   uint64_t free_list_seed;/* 0: blocks handed out 0,1,2,...; otherwise the
                              free list is a seeded random permutation       */
 } tdl_kv_config;
@@ -117,8 +118,14 @@ typedef struct {
  * channel d) of K is at k_pool[b*k_strides[0] + g*k_strides[1] +
  * s*k_strides[2] + d*k_strides[3]] (strides in elements; same for V).  K is
  * stored [block][head][slot][d]; V is stored [block][head][d][slot] so that
- * the 16 tokens of one channel are contiguous.  For TDL_U8_ASYM the four
- * parameter arrays hold [n_kv_heads * head_dim] entries; otherwise NULL. */
+ * the 16 tokens of one channel are contiguous.  For TDL_U8_ASYM and
+ * TDL_U4_ASYM the four parameter arrays hold [n_kv_heads * head_dim]
+ * entries; otherwise NULL.
+ * TDL_U4_ASYM (elem_bytes 0): two 4-bit codes per byte, low nibble first,
+ * and the strides count bytes.  K row (block b, head g, slot s) is D/2
+ * bytes; its byte 4j + i (i < 4) holds channels 8j + i and 8j + 4 + i.  V
+ * is [block][head][D/2 channel pairs][16 slots] bytes: byte (c, s) holds
+ * channels 2c and 2c + 1 of slot s.  Every byte belongs to one token. */
 typedef struct {
   void* k_pool;
   void* v_pool;
@@ -277,7 +284,8 @@ tdl_status stack_decode_paged(tdl_stack* stack, tdl_stream stream, const void* x
 /* ------------------------------------------------------------- KV cache */
 
 /* Bytes of device memory a cache with this configuration needs (pools plus,
- * for TDL_U8_ASYM, the per-channel parameters).  0 for an invalid config. */
+ * for TDL_U8_ASYM / TDL_U4_ASYM, the per-channel parameters).  0 for an
+ * invalid config. */
 size_t kv_cache_bytes(const tdl_kv_config* cfg);
 
 /* Creates a cache handle.  dev_mem == NULL: the library allocates
@@ -311,10 +319,12 @@ tdl_status kv_block_release(tdl_kv_cache* kv, const int32_t* blocks, int32_t n);
 /* Number of blocks on the free list. */
 int32_t kv_free_blocks(const tdl_kv_cache* kv);
 
-/* TDL_U8_ASYM only: sets the per-channel (kv head, d) parameters of K and of
- * V from n_tokens float32 rows k, v [n_tokens, Hkv, D] (device):
- * scale = (max - min) / 255, zero_point = round_half_even(-min / scale),
- * scale 1 for a flat channel ([HET] 2.6).  Later writes use them. */
+/* TDL_U8_ASYM / TDL_U4_ASYM only: sets the per-channel (kv head, d)
+ * parameters of K and of V from n_tokens float32 rows k, v [n_tokens, Hkv,
+ * D] (device): scale = (max - min) / L with L = 255 (u8) or 15 (u4),
+ * zero_point = round_half_even(-min / scale), scale 1 for a flat channel
+ * ([HET] 2.6; the pages give the formula for 8 bits only, u4 takes the same
+ * one with 15 levels).  Later writes use them. */
 tdl_status kv_cache_calibrate(tdl_kv_cache* kv, tdl_stream stream, const float* k,
                               const float* v, int64_t n_tokens);
 
@@ -322,8 +332,8 @@ tdl_status kv_cache_calibrate(tdl_kv_cache* kv, tdl_stream stream, const float* 
  * ([rows, Hkv, D], src_dtype TDL_F32 or TDL_BF16, device) belong to sequence
  * i and go to positions start_pos[i] + 0, 1, ... through block_tables
  * (device int32 [n_seqs, max_blocks]).  cu_rows, start_pos: device int32.
- * bf16 caches round to nearest even; u8 caches quantise with
- * clamp(round_half_even(x / scale) + zero_point, 0, 255). */
+ * bf16 caches round to nearest even; u8 / u4 caches quantise with
+ * clamp(round_half_even(x / scale) + zero_point, 0, L), L = 255 / 15. */
 tdl_status kv_cache_write(tdl_kv_cache* kv, tdl_stream stream, int32_t n_seqs,
                           const int32_t* cu_rows, const int32_t* start_pos,
                           const int32_t* block_tables, int32_t max_blocks, int32_t src_dtype,

@@ -71,7 +71,7 @@ class Workload:
     ctx_lo: int = 0              # decode context lengths ~ U[ctx_lo, ctx_hi]
     ctx_hi: int = 0
     ctx_fixed: int = 0           # if > 0, every decode sequence has this context
-    kv_dtype: str = "none"       # "none" | "bf16" | "u8"
+    kv_dtype: str = "none"       # "none" | "bf16" | "u8" | "u4"
 
 
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
@@ -82,6 +82,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
              kv_dtype="bf16"),
     Workload("qwen3_decode_u8_b128", QWEN3_8B, "decode", decode_batch=128, ctx_lo=512, ctx_hi=8192,
              kv_dtype="u8"),
+    Workload("qwen3_decode_u4_b128", QWEN3_8B, "decode", decode_batch=128, ctx_lo=512, ctx_hi=8192,
+             kv_dtype="u4"),
     Workload("qwen3_q80_mixed", QWEN3_8B_Q80, "mixed", prefill_len=2048, decode_batch=64,
              ctx_fixed=2048, kv_dtype="bf16"),
 ]}

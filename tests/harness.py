@@ -46,20 +46,40 @@ def compare(y, ref) -> Err:
     return Err(float(d.max()), float(np.abs(ref).max()), float(d.sum() / max(np.abs(ref).sum(), 1e-300)))
 
 
+def unpack_u4(kt, vt):
+    """Codes of a u4 pool from its byte views (KvCache.tensors): K [blocks,
+    Hkv, 16, D], V [blocks, Hkv, D, 16].  Byte layout as include/tdl.h states
+    it: K byte 4j + i of a row holds channels 8j + i (low nibble) and 8j + 4
+    + i (high); V byte (c, slot) holds channels 2c and 2c + 1."""
+    k = kt.cpu().numpy()
+    v = vt.cpu().numpy()
+    hd = k.shape[-1]
+    K = np.empty(k.shape[:-1] + (2 * hd,), np.uint8)
+    j, i = np.arange(hd) // 4, np.arange(hd) % 4
+    K[..., 8 * j + i] = k & 15
+    K[..., 8 * j + 4 + i] = k >> 4
+    V = np.empty(v.shape[:2] + (2 * hd, v.shape[3]), np.uint8)
+    V[:, :, 0::2, :] = v & 15
+    V[:, :, 1::2, :] = v >> 4
+    return K, V
+
+
 # ------------------------------------------------------------------ oracle
 
 def oracle_cache(inp: synth.LayerInputs, seqs=None) -> Optional[oracle.PagedCache]:
     """The oracle's cache holding the already-cached tokens of the chosen
-    sequences (all by default).  u8 parameters come from every cached token."""
+    sequences (all by default).  u8 / u4 parameters come from every cached
+    token."""
     wl, shape, b = inp.workload, inp.workload.shape, inp.batch
     if wl.kv_dtype == "none":
         return None
     if wl.kv_dtype == "bf16":
         cache = oracle.PagedCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, "bf16")
     else:
-        kp = oracle.kv_calibrate(inp.cache_k)
-        vp = oracle.kv_calibrate(inp.cache_v)
-        cache = oracle.PagedCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, "u8", kp, vp)
+        bits = 4 if wl.kv_dtype == "u4" else 8
+        kp = oracle.kv_calibrate(inp.cache_k, bits)
+        vp = oracle.kv_calibrate(inp.cache_v, bits)
+        cache = oracle.PagedCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, wl.kv_dtype, kp, vp)
     if inp.cache_k is not None:
         seqs = range(b.n_seqs) if seqs is None else seqs
         off = np.concatenate([[0], np.cumsum(b.ctx_len)])
@@ -140,7 +160,7 @@ def gpu_setup(inp: synth.LayerInputs, max_tokens: Optional[int] = None, max_posi
         if inp.cache_k is not None:
             ck = torch.from_numpy(inp.cache_k).cuda()
             cv = torch.from_numpy(inp.cache_v).cuda()
-            if wl.kv_dtype == "u8":
+            if wl.kv_dtype in ("u8", "u4"):
                 kv.calibrate(ck, cv)
             cu = torch.from_numpy(np.concatenate([[0], np.cumsum(b.ctx_len)]).astype(np.int32)).cuda()
             zero = torch.zeros(b.n_seqs, dtype=torch.int32, device="cuda")

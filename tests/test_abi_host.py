@@ -96,6 +96,11 @@ def test_kv_cache_bytes():
     assert tdl._kv_bytes(ctypes.byref(c)) == 2 * 100 * 4 * 16 * 128 * 2
     c = tdl.KvConfig(100, 16, 8, 128, tdl.TDL_U8_ASYM, 0)
     assert tdl._kv_bytes(ctypes.byref(c)) == 2 * 100 * 8 * 16 * 128 + 4 * 8 * 128 * 4
+    # u4: two codes per byte (half the u8 pool), the same parameter arrays
+    c = tdl.KvConfig(100, 16, 8, 128, tdl.TDL_U4_ASYM, 0)
+    assert tdl._kv_bytes(ctypes.byref(c)) == 2 * 100 * 8 * 16 * 64 + 4 * 8 * 128 * 4
+    assert tdl._kv_bytes(ctypes.byref(tdl.KvConfig(100, 16, 8, 96, tdl.TDL_U4_ASYM, 0))) == 0
+    assert tdl._kv_bytes(ctypes.byref(tdl.KvConfig(100, 16, 8, 128, 5, 0))) == 0
     assert tdl._kv_bytes(ctypes.byref(tdl.KvConfig(100, 32, 4, 128, tdl.TDL_BF16, 0))) == 0
     assert tdl._kv_bytes(ctypes.byref(tdl.KvConfig(0, 16, 4, 128, tdl.TDL_BF16, 0))) == 0
 
@@ -108,6 +113,23 @@ def test_kv_cache_view_strides():
     assert list(v.v_strides) == [4 * 16 * 128, 16 * 128, 1, 16]
     assert v.v_pool - v.k_pool == 10 * 4 * 16 * 128 * 2
     assert v.elem_bytes == 2 and not v.k_scale
+    kv.close()
+    # u4: byte strides, D/2 bytes per K row and per V channel-pair column
+    kv = tdl.KvCache.host_only(10, 4, 128, "u4")
+    v = kv.view()
+    assert list(v.k_strides) == [4 * 16 * 64, 16 * 64, 64, 1]
+    assert list(v.v_strides) == [4 * 16 * 64, 16 * 64, 1, 16]
+    assert v.v_pool - v.k_pool == 10 * 4 * 16 * 64
+    assert v.elem_bytes == 0 and v.k_scale and v.v_zero_point
+    assert v.k_zero_point - v.k_scale == 4 * 128 * 4
+    kv.close()
+
+
+def test_kv_calibrate_rejects_bf16_cache():
+    import transformer_decoder_layer_amd as tdl
+    kv = tdl.KvCache.host_only(10, 4, 128)
+    assert tdl._kv_calibrate(kv.handle, None, 1 << 20, 1 << 20, 16) == tdl.TDL_E_INVALID
+    assert b"TDL_U4_ASYM" in tdl._last_error()
     kv.close()
 
 

@@ -1,4 +1,4 @@
-"""Bit-exact GPU checks through the C-ABI: cache slot placement, u8
+"""Bit-exact GPU checks through the C-ABI: cache slot placement, u8 / u4
 calibration and codes against the oracle's quantiser on identical fp32
 inputs, paged-table independence, and run-to-run determinism."""
 import dataclasses
@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from harness import gpu_call, gpu_setup
+from harness import gpu_call, gpu_setup, unpack_u4
 
 pytestmark = pytest.mark.gpu
 
@@ -109,6 +109,40 @@ def test_u8_calibration_and_codes_match_oracle_quantiser():
         assert np.array_equal(vc[blk, :, :, off], qv[r]), r
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_u4_calibration_and_codes_match_oracle_quantiser(D):
+    import torch
+    lens, starts = (300, 477), (0, 3)
+    kv, dev, cu, st, table_d, table, k, v = _write_setup("u4", n_blocks=60, D=D, lens=lens,
+                                                         starts=starts, seed=4)
+    kv.calibrate(dev(k), dev(v))
+    kv.write(cu, st, table_d, dev(k), dev(v))
+    torch.cuda.synchronize()
+    kt, vt, ks, kz, vs, vz = kv.tensors()
+    assert kt.shape[-1] == D // 2 and vt.shape[-2] == D // 2
+    sk, zk = oracle.kv_calibrate(k, 4)
+    sv, zv = oracle.kv_calibrate(v, 4)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), sk.reshape(-1).view(np.uint32))
+    assert np.array_equal(kz.cpu().numpy(), zk.reshape(-1))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), sv.reshape(-1).view(np.uint32))
+    assert np.array_equal(vz.cpu().numpy(), zv.reshape(-1))
+    kc, vc = unpack_u4(kt, vt)
+    qk, qv = oracle.kv_quantize(k, sk, zk, 4), oracle.kv_quantize(v, sv, zv, 4)
+    slots = _slots(table, lens, starts)
+    for r, (blk, off) in enumerate(slots):
+        assert np.array_equal(kc[blk, :, off, :], qk[r]), r
+        assert np.array_equal(vc[blk, :, :, off], qv[r]), r
+    # whole bytes per token: every pool byte of an unwritten slot keeps the
+    # sentinel (D/2 K bytes and D/2 V bytes per slot and head)
+    written = np.zeros(kt.shape[:3], bool)  # [block, head, slot]
+    for blk, off in slots:
+        written[blk, :, off] = True
+    kb, vb = kt.cpu().numpy(), vt.cpu().numpy()
+    assert np.all(kb[~written] == 0x5A)
+    assert np.all(vb.transpose(0, 1, 3, 2)[~written] == 0x5A)
+    assert int(written.sum()) == 2 * sum(lens)
+
+
 def _tiny_decode_inputs(kv_dtype, seed, table_seed):
     shape = dataclasses.replace(synth.TINY, qkv_bias=False, qk_norm=True, weight_dtype="bf16")
     wl = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=shape, kv_dtype=kv_dtype)
@@ -128,7 +162,7 @@ def _tiny_decode_inputs(kv_dtype, seed, table_seed):
     return dataclasses.replace(inp, batch=b), dataclasses.replace(inp, batch=ident)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "u8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "u8", "u4"])
 def test_paged_decode_independent_of_block_placement(kv_dtype):
     import torch
     a, b = _tiny_decode_inputs(kv_dtype, seed=7, table_seed=11)

@@ -44,7 +44,7 @@ def test_gqa_ratios_prefill_and_decode(shape):
     inp = synth.make_inputs(wl, seed=21, prefill_len=70, prefill_start=19, spare_blocks=2)
     layer, kv, t, cache, rows = check_layer(inp, what=f"prefill {shape.name}")
     check_cache_rows(inp, kv, cache, [0])
-    for kvd in ("bf16", "u8"):
+    for kvd in ("bf16", "u8", "u4"):
         wd = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=shape, kv_dtype=kvd)
         ctx = [0, 9, 33, 255, 700]
         inp = synth.make_inputs(wd, seed=22, decode_batch=len(ctx), decode_ctx=ctx)

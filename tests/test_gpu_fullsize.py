@@ -1,7 +1,7 @@
 """GPU parity at the full sizes of the five workloads, in the launch
 configuration the benchmark uses.  Where the oracle would take minutes the
 check runs on a sample of rows or sequences (the oracle still writes every
-row's K/V into its cache and calibrates u8 on every cached token)."""
+row's K/V into its cache and calibrates u8 / u4 on every cached token)."""
 import numpy as np
 import pytest
 
@@ -51,6 +51,13 @@ def test_qwen3_decode_u8_b128_sampled_seqs():
     ctx = inp.batch.ctx_len
     seqs = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 17, 64, 101, 127})
     _check(inp, seqs, what="qwen3 u8 decode b128")
+
+
+def test_qwen3_decode_u4_b128_sampled_seqs():
+    inp = synth.make_inputs(synth.WORKLOADS["qwen3_decode_u4_b128"])
+    ctx = inp.batch.ctx_len
+    seqs = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 17, 64, 101, 127})
+    _check(inp, seqs, what="qwen3 u4 decode b128")
 
 
 def test_qwen3_q80_mixed_sampled():

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from harness import compare, gpu_call, gpu_setup, run_oracle
+from harness import compare, gpu_call, gpu_setup, run_oracle, unpack_u4
 
 pytestmark = pytest.mark.gpu
 
@@ -75,10 +75,13 @@ def check_layer(inp, seqs=None, what="", stages=True, **setup):
 
 def check_cache_rows(inp, kv, cache, seqs):
     """New tokens' K/V in the GPU pool: bf16 values within tolerance of the
-    oracle's (both round their own projections), u8 codes within one code."""
+    oracle's (both round their own projections), u8 / u4 codes within one
+    code."""
     import torch
     b = inp.batch
     kt, vt = kv.tensors()[:2]
+    if cache.dtype == "u4":
+        kt, vt = map(torch.from_numpy, unpack_u4(kt, vt))
     kg, vg, kr, vr = [], [], [], []
     for i in seqs:
         for p in range(int(b.ctx_len[i]), int(b.ctx_len[i] + b.q_len[i])):
@@ -88,7 +91,7 @@ def check_cache_rows(inp, kv, cache, seqs):
             kr.append(cache.k[blk, :, off, :].astype(np.float64))
             vr.append(cache.v[blk, :, off, :].astype(np.float64))
     kg, vg, kr, vr = map(np.array, (kg, vg, kr, vr))
-    if cache.dtype == "u8":
+    if cache.dtype in ("u8", "u4"):
         assert np.abs(kg - kr).max() <= 1 and np.abs(vg - vr).max() <= 1
         assert (kg != kr).mean() < 0.05 and (vg != vr).mean() < 0.05
     else:
@@ -134,6 +137,15 @@ def test_tiny_decode_u8():
     ctx = [1, 15, 16, 17, 64, 300, 777, 2048]
     inp = synth.make_inputs(wl, seed=4, decode_batch=len(ctx), decode_ctx=ctx)
     layer, kv, t, cache, rows = check_layer(inp, what="decode u8 tiny")
+    check_cache_rows(inp, kv, cache, range(len(ctx)))
+
+
+@pytest.mark.parametrize("shape", [TINY_Q3, TINY_D128], ids=lambda s: s.name)
+def test_tiny_decode_u4(shape):
+    wl = dataclasses.replace(synth.WORKLOADS["qwen3_decode_u4_b128"], shape=shape)
+    ctx = [0, 1, 15, 16, 17, 64, 300, 777, 2048]
+    inp = synth.make_inputs(wl, seed=14, decode_batch=len(ctx), decode_ctx=ctx)
+    layer, kv, t, cache, rows = check_layer(inp, what=f"decode u4 {shape.name}")
     check_cache_rows(inp, kv, cache, range(len(ctx)))
 
 

@@ -45,7 +45,7 @@ def stack_inputs(wl, n_layers, ctx, seed):
     return out
 
 
-@pytest.mark.parametrize("kvd", ["bf16", "u8"])
+@pytest.mark.parametrize("kvd", ["bf16", "u8", "u4"])
 def test_stack_decode_matches_chained_oracle(kvd):
     import torch
     import transformer_decoder_layer_amd as tdl

@@ -22,8 +22,8 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 TDL_OK, TDL_E_INVALID, TDL_E_UNSUPPORTED, TDL_E_CAPACITY, TDL_E_NOMEM, TDL_E_HIP = range(6)
-TDL_BF16, TDL_F32, TDL_Q8_0, TDL_U8_ASYM = range(4)
-_DTYPES = {"bf16": TDL_BF16, "f32": TDL_F32, "q80": TDL_Q8_0, "u8": TDL_U8_ASYM}
+TDL_BF16, TDL_F32, TDL_Q8_0, TDL_U8_ASYM, TDL_U4_ASYM = range(5)
+_DTYPES = {"bf16": TDL_BF16, "f32": TDL_F32, "q80": TDL_Q8_0, "u8": TDL_U8_ASYM, "u4": TDL_U4_ASYM}
 
 c_i32, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 P_i32 = ctypes.POINTER(ctypes.c_int32)
@@ -223,24 +223,28 @@ class KvCache:
 
     def tensors(self):
         """torch views (k_pool, v_pool[, k_scale, k_zp, v_scale, v_zp]) of the
-        cache memory: k [blocks, Hkv, 16, D], v [blocks, Hkv, D, 16]."""
+        cache memory: k [blocks, Hkv, 16, D], v [blocks, Hkv, D, 16]; u4:
+        bytes k [blocks, Hkv, 16, D/2], v [blocks, Hkv, D/2, 16], two codes
+        per byte (include/tdl.h gives the nibble order)."""
         import torch
         v = self.view()
         nb, hk, d = self.cfg.n_blocks, self.cfg.n_kv_heads, self.cfg.head_dim
         base = self.memory.data_ptr()
         esz = v.elem_bytes
+        if esz == 0:
+            d //= 2
         n = nb * hk * 16 * d
 
         def sl(ptr, count, dt):
             off = ptr - base
             return self.memory[off:off + count * torch.tensor([], dtype=dt).element_size()].view(dt)
 
-        pool_dt = torch.uint8 if esz == 1 else torch.bfloat16
+        pool_dt = torch.bfloat16 if esz == 2 else torch.uint8
         k = sl(v.k_pool, n, pool_dt).view(nb, hk, 16, d)
         vv = sl(v.v_pool, n, pool_dt).view(nb, hk, d, 16)
-        if self.dtype != "u8":
+        if self.dtype not in ("u8", "u4"):
             return k, vv
-        c = hk * d
+        c = hk * self.cfg.head_dim
         return (k, vv, sl(v.k_scale, c, torch.float32), sl(v.k_zero_point, c, torch.int32),
                 sl(v.v_scale, c, torch.float32), sl(v.v_zero_point, c, torch.int32))
 

@@ -200,8 +200,8 @@ size_t decode_part_need(const tdl_layer_config& c, int max_batch) {
   size_t w = 0;
   const int max_blk = (c.max_position + 15) / 16;
   for (int b = 1; b <= max_batch; ++b)
-    for (int u8 = 0; u8 < 2; ++u8)
-      w = std::max(w, decode_plan(b, c.n_q_heads, c.n_kv_heads, c.head_dim, max_blk * 16, u8).part_floats_bound);
+    for (int fmt : {kKvBf16, kKvU8, kKvU4})
+      w = std::max(w, decode_plan(b, c.n_q_heads, c.n_kv_heads, c.head_dim, max_blk * 16, fmt).part_floats_bound);
   return w;
 }
 
@@ -210,7 +210,7 @@ KvPool pool_of(const tdl_layer* L, const tdl_kv_cache* kv) {
   if (kv) {
     p.k = kv->k;
     p.v = kv->v;
-    p.u8 = kv->cfg.kv_dtype == TDL_U8_ASYM;
+    p.fmt = kv->cfg.kv_dtype == TDL_U8_ASYM ? kKvU8 : kv->cfg.kv_dtype == TDL_U4_ASYM ? kKvU4 : kKvBf16;
     p.k_scale = kv->k_scale;
     p.k_zp = kv->k_zp;
     p.v_scale = kv->v_scale;
@@ -302,7 +302,7 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   const int H = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, I = c.intermediate;
   DecodePlan dp{};
   if (n_dec) {
-    dp = decode_plan(n_dec, Hq, Hkv, D, max_ctx_len, pool.u8 != 0);
+    dp = decode_plan(n_dec, Hq, Hkv, D, max_ctx_len, pool.fmt);
     if (dp.part_floats > L->dec_part_floats)
       return fail(TDL_E_CAPACITY, "decode workspace too small (batch %d, max_ctx_len %d)", n_dec,
                   max_ctx_len);
@@ -615,8 +615,8 @@ extern "C" tdl_status layer_prefill(tdl_layer* L, tdl_stream stream, const void*
   if (!kv && start_pos != 0) return fail(TDL_E_INVALID, "start_pos > 0 needs a KV cache");
   if (kv && !block_table) return fail(TDL_E_INVALID, "a KV cache needs a block table");
   TRY(check_kv_matches(L, kv));
-  if (kv && kv->cfg.kv_dtype == TDL_U8_ASYM)
-    return fail(TDL_E_UNSUPPORTED, "prefill attention over a u8 cache is not implemented");
+  if (kv && kv->cfg.kv_dtype != TDL_BF16)
+    return fail(TDL_E_UNSUPPORTED, "prefill attention over a u8 / u4 cache is not implemented");
   const int total = start_pos + n_tokens;
   if (kv && total > kv->cfg.n_blocks * 16)
     return fail(TDL_E_CAPACITY, "sequence longer than the cache pool");
@@ -779,8 +779,8 @@ extern "C" tdl_status layer_step(tdl_layer* L, tdl_stream stream, const tdl_batc
   if (b->max_ctx_len > L->cfg.max_position)
     return fail(TDL_E_CAPACITY, "max_ctx_len exceeds max_position");
   TRY(check_kv_matches(L, kv));
-  if (kv->cfg.kv_dtype == TDL_U8_ASYM && b->n_prefill_seqs > 0)
-    return fail(TDL_E_UNSUPPORTED, "prefill attention over a u8 cache is not implemented");
+  if (kv->cfg.kv_dtype != TDL_BF16 && b->n_prefill_seqs > 0)
+    return fail(TDL_E_UNSUPPORTED, "prefill attention over a u8 / u4 cache is not implemented");
   hipStream_t st = (hipStream_t)stream;
   if (debug_checks())
     TRY(debug_check_tables(b->ctx_len, b->q_len, b->n_seqs, 1, b->block_tables, b->max_blocks,
@@ -849,14 +849,18 @@ namespace {
 bool kv_config_ok(const tdl_kv_config* c) {
   return c && c->n_blocks > 0 && c->block_size == 16 && c->n_kv_heads > 0 &&
          (c->head_dim == 64 || c->head_dim == 128) &&
-         (c->kv_dtype == TDL_BF16 || c->kv_dtype == TDL_U8_ASYM);
+         (c->kv_dtype == TDL_BF16 || c->kv_dtype == TDL_U8_ASYM || c->kv_dtype == TDL_U4_ASYM);
+}
+bool kv_coded(const tdl_kv_config* c) {
+  return c->kv_dtype == TDL_U8_ASYM || c->kv_dtype == TDL_U4_ASYM;
 }
 size_t pool_bytes(const tdl_kv_config* c) {
-  const size_t esz = c->kv_dtype == TDL_U8_ASYM ? 1 : 2;
-  return align256((size_t)c->n_blocks * c->n_kv_heads * 16 * c->head_dim * esz);
+  // bytes per (block, head): 16 tokens x D elements of 2, 1 or 1/2 bytes
+  const size_t half_bytes = c->kv_dtype == TDL_BF16 ? 4 : c->kv_dtype == TDL_U8_ASYM ? 2 : 1;
+  return align256((size_t)c->n_blocks * c->n_kv_heads * 16 * c->head_dim * half_bytes / 2);
 }
 size_t param_bytes(const tdl_kv_config* c) {
-  return c->kv_dtype == TDL_U8_ASYM ? 4 * align256((size_t)c->n_kv_heads * c->head_dim * 4) : 0;
+  return kv_coded(c) ? 4 * align256((size_t)c->n_kv_heads * c->head_dim * 4) : 0;
 }
 }  // namespace
 
@@ -894,7 +898,7 @@ extern "C" tdl_status kv_cache_alloc(const tdl_kv_config* cfg, void* dev_mem, td
   char* base = (char*)kv->mem;
   kv->k = base;
   kv->v = base + pool_bytes(cfg);
-  if (cfg->kv_dtype == TDL_U8_ASYM) {
+  if (kv_coded(cfg)) {
     char* pb = base + 2 * pool_bytes(cfg);
     const size_t ps = align256((size_t)cfg->n_kv_heads * cfg->head_dim * 4);
     kv->k_scale = (float*)pb;
@@ -928,17 +932,20 @@ extern "C" tdl_status kv_cache_free(tdl_kv_cache* kv) {
 extern "C" tdl_status kv_cache_view(const tdl_kv_cache* kv, tdl_kv_view* out) {
   if (!kv || !out) return fail(TDL_E_INVALID, "NULL argument");
   const int64_t D = kv->cfg.head_dim, Hkv = kv->cfg.n_kv_heads;
+  // u4: strides over bytes, the last index a byte of the row (K) or a
+  // channel pair (V)
+  const int64_t W = kv->cfg.kv_dtype == TDL_U4_ASYM ? D / 2 : D;
   out->k_pool = kv->k;
   out->v_pool = kv->v;
-  out->k_strides[0] = Hkv * 16 * D;
-  out->k_strides[1] = 16 * D;
-  out->k_strides[2] = D;
+  out->k_strides[0] = Hkv * 16 * W;
+  out->k_strides[1] = 16 * W;
+  out->k_strides[2] = W;
   out->k_strides[3] = 1;
-  out->v_strides[0] = Hkv * 16 * D;
-  out->v_strides[1] = 16 * D;
+  out->v_strides[0] = Hkv * 16 * W;
+  out->v_strides[1] = 16 * W;
   out->v_strides[2] = 1;
   out->v_strides[3] = 16;
-  out->elem_bytes = kv->cfg.kv_dtype == TDL_U8_ASYM ? 1 : 2;
+  out->elem_bytes = kv->cfg.kv_dtype == TDL_BF16 ? 2 : kv->cfg.kv_dtype == TDL_U8_ASYM ? 1 : 0;
   out->k_scale = kv->k_scale;
   out->k_zero_point = kv->k_zp;
   out->v_scale = kv->v_scale;
@@ -1003,12 +1010,13 @@ extern "C" int32_t kv_free_blocks(const tdl_kv_cache* kv) {
 extern "C" tdl_status kv_cache_calibrate(tdl_kv_cache* kv, tdl_stream stream, const float* k,
                                          const float* v, int64_t n_tokens) {
   if (!kv || !k || !v) return fail(TDL_E_INVALID, "NULL argument");
-  if (kv->cfg.kv_dtype != TDL_U8_ASYM) return fail(TDL_E_INVALID, "cache is not TDL_U8_ASYM");
+  if (!kv_coded(&kv->cfg)) return fail(TDL_E_INVALID, "cache is not TDL_U8_ASYM or TDL_U4_ASYM");
   if (n_tokens < 1) return fail(TDL_E_INVALID, "n_tokens < 1");
   hipStream_t st = (hipStream_t)stream;
   const int C = kv->cfg.n_kv_heads * kv->cfg.head_dim;
-  HIP_TRY(tdl::kv_calibrate(k, n_tokens, C, kv->k_scale, kv->k_zp, st));
-  HIP_TRY(tdl::kv_calibrate(v, n_tokens, C, kv->v_scale, kv->v_zp, st));
+  const int levels = kv->cfg.kv_dtype == TDL_U8_ASYM ? 255 : 15;
+  HIP_TRY(tdl::kv_calibrate(k, n_tokens, C, levels, kv->k_scale, kv->k_zp, st));
+  HIP_TRY(tdl::kv_calibrate(v, n_tokens, C, levels, kv->v_scale, kv->v_zp, st));
   return TDL_OK;
 }
 

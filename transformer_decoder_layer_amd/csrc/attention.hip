@@ -22,10 +22,11 @@
 // Decode: a workgroup owns (sequence, KV head, context partition); its four
 // waves walk the partition's blocks through the block table, one 16-token
 // block per step, with the whole query-head group packed into the 16 columns
-// of one MFMA tile.  u8 caches are dequantised in registers: a code c
-// becomes the fp16 value 1024 + c exactly (one byte permute per two codes);
-// the K scale is folded into q and the zero point and bias into a per-head
-// constant, the V scale, zero point and bias are applied once at the end.
+// of one MFMA tile.  u8 / u4 caches are dequantised in registers: a code c
+// becomes the fp16 value 1024 + c (u8) or 64 + c (u4) exactly (a byte
+// permute per two codes, after a nibble mask for u4); the K scale is folded
+// into q and the zero point and bias into a per-head constant, the V scale,
+// zero point and bias are applied once at the end.
 // A second kernel merges the partitions' (m, l, acc) triples of each
 // (sequence, KV head) in partition order.
 
@@ -345,45 +346,63 @@ struct DecArgs {
 
 constexpr int kPartStride(int D) { return 16 * D + 32; }
 
-template <int D, bool U8>
+template <int D, int F>
 struct DecFrags {
-  // K rows (A operand): key lane%16, one 16-byte chunk per entry; bf16:
-  // channels 32s + 8*(lane/16) .. +7 of product s; u8: channels 64h +
-  // 16*(lane/16) .. +15, the first 8 for product 2h, the last 8 for product
-  // 2h + 1 (dec_kchan)
-  using KT = typename std::conditional<U8, uint4, bf16x8>::type;
-  KT k[U8 ? D / 64 : D / 32];
-  // V^T rows (A operand): channel 16t + lane%16, keys 4*(lane/16) .. +3
-  typename std::conditional<U8, uint32_t, bf16x4>::type v[D / 16];
+  // K rows (A operand): key lane%16.  bf16: one 16-byte chunk per product
+  // s, channels 32s + 8*(lane/16) .. +7; u8: one chunk per product pair,
+  // channels 64h + 16*(lane/16) .. +15, the first 8 for product 2h, the
+  // last 8 for 2h + 1; u4: one D/8-byte piece for all products, dword s
+  // (8 codes) for product s (dec_kchan)
+  using KT = typename std::conditional<
+      F == kKvBf16, bf16x8,
+      typename std::conditional<F == kKvU8 || D == 128, uint4, uint2>::type>::type;
+  KT k[F == kKvBf16 ? D / 32 : F == kKvU8 ? D / 64 : 1];
+  // V^T rows (A operand), keys 4*(lane/16) .. +3: bf16 / u8: channel 16t +
+  // lane%16 of tile t; u4: one dword per tile pair, the low nibbles for
+  // tile 2u, the high ones for 2u + 1 (dec_vchan)
+  using VT = typename std::conditional<F == kKvBf16, bf16x4, uint32_t>::type;
+  VT v[F == kKvU4 ? D / 32 : D / 16];
 };
 
 // First of the 8 channels lane group grp feeds to k-slots 8grp .. 8grp+7
 // of the key-query product s (any channel order gives the same dot product,
 // as long as K and q use the same one).  u8: a lane takes one 16-byte chunk
-// (16 channels) of its key row per pair of products.
-template <bool U8>
+// (16 channels) of its key row per pair of products; u4: the lane's D/4
+// channels of the row at once, dword s of them (channels 8s .. 8s+7 of the
+// piece, by the pool's nibble order) for product s.
+template <int D, int F>
 __device__ __forceinline__ int dec_kchan(int s, int grp) {
-  return U8 ? 64 * (s >> 1) + 16 * grp + 8 * (s & 1) : 32 * s + 8 * grp;
+  return F == kKvBf16 ? 32 * s + 8 * grp
+       : F == kKvU8   ? 64 * (s >> 1) + 16 * grp + 8 * (s & 1)
+                      : (D / 4) * grp + 8 * s;
+}
+// Channel of row i of output tile t (row i of the V^T operand).  u4: a
+// dword of the [channel pair][key] tile gives channel 2c in its low
+// nibbles and 2c + 1 in its high ones: tiles 2u and 2u + 1 take the even
+// and odd channels of pairs 16u .. 16u + 15.
+template <int F>
+__device__ __forceinline__ int dec_vchan(int t, int i) {
+  return F == kKvU4 ? 2 * (16 * (t >> 1) + i) + (t & 1) : 16 * t + i;
 }
 
-// LDS staging of one block-head: K (16 keys x D elements), then for u8
-// V^T (D channels x 16 codes); bf16 V^T fragments load straight into
-// registers (each of their loads already reads whole cache lines).  16-byte
-// chunks; K chunk c of key r sits at slot r * CPR + (c ^ x(r)), so the 8
-// lanes that read a 128-byte LDS row together (same chunk, keys r..r+7) hit
-// 8 different bank quads, while each copy instruction still reads 1 KB of
-// whole key rows.
-template <int D, bool U8>
+// LDS staging of one block-head: K (16 keys x D codes or elements), then
+// for u8 / u4 the V^T tile (as many bytes again); bf16 V^T fragments load
+// straight into registers (each of their loads already reads whole cache
+// lines).  16-byte chunks; K chunk c of key r sits at slot r * CPR + (c ^
+// x(r)), so the 8 lanes that read a 128-byte LDS row together (same chunk,
+// keys r..r+7) hit 8 different bank quads, while each copy instruction
+// still reads 1 KB of whole key rows.  (u4 with D = 64: 32-byte rows, read
+// 8 bytes per lane, not swizzled.)
+template <int D, int F>
 struct DecStage {
-  static constexpr int kRow = D * (U8 ? 1 : 2);    // bytes per key row
+  static constexpr int kRow = F == kKvBf16 ? 2 * D : F == kKvU8 ? D : D / 2;  // bytes per key row
   static constexpr int kK = kBlockTokens * kRow;   // K bytes
-  static constexpr int kV = U8 ? kBlockTokens * D : 0;
+  static constexpr int kV = F == kKvBf16 ? 0 : kK; // V^T bytes ([D or D/2][16] bytes)
   static constexpr int kBytes = kK + kV;
-  static constexpr int kInstK = kK / 1024;         // copy instructions
-  static constexpr int kInstV = kV / 1024;
+  static constexpr int kInst = kBytes / 1024;      // copy instructions
   static constexpr int CPR = kRow / 16;            // chunks per key row
-  static_assert(CPR >= 4 && kK % 1024 == 0, "head dim");
-  __device__ static int x(int r) { return CPR >= 8 ? (r & 7) : ((r >> 1) & 3); }
+  static_assert(CPR >= 2 && kBytes % 1024 == 0, "head dim");
+  __device__ static int x(int r) { return CPR >= 8 ? (r & 7) : CPR == 4 ? ((r >> 1) & 3) : 0; }
   __device__ static int k_slot(int r, int c) { return r * CPR + (c ^ x(r)); }
   // source byte offset of the chunk that goes to slot s
   __device__ static int k_src(int s) {
@@ -392,18 +411,18 @@ struct DecStage {
   }
 };
 constexpr int kDecStages = 3;  // blocks per wave in rotation (one read, two in flight)
-template <int D, bool U8>
+template <int D, int F>
 constexpr int dec_stage_array_bytes() {
   constexpr int o = 2 * D * 16 * 4;  // two waves' O^T tiles
-  constexpr int st = 4 * DecStage<D, U8>::kBytes;
+  constexpr int st = 4 * DecStage<D, F>::kBytes;
   return o > st ? o : st;
 }
 
 // bf16 V^T fragments straight from the pool into registers
-template <int D, bool U8>
-__device__ __forceinline__ void dec_load_v(DecFrags<D, U8>& f, const DecArgs& a, int phys, int g,
+template <int D, int F>
+__device__ __forceinline__ void dec_load_v(DecFrags<D, F>& f, const DecArgs& a, int phys, int g,
                                            int col, int grp) {
-  static_assert(!U8, "u8 blocks are staged through LDS whole");
+  static_assert(F == kKvBf16, "code blocks are staged through LDS whole");
   const size_t hb = ((size_t)phys * a.Hkv + g) * (kBlockTokens * D);
   const bf16* vb = (const bf16*)a.pool.v + hb;
 #pragma unroll
@@ -430,15 +449,40 @@ __device__ __forceinline__ f16x4 u8x4_to_f16_biased(uint32_t w) {
   return __builtin_bit_cast(f16x4, r);
 }
 
-template <int D, bool U8>
+// u4 codes as fp16 operands: a code c in the high nibble of a byte under
+// the byte 0x54 is the fp16 value 2^6 * (1 + 16c / 1024) = 64 + c exactly
+// (unit spacing in [64, 128)); the bias 64 goes into the zero points.  A
+// dword of 8 codes holds channels b (low nibble) and 4 + b (high) in byte b.
+constexpr float kU4Bias = 64.f;
+__device__ __forceinline__ uint32_t u4x2_biased(uint32_t hi_nibbles, uint32_t sel) {
+  return __builtin_amdgcn_perm(0x54545454u, hi_nibbles, sel);
+}
+__device__ __forceinline__ f16x8 u4x8_to_f16_biased(uint32_t w) {
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4v;
+  const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
+  const u32x4v r = {u4x2_biased(lo, 0x04010400u), u4x2_biased(lo, 0x04030402u),
+                    u4x2_biased(hi, 0x04010400u), u4x2_biased(hi, 0x04030402u)};
+  return __builtin_bit_cast(f16x8, r);
+}
+// the low (n = 0) or high (n = 1) nibbles of the 4 bytes, in byte order
+__device__ __forceinline__ f16x4 u4x4_to_f16_biased(uint32_t w, int n) {
+  const uint32_t x = (n ? w : w << 4) & 0xF0F0F0F0u;
+  const u32x2 r = {u4x2_biased(x, 0x04010400u), u4x2_biased(x, 0x04030402u)};
+  return __builtin_bit_cast(f16x4, r);
+}
+
+template <int D, int F>
 __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
+  constexpr bool Q = F != kKvBf16;  // codes with per-channel scale / zero point
+  constexpr bool U4 = F == kKvU4;
+  constexpr float kBias = U4 ? kU4Bias : kU8Bias;
   constexpr int NT = D / 16;  // 16-channel tiles of the output
   __shared__ float sm_m[4][16], sm_l[4][16];
   // Stage j of every wave's block rotation lives in its own array, so
   // the compiler can tell a wave's reads of one stage from the copies still
   // landing in the others (one array would make every read wait for all
   // copies).  After the loop st0 / st1 hold the four waves' accumulators.
-  constexpr int SZ = dec_stage_array_bytes<D, U8>();
+  constexpr int SZ = dec_stage_array_bytes<D, F>();
   __shared__ __attribute__((aligned(16))) uint8_t st0[SZ];
   __shared__ __attribute__((aligned(16))) uint8_t st1[SZ];
   __shared__ __attribute__((aligned(16))) uint8_t st2[SZ];
@@ -462,13 +506,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 
   // query fragments (B operand of S^T = K Q^T): q[head col][channels of
   // dec_kchan], carried as a pair hi + lo so the fp32 query keeps its
-  // precision (MFMA time is free here).  bf16 cache: bf16 pairs.  u8 cache:
-  // fp16 pairs of q' = q * k_scale * 2^e (the K scale folded in, 2^e puts
-  // the head's largest |q'| in [128, 256) and comes back out through the
-  // score scale); the codes enter as 1024 + c, so the zero point and bias
-  // enter through corr = sum_d q'[d] * (1024 + zp[d]) in fp32.
-  using QT = typename std::conditional<U8, f16x8, bf16x8>::type;
-  using PT = typename std::conditional<U8, f16x4, bf16x4>::type;
+  // precision (MFMA time is free here).  bf16 cache: bf16 pairs.  u8 / u4
+  // cache: fp16 pairs of q' = q * k_scale * 2^e (the K scale folded in, 2^e
+  // puts the head's largest |q'| in [128, 256) and comes back out through
+  // the score scale); the codes enter as bias + c, so the zero point and
+  // bias enter through corr = sum_d q'[d] * (bias + zp[d]) in fp32.
+  using QT = typename std::conditional<Q, f16x8, bf16x8>::type;
+  using PT = typename std::conditional<Q, f16x4, bf16x4>::type;
   QT qf[D / 32];
   QT qlo[D / 32];
   float corr = 0.f;
@@ -482,21 +526,21 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[s][e] = 0.f;
       if (head_ok) {
-        const float* qs = qp + dec_kchan<U8>(s, grp);
+        const float* qs = qp + dec_kchan<D, F>(s, grp);
         const float4 x0 = *(const float4*)qs, x1 = *(const float4*)(qs + 4);
         qv[s][0] = x0.x; qv[s][1] = x0.y; qv[s][2] = x0.z; qv[s][3] = x0.w;
         qv[s][4] = x1.x; qv[s][5] = x1.y; qv[s][6] = x1.z; qv[s][7] = x1.w;
       }
-      if constexpr (U8) {
+      if constexpr (Q) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          qv[s][e] *= a.pool.k_scale[g * D + dec_kchan<U8>(s, grp) + e];
+          qv[s][e] *= a.pool.k_scale[g * D + dec_kchan<D, F>(s, grp) + e];
           amax = fmaxf(amax, fabsf(qv[s][e]));
         }
       }
     }
     float qscale = 1.f;
-    if constexpr (U8) {
+    if constexpr (Q) {
       amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
       int ex = 0;
@@ -511,8 +555,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float qs = qv[s][e] * qscale;
-        if constexpr (U8) {
-          corr += qs * (kU8Bias + (float)a.pool.k_zp[g * D + dec_kchan<U8>(s, grp) + e]);
+        if constexpr (Q) {
+          corr += qs * (kBias + (float)a.pool.k_zp[g * D + dec_kchan<D, F>(s, grp) + e]);
           hi[e] = (_Float16)qs;
           lo[e] = (_Float16)(qs - (float)hi[e]);
         } else {
@@ -523,7 +567,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       qf[s] = hi;
       qlo[s] = lo;
     }
-    if constexpr (U8) {
+    if constexpr (Q) {
       corr += __shfl_xor(corr, 16, 64);
       corr += __shfl_xor(corr, 32, 64);
     }
@@ -552,7 +596,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   for (int h = 0; h < 2; ++h)
     if (64 * h + lane < cnt) my_phys[h] = seq_block(a.seq, sidx, blk0 + wave + 4 * (64 * h + lane));
 
-  auto compute = [&](const DecFrags<D, U8>& f, int i) {
+  auto compute = [&](const DecFrags<D, F>& f, int i) {
     const int blk = blk0 + wave + 4 * i;
     // S^T[key][head]: A = K rows (key = lane%16), B = Q^T (hi + lo, two
     // independent accumulation chains)
@@ -560,7 +604,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       QT kf;
-      if constexpr (U8) {
+      if constexpr (U4) {
+        kf = u4x8_to_f16_biased(reinterpret_cast<const uint32_t*>(&f.k[0])[s]);
+      } else if constexpr (Q) {
         const uint4 w = f.k[s >> 1];
         kf = (s & 1) ? u8x8_to_f16_biased(w.z, w.w) : u8x8_to_f16_biased(w.x, w.y);
       } else {
@@ -610,7 +656,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float pv = exp2f(sv[r] - m_run);
-      if constexpr (U8) {
+      if constexpr (Q) {
         pf[r] = (_Float16)pv;
         pl[r] = (_Float16)(pv - (float)pf[r]);
       } else {
@@ -623,7 +669,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       PT vf;
-      if constexpr (U8) {
+      if constexpr (U4) {
+        vf = u4x4_to_f16_biased(f.v[t >> 1], t & 1);  // finite, so P = 0 cancels unwritten slots
+      } else if constexpr (Q) {
         vf = u8x4_to_f16_biased(f.v[t]);  // finite, so P = 0 cancels unwritten slots
       } else {
         vf = f.v[t];
@@ -643,20 +691,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   // vector-memory operations in program order; the scheduling barriers keep
   // the compiler from moving loads or their uses across them.
   {
-    // K (and u8 V) blocks go to LDS as whole cache lines (16 bytes per lane,
+    // K (and u8 / u4 V) blocks go to LDS as whole cache lines (16 bytes per lane,
     // 1 KB per instruction; kDecStages blocks per wave in rotation) and the
     // fragments are read back from there.  Read in place as register
     // fragments, K would cost 2-4x the cache-line requests (a fragment load
     // takes 32-64 bytes of each of 16 key rows), and requests, not bytes,
     // bound this kernel.
-    using St = DecStage<D, U8>;
+    using St = DecStage<D, F>;
     constexpr int NB = kDecStages;
-    constexpr int LOADS = St::kInstK + (U8 ? St::kInstV : D / 16);
+    constexpr int LOADS = St::kInst + (Q ? 0 : D / 16);
     constexpr int kWaitIn = (NB - 2) * LOADS;  // blocks i+1 .. i+NB-2 may be in flight
     constexpr int kWait = (kWaitIn & 15) | (7 << 4) | (15 << 8) | (((kWaitIn >> 4) & 3) << 14);
     static_assert(NB == 3, "one LDS array per stage");
     auto stage = [&](int j) { return (j == 0 ? st0 : j == 1 ? st1 : st2) + wave * St::kBytes; };
-    DecFrags<D, U8> fv[U8 ? 1 : NB];  // bf16: V^T register sets in rotation
+    DecFrags<D, F> fv[Q ? 1 : NB];  // bf16: V^T register sets in rotation
     if (cnt > 0) {
       auto phys_of = [&](int i) {
         i = min(i, cnt - 1);  // wave-uniform
@@ -666,20 +714,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
         const int phys = phys_of(i);
         const size_t hb = ((size_t)phys * a.Hkv + g) * (kBlockTokens * St::kRow);
         const uint8_t* kb = (const uint8_t*)a.pool.k + hb;
+        const uint8_t* vb = (const uint8_t*)a.pool.v + hb;  // V^T tile, same size (codes)
         uint8_t* kd = stage(buf);
+        // stage byte o = 1024j + 16 lane comes from K (swizzled) while o <
+        // kK, then from V^T in order (u4 with D = 64: both in one copy)
 #pragma unroll
-        for (int j = 0; j < St::kInstK; ++j)
-          __builtin_amdgcn_global_load_lds((const void*)(kb + St::k_src(64 * j + lane)),
-                                           (lds_void*)(kd + 1024 * j), 16, 0, 0);
-        if constexpr (U8) {
-          const uint8_t* vb = (const uint8_t*)a.pool.v + hb;
-#pragma unroll
-          for (int j = 0; j < St::kInstV; ++j)
-            __builtin_amdgcn_global_load_lds((const void*)(vb + 1024 * j + 16 * lane),
-                                             (lds_void*)(kd + St::kK + 1024 * j), 16, 0, 0);
-        } else {
-          dec_load_v<D, U8>(fv[buf], a, phys, g, col, grp);
+        for (int j = 0; j < St::kInst; ++j) {
+          const int o = 1024 * j + 16 * lane;
+          const bool in_k = St::kK % 1024 == 0 ? 1024 * j < St::kK : o < St::kK;
+          const uint8_t* src = in_k ? kb + St::k_src(o / 16) : vb + (o - St::kK);
+          __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(kd + 1024 * j), 16, 0, 0);
         }
+        if constexpr (!Q) dec_load_v<D, F>(fv[buf], a, phys, g, col, grp);
       };
 #pragma unroll
       for (int j = 0; j < NB - 1; ++j) issue(j, j);
@@ -693,13 +739,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
           __builtin_amdgcn_sched_barrier(0);
           if (j == 0 || i + j < cnt) {
             const uint8_t* kd = stage(j);
-            DecFrags<D, U8> f;
+            DecFrags<D, F> f;
+            using KT = typename DecFrags<D, F>::KT;
+            if constexpr (St::CPR == 2) {  // u4, D = 64: 8 bytes of the 32-byte row
+              f.k[0] = *(const KT*)(kd + col * St::kRow + 8 * grp);
+            } else {
 #pragma unroll
-            for (int h = 0; h < St::kRow / 64; ++h)
-              f.k[h] = *(const typename DecFrags<D, U8>::KT*)(kd + St::k_slot(col, 4 * h + grp) * 16);
-            if constexpr (U8) {
+              for (int h = 0; h < St::kRow / 64; ++h)
+                f.k[h] = *(const KT*)(kd + St::k_slot(col, 4 * h + grp) * 16);
+            }
+            if constexpr (Q) {
 #pragma unroll
-              for (int t = 0; t < D / 16; ++t)
+              for (int t = 0; t < (U4 ? D / 32 : D / 16); ++t)
                 f.v[t] = *(const uint32_t*)(kd + St::kK + (16 * t + col) * 16 + 4 * grp);
             } else {
 #pragma unroll
@@ -714,7 +765,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     __syncthreads();  // every wave is done with its stages before they take the accumulators
   }
 
-  // ---- merge the four waves: acc[t][r] = O^T[16t + 4grp + r][head col]
+  // ---- merge the four waves: acc[t][r] = O^T[dec_vchan(t, 4grp + r)][head col]
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (lane < 16) {
@@ -724,7 +775,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o_tile(wave)[o_idx(16 * t + 4 * grp + r, col)] = acc[t][r];
+    for (int r = 0; r < 4; ++r) o_tile(wave)[o_idx(dec_vchan<F>(t, 4 * grp + r), col)] = acc[t][r];
   __syncthreads();
 
   float* pp = a.part + (((size_t)b * a.Hkv + g) * a.max_parts + p) * kPartStride(D);
@@ -741,9 +792,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       O += o_tile(w)[o_idx(d, hh)] * f;
       L += sm_l[w][hh] * f;
     }
-    if constexpr (U8) {
+    if constexpr (Q) {
       const int ch = g * D + d;
-      O = a.pool.v_scale[ch] * (O - (kU8Bias + (float)a.pool.v_zp[ch]) * L);
+      O = a.pool.v_scale[ch] * (O - (kBias + (float)a.pool.v_zp[ch]) * L);
     }
     if (n_parts == 1) {
       a.o[(size_t)row * a.Hq * D + (size_t)(g * n_rep + hh) * D + d] = to_f16(O / L);
@@ -835,18 +886,19 @@ hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, int n_prefill, 
   return hipErrorInvalidValue;
 }
 
-DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len, bool u8) {
+DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len, int fmt) {
   (void)Hq;
   DecodePlan pl{};
   const int max_blk = cdiv(max_ctx_len, kBlockTokens);
   // Parts per sequence (for the longest one; each sequence is cut into
   // near-equal parts of at most part_blocks blocks).  Measured on ragged
   // batches: enough (sequence, KV head) pairs x parts for one workgroup per
-  // CU, and no part above ~2 MB of cache (257 bf16 / 171 u8 blocks of a
-  // 128-wide head; u8 blocks cost more compute per byte); more, shorter
-  // parts only add workgroup start-up, partial writes and the merge.
+  // CU, and no part above ~2 MB of cache (257 bf16 / 171 u8 or u4 blocks
+  // of a 128-wide head; code blocks cost more compute per byte, and u4
+  // timings hardly move between 128 and 257); more, shorter parts only add
+  // workgroup start-up, partial writes and the merge.
   const int pairs = batch * Hkv;
-  const int cap = std::min(kMaxPartBlocks, (u8 ? 171 : 257) * 128 / D);
+  const int cap = std::min(kMaxPartBlocks, (fmt == kKvBf16 ? 257 : 171) * 128 / D);
   int parts = std::max(cdiv(256, pairs), cdiv(max_blk, cap));
   parts = std::max(1, std::min(parts, max_blk));
   int pb = cdiv(max_blk, parts);
@@ -867,13 +919,11 @@ hipError_t attn_decode(const DecodePlan& pl, const void* q, KvPool pool, SeqInfo
   DecArgs a{(const float*)q, pool, seq, first_seq, Hq, Hkv, pl.part_blocks, pl.max_parts, part,
             (f16*)o};
   dim3 grid(Hkv, batch, pl.max_parts);
-  if (D == 128) {
-    if (pool.u8) attn_decode_kernel<128, true><<<grid, 256, 0, s>>>(a);
-    else attn_decode_kernel<128, false><<<grid, 256, 0, s>>>(a);
-  } else {
-    if (pool.u8) attn_decode_kernel<64, true><<<grid, 256, 0, s>>>(a);
-    else attn_decode_kernel<64, false><<<grid, 256, 0, s>>>(a);
-  }
+#define TDL_DECODE_CASE(DD, FF) \
+  if (D == DD && pool.fmt == FF) attn_decode_kernel<DD, FF><<<grid, 256, 0, s>>>(a);
+  TDL_DECODE_CASE(128, kKvBf16) TDL_DECODE_CASE(128, kKvU8) TDL_DECODE_CASE(128, kKvU4)
+  TDL_DECODE_CASE(64, kKvBf16) TDL_DECODE_CASE(64, kKvU8) TDL_DECODE_CASE(64, kKvU4)
+#undef TDL_DECODE_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.max_parts == 1) return e;
   dim3 mgrid(Hkv, batch);

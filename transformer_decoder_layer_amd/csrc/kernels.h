@@ -105,10 +105,17 @@ struct SeqInfo {
   int rows_are_seqs;  // 1: row r is sequence r with one new token at ctx_len[r]
 };
 
+// Cache element formats.  u4 packs two codes per byte, low nibble first:
+// byte 4j + b of a K row (one token, D/2 bytes) holds channels 8j + b and
+// 8j + 4 + b; byte (c, slot) of a V block-head tile [D/2][16] holds channels
+// 2c and 2c + 1 of that token.  Every byte belongs to one token, so writers
+// of different tokens never share a byte.
+enum KvFmt : int { kKvBf16 = 0, kKvU8 = 1, kKvU4 = 2 };
+
 struct KvPool {
-  void* k;          // [blocks][Hkv][16][D]
-  void* v;          // [blocks][Hkv][D][16]
-  int u8;           // 0: bf16 elements, 1: uint8 codes
+  void* k;          // [blocks][Hkv][16][D] (u4: [blocks][Hkv][16][D/2] bytes)
+  void* v;          // [blocks][Hkv][D][16] (u4: [blocks][Hkv][D/2][16] bytes)
+  int fmt;          // KvFmt
   const float* k_scale;
   const int* k_zp;
   const float* v_scale;
@@ -129,9 +136,10 @@ hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, cons
 // Writes caller K/V rows into the pool (kv_cache_write).
 hipError_t kv_write_rows(const void* k, const void* v, int src_f32, int rows, int Hkv, int D,
                          SeqInfo seq, KvPool pool, hipStream_t s);
-// Per-channel min/max -> scale / zero point (kv_cache_calibrate).
-hipError_t kv_calibrate(const float* x, int64_t n_tokens, int channels, float* scale, int* zp,
-                        hipStream_t s);
+// Per-channel min/max -> scale = (max - min) / levels, zero point
+// (kv_cache_calibrate; levels 255 for u8 codes, 15 for u4).
+hipError_t kv_calibrate(const float* x, int64_t n_tokens, int channels, int levels, float* scale,
+                        int* zp, hipStream_t s);
 
 // cos/sin table of RoPE angles pos * theta^(-2i/D), formed in float64.
 hipError_t rope_table_build(float2* tab, int max_pos, int D, double theta, hipStream_t s);
@@ -182,7 +190,7 @@ struct DecodePlan {
   size_t part_floats;        // partial-result workspace of this launch
   size_t part_floats_bound;  // >= part_floats of any max_ctx_len up to this one
 };
-DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len, bool u8);
+DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len, int fmt);
 hipError_t attn_decode(const DecodePlan& plan, const void* q, KvPool pool, SeqInfo seq,
                        int first_seq, int batch, int Hq, int Hkv, int D, void* o, float* part,
                        hipStream_t s);

@@ -80,29 +80,40 @@ __device__ __forceinline__ int block_of(const SeqInfo& s, int seq, int pos) {
   return s.tables[(size_t)seq * s.max_blocks + pos / kBlockTokens];
 }
 
-// Quantise one value: clamp(round_half_even(x / scale) + zp, 0, 255), with a
-// correctly rounded fp32 divide.
-__device__ __forceinline__ uint8_t quant_u8(float x, float scale, int zp) {
+// Quantise one value: clamp(round_half_even(x / scale) + zp, 0, top), with a
+// correctly rounded fp32 divide (top 255 for u8 codes, 15 for u4).
+__device__ __forceinline__ int quant_code(float x, float scale, int zp, int top) {
   const float q = __builtin_rintf(__fdiv_rn(x, scale));
-  int c = (int)q + zp;
-  c = c < 0 ? 0 : (c > 255 ? 255 : c);
-  return (uint8_t)c;
+  const int c = (int)q + zp;
+  return c < 0 ? 0 : (c > top ? top : c);
 }
 
+// bf16 / u8 pools: one element per (slot, d)
 __device__ __forceinline__ void store_kv(const KvPool& pool, int blk, int g, int Hkv, int D, int slot,
                                          int d, float kval, float vval) {
   const size_t head = ((size_t)blk * Hkv + g) * kBlockTokens * D;
   const size_t kidx = head + (size_t)slot * D + d;   // K: [blk][g][slot][d]
   const size_t vidx = head + (size_t)d * kBlockTokens + slot;  // V: [blk][g][d][slot]
-  if (pool.u8) {
+  if (pool.fmt == kKvU8) {
     const int ch = g * D + d;
-    ((uint8_t*)pool.k)[kidx] = quant_u8(kval, pool.k_scale[ch], pool.k_zp[ch]);
-    ((uint8_t*)pool.v)[vidx] = quant_u8(vval, pool.v_scale[ch], pool.v_zp[ch]);
+    ((uint8_t*)pool.k)[kidx] = (uint8_t)quant_code(kval, pool.k_scale[ch], pool.k_zp[ch], 255);
+    ((uint8_t*)pool.v)[vidx] = (uint8_t)quant_code(vval, pool.v_scale[ch], pool.v_zp[ch], 255);
   } else {
     ((bf16*)pool.k)[kidx] = f32_to_bf16(kval);
     ((bf16*)pool.v)[vidx] = f32_to_bf16(vval);
   }
 }
+
+// u4 pools: byte offsets of a block-head tile (8*D bytes for K and for V)
+__device__ __forceinline__ size_t u4_head(int blk, int g, int Hkv, int D) {
+  return ((size_t)blk * Hkv + g) * kBlockTokens * (D / 2);
+}
+// K byte of channel d (d & 4 == 0; its partner d + 4 is the high nibble)
+__device__ __forceinline__ int u4_kbyte(int slot, int d, int D) {
+  return slot * (D / 2) + 4 * (d >> 3) + (d & 3);
+}
+// V byte of channel d (d even; its partner d + 1 is the high nibble)
+__device__ __forceinline__ int u4_vbyte(int slot, int d) { return (d >> 1) * kBlockTokens + slot; }
 
 // ------------------------------------------------ Q/K-norm + RoPE + KV
 // One workgroup (4 waves) per row; each wave takes one head at a time: the
@@ -164,17 +175,46 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     }
     const float r1 = x1 * cs.x - x2 * cs.y;
     const float r2 = x1 * cs.y + x2 * cs.x;
+    if (is_q) {  // wave-uniform
+      if (act) {
+        float* qo = q_out + ((size_t)row * Hq + h) * D;
+        qo[lane] = r1;
+        qo[lane + half] = r2;
+      }
+      continue;
+    }
+    const int g = h - Hq;
+    const int vc = (Hq + Hkv + g) * D;
+    const float v1 = val(vc + ln), v2 = val(vc + ln + half);
+    if (pool.fmt != kKvU4) {
+      if (act) {
+        store_kv(pool, blk, g, Hkv, D, slot, lane, r1, v1);
+        store_kv(pool, blk, g, Hkv, D, slot, lane + half, r2, v2);
+      }
+      continue;
+    }
+    // u4: lane i holds channels i and i + D/2; a byte pairs channels d, d + 4
+    // (K) or d, d + 1 (V), whose codes sit in lanes i ^ 4 / i ^ 1 (D/2 is a
+    // multiple of 8, so partners of active lanes are active).  Every lane
+    // takes part in the exchange.
+    const int c1 = g * D + ln, c2 = c1 + half;
+    const int k1 = quant_code(r1, pool.k_scale[c1], pool.k_zp[c1], 15);
+    const int k2 = quant_code(r2, pool.k_scale[c2], pool.k_zp[c2], 15);
+    const int w1 = quant_code(v1, pool.v_scale[c1], pool.v_zp[c1], 15);
+    const int w2 = quant_code(v2, pool.v_scale[c2], pool.v_zp[c2], 15);
+    const int pk1 = __shfl_xor(k1, 4, 64), pk2 = __shfl_xor(k2, 4, 64);
+    const int pw1 = __shfl_xor(w1, 1, 64), pw2 = __shfl_xor(w2, 1, 64);
     if (!act) continue;
-    if (is_q) {
-      float* qo = q_out + ((size_t)row * Hq + h) * D;
-      qo[lane] = r1;
-      qo[lane + half] = r2;
-    } else {
-      const int g = h - Hq;
-      const int vc = (Hq + Hkv + g) * D;
-      const float v1 = val(vc + ln), v2 = val(vc + ln + half);
-      store_kv(pool, blk, g, Hkv, D, slot, lane, r1, v1);
-      store_kv(pool, blk, g, Hkv, D, slot, lane + half, r2, v2);
+    const size_t hb = u4_head(blk, g, Hkv, D);
+    uint8_t* kp = (uint8_t*)pool.k + hb;
+    uint8_t* vp = (uint8_t*)pool.v + hb;
+    if (!(lane & 4)) {
+      kp[u4_kbyte(slot, lane, D)] = (uint8_t)(k1 | (pk1 << 4));
+      kp[u4_kbyte(slot, lane + half, D)] = (uint8_t)(k2 | (pk2 << 4));
+    }
+    if (!(lane & 1)) {
+      vp[u4_vbyte(slot, lane)] = (uint8_t)(w1 | (pw1 << 4));
+      vp[u4_vbyte(slot, lane + half)] = (uint8_t)(w2 | (pw2 << 4));
     }
   }
 }
@@ -254,11 +294,30 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ 
   const int pos = row_position(seq, sidx, row);
   const int blk = block_of(seq, sidx, pos);
   const int slot = pos % kBlockTokens;
-  for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
-    const size_t idx = (size_t)row * Hkv * D + e;
-    const float kv = src_f32 ? ((const float*)k)[idx] : (float)((const bf16*)k)[idx];
-    const float vv = src_f32 ? ((const float*)v)[idx] : (float)((const bf16*)v)[idx];
-    store_kv(pool, blk, e / D, Hkv, D, slot, e % D, kv, vv);
+  auto ld = [&](const void* p, size_t i) {
+    return src_f32 ? ((const float*)p)[i] : (float)((const bf16*)p)[i];
+  };
+  if (pool.fmt != kKvU4) {
+    for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
+      const size_t idx = (size_t)row * Hkv * D + e;
+      store_kv(pool, blk, e / D, Hkv, D, slot, e % D, ld(k, idx), ld(v, idx));
+    }
+    return;
+  }
+  // u4: one thread per K byte and V byte (two channels each)
+  const int hd = D / 2;
+  for (int e = threadIdx.x; e < Hkv * hd; e += blockDim.x) {
+    const int g = e / hd, i = e % hd;
+    const int dk = 8 * (i >> 2) + (i & 3), dv = 2 * i;  // low-nibble channels
+    const size_t src = (size_t)row * Hkv * D + (size_t)g * D;
+    const int ck = g * D + dk, cv = g * D + dv;
+    const int klo = quant_code(ld(k, src + dk), pool.k_scale[ck], pool.k_zp[ck], 15);
+    const int khi = quant_code(ld(k, src + dk + 4), pool.k_scale[ck + 4], pool.k_zp[ck + 4], 15);
+    const int vlo = quant_code(ld(v, src + dv), pool.v_scale[cv], pool.v_zp[cv], 15);
+    const int vhi = quant_code(ld(v, src + dv + 1), pool.v_scale[cv + 1], pool.v_zp[cv + 1], 15);
+    const size_t hb = u4_head(blk, g, Hkv, D);
+    ((uint8_t*)pool.k)[hb + u4_kbyte(slot, dk, D)] = (uint8_t)(klo | (khi << 4));
+    ((uint8_t*)pool.v)[hb + u4_vbyte(slot, dv)] = (uint8_t)(vlo | (vhi << 4));
   }
 }
 
@@ -296,11 +355,12 @@ __global__ void minmax_init(int* mn, int* mx, int C) {
 }
 // scale = (max - min) / 255 (1 for a flat channel); zp = rint(-min / scale)
 // -- the per-channel formula of the devpress engine page, section 2.6.
-__global__ void calib_finish(const int* mn, const int* mx, int C, float* scale, int* zp) {
+__global__ void calib_finish(const int* mn, const int* mx, int C, float levels, float* scale,
+                             int* zp) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= C) return;
   const float lo = ord2f(mn[c]), hi = ord2f(mx[c]);
-  float s = __fdiv_rn(hi - lo, 255.0f);
+  float s = __fdiv_rn(hi - lo, levels);
   if (s == 0.f) s = 1.0f;
   scale[c] = s;
   zp[c] = (int)__builtin_rintf(__fdiv_rn(-lo, s));
@@ -434,7 +494,8 @@ hipError_t kv_write_rows(const void* k, const void* v, int src_f32, int rows, in
   return hipGetLastError();
 }
 
-hipError_t kv_calibrate(const float* x, int64_t n, int C, float* scale, int* zp, hipStream_t s) {
+hipError_t kv_calibrate(const float* x, int64_t n, int C, int levels, float* scale, int* zp,
+                        hipStream_t s) {
   // min/max scratch lives in the zero-point array (int) and the scale array
   // reinterpreted as int until calib_finish overwrites both.
   int* mn = zp;
@@ -446,7 +507,7 @@ hipError_t kv_calibrate(const float* x, int64_t n, int C, float* scale, int* zp,
     dim3 grid((unsigned)nb, cdiv(C, 256));
     minmax_kernel<<<grid, 256, 0, s>>>(x, n, C, rows_per_block, mn, mx);
   }
-  calib_finish<<<cdiv(C, 256), 256, 0, s>>>(mn, mx, C, scale, zp);
+  calib_finish<<<cdiv(C, 256), 256, 0, s>>>(mn, mx, C, (float)levels, scale, zp);
   return hipGetLastError();
 }
 
