@@ -311,13 +311,53 @@ tdl_status kv_cache_view(const tdl_kv_cache* kv, tdl_kv_view* out);
 tdl_status kv_block_table(tdl_kv_cache* kv, int32_t n_seqs, const int32_t* n_tokens,
                           int32_t max_blocks, int32_t* table);
 
-/* Returns blocks to the free list ([HET] 4.3 release).  A block that is out
- * of range or already free fails the whole call with TDL_E_INVALID and
- * nothing is released. */
+/* Block holders ([HET] 4.3: each physical block carries a ref_count).  A
+ * block handed out by kv_block_table has one holder; kv_block_share adds
+ * one per listed entry, kv_block_release drops one per listed entry, and a
+ * block whose last holder lets go returns to the free list.  Sequences that
+ * share a block read it; only a block with one holder may be written (the
+ * kernels cannot check this: the caller appends only to blocks it holds
+ * alone).  A listed block that is out of range or free, or (release) listed
+ * more often than it has holders, fails the whole call with TDL_E_INVALID
+ * and nothing changes. */
 tdl_status kv_block_release(tdl_kv_cache* kv, const int32_t* blocks, int32_t n);
+tdl_status kv_block_share(tdl_kv_cache* kv, const int32_t* blocks, int32_t n);
+
+/* Holders of a block (0: free); -1 for a NULL handle or a block out of range. */
+int32_t kv_block_refs(const tdl_kv_cache* kv, int32_t block);
 
 /* Number of blocks on the free list. */
 int32_t kv_free_blocks(const tdl_kv_cache* kv);
+
+/* Prefix index ([HET] 4.7 prefix cache: block-aligned longest common prefix,
+ * matched blocks serve as the initial KV of a prefill at start_pos =
+ * 16 * matched).  Host-side map from a caller-chosen 64-bit key to a full
+ * block.  The key of a sequence's block i must identify every token of
+ * blocks 0..i (for example a hash chain over the token ids), because a
+ * block's K/V depend on all earlier tokens.
+ *
+ * kv_prefix_publish: block i (allocated, full, never written again) is
+ * indexed under keys[i]; the index becomes one of its holders.  A key that
+ * is already indexed keeps its block (the first publisher wins; the
+ * caller's block is left as it is).  A block indexed under another key, an
+ * entry that pairs a key or block of an earlier entry differently, or a
+ * free or out-of-range block fails the call (TDL_E_INVALID, no change).
+ *
+ * kv_prefix_match: walks keys[0..n-1] and stops at the first key not in the
+ * index; blocks[0 .. *n_matched-1] receive the matched blocks, each with one
+ * more holder (the caller, who releases them like its own).
+ *
+ * kv_prefix_evict: drops up to n_blocks index entries whose block no one
+ * but the index holds, least recently matched or published first; their
+ * blocks return to the free list.  Returns the number dropped.
+ *
+ * kv_prefix_size: entries in the index. */
+tdl_status kv_prefix_publish(tdl_kv_cache* kv, const uint64_t* keys, const int32_t* blocks,
+                             int32_t n);
+tdl_status kv_prefix_match(tdl_kv_cache* kv, const uint64_t* keys, int32_t n, int32_t* blocks,
+                           int32_t* n_matched);
+int32_t kv_prefix_evict(tdl_kv_cache* kv, int32_t n_blocks);
+int32_t kv_prefix_size(const tdl_kv_cache* kv);
 
 /* TDL_U8_ASYM / TDL_U4_ASYM only: sets the per-channel (kv head, d)
  * parameters of K and of V from n_tokens float32 rows k, v [n_tokens, Hkv,

@@ -181,6 +181,84 @@ def test_block_release_errors():
     assert kv.free_blocks() == 5
 
 
+def test_block_sharing_holders():
+    # [HET 4.3]: blocks carry a holder count; a block returns to the free
+    # list when its last holder releases it
+    import transformer_decoder_layer_amd as tdl
+    kv = tdl.KvCache.host_only(6, 2, 64)
+    t = kv.block_table([40], 3)                 # blocks 0, 1, 2
+    assert [kv.refs(b) for b in range(6)] == [1, 1, 1, 0, 0, 0]
+    kv.share([0, 1, 1])                         # a second sequence takes 0 and 1; 1 twice
+    assert [kv.refs(b) for b in range(3)] == [2, 3, 1]
+    with pytest.raises(tdl.TdlError):
+        kv.share([0, 4])                        # 4 is free: nothing changes
+    assert kv.refs(0) == 2 and kv.refs(4) == 0
+    with pytest.raises(tdl.TdlError):
+        kv.release([2, 2])                      # more often than it is held
+    assert kv.refs(2) == 1 and kv.free_blocks() == 3
+    kv.release(t[0].tolist())                   # the first sequence lets go
+    assert [kv.refs(b) for b in range(3)] == [1, 2, 0] and kv.free_blocks() == 4
+    kv.release([1, 1, 0])
+    assert kv.free_blocks() == 6 and all(kv.refs(b) == 0 for b in range(6))
+    assert kv.refs(6) == -1 and kv.refs(-1) == -1
+    # a block table entry that holds a shared block is kept, not reallocated
+    t1 = kv.block_table([16], 2)
+    kv.share(t1[0, :1].tolist())
+    t2 = np.full((1, 2), -1, np.int32)
+    t2[0, 0] = t1[0, 0]
+    kv.block_table([20], 2, t2)
+    assert t2[0, 0] == t1[0, 0] and t2[0, 1] != t1[0, 0] and kv.refs(int(t1[0, 0])) == 2
+
+
+def test_prefix_index_match_publish_evict():
+    # [HET 4.7]: block-aligned longest-prefix matching; a hit gives the
+    # caller a hold on the block; idle entries go least recently used first
+    import transformer_decoder_layer_amd as tdl
+    kv = tdl.KvCache.host_only(10, 2, 64)
+    a = kv.block_table([64], 4)[0]              # 4 full blocks of sequence A
+    keys = [101, 102, 103, 104]
+    kv.prefix_publish(keys, a)
+    assert kv.prefix_size() == 4 and all(kv.refs(int(b)) == 2 for b in a)
+    # B shares A's first three blocks, then diverges
+    m = kv.prefix_match([101, 102, 103, 999, 104])
+    assert m.tolist() == a[:3].tolist()
+    assert [kv.refs(int(b)) for b in a] == [3, 3, 3, 2]
+    assert kv.prefix_match([555, 101]).size == 0  # the prefix ends at the first miss
+    # publishing again: same pairs refresh; a known key keeps its block
+    kv.prefix_publish(keys[:2], a[:2])
+    other = kv.block_table([16], 1)[0]
+    kv.prefix_publish([104], other)             # first publisher wins
+    assert kv.refs(int(other[0])) == 1 and kv.prefix_match([101, 102, 103, 104])[3] == a[3]
+    kv.release(a[:4].tolist())                  # undo that last match
+    with pytest.raises(tdl.TdlError):
+        kv.prefix_publish([777], a[:1])         # block 0 is indexed under 101
+    with pytest.raises(tdl.TdlError):
+        kv.prefix_publish([778, 778], [int(other[0]), int(a[3])])  # one key, two blocks
+    with pytest.raises(tdl.TdlError):
+        kv.prefix_publish([779], [9])           # a free block
+    assert kv.prefix_size() == 4
+    # A finishes: its blocks stay cached (the index holds them); B still
+    # holds the first three, so only block a[3] is idle
+    kv.release(a.tolist())
+    assert [kv.refs(int(b)) for b in a] == [2, 2, 2, 1]
+    free0 = kv.free_blocks()
+    assert kv.prefix_evict(10) == 1 and kv.free_blocks() == free0 + 1
+    assert kv.prefix_match([104]).size == 0 and kv.prefix_size() == 3
+    kv.release(m.tolist())                      # B finishes
+    # all idle now; a match refreshes 102, so 101 and 103 go first
+    kv.release(kv.prefix_match([101, 102]).tolist())
+    kv.prefix_match([102])
+    kv.release(a[1:2].tolist())
+    assert kv.prefix_evict(2) == 2
+    assert kv.prefix_size() == 1 and kv.prefix_match([101]).size == 0
+    hit = kv.prefix_match([102])
+    assert hit.tolist() == [a[1]]
+    kv.release(hit.tolist())
+    assert kv.prefix_evict(5) == 1 and kv.prefix_size() == 0
+    kv.release(other.tolist())
+    assert kv.free_blocks() == 10
+
+
 def test_seeded_free_list_is_a_permutation():
     import transformer_decoder_layer_amd as tdl
     kv = tdl.KvCache.host_only(300, 2, 64, seed=1234)

@@ -31,7 +31,8 @@ P_i32 = ctypes.POINTER(ctypes.c_int32)
 EXPORTS = ["layer_create", "layer_destroy", "layer_prefill", "layer_decode_paged", "layer_step",
            "layer_workspace_view", "layer_profile_enable", "layer_profile_read", "stack_create",
            "stack_destroy", "stack_decode_paged", "kv_cache_bytes", "kv_cache_alloc", "kv_cache_free",
-           "kv_cache_view", "kv_block_table", "kv_block_release", "kv_free_blocks",
+           "kv_cache_view", "kv_block_table", "kv_block_release", "kv_block_share", "kv_block_refs",
+           "kv_free_blocks", "kv_prefix_publish", "kv_prefix_match", "kv_prefix_evict", "kv_prefix_size",
            "kv_cache_calibrate", "kv_cache_write", "tdl_status_string", "tdl_last_error"]
 
 
@@ -105,6 +106,13 @@ _kv_view = _sig("kv_cache_view", c_i32, c_vp, ctypes.POINTER(KvView))
 _kv_table = _sig("kv_block_table", c_i32, c_vp, c_i32, P_i32, c_i32, P_i32)
 _kv_release = _sig("kv_block_release", c_i32, c_vp, P_i32, c_i32)
 _kv_free_blocks = _sig("kv_free_blocks", c_i32, c_vp)
+_kv_share = _sig("kv_block_share", c_i32, c_vp, P_i32, c_i32)
+_kv_refs = _sig("kv_block_refs", c_i32, c_vp, c_i32)
+P_u64 = ctypes.POINTER(ctypes.c_uint64)
+_kv_publish = _sig("kv_prefix_publish", c_i32, c_vp, P_u64, P_i32, c_i32)
+_kv_match = _sig("kv_prefix_match", c_i32, c_vp, P_u64, c_i32, P_i32, P_i32)
+_kv_evict = _sig("kv_prefix_evict", c_i32, c_vp, c_i32)
+_kv_prefix_size = _sig("kv_prefix_size", c_i32, c_vp)
 _kv_calibrate = _sig("kv_cache_calibrate", c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_int64)
 _kv_write = _sig("kv_cache_write", c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp,
                  c_vp, c_i32)
@@ -215,6 +223,35 @@ class KvCache:
 
     def free_blocks(self) -> int:
         return _kv_free_blocks(self._h)
+
+    def share(self, blocks: Sequence[int]):
+        b = _host_i32(blocks)
+        _check("kv_block_share", _kv_share(self._h, _i32p(b), len(b)))
+
+    def refs(self, block: int) -> int:
+        return _kv_refs(self._h, int(block))
+
+    def prefix_publish(self, keys: Sequence[int], blocks: Sequence[int]):
+        k = np.ascontiguousarray(keys, dtype=np.uint64)
+        b = _host_i32(blocks)
+        assert len(k) == len(b)
+        _check("kv_prefix_publish", _kv_publish(self._h, k.ctypes.data_as(P_u64), _i32p(b), len(b)))
+
+    def prefix_match(self, keys: Sequence[int]) -> np.ndarray:
+        """Blocks of the longest indexed prefix of ``keys`` (the caller now
+        holds each of them once)."""
+        k = np.ascontiguousarray(keys, dtype=np.uint64)
+        out = np.full(len(k), -1, np.int32)
+        m = c_i32(0)
+        _check("kv_prefix_match", _kv_match(self._h, k.ctypes.data_as(P_u64), len(k), _i32p(out),
+                                            ctypes.byref(m)))
+        return out[:m.value]
+
+    def prefix_evict(self, n_blocks: int) -> int:
+        return _kv_evict(self._h, int(n_blocks))
+
+    def prefix_size(self) -> int:
+        return _kv_prefix_size(self._h)
 
     def view(self) -> KvView:
         v = KvView()

@@ -20,6 +20,7 @@
 #include <limits>
 #include <memory>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 using namespace tdl;
@@ -68,7 +69,15 @@ struct tdl_kv_cache {
   float* v_scale = nullptr;
   int32_t* v_zp = nullptr;
   std::vector<int32_t> free_list;  // LIFO: back() is handed out next
-  std::vector<uint8_t> is_free;
+  std::vector<int32_t> refs;       // holders of each block; 0: on the free list
+  // prefix index: key -> (block, last use); the index is one of the block's holders
+  struct PrefixEntry {
+    int32_t block;
+    uint64_t used;
+  };
+  std::unordered_map<uint64_t, PrefixEntry> prefix;
+  std::unordered_map<int32_t, uint64_t> key_of;  // indexed block -> its key
+  uint64_t tick = 0;
 };
 
 struct tdl_layer {
@@ -917,7 +926,7 @@ extern "C" tdl_status kv_cache_alloc(const tdl_kv_config* cfg, void* dev_mem, td
     }
   }
   kv->free_list.assign(order.rbegin(), order.rend());
-  kv->is_free.assign(cfg->n_blocks, 1);
+  kv->refs.assign(cfg->n_blocks, 0);
   *out = kv;
   return TDL_OK;
 }
@@ -966,7 +975,7 @@ extern "C" tdl_status kv_block_table(tdl_kv_cache* kv, int32_t n_seqs, const int
     for (int b = 0; b < nb; ++b) {
       const int32_t e = table[(size_t)i * max_blocks + b];
       if (e < 0) ++need;
-      else if (e >= kv->cfg.n_blocks || kv->is_free[e])
+      else if (e >= kv->cfg.n_blocks || kv->refs[e] == 0)
         return fail(TDL_E_INVALID, "sequence %d entry %d holds block %d that is not allocated", i,
                     b, e);
     }
@@ -980,27 +989,122 @@ extern "C" tdl_status kv_block_table(tdl_kv_cache* kv, int32_t n_seqs, const int
       if (e >= 0) continue;
       e = kv->free_list.back();
       kv->free_list.pop_back();
-      kv->is_free[e] = 0;
+      kv->refs[e] = 1;
     }
   }
   return TDL_OK;
 }
 
+namespace {
+// Every listed block is allocated, and none is listed more often than it has
+// holders (when `holders` is set).
+bool check_held(const tdl_kv_cache* kv, const int32_t* blocks, int32_t n, bool holders) {
+  std::unordered_map<int32_t, int32_t> times;
+  for (int i = 0; i < n; ++i) {
+    const int32_t b = blocks[i];
+    if (b < 0 || b >= kv->cfg.n_blocks) return fail(TDL_E_INVALID, "block %d out of range", b), false;
+    if (kv->refs[b] == 0) return fail(TDL_E_INVALID, "block %d is free", b), false;
+    if (holders && ++times[b] > kv->refs[b])
+      return fail(TDL_E_INVALID, "block %d released more often than it is held", b), false;
+  }
+  return true;
+}
+void drop_hold(tdl_kv_cache* kv, int32_t b) {
+  if (--kv->refs[b] == 0) kv->free_list.push_back(b);
+}
+}  // namespace
+
 extern "C" tdl_status kv_block_release(tdl_kv_cache* kv, const int32_t* blocks, int32_t n) {
   if (!kv || (!blocks && n > 0)) return fail(TDL_E_INVALID, "NULL argument");
   if (n < 0) return fail(TDL_E_INVALID, "n < 0");
-  std::vector<uint8_t> seen(kv->cfg.n_blocks, 0);
-  for (int i = 0; i < n; ++i) {
-    const int32_t b = blocks[i];
-    if (b < 0 || b >= kv->cfg.n_blocks) return fail(TDL_E_INVALID, "block %d out of range", b);
-    if (kv->is_free[b] || seen[b]) return fail(TDL_E_INVALID, "block %d is already free", b);
-    seen[b] = 1;
+  if (!check_held(kv, blocks, n, true)) return TDL_E_INVALID;
+  for (int i = 0; i < n; ++i) drop_hold(kv, blocks[i]);
+  return TDL_OK;
+}
+
+extern "C" tdl_status kv_block_share(tdl_kv_cache* kv, const int32_t* blocks, int32_t n) {
+  if (!kv || (!blocks && n > 0)) return fail(TDL_E_INVALID, "NULL argument");
+  if (n < 0) return fail(TDL_E_INVALID, "n < 0");
+  if (!check_held(kv, blocks, n, false)) return TDL_E_INVALID;
+  for (int i = 0; i < n; ++i) ++kv->refs[blocks[i]];
+  return TDL_OK;
+}
+
+extern "C" int32_t kv_block_refs(const tdl_kv_cache* kv, int32_t block) {
+  if (!kv || block < 0 || block >= kv->cfg.n_blocks) return -1;
+  return kv->refs[block];
+}
+
+extern "C" tdl_status kv_prefix_match(tdl_kv_cache* kv, const uint64_t* keys, int32_t n,
+                                      int32_t* blocks, int32_t* n_matched) {
+  if (!kv || !n_matched || (n > 0 && (!keys || !blocks))) return fail(TDL_E_INVALID, "NULL argument");
+  if (n < 0) return fail(TDL_E_INVALID, "n < 0");
+  const uint64_t now = ++kv->tick;
+  int32_t m = 0;
+  for (; m < n; ++m) {
+    auto it = kv->prefix.find(keys[m]);
+    if (it == kv->prefix.end()) break;  // the prefix ends at the first miss
+    it->second.used = now;
+    blocks[m] = it->second.block;
+    ++kv->refs[it->second.block];       // the caller now holds it
   }
+  *n_matched = m;
+  return TDL_OK;
+}
+
+extern "C" tdl_status kv_prefix_publish(tdl_kv_cache* kv, const uint64_t* keys,
+                                        const int32_t* blocks, int32_t n) {
+  if (!kv || (n > 0 && (!keys || !blocks))) return fail(TDL_E_INVALID, "NULL argument");
+  if (n < 0) return fail(TDL_E_INVALID, "n < 0");
+  if (!check_held(kv, blocks, n, false)) return TDL_E_INVALID;
+  std::unordered_map<uint64_t, int32_t> call_block;
+  std::unordered_map<int32_t, uint64_t> call_key;
   for (int i = 0; i < n; ++i) {
-    kv->is_free[blocks[i]] = 1;
-    kv->free_list.push_back(blocks[i]);
+    auto a = call_block.emplace(keys[i], blocks[i]);
+    auto b = call_key.emplace(blocks[i], keys[i]);
+    if (a.first->second != blocks[i] || b.first->second != keys[i])
+      return fail(TDL_E_INVALID, "entry %d pairs a key or a block of an earlier entry differently", i);
+    auto it = kv->prefix.find(keys[i]);
+    if (it != kv->prefix.end() && it->second.block != blocks[i]) continue;  // first publisher wins
+    auto k = kv->key_of.find(blocks[i]);
+    if (k != kv->key_of.end() && k->second != keys[i])
+      return fail(TDL_E_INVALID, "block %d is already indexed under another key", blocks[i]);
+  }
+  const uint64_t now = ++kv->tick;
+  for (int i = 0; i < n; ++i) {
+    auto it = kv->prefix.find(keys[i]);
+    if (it != kv->prefix.end()) {
+      if (it->second.block == blocks[i]) it->second.used = now;
+      continue;
+    }
+    kv->prefix.emplace(keys[i], tdl_kv_cache::PrefixEntry{blocks[i], now});
+    kv->key_of[blocks[i]] = keys[i];
+    ++kv->refs[blocks[i]];  // the index's own hold
   }
   return TDL_OK;
+}
+
+extern "C" int32_t kv_prefix_evict(tdl_kv_cache* kv, int32_t n_blocks) {
+  if (!kv || n_blocks <= 0) return 0;
+  // entries whose block only the index holds, least recently used first
+  std::vector<std::pair<uint64_t, uint64_t>> idle;  // (last use, key)
+  for (auto& e : kv->prefix)
+    if (kv->refs[e.second.block] == 1) idle.push_back({e.second.used, e.first});
+  std::sort(idle.begin(), idle.end());
+  int32_t done = 0;
+  for (auto& u : idle) {
+    if (done == n_blocks) break;
+    auto it = kv->prefix.find(u.second);
+    kv->key_of.erase(it->second.block);
+    drop_hold(kv, it->second.block);
+    kv->prefix.erase(it);
+    ++done;
+  }
+  return done;
+}
+
+extern "C" int32_t kv_prefix_size(const tdl_kv_cache* kv) {
+  return kv ? (int32_t)kv->prefix.size() : 0;
 }
 
 extern "C" int32_t kv_free_blocks(const tdl_kv_cache* kv) {
