@@ -16,7 +16,7 @@ Every step is written from the definition it cites.  Where the pages are
 silent or garbled the plainest reading is taken and named in the docstring.
 
 Parity status of each function (what pins it, see tests/test_oracle_*.py):
-  round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, kv_levels,
+  round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, iq8_expand, kv_levels,
   kv_calibrate, kv_quantize, kv_dequantize, attention, attention_online, PagedCache,
   layer_forward -- all pinned (worked examples, closed forms, brute force,
   special cases).  The pages' own printed layer output (Qwen2.5-7B-Instruct
@@ -151,6 +151,19 @@ def swiglu(gate, up) -> np.ndarray:
     "Unary (SwiGLU)"; [QWEN] architecture overview "SwiGLU MLP").  The gate
     branch is the one that goes through SiLU."""
     return silu(gate) * np.asarray(up, np.float64)
+
+
+def iq8_expand(codes: np.ndarray, scale: np.ndarray, zero_point: np.ndarray) -> np.ndarray:
+    """Weight-only int8 with one (scale, zero point) per output channel to
+    real values: W[n, k] = (code[n, k] - zero_point[n]) * scale[n] ([HET]
+    section 4.4, the per-channel GEMV that dequantises in registers; its
+    listing takes int8 codes, an int8 zero point and a float scale per row n
+    of the [N, K] matrix).  Exact in float64 (a 9-bit integer times a float32).
+    """
+    n, k = codes.shape
+    assert codes.dtype == np.int8 and scale.shape == (n,) and zero_point.shape == (n,)
+    q = codes.astype(np.float64) - zero_point.astype(np.float64)[:, None]
+    return q * scale.astype(np.float32).astype(np.float64)[:, None]
 
 
 # --------------------------------------------------------------------------
@@ -343,13 +356,16 @@ def attention_online(q, q_pos, K, V, tile: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def expand_weights(shape, w: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
-    """float64 copies of the weights; Q8_0 matrices expanded exactly."""
+    """float64 copies of the weights; Q8_0 and per-channel int8 matrices
+    expanded exactly."""
     out = {}
     for name, a in w.items():
-        if name.endswith("_scale"):
+        if name.endswith("_scale") or name.endswith("_zp"):
             continue
         if shape.weight_dtype == "q80" and name + "_scale" in w:
             out[name] = q80_expand(a, w[name + "_scale"])
+        elif shape.weight_dtype == "iq8" and name + "_scale" in w:
+            out[name] = iq8_expand(a, w[name + "_scale"], w[name + "_zp"])
         else:
             out[name] = np.asarray(a, np.float64)
     return out

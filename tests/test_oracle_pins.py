@@ -144,6 +144,40 @@ def test_q80_expand_exact():
     assert list(oracle.q80_expand(c, s)[0, ::32]) == [1.0, 2.0, 4.0]
 
 
+# ------------------------------------------- per-channel int8 weights ---
+
+def test_iq8_expand_worked_example():
+    g = load("iq8_worked.json")
+    codes = np.array(g["codes"], np.int8)
+    zp = np.array(g["zero_point"], np.int8)
+    scale = np.array([float.fromhex(h) for h in g["scale_hex"]], np.float32)
+    W = oracle.iq8_expand(codes, scale, zp)
+    assert W[:2].tolist() == g["expect_rows_0_1"]
+    assert [float(v) for v in W[2]] == [float.fromhex(h) for h in g["expect_row_2_hex"]]
+
+
+def test_iq8_expand_special_cases_and_orientation():
+    rng = np.random.default_rng(8)
+    codes = rng.integers(-128, 128, size=(6, 40), dtype=np.int8)
+    # zero point 0, scale 1: the codes themselves
+    W = oracle.iq8_expand(codes, np.ones(6, np.float32), np.zeros(6, np.int8))
+    assert np.array_equal(W, codes.astype(np.float64))
+    # a zero point equal to a row's constant code gives a zero row
+    c = np.full((2, 8), 7, np.int8)
+    assert not oracle.iq8_expand(c, np.float32([3, 3]), np.int8([7, 0])).any(axis=1)[0]
+    # parameters belong to output rows (n), not to input columns (k)
+    sc = np.float32([1, 2, 4, 8, 16, 32])
+    zp = np.int8([0, 1, 2, 3, 4, 5])
+    W = oracle.iq8_expand(codes, sc, zp)
+    for n in range(6):
+        assert np.array_equal(W[n], (codes[n].astype(np.float64) - zp[n]) * sc[n])
+    # linear through the expanded matrix: y = s[n] * sum_k x[k] (q[n,k] - zp[n])
+    x = rng.standard_normal((3, 40))
+    y = oracle.linear(x, W)
+    ref = (x @ codes.T.astype(np.float64) - x.sum(1, keepdims=True) * zp.astype(np.float64)) * sc
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------- int8 KV quantisation ---
 
 def test_kv_quant_worked_examples():
