@@ -11,8 +11,9 @@ Also reported (same JSON line): the paged decode step of the same layer (batch
 with its HBM fraction; the dominant kernel's roofline (per-kernel HIP-event
 durations recorded by the library on the call's stream over the timed
 region); the other configurations (the 512-token prefill, the Qwen3-8B
-decode over u8 and u4 caches at batch 128, the Qwen3-8B Q8_0 mixed step, a
-28-layer decode stack), each with
+decode over u8 and u4 caches at batch 128, the Qwen2.5-7B decode with
+per-row int8 weights, the Qwen3-8B Q8_0 mixed step, a 28-layer decode
+stack), each with
 its roofline fraction; and the oracle's CPU throughput on a bounded sample of
 the prefill.
 
@@ -180,7 +181,8 @@ def quantised_decode(args, torch, synth, tdl, stream, kvd, flush, sink):
 def other_workloads(args, torch, synth, tdl, stream, layer512):
     """The other configurations of the layer, measured the same way (synthetic
     inputs, resident in HBM): the 512-token prefill of the same Qwen2.5-7B
-    layer, the Qwen3-8B decode over a u8 and over a u4 cache (batch 128), the Qwen3-8B
+    layer, the Qwen3-8B decode over a u8 and over a u4 cache (batch 128), the
+    Qwen2.5-7B decode with per-row int8 weights (batch 64), the Qwen3-8B
     Q8_0 mixed step (a 2048-token chunk + 64 decode rows), and a 28-layer
     stack of the Qwen2.5-7B layer decoding batch 64."""
     out = {}
@@ -256,6 +258,52 @@ def other_workloads(args, torch, synth, tdl, stream, layer512):
     layer.close()
     kv.close()
     del x, y, kv, tab
+
+    # ---- Qwen2.5-7B decode with weight-only per-row int8 weights: batch,
+    # contexts, block placement and cache drawn as for the bf16 decode
+    wl = synth.WORKLOADS["qwen25_iq8_decode_b64"]
+    shape = wl.shape
+    Hkv, D, H = shape.n_kv_heads, shape.head_dim, shape.hidden
+    B = wl.decode_batch
+    ctx = synth.context_lengths(np.random.default_rng(0), wl)
+    totals = (ctx + 1).tolist()
+    nb = int(sum(math.ceil(t / 16) for t in totals))
+    tab = torch.from_numpy(synth.random_tables(np.random.default_rng(3), totals, n_blocks=nb)).cuda()
+    log(f"qwen2.5 iq8 decode: weights, cache of {int(ctx.sum())} tokens")
+    layer = tdl.Layer(tdl.make_config(shape, max_tokens=B, max_seqs=B, max_position=4352),
+                      synth.torch_weights(shape, seed=7))
+    kv = tdl.KvCache(nb, Hkv, D, "bf16")
+    n_cached = int(ctx.sum())
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)).cuda()
+    kv.write(cu, torch.zeros(B, dtype=torch.int32, device="cuda"), tab,
+             synth.torch_normal((n_cached, Hkv, D), seed=4, dtype=torch.bfloat16),
+             synth.torch_normal((n_cached, Hkv, D), seed=5, dtype=torch.bfloat16))
+    ctx_d = torch.from_numpy(ctx).cuda()
+    x = synth.torch_normal((B, H), seed=6, dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    max_ctx = int(ctx.max()) + 1
+    for _ in range(3):
+        layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv)
+    times = timed_steps(torch, stream, lambda: layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv),
+                        args.decode_steps, flush, sink)
+    us = 1e3 * float(np.median(times))
+    n_rows = shape.n_q_heads * D + 2 * Hkv * D + H + 2 * shape.intermediate + H
+    w_bytes = weight_bytes(shape) // 2 + 5 * n_rows  # 1-byte codes + fp32 scale and int8 zero point per row
+    step_bytes = w_bytes + int(sum(totals)) * Hkv * D * 2 * 2 + 2 * B * H * 2
+    assert torch.isfinite(y.float()).all(), "non-finite iq8 decode output"
+    out["qwen25_iq8_decode_b64"] = {
+        "workload": "qwen2.5-7b-shaped layer with weight-only per-row int8 weights (code - zp) * scale, "
+                    "paged decode, batch 64, ctx U[128,4096], bf16 KV, block 16, random block permutation; "
+                    "L2/MALL flushed between steps",
+        "us_per_step": round(us, 2), "algorithmic_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(step_bytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "stages_ms": stage_profile(layer, lambda: layer.decode_paged(x, y, ctx_d, tab, max_ctx, kv), 5,
+                                   lambda: torch.sum(flush, dim=0, out=sink))}
+    log(f"qwen2.5 iq8 decode: {us:.1f} us/step")
+    layer.close()
+    kv.close()
+    del x, y, kv, tab, ctx_d
 
     # ---- a 28-layer stack of Qwen2.5-7B-shaped layers (each with its own
     # weights and bf16 cache), decode batch 64: one token of every sequence

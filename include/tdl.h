@@ -64,7 +64,8 @@ typedef enum {
   TDL_F32 = 1,
   TDL_Q8_0 = 2,    /* 32 int8 codes + one fp16 scale per block along K          */
   TDL_U8_ASYM = 3, /* uint8 codes + per-channel fp32 scale and int32 zero point */
-  TDL_U4_ASYM = 4  /* uint4 codes, two per byte, + the same per-channel parameters */
+  TDL_U4_ASYM = 4, /* uint4 codes, two per byte, + the same per-channel parameters */
+  TDL_I8_ROW = 5   /* weight-only int8: codes + per-output-row fp32 scale and int8 zero point */
 } tdl_dtype;
 
 typedef void* tdl_stream; /* hipStream_t */
@@ -84,7 +85,7 @@ typedef struct {
   float rope_theta;       /* RoPE base; half-split pairs (i, i + D/2)       */
   int32_t qkv_bias;       /* 1: Q/K/V projections have a bias               */
   int32_t qk_norm;        /* 1: per-head RMSNorm on q and k before RoPE     */
-  int32_t weight_dtype;   /* TDL_F32, TDL_BF16 or TDL_Q8_0                  */
+  int32_t weight_dtype;   /* TDL_F32, TDL_BF16, TDL_Q8_0 or TDL_I8_ROW       */
   int32_t max_tokens;     /* most rows (new tokens) in one call             */
   int32_t max_seqs;       /* most sequences in one call                     */
   int32_t max_position;   /* positions 0 .. max_position-1 can be rotated   */
@@ -93,7 +94,11 @@ typedef struct {
 /* Weights, device pointers in PyTorch Linear layout ([out, in], row-major).
  * Matrices wq [Hq*D, H], wk/wv [Hkv*D, H], wo [H, Hq*D], wg/wu [I, H],
  * wd [H, I] hold weight_dtype elements: float32, bf16, or for Q8_0 the int8
- * codes, with the fp16 scales in w*_scale [out, in/32].  Biases bq/bk/bv
+ * codes, with the fp16 scales in w*_scale [out, in/32].  TDL_I8_ROW
+ * (weight-only per-channel int8, [HET] 4.4): int8 codes, w*_scale float32
+ * [out] and w*_zp int8 [out], W[n][k] = (code[n][k] - zp[n]) * scale[n];
+ * decode-sized calls (<= 128 rows) stream the codes, larger ones use fp16 /
+ * bf16 copies expanded at create time (when max_tokens > 128).  Biases bq/bk/bv
  * (if qkv_bias) and gains ln1/ln2 [H], q_norm/k_norm [D] (if qk_norm) are
  * float32.  Unused pointers may be NULL.  layer_create copies (and repacks)
  * everything into library-owned memory; the caller may free its copies once
@@ -101,6 +106,7 @@ typedef struct {
 typedef struct {
   const void *ln1, *wq, *bq, *wk, *bk, *wv, *bv, *wo, *ln2, *wg, *wu, *wd, *q_norm, *k_norm;
   const void *wq_scale, *wk_scale, *wv_scale, *wo_scale, *wg_scale, *wu_scale, *wd_scale;
+  const void *wq_zp, *wk_zp, *wv_zp, *wo_zp, *wg_zp, *wu_zp, *wd_zp;  /* TDL_I8_ROW only */
 } tdl_layer_weights;
 
 /* Paged KV cache ([TFF] 3.6.4 KVConfig; [HET] 4.3 BlockManager). */

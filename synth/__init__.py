@@ -85,6 +85,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
              kv_dtype="u8"),
     Workload("qwen3_decode_u4_b128", QWEN3_8B, "decode", decode_batch=128, ctx_lo=512, ctx_hi=8192,
              kv_dtype="u4"),
+    Workload("qwen25_iq8_decode_b64", QWEN25_7B_IQ8, "decode", decode_batch=64, ctx_lo=128,
+             ctx_hi=4096, kv_dtype="bf16"),
     Workload("qwen3_q80_mixed", QWEN3_8B_Q80, "mixed", prefill_len=2048, decode_batch=64,
              ctx_fixed=2048, kv_dtype="bf16"),
 ]}

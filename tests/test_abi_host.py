@@ -49,6 +49,7 @@ def cfg_ok(tdl, **kw):
     (dict(head_dim=96), 2), (dict(n_q_heads=6, n_kv_heads=4), 1), (dict(n_q_heads=12, n_kv_heads=4), 2),
     (dict(hidden=200), 2), (dict(intermediate=100), 2), (dict(weight_dtype=3), 1),
     (dict(max_tokens=0), 1), (dict(rope_theta=0.0), 1), (dict(weight_dtype=2, intermediate=688), 1),
+    (dict(weight_dtype=5, intermediate=688), 1), (dict(weight_dtype=6), 1),
     (dict(max_seqs=4096, max_tokens=4096), 2), (dict(max_position=300000), 2),
 ])
 def test_layer_create_rejects_bad_config(kw, status):
@@ -68,6 +69,20 @@ def test_layer_create_rejects_missing_weights():
     h = ctypes.c_void_p()
     assert tdl._layer_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(h)) == tdl.TDL_E_INVALID
     assert b"NULL" in tdl._last_error()
+
+
+def test_layer_create_iq8_needs_scales_and_zero_points():
+    # per-row int8 weights: every matrix needs its scale and zero point
+    import transformer_decoder_layer_amd as tdl
+    cfg = cfg_ok(tdl, weight_dtype=tdl.TDL_I8_ROW, intermediate=704)
+    w = tdl.LayerWeights()
+    for name in ("ln1", "wq", "bq", "wk", "bk", "wv", "bv", "wo", "ln2", "wg", "wu", "wd"):
+        setattr(w, name, 1 << 20)              # never dereferenced: the checks come first
+    for m in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+        setattr(w, m + "_scale", 1 << 20)
+    h = ctypes.c_void_p()
+    assert tdl._layer_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(h)) == tdl.TDL_E_INVALID
+    assert b"_zp" in tdl._last_error() and not h.value
 
 
 def test_null_handles_are_invalid():

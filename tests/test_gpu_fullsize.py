@@ -60,6 +60,10 @@ def test_qwen3_decode_u4_b128_sampled_seqs():
     _check(inp, seqs, what="qwen3 u4 decode b128")
 
 
+def test_qwen25_iq8_decode_b64_full():
+    _check(synth.make_inputs(synth.WORKLOADS["qwen25_iq8_decode_b64"]), what="qwen2.5 iq8 decode b64")
+
+
 def test_qwen3_q80_mixed_sampled():
     inp = synth.make_inputs(synth.WORKLOADS["qwen3_q80_mixed"])
     # sequence 0 is the 2048-token chunk (rows 0..2047), then 64 decode rows

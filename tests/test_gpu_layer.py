@@ -16,6 +16,10 @@ pytestmark = pytest.mark.gpu
 TINY_Q3 = dataclasses.replace(synth.TINY, name="tiny-qwen3", qkv_bias=False, qk_norm=True,
                               weight_dtype="bf16", rope_theta=1e6)
 TINY_Q80 = dataclasses.replace(TINY_Q3, name="tiny-q8_0", intermediate=704, weight_dtype="q80")
+# per-row int8: 704 (down K packable) and 736 (down K % 64 = 32: row-major expanded copy)
+TINY_IQ8 = dataclasses.replace(synth.TINY, name="tiny-iq8", intermediate=704, weight_dtype="iq8")
+TINY_IQ8_736 = dataclasses.replace(TINY_IQ8, name="tiny-iq8-736", intermediate=736, qkv_bias=False,
+                                   qk_norm=True)
 TINY_D128 = dataclasses.replace(synth.TINY, name="tiny-d128", hidden=512, n_q_heads=7, n_kv_heads=1,
                                 head_dim=128, intermediate=1024, weight_dtype="bf16", rope_theta=1e6)
 
@@ -147,6 +151,24 @@ def test_tiny_decode_u4(shape):
     inp = synth.make_inputs(wl, seed=14, decode_batch=len(ctx), decode_ctx=ctx)
     layer, kv, t, cache, rows = check_layer(inp, what=f"decode u4 {shape.name}")
     check_cache_rows(inp, kv, cache, range(len(ctx)))
+
+
+@pytest.mark.parametrize("shape", [TINY_IQ8, TINY_IQ8_736], ids=lambda s: s.name)
+def test_tiny_iq8_decode_prefill_mixed(shape):
+    # decode rows stream the int8 codes; 45 rows too; 150 rows (> 128) take
+    # the expanded fp16/bf16 copies, in the mixed step as well
+    wl = dataclasses.replace(synth.WORKLOADS["qwen25_iq8_decode_b64"], shape=shape)
+    ctx = [0, 1, 16, 47, 300, 1023]
+    inp = synth.make_inputs(wl, seed=61, decode_batch=len(ctx), decode_ctx=ctx)
+    layer, kv, t, cache, rows = check_layer(inp, what=f"decode {shape.name}")
+    check_cache_rows(inp, kv, cache, range(len(ctx)))
+    for T in (45, 150):
+        wp = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=shape, kv_dtype="bf16")
+        inp = synth.make_inputs(wp, seed=62 + T, prefill_len=T, prefill_start=20, spare_blocks=1)
+        check_layer(inp, what=f"prefill {T} {shape.name}")
+    wm = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=shape)
+    inp = synth.make_inputs(wm, seed=64, prefill_len=140, decode_batch=4, decode_ctx=[3, 16, 40, 129])
+    check_layer(inp, what=f"mixed {shape.name}")
 
 
 def test_tiny_mixed_q80():

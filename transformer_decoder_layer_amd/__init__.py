@@ -22,8 +22,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 TDL_OK, TDL_E_INVALID, TDL_E_UNSUPPORTED, TDL_E_CAPACITY, TDL_E_NOMEM, TDL_E_HIP = range(6)
-TDL_BF16, TDL_F32, TDL_Q8_0, TDL_U8_ASYM, TDL_U4_ASYM = range(5)
-_DTYPES = {"bf16": TDL_BF16, "f32": TDL_F32, "q80": TDL_Q8_0, "u8": TDL_U8_ASYM, "u4": TDL_U4_ASYM}
+TDL_BF16, TDL_F32, TDL_Q8_0, TDL_U8_ASYM, TDL_U4_ASYM, TDL_I8_ROW = range(6)
+_DTYPES = {"bf16": TDL_BF16, "f32": TDL_F32, "q80": TDL_Q8_0, "u8": TDL_U8_ASYM, "u4": TDL_U4_ASYM,
+           "iq8": TDL_I8_ROW}
 
 c_i32, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 P_i32 = ctypes.POINTER(ctypes.c_int32)
@@ -46,7 +47,8 @@ class LayerConfig(ctypes.Structure):
 
 _WEIGHT_FIELDS = ["ln1", "wq", "bq", "wk", "bk", "wv", "bv", "wo", "ln2", "wg", "wu", "wd",
                   "q_norm", "k_norm", "wq_scale", "wk_scale", "wv_scale", "wo_scale", "wg_scale",
-                  "wu_scale", "wd_scale"]
+                  "wu_scale", "wd_scale", "wq_zp", "wk_zp", "wv_zp", "wo_zp", "wg_zp", "wu_zp",
+                  "wd_zp"]
 
 
 class LayerWeights(ctypes.Structure):
@@ -302,7 +304,7 @@ class KvCache:
 def make_config(shape, max_tokens: int, max_seqs: int = 1, max_position: int = 8192) -> LayerConfig:
     """LayerConfig from any object with the layer-shape attributes (hidden,
     n_q_heads, n_kv_heads, head_dim, intermediate, rms_eps, rope_theta,
-    qkv_bias, qk_norm, weight_dtype in {"f32", "bf16", "q80"})."""
+    qkv_bias, qk_norm, weight_dtype in {"f32", "bf16", "q80", "iq8"})."""
     return LayerConfig(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                        shape.intermediate, shape.rms_eps, shape.rope_theta, int(shape.qkv_bias),
                        int(shape.qk_norm), _DTYPES[shape.weight_dtype], max_tokens, max_seqs,

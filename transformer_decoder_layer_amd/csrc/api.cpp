@@ -83,6 +83,12 @@ struct tdl_kv_cache {
 struct tdl_layer {
   tdl_layer_config cfg;
   bool q80 = false;
+  bool iq8 = false;  // per-row int8 codes (TDL_I8_ROW)
+  // per-row int8: scale and zero point (as floats) of every stored row, in
+  // the stored row order (QKV rows concatenated, gate/up interleaved)
+  float *wqkv_rs = nullptr, *wqkv_rz = nullptr, *wo_rs = nullptr, *wo_rz = nullptr;
+  float *wgu_rs = nullptr, *wgu_rz = nullptr, *wd_rs = nullptr, *wd_rz = nullptr;
+  int wexp_packed[4] = {1, 1, 1, 1};  // expanded copies in the packed layout (else row-major)
   int Nqkv = 0;
   // weights (library-owned)
   void* wqkv = nullptr;
@@ -93,11 +99,13 @@ struct tdl_layer {
   void* wgu = nullptr;
   __half* wgu_s = nullptr;
   // per weight matrix (QKV, output, gate/up, down): stored in the packed
-  // tile layout (bf16/fp16 with N % 16 == 0 and K % 64 == 0) or row-major
+  // tile layout (bf16/fp16, or per-row int8 codes in the packed code layout,
+  // with N % 16 == 0 and K % 64 == 0) or row-major
   int packed[4] = {0, 0, 0, 0};
-  // Q8_0 layers that take more than 128 rows: the four matrices expanded to
-  // fp16 (bf16 for the down projection) in the packed tile layout, for the
-  // compute-bound GEMMs (the decode-sized ones stream the 1-byte codes)
+  // int8 layers that take more than 128 rows: the four matrices expanded to
+  // fp16 (bf16 for the down projection), in the packed tile layout where the
+  // shape allows, for the compute-bound GEMMs (the decode-sized ones stream
+  // the 1-byte codes)
   void* wexp[4] = {nullptr, nullptr, nullptr, nullptr};
   void* wd = nullptr;
   __half* wd_s = nullptr;
@@ -170,11 +178,12 @@ tdl_status check_config(const tdl_layer_config* c) {
     return fail(TDL_E_UNSUPPORTED, "hidden must be a multiple of 64 (got %d)", c->hidden);
   if (c->intermediate % 16)
     return fail(TDL_E_UNSUPPORTED, "intermediate must be a multiple of 16 (got %d)", c->intermediate);
-  if (c->weight_dtype != TDL_F32 && c->weight_dtype != TDL_BF16 && c->weight_dtype != TDL_Q8_0)
-    return fail(TDL_E_INVALID, "weight_dtype must be TDL_F32, TDL_BF16 or TDL_Q8_0");
-  if (c->weight_dtype == TDL_Q8_0 && (c->hidden % 32 || c->intermediate % 32 ||
-                                      (c->n_q_heads * c->head_dim) % 32))
-    return fail(TDL_E_INVALID, "Q8_0 needs every input dimension to be a multiple of 32");
+  if (c->weight_dtype != TDL_F32 && c->weight_dtype != TDL_BF16 && c->weight_dtype != TDL_Q8_0 &&
+      c->weight_dtype != TDL_I8_ROW)
+    return fail(TDL_E_INVALID, "weight_dtype must be TDL_F32, TDL_BF16, TDL_Q8_0 or TDL_I8_ROW");
+  if ((c->weight_dtype == TDL_Q8_0 || c->weight_dtype == TDL_I8_ROW) &&
+      (c->hidden % 32 || c->intermediate % 32 || (c->n_q_heads * c->head_dim) % 32))
+    return fail(TDL_E_INVALID, "int8 weights need every input dimension to be a multiple of 32");
   if (c->max_tokens <= 0 || c->max_seqs <= 0 || c->max_position <= 0)
     return fail(TDL_E_INVALID, "max_tokens, max_seqs and max_position must be positive");
   if (std::min(c->max_seqs, c->max_tokens) > kMaxDecodeSeqs || c->max_position > kMaxDecodePosition)
@@ -192,14 +201,14 @@ struct GemmShapes {
 // Largest split-K workspace over every row count a call may use.
 // (Q8_0 layers with expanded copies plan rows > kQ80CodeRows on those.)
 constexpr int kQ80CodeRows = 128;
-void gemm_ws_need(const tdl_layer_config& c, int Nqkv, bool q80, bool expanded, size_t* ws) {
+void gemm_ws_need(const tdl_layer_config& c, int Nqkv, int wf, bool expanded, size_t* ws) {
   const int H = c.hidden, QD = c.n_q_heads * c.head_dim, I = c.intermediate;
   const int shapes[4][3] = {{Nqkv, H, EPI_BIAS_F32}, {H, QD, EPI_RESID_F32},
                             {2 * I, H, EPI_SILU_GATE}, {H, I, EPI_RESID_BF16}};
   size_t w = 0;
   for (int M = 1; M <= c.max_tokens; ++M) {
-    const bool codes = q80 && !(expanded && M > kQ80CodeRows);
-    for (auto& s : shapes) w = std::max(w, gemm_plan(M, s[0], s[1], codes, s[2]).ws_floats);
+    const int f = expanded && M > kQ80CodeRows ? kWDense : wf;
+    for (auto& s : shapes) w = std::max(w, gemm_plan(M, s[0], s[1], f, s[2]).ws_floats);
   }
   *ws = w;
 }
@@ -233,19 +242,22 @@ KvPool pool_of(const tdl_layer* L, const tdl_kv_cache* kv) {
 
 // defer: a split-K plan leaves its fp32 partials in the GEMM workspace for
 // the next kernel to sum (*splits_out tells how many; 1 = C was written).
-tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const void* A, const void* B,
-                    const __half* Bs, int packed, const void* Bexp, int epi, const float* bias,
-                    const void* resid, int ldr, void* C, int ldc, bool defer = false,
-                    int* splits_out = nullptr) {
-  // Q8_0: more than kQ80CodeRows rows take the expanded (packed) copy
-  bool q80 = L->q80;
-  if (q80 && M > kQ80CodeRows && Bexp) {
-    q80 = false;
+tdl_status run_gemm(tdl_layer* L, hipStream_t st, int mat, int M, int N, int K, const void* A,
+                    const void* B, const __half* Bs, const float* Brs, const float* Brz,
+                    const void* Bexp, int epi, const float* bias, const void* resid, int ldr, void* C,
+                    int ldc, bool defer = false, int* splits_out = nullptr) {
+  int wf = L->q80 ? kWQ80 : L->iq8 ? kWIQ8 : kWDense;
+  int packed = L->packed[mat];
+  // int8 layers: more than kQ80CodeRows rows take the expanded copy
+  if (wf != kWDense && M > kQ80CodeRows && Bexp) {
+    wf = kWDense;
     B = Bexp;
     Bs = nullptr;
-    packed = 1;
+    packed = L->wexp_packed[mat];
   }
-  const GemmPlan pl = gemm_plan(M, N, K, q80, epi);
+  if (wf == kWIQ8 && M > kQ80CodeRows)
+    return fail(TDL_E_UNSUPPORTED, "per-row int8 weights without an expanded copy at M=%d", M);
+  const GemmPlan pl = gemm_plan(M, N, K, wf, epi);
   if (splits_out) *splits_out = defer ? pl.splits : 1;
   if (pl.ws_floats > L->gemm_ws_floats)
     return fail(TDL_E_CAPACITY, "GEMM workspace too small for M=%d N=%d K=%d", M, N, K);
@@ -255,6 +267,8 @@ tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const voi
   a.B = B;
   a.ldb = K;
   a.B_scale = Bs;
+  a.B_rscale = wf == kWIQ8 ? Brs : nullptr;
+  a.B_rzp = wf == kWIQ8 ? Brz : nullptr;
   a.M = M;
   a.N = N;
   a.K = K;
@@ -265,7 +279,7 @@ tdl_status run_gemm(tdl_layer* L, hipStream_t st, int M, int N, int K, const voi
   a.ldc = ldc;
   a.ws = L->gemm_ws;
   a.b_packed = packed;
-  HIP_TRY(gemm_launch(pl, a, q80, epi, st, !defer));
+  HIP_TRY(gemm_launch(pl, a, wf, epi, st, !defer));
   return TDL_OK;
 }
 
@@ -326,7 +340,7 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   int qkv_splits = 1;
   {
     StageTimer t(L, TDL_STAGE_QKV, st);
-    TRY(run_gemm(L, st, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->packed[0], L->wexp[0], EPI_BIAS_F32, L->bqkv, nullptr,
+    TRY(run_gemm(L, st, 0, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->wqkv_rs, L->wqkv_rz, L->wexp[0], EPI_BIAS_F32, L->bqkv, nullptr,
                  0, L->qkv, L->Nqkv, true, &qkv_splits));
   }
   {
@@ -347,7 +361,7 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   int o_splits = 1;
   {
     StageTimer t(L, TDL_STAGE_O_PROJ, st);
-    TRY(run_gemm(L, st, rows, H, Hq * D, L->o, L->wo, L->wo_s, L->packed[1], L->wexp[1], EPI_RESID_F32, nullptr, x, H, L->h,
+    TRY(run_gemm(L, st, 1, rows, H, Hq * D, L->o, L->wo, L->wo_s, L->wo_rs, L->wo_rz, L->wexp[1], EPI_RESID_F32, nullptr, x, H, L->h,
                  H, H <= kFusedNormMaxH, &o_splits));
   }
   {
@@ -359,12 +373,12 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   }
   {
     StageTimer t(L, TDL_STAGE_GATE_UP, st);
-    TRY(run_gemm(L, st, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, L->packed[2], L->wexp[2], EPI_SILU_GATE, nullptr, nullptr, 0,
+    TRY(run_gemm(L, st, 2, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, L->wgu_rs, L->wgu_rz, L->wexp[2], EPI_SILU_GATE, nullptr, nullptr, 0,
                  L->a, I));
   }
   {
     StageTimer t(L, TDL_STAGE_DOWN, st);
-    TRY(run_gemm(L, st, rows, H, I, L->a, L->wd, L->wd_s, L->packed[3], L->wexp[3], EPI_RESID_BF16, nullptr, L->h, H, y, H));
+    TRY(run_gemm(L, st, 3, rows, H, I, L->a, L->wd, L->wd_s, L->wd_rs, L->wd_rz, L->wexp[3], EPI_RESID_BF16, nullptr, L->h, H, y, H));
   }
   return TDL_OK;
 }
@@ -418,6 +432,8 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   if (!w) return fail(TDL_E_INVALID, "weights are NULL");
   const tdl_layer_config& c = *cfg;
   const bool q80 = c.weight_dtype == TDL_Q8_0;
+  const bool iq8 = c.weight_dtype == TDL_I8_ROW;
+  const bool codes = q80 || iq8;  // 1-byte codes stored as given
   if (!w->ln1 || !w->wq || !w->wk || !w->wv || !w->wo || !w->ln2 || !w->wg || !w->wu || !w->wd)
     return fail(TDL_E_INVALID, "a required weight pointer is NULL");
   if (c.qkv_bias && (!w->bq || !w->bk || !w->bv))
@@ -427,11 +443,16 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   if (q80 && (!w->wq_scale || !w->wk_scale || !w->wv_scale || !w->wo_scale || !w->wg_scale ||
               !w->wu_scale || !w->wd_scale))
     return fail(TDL_E_INVALID, "Q8_0 weights need every *_scale pointer");
+  if (iq8 && (!w->wq_scale || !w->wk_scale || !w->wv_scale || !w->wo_scale || !w->wg_scale ||
+              !w->wu_scale || !w->wd_scale || !w->wq_zp || !w->wk_zp || !w->wv_zp || !w->wo_zp ||
+              !w->wg_zp || !w->wu_zp || !w->wd_zp))
+    return fail(TDL_E_INVALID, "per-row int8 weights need every *_scale and *_zp pointer");
 
   hipStream_t st = (hipStream_t)stream;
   tdl_layer* L = new tdl_layer();
   L->cfg = c;
   L->q80 = q80;
+  L->iq8 = iq8;
   const int H = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, I = c.intermediate;
   const int QD = Hq * D, KD = Hkv * D;
   L->Nqkv = QD + 2 * KD;
@@ -453,7 +474,7 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   } while (0)
 
   // ---- weights: bf16 copies (f32 rounded to nearest even), or Q8_0 codes
-  const size_t wel = q80 ? 1 : 2;  // bytes per stored weight element
+  const size_t wel = codes ? 1 : 2;  // bytes per stored weight element
   CTRY(dalloc(L, &L->wqkv, (size_t)L->Nqkv * H * wel));
   CTRY(dalloc(L, &L->wo, (size_t)H * QD * wel));
   CTRY(dalloc(L, &L->wgu, (size_t)2 * I * H * wel));
@@ -465,7 +486,7 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   CTRY(dalloc(L, &n_sat, 4));
   CHIP(hipMemsetAsync(n_sat, 0, 4, st));
   auto put = [&](const void* src, void* dst, int64_t n, int to_f16) -> tdl_status {
-    const hipError_t e = q80 ? hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, st)
+    const hipError_t e = codes ? hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, st)
                              : convert_weights(src, c.weight_dtype == TDL_F32, dst, to_f16, n,
                                                n_sat, st);
     if (e != hipSuccess) return fail(TDL_E_HIP, "weight copy failed: %s", hipGetErrorString(e));
@@ -492,7 +513,7 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
       (void)hipFree(p);
     }
   }
-  if (!q80) {
+  if (!codes) {
     // repack every matrix the tiled readers can take (one temporary the size
     // of the largest)
     const int shapes[4][2] = {{L->Nqkv, H}, {H, QD}, {2 * I, H}, {H, I}};
@@ -550,6 +571,83 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
       }
     }
   }
+  if (iq8) {
+    // per-row scales (float32, copied) and zero points (int8 -> float), in
+    // the stored row order; gate/up rows interleaved like the codes
+    auto rows_f32 = [&](float** dst, int n) { return dalloc(L, dst, (size_t)n * 4); };
+    CTRY(rows_f32(&L->wqkv_rs, L->Nqkv));
+    CTRY(rows_f32(&L->wqkv_rz, L->Nqkv));
+    CTRY(rows_f32(&L->wo_rs, H));
+    CTRY(rows_f32(&L->wo_rz, H));
+    CTRY(rows_f32(&L->wgu_rs, 2 * I));
+    CTRY(rows_f32(&L->wgu_rz, 2 * I));
+    CTRY(rows_f32(&L->wd_rs, H));
+    CTRY(rows_f32(&L->wd_rz, H));
+    CHIP(copy_f32((const float*)w->wq_scale, L->wqkv_rs, QD, st));
+    CHIP(copy_f32((const float*)w->wk_scale, L->wqkv_rs + QD, KD, st));
+    CHIP(copy_f32((const float*)w->wv_scale, L->wqkv_rs + QD + KD, KD, st));
+    CHIP(i8_to_f32(w->wq_zp, L->wqkv_rz, QD, st));
+    CHIP(i8_to_f32(w->wk_zp, L->wqkv_rz + QD, KD, st));
+    CHIP(i8_to_f32(w->wv_zp, L->wqkv_rz + QD + KD, KD, st));
+    CHIP(copy_f32((const float*)w->wo_scale, L->wo_rs, H, st));
+    CHIP(i8_to_f32(w->wo_zp, L->wo_rz, H, st));
+    CHIP(copy_f32((const float*)w->wd_scale, L->wd_rs, H, st));
+    CHIP(i8_to_f32(w->wd_zp, L->wd_rz, H, st));
+    float* gz = nullptr;
+    float* uz = nullptr;
+    CTRY(rows_f32(&gz, I));
+    CTRY(rows_f32(&uz, I));
+    CHIP(i8_to_f32(w->wg_zp, gz, I, st));
+    CHIP(i8_to_f32(w->wu_zp, uz, I, st));
+    CHIP(interleave_gate_up(w->wg_scale, w->wu_scale, 4, I, L->wgu_rs, st));
+    CHIP(interleave_gate_up(gz, uz, 4, I, L->wgu_rz, st));
+    CHIP(hipStreamSynchronize(st));
+    for (void* p : {(void*)gz, (void*)uz}) {
+      L->allocs.erase(std::find(L->allocs.begin(), L->allocs.end(), p));
+      (void)hipFree(p);
+    }
+    if (c.max_tokens > kQ80CodeRows) {
+      // expanded copies for the compute-bound GEMMs: packed where the shape
+      // allows, row-major otherwise (the large-M kernels have no int8 path)
+      const int shapes[4][2] = {{L->Nqkv, H}, {H, QD}, {2 * I, H}, {H, I}};
+      const void* cm[4] = {L->wqkv, L->wo, L->wgu, L->wd};
+      const float* rs[4] = {L->wqkv_rs, L->wo_rs, L->wgu_rs, L->wd_rs};
+      const float* rz[4] = {L->wqkv_rz, L->wo_rz, L->wgu_rz, L->wd_rz};
+      size_t most = 0;
+      for (auto& sh : shapes) most = std::max(most, (size_t)sh[0] * sh[1] * 2);
+      void* tmp = nullptr;
+      CTRY(dalloc(L, &tmp, most));
+      for (int i = 0; i < 4; ++i) {
+        const bool pk = shapes[i][0] % 16 == 0 && shapes[i][1] % 64 == 0;
+        CTRY(dalloc(L, &L->wexp[i], (size_t)shapes[i][0] * shapes[i][1] * 2));
+        CHIP(expand_iq8(cm[i], rs[i], rz[i], shapes[i][0], shapes[i][1], pk ? tmp : L->wexp[i],
+                        i != 3, st));
+        if (pk) CHIP(pack_weights(tmp, L->wexp[i], shapes[i][0], shapes[i][1], st));
+        L->wexp_packed[i] = pk;
+      }
+      CHIP(hipStreamSynchronize(st));
+      L->allocs.erase(std::find(L->allocs.begin(), L->allocs.end(), tmp));
+      (void)hipFree(tmp);
+    }
+    // the codes themselves in the stream kernel's packed layout where the
+    // shape allows (one contiguous 1 KB read per wave and stage); after the
+    // expansion above, which reads them row-major
+    const int shapes[4][2] = {{L->Nqkv, H}, {H, QD}, {2 * I, H}, {H, I}};
+    void* mats[4] = {L->wqkv, L->wo, L->wgu, L->wd};
+    size_t most = 0;
+    for (auto& sh : shapes) most = std::max(most, (size_t)sh[0] * sh[1]);
+    void* tmp = nullptr;
+    CTRY(dalloc(L, &tmp, most));
+    for (int i = 0; i < 4; ++i) {
+      if (shapes[i][0] % 16 != 0 || shapes[i][1] % 64 != 0) continue;
+      CHIP(pack_codes(mats[i], tmp, shapes[i][0], shapes[i][1], st));
+      CHIP(hipMemcpyAsync(mats[i], tmp, (size_t)shapes[i][0] * shapes[i][1], hipMemcpyDeviceToDevice, st));
+      L->packed[i] = 1;
+    }
+    CHIP(hipStreamSynchronize(st));
+    L->allocs.erase(std::find(L->allocs.begin(), L->allocs.end(), tmp));
+    (void)hipFree(tmp);
+  }
   if (c.qkv_bias) {
     CTRY(dalloc(L, &L->bqkv, (size_t)L->Nqkv * 4));
     CHIP(copy_f32((const float*)w->bq, L->bqkv, QD, st));
@@ -577,7 +675,8 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   CTRY(dalloc(L, &L->h, (size_t)T * H * 4));
   CTRY(dalloc(L, &L->hn, (size_t)T * H * 2));
   CTRY(dalloc(L, &L->a, (size_t)T * I * 2));
-  gemm_ws_need(c, L->Nqkv, q80, L->wexp[0] != nullptr, &L->gemm_ws_floats);
+  gemm_ws_need(c, L->Nqkv, q80 ? kWQ80 : iq8 ? kWIQ8 : kWDense, L->wexp[0] != nullptr,
+               &L->gemm_ws_floats);
   CTRY(dalloc(L, &L->gemm_ws, L->gemm_ws_floats * 4));
   const int max_dec = std::min(c.max_seqs, c.max_tokens);
   L->dec_part_floats = decode_part_need(c, max_dec);

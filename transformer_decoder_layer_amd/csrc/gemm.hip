@@ -734,11 +734,12 @@ hipError_t tail_reduce(const GemmPlan& pl, const GemmArgs& a, int epi, hipStream
 // Chooses the tile configuration and split-K factor with the lowest estimated
 // time: rounds of workgroups over the 256 CUs times the per-workgroup work,
 // divided by the configuration's relative efficiency.
-GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
+GemmPlan gemm_plan(int M, int N, int K, int wf, int epi) {
+  const bool q80 = wf == kWQ80;  // per-row int8 has no large-M kernel: callers expand it
   constexpr int kCUs = 256;
   {
     GemmPlan sk{};
-    if (skinny_plan(M, N, K, q80, epi, &sk)) return sk;
+    if (skinny_plan(M, N, K, wf, epi, &sk)) return sk;
   }
   const int KT = cdiv(K, BK);
   GemmPlan best{};
@@ -805,7 +806,7 @@ GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi) {
   return best;
 }
 
-hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, bool q80, int epi, hipStream_t s, bool reduce) {
+hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, int wf, int epi, hipStream_t s, bool reduce) {
   a.splits = pl.splits;
   a.k_tiles_per_split = pl.k_tiles_per_split;
   a.full_tiles = pl.full_tiles;
@@ -814,9 +815,10 @@ hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, bool q80, int epi, hipStr
   a.tail_ws = pl.tail_splits > 1 ? a.ws : nullptr;
   a.rng_count = pl.rng_count;
   if (pl.tail_splits > 1 && (!a.ws || pl.splits != 1)) return hipErrorInvalidValue;
-  const hipError_t e = pl.cfg >= 10 ? gemm_skinny_launch(pl, a, q80, epi, s)
-                       : q80          ? launch_epi<true>(pl.cfg, pl.grid, epi, a, s)
-                                      : launch_epi<false>(pl.cfg, pl.grid, epi, a, s);
+  if (pl.cfg < 10 && wf == kWIQ8) return hipErrorInvalidValue;
+  const hipError_t e = pl.cfg >= 10     ? gemm_skinny_launch(pl, a, wf, epi, s)
+                       : wf == kWQ80 ? launch_epi<true>(pl.cfg, pl.grid, epi, a, s)
+                                        : launch_epi<false>(pl.cfg, pl.grid, epi, a, s);
   if (e != hipSuccess) return e;
   if (pl.tail_splits > 1) return tail_reduce(pl, a, epi, s);
   if (pl.splits == 1 || !reduce) return e;

@@ -34,7 +34,11 @@
 //
 // Q8_0 weights: a lane loads 8 int8 codes of its row per 32-k step plus the
 // block's fp16 scale; the codes convert exactly to fp16 and the scale
-// multiplies that step's MFMA product in fp32.
+// multiplies that step's MFMA product in fp32.  Per-row int8 weights (the
+// per-channel weight-only GEMV of the devpress heterogeneous-engine page,
+// section 4.4): a lane loads 8 codes per step; code - zero point (an
+// integer in [-255, 255], exact in fp16 and bf16) is the MFMA operand, and
+// the row's fp32 scale multiplies the finished sum once.
 
 #include "common.h"
 #include "kernels.h"
@@ -52,18 +56,20 @@ constexpr int kMaxStages = 8;
 // this wave are outstanding and leaves the other counters alone.
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
-template <bool Q80, typename T> struct BFrag;
-template <typename T> struct BFrag<false, T> { typename Mfma<T>::v8 v; };
-template <typename T> struct BFrag<true, T> { uint2 codes; uint32_t scale; };
+template <int WF, typename T> struct BFrag;
+template <typename T> struct BFrag<kWDense, T> { typename Mfma<T>::v8 v; };
+template <typename T> struct BFrag<kWQ80, T> { uint2 codes; uint32_t scale; };
+template <typename T> struct BFrag<kWIQ8, T> { uint2 codes; };
 
 // (at most 128 registers up to 64 rows of A: four waves per SIMD, i.e. two
 // 8-wave workgroups per CU, so that every workgroup of a launch is resident
 // at once; 128 rows of A need more and run two waves per SIMD)
 // RW row waves per k-slice (64 * RW / 4 ... 16 * RW weight rows per
 // workgroup), NS pipeline stages (= LDS ring buffers = register sets).
-template <typename T, bool Q80, int MT, int KW, int RW, int NS, int EPI, bool PACKED = false>
+template <typename T, int WF, int MT, int KW, int RW, int NS, int EPI, bool PACKED = false>
 __global__ __launch_bounds__(64 * RW * KW) __attribute__((amdgpu_waves_per_eu(MT == 8 ? 2 : 4)))
 void gemm_stream_kernel(GemmArgs p) {
+  constexpr bool Q80 = WF == kWQ80, IQ8 = WF == kWIQ8;
   constexpr int kRowWaves = RW, kStages = NS;
   static_assert(NS >= 3 && NS <= kMaxStages && RW % 2 == 0, "stream GEMM shape");
   typedef typename Mfma<T>::v8 T8;
@@ -71,7 +77,9 @@ void gemm_stream_kernel(GemmArgs p) {
   constexpr int AE = MT * 16 * kStageK;              // A elements per slice and stage
   constexpr int A_CHUNKS = 2 * MT;                   // 1 KB direct loads per slice and stage
   constexpr int A_PER_WAVE = (A_CHUNKS + RW - 1) / RW;  // per wave (the last chunk repeats)
-  constexpr int LOADS = A_PER_WAVE + FN * 2 * (Q80 ? 2 : 1);  // vector-memory ops per stage
+  // packed per-row int8 codes: one 16-byte load per stage (both 32-k steps)
+  constexpr bool IQ8P = IQ8 && PACKED;
+  constexpr int LOADS = A_PER_WAVE + FN * (IQ8P ? 1 : 2 * (Q80 ? 2 : 1));  // vector-memory ops per stage
   // separate arrays (not one indexed array): the compiler can then tell that
   // reading one buffer does not depend on the loads still filling another
   // (arrays past NS are never referenced and take no LDS)
@@ -130,14 +138,21 @@ void gemm_stream_kernel(GemmArgs p) {
 #pragma unroll
   for (int f = 0; f < FN; ++f) b_row[f] = (size_t)min(n0 + 16 * (min(wr, ng - 1) * FN + f) + r16, p.N - 1);
 
-  BFrag<Q80, T> breg[kStages][FN][2];
+  BFrag<WF, T> breg[kStages][FN][2];
+  // per-row int8: this lane's row scale and zero point
+  float rsc[FN], rzp[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    rsc[f] = IQ8 ? p.B_rscale[b_row[f]] : 1.f;
+    rzp[f] = IQ8 ? p.B_rzp[b_row[f]] : 0.f;
+  }
   f32x4 acc[MT][FN];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int f = 0; f < FN; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto issue = [&](int it, T* ring, BFrag<Q80, T> (&b)[FN][2]) {
+  auto issue = [&](int it, T* ring, BFrag<WF, T> (&b)[FN][2]) {
     const int st = min(my0 + it, last);
     const int k0 = st * kStageK;
     // A: the whole stage chunk; a k past K (a half stage at the end) reads
@@ -147,6 +162,17 @@ void gemm_stream_kernel(GemmArgs p) {
     for (int q = 0; q < A_PER_WAVE; ++q)
       __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + a_off), (lds_void*)&ring[a_dst[q]], 16, 0,
                                        0);
+    if constexpr (IQ8P) {
+      // tile (stage, row group): one contiguous 1 KB read per wave
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        const uint4 c = *(const uint4*)((const int8_t*)p.B +
+                                        ((size_t)st * (p.N >> 4) + (b_row[f] >> 4)) * 1024 + lane * 16);
+        b[f][0].codes = make_uint2(c.x, c.y);
+        b[f][1].codes = make_uint2(c.z, c.w);
+      }
+      return;
+    }
 #pragma unroll
     for (int f = 0; f < FN; ++f)
 #pragma unroll
@@ -156,6 +182,8 @@ void gemm_stream_kernel(GemmArgs p) {
         if constexpr (Q80) {
           b[f][u].codes = *(const uint2*)((const int8_t*)p.B + b_row[f] * p.ldb + k);
           b[f][u].scale = *(const uint16_t*)(p.B_scale + b_row[f] * (p.ldb / 32) + ks);
+        } else if constexpr (IQ8) {
+          b[f][u].codes = *(const uint2*)((const int8_t*)p.B + b_row[f] * p.ldb + k);
         } else if constexpr (PACKED) {
           // fragment = chunk `lane` of tile (row group, ks): one 1 KB read
           b[f][u].v = *(const T8*)((const T*)p.B + ((size_t)ks * (p.N >> 4) + (b_row[f] >> 4)) * 512 + lane * 8);
@@ -165,7 +193,7 @@ void gemm_stream_kernel(GemmArgs p) {
       }
   };
 
-  auto compute = [&](int it, const T* ring, const BFrag<Q80, T> (&b)[FN][2]) {
+  auto compute = [&](int it, const T* ring, const BFrag<WF, T> (&b)[FN][2]) {
     const int st = my0 + it;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -183,6 +211,14 @@ void gemm_stream_kernel(GemmArgs p) {
           }
           bv[f] = v;
           sc[f] = valid ? __half2float(__ushort_as_half((unsigned short)b[f][u].scale)) : 0.f;
+        } else if constexpr (IQ8) {
+          T8 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = (T)((float)(int8_t)(b[f][u].codes.x >> (8 * e)) - rzp[f]);
+            v[4 + e] = (T)((float)(int8_t)(b[f][u].codes.y >> (8 * e)) - rzp[f]);
+          }
+          bv[f] = valid ? v : T8{};
         } else {
           bv[f] = valid ? b[f][u].v : T8{};
         }
@@ -229,6 +265,12 @@ void gemm_stream_kernel(GemmArgs p) {
   // the last refills are still landing in the ring: drain them before the
   // ring is reused or the workgroup exits
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if constexpr (IQ8) {  // the row scale, once per output (and per partial)
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int f = 0; f < FN; ++f) acc[i][f] *= rsc[f];
+  }
 
   // ---- k-slices meet in LDS, summed in a fixed order
   if constexpr (KW > 1) {
@@ -323,34 +365,37 @@ void gemm_stream_kernel(GemmArgs p) {
   }
 }
 
-template <bool Q80, int MT, int KW, int RW, int NS, bool PK>
+template <int WF, int MT, int KW, int RW, int NS, bool PK>
 hipError_t launch_stream2(int grid, int epi, const GemmArgs& a, hipStream_t s) {
   constexpr int threads = 64 * RW * KW;
   switch (epi) {
     case EPI_BIAS_F32:
-      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_BIAS_F32, PK><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<f16, WF, MT, KW, RW, NS, EPI_BIAS_F32, PK><<<grid, threads, 0, s>>>(a);
       break;
     case EPI_RESID_F32:
-      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_RESID_F32, PK><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<f16, WF, MT, KW, RW, NS, EPI_RESID_F32, PK><<<grid, threads, 0, s>>>(a);
       break;
     case EPI_RESID_BF16:
-      gemm_stream_kernel<bf16, Q80, MT, KW, RW, NS, EPI_RESID_BF16, PK><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<bf16, WF, MT, KW, RW, NS, EPI_RESID_BF16, PK><<<grid, threads, 0, s>>>(a);
       break;
     default:
-      gemm_stream_kernel<f16, Q80, MT, KW, RW, NS, EPI_SILU_GATE, PK><<<grid, threads, 0, s>>>(a);
+      gemm_stream_kernel<f16, WF, MT, KW, RW, NS, EPI_SILU_GATE, PK><<<grid, threads, 0, s>>>(a);
       break;
   }
   return hipGetLastError();
 }
 
-template <bool Q80, int MT, int KW, int RW, int NS>
+template <int WF, int MT, int KW, int RW, int NS>
 hipError_t launch_stream(int grid, int epi, const GemmArgs& a, hipStream_t s) {
-  if constexpr (Q80) {
+  if constexpr (WF == kWIQ8) {
+    return a.b_packed ? launch_stream2<WF, MT, KW, RW, NS, true>(grid, epi, a, s)
+                      : launch_stream2<WF, MT, KW, RW, NS, false>(grid, epi, a, s);
+  } else if constexpr (WF != kWDense) {
     if (a.b_packed) return hipErrorInvalidValue;  // Q8_0 codes stay row-major
-    return launch_stream2<true, MT, KW, RW, NS, false>(grid, epi, a, s);
+    return launch_stream2<WF, MT, KW, RW, NS, false>(grid, epi, a, s);
   } else {
-    return a.b_packed ? launch_stream2<false, MT, KW, RW, NS, true>(grid, epi, a, s)
-                      : launch_stream2<false, MT, KW, RW, NS, false>(grid, epi, a, s);
+    return a.b_packed ? launch_stream2<kWDense, MT, KW, RW, NS, true>(grid, epi, a, s)
+                      : launch_stream2<kWDense, MT, KW, RW, NS, false>(grid, epi, a, s);
   }
 }
 
@@ -360,9 +405,12 @@ hipError_t launch_stream(int grid, int epi, const GemmArgs& a, hipStream_t s) {
 // cfg = 10000 + 1000 * MT + 100 * RW + 10 * NS + KW.
 int stream_cfg(int MT, int RW, int NS, int KW) { return 10000 + 1000 * MT + 100 * RW + 10 * NS + KW; }
 
-// Row waves per workgroup that are built (RW), and the pipeline depth.
+// Row waves per workgroup that are built (RW), and the pipeline depth: 4
+// stages of 2 KB per wave (bf16/fp16, Q8_0); per-row int8 stages carry 1 KB
+// (64 k of 16 rows), so 7 stages keep as many bytes in flight.
 constexpr int kStreamRW[3] = {4, 8, 10};
 constexpr int kStreamNS = 4;
+constexpr int kStreamNSIQ8 = 7;
 
 // Chooses (RW, row ranges, K splits) by a model of the decode-sized stream,
 // fitted to measurements on the Qwen2.5-7B decode shapes: a CU streams its
@@ -370,7 +418,7 @@ constexpr int kStreamNS = 4;
 // live row wave, up to ~22 GB/s, and the GPU at ~5.5 TB/s; the busiest CU
 // sets the time.  K splits add streams (and fp32 partials that are written
 // and read once more).
-bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl) {
+bool skinny_plan(int M, int N, int K, int wf, int epi, GemmPlan* pl) {
   if (M > 128 || K % 32 != 0) return false;
   constexpr int kCUs = 256;
   const int MT = M <= 32 ? 2 : M <= 64 ? 4 : 8;
@@ -378,7 +426,8 @@ bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl) {
   const int units = cdiv(N, 16) / PG;
   if (units < 1) return false;
   const int KS = cdiv(K / 32, 2);
-  const double wb = q80 ? 1.0625 : 2.0;  // weight bytes per element (Q8_0: + fp16 scale per 32)
+  // weight bytes per element (Q8_0: + fp16 scale per 32)
+  const double wb = wf == kWQ80 ? 1.0625 : wf == kWIQ8 ? 1.0 : 2.0;
   const double total = (double)N * K * wb;
   // Spare row waves (a range shorter than RW), which repeat a live wave's
   // loads and MFMAs, slow the live ones: rate x live/RW.  4-wave
@@ -389,6 +438,8 @@ bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl) {
   // at 64 rows).
   const bool big = MT == 8;
   const double wave_lat = big ? 2.3e-6 : 1.5e-6;
+  const int NS = wf == kWIQ8 ? kStreamNSIQ8 : kStreamNS;
+  const double stage_bytes = wf == kWIQ8 ? 1024.0 : 2048.0;  // per live row wave
   double best = 1e300;
   for (int RW : kStreamRW) {
     if (RW < 8 && units > 16) continue;  // (tiny N: too few row groups for 8 waves)
@@ -396,7 +447,7 @@ bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl) {
     const int rmin = cdiv(units, per);
     for (int s = 1; s <= 16; ++s) {
       const int kps = cdiv(KS, s), sp = cdiv(KS, kps);
-      if (sp != s || (sp > 1 && kps < 2 * kStreamNS)) continue;
+      if (sp != s || (sp > 1 && kps < 2 * NS)) continue;
       const int cands[3] = {rmin, kCUs / sp, 2 * kCUs / sp};
       for (int R : cands) {
         if (R < rmin || R > units || R < 1) continue;
@@ -404,7 +455,7 @@ bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl) {
         const int wg_per_cu = cdiv(W, kCUs);
         const int groups = cdiv(units, R) * PG;          // live row waves of the largest range
         const double wg_bytes = (double)groups * 16 * kps * 64 * wb;
-        double rate = std::min(22e9, wg_per_cu * groups * (kStreamNS - 1) * 2048.0 / wave_lat);
+        double rate = std::min(22e9, wg_per_cu * groups * (NS - 1) * stage_bytes / wave_lat);
         rate *= (double)groups / RW;
         double t = std::max(wg_per_cu * wg_bytes / rate, total / 5.5e12);
         if (sp > 1) t += 2.0 * sp * (double)M * N * 4.0 / 5.0e12;
@@ -412,7 +463,7 @@ bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl) {
         if (t < best) {
           best = t;
           *pl = GemmPlan{};
-          pl->cfg = stream_cfg(MT, RW, kStreamNS, 1);
+          pl->cfg = stream_cfg(MT, RW, NS, 1);
           pl->rng_count = R;
           pl->splits = sp;
           pl->k_tiles_per_split = kps;
@@ -425,16 +476,24 @@ bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl) {
   return best < 1e300;
 }
 
-hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, bool q80, int epi,
+hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, int wf, int epi,
                               hipStream_t s) {
 #define TDL_STREAM_CFG(MT, RW, NS, KW)                                                      \
   if (pl.cfg == stream_cfg(MT, RW, NS, KW))                                                 \
-    return q80 ? launch_stream<true, MT, KW, RW, NS>(pl.grid, epi, a, s)                    \
-               : launch_stream<false, MT, KW, RW, NS>(pl.grid, epi, a, s);
+    return wf == kWQ80   ? launch_stream<kWQ80, MT, KW, RW, NS>(pl.grid, epi, a, s)         \
+           : wf == kWIQ8 ? launch_stream<kWIQ8, MT, KW, RW, NS>(pl.grid, epi, a, s)         \
+                         : launch_stream<kWDense, MT, KW, RW, NS>(pl.grid, epi, a, s);
   TDL_STREAM_CFG(2, 4, 4, 1) TDL_STREAM_CFG(2, 8, 4, 1) TDL_STREAM_CFG(2, 10, 4, 1)
   TDL_STREAM_CFG(4, 4, 4, 1) TDL_STREAM_CFG(4, 8, 4, 1) TDL_STREAM_CFG(4, 10, 4, 1)
   TDL_STREAM_CFG(8, 4, 4, 1) TDL_STREAM_CFG(8, 8, 4, 1) TDL_STREAM_CFG(8, 10, 4, 1)
 #undef TDL_STREAM_CFG
+#define TDL_STREAM_CFG_IQ8(MT, RW, NS, KW)                                                  \
+  if (pl.cfg == stream_cfg(MT, RW, NS, KW) && wf == kWIQ8)                                  \
+    return launch_stream<kWIQ8, MT, KW, RW, NS>(pl.grid, epi, a, s);
+  TDL_STREAM_CFG_IQ8(2, 4, 7, 1) TDL_STREAM_CFG_IQ8(2, 8, 7, 1) TDL_STREAM_CFG_IQ8(2, 10, 7, 1)
+  TDL_STREAM_CFG_IQ8(4, 4, 7, 1) TDL_STREAM_CFG_IQ8(4, 8, 7, 1) TDL_STREAM_CFG_IQ8(4, 10, 7, 1)
+  TDL_STREAM_CFG_IQ8(8, 4, 7, 1) TDL_STREAM_CFG_IQ8(8, 8, 7, 1) TDL_STREAM_CFG_IQ8(8, 10, 7, 1)
+#undef TDL_STREAM_CFG_IQ8
   return hipErrorInvalidValue;
 }
 

@@ -19,12 +19,19 @@ enum GemmEpilogue {
                        // gate/up in alternating 16-column groups of B
 };
 
+// Weight formats of the GEMMs: bf16/fp16 elements; Q8_0 (int8 codes, one
+// fp16 scale per 32 along K); per-row int8 (int8 codes, one fp32 scale and
+// one zero point per output row: W = (code - zp) * scale).
+enum WeightFmt : int { kWDense = 0, kWQ80 = 1, kWIQ8 = 2 };
+
 struct GemmArgs {
   const void* A;
   int lda;
   const void* B;
   int ldb;
   const __half* B_scale;  // Q8_0 only, [N, K/32]
+  const float* B_rscale;  // per-row int8 only, [N]
+  const float* B_rzp;     // per-row int8 only, [N] (zero points as floats)
   int M, N, K;
   const float* bias;
   const void* resid;
@@ -65,15 +72,15 @@ struct GemmPlan {
   int tail_kps;
   int rng_count;      // decode-sized kernel: row ranges
 };
-GemmPlan gemm_plan(int M, int N, int K, bool q80, int epi);
+GemmPlan gemm_plan(int M, int N, int K, int wf, int epi);
 // Decode-sized M (<= 128, K % 32 == 0): weights streamed straight from HBM
 // into MFMA operands, activations shared through LDS (cfg >= 100).
-bool skinny_plan(int M, int N, int K, bool q80, int epi, GemmPlan* pl);
-hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, bool q80, int epi,
+bool skinny_plan(int M, int N, int K, int wf, int epi, GemmPlan* pl);
+hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, int wf, int epi,
                               hipStream_t s);
 // reduce = false leaves split-K partials in a.ws for a consumer that sums them
 // (only meaningful when plan.splits > 1).
-hipError_t gemm_launch(const GemmPlan& plan, GemmArgs a, bool q80, int epi, hipStream_t s,
+hipError_t gemm_launch(const GemmPlan& plan, GemmArgs a, int wf, int epi, hipStream_t s,
                        bool reduce = true);
 
 // -------------------------------------------------------- element-wise
@@ -164,7 +171,18 @@ hipError_t copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 // (dst_f16 = 1, saturating) or bf16: code * scale rounded to nearest even.
 hipError_t expand_q80(const void* codes, const void* scales, int N, int K, void* dst, int dst_f16,
                       hipStream_t s);
+// Per-row int8 codes [N][K], scale [N] and zero point [N] (as floats) ->
+// dst [N][K] fp16 (saturating) or bf16: (code - zp) * scale rounded once.
+hipError_t expand_iq8(const void* codes, const float* scale, const float* zp, int N, int K, void* dst,
+                      int dst_f16, hipStream_t s);
+// int8 [n] -> float [n]
+hipError_t i8_to_f32(const void* src, float* dst, int64_t n, hipStream_t s);
 hipError_t pack_weights(const void* src, void* dst, int N, int K, hipStream_t s);
+// int8 codes [N][K] -> the stream kernel's packed code layout: 1 KB tiles
+// (64-k stage st, 16-row group g) at ((st * N/16) + g) KB, lane l's 16 bytes
+// = codes of row 16g + l%16 at k = 64st + 8(l/16) .. +7, then the same at
+// k + 32 (the two 32-k steps of the stage).  Needs N % 16 == 0, K % 64 == 0.
+hipError_t pack_codes(const void* src, void* dst, int N, int K, hipStream_t s);
 // Element offset of (n, k) in that layout.
 __host__ __device__ inline size_t packed_offset(int n, int k, int N) {
   return ((size_t)(k >> 5) * (N >> 4) + (n >> 4)) * 512 + (size_t)((((k >> 3) & 3) << 4) + (n & 15)) * 8 +

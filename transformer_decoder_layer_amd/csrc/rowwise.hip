@@ -410,6 +410,38 @@ __global__ void expand_q80_kernel(const int8_t* __restrict__ codes, const __half
     }
   }
 }
+// per-row int8: (code - zp[n]) * scale[n], rounded once to the stored type
+__global__ void expand_iq8_kernel(const int8_t* __restrict__ codes, const float* __restrict__ scale,
+                                  const float* __restrict__ zp, int N, int K, void* __restrict__ dst,
+                                  int dst_f16) {
+  const int64_t n8 = (int64_t)N * (K / 8);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int n = (int)(i / (K / 8)), k = (int)(i % (K / 8)) * 8;
+    const float sc = scale[n], z = zp[n];
+    const uint2 c = *(const uint2*)(codes + (size_t)n * K + k);
+    const uint32_t w[2] = {c.x, c.y};
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = ((float)(int8_t)(w[e >> 2] >> (8 * (e & 3))) - z) * sc;
+    if (dst_f16) {
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = f32_to_f16_sat(v[e]);
+      *(f16x8*)((f16*)dst + (size_t)n * K + k) = o;
+    } else {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16(v[e]);
+      *(bf16x8*)((bf16*)dst + (size_t)n * K + k) = o;
+    }
+  }
+}
+__global__ void i8_to_f32_kernel(const int8_t* __restrict__ src, float* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = (float)src[i];
+}
 __global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -435,6 +467,21 @@ __global__ void pack_kernel(const uint4* __restrict__ src, uint4* __restrict__ d
        c += (int64_t)gridDim.x * blockDim.x) {
     const int n = (int)(c / (K / 8)), k = (int)(c % (K / 8)) * 8;
     dst[packed_offset(n, k, N) / 8] = src[c];
+  }
+}
+
+// one thread per 16-byte destination chunk of the packed code layout
+__global__ void pack_codes_kernel(const int8_t* __restrict__ src, uint4* __restrict__ dst, int N, int K) {
+  const int64_t chunks = (int64_t)N * (K / 16);
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(c & 63);
+    const int64_t tile = c >> 6;
+    const int g = (int)(tile % (N / 16)), st = (int)(tile / (N / 16));
+    const int n = 16 * g + (l & 15), k = 64 * st + 8 * (l >> 4);
+    const uint2 lo = *(const uint2*)(src + (size_t)n * K + k);
+    const uint2 hi = *(const uint2*)(src + (size_t)n * K + k + 32);
+    dst[c] = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
 
@@ -529,6 +576,18 @@ hipError_t expand_q80(const void* codes, const void* scales, int N, int K, void*
   return hipGetLastError();
 }
 
+hipError_t expand_iq8(const void* codes, const float* scale, const float* zp, int N, int K, void* dst,
+                      int dst_f16, hipStream_t s) {
+  if (K % 8 != 0) return hipErrorInvalidValue;
+  expand_iq8_kernel<<<2048, 256, 0, s>>>((const int8_t*)codes, scale, zp, N, K, dst, dst_f16);
+  return hipGetLastError();
+}
+
+hipError_t i8_to_f32(const void* src, float* dst, int64_t n, hipStream_t s) {
+  i8_to_f32_kernel<<<256, 256, 0, s>>>((const int8_t*)src, dst, n);
+  return hipGetLastError();
+}
+
 hipError_t interleave_gate_up(const void* gate, const void* up, int row_bytes, int I, void* dst,
                               hipStream_t s) {
   interleave_kernel<<<2 * I, 256, 0, s>>>((const uint8_t*)gate, (const uint8_t*)up, row_bytes, I,
@@ -539,6 +598,12 @@ hipError_t interleave_gate_up(const void* gate, const void* up, int row_bytes, i
 hipError_t pack_weights(const void* src, void* dst, int N, int K, hipStream_t s) {
   if (N % 16 != 0 || K % 32 != 0) return hipErrorInvalidValue;
   pack_kernel<<<2048, 256, 0, s>>>((const uint4*)src, (uint4*)dst, N, K);
+  return hipGetLastError();
+}
+
+hipError_t pack_codes(const void* src, void* dst, int N, int K, hipStream_t s) {
+  if (N % 16 != 0 || K % 64 != 0) return hipErrorInvalidValue;
+  pack_codes_kernel<<<2048, 256, 0, s>>>((const int8_t*)src, (uint4*)dst, N, K);
   return hipGetLastError();
 }
 
