@@ -16,7 +16,7 @@ Every step is written from the definition it cites.  Where the pages are
 silent or garbled the plainest reading is taken and named in the docstring.
 
 Parity status of each function (what pins it, see tests/test_oracle_*.py):
-  round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, iq8_expand, kv_levels,
+  round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, iq8_expand, a8w8_gemm, kv_levels,
   kv_calibrate, kv_quantize, kv_dequantize, attention, attention_online, PagedCache,
   layer_forward -- all pinned (worked examples, closed forms, brute force,
   special cases).  The pages' own printed layer output (Qwen2.5-7B-Instruct
@@ -164,6 +164,22 @@ def iq8_expand(codes: np.ndarray, scale: np.ndarray, zero_point: np.ndarray) -> 
     assert codes.dtype == np.int8 and scale.shape == (n,) and zero_point.shape == (n,)
     q = codes.astype(np.float64) - zero_point.astype(np.float64)[:, None]
     return q * scale.astype(np.float32).astype(np.float64)[:, None]
+
+
+def a8w8_gemm(a_codes: np.ndarray, b_codes: np.ndarray, a_scale: np.ndarray, b_scale: np.ndarray):
+    """int8 x int8 GEMM with a dequantising epilogue ([HET] section 4.5):
+    C[m, n] = sum_k A[m, k] * B[n, k] accumulated exactly (the s8s8s32 MMA),
+    then out[m, n] = C[m, n] * a_scale[m] * b_scale[n].  A [M, K] and B [N, K]
+    are int8 (B in Linear layout, like every weight here); the scales are
+    float32.  Returns (C as int64, out in float64)."""
+    assert a_codes.dtype == np.int8 and b_codes.dtype == np.int8
+    M, K = a_codes.shape
+    N, K2 = b_codes.shape
+    assert K == K2 and a_scale.shape == (M,) and b_scale.shape == (N,)
+    C = a_codes.astype(np.int64) @ b_codes.astype(np.int64).T
+    out = (C.astype(np.float64) * a_scale.astype(np.float32).astype(np.float64)[:, None]
+           * b_scale.astype(np.float32).astype(np.float64)[None, :])
+    return C, out
 
 
 # --------------------------------------------------------------------------

@@ -178,6 +178,29 @@ def test_iq8_expand_special_cases_and_orientation():
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
 
 
+def test_a8w8_gemm_brute_force_and_extremes():
+    rng = np.random.default_rng(9)
+    A = rng.integers(-128, 128, size=(3, 7), dtype=np.int8)
+    B = rng.integers(-128, 128, size=(5, 7), dtype=np.int8)
+    sa = np.float32([0.5, 2.0, 0.25])
+    sb = np.float32([1.0, 0.125, 4.0, 3.0, 0.5])
+    C, out = oracle.a8w8_gemm(A, B, sa, sb)
+    for m in range(3):                           # explicit loops, Python ints
+        for n in range(5):
+            acc = 0
+            for k in range(7):
+                acc += int(A[m, k]) * int(B[n, k])
+            assert C[m, n] == acc
+            assert out[m, n] == acc * float(sa[m]) * float(sb[n])   # power-of-two scales: exact
+    # the scale of row m multiplies row m, the scale of column n column n
+    C1, out1 = oracle.a8w8_gemm(A, B, np.float32([1, 1, 1]), np.float32([1, 0, 0, 0, 0]))
+    assert np.array_equal(out1[:, 0], C1[:, 0]) and not out1[:, 1:].any()
+    # extremes: -128 * -128 over K = 4096 is 2^26, well inside int32
+    big = np.full((1, 4096), -128, np.int8)
+    Cb, _ = oracle.a8w8_gemm(big, big, np.float32([1]), np.float32([1]))
+    assert Cb[0, 0] == 1 << 26
+
+
 # ------------------------------------------------- int8 KV quantisation ---
 
 def test_kv_quant_worked_examples():
