@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
+PEAK_INT8_TOPS = 5000.0   # dense int8 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -182,7 +183,8 @@ def other_workloads(args, torch, synth, tdl, stream, layer512):
     """The other configurations of the layer, measured the same way (synthetic
     inputs, resident in HBM): the 512-token prefill of the same Qwen2.5-7B
     layer, the Qwen3-8B decode over a u8 and over a u4 cache (batch 128), the
-    Qwen2.5-7B decode with per-row int8 weights (batch 64), the Qwen3-8B
+    Qwen2.5-7B decode with per-row int8 weights (batch 64), the int8 x int8
+    GEMM at the gate/up shape, the Qwen3-8B
     Q8_0 mixed step (a 2048-token chunk + 64 decode rows), and a 28-layer
     stack of the Qwen2.5-7B layer decoding batch 64."""
     out = {}
@@ -304,6 +306,31 @@ def other_workloads(args, torch, synth, tdl, stream, layer512):
     layer.close()
     kv.close()
     del x, y, kv, tab, ctx_d
+
+    # ---- int8 x int8 GEMM (activation-quantised), at the gate/up shape of
+    # the 4096-token prefill: M 4096, N 2 x 18944, K 3584
+    M, N, K = 4096, 37888, 3584
+    g = torch.Generator(device="cuda")
+    g.manual_seed(80)
+    A8 = torch.randint(-128, 128, (M, K), generator=g, device="cuda", dtype=torch.int8)
+    B8 = torch.randint(-128, 128, (N, K), generator=g, device="cuda", dtype=torch.int8)
+    sa = torch.rand(M, generator=g, device="cuda") * 0.01 + 1e-4
+    sb = torch.rand(N, generator=g, device="cuda") * 0.01 + 1e-4
+    o8 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        tdl.gemm_a8w8(A8, B8, sa, sb, o8)
+    times = timed_steps(torch, stream, lambda: tdl.gemm_a8w8(A8, B8, sa, sb, o8), n_steps)
+    ms = float(np.median(times))
+    tops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    assert torch.isfinite(o8).all(), "non-finite a8w8 output"
+    out["a8w8_gemm_4096x37888x3584"] = {
+        "workload": "int8 x int8 GEMM, int32 accumulation, per-row x per-column fp32 dequantising epilogue, "
+                    "fp32 output; M 4096, N 37888, K 3584 (the Qwen2.5-7B gate/up shape of the 4096-token prefill)",
+        "ms_per_call": round(ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": round(tops / PEAK_INT8_TOPS, 4)}}
+    log(f"a8w8 gemm: {ms * 1e3:.1f} us, {tops:.0f} TOP/s")
+    del A8, B8, o8
 
     # ---- a 28-layer stack of Qwen2.5-7B-shaped layers (each with its own
     # weights and bf16 cache), decode batch 64: one token of every sequence

@@ -385,6 +385,21 @@ tdl_status kv_cache_write(tdl_kv_cache* kv, tdl_stream stream, int32_t n_seqs,
                           const int32_t* block_tables, int32_t max_blocks, int32_t src_dtype,
                           const void* k, const void* v, int32_t n_rows);
 
+/* ------------------------------------------------------------ A8W8 GEMM */
+
+/* int8 x int8 GEMM with a dequantising epilogue ([HET] 4.5, activation
+ * quantisation: int8 activations and weights on the int8 matrix units,
+ * accumulated in int32, then out = C * a_scale[m] * b_scale[n]).
+ * A [M, K] and B [N, K] int8, row-major (B in Linear layout), 16-byte
+ * aligned; a_scale [M], b_scale [N] float32; out [M, N] float32; C_accum
+ * [M, N] int32 receives the exact sums when not NULL (all device memory).
+ * K must be a positive multiple of 16; M or N == 0 is a no-op.  The sums are
+ * exact while |C| < 2^31 (K <= 131072 always is).  Enqueued on the stream;
+ * no allocation, no synchronisation. */
+tdl_status gemm_a8w8(tdl_stream stream, const void* A, const void* B, const float* a_scale,
+                     const float* b_scale, int32_t* C_accum, float* out, int32_t M, int32_t N,
+                     int32_t K);
+
 /* --------------------------------------------------------------- errors */
 
 const char* tdl_status_string(tdl_status s);

@@ -85,6 +85,18 @@ def test_layer_create_iq8_needs_scales_and_zero_points():
     assert b"_zp" in tdl._last_error() and not h.value
 
 
+def test_gemm_a8w8_argument_checks():
+    import transformer_decoder_layer_amd as tdl
+    P = 1 << 20                                  # never dereferenced: the checks come first
+    g = tdl._gemm_a8w8
+    assert g(None, P, P, P, P, None, P, 0, 8, 16) == tdl.TDL_OK           # empty: nothing to do
+    assert g(None, P, P, P, P, None, P, 4, 8, 24) == tdl.TDL_E_INVALID    # K % 16
+    assert g(None, P, P, P, P, None, P, 4, 8, 0) == tdl.TDL_E_INVALID
+    assert g(None, P, None, P, P, None, P, 4, 8, 16) == tdl.TDL_E_INVALID
+    assert g(None, P + 8, P, P, P, None, P, 4, 8, 16) == tdl.TDL_E_INVALID  # alignment
+    assert g(None, P, P, P, P, None, P, -1, 8, 16) == tdl.TDL_E_INVALID
+
+
 def test_null_handles_are_invalid():
     import transformer_decoder_layer_amd as tdl
     assert tdl._layer_prefill(None, None, 1, 2, 4, 0, None, None) == tdl.TDL_E_INVALID

@@ -34,7 +34,7 @@ EXPORTS = ["layer_create", "layer_destroy", "layer_prefill", "layer_decode_paged
            "stack_destroy", "stack_decode_paged", "kv_cache_bytes", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_view", "kv_block_table", "kv_block_release", "kv_block_share", "kv_block_refs",
            "kv_free_blocks", "kv_prefix_publish", "kv_prefix_match", "kv_prefix_evict", "kv_prefix_size",
-           "kv_cache_calibrate", "kv_cache_write", "tdl_status_string", "tdl_last_error"]
+           "kv_cache_calibrate", "kv_cache_write", "gemm_a8w8", "tdl_status_string", "tdl_last_error"]
 
 
 class LayerConfig(ctypes.Structure):
@@ -115,6 +115,7 @@ _kv_publish = _sig("kv_prefix_publish", c_i32, c_vp, P_u64, P_i32, c_i32)
 _kv_match = _sig("kv_prefix_match", c_i32, c_vp, P_u64, c_i32, P_i32, P_i32)
 _kv_evict = _sig("kv_prefix_evict", c_i32, c_vp, c_i32)
 _kv_prefix_size = _sig("kv_prefix_size", c_i32, c_vp)
+_gemm_a8w8 = _sig("gemm_a8w8", c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32)
 _kv_calibrate = _sig("kv_cache_calibrate", c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_int64)
 _kv_write = _sig("kv_cache_write", c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp,
                  c_vp, c_i32)
@@ -299,6 +300,15 @@ class KvCache:
         _check("kv_cache_write", _kv_write(self._h, _stream(stream), start_pos.shape[0], _ptr(cu_rows),
                                            _ptr(start_pos), _ptr(block_tables), block_tables.shape[1],
                                            src, _ptr(k), _ptr(v), k.shape[0]))
+
+
+def gemm_a8w8(a, b, a_scale, b_scale, out, c_accum=None, stream=None):
+    """out [M, N] float32 = (a [M, K] int8 @ b [N, K]^T int8, in int32) *
+    a_scale[m] * b_scale[n]; c_accum [M, N] int32 (optional) gets the sums."""
+    M, K = a.shape
+    N = b.shape[0]
+    _check("gemm_a8w8", _gemm_a8w8(_stream(stream), _ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale),
+                                   _ptr(c_accum), _ptr(out), M, N, K))
 
 
 def make_config(shape, max_tokens: int, max_seqs: int = 1, max_position: int = 8192) -> LayerConfig:

@@ -1,0 +1,130 @@
+// int8 x int8 GEMM with a dequantising epilogue (the activation-quantised
+// GEMM of the devpress heterogeneous-engine page, section 4.5): C = A B^T
+// accumulated in int32 on the int8 MFMA units, then out = C * a_scale[m] *
+// b_scale[n] in fp32.  A [M, K] and B [N, K] are int8, row-major (B in
+// Linear layout).
+//
+// A workgroup (4 waves, 2 x 2) owns a 128 x 128 tile of C; each wave a
+// 64 x 64 quarter as 4 x 4 MFMA tiles of 16 x 16 (v_mfma_i32_16x16x64_i8:
+// one 64-wide k step per instruction).  A and B k-slices of 64 bytes per row
+// go global -> registers -> LDS, double-buffered: the next slice's loads are
+// issued before the current slice's MFMAs.  In LDS a row is 4 chunks of 16
+// bytes; chunk c of row r sits at position c ^ ((r >> 2) & 3), so the 16
+// rows one fragment read touches (same chunk) fall on distinct banks.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace tdl {
+
+namespace {
+
+constexpr int kTile = 128;  // rows of A and of B per workgroup
+constexpr int kStep = 64;   // k per step (bytes per row and step)
+
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kStep + 16 * (c ^ ((r >> 2) & 3)); }
+
+__global__ __launch_bounds__(256) void a8w8_gemm_kernel(const int8_t* __restrict__ A,
+                                                        const int8_t* __restrict__ B,
+                                                        const float* __restrict__ a_scale,
+                                                        const float* __restrict__ b_scale,
+                                                        int32_t* __restrict__ C, float* __restrict__ out,
+                                                        int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) int8_t As[2][kTile * kStep];
+  __shared__ __attribute__((aligned(16))) int8_t Bs[2][kTile * kStep];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * kTile, n0 = blockIdx.x * kTile;
+  const int steps = (K + kStep - 1) / kStep;
+
+  // this thread's two 16-byte chunks of each tile: chunk q = tid + 256 i,
+  // row q / 4, chunk q % 4; rows past M / N and k past K read as zero
+  struct Regs {
+    i32x4 a[2], b[2];
+  };
+  auto load = [&](int s, Regs& R) {
+    i32x4* ra = R.a;
+    i32x4* rb = R.b;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 256 * i, r = q >> 2, k = s * kStep + 16 * (q & 3);
+      const bool kin = k < K;
+      ra[i] = (m0 + r < M && kin) ? *(const i32x4*)(A + (size_t)(m0 + r) * K + k) : i32x4{0, 0, 0, 0};
+      rb[i] = (n0 + r < N && kin) ? *(const i32x4*)(B + (size_t)(n0 + r) * K + k) : i32x4{0, 0, 0, 0};
+    }
+  };
+  auto store = [&](int buf, const Regs& R) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 256 * i, r = q >> 2, c = q & 3;
+      *(i32x4*)&As[buf][lds_off(r, c)] = R.a[i];
+      *(i32x4*)&Bs[buf][lds_off(r, c)] = R.b[i];
+    }
+  };
+
+  i32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+  auto mma_step = [&](int buf) {
+    // fragments: lane l takes row l % 16 of a 16-row tile, chunk l / 16
+    i32x4 af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[i] = *(const i32x4*)&As[buf][lds_off(wm * 64 + 16 * i + (lane & 15), lane >> 4)];
+      bfr[i] = *(const i32x4*)&Bs[buf][lds_off(wn * 64 + 16 * i + (lane & 15), lane >> 4)];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+  Regs R;
+  load(0, R);
+  store(0, R);
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) load(s + 1, R);  // in flight during this step's MFMAs
+    mma_step(buf);
+    if (s + 1 < steps) {
+      store(buf ^ 1, R);  // the other buffer: last read a step ago, before the barrier below
+      __syncthreads();
+    }
+  }
+
+  // acc[i][j][r] = C[row 16i + 4(lane/16) + r][col 16j + lane%16] of the wave's quarter
+  const int rq = 4 * (lane >> 4), cq = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * 64 + 16 * j + cq;
+    if (n >= N) continue;
+    const float sb = b_scale[n];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 64 + 16 * i + rq + r;
+        if (m >= M) continue;
+        const int32_t c = acc[i][j][r];
+        if (C) C[(size_t)m * N + n] = c;
+        out[(size_t)m * N + n] = (float)c * a_scale[m] * sb;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t a8w8_gemm(const void* A, const void* B, const float* a_scale, const float* b_scale,
+                     int32_t* C, float* out, int M, int N, int K, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (M < 0 || N < 0 || K < 16 || K % 16 != 0) return hipErrorInvalidValue;
+  dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
+  a8w8_gemm_kernel<<<grid, 256, 0, s>>>((const int8_t*)A, (const int8_t*)B, a_scale, b_scale, C, out, M, N,
+                                        K);
+  return hipGetLastError();
+}
+
+}  // namespace tdl

@@ -1248,6 +1248,20 @@ extern "C" tdl_status kv_cache_write(tdl_kv_cache* kv, tdl_stream stream, int32_
   return TDL_OK;
 }
 
+// ============================================================ A8W8 GEMM
+
+extern "C" tdl_status gemm_a8w8(tdl_stream stream, const void* A, const void* B,
+                                const float* a_scale, const float* b_scale, int32_t* C_accum,
+                                float* out, int32_t M, int32_t N, int32_t K) {
+  if (M < 0 || N < 0 || K < 0) return fail(TDL_E_INVALID, "negative size");
+  if (M == 0 || N == 0) return TDL_OK;
+  if (!A || !B || !a_scale || !b_scale || !out) return fail(TDL_E_INVALID, "NULL argument");
+  if (K == 0 || K % 16 != 0) return fail(TDL_E_INVALID, "K must be a positive multiple of 16");
+  if (((uintptr_t)A | (uintptr_t)B) & 15) return fail(TDL_E_INVALID, "A and B must be 16-byte aligned");
+  HIP_TRY(tdl::a8w8_gemm(A, B, a_scale, b_scale, C_accum, out, M, N, K, (hipStream_t)stream));
+  return TDL_OK;
+}
+
 // =============================================================== errors
 
 extern "C" const char* tdl_status_string(tdl_status s) {

@@ -175,6 +175,10 @@ hipError_t expand_q80(const void* codes, const void* scales, int N, int K, void*
 // dst [N][K] fp16 (saturating) or bf16: (code - zp) * scale rounded once.
 hipError_t expand_iq8(const void* codes, const float* scale, const float* zp, int N, int K, void* dst,
                       int dst_f16, hipStream_t s);
+// int8 x int8 GEMM: C = A[M,K] B[N,K]^T in int32 (written if C != null),
+// out = C * a_scale[m] * b_scale[n] in fp32.  K % 16 == 0.
+hipError_t a8w8_gemm(const void* A, const void* B, const float* a_scale, const float* b_scale,
+                     int32_t* C, float* out, int M, int N, int K, hipStream_t s);
 // int8 [n] -> float [n]
 hipError_t i8_to_f32(const void* src, float* dst, int64_t n, hipStream_t s);
 hipError_t pack_weights(const void* src, void* dst, int N, int K, hipStream_t s);
