@@ -12,10 +12,11 @@
 // bytes; chunk c of row r sits at position c ^ ((r >> 2) & 3), so the 16
 // rows one fragment read touches (same chunk) fall on distinct banks.
 //
-// K % 64 == 0 (every slice whole): the slices go straight to LDS instead
-// (direct-to-LDS copies, 1 KB = 16 rows per instruction, the swizzle
-// applied on the source side) into a ring of three stages, one LDS array
-// per stage, so that two slices are in flight during each step's MFMAs.
+// K % 64 == 0 (every slice whole): 256 x 128 tiles of 8 waves (4 x 2, each
+// still 64 x 64), the slices going straight to LDS instead (direct-to-LDS
+// copies, 1 KB = 16 rows per instruction, the swizzle applied on the source
+// side) into a ring of three stages, one LDS array per stage, so that two
+// slices are in flight during each step's MFMAs.
 
 #include "common.h"
 #include "kernels.h"
@@ -120,52 +121,54 @@ __global__ __launch_bounds__(256) void a8w8_gemm_kernel(const int8_t* __restrict
   }
 }
 
-// Direct-to-LDS variant (K % 64 == 0).  Each wave issues 2 copies of A and
-// 2 of B per stage (instructions w and w + 4 of the 8 per tile); rows past
-// M / N are clamped to the last row (computed, never stored).  Loads past
-// the last stage repeat it into a buffer that is not read again, so every
-// step waits for the same count.
+// Direct-to-LDS variant (K % 64 == 0).  Each wave issues 2 copies of A
+// (instructions w and w + 8 of the 16 per A tile) and 1 of B (instruction w
+// of 8) per stage; rows past M / N are clamped to the last row (computed,
+// never stored).  Loads past the last stage repeat it into a buffer that is
+// not read again, so every step waits for the same count.
 constexpr int kRing = 3;
+constexpr int kTileM = 256;
 constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
-__global__ __launch_bounds__(256) void a8w8_gemm_direct_kernel(const int8_t* __restrict__ A,
+__global__ __launch_bounds__(512) void a8w8_gemm_direct_kernel(const int8_t* __restrict__ A,
                                                                const int8_t* __restrict__ B,
                                                                const float* __restrict__ a_scale,
                                                                const float* __restrict__ b_scale,
                                                                int32_t* __restrict__ C,
                                                                float* __restrict__ out, int M, int N,
                                                                int K) {
-  __shared__ __attribute__((aligned(16))) int8_t A0[kTile * kStep];
-  __shared__ __attribute__((aligned(16))) int8_t A1[kTile * kStep];
-  __shared__ __attribute__((aligned(16))) int8_t A2[kTile * kStep];
+  __shared__ __attribute__((aligned(16))) int8_t A0[kTileM * kStep];
+  __shared__ __attribute__((aligned(16))) int8_t A1[kTileM * kStep];
+  __shared__ __attribute__((aligned(16))) int8_t A2[kTileM * kStep];
   __shared__ __attribute__((aligned(16))) int8_t B0[kTile * kStep];
   __shared__ __attribute__((aligned(16))) int8_t B1[kTile * kStep];
   __shared__ __attribute__((aligned(16))) int8_t B2[kTile * kStep];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * kTile, n0 = blockIdx.x * kTile;
+  const int m0 = blockIdx.y * kTileM, n0 = blockIdx.x * kTile;
   const int steps = K / kStep;
 
-  // the two copy instructions of this wave: rows 16j .. 16j+15, j = wave and
-  // wave + 4; lane l lands at row 16j + l/4, position l%4, holding source
-  // chunk (l%4) ^ ((row >> 2) & 3)
+  // this wave's copy instructions: A rows 16j .. 16j+15 for j = wave and
+  // wave + 8, B rows 16 wave ..; lane l lands at row 16j + l/4, position
+  // l%4, holding source chunk (l%4) ^ ((row >> 2) & 3)
   const int8_t* a_src[2];
-  const int8_t* b_src[2];
+  const int8_t* b_src;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int j = wave + 4 * h, r = 16 * j + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    a_src[h] = A + (size_t)min(m0 + r, M - 1) * K + 16 * c;
-    b_src[h] = B + (size_t)min(n0 + r, N - 1) * K + 16 * c;
+    const int j = wave + 8 * h, r = 16 * j + (lane >> 2);
+    a_src[h] = A + (size_t)min(m0 + r, M - 1) * K + 16 * ((lane & 3) ^ ((r >> 2) & 3));
+  }
+  {
+    const int r = 16 * wave + (lane >> 2);
+    b_src = B + (size_t)min(n0 + r, N - 1) * K + 16 * ((lane & 3) ^ ((r >> 2) & 3));
   }
   auto issue = [&](int s, int8_t* Ad, int8_t* Bd) {
     const size_t k0 = (size_t)min(s, steps - 1) * kStep;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = wave + 4 * h;
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[h] + k0), (lds_void*)(Ad + 1024 * j), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[h] + k0), (lds_void*)(Bd + 1024 * j), 16, 0, 0);
-    }
+    for (int h = 0; h < 2; ++h)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[h] + k0), (lds_void*)(Ad + 1024 * (wave + 8 * h)), 16,
+                                       0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(b_src + k0), (lds_void*)(Bd + 1024 * wave), 16, 0, 0);
   };
 
   i32x4 acc[4][4];
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(256) void a8w8_gemm_direct_kernel(const int8_t* __r
       // stage s + j landed for every wave (only stage s + j + 1 may be in
       // flight), and every wave is done with the buffer refilled next
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vm_wait(4));
+      __builtin_amdgcn_s_waitcnt(vm_wait(3));
       asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       const int nb = (j + 2) % kRing;
@@ -230,12 +233,13 @@ hipError_t a8w8_gemm(const void* A, const void* B, const float* a_scale, const f
                      int32_t* C, float* out, int M, int N, int K, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   if (M < 0 || N < 0 || K < 16 || K % 16 != 0) return hipErrorInvalidValue;
-  dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
   if (K % kStep == 0) {
-    a8w8_gemm_direct_kernel<<<grid, 256, 0, s>>>((const int8_t*)A, (const int8_t*)B, a_scale, b_scale, C, out,
+    dim3 grid((N + kTile - 1) / kTile, (M + kTileM - 1) / kTileM);
+    a8w8_gemm_direct_kernel<<<grid, 512, 0, s>>>((const int8_t*)A, (const int8_t*)B, a_scale, b_scale, C, out,
                                                  M, N, K);
     return hipGetLastError();
   }
+  dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
   a8w8_gemm_kernel<<<grid, 256, 0, s>>>((const int8_t*)A, (const int8_t*)B, a_scale, b_scale, C, out, M, N,
                                         K);
   return hipGetLastError();
