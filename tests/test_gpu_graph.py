@@ -64,6 +64,36 @@ def test_graph_tiny_decode():
     assert err.ok
 
 
+@pytest.mark.parametrize("kvd,wdt", [("u4", "bf16"), ("bf16", "iq8"), ("u8", "iq8")])
+def test_graph_tiny_decode_quantised(kvd, wdt):
+    # code caches and per-row int8 weights replay like the bf16 path
+    shape = dataclasses.replace(synth.TINY, name=f"tiny-{wdt}", intermediate=704, weight_dtype=wdt)
+    wl = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=shape, kv_dtype=kvd)
+    ctx = [0, 15, 16, 100, 511]
+    inp = synth.make_inputs(wl, seed=13, decode_batch=len(ctx), decode_ctx=ctx)
+    layer, kv, t = gpu_setup(inp)
+    log(f"[graph tiny decode {kvd} {wdt}] capture + replays")
+    y = replay_matches(lambda: gpu_call(inp, layer, kv, t), t["y"])
+    rows, ref, _ = run_oracle(inp)
+    err = compare(y.float().cpu().numpy()[rows], ref)
+    log(f"[graph tiny decode {kvd} {wdt}] vs oracle: {err}")
+    assert err.ok
+
+
+def test_graph_a8w8_gemm():
+    import torch
+    import transformer_decoder_layer_amd as tdl
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    A = torch.randint(-128, 128, (300, 512), generator=g, device="cuda", dtype=torch.int8)
+    B = torch.randint(-128, 128, (200, 512), generator=g, device="cuda", dtype=torch.int8)
+    sa = torch.rand(300, generator=g, device="cuda")
+    sb = torch.rand(200, generator=g, device="cuda")
+    out = torch.empty((300, 200), dtype=torch.float32, device="cuda")
+    log("[graph a8w8] capture + replays")
+    replay_matches(lambda: tdl.gemm_a8w8(A, B, sa, sb, out), out)
+
+
 def test_graph_tiny_prefill():
     wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], kv_dtype="bf16")
     inp = synth.make_inputs(wl, seed=12, prefill_len=77, spare_blocks=2)
