@@ -17,7 +17,7 @@ stack), each with
 its roofline fraction; and the oracle's CPU throughput on a bounded sample of
 the prefill.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 10]
 """
 from __future__ import annotations
 
@@ -46,7 +46,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=30)
     ap.add_argument("--prefill-len", type=int, default=4096)
     ap.add_argument("--cpu-tokens", type=int, default=4096,
@@ -426,13 +426,26 @@ def main():
         layer.prefill(x, y, 0, kv, table)
     torch.cuda.synchronize()
     log(f"prefill: timing {args.steps} steps")
+    # the K timed steps: wall clock between two synchronisations (value,
+    # ms_per_step) and a HIP-event pair around each call on its stream
+    # (median, p10, p90 of the per-call times)
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for e0, e1 in pev:
+        e0.record(stream)
         layer.prefill(x, y, 0, kv, table)
+        e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     tok_s = T * args.steps / (t1 - t0)
+    pcall = sorted(e0.elapsed_time(e1) for e0, e1 in pev)
+    prefill_call_ms = {"median": round(float(np.median(pcall)), 4),
+                       "p10": round(pcall[len(pcall) // 10], 4),
+                       "p90": round(pcall[(9 * len(pcall)) // 10], 4)}
+    log(f"prefill: {ms_step:.4f} ms/step wall, per call {prefill_call_ms}")
     # per-kernel durations from the library's HIP events (a separate pass: the
     # event records are kept out of the timed steps)
     layer.profile_enable(True)
@@ -583,6 +596,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "prefill_call_ms": prefill_call_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

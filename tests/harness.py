@@ -5,8 +5,8 @@ Tolerance (the bf16 bar): max |y - r| <= 2e-2 * max |r| and
 sum |y - r| / sum |r| <= 5e-3 (a normalised L1; a per-element ratio is
 ill-conditioned near zero).  The GPU tests apply it to the layer output y and
 to the stage buffers (RMSNorm output, rotated q, attention output, the
-attention branch h - x, the SwiGLU product), so a residual add cannot hide an
-error in a branch."""
+attention branch h - x, the SwiGLU product, the MLP branch y - h), so a
+residual add cannot hide an error in a branch."""
 from __future__ import annotations
 
 import dataclasses
@@ -44,6 +44,23 @@ def compare(y, ref) -> Err:
     assert np.all(np.isfinite(y)), "non-finite output"
     d = np.abs(y - ref)
     return Err(float(d.max()), float(np.abs(ref).max()), float(d.sum() / max(np.abs(ref).sum(), 1e-300)))
+
+
+def compare_branch_bf16(y, h, y_ref, h_ref) -> Err:
+    """The MLP branch y - h of a layer whose output y is bf16.  y is the GPU's
+    fp32 sum h + branch rounded once to bf16, so y - h carries up to half a
+    bf16 quantum of |y| that is no error of the branch; only the part of
+    |(y - h) - (y_ref - h_ref)| beyond that half quantum counts, against the
+    same bar as every other stage (relative to the branch, not to y)."""
+    y = np.asarray(y, np.float64)
+    h = np.asarray(h, np.float64)
+    br_ref = np.asarray(y_ref, np.float64) - np.asarray(h_ref, np.float64)
+    assert np.all(np.isfinite(y)), "non-finite output"
+    _, e = np.frexp(y)
+    half_quantum = np.ldexp(np.ones_like(y), np.maximum(e - 9, -134))
+    d = np.maximum(np.abs((y - h) - br_ref) - half_quantum, 0.0)
+    return Err(float(d.max()), float(np.abs(br_ref).max()),
+               float(d.sum() / max(np.abs(br_ref).sum(), 1e-300)))
 
 
 def unpack_u4(kt, vt):

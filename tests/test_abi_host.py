@@ -303,3 +303,25 @@ def test_kv_alloc_rejects_unaligned_memory_and_bad_block_size():
     assert tdl._kv_alloc(ctypes.byref(c), 0x100010, ctypes.byref(h)) == tdl.TDL_E_INVALID
     c = tdl.KvConfig(4, 32, 2, 64, tdl.TDL_BF16, 0)
     assert tdl._kv_alloc(ctypes.byref(c), 0x100000, ctypes.byref(h)) == tdl.TDL_E_UNSUPPORTED
+
+
+def test_gemm_a8w8_binding_checks_tensors():
+    # the Python wrapper refuses mismatched shapes, dtypes and host tensors
+    # before anything reaches the library
+    import torch
+    import transformer_decoder_layer_amd as tdl
+    M, N, K = 4, 8, 32
+    a = torch.zeros(M, K, dtype=torch.int8)
+    b = torch.zeros(N, K, dtype=torch.int8)
+    sa, sb = torch.ones(M), torch.ones(N)
+    out = torch.zeros(M, N)
+    with pytest.raises(ValueError, match="b: expected"):
+        tdl.gemm_a8w8(a, torch.zeros(N, K + 16, dtype=torch.int8), sa, sb, out)
+    with pytest.raises(ValueError, match="out: expected"):
+        tdl.gemm_a8w8(a, b, sa, sb, torch.zeros(M, N - 1))
+    with pytest.raises(ValueError, match="a_scale: expected"):
+        tdl.gemm_a8w8(a, b, sa.double(), sb, out)
+    with pytest.raises(ValueError, match="c_accum: expected"):
+        tdl.gemm_a8w8(a, b, sa, sb, out, c_accum=torch.zeros(M, N))
+    with pytest.raises(ValueError, match="contiguous GPU tensor"):
+        tdl.gemm_a8w8(a, b, sa, sb, out)

@@ -47,7 +47,8 @@ def test_qwen25_decode_b64_full():
 
 
 def test_qwen3_decode_u8_b128_sampled_seqs():
-    inp = synth.make_inputs(synth.WORKLOADS["qwen3_decode_u8_b128"])
+    # norm gains N(1, 0.1) (ln1, ln2, q_norm, k_norm) at the full size
+    inp = synth.make_inputs(synth.WORKLOADS["qwen3_decode_u8_b128"], random_gains=True)
     ctx = inp.batch.ctx_len
     seqs = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 17, 64, 101, 127})
     _check(inp, seqs, what="qwen3 u8 decode b128")

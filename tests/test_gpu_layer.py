@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from harness import compare, gpu_call, gpu_setup, run_oracle, unpack_u4
+from harness import compare, compare_branch_bf16, gpu_call, gpu_setup, run_oracle, unpack_u4
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +70,9 @@ def check_layer(inp, seqs=None, what="", stages=True, **setup):
         errs["o"] = compare(g["o"], st["o"])
         errs["h-x"] = compare(g["h"] - x_gpu, st["h"] - x)
         errs["a"] = compare(g["a"], st["a"])
+        # the down projection on its own (the residual would hide it: the MLP
+        # branch is a few percent of y in the small layers)
+        errs["y-h"] = compare_branch_bf16(y, g["h"], ref, st["h"])
     for k, e in errs.items():
         log(f"[{what}] {k}: {e}")
     bad = [k for k, e in errs.items() if not e.ok]
@@ -106,15 +109,19 @@ def check_cache_rows(inp, kv, cache, seqs):
 
 # ----------------------------------------------------------------- tiny ---
 
+# Norm gains: the tiny cases below draw ln1, ln2, q_norm and k_norm from
+# N(1, 0.1) (random_gains), so a dropped, swapped or mis-indexed gain multiply
+# in RMSNorm-1, RMSNorm-2 (also its split-sum form) or the Q/K norm fails.
+
 def test_tiny_prefill_no_cache():
-    inp = synth.make_inputs(synth.WORKLOADS["tiny_prefill_32"])
+    inp = synth.make_inputs(synth.WORKLOADS["tiny_prefill_32"], random_gains=True)
     check_layer(inp, what="tiny prefill 32")
 
 
 @pytest.mark.parametrize("T", [1, 45, 130])
 def test_tiny_prefill_paged(T):
     wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], kv_dtype="bf16")
-    inp = synth.make_inputs(wl, seed=T, prefill_len=T, spare_blocks=3)
+    inp = synth.make_inputs(wl, seed=T, prefill_len=T, spare_blocks=3, random_gains=True)
     layer, kv, t, cache, rows = check_layer(inp, what=f"tiny paged prefill {T}")
     check_cache_rows(inp, kv, cache, [0])
 
@@ -122,7 +129,8 @@ def test_tiny_prefill_paged(T):
 def test_tiny_chunked_prefill_start_pos():
     # a second chunk attends to the cached first chunk
     wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=TINY_Q3, kv_dtype="bf16")
-    inp = synth.make_inputs(wl, seed=5, prefill_len=37, prefill_start=83, spare_blocks=2)
+    inp = synth.make_inputs(wl, seed=5, prefill_len=37, prefill_start=83, spare_blocks=2,
+                            random_gains=True)
     layer, kv, t, cache, rows = check_layer(inp, what="tiny chunk start 83")
     check_cache_rows(inp, kv, cache, [0])
 
@@ -131,7 +139,7 @@ def test_tiny_chunked_prefill_start_pos():
 def test_tiny_decode_bf16(shape):
     wl = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=shape)
     ctx = [0, 1, 15, 16, 17, 31, 100, 250, 511, 1000]
-    inp = synth.make_inputs(wl, seed=3, decode_batch=len(ctx), decode_ctx=ctx)
+    inp = synth.make_inputs(wl, seed=3, decode_batch=len(ctx), decode_ctx=ctx, random_gains=True)
     layer, kv, t, cache, rows = check_layer(inp, what=f"decode bf16 {shape.name}")
     check_cache_rows(inp, kv, cache, range(len(ctx)))
 
@@ -139,7 +147,7 @@ def test_tiny_decode_bf16(shape):
 def test_tiny_decode_u8():
     wl = dataclasses.replace(synth.WORKLOADS["qwen3_decode_u8_b128"], shape=TINY_Q3)
     ctx = [1, 15, 16, 17, 64, 300, 777, 2048]
-    inp = synth.make_inputs(wl, seed=4, decode_batch=len(ctx), decode_ctx=ctx)
+    inp = synth.make_inputs(wl, seed=4, decode_batch=len(ctx), decode_ctx=ctx, random_gains=True)
     layer, kv, t, cache, rows = check_layer(inp, what="decode u8 tiny")
     check_cache_rows(inp, kv, cache, range(len(ctx)))
 
@@ -148,7 +156,7 @@ def test_tiny_decode_u8():
 def test_tiny_decode_u4(shape):
     wl = dataclasses.replace(synth.WORKLOADS["qwen3_decode_u4_b128"], shape=shape)
     ctx = [0, 1, 15, 16, 17, 64, 300, 777, 2048]
-    inp = synth.make_inputs(wl, seed=14, decode_batch=len(ctx), decode_ctx=ctx)
+    inp = synth.make_inputs(wl, seed=14, decode_batch=len(ctx), decode_ctx=ctx, random_gains=True)
     layer, kv, t, cache, rows = check_layer(inp, what=f"decode u4 {shape.name}")
     check_cache_rows(inp, kv, cache, range(len(ctx)))
 
@@ -173,9 +181,41 @@ def test_tiny_iq8_decode_prefill_mixed(shape):
 
 def test_tiny_mixed_q80():
     wl = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=TINY_Q80)
-    inp = synth.make_inputs(wl, seed=6, prefill_len=77, decode_batch=5, decode_ctx=[3, 16, 40, 129, 500])
+    inp = synth.make_inputs(wl, seed=6, prefill_len=77, decode_batch=5, decode_ctx=[3, 16, 40, 129, 500],
+                            random_gains=True)
     layer, kv, t, cache, rows = check_layer(inp, what="mixed q80 tiny")
     check_cache_rows(inp, kv, cache, range(6))
+
+
+@pytest.mark.parametrize("inter", [688, 736], ids=["I688", "I736"])
+def test_down_projection_branch(inter):
+    # The MLP branch made the larger part of y (down weights x32, x / 8: both
+    # powers of two, so bf16 inputs stay exact) so that y - h is compared at
+    # the plain bar: the down GEMM's K tails (688 = 10 x 64 + 48; 736 ends in
+    # a half 64-k stage) and the residual add on their own.
+    shape = dataclasses.replace(TINY_Q3, name=f"tiny-down-{inter}", intermediate=inter)
+    for kind in ("prefill", "decode"):
+        if kind == "prefill":
+            wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=shape, kv_dtype="bf16")
+            inp = synth.make_inputs(wl, seed=71, prefill_len=50, spare_blocks=1, random_gains=True)
+        else:
+            wl = dataclasses.replace(synth.WORKLOADS["qwen25_decode_b64"], shape=shape)
+            ctx = [0, 17, 200, 33]
+            inp = synth.make_inputs(wl, seed=72, decode_batch=len(ctx), decode_ctx=ctx,
+                                    random_gains=True)
+        inp.weights["wd"] = inp.weights["wd"] * np.float32(32)
+        inp.x[...] = inp.x / np.float32(8)
+        import torch
+        layer, kv, t = gpu_setup(inp)
+        gpu_call(inp, layer, kv, t)
+        torch.cuda.synchronize()
+        rows, (ref, st), _ = run_oracle(inp, want_stages=True)
+        y = t["y"].float().cpu().numpy()[rows]
+        h = gpu_stages(layer, t, rows, shape)["h"]
+        share = np.abs(ref - st["h"]).sum() / np.abs(ref).sum()
+        e = compare(y - h, ref - st["h"])
+        log(f"[down {inter} {kind}] branch share of y {share:.2f}; y-h: {e}")
+        assert share > 0.7 and e.ok, f"down projection {inter} {kind}: {e}"
 
 
 # ------------------------------------------------------ full-size shapes ---

@@ -434,6 +434,70 @@ def test_layer_single_token_closed_form():
     np.testing.assert_allclose(y[0], want, rtol=1e-12, atol=1e-12)
 
 
+def test_layer_two_token_closed_form_qk_norm_gains():
+    # T = 2 with per-head Q/K RMSNorm and distinct random gains everywhere
+    # (ln1, ln2, q_norm, k_norm).  Written as plain matrix algebra: RoPE as an
+    # explicit D x D rotation matrix per position, softmax over the two keys
+    # by hand.  Non-uniform gains do not commute with the rotation (pair
+    # members i and i + D/2 get different gains), so this fails if the Q/K
+    # norm runs after RoPE, if q_norm and k_norm are swapped, or if a gain is
+    # dropped.  [QWEN] section 2 (RMSNorm times the weight; RoPE on Q and K).
+    D, Hq, Hkv = 8, 4, 2
+    shape = tiny_shape(qkv_bias=False, qk_norm=True)
+    w = synth.make_weights(shape, seed=21, random_gains=True)
+    assert not np.allclose(w["q_norm"], w["k_norm"])
+    x = np.random.default_rng(22).standard_normal((2, 32))
+    y, st = run_prefill(shape, w, x)
+    W = {k: np.asarray(v, np.float64) for k, v in w.items()}
+
+    def rms(a, g):
+        return a / np.sqrt(np.mean(a * a) + 1e-6) * g
+
+    def rot(p):
+        R = np.zeros((D, D))
+        for i in range(D // 2):
+            ang = p * 1e4 ** (-2.0 * i / D)
+            c, s = np.cos(ang), np.sin(ang)
+            R[i, i], R[i, i + D // 2] = c, -s
+            R[i + D // 2, i], R[i + D // 2, i + D // 2] = s, c
+        return R
+
+    q = np.zeros((2, Hq, D))
+    k = np.zeros((2, Hkv, D))
+    v = np.zeros((2, Hkv, D))
+    for t in range(2):
+        xn = rms(x[t], W["ln1"])
+        qr, kr, vr = W["wq"] @ xn, W["wk"] @ xn, W["wv"] @ xn
+        for hh in range(Hq):
+            q[t, hh] = rot(t) @ rms(qr[hh * D:(hh + 1) * D], W["q_norm"])
+        for g in range(Hkv):
+            k[t, g] = rot(t) @ rms(kr[g * D:(g + 1) * D], W["k_norm"])
+            v[t, g] = vr[g * D:(g + 1) * D]
+    np.testing.assert_allclose(st["q"], q, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st["k"], k, rtol=1e-12, atol=1e-12)
+    want = np.zeros((2, 32))
+    for t in range(2):
+        o = np.zeros(Hq * D)
+        for hh in range(Hq):
+            g = hh // (Hq // Hkv)
+            if t == 0:
+                o[hh * D:(hh + 1) * D] = v[0, g]
+            else:
+                s0 = q[1, hh] @ k[0, g] / np.sqrt(D)
+                s1 = q[1, hh] @ k[1, g] / np.sqrt(D)
+                p0 = 1.0 / (1.0 + np.exp(s1 - s0))
+                o[hh * D:(hh + 1) * D] = p0 * v[0, g] + (1.0 - p0) * v[1, g]
+        h = x[t] + W["wo"] @ o
+        hn = rms(h, W["ln2"])
+        gte, up = W["wg"] @ hn, W["wu"] @ hn
+        want[t] = h + W["wd"] @ (gte / (1 + np.exp(-gte)) * up)
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12)
+    # the norm's gains matter here: swapping q_norm and k_norm changes q
+    w_sw = dict(w, q_norm=w["k_norm"], k_norm=w["q_norm"])
+    _, st_sw = run_prefill(shape, w_sw, x)
+    assert np.abs(st_sw["q"] - q).max() > 1e-3
+
+
 def test_layer_zero_branches():
     shape = tiny_shape()
     w = synth.make_weights(shape, seed=3)

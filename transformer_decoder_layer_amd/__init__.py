@@ -304,9 +304,25 @@ class KvCache:
 
 def gemm_a8w8(a, b, a_scale, b_scale, out, c_accum=None, stream=None):
     """out [M, N] float32 = (a [M, K] int8 @ b [N, K]^T int8, in int32) *
-    a_scale[m] * b_scale[n]; c_accum [M, N] int32 (optional) gets the sums."""
+    a_scale[m] * b_scale[n]; c_accum [M, N] int32 (optional) gets the sums.
+    Raises ValueError before the call when a tensor's shape, dtype, layout or
+    device does not match what the kernel reads and writes."""
+    import torch
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
     M, K = a.shape
     N = b.shape[0]
+    want = [("a", a, (M, K), torch.int8), ("b", b, (N, K), torch.int8),
+            ("a_scale", a_scale, (M,), torch.float32), ("b_scale", b_scale, (N,), torch.float32),
+            ("out", out, (M, N), torch.float32)]
+    if c_accum is not None:
+        want.append(("c_accum", c_accum, (M, N), torch.int32))
+    for name, t, shp, dt in want:
+        if tuple(t.shape) != shp or t.dtype != dt:
+            raise ValueError(f"{name}: expected {dt} {shp}, got {t.dtype} {tuple(t.shape)}")
+    for name, t, _, _ in want:
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
     _check("gemm_a8w8", _gemm_a8w8(_stream(stream), _ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale),
                                    _ptr(c_accum), _ptr(out), M, N, K))
 

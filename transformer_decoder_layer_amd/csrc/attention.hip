@@ -346,6 +346,18 @@ struct DecArgs {
 
 constexpr int kPartStride(int D) { return 16 * D + 32; }
 
+// Blocks of a decode sequence with ctx cached tokens (ctx + 1 keys), cut to
+// what the launch was sized for (max_parts partitions of part_blocks) and to
+// the block-table width: the device arrays are trusted, and this keeps a
+// context above the host's max_ctx_len bound inside the partition workspace,
+// the merge kernel's LDS and the table row.
+__device__ __forceinline__ int dec_blocks(const DecArgs& a, int ctx) {
+  int n = cdiv(max(ctx, 0) + 1, kBlockTokens);
+  n = min(n, a.max_parts * a.part_blocks);
+  if (a.seq.tables && a.seq.max_blocks > 0) n = min(n, a.seq.max_blocks);
+  return n;
+}
+
 template <int D, int F>
 struct DecFrags {
   // K rows (A operand): key lane%16.  bf16: one 16-byte chunk per product
@@ -574,9 +586,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   }
 
   // the sequence's context is cut into n_parts partitions of (nearly) equal
-  // size, at most part_blocks blocks each
-  const int n_keys = ctx + 1;
-  const int n_blk = cdiv(n_keys, kBlockTokens);
+  // size, at most part_blocks blocks each (a context beyond the host bound
+  // is cut to it: wrong output, but no access outside the workspace or the
+  // block table)
+  const int n_blk = dec_blocks(a, ctx);
+  const int n_keys = min(ctx + 1, n_blk * kBlockTokens);
   const int n_parts = cdiv(n_blk, a.part_blocks);
   if (p >= n_parts) return;
   const int part_size = cdiv(n_blk, n_parts);
@@ -822,7 +836,7 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(DecArgs a) {
   const int g = blockIdx.x, b = blockIdx.y;
   const int sidx = a.first_seq + b;
   const int n_rep = a.Hq / a.Hkv;
-  const int n_blk = cdiv(seq_ctx(a.seq, sidx) + 1, kBlockTokens);
+  const int n_blk = dec_blocks(a, seq_ctx(a.seq, sidx));
   const int n_parts = cdiv(n_blk, a.part_blocks);
   if (n_parts <= 1) return;
   const int row = seq_row(a.seq, sidx);
