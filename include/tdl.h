@@ -227,6 +227,23 @@ tdl_status layer_decode_paged(tdl_layer* layer, tdl_stream stream, const void* x
                               const int32_t* block_tables, int32_t max_blocks,
                               int32_t max_ctx_len, tdl_kv_cache* kv);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid hipMalloc): layer_decode_paged
+ * with the same arguments, kernels and results, whose split-K partial slices
+ * and decode partition results live in a static 32 MiB array the library
+ * holds on each GPU it runs on (until the process ends) instead of the
+ * layer's workspace.  Calls no hipMalloc, hipFree, event or synchronising
+ * function; records no stage timing; skips the TDL_DEBUG table check.  A
+ * step whose partial results exceed 32 MiB is TDL_E_CAPACITY (for example a
+ * Qwen3-8B-shaped layer at batch 128 over 8192-token contexts; a
+ * Qwen2.5-7B-shaped one at batch 64 needs about 10 MB).  Every call on a GPU
+ * shares that GPU's array (each call writes what it reads first): calls that
+ * overlap on one GPU, on any streams, race. */
+tdl_status layer_decode_paged_noalloc(tdl_layer* layer, tdl_stream stream, const void* x, void* y,
+                                      int32_t batch, const int32_t* ctx_lens,
+                                      const int32_t* block_tables, int32_t max_blocks,
+                                      int32_t max_ctx_len, tdl_kv_cache* kv);
+
 /* A mixed step over a tdl_batch: all rows go through the projections and the
  * MLP together; prefill sequences use the flash prefill attention kernel and
  * decode sequences the paged decode kernel.  x, y [n_rows, H] bf16. */

@@ -29,7 +29,8 @@ _DTYPES = {"bf16": TDL_BF16, "f32": TDL_F32, "q80": TDL_Q8_0, "u8": TDL_U8_ASYM,
 c_i32, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 P_i32 = ctypes.POINTER(ctypes.c_int32)
 
-EXPORTS = ["layer_create", "layer_destroy", "layer_prefill", "layer_decode_paged", "layer_step",
+EXPORTS = ["layer_create", "layer_destroy", "layer_prefill", "layer_decode_paged",
+           "layer_decode_paged_noalloc", "layer_step",
            "layer_workspace_view", "layer_profile_enable", "layer_profile_read", "stack_create",
            "stack_destroy", "stack_decode_paged", "kv_cache_bytes", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_view", "kv_block_table", "kv_block_release", "kv_block_share", "kv_block_refs",
@@ -97,6 +98,8 @@ _layer_destroy = _sig("layer_destroy", c_i32, c_vp)
 _layer_prefill = _sig("layer_prefill", c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp)
 _layer_decode = _sig("layer_decode_paged", c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32,
                      c_i32, c_vp)
+_layer_decode_na = _sig("layer_decode_paged_noalloc", c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp,
+                        c_i32, c_i32, c_vp)
 _layer_step = _sig("layer_step", c_i32, c_vp, c_vp, ctypes.POINTER(Batch), c_vp, c_vp, c_vp)
 _layer_ws = _sig("layer_workspace_view", c_i32, c_vp, ctypes.POINTER(WorkspaceView))
 _layer_prof_enable = _sig("layer_profile_enable", c_i32, c_vp, c_i32)
@@ -374,6 +377,14 @@ class Layer:
         _check("layer_decode_paged", _layer_decode(self._h, _stream(stream), _ptr(x), _ptr(y),
                                                    x.shape[0], _ptr(ctx_lens), _ptr(block_tables),
                                                    block_tables.shape[1], max_ctx_len, kv.handle))
+
+    def decode_paged_noalloc(self, x, y, ctx_lens, block_tables, max_ctx_len: int, kv: KvCache,
+                             stream=None):
+        """decode_paged with its partial results in the library's static
+        scratch (layer_decode_paged_noalloc: no device allocation)."""
+        _check("layer_decode_paged_noalloc",
+               _layer_decode_na(self._h, _stream(stream), _ptr(x), _ptr(y), x.shape[0], _ptr(ctx_lens),
+                                _ptr(block_tables), block_tables.shape[1], max_ctx_len, kv.handle))
 
     def step(self, x, y, q_start, q_len, ctx_len, block_tables, n_prefill_seqs: int, max_q_len: int,
              max_ctx_len: int, kv: KvCache, stream=None):

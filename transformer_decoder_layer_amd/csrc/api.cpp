@@ -19,11 +19,15 @@
 #include <cstring>
 #include <limits>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
 
 using namespace tdl;
+
+// The static scratch of layer_decode_paged_noalloc (see scratch_of below).
+static __device__ __align__(256) float scratch[(size_t(32) << 20) / sizeof(float)];
 
 namespace {
 
@@ -53,6 +57,37 @@ bool debug_checks() {
 }
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// ------------------------------------------------------ static scratch
+// Device memory of layer_decode_paged_noalloc: the split-K partial slices and
+// the decode partitions' partial results of a call live in this array
+// instead of the layer's workspace, for callers that cannot allocate.  Each
+// GPU the library runs on holds one copy, at its own address, until the
+// process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: kernels only ever receive the address hipGetSymbolAddress
+// returns for the current device (scratch_of).
+constexpr size_t kStaticScratchBytes = sizeof(scratch);  // 32 MiB per GPU
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+float* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up once per device (with
+// that device current) and kept.
+hipError_t scratch_of(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? (float*)p : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
 
 }  // namespace
 
@@ -240,9 +275,31 @@ KvPool pool_of(const tdl_layer* L, const tdl_kv_cache* kv) {
   return p;
 }
 
+// Where one call keeps its partial results: the split-K slices of the GEMMs
+// and the decode partitions' (O, m, l).  The layer's own workspace, or the
+// library's static scratch (layer_decode_paged_noalloc).  timed: per-stage
+// events may be recorded (layer_profile_enable).
+struct Scratch {
+  float* gemm_ws;
+  size_t gemm_floats;
+  float* dec_part;
+  size_t dec_floats;
+  bool timed;
+};
+Scratch own_scratch(tdl_layer* L) {
+  return Scratch{L->gemm_ws, L->gemm_ws_floats, L->dec_part, L->dec_part_floats, true};
+}
+
+// Weight format and plan of projection `mat` over M rows: int8 layers with an
+// expanded copy take it above kQ80CodeRows rows.
+int gemm_format(const tdl_layer* L, int mat, int M) {
+  const int wf = L->q80 ? kWQ80 : L->iq8 ? kWIQ8 : kWDense;
+  return (wf != kWDense && M > kQ80CodeRows && L->wexp[mat]) ? kWDense : wf;
+}
+
 // defer: a split-K plan leaves its fp32 partials in the GEMM workspace for
 // the next kernel to sum (*splits_out tells how many; 1 = C was written).
-tdl_status run_gemm(tdl_layer* L, hipStream_t st, int mat, int M, int N, int K, const void* A,
+tdl_status run_gemm(tdl_layer* L, const Scratch& sc, hipStream_t st, int mat, int M, int N, int K, const void* A,
                     const void* B, const __half* Bs, const float* Brs, const float* Brz,
                     const void* Bexp, int epi, const float* bias, const void* resid, int ldr, void* C,
                     int ldc, bool defer = false, int* splits_out = nullptr) {
@@ -259,7 +316,7 @@ tdl_status run_gemm(tdl_layer* L, hipStream_t st, int mat, int M, int N, int K, 
     return fail(TDL_E_UNSUPPORTED, "per-row int8 weights without an expanded copy at M=%d", M);
   const GemmPlan pl = gemm_plan(M, N, K, wf, epi);
   if (splits_out) *splits_out = defer ? pl.splits : 1;
-  if (pl.ws_floats > L->gemm_ws_floats)
+  if (pl.ws_floats > sc.gemm_floats)
     return fail(TDL_E_CAPACITY, "GEMM workspace too small for M=%d N=%d K=%d", M, N, K);
   GemmArgs a{};
   a.A = A;
@@ -277,7 +334,7 @@ tdl_status run_gemm(tdl_layer* L, hipStream_t st, int mat, int M, int N, int K, 
   a.ldr = ldr;
   a.C = C;
   a.ldc = ldc;
-  a.ws = L->gemm_ws;
+  a.ws = sc.gemm_ws;
   a.b_packed = packed;
   HIP_TRY(gemm_launch(pl, a, wf, epi, st, !defer));
   return TDL_OK;
@@ -307,7 +364,8 @@ struct StageTimer {
   tdl_layer* L;
   hipStream_t st;
   int mark;
-  StageTimer(tdl_layer* l, int stage, hipStream_t s) : L(l), st(s), mark(prof_begin(l, stage, s)) {}
+  StageTimer(tdl_layer* l, int stage, hipStream_t s, bool timed = true)
+      : L(l), st(s), mark(timed ? prof_begin(l, stage, s) : -1) {}
   ~StageTimer() {
     if (mark >= 0) (void)hipEventRecord(L->prof_pending[mark].b, st);
   }
@@ -318,20 +376,20 @@ struct StageTimer {
 // the paged decode kernel.
 constexpr int kFusedNormMaxH = 8192;  // hidden sizes the fused split-sum RMSNorm takes
 
-tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int rows, SeqInfo seq,
-                     KvPool pool, int n_prefill, int max_q_len, int dec_first, int n_dec,
-                     int max_ctx_len) {
+tdl_status run_layer(tdl_layer* L, const Scratch& sc, hipStream_t st, const void* x, void* y,
+                     int rows, SeqInfo seq, KvPool pool, int n_prefill, int max_q_len, int dec_first,
+                     int n_dec, int max_ctx_len) {
   const tdl_layer_config& c = L->cfg;
   const int H = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, I = c.intermediate;
   DecodePlan dp{};
   if (n_dec) {
     dp = decode_plan(n_dec, Hq, Hkv, D, max_ctx_len, pool.fmt);
-    if (dp.part_floats > L->dec_part_floats)
+    if (dp.part_floats > sc.dec_floats)
       return fail(TDL_E_CAPACITY, "decode workspace too small (batch %d, max_ctx_len %d)", n_dec,
                   max_ctx_len);
   }
   {
-    StageTimer t(L, TDL_STAGE_RMSNORM1, st);
+    StageTimer t(L, TDL_STAGE_RMSNORM1, st, sc.timed);
     HIP_TRY(rmsnorm_bf16in(x, L->ln1, L->xn, rows, H, c.rms_eps, st));
   }
   // a split QKV projection is summed (with its bias) by the RoPE kernel, and
@@ -339,46 +397,46 @@ tdl_status run_layer(tdl_layer* L, hipStream_t st, const void* x, void* y, int r
   // launches and no second round trip of the sums
   int qkv_splits = 1;
   {
-    StageTimer t(L, TDL_STAGE_QKV, st);
-    TRY(run_gemm(L, st, 0, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->wqkv_rs, L->wqkv_rz, L->wexp[0], EPI_BIAS_F32, L->bqkv, nullptr,
+    StageTimer t(L, TDL_STAGE_QKV, st, sc.timed);
+    TRY(run_gemm(L, sc, st, 0, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->wqkv_rs, L->wqkv_rz, L->wexp[0], EPI_BIAS_F32, L->bqkv, nullptr,
                  0, L->qkv, L->Nqkv, true, &qkv_splits));
   }
   {
-    StageTimer t(L, TDL_STAGE_ROPE_KV, st);
-    HIP_TRY(rope_kv_write(qkv_splits > 1 ? (const void*)L->gemm_ws : (const void*)L->qkv, rows, Hq, Hkv,
+    StageTimer t(L, TDL_STAGE_ROPE_KV, st, sc.timed);
+    HIP_TRY(rope_kv_write(qkv_splits > 1 ? (const void*)sc.gemm_ws : (const void*)L->qkv, rows, Hq, Hkv,
                           D, L->rope, c.qk_norm ? L->qn : nullptr, c.qk_norm ? L->kn : nullptr,
                           c.rms_eps, L->q, seq, pool, st, qkv_splits,
                           qkv_splits > 1 ? L->bqkv : nullptr));
   }
   if (n_prefill) {
-    StageTimer t(L, TDL_STAGE_ATTN_PREFILL, st);
+    StageTimer t(L, TDL_STAGE_ATTN_PREFILL, st, sc.timed);
     HIP_TRY(attn_prefill(L->q, pool, seq, n_prefill, max_q_len, Hq, Hkv, D, L->o, st));
   }
   if (n_dec) {
-    StageTimer t(L, TDL_STAGE_ATTN_DECODE, st);
-    HIP_TRY(attn_decode(dp, L->q, pool, seq, dec_first, n_dec, Hq, Hkv, D, L->o, L->dec_part, st));
+    StageTimer t(L, TDL_STAGE_ATTN_DECODE, st, sc.timed);
+    HIP_TRY(attn_decode(dp, L->q, pool, seq, dec_first, n_dec, Hq, Hkv, D, L->o, sc.dec_part, st));
   }
   int o_splits = 1;
   {
-    StageTimer t(L, TDL_STAGE_O_PROJ, st);
-    TRY(run_gemm(L, st, 1, rows, H, Hq * D, L->o, L->wo, L->wo_s, L->wo_rs, L->wo_rz, L->wexp[1], EPI_RESID_F32, nullptr, x, H, L->h,
+    StageTimer t(L, TDL_STAGE_O_PROJ, st, sc.timed);
+    TRY(run_gemm(L, sc, st, 1, rows, H, Hq * D, L->o, L->wo, L->wo_s, L->wo_rs, L->wo_rz, L->wexp[1], EPI_RESID_F32, nullptr, x, H, L->h,
                  H, H <= kFusedNormMaxH, &o_splits));
   }
   {
-    StageTimer t(L, TDL_STAGE_RMSNORM2, st);
+    StageTimer t(L, TDL_STAGE_RMSNORM2, st, sc.timed);
     if (o_splits > 1)
-      HIP_TRY(rmsnorm_splits_resid(L->gemm_ws, o_splits, x, L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
+      HIP_TRY(rmsnorm_splits_resid(sc.gemm_ws, o_splits, x, L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
     else
       HIP_TRY(rmsnorm_f32in(L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
   }
   {
-    StageTimer t(L, TDL_STAGE_GATE_UP, st);
-    TRY(run_gemm(L, st, 2, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, L->wgu_rs, L->wgu_rz, L->wexp[2], EPI_SILU_GATE, nullptr, nullptr, 0,
+    StageTimer t(L, TDL_STAGE_GATE_UP, st, sc.timed);
+    TRY(run_gemm(L, sc, st, 2, rows, 2 * I, H, L->hn, L->wgu, L->wgu_s, L->wgu_rs, L->wgu_rz, L->wexp[2], EPI_SILU_GATE, nullptr, nullptr, 0,
                  L->a, I));
   }
   {
-    StageTimer t(L, TDL_STAGE_DOWN, st);
-    TRY(run_gemm(L, st, 3, rows, H, I, L->a, L->wd, L->wd_s, L->wd_rs, L->wd_rz, L->wexp[3], EPI_RESID_BF16, nullptr, L->h, H, y, H));
+    StageTimer t(L, TDL_STAGE_DOWN, st, sc.timed);
+    TRY(run_gemm(L, sc, st, 3, rows, H, I, L->a, L->wd, L->wd_s, L->wd_rs, L->wd_rz, L->wexp[3], EPI_RESID_BF16, nullptr, L->h, H, y, H));
   }
   return TDL_OK;
 }
@@ -449,6 +507,12 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
     return fail(TDL_E_INVALID, "per-row int8 weights need every *_scale and *_zp pointer");
 
   hipStream_t st = (hipStream_t)stream;
+  {
+    // set-up of the static scratch on this device (layer_decode_paged_noalloc)
+    float* sp = nullptr;
+    const hipError_t e = scratch_of(&sp);
+    if (e != hipSuccess) return fail(TDL_E_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+  }
   tdl_layer* L = new tdl_layer();
   L->cfg = c;
   L->q80 = q80;
@@ -745,7 +809,7 @@ extern "C" tdl_status layer_prefill(tdl_layer* L, tdl_stream stream, const void*
   seq.ctx0 = start_pos;
   seq.tables = kv ? block_table : L->priv_table;
   seq.max_blocks = 0;
-  return run_layer(L, st, x, y, n_tokens, seq, pool_of(L, kv), 1, n_tokens, 0, 0, 0);
+  return run_layer(L, own_scratch(L), st, x, y, n_tokens, seq, pool_of(L, kv), 1, n_tokens, 0, 0, 0);
 }
 
 // Host-side checks of a decode step (nothing is enqueued).
@@ -769,10 +833,10 @@ tdl_status check_decode(const tdl_layer* L, const void* x, const void* y, int32_
   return check_kv_matches(L, kv);
 }
 
-tdl_status enqueue_decode(tdl_layer* L, hipStream_t st, const void* x, void* y, int32_t batch,
-                          const int32_t* ctx_lens, const int32_t* block_tables, int32_t max_blocks,
-                          int32_t max_ctx_len, tdl_kv_cache* kv) {
-  if (debug_checks())
+tdl_status enqueue_decode(tdl_layer* L, const Scratch& sc, hipStream_t st, const void* x, void* y,
+                          int32_t batch, const int32_t* ctx_lens, const int32_t* block_tables,
+                          int32_t max_blocks, int32_t max_ctx_len, tdl_kv_cache* kv) {
+  if (sc.timed && debug_checks())
     TRY(debug_check_tables(ctx_lens, nullptr, batch, 1, block_tables, max_blocks, kv->cfg.n_blocks,
                            max_ctx_len, st));
   SeqInfo seq{};
@@ -781,7 +845,7 @@ tdl_status enqueue_decode(tdl_layer* L, hipStream_t st, const void* x, void* y, 
   seq.tables = block_tables;
   seq.max_blocks = max_blocks;
   seq.rows_are_seqs = 1;
-  return run_layer(L, st, x, y, batch, seq, pool_of(L, kv), 0, 0, 0, batch, max_ctx_len);
+  return run_layer(L, sc, st, x, y, batch, seq, pool_of(L, kv), 0, 0, 0, batch, max_ctx_len);
 }
 
 extern "C" tdl_status layer_decode_paged(tdl_layer* L, tdl_stream stream, const void* x, void* y,
@@ -789,7 +853,38 @@ extern "C" tdl_status layer_decode_paged(tdl_layer* L, tdl_stream stream, const 
                                          const int32_t* block_tables, int32_t max_blocks,
                                          int32_t max_ctx_len, tdl_kv_cache* kv) {
   TRY(check_decode(L, x, y, batch, ctx_lens, block_tables, max_blocks, max_ctx_len, kv));
-  return enqueue_decode(L, (hipStream_t)stream, x, y, batch, ctx_lens, block_tables, max_blocks,
+  return enqueue_decode(L, own_scratch(L), (hipStream_t)stream, x, y, batch, ctx_lens, block_tables,
+                        max_blocks, max_ctx_len, kv);
+}
+
+// The same decode step with its partial results in the library's static
+// scratch (no allocation, no event, no synchronisation).
+extern "C" tdl_status layer_decode_paged_noalloc(tdl_layer* L, tdl_stream stream, const void* x,
+                                                 void* y, int32_t batch, const int32_t* ctx_lens,
+                                                 const int32_t* block_tables, int32_t max_blocks,
+                                                 int32_t max_ctx_len, tdl_kv_cache* kv) {
+  TRY(check_decode(L, x, y, batch, ctx_lens, block_tables, max_blocks, max_ctx_len, kv));
+  const tdl_layer_config& c = L->cfg;
+  const int H = c.hidden, QD = c.n_q_heads * c.head_dim, I = c.intermediate;
+  const int shapes[4][3] = {{L->Nqkv, H, EPI_BIAS_F32}, {H, QD, EPI_RESID_F32},
+                            {2 * I, H, EPI_SILU_GATE}, {H, I, EPI_RESID_BF16}};
+  size_t g = 0;
+  for (int m = 0; m < 4; ++m)
+    g = std::max(g, gemm_plan(batch, shapes[m][0], shapes[m][1], gemm_format(L, m, batch), shapes[m][2]).ws_floats);
+  const DecodePlan dp = decode_plan(batch, c.n_q_heads, c.n_kv_heads, c.head_dim, max_ctx_len,
+                                    pool_of(L, kv).fmt);
+  const size_t g_al = (g + 63) & ~size_t(63);  // partition results start 256-byte aligned
+  const size_t need = (g_al + dp.part_floats) * sizeof(float);
+  if (need > kStaticScratchBytes)
+    return fail(TDL_E_CAPACITY,
+                "decode step of batch %d, max_ctx_len %d needs %zu bytes of static scratch; the "
+                "maximum is %zu (use layer_decode_paged)",
+                batch, max_ctx_len, need, kStaticScratchBytes);
+  float* sp = nullptr;
+  const hipError_t e = scratch_of(&sp);
+  if (e != hipSuccess) return fail(TDL_E_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+  const Scratch sc{sp, g, sp + g_al, dp.part_floats, false};
+  return enqueue_decode(L, sc, (hipStream_t)stream, x, y, batch, ctx_lens, block_tables, max_blocks,
                         max_ctx_len, kv);
 }
 
@@ -860,8 +955,8 @@ extern "C" tdl_status stack_decode_paged(tdl_stack* S, tdl_stream stream, const 
     if (st != TDL_OK) return st;
   }
   for (int i = 0; i < n; ++i)
-    TRY(enqueue_decode(S->layers[i], (hipStream_t)stream, in_of(i), out_of(i), batch, ctx_lens,
-                       block_tables, max_blocks, max_ctx_len, kvs[i]));
+    TRY(enqueue_decode(S->layers[i], own_scratch(S->layers[i]), (hipStream_t)stream, in_of(i),
+                       out_of(i), batch, ctx_lens, block_tables, max_blocks, max_ctx_len, kvs[i]));
   return TDL_OK;
 }
 
@@ -900,7 +995,7 @@ extern "C" tdl_status layer_step(tdl_layer* L, tdl_stream stream, const tdl_batc
   seq.n_seqs = b->n_seqs;
   seq.tables = b->block_tables;
   seq.max_blocks = b->max_blocks;
-  return run_layer(L, st, x, y, b->n_rows, seq, pool_of(L, kv), b->n_prefill_seqs, b->max_q_len,
+  return run_layer(L, own_scratch(L), st, x, y, b->n_rows, seq, pool_of(L, kv), b->n_prefill_seqs, b->max_q_len,
                    b->n_prefill_seqs, n_dec, b->max_ctx_len);
 }
 
