@@ -255,6 +255,10 @@ class LayerInputs:
     batch: Batch
     cache_k: Optional[np.ndarray]  # [n_cached, Hkv, D] float32, tokens in (seq, pos) order
     cache_v: Optional[np.ndarray]
+    # u8 / u4 caches: rows [n, Hkv, D] the per-channel parameters are
+    # calibrated on; None: the cached tokens
+    calib_k: Optional[np.ndarray] = None
+    calib_v: Optional[np.ndarray] = None
 
 
 def make_inputs(wl: Workload, seed: int = 0, shape: Optional[LayerShape] = None,

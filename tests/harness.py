@@ -94,8 +94,10 @@ def oracle_cache(inp: synth.LayerInputs, seqs=None) -> Optional[oracle.PagedCach
         cache = oracle.PagedCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, "bf16")
     else:
         bits = 4 if wl.kv_dtype == "u4" else 8
-        kp = oracle.kv_calibrate(inp.cache_k, bits)
-        vp = oracle.kv_calibrate(inp.cache_v, bits)
+        ck = inp.cache_k if inp.calib_k is None else inp.calib_k
+        cv = inp.cache_v if inp.calib_v is None else inp.calib_v
+        kp = oracle.kv_calibrate(ck, bits)
+        vp = oracle.kv_calibrate(cv, bits)
         cache = oracle.PagedCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, wl.kv_dtype, kp, vp)
     if inp.cache_k is not None:
         seqs = range(b.n_seqs) if seqs is None else seqs
@@ -174,10 +176,12 @@ def gpu_setup(inp: synth.LayerInputs, max_tokens: Optional[int] = None, max_posi
     t["ctx_len"] = torch.from_numpy(b.ctx_len).cuda()
     if wl.kv_dtype != "none":
         kv = tdl.KvCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, wl.kv_dtype)
+        if inp.calib_k is not None and wl.kv_dtype in ("u8", "u4"):
+            kv.calibrate(torch.from_numpy(inp.calib_k).cuda(), torch.from_numpy(inp.calib_v).cuda())
         if inp.cache_k is not None:
             ck = torch.from_numpy(inp.cache_k).cuda()
             cv = torch.from_numpy(inp.cache_v).cuda()
-            if wl.kv_dtype in ("u8", "u4"):
+            if wl.kv_dtype in ("u8", "u4") and inp.calib_k is None:
                 kv.calibrate(ck, cv)
             cu = torch.from_numpy(np.concatenate([[0], np.cumsum(b.ctx_len)]).astype(np.int32)).cuda()
             zero = torch.zeros(b.n_seqs, dtype=torch.int32, device="cuda")

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtdl.so")
-SOURCES = ["api.cpp", "gemm.hip", "gemm_skinny.hip", "rowwise.hip", "attention.hip", "a8w8.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "gemm_skinny.hip", "rowwise.hip", "attention.hip",
+           "prefill_attention.hip", "a8w8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed-fp32-ops off: the compiler may not emit v_pk_{fma,mul,add}_f32
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

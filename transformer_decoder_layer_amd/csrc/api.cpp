@@ -153,6 +153,9 @@ struct tdl_layer {
   size_t gemm_ws_floats = 0;
   float* dec_part = nullptr;
   size_t dec_part_floats = 0;
+  _Float16* stage_k = nullptr;  // prefill staging copies of the new tokens' K / V
+  _Float16* stage_v = nullptr;
+  int stage_rows = 0;
   void* priv_k = nullptr;  // bf16 pool for calls without a KV cache
   void* priv_v = nullptr;
   int32_t* priv_table = nullptr;  // identity block table of the private pool
@@ -396,6 +399,7 @@ tdl_status run_layer(tdl_layer* L, const Scratch& sc, hipStream_t st, const void
   // a split output projection (with the residual) by RMSNorm-2: two fewer
   // launches and no second round trip of the sums
   int qkv_splits = 1;
+  PrefillStage stage{L->stage_k, L->stage_v, L->stage_rows, std::min(n_prefill, kStagedSeqs)};
   {
     StageTimer t(L, TDL_STAGE_QKV, st, sc.timed);
     TRY(run_gemm(L, sc, st, 0, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->wqkv_rs, L->wqkv_rz, L->wexp[0], EPI_BIAS_F32, L->bqkv, nullptr,
@@ -405,12 +409,12 @@ tdl_status run_layer(tdl_layer* L, const Scratch& sc, hipStream_t st, const void
     StageTimer t(L, TDL_STAGE_ROPE_KV, st, sc.timed);
     HIP_TRY(rope_kv_write(qkv_splits > 1 ? (const void*)sc.gemm_ws : (const void*)L->qkv, rows, Hq, Hkv,
                           D, L->rope, c.qk_norm ? L->qn : nullptr, c.qk_norm ? L->kn : nullptr,
-                          c.rms_eps, L->q, seq, pool, st, qkv_splits,
+                          c.rms_eps, L->q, seq, pool, stage, st, qkv_splits,
                           qkv_splits > 1 ? L->bqkv : nullptr));
   }
   if (n_prefill) {
     StageTimer t(L, TDL_STAGE_ATTN_PREFILL, st, sc.timed);
-    HIP_TRY(attn_prefill(L->q, pool, seq, n_prefill, max_q_len, Hq, Hkv, D, L->o, st));
+    HIP_TRY(attn_prefill(L->q, pool, seq, stage, n_prefill, max_q_len, Hq, Hkv, D, L->o, st));
   }
   if (n_dec) {
     StageTimer t(L, TDL_STAGE_ATTN_DECODE, st, sc.timed);
@@ -745,6 +749,16 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   const int max_dec = std::min(c.max_seqs, c.max_tokens);
   L->dec_part_floats = decode_part_need(c, max_dec);
   CTRY(dalloc(L, &L->dec_part, L->dec_part_floats * 4));
+  // prefill staging: K and V of the new tokens as fp16, zeroed once so that
+  // rows no call has written hold finite values
+  L->stage_rows = prefill_stage_rows(T);
+  {
+    const size_t sb = (size_t)KD * L->stage_rows * sizeof(_Float16);
+    CTRY(dalloc(L, &L->stage_k, sb));
+    CTRY(dalloc(L, &L->stage_v, sb));
+    CHIP(hipMemsetAsync(L->stage_k, 0, sb, st));
+    CHIP(hipMemsetAsync(L->stage_v, 0, sb, st));
+  }
   const size_t priv_blocks = (size_t)(T + 15) / 16;
   CTRY(dalloc(L, &L->priv_k, priv_blocks * KD * 16 * 2));
   CTRY(dalloc(L, &L->priv_v, priv_blocks * KD * 16 * 2));
@@ -787,8 +801,6 @@ extern "C" tdl_status layer_prefill(tdl_layer* L, tdl_stream stream, const void*
   if (!kv && start_pos != 0) return fail(TDL_E_INVALID, "start_pos > 0 needs a KV cache");
   if (kv && !block_table) return fail(TDL_E_INVALID, "a KV cache needs a block table");
   TRY(check_kv_matches(L, kv));
-  if (kv && kv->cfg.kv_dtype != TDL_BF16)
-    return fail(TDL_E_UNSUPPORTED, "prefill attention over a u8 / u4 cache is not implemented");
   const int total = start_pos + n_tokens;
   if (kv && total > kv->cfg.n_blocks * 16)
     return fail(TDL_E_CAPACITY, "sequence longer than the cache pool");
@@ -982,8 +994,6 @@ extern "C" tdl_status layer_step(tdl_layer* L, tdl_stream stream, const tdl_batc
   if (b->max_ctx_len > L->cfg.max_position)
     return fail(TDL_E_CAPACITY, "max_ctx_len exceeds max_position");
   TRY(check_kv_matches(L, kv));
-  if (kv->cfg.kv_dtype != TDL_BF16 && b->n_prefill_seqs > 0)
-    return fail(TDL_E_UNSUPPORTED, "prefill attention over a u8 / u4 cache is not implemented");
   hipStream_t st = (hipStream_t)stream;
   if (debug_checks())
     TRY(debug_check_tables(b->ctx_len, b->q_len, b->n_seqs, 1, b->block_tables, b->max_blocks,

@@ -1,4 +1,6 @@
-// Causal grouped-query attention over the block-paged KV cache.
+// Paged decode attention: grouped-query attention of one new token per
+// sequence over the block-paged KV cache (prefill attention is in
+// prefill_attention.hip).
 //
 // KV pool layout (elements): K [block][kv_head][slot 0..15][d] -- one head's
 // block is one contiguous tile (the per-block base address of the paged
@@ -6,7 +8,7 @@
 // [slot], so that the 16 tokens of a channel are contiguous and feed the
 // key-dimension of the P*V matrix product directly.
 //
-// Both kernels compute S^T = K * Q^T on the MFMA units (keys as rows), so
+// The kernel computes S^T = K * Q^T on the MFMA units (keys as rows), so
 // the softmax of one query row lives in one lane (plus its partner lanes),
 // and O^T = V^T * P^T, whose B operand is exactly the register layout the
 // first product leaves P in -- P never goes through LDS.  Scores are scaled
@@ -14,12 +16,7 @@
 // (running max m, denominator l, rescaled accumulator) of the TFFInfer page,
 // section 3.7.2 item 5, with the per-tile update written in full.
 //
-// Prefill: a workgroup owns one KV head and 32 query positions of one
-// sequence, with one wave per query head of the group: each 64-key K/V tile
-// is read from HBM once into LDS and used by every head that shares it (no
-// repeat_kv copy, cf. the Qwen2.5-7B page, section 3).
-//
-// Decode: a workgroup owns (sequence, KV head, context partition); its four
+// A workgroup owns (sequence, KV head, context partition); its four
 // waves walk the partition's blocks through the block table, one 16-token
 // block per step, with the whole query-head group packed into the 16 columns
 // of one MFMA tile.  u8 / u4 caches are dequantised in registers: a code c
@@ -41,27 +38,12 @@ namespace tdl {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.f;  // prefill softmax: slack of the running maximum (log2 units)
+constexpr float kLazy = 8.f;  // slack of the running maximum (log2 units)
 
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
-__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// bf16 / fp32 -> fp16, saturating at the fp16 range.  A bf16 value inside the
-// range converts exactly (8 significant bits fit in 11).
+// fp32 -> fp16, saturating at the fp16 range
 __device__ __forceinline__ f16 to_f16(float v) { return f32_to_f16_sat(v); }
-typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-// one packed convert of two bf16 cache values to fp16: exact inside the fp16
-// range, which is the prefill kernel's domain for K and V (|K|, |V| <=
-// 65504; no clamp -- it would cost the tile conversion 40% of its work and
-// would not make values outside the range correct either)
-__device__ __forceinline__ uint32_t bf16pair_to_f16pair(uint32_t w) {
-  const f32x2v v = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
-}
 
 __device__ __forceinline__ int seq_row(const SeqInfo& s, int sidx) {
   if (s.rows_are_seqs) return sidx;
@@ -78,258 +60,6 @@ __device__ __forceinline__ int seq_ctx(const SeqInfo& s, int sidx) {
 __device__ __forceinline__ int seq_block(const SeqInfo& s, int sidx, int lblk) {
   if (!s.tables) return lblk;
   return s.tables[(size_t)sidx * s.max_blocks + lblk];
-}
-
-// ================================================================ prefill
-constexpr int PQ = 32;   // query positions per workgroup
-constexpr int PK = 64;   // keys per tile
-
-// K and V tiles are held in LDS as fp16 (converted exactly from the bf16
-// cache): with fp16 query and probability operands the MFMA inputs carry 11
-// significant bits instead of bf16's 8, at the same MFMA rate.
-template <int D>
-struct PrefillSmem {
-  f16 k[2][PK * D];      // [key][d], 16-byte chunks XOR-swizzled by key
-  f16 vt[2][D * PK];     // [d][key], 8-byte units XOR-swizzled by d
-};
-
-template <int D>
-__device__ __forceinline__ int k_off(int key, int chunk) {  // chunk of 8 bf16
-  return key * D + ((chunk ^ (key & (D / 8 - 1))) << 3);
-}
-__device__ __forceinline__ int vt_off(int d, int unit) {  // unit of 4 bf16
-  return d * PK + ((unit ^ (d & 15)) << 2);
-}
-
-template <int D, int NREP>
-__global__ __launch_bounds__(NREP * 64) void attn_prefill_kernel(const float* __restrict__ q,
-                                                                 KvPool pool, SeqInfo seq, int Hq,
-                                                                 int Hkv, int n_qtiles, int paired,
-                                                                 f16* __restrict__ o) {
-  __shared__ __attribute__((aligned(16))) PrefillSmem<D> sm;
-  constexpr int n_rep = NREP;
-  constexpr int nthreads = NREP * 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = blockIdx.y;
-  const int sidx = blockIdx.z;
-  const int q_len = seq_qlen(seq, sidx);
-  const int ctx = seq_ctx(seq, sidx);
-  const int n_keys = ctx + q_len;  // keys in the cache
-  const int h = g * n_rep + wave;
-  const int ql = lane & 31, G = lane >> 5;
-  const int nq_seq = cdiv(q_len, PQ);  // this sequence's query tiles
-  const bf16* kpool = (const bf16*)pool.k;
-  const bf16* vpool = (const bf16*)pool.v;
-  constexpr int head_elems = kBlockTokens * D;
-  constexpr int K_CHUNKS = PK * D / 8;  // 16-byte chunks of K per tile
-  constexpr int V_CHUNKS = D * PK / 8;
-  constexpr int CHUNKS_PER_BLOCK = head_elems / 8;
-  constexpr int MAX_PER_T = (K_CHUNKS + V_CHUNKS + nthreads - 1) / nthreads;
-  const float sc = kLog2e * rsqrtf((float)D);
-  const int* tab = seq.tables + (size_t)sidx * seq.max_blocks;  // never null here
-
-  // paired mode: workgroup x takes query tiles x and n_qtiles-1-x (equal
-  // causal work per workgroup); otherwise the tiles in longest-first order
-  const int n_items = paired ? 2 : 1;
-  for (int item = 0; item < n_items; ++item) {
-    int qt;
-    if (paired) {
-      qt = item == 0 ? (int)blockIdx.x : n_qtiles - 1 - (int)blockIdx.x;
-      if (item == 1 && qt == (int)blockIdx.x) break;   // odd count: middle tile once
-    } else {
-      qt = n_qtiles - 1 - (int)blockIdx.x;
-    }
-    if (qt >= nq_seq) continue;  // uniform over the workgroup
-    const int row0 = seq_row(seq, sidx) + qt * PQ;
-    const int last_q = ctx + min(qt * PQ + PQ, q_len) - 1;  // last query position
-    const int n_tiles = cdiv(last_q + 1, PK);
-    const int first_q = ctx + qt * PQ;
-    const int my_q = first_q + ql;
-
-    // Q fragments: B operand of S^T = K Q^T; lane supplies q[ql][16s + 8G .. +7]
-    f16x8 qf[D / 16];
-    {
-      const bool valid = qt * PQ + ql < q_len;
-      const float* qp = q + ((size_t)(row0 + ql) * Hq + h) * D + 8 * G;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        f16x8 v{};
-        if (valid) {
-          const float4 a = *(const float4*)(qp + 16 * s), b = *(const float4*)(qp + 16 * s + 4);
-          v[0] = to_f16(a.x * sc); v[1] = to_f16(a.y * sc); v[2] = to_f16(a.z * sc);
-          v[3] = to_f16(a.w * sc); v[4] = to_f16(b.x * sc); v[5] = to_f16(b.y * sc);
-          v[6] = to_f16(b.z * sc); v[7] = to_f16(b.w * sc);
-        }
-        qf[s] = v;
-      }
-    }
-
-    // tile loader: the tile's four block-table entries are uniform loads;
-    // every chunk load is then unconditional (blocks past the sequence read
-    // block 0 and are zeroed when stored), so all loads are in flight at once
-    uint4 rk[MAX_PER_T];
-    int phys[PK / kBlockTokens];  // physical blocks of the tile to load next
-    // (loaded one tile ahead and not touched until the tile is fetched, so
-    // no wait on the table sits between the K/V loads and the MFMAs)
-    auto load_table = [&](int t) {
-#pragma unroll
-      for (int b = 0; b < PK / kBlockTokens; ++b) {
-        const int lblk = t * (PK / kBlockTokens) + b;
-        phys[b] = tab[lblk * kBlockTokens < n_keys ? lblk : 0];
-      }
-    };
-    auto load_tile = [&](int t) {
-#pragma unroll
-      for (int i = 0; i < MAX_PER_T; ++i) {
-        const int c = tid + i * nthreads;
-        if (c < K_CHUNKS + V_CHUNKS) {
-          const bool isk = c < K_CHUNKS;
-          const int cc = isk ? c : c - K_CHUNKS;
-          const int lb = cc / CHUNKS_PER_BLOCK, within = cc % CHUNKS_PER_BLOCK;
-          const bf16* src = (isk ? kpool : vpool) + ((size_t)phys[lb] * Hkv + g) * head_elems + within * 8;
-          rk[i] = *(const uint4*)src;
-        }
-      }
-    };
-    // convert to fp16 (keys past the end of the sequence become zero) and store
-    auto store_tile = [&](int t, int buf) {
-#pragma unroll
-      for (int i = 0; i < MAX_PER_T; ++i) {
-        const int c = tid + i * nthreads;
-        if (c >= K_CHUNKS + V_CHUNKS) continue;
-        const bool isk = c < K_CHUNKS;
-        const int cc = isk ? c : c - K_CHUNKS;
-        const int lb = cc / CHUNKS_PER_BLOCK, within = cc % CHUNKS_PER_BLOCK;
-        const int base_key = (t * (PK / kBlockTokens) + lb) * kBlockTokens;
-        uint32_t w[4] = {rk[i].x, rk[i].y, rk[i].z, rk[i].w};
-        if (isk) {
-          if (base_key + (within * 8) / D >= n_keys) w[0] = w[1] = w[2] = w[3] = 0;
-          const int key = lb * kBlockTokens + (within * 8) / D;
-          const int chunk = ((within * 8) % D) / 8;
-          *(uint4*)(&sm.k[buf][k_off<D>(key, chunk)]) =
-              make_uint4(bf16pair_to_f16pair(w[0]), bf16pair_to_f16pair(w[1]),
-                         bf16pair_to_f16pair(w[2]), bf16pair_to_f16pair(w[3]));
-        } else {
-          const int key0 = (within * 8) % kBlockTokens;  // 8 keys of one channel
-          if (base_key + kBlockTokens > n_keys) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (base_key + key0 + e >= n_keys) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-          const int d = (within * 8) / kBlockTokens;
-          const int unit = (lb * kBlockTokens + key0) / 4;  // even
-          *(u32x2*)(&sm.vt[buf][vt_off(d, unit)]) =
-              u32x2{bf16pair_to_f16pair(w[0]), bf16pair_to_f16pair(w[1])};
-          *(u32x2*)(&sm.vt[buf][vt_off(d, unit + 1)]) =
-              u32x2{bf16pair_to_f16pair(w[2]), bf16pair_to_f16pair(w[3])};
-        }
-      }
-    };
-
-    f32x16 acc[D / 32];
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
-
-    __syncthreads();  // the previous item's last tile may still be read
-    load_table(0);
-    load_tile(0);
-    load_table(1);
-    store_tile(0, 0);
-    __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
-      const int cur = t & 1;
-      // unconditional (a tile past the end reads valid blocks and is never
-      // stored), so no loaded register is merged across a branch
-      load_tile(t + 1);
-      load_table(t + 2);
-
-      // S^T for 64 keys x 32 queries: two independent 32-key halves
-      f32x16 st[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const f16x8 k0 = *(const f16x8*)(&sm.k[cur][k_off<D>(ql, 2 * s + G)]);
-        const f16x8 k1 = *(const f16x8*)(&sm.k[cur][k_off<D>(32 + ql, 2 * s + G)]);
-        st[0] = mfma32x32x16(k0, qf[s], st[0]);
-        st[1] = mfma32x32x16(k1, qf[s], st[1]);
-      }
-      // lane holds keys kh*32 + 8(r/4) + 4G + r%4 of query ql; keys past
-      // min(own position, last cached key) are masked (only near the
-      // diagonal and in the sequence's last tile)
-      const int key_base = t * PK;
-      if (key_base + PK - 1 > first_q || key_base + PK > n_keys) {
-        const int lim = min(my_q, n_keys - 1) - key_base - 4 * G;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            st[kh][r] = kh * 32 + 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : st[kh][r];
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, st[kh][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      // the reference point m_run of the exponentials moves only when a row's
-      // maximum exceeds it by more than kLazy (log2 units): softmax does not
-      // depend on it, P stays <= 2^kLazy (exact in fp16), and the rescale of
-      // the accumulators is skipped for the wave in most tiles
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int t2 = 0; t2 < D / 32; ++t2) acc[t2] *= alpha;
-      }
-      f16x8 pb[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // masked keys are -inf: exp2 gives 0
-          const float pv = __builtin_amdgcn_exp2f(st[kh][r] - m_run);
-          psum += pv;
-          pb[kh * 2 + (r >> 3)][r & 7] = (f16)pv;
-        }
-      l_run += psum;
-      // O^T += V^T P^T, 16 keys per MFMA: chunk kc covers keys kc*16 .. +15;
-      // lane supplies keys kc*16 + 4G + 0..3 and kc*16 + 8 + 4G + 0..3
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-        for (int t2 = 0; t2 < D / 32; ++t2) {
-          const int d = 32 * t2 + ql;
-          const u32x2 lo = *(const u32x2*)(&sm.vt[cur][vt_off(d, kc * 4 + G)]);
-          const u32x2 hi = *(const u32x2*)(&sm.vt[cur][vt_off(d, kc * 4 + 2 + G)]);
-          const uint4 w = make_uint4(lo[0], lo[1], hi[0], hi[1]);
-          acc[t2] = mfma32x32x16(__builtin_bit_cast(f16x8, w), pb[kc], acc[t2]);
-        }
-      }
-      // unconditional, so that its conversions can interleave with the PV
-      // MFMAs above: past the last tile it fills the idle buffer from valid
-      // blocks (the next query tile reloads both buffers after a barrier)
-      store_tile(t + 1, cur ^ 1);
-      __syncthreads();
-    }
-
-    l_run += __shfl_xor(l_run, 32, 64);
-    if (qt * PQ + ql < q_len) {
-      const float inv = 1.f / l_run;
-      f16* op = o + (size_t)(row0 + ql) * Hq * D + (size_t)h * D;
-#pragma unroll
-      for (int t2 = 0; t2 < D / 32; ++t2)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          f16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = to_f16(acc[t2][4 * a + e] * inv);
-          *(f16x4*)(op + 32 * t2 + 8 * a + 4 * G) = v4;
-        }
-    }
-  }
 }
 
 // ================================================================= decode
@@ -877,28 +607,6 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(DecArgs a) {
 }
 
 }  // namespace
-
-hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, int n_prefill, int max_q_len,
-                        int Hq, int Hkv, int D, void* o, hipStream_t s) {
-  if (n_prefill == 0 || max_q_len == 0) return hipSuccess;
-  const int n_qtiles = cdiv(max_q_len, PQ);
-  // pair tiles (x, n-1-x) when that still leaves a workgroup for every CU
-  const int paired = (long)cdiv(n_qtiles, 2) * Hkv * n_prefill >= 256 ? 1 : 0;
-  dim3 grid(paired ? cdiv(n_qtiles, 2) : n_qtiles, Hkv, n_prefill);
-  const int n_rep = Hq / Hkv;
-#define TDL_PREFILL_CASE(DD, NR)                                                               \
-  if (D == DD && n_rep == NR) {                                                                \
-    attn_prefill_kernel<DD, NR><<<grid, NR * 64, 0, s>>>((const float*)q, pool, seq, Hq, Hkv,  \
-                                                        n_qtiles, paired, (f16*)o);           \
-    return hipGetLastError();                                                                  \
-  }
-  TDL_PREFILL_CASE(128, 1) TDL_PREFILL_CASE(128, 2) TDL_PREFILL_CASE(128, 4)
-  TDL_PREFILL_CASE(128, 7) TDL_PREFILL_CASE(128, 8)
-  TDL_PREFILL_CASE(64, 1) TDL_PREFILL_CASE(64, 2) TDL_PREFILL_CASE(64, 4)
-  TDL_PREFILL_CASE(64, 7) TDL_PREFILL_CASE(64, 8)
-#undef TDL_PREFILL_CASE
-  return hipErrorInvalidValue;
-}
 
 DecodePlan decode_plan(int batch, int Hq, int Hkv, int D, int max_ctx_len, int fmt) {
   (void)Hq;

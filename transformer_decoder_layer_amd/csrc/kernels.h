@@ -129,15 +129,62 @@ struct KvPool {
   const int* v_zp;
 };
 
+// fp16 copies of the new tokens' K and V of the first n_seqs prefill
+// sequences of a call, in the prefill attention kernel's tile layout
+// (written by the RoPE kernel, read by prefill attention).  Per KV head g:
+// K rows [rows][D] at k + g * rows * D, element (r, d) at prefill_k_index;
+// V blocks of 16 rows at v + g * rows * D, element (r, d) at
+// prefill_v_index.  Row r of sequence i's chunk is prefill_stage_base(seq, i)
+// + r.  rows % 16 == 0.
+constexpr int kStagedSeqs = 64;  // prefill sequences of one call with a staged copy
+struct PrefillStage {
+  _Float16* k;
+  _Float16* v;
+  int rows;
+  int n_seqs;
+};
+// Staging rows sized for max_tokens new rows: every sequence starts on a
+// 16-row boundary, and the last tile of a sequence may read 64 rows on.
+__host__ __device__ constexpr int prefill_stage_rows(int max_tokens) {
+  return ((max_tokens + 16 * kStagedSeqs + 64) + 15) & ~15;
+}
+__device__ __forceinline__ int prefill_stage_base(const SeqInfo& s, int i) {
+  return s.q_start ? ((s.q_start[i] + 15 * i + 15) & ~15) : 0;
+}
+__device__ __forceinline__ int prefill_stage_vperm(int p) {  // an involution
+  return (p & 12) == 4 ? p + 4 : (p & 12) == 8 ? p - 4 : p;
+}
+// K: the 16-byte chunk c of row r sits at chunk c ^ swz(r).  A 128-byte-wide
+// read of 16 lanes (one chunk each, rows r..r+15 of one chunk column) then
+// touches 16 distinct chunk positions of the 64 four-byte LDS banks: rows of
+// 256 bytes (D = 128) take r & 15; rows of 128 bytes (D = 64, two rows per
+// bank line) take a swizzle distinct over the 8 rows of each parity.
+__device__ __forceinline__ int prefill_k_swz(int r, int D) {
+  return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+}
+__device__ __forceinline__ int prefill_k_index(int r, int d, int D) {
+  return r * D + ((((d >> 3) ^ prefill_k_swz(r, D))) << 3) + (d & 7);
+}
+// V: a block of 16 rows is two halves [2][D][8]; row r of the block goes to
+// half vperm(r) >> 3, place vperm(r) & 7 (the keys an MFMA lane group feeds
+// for one channel are one 16-byte piece, and a half's channels are
+// consecutive pieces).  Index relative to the tile or staging base.
+__device__ __forceinline__ int prefill_v_index(int r, int d, int D) {
+  const int vp = prefill_stage_vperm(r & 15);
+  return (r >> 4) * 16 * D + ((vp >> 3) * D + d) * 8 + (vp & 7);
+}
+
 // Per row of qkv (float32 [rows][(Hq+2Hkv)*D]): optional per-head RMSNorm of
 // q and k, RoPE of q and k (half-split pairs, cos/sin table [max_pos][D/2]),
 // q -> q_out [rows][Hq][D] float32, k and v -> the pool slot of the row's
 // position (rounded once, from fp32).  splits > 1: qkv holds that many fp32
 // partial slices [splits][rows][(Hq+2Hkv)*D] of the projection, summed here
 // in slice order, plus bias (may be null).
+// The rows of sequences < stage.n_seqs also write their K and V (the values
+// the cache holds, to fp16) into the prefill staging copy.
 hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, const float2* tab,
                          const float* q_norm, const float* k_norm, float eps, void* q_out,
-                         SeqInfo seq, KvPool pool, hipStream_t s, int splits = 1,
+                         SeqInfo seq, KvPool pool, PrefillStage stage, hipStream_t s, int splits = 1,
                          const float* bias = nullptr);
 
 // Writes caller K/V rows into the pool (kv_cache_write).
@@ -194,11 +241,12 @@ __host__ __device__ inline size_t packed_offset(int n, int k, int N) {
 }
 
 // ------------------------------------------------------------- attention
-// Flash prefill attention over sequences 0..n_prefill-1 of `seq`; K/V read
-// from the (bf16) pool through the tables.  q [rows][Hq][D] f32; o
-// [rows][Hq*D] fp16 (saturating).
-hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, int n_prefill, int max_q_len,
-                        int Hq, int Hkv, int D, void* o, hipStream_t s);
+// Flash prefill attention over sequences 0..n_prefill-1 of `seq`: keys
+// before each chunk from the pool (bf16, u8 or u4) through the tables, the
+// chunk's own keys from `st` (sequences < st.n_seqs) or from the pool.  q
+// [rows][Hq][D] f32; o [rows][Hq*D] fp16 (saturating).
+hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, PrefillStage st, int n_prefill,
+                        int max_q_len, int Hq, int Hkv, int D, void* o, hipStream_t s);
 
 // Paged decode attention for decode sequences first_seq .. first_seq+batch-1
 // (one query row each).  Each sequence's context is cut into partitions of

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
                                                       const float* __restrict__ qn,
                                                       const float* __restrict__ kn, float eps,
                                                       float* __restrict__ q_out, SeqInfo seq,
-                                                      KvPool pool, int splits,
+                                                      KvPool pool, PrefillStage stage, int splits,
                                                       const float* __restrict__ bias, int hpw) {
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -157,6 +157,9 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
   if (act) cs = tab[(size_t)pos * half + lane];
   const int blk = block_of(seq, sidx, pos);
   const int slot = pos % kBlockTokens;
+  // the row of the prefill staging copy (sequences < stage.n_seqs)
+  const bool staged = !seq.rows_are_seqs && sidx < stage.n_seqs;
+  const int srow = staged ? prefill_stage_base(seq, sidx) + row - (seq.q_start ? seq.q_start[sidx] : 0) : 0;
 
   // one wave per head: workgroup (row, y) takes heads hpw*y .. hpw*y + hpw-1
   for (int h = hpw * blockIdx.y + wave; h < min(Hq + Hkv, hpw * ((int)blockIdx.y + 1)); h += 4) {
@@ -186,6 +189,27 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     const int g = h - Hq;
     const int vc = (Hq + Hkv + g) * D;
     const float v1 = val(vc + ln), v2 = val(vc + ln + half);
+    if (staged && act) {
+      // fp16 copy of what the cache holds (bf16-rounded, or the dequantised
+      // code) for prefill attention
+      const int c1 = g * D + lane, c2 = c1 + half;
+      float sk1, sk2, sv1, sv2;
+      if (pool.fmt == kKvBf16) {
+        sk1 = (float)f32_to_bf16(r1); sk2 = (float)f32_to_bf16(r2);
+        sv1 = (float)f32_to_bf16(v1); sv2 = (float)f32_to_bf16(v2);
+      } else {
+        const int top = pool.fmt == kKvU8 ? 255 : 15;
+        sk1 = (float)(quant_code(r1, pool.k_scale[c1], pool.k_zp[c1], top) - pool.k_zp[c1]) * pool.k_scale[c1];
+        sk2 = (float)(quant_code(r2, pool.k_scale[c2], pool.k_zp[c2], top) - pool.k_zp[c2]) * pool.k_scale[c2];
+        sv1 = (float)(quant_code(v1, pool.v_scale[c1], pool.v_zp[c1], top) - pool.v_zp[c1]) * pool.v_scale[c1];
+        sv2 = (float)(quant_code(v2, pool.v_scale[c2], pool.v_zp[c2], top) - pool.v_zp[c2]) * pool.v_scale[c2];
+      }
+      const size_t hb = (size_t)g * stage.rows * D;
+      stage.k[hb + prefill_k_index(srow, lane, D)] = f32_to_f16_sat(sk1);
+      stage.k[hb + prefill_k_index(srow, lane + half, D)] = f32_to_f16_sat(sk2);
+      stage.v[hb + prefill_v_index(srow, lane, D)] = f32_to_f16_sat(sv1);
+      stage.v[hb + prefill_v_index(srow, lane + half, D)] = f32_to_f16_sat(sv2);
+    }
     if (pool.fmt != kKvU4) {
       if (act) {
         store_kv(pool, blk, g, Hkv, D, slot, lane, r1, v1);
@@ -523,14 +547,15 @@ hipError_t rmsnorm_f32in(const float* x, const float* g, void* y, int rows, int 
 
 hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, const float2* tab,
                          const float* q_norm, const float* k_norm, float eps, void* q_out,
-                         SeqInfo seq, KvPool pool, hipStream_t s, int splits, const float* bias) {
+                         SeqInfo seq, KvPool pool, PrefillStage stage, hipStream_t s, int splits,
+                         const float* bias) {
   if (rows == 0) return hipSuccess;
   // few rows (decode): four heads per workgroup for parallelism; many rows
   // (prefill): all heads of a row in one workgroup
   const int hpw = rows >= 1024 ? Hq + Hkv : 4;
   rope_kv_kernel<<<dim3(rows, cdiv(Hq + Hkv, hpw)), 256, 0, s>>>(
-      (const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps, (float*)q_out, seq, pool, splits, bias,
-      hpw);
+      (const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps, (float*)q_out, seq, pool, stage, splits,
+      bias, hpw);
   return hipGetLastError();
 }
 
