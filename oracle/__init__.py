@@ -16,7 +16,7 @@ Every step is written from the definition it cites.  Where the pages are
 silent or garbled the plainest reading is taken and named in the docstring.
 
 Parity status of each function (what pins it, see tests/test_oracle_*.py):
-  round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, iq8_expand, a8w8_gemm, kv_levels,
+  round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, q80_from_gguf, iq8_expand, a8w8_gemm, kv_levels,
   kv_calibrate, kv_quantize, kv_dequantize, attention, attention_online, PagedCache,
   layer_forward -- all pinned (worked examples, closed forms, brute force,
   special cases).  The pages' own printed layer output (Qwen2.5-7B-Instruct
@@ -69,6 +69,31 @@ def q80_expand(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     assert k % 32 == 0 and scales.shape == (n, k // 32)
     s = np.repeat(scales.astype(np.float64), 32, axis=1)
     return s * codes.astype(np.float64)
+
+
+def q80_from_gguf(raw, rows: int, cols: int):
+    """GGUF's interleaved Q8_0 tensor data to split arrays (int8 codes [rows,
+    cols], fp16 scales [rows, cols/32]).
+
+    [TFF] section 1.1 loads Qwen3-8B as a Q8_0 GGUF file; section 3.4's
+    block-aware strides store a row of `cols` values as cols/32 consecutive
+    blocks.  Reading of the block itself (the pages name it only): 34 bytes,
+    the scale as a little-endian IEEE binary16 first, then the 32 int8 codes
+    of columns 32b .. 32b+31 in order.  Parsed here one block at a time with
+    the struct module, independent of numpy's views.
+    """
+    import struct
+    raw = bytes(np.asarray(raw, np.uint8).tobytes()) if not isinstance(raw, (bytes, bytearray)) else bytes(raw)
+    assert cols % 32 == 0 and len(raw) == rows * (cols // 32) * 34
+    codes = np.empty((rows, cols), np.int8)
+    scales = np.empty((rows, cols // 32), np.float16)
+    for r in range(rows):
+        for b in range(cols // 32):
+            off = (r * (cols // 32) + b) * 34
+            (d,) = struct.unpack_from("<e", raw, off)
+            scales[r, b] = d
+            codes[r, 32 * b:32 * b + 32] = struct.unpack_from("<32b", raw, off + 2)
+    return codes, scales
 
 
 # --------------------------------------------------------------------------

@@ -144,6 +144,29 @@ def test_q80_expand_exact():
     assert list(oracle.q80_expand(c, s)[0, ::32]) == [1.0, 2.0, 4.0]
 
 
+def test_q80_from_gguf_hand_blocks():
+    """Hand-written 34-byte blocks (tests/golden/q80_gguf_blocks.json): the
+    scale bytes come first and are little-endian binary16, the codes are
+    signed, and a row's blocks precede the next row's."""
+    g = load("q80_gguf_blocks.json")
+    for case in g["cases"]:
+        raw = bytes.fromhex(case["hex"])
+        codes, scales = oracle.q80_from_gguf(raw, case["rows"], case["cols"])
+        assert codes.dtype == np.int8 and scales.dtype == np.float16
+        assert scales.astype(float).tolist() == case["scales"]
+        nb = case["cols"] // 32
+        heads = [codes[r, 32 * b:32 * b + 5].tolist() for r in range(case["rows"]) for b in range(nb)]
+        assert heads == case["codes_head"]
+        W = oracle.q80_expand(codes, scales)
+        vals = [W[r, 32 * b:32 * b + 5].tolist() for r in range(case["rows"]) for b in range(nb)]
+        assert vals == case["values_head"]
+    # every byte of a block lands somewhere: all 256 code bytes round-trip
+    raw = b"".join(b"\x00\x3c" + bytes(range(32 * i, 32 * i + 32)) for i in range(8))
+    codes, scales = oracle.q80_from_gguf(raw, 1, 256)
+    assert codes.view(np.uint8).tolist()[0] == list(range(256))
+    assert (scales == 1.0).all()
+
+
 # ------------------------------------------- per-channel int8 weights ---
 
 def test_iq8_expand_worked_example():
