@@ -84,6 +84,14 @@ def measured_traffic():
     return meta.get("traffic_bytes_per_launch")
 
 
+def layer_weight_bytes_q80(s):
+    """Bytes a Q8_0 layer keeps for its four projections: one byte per code
+    plus a 2-byte scale per 32 codes."""
+    qd, kd = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    n = (qd + 2 * kd) * s.hidden + s.hidden * qd + 3 * s.intermediate * s.hidden
+    return n + n // 32 * 2
+
+
 def linear_flops_per_token(s):
     D = s.head_dim
     n = (s.n_q_heads + 2 * s.n_kv_heads) * D * s.hidden + s.hidden * s.n_q_heads * D \
@@ -249,12 +257,17 @@ def other_workloads(args, torch, synth, tdl, stream, layer512):
     fl = linear_flops_per_token(shape) * rows + attention_flops(D, Hq, Tc * (Tc + 1) // 2 + B * (c0 + 1))
     assert torch.isfinite(y.float()).all(), "non-finite mixed-step output"
     out["qwen3_q80_mixed"] = {
-        "workload": "qwen3-8b-shaped layer with Q8_0 weights, mixed step: 2048-token chunked prefill + "
-                    "64 decode rows at ctx 2048, bf16 paged KV cache (Q8_0 codes convert exactly to fp16 "
-                    "MFMA operands, so the fp16 peak applies)",
+        "workload": "qwen3-8b-shaped layer with Q8_0 weights (codes + fp16 block scales only, 1.0625 "
+                    "bytes per weight), mixed step: 2048-token chunked prefill + 64 decode rows at ctx "
+                    "2048, bf16 paged KV cache.  The codes enter fp16/bf16 MFMAs exactly and each 32-input "
+                    "block's product is scaled in fp32, so the fp16 peak bounds this path; the int8 "
+                    "matrix peak is given beside it",
         "ms_per_step": round(ms, 4), "rows_per_s": round(rows / (ms * 1e-3), 1),
+        "weight_bytes": int(layer_weight_bytes_q80(shape)),
         "roofline": {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 1), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)},
+        "roofline_int8": {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 1), "peak": PEAK_INT8_TOPS,
+                          "unit": "TOP/s", "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)},
         "stages_ms": stage_profile(layer, step, 5)}
     log(f"q8_0 mixed: {ms * 1e3:.1f} us/step")
     layer.close()

@@ -188,10 +188,11 @@ typedef struct {
 /* Validates the configuration, allocates the library-owned weight copies and
  * workspace (sized by max_tokens / max_seqs), converts f32 weights to bf16
  * and interleaves gate/up rows for the fused SiLU-gate epilogue.  A Q8_0
- * layer with max_tokens > 128 also keeps each matrix expanded (code x scale
- * rounded once to fp16, bf16 for the down projection: about twice the
- * codes' memory) for calls of more than 128 rows, whose GEMMs are bound by
- * MFMA throughput; calls of up to 128 rows stream the 1-byte codes.
+ * layer keeps only its codes (repacked into 1 KB tiles of 16 rows x 64
+ * inputs where N % 16 == 0 and K % 64 == 0) and fp16 block scales, about
+ * 1.06 bytes per weight: every call multiplies exact fp16/bf16 copies of the
+ * codes on the matrix units and scales each 32-input block's product by its
+ * scale in fp32.
  * Synchronises `stream` before returning.  *out is NULL on failure.
  * TDL_E_UNSUPPORTED when min(max_seqs, max_tokens) > 2048 (decode sequences
  * in one call) or max_position > 131072. */
@@ -416,6 +417,22 @@ tdl_status kv_cache_write(tdl_kv_cache* kv, tdl_stream stream, int32_t n_seqs,
 tdl_status gemm_a8w8(tdl_stream stream, const void* A, const void* B, const float* a_scale,
                      const float* b_scale, int32_t* C_accum, float* out, int32_t M, int32_t N,
                      int32_t K);
+
+/* ---------------------------------------------------- GGUF Q8_0 import */
+
+/* Splits GGUF's interleaved Q8_0 tensor data into the arrays layer_create
+ * takes for TDL_Q8_0 weights.  The TFFInfer page loads Qwen3-8B as a Q8_0
+ * GGUF file (section 1.1) and stores a quantised row of `cols` values as
+ * cols/32 consecutive blocks (section 3.4, block-aware strides).  A block is
+ * 34 bytes: the scale as a little-endian IEEE binary16, then the 32 int8
+ * codes of columns 32b .. 32b+31 in order.
+ * blocks: rows * cols/32 blocks, row-major, 2-byte aligned; codes: int8
+ * [rows, cols], 16-byte aligned; scales: fp16 [rows, cols/32], 2-byte
+ * aligned (all device memory, caller-owned).  cols must be a positive
+ * multiple of 32; rows == 0 is a no-op.  A bit-exact copy; enqueued on the
+ * stream, no allocation, no synchronisation. */
+tdl_status q80_import_gguf(tdl_stream stream, const void* blocks, int64_t rows, int64_t cols,
+                           void* codes, void* scales);
 
 /* --------------------------------------------------------------- errors */
 

@@ -175,6 +175,19 @@ def make_weights(shape: LayerShape, seed: int = 0, random_gains: bool = False,
     return w
 
 
+def gguf_q80_bytes(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Serialises Q8_0 codes [rows, cols] int8 and scales [rows, cols/32]
+    float16 as GGUF-style interleaved blocks (uint8 [rows * cols/32 * 34]):
+    per block the scale's two little-endian bytes, then its 32 codes.  An
+    input generator for the import path (no arithmetic of the layer)."""
+    rows, cols = codes.shape
+    nb = cols // 32
+    blk = np.empty((rows, nb, 34), np.uint8)
+    blk[:, :, 0:2] = np.ascontiguousarray(scales.astype("<f2")).view(np.uint8).reshape(rows, nb, 2)
+    blk[:, :, 2:] = codes.reshape(rows, nb, 32).view(np.uint8)
+    return blk.reshape(-1)
+
+
 def make_x(rng: np.random.Generator, n_rows: int, hidden: int, bf16: bool = True) -> np.ndarray:
     x = _normal(rng, (n_rows, hidden))
     return to_bf16_values(x) if bf16 else x

@@ -325,3 +325,29 @@ def test_gemm_a8w8_binding_checks_tensors():
         tdl.gemm_a8w8(a, b, sa, sb, out, c_accum=torch.zeros(M, N))
     with pytest.raises(ValueError, match="contiguous GPU tensor"):
         tdl.gemm_a8w8(a, b, sa, sb, out)
+
+
+def test_q80_import_gguf_argument_checks():
+    # the wrapper refuses mismatched tensors; the C entry point refuses bad
+    # sizes, NULLs and misaligned pointers before any HIP call
+    import torch
+    import transformer_decoder_layer_amd as tdl
+    rows, cols = 3, 64
+    blocks = torch.zeros(rows * 2 * 34, dtype=torch.uint8)
+    codes = torch.zeros(rows, cols, dtype=torch.int8)
+    scales = torch.zeros(rows, 2, dtype=torch.float16)
+    with pytest.raises(ValueError, match="multiple of 32"):
+        tdl.q80_import_gguf(blocks, rows, 48, codes, scales)
+    with pytest.raises(ValueError, match="blocks: expected"):
+        tdl.q80_import_gguf(blocks[:-1], rows, cols, codes, scales)
+    with pytest.raises(ValueError, match="scales: expected"):
+        tdl.q80_import_gguf(blocks, rows, cols, codes, scales.float())
+    with pytest.raises(ValueError, match="contiguous GPU tensor"):
+        tdl.q80_import_gguf(blocks, rows, cols, codes, scales)
+    f = tdl._q80_gguf
+    assert f(None, None, 1, 48, None, None) == tdl.TDL_E_INVALID
+    assert f(None, None, -1, 64, None, None) == tdl.TDL_E_INVALID
+    assert f(None, None, 0, 64, None, None) == 0  # no rows: a no-op
+    assert f(None, None, 2, 64, None, None) == tdl.TDL_E_INVALID
+    assert f(None, 0x1001, 2, 64, 0x2000, 0x3000) == tdl.TDL_E_INVALID  # blocks odd
+    assert f(None, 0x1000, 2, 64, 0x2008, 0x3000) == tdl.TDL_E_INVALID  # codes not 16-byte aligned

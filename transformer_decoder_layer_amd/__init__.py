@@ -35,7 +35,8 @@ EXPORTS = ["layer_create", "layer_destroy", "layer_prefill", "layer_decode_paged
            "stack_destroy", "stack_decode_paged", "kv_cache_bytes", "kv_cache_alloc", "kv_cache_free",
            "kv_cache_view", "kv_block_table", "kv_block_release", "kv_block_share", "kv_block_refs",
            "kv_free_blocks", "kv_prefix_publish", "kv_prefix_match", "kv_prefix_evict", "kv_prefix_size",
-           "kv_cache_calibrate", "kv_cache_write", "gemm_a8w8", "tdl_status_string", "tdl_last_error"]
+           "kv_cache_calibrate", "kv_cache_write", "gemm_a8w8", "q80_import_gguf", "tdl_status_string",
+           "tdl_last_error"]
 
 
 class LayerConfig(ctypes.Structure):
@@ -119,6 +120,7 @@ _kv_match = _sig("kv_prefix_match", c_i32, c_vp, P_u64, c_i32, P_i32, P_i32)
 _kv_evict = _sig("kv_prefix_evict", c_i32, c_vp, c_i32)
 _kv_prefix_size = _sig("kv_prefix_size", c_i32, c_vp)
 _gemm_a8w8 = _sig("gemm_a8w8", c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32)
+_q80_gguf = _sig("q80_import_gguf", c_i32, c_vp, c_vp, ctypes.c_int64, ctypes.c_int64, c_vp, c_vp)
 _kv_calibrate = _sig("kv_cache_calibrate", c_i32, c_vp, c_vp, c_vp, c_vp, ctypes.c_int64)
 _kv_write = _sig("kv_cache_write", c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp,
                  c_vp, c_i32)
@@ -328,6 +330,25 @@ def gemm_a8w8(a, b, a_scale, b_scale, out, c_accum=None, stream=None):
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     _check("gemm_a8w8", _gemm_a8w8(_stream(stream), _ptr(a), _ptr(b), _ptr(a_scale), _ptr(b_scale),
                                    _ptr(c_accum), _ptr(out), M, N, K))
+
+
+def q80_import_gguf(blocks, rows: int, cols: int, codes, scales, stream=None):
+    """GGUF Q8_0 tensor data (blocks: uint8 [rows * cols/32 * 34], on the GPU)
+    -> codes int8 [rows, cols] and scales float16 [rows, cols/32], the arrays
+    a TDL_Q8_0 layer takes.  Raises ValueError before the call when a tensor's
+    shape, dtype, layout or device does not match."""
+    import torch
+    if cols <= 0 or cols % 32 != 0 or rows < 0:
+        raise ValueError("rows >= 0 and a positive multiple of 32 columns required")
+    want = [("blocks", blocks, (rows * (cols // 32) * 34,), torch.uint8),
+            ("codes", codes, (rows, cols), torch.int8), ("scales", scales, (rows, cols // 32), torch.float16)]
+    for name, t, shp, dt in want:
+        if tuple(t.shape) != shp or t.dtype != dt:
+            raise ValueError(f"{name}: expected {dt} {shp}, got {t.dtype} {tuple(t.shape)}")
+    for name, t, _, _ in want:
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    _check("q80_import_gguf", _q80_gguf(_stream(stream), _ptr(blocks), rows, cols, _ptr(codes), _ptr(scales)))
 
 
 def make_config(shape, max_tokens: int, max_seqs: int = 1, max_position: int = 8192) -> LayerConfig:

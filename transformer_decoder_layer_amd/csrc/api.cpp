@@ -237,7 +237,8 @@ struct GemmShapes {
 };
 
 // Largest split-K workspace over every row count a call may use.
-// (Q8_0 layers with expanded copies plan rows > kQ80CodeRows on those.)
+// (per-row int8 layers with expanded copies plan rows > kQ80CodeRows on
+// those; Q8_0 layers run on their codes at every row count.)
 constexpr int kQ80CodeRows = 128;
 void gemm_ws_need(const tdl_layer_config& c, int Nqkv, int wf, bool expanded, size_t* ws) {
   const int H = c.hidden, QD = c.n_q_heads * c.head_dim, I = c.intermediate;
@@ -246,7 +247,10 @@ void gemm_ws_need(const tdl_layer_config& c, int Nqkv, int wf, bool expanded, si
   size_t w = 0;
   for (int M = 1; M <= c.max_tokens; ++M) {
     const int f = expanded && M > kQ80CodeRows ? kWDense : wf;
-    for (auto& s : shapes) w = std::max(w, gemm_plan(M, s[0], s[1], f, s[2]).ws_floats);
+    for (auto& s : shapes) {
+      const bool packed = s[0] % 16 == 0 && s[1] % 64 == 0;  // as layer_create packs them
+      w = std::max(w, gemm_plan(M, s[0], s[1], f, s[2], f != kWDense && packed).ws_floats);
+    }
   }
   *ws = w;
 }
@@ -293,8 +297,8 @@ Scratch own_scratch(tdl_layer* L) {
   return Scratch{L->gemm_ws, L->gemm_ws_floats, L->dec_part, L->dec_part_floats, true};
 }
 
-// Weight format and plan of projection `mat` over M rows: int8 layers with an
-// expanded copy take it above kQ80CodeRows rows.
+// Weight format and plan of projection `mat` over M rows: per-row int8
+// layers take their expanded copy above kQ80CodeRows rows.
 int gemm_format(const tdl_layer* L, int mat, int M) {
   const int wf = L->q80 ? kWQ80 : L->iq8 ? kWIQ8 : kWDense;
   return (wf != kWDense && M > kQ80CodeRows && L->wexp[mat]) ? kWDense : wf;
@@ -308,7 +312,7 @@ tdl_status run_gemm(tdl_layer* L, const Scratch& sc, hipStream_t st, int mat, in
                     int ldc, bool defer = false, int* splits_out = nullptr) {
   int wf = L->q80 ? kWQ80 : L->iq8 ? kWIQ8 : kWDense;
   int packed = L->packed[mat];
-  // int8 layers: more than kQ80CodeRows rows take the expanded copy
+  // per-row int8 layers: more than kQ80CodeRows rows take the expanded copy
   if (wf != kWDense && M > kQ80CodeRows && Bexp) {
     wf = kWDense;
     B = Bexp;
@@ -317,7 +321,7 @@ tdl_status run_gemm(tdl_layer* L, const Scratch& sc, hipStream_t st, int mat, in
   }
   if (wf == kWIQ8 && M > kQ80CodeRows)
     return fail(TDL_E_UNSUPPORTED, "per-row int8 weights without an expanded copy at M=%d", M);
-  const GemmPlan pl = gemm_plan(M, N, K, wf, epi);
+  const GemmPlan pl = gemm_plan(M, N, K, wf, epi, wf != kWDense && packed);
   if (splits_out) *splits_out = defer ? pl.splits : 1;
   if (pl.ws_floats > sc.gemm_floats)
     return fail(TDL_E_CAPACITY, "GEMM workspace too small for M=%d N=%d K=%d", M, N, K);
@@ -614,30 +618,7 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
     CHIP(hipMemcpyAsync(L->wo_s, w->wo_scale, (size_t)H * (QD / 32) * 2, hipMemcpyDeviceToDevice, st));
     CHIP(hipMemcpyAsync(L->wd_s, w->wd_scale, (size_t)H * (I / 32) * 2, hipMemcpyDeviceToDevice, st));
     CHIP(interleave_gate_up(w->wg_scale, w->wu_scale, (int)rs, I, L->wgu_s, st));
-    if (c.max_tokens > kQ80CodeRows) {
-      // expanded copies for the compute-bound GEMMs (one packing temporary)
-      const int shapes[4][2] = {{L->Nqkv, H}, {H, QD}, {2 * I, H}, {H, I}};
-      const void* codes[4] = {L->wqkv, L->wo, L->wgu, L->wd};
-      const void* scales[4] = {L->wqkv_s, L->wo_s, L->wgu_s, L->wd_s};
-      bool ok = true;
-      size_t most = 0;
-      for (auto& sh : shapes) {
-        ok = ok && sh[0] % 16 == 0 && sh[1] % 64 == 0;
-        most = std::max(most, (size_t)sh[0] * sh[1] * 2);
-      }
-      if (ok) {
-        void* tmp = nullptr;
-        CTRY(dalloc(L, &tmp, most));
-        for (int i = 0; i < 4; ++i) {
-          CTRY(dalloc(L, &L->wexp[i], (size_t)shapes[i][0] * shapes[i][1] * 2));
-          CHIP(expand_q80(codes[i], scales[i], shapes[i][0], shapes[i][1], tmp, i != 3, st));
-          CHIP(pack_weights(tmp, L->wexp[i], shapes[i][0], shapes[i][1], st));
-        }
-        CHIP(hipStreamSynchronize(st));
-        L->allocs.erase(std::find(L->allocs.begin(), L->allocs.end(), tmp));
-        (void)hipFree(tmp);
-      }
-    }
+    CHIP(hipStreamSynchronize(st));
   }
   if (iq8) {
     // per-row scales (float32, copied) and zero points (int8 -> float), in
@@ -697,9 +678,12 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
       L->allocs.erase(std::find(L->allocs.begin(), L->allocs.end(), tmp));
       (void)hipFree(tmp);
     }
-    // the codes themselves in the stream kernel's packed layout where the
-    // shape allows (one contiguous 1 KB read per wave and stage); after the
-    // expansion above, which reads them row-major
+  }
+  if (codes) {
+    // the codes themselves in the packed code layout where the shape allows
+    // (the stream kernel: one contiguous 1 KB read per wave and stage; the
+    // large-M Q8_0 kernel: one direct 1 KB copy per 16 rows and 64 k); after
+    // any expansion above, which reads them row-major
     const int shapes[4][2] = {{L->Nqkv, H}, {H, QD}, {2 * I, H}, {H, I}};
     void* mats[4] = {L->wqkv, L->wo, L->wgu, L->wd};
     size_t most = 0;
@@ -882,7 +866,11 @@ extern "C" tdl_status layer_decode_paged_noalloc(tdl_layer* L, tdl_stream stream
                             {2 * I, H, EPI_SILU_GATE}, {H, I, EPI_RESID_BF16}};
   size_t g = 0;
   for (int m = 0; m < 4; ++m)
-    g = std::max(g, gemm_plan(batch, shapes[m][0], shapes[m][1], gemm_format(L, m, batch), shapes[m][2]).ws_floats);
+    {
+      const int f = gemm_format(L, m, batch);
+      g = std::max(g, gemm_plan(batch, shapes[m][0], shapes[m][1], f, shapes[m][2],
+                                f != kWDense && L->packed[m]).ws_floats);
+    }
   const DecodePlan dp = decode_plan(batch, c.n_q_heads, c.n_kv_heads, c.head_dim, max_ctx_len,
                                     pool_of(L, kv).fmt);
   const size_t g_al = (g + 63) & ~size_t(63);  // partition results start 256-byte aligned
@@ -1364,6 +1352,20 @@ extern "C" tdl_status gemm_a8w8(tdl_stream stream, const void* A, const void* B,
   if (K == 0 || K % 16 != 0) return fail(TDL_E_INVALID, "K must be a positive multiple of 16");
   if (((uintptr_t)A | (uintptr_t)B) & 15) return fail(TDL_E_INVALID, "A and B must be 16-byte aligned");
   HIP_TRY(tdl::a8w8_gemm(A, B, a_scale, b_scale, C_accum, out, M, N, K, (hipStream_t)stream));
+  return TDL_OK;
+}
+
+// ====================================================== GGUF Q8_0 import
+
+extern "C" tdl_status q80_import_gguf(tdl_stream stream, const void* blocks, int64_t rows, int64_t cols,
+                                      void* codes, void* scales) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0)
+    return fail(TDL_E_INVALID, "rows >= 0 and a positive multiple of 32 columns required");
+  if (rows == 0) return TDL_OK;
+  if (!blocks || !codes || !scales) return fail(TDL_E_INVALID, "NULL argument");
+  if (((uintptr_t)blocks & 1) || ((uintptr_t)scales & 1) || ((uintptr_t)codes & 15))
+    return fail(TDL_E_INVALID, "blocks and scales must be 2-byte aligned, codes 16-byte aligned");
+  HIP_TRY(tdl::q80_from_gguf(blocks, rows * (cols / 32), codes, scales, (hipStream_t)stream));
   return TDL_OK;
 }
 

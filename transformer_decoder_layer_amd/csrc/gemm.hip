@@ -50,6 +50,38 @@ __device__ __forceinline__ int swz(int row, int chunk) {  // offset in bf16 elem
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// Eight int8 codes (little-endian bytes of c) as an exact MFMA operand.
+// fp16: code + 128 is a byte u; the half with exponent byte 0x64 and u as its
+// low mantissa bits is 1024 + u (one byte permute per two codes), and
+// subtracting 1152 leaves the code exactly.  bf16 (7 fraction bits) cannot
+// hold 1024 + u: u goes through the byte-to-float conversion instead.
+template <typename T> struct Q80Codes;
+template <> struct Q80Codes<f16> {
+  __device__ static f16x8 cvt(uint2 c) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const uint32_t w[2] = {c.x ^ 0x80808080u, c.y ^ 0x80808080u};
+    f16x8 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // bytes (u0, 0x64, u1, 0x64) from (w, 0x64646464)
+      const uint32_t bits = __builtin_amdgcn_perm(0x64646464u, w[q >> 1], (q & 1) ? 0x04030402u : 0x04010400u);
+      const h2 v = __builtin_bit_cast(h2, bits) - h2{(_Float16)1152.f, (_Float16)1152.f};
+      o[2 * q] = v.x;
+      o[2 * q + 1] = v.y;
+    }
+    return o;
+  }
+};
+template <> struct Q80Codes<bf16> {
+  __device__ static bf16x8 cvt(uint2 c) {
+    const uint32_t w[2] = {c.x ^ 0x80808080u, c.y ^ 0x80808080u};
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)((w[e >> 2] >> (8 * (e & 3))) & 0xffu) - 128.f);
+    return o;
+  }
+};
+
 
 // Result of one wave's FM x FN accumulator block whose top-left output
 // element is (mw, nw): v[i][j][r] = C[mw + i*16 + 4*(lane/16) + r][nw + j*16 +
@@ -270,11 +302,17 @@ __device__ __forceinline__ size_t tail_offset(const GemmArgs& p, int tail, int s
 // applied on the source side.  B: weights in the packed tile layout
 // (pack_weights); one load instruction copies one 1 KB tile as is, and a
 // B fragment is then chunk `lane` of a tile in LDS (linear, conflict-free).
-// Needs K % 64 == 0 and packed bf16/fp16 weights.
+// Q8_0 (Q80 && DIRECT): the codes in the packed code layout (pack_codes),
+// one 1 KB tile per 16 rows and 64 k; a lane's 16 bytes hold its fragments
+// of both 32-k steps, converted exactly to the operand type after the LDS
+// read; each lane loads its columns' two block scales per tile into
+// registers, one tile ahead, and every 32-k step's MFMA product is scaled by
+// its block's scale in fp32 (the Q8_0 arithmetic, no rounded weight copy).
+// Needs K % 64 == 0 and packed weights.
 template <int BM, int BN, int WM, int WN, bool Q80, int EPI, typename T, bool DIRECT>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   typedef typename Mfma<T>::v8 T8;
-  static_assert(!(DIRECT && Q80), "direct loads carry bf16/fp16 weights only");
+  constexpr bool Q80D = Q80 && DIRECT;
   constexpr int NW = WM * WN;
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -291,9 +329,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   // from reads of the other and does not wait for the fill
   __shared__ __attribute__((aligned(16))) T As0[BM * BK];
   __shared__ __attribute__((aligned(16))) T As1[BM * BK];
-  __shared__ __attribute__((aligned(16))) T Bs0[BN * BK];
-  __shared__ __attribute__((aligned(16))) T Bs1[BN * BK];
-  __shared__ float Ss[Q80 ? 2 : 1][Q80 ? BN * 2 : 1];
+  // (Q8_0 direct: BN rows of 64 one-byte codes)
+  __shared__ __attribute__((aligned(16))) T Bs0[Q80D ? BN * BK / 2 : BN * BK];
+  __shared__ __attribute__((aligned(16))) T Bs1[Q80D ? BN * BK / 2 : BN * BK];
+  __shared__ float Ss[Q80 && !DIRECT ? 2 : 1][Q80 && !DIRECT ? BN * 2 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -379,10 +418,22 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
       const T* src = A + (size_t)grow * p.lda + k0 + ((pc ^ (row & 7)) << 3);
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&Ad[i * 512], 16, 0, 0);
     }
+    const int NG = p.N >> 4;
+    if constexpr (Q80D) {
+      // codes: instruction i copies the tile of row group i (groups past N
+      // repeat the last one: computed, never stored)
+      const int8_t* __restrict__ Bq = (const int8_t*)p.B;
+#pragma unroll
+      for (int i = wave; i < BN / 16; i += NW) {
+        const int grp = min((n0 >> 4) + i, NG - 1);
+        const int8_t* src = Bq + ((size_t)kt * NG + grp) * 1024 + lane * 16;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&Bd[i * 512], 16, 0, 0);
+      }
+      return;
+    }
     // B: instruction i copies tile (k slice i / (BN/16), row group i % (BN/16));
     // groups past N repeat the last one (computed, never stored)
     const T* __restrict__ B = (const T*)p.B;
-    const int NG = p.N >> 4;
 #pragma unroll
     for (int i = wave; i < BN / 8; i += NW) {
       const int ks = (k0 >> 5) + i / (BN / 16);
@@ -443,6 +494,44 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Q8_0 direct: this lane's block scales (two fp16 per column, for the two
+  // 32-k steps of tile kt), columns past N clamped
+  auto load_scales = [&](int kt, uint32_t (&sc)[FN]) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = min(n0 + wn * WTN + j * 16 + col_l, p.N - 1);
+      sc[j] = *(const uint32_t*)(p.B_scale + (size_t)n * (p.K / 32) + 2 * kt);
+    }
+  };
+  // one k-tile of MFMAs from a Q8_0 direct stage
+  auto compute_q80 = [&](const T* Ab, const T* Bb, const uint32_t (&sc)[FN]) {
+    uint2 bq[FN][2];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const uint4 c = *(const uint4*)((const int8_t*)Bb + ((wn * WTN + j * 16) / 16) * 1024 + lane * 16);
+      bq[j][0] = make_uint2(c.x, c.y);
+      bq[j][1] = make_uint2(c.z, c.w);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      T8 af[FM];
+      const int ch = kk * 4 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *(const T8*)(&Ab[swz(wm * WTM + i * 16 + (lane & 15), ch)]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const T8 bfr = Q80Codes<T>::cvt(bq[j][kk]);
+        const float s = __half2float(__ushort_as_half((unsigned short)(sc[j] >> (16 * kk))));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const f32x4 t = Mfma<T>::mma(af[i], bfr, f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[i][j] += t * s;
+        }
+      }
+    }
+  };
+
   // one k-tile of MFMAs from the given LDS stage
   auto compute = [&](const T* Ab, const T* Bb, int sbuf) {
 #pragma unroll
@@ -472,7 +561,34 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
     }
   };
 
-  if constexpr (DIRECT) {
+  if constexpr (Q80D) {
+    // as below, with each stage's block scales in registers beside it
+    uint32_t sc0[FN], sc1[FN];
+    if (kt0 < kt1) {
+      issue_tile(kt0, As0, Bs0);
+      load_scales(kt0, sc0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      if (kt + 1 < kt1) {
+        issue_tile(kt + 1, As1, Bs1);
+        load_scales(kt + 1, sc1);
+      }
+      compute_q80(As0, Bs0, sc0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kt + 1 < kt1) {
+        if (kt + 2 < kt1) {
+          issue_tile(kt + 2, As0, Bs0);
+          load_scales(kt + 2, sc0);
+        }
+        compute_q80(As1, Bs1, sc1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  } else if constexpr (DIRECT) {
     // stage 0 holds tile kt, stage 1 tile kt+1; the fill of the next tile
     // runs while this one feeds the MFMAs
     if (kt0 < kt1) issue_tile(kt0, As0, Bs0);
@@ -649,7 +765,7 @@ constexpr Cfg kCfgs[kNumCfgs] = {{256, 256, 1.0f}, {256, 224, 0.96f}, {128, 128,
 template <bool Q80, int EPI, typename T, bool DIRECT>
 hipError_t launch_cfg2(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
   switch (cfg) {
-    case 0:  // the planner gives the eight-wave tiles bf16/fp16 weights only
+    case 0:  // the planner gives the eight-wave 256x256 tiles bf16/fp16 weights only
       if constexpr (!Q80) gemm_kernel<256, 256, 2, 4, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
       else return hipErrorInvalidValue;
       break;
@@ -667,7 +783,7 @@ hipError_t launch_cfg2(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
       else return hipErrorInvalidValue;
       break;
     case 6:
-      if constexpr (!Q80) gemm_kernel<192, 256, 2, 4, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
+      if constexpr (!Q80 || DIRECT) gemm_kernel<192, 256, 2, 4, Q80, EPI, T, DIRECT><<<grid, 512, 0, s>>>(a);
       else return hipErrorInvalidValue;
       break;
     case 3:
@@ -682,13 +798,10 @@ hipError_t launch_cfg2(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
 
 template <bool Q80, int EPI, typename T>
 hipError_t launch_cfg(int cfg, int grid, const GemmArgs& a, hipStream_t s) {
-  if constexpr (!Q80) {
-    if (a.b_packed) {
-      if (a.K % BK != 0 || a.N % 16 != 0) return hipErrorInvalidValue;
-      return launch_cfg2<Q80, EPI, T, true>(cfg, grid, a, s);
-    }
+  if (a.b_packed) {
+    if (a.K % BK != 0 || a.N % 16 != 0) return hipErrorInvalidValue;
+    return launch_cfg2<Q80, EPI, T, true>(cfg, grid, a, s);
   }
-  if (a.b_packed) return hipErrorInvalidValue;  // Q8_0 codes are row-major
   return launch_cfg2<Q80, EPI, T, false>(cfg, grid, a, s);
 }
 
@@ -734,7 +847,7 @@ hipError_t tail_reduce(const GemmPlan& pl, const GemmArgs& a, int epi, hipStream
 // Chooses the tile configuration and split-K factor with the lowest estimated
 // time: rounds of workgroups over the 256 CUs times the per-workgroup work,
 // divided by the configuration's relative efficiency.
-GemmPlan gemm_plan(int M, int N, int K, int wf, int epi) {
+GemmPlan gemm_plan(int M, int N, int K, int wf, int epi, bool packed) {
   const bool q80 = wf == kWQ80;  // per-row int8 has no large-M kernel: callers expand it
   constexpr int kCUs = 256;
   {
@@ -748,7 +861,10 @@ GemmPlan gemm_plan(int M, int N, int K, int wf, int epi) {
     const Cfg c = kCfgs[cfg];
     if (cfg == 1 && (epi == EPI_SILU_GATE || N % 224 != 0)) continue;
     if (cfg == 5 && (epi == EPI_SILU_GATE || N % 288 != 0)) continue;
-    if (q80 && (cfg <= 1 || cfg >= 5)) continue;  // Q8_0 staging needs the register path
+    // Q8_0: row-major codes take the four-wave register path; packed codes
+    // also the eight-wave 192x256 tiles (the larger eight-wave tiles would
+    // spill with the scales and codes beside the accumulators)
+    if (q80 && (cfg <= 1 || cfg == 5 || (!packed && cfg == 6))) continue;
     if ((cfg == 3 || cfg == 4) && M > 128) continue;  // the decode shapes only
     if (cfg == 3 && M > 64) continue;
     const int tiles = cdiv(M, c.BM) * cdiv(N, c.BN);

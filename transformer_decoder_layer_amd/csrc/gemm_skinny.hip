@@ -77,9 +77,10 @@ void gemm_stream_kernel(GemmArgs p) {
   constexpr int AE = MT * 16 * kStageK;              // A elements per slice and stage
   constexpr int A_CHUNKS = 2 * MT;                   // 1 KB direct loads per slice and stage
   constexpr int A_PER_WAVE = (A_CHUNKS + RW - 1) / RW;  // per wave (the last chunk repeats)
-  // packed per-row int8 codes: one 16-byte load per stage (both 32-k steps)
-  constexpr bool IQ8P = IQ8 && PACKED;
-  constexpr int LOADS = A_PER_WAVE + FN * (IQ8P ? 1 : 2 * (Q80 ? 2 : 1));  // vector-memory ops per stage
+  // packed int8 codes: one 16-byte load per stage (both 32-k steps), plus the
+  // two block scales for Q8_0
+  constexpr bool IQ8P = IQ8 && PACKED, Q80P = Q80 && PACKED;
+  constexpr int LOADS = A_PER_WAVE + FN * (IQ8P ? 1 : Q80P ? 3 : 2 * (Q80 ? 2 : 1));  // vector-memory ops per stage
   // separate arrays (not one indexed array): the compiler can then tell that
   // reading one buffer does not depend on the loads still filling another
   // (arrays past NS are never referenced and take no LDS)
@@ -162,7 +163,7 @@ void gemm_stream_kernel(GemmArgs p) {
     for (int q = 0; q < A_PER_WAVE; ++q)
       __builtin_amdgcn_global_load_lds((const void*)(a_src[q] + a_off), (lds_void*)&ring[a_dst[q]], 16, 0,
                                        0);
-    if constexpr (IQ8P) {
+    if constexpr (IQ8P || Q80P) {
       // tile (stage, row group): one contiguous 1 KB read per wave
 #pragma unroll
       for (int f = 0; f < FN; ++f) {
@@ -170,6 +171,11 @@ void gemm_stream_kernel(GemmArgs p) {
                                         ((size_t)st * (p.N >> 4) + (b_row[f] >> 4)) * 1024 + lane * 16);
         b[f][0].codes = make_uint2(c.x, c.y);
         b[f][1].codes = make_uint2(c.z, c.w);
+        if constexpr (Q80P) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            b[f][u].scale = *(const uint16_t*)(p.B_scale + b_row[f] * (p.ldb / 32) + min(2 * st + u, KS32 - 1));
+        }
       }
       return;
     }
@@ -387,12 +393,9 @@ hipError_t launch_stream2(int grid, int epi, const GemmArgs& a, hipStream_t s) {
 
 template <int WF, int MT, int KW, int RW, int NS>
 hipError_t launch_stream(int grid, int epi, const GemmArgs& a, hipStream_t s) {
-  if constexpr (WF == kWIQ8) {
+  if constexpr (WF != kWDense) {
     return a.b_packed ? launch_stream2<WF, MT, KW, RW, NS, true>(grid, epi, a, s)
                       : launch_stream2<WF, MT, KW, RW, NS, false>(grid, epi, a, s);
-  } else if constexpr (WF != kWDense) {
-    if (a.b_packed) return hipErrorInvalidValue;  // Q8_0 codes stay row-major
-    return launch_stream2<WF, MT, KW, RW, NS, false>(grid, epi, a, s);
   } else {
     return a.b_packed ? launch_stream2<kWDense, MT, KW, RW, NS, true>(grid, epi, a, s)
                       : launch_stream2<kWDense, MT, KW, RW, NS, false>(grid, epi, a, s);

@@ -72,7 +72,9 @@ struct GemmPlan {
   int tail_kps;
   int rng_count;      // decode-sized kernel: row ranges
 };
-GemmPlan gemm_plan(int M, int N, int K, int wf, int epi);
+// packed: B in the packed tile layout (Q8_0 codes: pack_codes), which opens
+// the direct-load tiles to Q8_0.
+GemmPlan gemm_plan(int M, int N, int K, int wf, int epi, bool packed = false);
 // Decode-sized M (<= 128, K % 32 == 0): weights streamed straight from HBM
 // into MFMA operands, activations shared through LDS (cfg >= 100).
 bool skinny_plan(int M, int N, int K, int wf, int epi, GemmPlan* pl);
@@ -218,6 +220,9 @@ hipError_t copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 // (dst_f16 = 1, saturating) or bf16: code * scale rounded to nearest even.
 hipError_t expand_q80(const void* codes, const void* scales, int N, int K, void* dst, int dst_f16,
                       hipStream_t s);
+// GGUF Q8_0 blocks [n_blocks][34 bytes] (2-byte aligned) -> codes
+// [n_blocks * 32] int8 (16-byte aligned) and scales [n_blocks] fp16, a copy.
+hipError_t q80_from_gguf(const void* blocks, int64_t n_blocks, void* codes, void* scales, hipStream_t s);
 // Per-row int8 codes [N][K], scale [N] and zero point [N] (as floats) ->
 // dst [N][K] fp16 (saturating) or bf16: (code - zp) * scale rounded once.
 hipError_t expand_iq8(const void* codes, const float* scale, const float* zp, int N, int K, void* dst,

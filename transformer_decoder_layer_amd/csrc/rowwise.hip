@@ -601,6 +601,31 @@ hipError_t expand_q80(const void* codes, const void* scales, int N, int K, void*
   return hipGetLastError();
 }
 
+// GGUF Q8_0 blocks (34 bytes: binary16 scale, then 32 int8 codes) to split
+// codes and scales; one thread per block, blocks in row-major order map to
+// codes at 32 i and scales at i.  Reads in 2-byte words (the blocks are only
+// 2-byte aligned), writes the codes as two 16-byte stores.
+__global__ void q80_gguf_kernel(const uint16_t* __restrict__ blocks, int64_t n, int8_t* __restrict__ codes,
+                                uint16_t* __restrict__ scales) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const uint16_t* b = blocks + 17 * i;
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = (uint32_t)b[1 + 2 * j] | ((uint32_t)b[2 + 2 * j] << 16);
+    scales[i] = b[0];
+    uint4* dst = (uint4*)(codes + 32 * i);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+hipError_t q80_from_gguf(const void* blocks, int64_t n_blocks, void* codes, void* scales, hipStream_t s) {
+  if (n_blocks == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((n_blocks + 255) / 256, 4096);
+  q80_gguf_kernel<<<grid, 256, 0, s>>>((const uint16_t*)blocks, n_blocks, (int8_t*)codes, (uint16_t*)scales);
+  return hipGetLastError();
+}
+
 hipError_t expand_iq8(const void* codes, const float* scale, const float* zp, int N, int K, void* dst,
                       int dst_f16, hipStream_t s) {
   if (K % 8 != 0) return hipErrorInvalidValue;
