@@ -17,7 +17,8 @@ silent or garbled the plainest reading is taken and named in the docstring.
 
 Parity status of each function (what pins it, see tests/test_oracle_*.py):
   round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, q80_from_gguf, iq8_expand, a8w8_gemm, kv_levels,
-  kv_calibrate, kv_quantize, kv_dequantize, attention, attention_online, PagedCache,
+  kv_calibrate, kv_quantize, kv_dequantize, kv_block_exponent, kv_quantize_block,
+  attention, attention_online, PagedCache (per-channel and per-block x per-channel),
   layer_forward -- all pinned (worked examples, closed forms, brute force,
   special cases).  The pages' own printed layer output (Qwen2.5-7B-Instruct
   weights, [QWEN] section "运行结果") cannot be reproduced without those
@@ -251,9 +252,49 @@ def kv_quantize(x, scale, zp, n_bits: int = 8) -> np.ndarray:
     return np.clip(q, 0, kv_levels(n_bits)).astype(np.uint8)
 
 
-def kv_dequantize(codes, scale, zp) -> np.ndarray:
-    """x ~ (Q_c - zero_point_c) * scale_c ([HET] section 2.6)."""
-    return (np.asarray(codes, np.float64) - zp.astype(np.float64)) * scale.astype(np.float64)
+def kv_dequantize(codes, scale, zp, e=0) -> np.ndarray:
+    """x ~ (Q_c - zero_point_c) * scale_c ([HET] section 2.6), times 2^e for
+    a block with a per-block factor (kv_block_exponent)."""
+    return (np.asarray(codes, np.float64) - zp.astype(np.float64)) * scale.astype(np.float64) * 2.0 ** e
+
+
+KV_MAX_BLOCK_EXP = 7
+
+
+def kv_block_exponent(x, scale, zp, n_bits: int = 8) -> int:
+    """Per-block factor of a block's per-channel parameters, 2^e.
+
+    [HET] section 2.4 pairs the int8 / uint4 KV cache with scales managed per
+    channel and per block, and the paged kernel of section 4.3 dequantises a
+    block with its own scales[b].  Reading taken: a block keeps the pool's
+    per-channel (scale_c, zero_point_c) and multiplies the scale by a
+    power of two 2^e of its own (per KV head, separately for K and V), e the
+    smallest integer in [0, KV_MAX_BLOCK_EXP] for which no value x of the
+    block (x: [n, D] for one head) clamps: zero_point_c + round(q * 2^-e) is
+    in [0, L] with q = x / scale_c (float32, correctly rounded, then scaled
+    exactly by the power of two; round half to even).  e = 0 keeps the
+    per-channel quantiser exactly; a larger e widens the block's range around
+    the zero point for values beyond the calibrated one.  If no e in the
+    range fits, e = KV_MAX_BLOCK_EXP (the rest clamps).
+    """
+    L = (1 << n_bits) - 1
+    q = (np.asarray(x, np.float32) / np.asarray(scale, np.float32)).astype(np.float32)
+    zp = np.asarray(zp, np.int64)
+    for e in range(KV_MAX_BLOCK_EXP + 1):
+        r = np.rint(q.astype(np.float64) * 2.0 ** -e).astype(np.int64) + zp
+        if np.all((r >= 0) & (r <= L)):
+            return e
+    return KV_MAX_BLOCK_EXP
+
+
+def kv_quantize_block(x, scale, zp, e: int, n_bits: int = 8) -> np.ndarray:
+    """Codes of values x in a block with factor 2^e: clamp(zero_point_c +
+    round(q * 2^-e), 0, L), q = x / scale_c in float32 (kv_block_exponent);
+    e = 0 is kv_quantize."""
+    L = (1 << n_bits) - 1
+    q = (np.asarray(x, np.float32) / np.asarray(scale, np.float32)).astype(np.float32)
+    r = np.rint(q.astype(np.float64) * 2.0 ** -e).astype(np.int64) + np.asarray(zp, np.int64)
+    return np.clip(r, 0, L).astype(np.uint8)
 
 
 # --------------------------------------------------------------------------
@@ -273,9 +314,15 @@ class PagedCache:
     """
 
     def __init__(self, n_blocks: int, n_kv_heads: int, head_dim: int, dtype: str,
-                 k_params=None, v_params=None):
+                 k_params=None, v_params=None, block_scales: bool = False):
         assert dtype in ("bf16", "u8", "u4")
+        assert not block_scales or dtype != "bf16"
         self.dtype = dtype
+        self.block_scales = block_scales
+        # per (block, kv head) exponents of K and V (kv_block_exponent); 0
+        # for every block until a call writes its first slot
+        self.ek = np.zeros((n_blocks, n_kv_heads), np.int64)
+        self.ev = np.zeros((n_blocks, n_kv_heads), np.int64)
         self.n_bits = 4 if dtype == "u4" else 8
         self.n_blocks, self.n_kv_heads, self.head_dim = n_blocks, n_kv_heads, head_dim
         shape = (n_blocks, n_kv_heads, BLOCK_SIZE, head_dim)
@@ -299,15 +346,43 @@ class PagedCache:
 
     def write(self, table_row, t: int, k, v):
         """Store token t's K and V ([n_kv_heads, head_dim] real values),
-        rounded to the cache dtype."""
+        rounded to the cache dtype (with block scales: the block's current
+        factor)."""
         blk, off = self.location(table_row, t)
         if self.dtype == "bf16":
             self.k[blk, :, off, :] = round_bf16(k)
             self.v[blk, :, off, :] = round_bf16(v)
+        elif self.block_scales:
+            for g in range(self.n_kv_heads):
+                self.k[blk, g, off, :] = kv_quantize_block(k[g], self.k_scale[g], self.k_zp[g],
+                                                           int(self.ek[blk, g]), self.n_bits)
+                self.v[blk, g, off, :] = kv_quantize_block(v[g], self.v_scale[g], self.v_zp[g],
+                                                           int(self.ev[blk, g]), self.n_bits)
+            self.written[blk, off] = True
         else:
             self.k[blk, :, off, :] = kv_quantize(k, self.k_scale, self.k_zp, self.n_bits)
             self.v[blk, :, off, :] = kv_quantize(v, self.v_scale, self.v_zp, self.n_bits)
             self.written[blk, off] = True
+
+    def write_tokens(self, table_row, start: int, ks, vs):
+        """One call's new tokens of one sequence: positions start ..
+        start+n-1 get ks[i], vs[i] ([n, n_kv_heads, head_dim]).  With block
+        scales, a block whose first slot this call writes takes its factor
+        from the tokens this call writes into it (kv_block_exponent, per KV
+        head, K and V separately) before they are stored; tokens written into
+        a block by a later call use the factor it has."""
+        n = len(ks)
+        if self.block_scales and n:
+            for bs in range((start + BLOCK_SIZE - 1) // BLOCK_SIZE * BLOCK_SIZE, start + n, BLOCK_SIZE):
+                blk, _ = self.location(table_row, bs)
+                sl = slice(bs - start, min(bs + BLOCK_SIZE, start + n) - start)
+                for g in range(self.n_kv_heads):
+                    self.ek[blk, g] = kv_block_exponent(np.asarray(ks)[sl, g], self.k_scale[g], self.k_zp[g],
+                                                        self.n_bits)
+                    self.ev[blk, g] = kv_block_exponent(np.asarray(vs)[sl, g], self.v_scale[g], self.v_zp[g],
+                                                        self.n_bits)
+        for i in range(n):
+            self.write(table_row, start + i, ks[i], vs[i])
 
     def read(self, table_row, n_tokens: int):
         """Keys and values of tokens 0..n_tokens-1, [n_tokens, n_kv_heads, D],
@@ -320,8 +395,10 @@ class PagedCache:
                 K[t], V[t] = self.k[blk, :, off, :], self.v[blk, :, off, :]
             else:
                 assert self.written[blk, off], "reading a slot never written"
-                K[t] = kv_dequantize(self.k[blk, :, off, :], self.k_scale, self.k_zp)
-                V[t] = kv_dequantize(self.v[blk, :, off, :], self.v_scale, self.v_zp)
+                ek = self.ek[blk][:, None] if self.block_scales else 0
+                ev = self.ev[blk][:, None] if self.block_scales else 0
+                K[t] = kv_dequantize(self.k[blk, :, off, :], self.k_scale, self.k_zp, ek)
+                V[t] = kv_dequantize(self.v[blk, :, off, :], self.v_scale, self.v_zp, ev)
         assert np.all(np.isfinite(K)) and np.all(np.isfinite(V)), "reading a slot never written"
         return K, V
 
@@ -474,8 +551,7 @@ def layer_forward(shape, w: Dict[str, np.ndarray], x: np.ndarray, q_start, q_len
             assert c == 0, "prior context needs a KV cache"
             Ks, Vs = k[r0:r0 + n], v[r0:r0 + n]
         else:
-            for t in range(n):
-                cache.write(table[i], c + t, k[r0 + t], v[r0 + t])
+            cache.write_tokens(table[i], c, k[r0:r0 + n], v[r0:r0 + n])
             Ks, Vs = cache.read(table[i], c + n)
         mine = np.arange(r0, r0 + n)[in_sel[r0:r0 + n]]
         if len(mine):
@@ -495,7 +571,6 @@ def fill_cache(cache: PagedCache, table: np.ndarray, ctx_len, cache_k, cache_v):
     come from consecutive rows of cache_k / cache_v ([n, Hkv, D])."""
     r = 0
     for i, c in enumerate(ctx_len):
-        for t in range(int(c)):
-            cache.write(table[i], t, cache_k[r], cache_v[r])
-            r += 1
+        cache.write_tokens(table[i], 0, cache_k[r:r + int(c)], cache_v[r:r + int(c)])
+        r += int(c)
     assert r == (0 if cache_k is None else cache_k.shape[0])

@@ -422,6 +422,93 @@ def test_paged_u4_roundtrip():
     assert np.all(Vp >= oracle.kv_dequantize(np.zeros((1, 2, 8)), *params) - 1e-12)
 
 
+# -------------------------------------------- per-block x per-channel KV ---
+
+def test_kv_block_exponent_worked_example():
+    """Hand-worked u8 block, D = 2, scale (0.5, 0.25), zero point (128, 10).
+    q = x / scale: token 0 (20, 4), token 1 (-140, 248), token 2 (1, 3).
+    e = 0 clamps -140 + 128 < 0; e = 1 fits every value, so e = 1 and the
+    codes are 128 + rint(q / 2), 10 + rint(q / 2) with ties to even:
+    (138, 12), (58, 134), (128 [0.5 -> 0], 12 [1.5 -> 2]); back: (c - zp) * scale * 2."""
+    scale = np.array([0.5, 0.25], np.float32)
+    zp = np.array([128, 10], np.int32)
+    x = np.array([[10.0, 1.0], [-70.0, 62.0], [0.5, 0.75]], np.float32)
+    assert oracle.kv_block_exponent(x, scale, zp, 8) == 1
+    codes = oracle.kv_quantize_block(x, scale, zp, 1, 8)
+    assert codes.tolist() == [[138, 12], [58, 134], [128, 12]]
+    back = oracle.kv_dequantize(codes, scale, zp, 1)
+    assert back.tolist() == [[10.0, 1.0], [-70.0, 62.0], [0.0, 1.0]]
+    # the same block without its outlier token needs no factor
+    assert oracle.kv_block_exponent(x[[0, 2]], scale, zp, 8) == 0
+    # beyond 2^7 times the range the largest factor is kept and the rest clamps
+    assert oracle.kv_block_exponent(np.array([[1e6, 0.0]], np.float32), scale, zp, 8) == oracle.KV_MAX_BLOCK_EXP
+
+
+def test_kv_block_exponent_brute_force():
+    """e is the smallest exponent whose codes need no clamping, found here by
+    another route: the pinned per-channel quantiser with the scale itself
+    multiplied by 2^e (exact in float32), against the unclamped codes."""
+    rng = np.random.default_rng(21)
+    for bits in (8, 4):
+        L = (1 << bits) - 1
+        for trial in range(60):
+            scale = (rng.random(6) * 0.2 + 0.01).astype(np.float32)
+            zp = rng.integers(0, L + 1, 6).astype(np.int32)
+            x = (rng.standard_normal((5, 6)) * rng.choice([0.1, 1.0, 5.0, 40.0])).astype(np.float32)
+            e = oracle.kv_block_exponent(x, scale, zp, bits)
+
+            def fits(k):
+                sk = (scale * np.float32(2.0 ** k)).astype(np.float32)
+                raw = np.rint(x / sk).astype(np.int64) + zp
+                return np.all((raw >= 0) & (raw <= L))
+            want = next((k for k in range(oracle.KV_MAX_BLOCK_EXP + 1) if fits(k)), oracle.KV_MAX_BLOCK_EXP)
+            assert e == want
+            sk = (scale * np.float32(2.0 ** e)).astype(np.float32)
+            assert np.array_equal(oracle.kv_quantize_block(x, scale, zp, e, bits), oracle.kv_quantize(x, sk, zp, bits))
+
+
+def test_paged_block_scales_calls():
+    """A call that writes a block's first slot sets its factor from the
+    tokens it writes there; a later call appending to the block keeps it and
+    clamps; values inside the calibrated range give the per-channel cache
+    exactly."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((40, 2, 8)).astype(np.float32)
+    params = oracle.kv_calibrate(x)
+    table = np.array([[3, 0, 2]], np.int32)
+    plain = oracle.PagedCache(4, 2, 8, "u8", params, params)
+    blk = oracle.PagedCache(4, 2, 8, "u8", params, params, block_scales=True)
+    for c in (plain, blk):
+        c.write_tokens(table[0], 0, x[:20], x[:20])
+        c.write_tokens(table[0], 20, x[20:40], x[20:40])
+    assert np.array_equal(plain.k, blk.k) and not blk.ek.any()
+    np.testing.assert_array_equal(plain.read(table[0], 40)[0], blk.read(table[0], 40)[0])
+    # tokens 0..9 of a new sequence, scaled by 3: the block takes e = 2 (x 4)
+    # where the values leave the range (per head), and the call's values
+    # come back within half a (widened) step
+    big = 3.0 * x[:10]
+    c2 = oracle.PagedCache(4, 2, 8, "u8", params, params, block_scales=True)
+    t2 = np.array([[1, 2, 3]], np.int32)
+    c2.write_tokens(t2[0], 0, big, -big)
+    for g in range(2):
+        assert c2.ek[1, g] == oracle.kv_block_exponent(big[:, g], params[0][g], params[1][g])
+        assert c2.ek[1, g] >= 1
+    K, V = c2.read(t2[0], 10)
+    step = params[0][None] * (2.0 ** c2.ek[1])[:, None]
+    assert np.all(np.abs(K - big) <= 0.5001 * step)
+    # a later call appends tokens 10..13 (same block) with the factor kept
+    e_before = c2.ek.copy()
+    c2.write_tokens(t2[0], 10, 10.0 * x[10:14], x[10:14])
+    assert np.array_equal(c2.ek, e_before)
+    K2, _ = c2.read(t2[0], 14)
+    hi = (255 - params[1].astype(np.float64)) * params[0] * 2.0 ** c2.ek[1][:, None]
+    assert np.all(K2[10:14] <= hi[None] + 1e-9)  # clamped at the block's top code
+    # the next block (tokens 16..) gets its own factor from its first call
+    c2.write_tokens(t2[0], 14, x[14:20], x[14:20])
+    assert np.array_equal(c2.ek[2], [oracle.kv_block_exponent(x[16:20, g], params[0][g], params[1][g])
+                                     for g in range(2)])
+
+
 # ---------------------------------------------------------------- layer ---
 
 def tiny_shape(**kw):
