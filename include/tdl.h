@@ -118,6 +118,18 @@ typedef struct {
   int32_t kv_dtype;       /* TDL_BF16, TDL_U8_ASYM or TDL_U4_ASYM ([HET] 2.4) */
   uint64_t free_list_seed;/* 0: blocks handed out 0,1,2,...; otherwise the
                              free list is a seeded random permutation       */
+  int32_t block_scales;   /* 0: per-channel parameters only.  1 (u8 / u4):
+                             per-block x per-channel ([HET] 2.4 scales per
+                             channel and per block; 4.3 dequantises block b
+                             with its own scales[b]): block b's KV head g
+                             multiplies the per-channel scales of K and of V
+                             by 2^e, e in [0, 7] the smallest exponent for
+                             which none of the values that the call writing
+                             the block's first slot puts there clamps; later
+                             calls appending to the block keep it.  A block
+                             whose first slot was never written by a call
+                             uses what its exponent bytes hold (0 in a
+                             library-allocated cache).                      */
 } tdl_kv_config;
 
 /* Where a cache's bytes live.  Element (block b, kv head g, token slot s,
@@ -142,6 +154,8 @@ typedef struct {
   int32_t* k_zero_point;
   float* v_scale;
   int32_t* v_zero_point;
+  int8_t* block_exp;      /* block_scales: [n_blocks][n_kv_heads][2] exponents
+                             (K, V); otherwise NULL */
 } tdl_kv_view;
 
 /* A batch of sequences for layer_step ([HET] 2.2, 4.2: prefill chunks and

@@ -272,6 +272,8 @@ class LayerInputs:
     # calibrated on; None: the cached tokens
     calib_k: Optional[np.ndarray] = None
     calib_v: Optional[np.ndarray] = None
+    # u8 / u4 caches: per-block x per-channel factors (tdl_kv_config.block_scales)
+    block_scales: bool = False
 
 
 def make_inputs(wl: Workload, seed: int = 0, shape: Optional[LayerShape] = None,

@@ -98,13 +98,15 @@ def oracle_cache(inp: synth.LayerInputs, seqs=None) -> Optional[oracle.PagedCach
         cv = inp.cache_v if inp.calib_v is None else inp.calib_v
         kp = oracle.kv_calibrate(ck, bits)
         vp = oracle.kv_calibrate(cv, bits)
-        cache = oracle.PagedCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, wl.kv_dtype, kp, vp)
+        cache = oracle.PagedCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, wl.kv_dtype, kp, vp,
+                                  block_scales=inp.block_scales)
     if inp.cache_k is not None:
+        # one call writes every sequence's cached tokens from position 0
         seqs = range(b.n_seqs) if seqs is None else seqs
         off = np.concatenate([[0], np.cumsum(b.ctx_len)])
         for i in seqs:
-            for t in range(int(b.ctx_len[i])):
-                cache.write(b.table[i], t, inp.cache_k[off[i] + t], inp.cache_v[off[i] + t])
+            n = int(b.ctx_len[i])
+            cache.write_tokens(b.table[i], 0, inp.cache_k[off[i]:off[i] + n], inp.cache_v[off[i]:off[i] + n])
     return cache
 
 
@@ -175,7 +177,8 @@ def gpu_setup(inp: synth.LayerInputs, max_tokens: Optional[int] = None, max_posi
     t["q_len"] = torch.from_numpy(b.q_len).cuda()
     t["ctx_len"] = torch.from_numpy(b.ctx_len).cuda()
     if wl.kv_dtype != "none":
-        kv = tdl.KvCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, wl.kv_dtype)
+        kv = tdl.KvCache(b.n_blocks, shape.n_kv_heads, shape.head_dim, wl.kv_dtype,
+                         block_scales=inp.block_scales)
         if inp.calib_k is not None and wl.kv_dtype in ("u8", "u4"):
             kv.calibrate(torch.from_numpy(inp.calib_k).cuda(), torch.from_numpy(inp.calib_v).cuda())
         if inp.cache_k is not None:

@@ -59,13 +59,14 @@ class LayerWeights(ctypes.Structure):
 
 class KvConfig(ctypes.Structure):
     _fields_ = [("n_blocks", c_i32), ("block_size", c_i32), ("n_kv_heads", c_i32),
-                ("head_dim", c_i32), ("kv_dtype", c_i32), ("free_list_seed", ctypes.c_uint64)]
+                ("head_dim", c_i32), ("kv_dtype", c_i32), ("free_list_seed", ctypes.c_uint64),
+                ("block_scales", c_i32)]
 
 
 class KvView(ctypes.Structure):
     _fields_ = [("k_pool", c_vp), ("v_pool", c_vp), ("k_strides", ctypes.c_int64 * 4),
                 ("v_strides", ctypes.c_int64 * 4), ("elem_bytes", c_i32), ("k_scale", c_vp),
-                ("k_zero_point", c_vp), ("v_scale", c_vp), ("v_zero_point", c_vp)]
+                ("k_zero_point", c_vp), ("v_scale", c_vp), ("v_zero_point", c_vp), ("block_exp", c_vp)]
 
 
 class Batch(ctypes.Structure):
@@ -169,9 +170,12 @@ class KvCache:
     """A paged KV cache; its device memory is one torch uint8 tensor."""
 
     def __init__(self, n_blocks: int, n_kv_heads: int, head_dim: int, dtype: str = "bf16",
-                 seed: int = 0, device: str = "cuda", block_size: int = 16, allocate: bool = True):
-        self.cfg = KvConfig(n_blocks, block_size, n_kv_heads, head_dim, _DTYPES[dtype], seed)
+                 seed: int = 0, device: str = "cuda", block_size: int = 16, allocate: bool = True,
+                 block_scales: bool = False):
+        self.cfg = KvConfig(n_blocks, block_size, n_kv_heads, head_dim, _DTYPES[dtype], seed,
+                            int(block_scales))
         self.dtype = dtype
+        self.block_scales = block_scales
         nbytes = _kv_bytes(ctypes.byref(self.cfg))
         if nbytes == 0:
             raise TdlError("kv_cache_bytes", TDL_E_INVALID)
@@ -188,12 +192,14 @@ class KvCache:
 
     @classmethod
     def host_only(cls, n_blocks, n_kv_heads, head_dim, dtype="bf16", seed=0, fake_ptr=1 << 20,
-                  block_size=16):
+                  block_size=16, block_scales=False):
         """A handle over a placeholder device address, for host-side tests of
         the block allocator (the library never dereferences it)."""
         self = cls.__new__(cls)
-        self.cfg = KvConfig(n_blocks, block_size, n_kv_heads, head_dim, _DTYPES[dtype], seed)
+        self.cfg = KvConfig(n_blocks, block_size, n_kv_heads, head_dim, _DTYPES[dtype], seed,
+                            int(block_scales))
         self.dtype = dtype
+        self.block_scales = block_scales
         self.memory = None
         self.nbytes = _kv_bytes(ctypes.byref(self.cfg))
         h = c_vp()
@@ -292,6 +298,16 @@ class KvCache:
         c = hk * self.cfg.head_dim
         return (k, vv, sl(v.k_scale, c, torch.float32), sl(v.k_zero_point, c, torch.int32),
                 sl(v.v_scale, c, torch.float32), sl(v.v_zero_point, c, torch.int32))
+
+    def block_exponents(self):
+        """torch int8 view [blocks, Hkv, 2] of the per-block factor exponents
+        (K, V) of a block_scales cache."""
+        import torch
+        v = self.view()
+        assert self.block_scales and v.block_exp
+        nb, hk = self.cfg.n_blocks, self.cfg.n_kv_heads
+        off = v.block_exp - self.memory.data_ptr()
+        return self.memory[off:off + nb * hk * 2].view(torch.int8).view(nb, hk, 2)
 
     def calibrate(self, k, v, stream=None):
         _check("kv_cache_calibrate", _kv_calibrate(self._h, _stream(stream), _ptr(k), _ptr(v),

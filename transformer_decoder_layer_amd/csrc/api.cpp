@@ -103,6 +103,7 @@ struct tdl_kv_cache {
   int32_t* k_zp = nullptr;
   float* v_scale = nullptr;
   int32_t* v_zp = nullptr;
+  int8_t* exps = nullptr;  // per-block factor exponents (block_scales)
   std::vector<int32_t> free_list;  // LIFO: back() is handed out next
   std::vector<int32_t> refs;       // holders of each block; 0: on the free list
   // prefix index: key -> (block, last use); the index is one of the block's holders
@@ -275,6 +276,7 @@ KvPool pool_of(const tdl_layer* L, const tdl_kv_cache* kv) {
     p.k_zp = kv->k_zp;
     p.v_scale = kv->v_scale;
     p.v_zp = kv->v_zp;
+    p.exps = kv->exps;
   } else {
     p.k = L->priv_k;
     p.v = L->priv_v;
@@ -1050,7 +1052,8 @@ namespace {
 bool kv_config_ok(const tdl_kv_config* c) {
   return c && c->n_blocks > 0 && c->block_size == 16 && c->n_kv_heads > 0 &&
          (c->head_dim == 64 || c->head_dim == 128) &&
-         (c->kv_dtype == TDL_BF16 || c->kv_dtype == TDL_U8_ASYM || c->kv_dtype == TDL_U4_ASYM);
+         (c->kv_dtype == TDL_BF16 || c->kv_dtype == TDL_U8_ASYM || c->kv_dtype == TDL_U4_ASYM) &&
+         (c->block_scales == 0 || (c->block_scales == 1 && c->kv_dtype != TDL_BF16));
 }
 bool kv_coded(const tdl_kv_config* c) {
   return c->kv_dtype == TDL_U8_ASYM || c->kv_dtype == TDL_U4_ASYM;
@@ -1063,11 +1066,15 @@ size_t pool_bytes(const tdl_kv_config* c) {
 size_t param_bytes(const tdl_kv_config* c) {
   return kv_coded(c) ? 4 * align256((size_t)c->n_kv_heads * c->head_dim * 4) : 0;
 }
+// per-block x per-channel: one exponent byte per (block, head) for K and V
+size_t exp_bytes(const tdl_kv_config* c) {
+  return c->block_scales ? align256((size_t)c->n_blocks * c->n_kv_heads * 2) : 0;
+}
 }  // namespace
 
 extern "C" size_t kv_cache_bytes(const tdl_kv_config* cfg) {
   if (!kv_config_ok(cfg)) return 0;
-  return 2 * pool_bytes(cfg) + param_bytes(cfg);
+  return 2 * pool_bytes(cfg) + param_bytes(cfg) + exp_bytes(cfg);
 }
 
 extern "C" tdl_status kv_cache_alloc(const tdl_kv_config* cfg, void* dev_mem, tdl_kv_cache** out) {
@@ -1106,6 +1113,7 @@ extern "C" tdl_status kv_cache_alloc(const tdl_kv_config* cfg, void* dev_mem, td
     kv->k_zp = (int32_t*)(pb + ps);
     kv->v_scale = (float*)(pb + 2 * ps);
     kv->v_zp = (int32_t*)(pb + 3 * ps);
+    if (cfg->block_scales) kv->exps = (int8_t*)(pb + param_bytes(cfg));
   }
   // free list: LIFO; blocks come out as 0, 1, 2, ... or in a seeded order
   std::vector<int32_t> order(cfg->n_blocks);
@@ -1151,6 +1159,7 @@ extern "C" tdl_status kv_cache_view(const tdl_kv_cache* kv, tdl_kv_view* out) {
   out->k_zero_point = kv->k_zp;
   out->v_scale = kv->v_scale;
   out->v_zero_point = kv->v_zp;
+  out->block_exp = kv->exps;
   return TDL_OK;
 }
 

@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   constexpr bool U4 = F == kKvU4;
   constexpr float kBias = U4 ? kU4Bias : kU8Bias;
   constexpr int NT = D / 16;  // 16-channel tiles of the output
-  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ float sm_m[4][16], sm_l[4][16], sm_lv[4][16];
   // Stage j of every wave's block rotation lives in its own array, so
   // the compiler can tell a wave's reads of one stage from the copies still
   // landing in the others (one array would make every read wait for all
@@ -331,6 +331,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  // per-block x per-channel caches: sum of P 2^eV (the weight of the V zero
+  // point, P entering the V product scaled by its block's factor)
+  float lv_run = 0.f;
 
   // this wave's blocks: blk0 + wave + 4i, i < cnt <= 128; the table
   // entries come in two loads (entry i in lane i % 64 of my_phys[i / 64])
@@ -340,8 +343,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   for (int h = 0; h < 2; ++h)
     if (64 * h + lane < cnt) my_phys[h] = seq_block(a.seq, sidx, blk0 + wave + 4 * (64 * h + lane));
 
-  auto compute = [&](const DecFrags<D, F>& f, int i) {
+  // ex: the block's factor exponents (eK in the low byte, eV in the high;
+  // 0 without block scales), P <= 2^kLazy times 2^eV <= 2^7 stays in the fp16
+  // range
+  auto compute = [&](const DecFrags<D, F>& f, int i, int ex) {
     const int blk = blk0 + wave + 4 * i;
+    const float sck = Q ? ldexpf(sc, (int8_t)(ex & 0xff)) : sc;
+    const float fvb = Q ? ldexpf(1.f, (int8_t)(ex >> 8)) : 1.f;
     // S^T[key][head]: A = K rows (key = lane%16), B = Q^T (hi + lo, two
     // independent accumulation chains)
     f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f}, st_lo = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     float mb = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sv[r] = (st[r] - corr) * sc;
+      sv[r] = (st[r] - corr) * sck;
       mb = fmaxf(mb, sv[r]);
     }
     if (partial) {
@@ -390,6 +398,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       const float alpha = exp2f(m_run - m_new);  // 0 on the first block
       m_run = m_new;
       l_run *= alpha;
+      lv_run *= alpha;
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] *= alpha;
     }
@@ -401,8 +410,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     for (int r = 0; r < 4; ++r) {
       const float pv = exp2f(sv[r] - m_run);
       if constexpr (Q) {
-        pf[r] = (_Float16)pv;
-        pl[r] = (_Float16)(pv - (float)pf[r]);
+        const float pw = pv * fvb;  // exact: a power of two
+        pf[r] = (_Float16)pw;
+        pl[r] = (_Float16)(pw - (float)pf[r]);
       } else {
         pf[r] = f32_to_bf16(pv);
         pl[r] = f32_to_bf16(pv - (float)pf[r]);
@@ -410,6 +420,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       psum += pv;
     }
     l_run += psum;
+    lv_run += psum * fvb;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       PT vf;
@@ -443,12 +454,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     // bound this kernel.
     using St = DecStage<D, F>;
     constexpr int NB = kDecStages;
-    constexpr int LOADS = St::kInst + (Q ? 0 : D / 16);
+    // (u8 / u4: plus one 2-byte load of the block's factor exponents, from a
+    // dummy address without block scales, so that every path counts alike)
+    constexpr int LOADS = St::kInst + (Q ? 1 : D / 16);
     constexpr int kWaitIn = (NB - 2) * LOADS;  // blocks i+1 .. i+NB-2 may be in flight
     constexpr int kWait = (kWaitIn & 15) | (7 << 4) | (15 << 8) | (((kWaitIn >> 4) & 3) << 14);
     static_assert(NB == 3, "one LDS array per stage");
     auto stage = [&](int j) { return (j == 0 ? st0 : j == 1 ? st1 : st2) + wave * St::kBytes; };
     DecFrags<D, F> fv[Q ? 1 : NB];  // bf16: V^T register sets in rotation
+    int exr[NB] = {0, 0, 0};        // u8 / u4: the blocks' exponents in rotation
+    const bool has_exp = a.pool.exps != nullptr;
     if (cnt > 0) {
       auto phys_of = [&](int i) {
         i = min(i, cnt - 1);  // wave-uniform
@@ -470,6 +485,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
           __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(kd + 1024 * j), 16, 0, 0);
         }
         if constexpr (!Q) dec_load_v<D, F>(fv[buf], a, phys, g, col, grp);
+        if constexpr (Q) {
+          const uint16_t* ep = has_exp ? (const uint16_t*)(a.pool.exps + ((size_t)phys * a.Hkv + g) * 2)
+                                       : (const uint16_t*)a.pool.k_zp;
+          exr[buf] = *ep;
+        }
       };
 #pragma unroll
       for (int j = 0; j < NB - 1; ++j) issue(j, j);
@@ -500,7 +520,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
               for (int t = 0; t < D / 16; ++t) f.v[t] = fv[j].v[t];
             }
-            compute(f, i + j);
+            compute(f, i + j, Q && has_exp ? exr[j] : 0);
           }
         }
       }
@@ -512,9 +532,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   // ---- merge the four waves: acc[t][r] = O^T[dec_vchan(t, 4grp + r)][head col]
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
+  lv_run += __shfl_xor(lv_run, 16, 64);
+  lv_run += __shfl_xor(lv_run, 32, 64);
   if (lane < 16) {
     sm_m[wave][lane] = m_run;
     sm_l[wave][lane] = l_run;
+    sm_lv[wave][lane] = lv_run;
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -529,16 +552,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     float M = sm_m[0][hh];
 #pragma unroll
     for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][hh]);
-    float O = 0.f, L = 0.f;
+    float O = 0.f, L = 0.f, Lv = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float f = exp2f(sm_m[w][hh] - M);  // 0 for a wave with no blocks
       O += o_tile(w)[o_idx(d, hh)] * f;
       L += sm_l[w][hh] * f;
+      Lv += sm_lv[w][hh] * f;
     }
-    if constexpr (Q) {
+    if constexpr (Q) {  // O = sum P 2^eV (bias + c): take out sum P 2^eV (bias + zp)
       const int ch = g * D + d;
-      O = a.pool.v_scale[ch] * (O - (kBias + (float)a.pool.v_zp[ch]) * L);
+      O = a.pool.v_scale[ch] * (O - (kBias + (float)a.pool.v_zp[ch]) * Lv);
     }
     if (n_parts == 1) {
       a.o[(size_t)row * a.Hq * D + (size_t)(g * n_rep + hh) * D + d] = to_f16(O / L);

@@ -129,7 +129,12 @@ struct KvPool {
   const int* k_zp;
   const float* v_scale;
   const int* v_zp;
+  // per-block x per-channel mode (u8 / u4): exponents e of the factor 2^e
+  // that block b's KV head g applies to the per-channel scales,
+  // exps[(b * Hkv + g) * 2 + 0] for K and + 1 for V; null: per-channel only
+  int8_t* exps;
 };
+constexpr int kMaxBlockExp = 7;  // block factors 2^0 .. 2^7
 
 // fp16 copies of the new tokens' K and V of the first n_seqs prefill
 // sequences of a call, in the prefill attention kernel's tile layout

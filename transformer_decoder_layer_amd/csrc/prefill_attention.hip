@@ -26,7 +26,8 @@
 //    sequences past kStagedSeqs): blocks gathered through the block table
 //    into registers, converted to fp16 (bf16 exactly; u8 / u4 codes
 //    dequantised as (c - zero_point) * scale, the page's formula in the
-//    devpress engine article, section 2.6) and stored to LDS.
+//    devpress engine article, section 2.6, times the block's factor 2^e in
+//    per-block x per-channel caches) and stored to LDS.
 // Either way the LDS tile holds the values the cache holds, rounded once to
 // fp16 (exact for bf16 inside the fp16 range).
 
@@ -272,6 +273,9 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
       constexpr int MAXC = (nchunks + NT - 1) / NT;
       uint4 rc[MAXC];
       int ph0, ph1;  // physical blocks of the tile (selected, never indexed)
+      // per-block x per-channel caches: the two blocks' factors 2^e of the
+      // K and V scales (1 otherwise)
+      float fk0 = 1.f, fk1 = 1.f, fv0 = 1.f, fv1 = 1.f;
       static_assert(NB == 2, "two blocks per tile");
       auto load_table = [&](int t) {
         auto entry = [&](int b) {
@@ -280,6 +284,16 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
         };
         ph0 = entry(0);
         ph1 = entry(1);
+        if constexpr (fmt != kKvBf16) {
+          if (a.pool.exps) {
+            const int8_t* e0 = a.pool.exps + ((size_t)ph0 * a.Hkv + g) * 2;
+            const int8_t* e1 = a.pool.exps + ((size_t)ph1 * a.Hkv + g) * 2;
+            fk0 = ldexpf(1.f, e0[0]);
+            fv0 = ldexpf(1.f, e0[1]);
+            fk1 = ldexpf(1.f, e1[0]);
+            fv1 = ldexpf(1.f, e1[1]);
+          }
+        }
       };
       auto load_regs = [&]() {
 #pragma unroll
@@ -340,6 +354,7 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
               const int slot = (within * 16) / D, d0 = (within * 16) % D;
               const int key = b * 16 + slot;
               const bool ok = key0 + key < n_pool_keys;
+              const float fb = b ? fk1 : fk0;
 #pragma unroll
               for (int hh = 0; hh < 2; ++hh) {
                 f16x8 v;
@@ -347,13 +362,13 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
                 for (int e = 0; e < 8; ++e) {
                   const int d = d0 + 8 * hh + e;
                   const int code = (w[(8 * hh + e) >> 2] >> (8 * (e & 3))) & 255;
-                  v[e] = ok ? f32_to_f16_sat(((float)code - dq[1][d]) * dq[0][d]) : (f16)0.f;
+                  v[e] = ok ? f32_to_f16_sat(((float)code - dq[1][d]) * dq[0][d] * fb) : (f16)0.f;
                 }
                 *(f16x8*)(tile + k_at<D>(key, (d0 >> 3) + hh)) = v;
               }
             } else {  // 16 slots of one channel
               const int d = within;
-              const float vs = dq[2][d], vz = dq[3][d];
+              const float vs = dq[2][d] * (b ? fv1 : fv0), vz = dq[3][d];
 #pragma unroll
               for (int u = 0; u < 4; ++u) {
                 f16x4 v;
@@ -371,6 +386,7 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
               const int slot = (within * 32) / D, c0 = (within * 32) % D;
               const int key = b * 16 + slot;
               const bool ok = key0 + key < n_pool_keys;
+              const float fb = b ? fk1 : fk0;
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 f16x8 v;
@@ -379,7 +395,7 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
                   const int d = c0 + 8 * j + e;
                   const int byte = (w[j] >> (8 * (e & 3))) & 255;
                   const int code = e < 4 ? byte & 15 : byte >> 4;
-                  v[e] = ok ? f32_to_f16_sat(((float)code - dq[1][d]) * dq[0][d]) : (f16)0.f;
+                  v[e] = ok ? f32_to_f16_sat(((float)code - dq[1][d]) * dq[0][d] * fb) : (f16)0.f;
                 }
                 *(f16x8*)(tile + k_at<D>(key, (c0 >> 3) + j)) = v;
               }
@@ -388,7 +404,7 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
               for (int n = 0; n < 2; ++n) {
                 const int d = 2 * c + n;
-                const float vs = dq[2][d], vz = dq[3][d];
+                const float vs = dq[2][d] * (b ? fv1 : fv0), vz = dq[3][d];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                   f16x4 v;

@@ -73,6 +73,14 @@ __device__ __forceinline__ int row_position(const SeqInfo& s, int seq, int row) 
   if (!s.q_start) return s.ctx0 + row;
   return s.ctx_len[seq] + row - s.q_start[seq];
 }
+// One past the last row of sequence `seq` in this call.  q_start without
+// q_len is the cumulative form (kv_cache_write's cu_rows, n_seqs + 1
+// entries).
+__device__ __forceinline__ int seq_end_row(const SeqInfo& s, int seq, int row) {
+  if (s.rows_are_seqs) return row + 1;
+  if (!s.q_start) return s.q_len0;
+  return s.q_len ? s.q_start[seq] + s.q_len[seq] : s.q_start[seq + 1];
+}
 // Physical block of token `pos` of sequence `seq` (the page table lookup,
 // get_location of the TFFInfer page section 3.6.4).
 __device__ __forceinline__ int block_of(const SeqInfo& s, int seq, int pos) {
@@ -80,24 +88,47 @@ __device__ __forceinline__ int block_of(const SeqInfo& s, int seq, int pos) {
   return s.tables[(size_t)seq * s.max_blocks + pos / kBlockTokens];
 }
 
-// Quantise one value: clamp(round_half_even(x / scale) + zp, 0, top), with a
-// correctly rounded fp32 divide (top 255 for u8 codes, 15 for u4).
-__device__ __forceinline__ int quant_code(float x, float scale, int zp, int top) {
-  const float q = __builtin_rintf(__fdiv_rn(x, scale));
+// Quantise one value in a block with factor 2^e: clamp(round_half_even((x /
+// scale) * 2^-e) + zp, 0, top), with a correctly rounded fp32 divide and an
+// exact power-of-two scaling (top 255 for u8 codes, 15 for u4; e = 0 is the
+// per-channel quantiser).
+__device__ __forceinline__ int quant_code(float x, float scale, int zp, int top, int e = 0) {
+  const float q = __builtin_rintf(ldexpf(__fdiv_rn(x, scale), -e));
   const int c = (int)q + zp;
   return c < 0 ? 0 : (c > top ? top : c);
 }
+// Smallest e in [0, kMaxBlockExp] for which x quantises without clamping
+// (kMaxBlockExp if none does).
+__device__ __forceinline__ int exp_needed(float x, float scale, int zp, int top) {
+  const float q = __fdiv_rn(x, scale);
+  for (int e = 0; e < kMaxBlockExp; ++e) {
+    const float c = __builtin_rintf(ldexpf(q, -e)) + (float)zp;
+    if (c >= 0.f && c <= (float)top) return e;
+  }
+  return kMaxBlockExp;
+}
+// The factor exponent of block blk, KV head g (kv 0: K, 1: V); 0 without
+// block scales.
+__device__ __forceinline__ int pool_exp(const KvPool& pool, int blk, int g, int Hkv, int kv) {
+  return pool.exps ? (int)pool.exps[((size_t)blk * Hkv + g) * 2 + kv] : 0;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
 
-// bf16 / u8 pools: one element per (slot, d)
+// bf16 / u8 pools: one element per (slot, d); u8 codes in a block with
+// factors 2^ek (K) and 2^ev (V)
 __device__ __forceinline__ void store_kv(const KvPool& pool, int blk, int g, int Hkv, int D, int slot,
-                                         int d, float kval, float vval) {
+                                         int d, float kval, float vval, int ek = 0, int ev = 0) {
   const size_t head = ((size_t)blk * Hkv + g) * kBlockTokens * D;
   const size_t kidx = head + (size_t)slot * D + d;   // K: [blk][g][slot][d]
   const size_t vidx = head + (size_t)d * kBlockTokens + slot;  // V: [blk][g][d][slot]
   if (pool.fmt == kKvU8) {
     const int ch = g * D + d;
-    ((uint8_t*)pool.k)[kidx] = (uint8_t)quant_code(kval, pool.k_scale[ch], pool.k_zp[ch], 255);
-    ((uint8_t*)pool.v)[vidx] = (uint8_t)quant_code(vval, pool.v_scale[ch], pool.v_zp[ch], 255);
+    ((uint8_t*)pool.k)[kidx] = (uint8_t)quant_code(kval, pool.k_scale[ch], pool.k_zp[ch], 255, ek);
+    ((uint8_t*)pool.v)[vidx] = (uint8_t)quant_code(vval, pool.v_scale[ch], pool.v_zp[ch], 255, ev);
   } else {
     ((bf16*)pool.k)[kidx] = f32_to_bf16(kval);
     ((bf16*)pool.v)[vidx] = f32_to_bf16(vval);
@@ -121,13 +152,21 @@ __device__ __forceinline__ int u4_vbyte(int slot, int d) { return (d >> 1) * kBl
 // the matching V head).  Q and K heads share the launch, as the RoPE kernel
 // of the Qwen2.5-7B page (section 2) does with its unified head indexing.
 // Half-split pairs (i, i + D/2): lane i < D/2 owns pair i.
+//
+// Per-block x per-channel caches take two launches.  mode 1: the row at
+// slot 0 of a block (the call writes the block's first slot) computes the
+// rotated K and the V of every row this call writes into that block and
+// stores the block's factor exponents (the smallest that leaves no code
+// clamped, per KV head, K and V separately); every other row does nothing.
+// mode 0: every row quantises with its block's exponents (set by this call's
+// mode-1 launch, or by the call that wrote the block's first slot).
 __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ qkv, int Hq, int Hkv,
                                                       int D, const float2* __restrict__ tab,
                                                       const float* __restrict__ qn,
                                                       const float* __restrict__ kn, float eps,
                                                       float* __restrict__ q_out, SeqInfo seq,
                                                       KvPool pool, PrefillStage stage, int splits,
-                                                      const float* __restrict__ bias, int hpw) {
+                                                      const float* __restrict__ bias, int hpw, int mode) {
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = D >> 1;
@@ -135,11 +174,19 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
   const int pos = row_position(seq, sidx, row);
   const int ldq = (Hq + 2 * Hkv) * D;
   const size_t slice = (size_t)gridDim.x * ldq;
-  const float* src = qkv + (size_t)row * ldq;
-  // element c of this row's projection: the partial slices in order (+
+  const int blk = block_of(seq, sidx, pos);
+  const int slot = pos % kBlockTokens;
+  // mode 1: only the rows at slot 0, for the rows of this call in the block
+  int n_blk_rows = 1;
+  if (mode == 1) {
+    if (slot != 0) return;
+    n_blk_rows = min(kBlockTokens, min(seq_end_row(seq, sidx, row), (int)gridDim.x) - row);
+  }
+  // element c of row row+i's projection: the partial slices in order (+
   // bias).  Four slices per batch of independent loads (slice indices past
   // the last repeat it and add nothing): a load per round trip otherwise.
-  auto val = [&](int c) {
+  auto val = [&](int i, int c) {
+    const float* src = qkv + (size_t)(row + i) * ldq;
     if (splits == 1) return bias ? src[c] + bias[c] : src[c];
     float v = 0.f;
     for (int s0 = 0; s0 < splits; s0 += 4) {
@@ -153,19 +200,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
   };
   const bool act = lane < half;
   const int ln = act ? lane : 0;  // lanes past D/2 load a valid element and store nothing
-  float2 cs = make_float2(1.f, 0.f);
-  if (act) cs = tab[(size_t)pos * half + lane];
-  const int blk = block_of(seq, sidx, pos);
-  const int slot = pos % kBlockTokens;
-  // the row of the prefill staging copy (sequences < stage.n_seqs)
-  const bool staged = !seq.rows_are_seqs && sidx < stage.n_seqs;
-  const int srow = staged ? prefill_stage_base(seq, sidx) + row - (seq.q_start ? seq.q_start[sidx] : 0) : 0;
-
-  // one wave per head: workgroup (row, y) takes heads hpw*y .. hpw*y + hpw-1
-  for (int h = hpw * blockIdx.y + wave; h < min(Hq + Hkv, hpw * ((int)blockIdx.y + 1)); h += 4) {
+  // head h of row row+i, normalised (Q/K) and rotated: channels ln, ln + D/2
+  auto rotated = [&](int i, int h, float& r1, float& r2) {
     const bool is_q = h < Hq;
     const int hc = h * D;  // q heads then k heads are contiguous
-    float x1 = val(hc + ln), x2 = val(hc + ln + half);
+    float x1 = val(i, hc + ln), x2 = val(i, hc + ln + half);
     if (!act) x1 = x2 = 0.f;
     const float* gn = is_q ? qn : kn;
     if (gn) {  // per-head RMSNorm over D
@@ -176,8 +215,46 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
         x2 = x2 * inv * gn[lane + half];
       }
     }
-    const float r1 = x1 * cs.x - x2 * cs.y;
-    const float r2 = x1 * cs.y + x2 * cs.x;
+    float2 cs = make_float2(1.f, 0.f);
+    if (act) cs = tab[(size_t)(pos + i) * half + lane];
+    r1 = x1 * cs.x - x2 * cs.y;
+    r2 = x1 * cs.y + x2 * cs.x;
+  };
+  // the row of the prefill staging copy (sequences < stage.n_seqs)
+  const bool staged = mode == 0 && !seq.rows_are_seqs && sidx < stage.n_seqs;
+  const int srow = staged ? prefill_stage_base(seq, sidx) + row - (seq.q_start ? seq.q_start[sidx] : 0) : 0;
+  const int top = pool.fmt == kKvU8 ? 255 : 15;
+
+  // one wave per head: workgroup (row, y) takes heads hpw*y .. hpw*y + hpw-1
+  for (int h = hpw * blockIdx.y + wave; h < min(Hq + Hkv, hpw * ((int)blockIdx.y + 1)); h += 4) {
+    const bool is_q = h < Hq;
+    if (mode == 1) {  // wave-uniform
+      if (is_q) continue;
+      const int g = h - Hq;
+      const int vc = (Hq + Hkv + g) * D;
+      const int c1 = g * D + ln, c2 = c1 + half;
+      int ek = 0, ev = 0;
+      for (int i = 0; i < n_blk_rows; ++i) {
+        float r1, r2;
+        rotated(i, h, r1, r2);
+        const float v1 = val(i, vc + ln), v2 = val(i, vc + ln + half);
+        if (act) {
+          ek = max(ek, max(exp_needed(r1, pool.k_scale[c1], pool.k_zp[c1], top),
+                           exp_needed(r2, pool.k_scale[c2], pool.k_zp[c2], top)));
+          ev = max(ev, max(exp_needed(v1, pool.v_scale[c1], pool.v_zp[c1], top),
+                           exp_needed(v2, pool.v_scale[c2], pool.v_zp[c2], top)));
+        }
+      }
+      ek = wave_max_i(ek);
+      ev = wave_max_i(ev);
+      if (lane == 0) {
+        pool.exps[((size_t)blk * Hkv + g) * 2] = (int8_t)ek;
+        pool.exps[((size_t)blk * Hkv + g) * 2 + 1] = (int8_t)ev;
+      }
+      continue;
+    }
+    float r1, r2;
+    rotated(0, h, r1, r2);
     if (is_q) {  // wave-uniform
       if (act) {
         float* qo = q_out + ((size_t)row * Hq + h) * D;
@@ -188,7 +265,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     }
     const int g = h - Hq;
     const int vc = (Hq + Hkv + g) * D;
-    const float v1 = val(vc + ln), v2 = val(vc + ln + half);
+    const float v1 = val(0, vc + ln), v2 = val(0, vc + ln + half);
+    const int ek = pool_exp(pool, blk, g, Hkv, 0), ev = pool_exp(pool, blk, g, Hkv, 1);
     if (staged && act) {
       // fp16 copy of what the cache holds (bf16-rounded, or the dequantised
       // code) for prefill attention
@@ -198,11 +276,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
         sk1 = (float)f32_to_bf16(r1); sk2 = (float)f32_to_bf16(r2);
         sv1 = (float)f32_to_bf16(v1); sv2 = (float)f32_to_bf16(v2);
       } else {
-        const int top = pool.fmt == kKvU8 ? 255 : 15;
-        sk1 = (float)(quant_code(r1, pool.k_scale[c1], pool.k_zp[c1], top) - pool.k_zp[c1]) * pool.k_scale[c1];
-        sk2 = (float)(quant_code(r2, pool.k_scale[c2], pool.k_zp[c2], top) - pool.k_zp[c2]) * pool.k_scale[c2];
-        sv1 = (float)(quant_code(v1, pool.v_scale[c1], pool.v_zp[c1], top) - pool.v_zp[c1]) * pool.v_scale[c1];
-        sv2 = (float)(quant_code(v2, pool.v_scale[c2], pool.v_zp[c2], top) - pool.v_zp[c2]) * pool.v_scale[c2];
+        const float fk = ldexpf(1.f, ek), fv = ldexpf(1.f, ev);
+        sk1 = (float)(quant_code(r1, pool.k_scale[c1], pool.k_zp[c1], top, ek) - pool.k_zp[c1]) * (pool.k_scale[c1] * fk);
+        sk2 = (float)(quant_code(r2, pool.k_scale[c2], pool.k_zp[c2], top, ek) - pool.k_zp[c2]) * (pool.k_scale[c2] * fk);
+        sv1 = (float)(quant_code(v1, pool.v_scale[c1], pool.v_zp[c1], top, ev) - pool.v_zp[c1]) * (pool.v_scale[c1] * fv);
+        sv2 = (float)(quant_code(v2, pool.v_scale[c2], pool.v_zp[c2], top, ev) - pool.v_zp[c2]) * (pool.v_scale[c2] * fv);
       }
       const size_t hb = (size_t)g * stage.rows * D;
       stage.k[hb + prefill_k_index(srow, lane, D)] = f32_to_f16_sat(sk1);
@@ -212,8 +290,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     }
     if (pool.fmt != kKvU4) {
       if (act) {
-        store_kv(pool, blk, g, Hkv, D, slot, lane, r1, v1);
-        store_kv(pool, blk, g, Hkv, D, slot, lane + half, r2, v2);
+        store_kv(pool, blk, g, Hkv, D, slot, lane, r1, v1, ek, ev);
+        store_kv(pool, blk, g, Hkv, D, slot, lane + half, r2, v2, ek, ev);
       }
       continue;
     }
@@ -222,10 +300,10 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     // multiple of 8, so partners of active lanes are active).  Every lane
     // takes part in the exchange.
     const int c1 = g * D + ln, c2 = c1 + half;
-    const int k1 = quant_code(r1, pool.k_scale[c1], pool.k_zp[c1], 15);
-    const int k2 = quant_code(r2, pool.k_scale[c2], pool.k_zp[c2], 15);
-    const int w1 = quant_code(v1, pool.v_scale[c1], pool.v_zp[c1], 15);
-    const int w2 = quant_code(v2, pool.v_scale[c2], pool.v_zp[c2], 15);
+    const int k1 = quant_code(r1, pool.k_scale[c1], pool.k_zp[c1], 15, ek);
+    const int k2 = quant_code(r2, pool.k_scale[c2], pool.k_zp[c2], 15, ek);
+    const int w1 = quant_code(v1, pool.v_scale[c1], pool.v_zp[c1], 15, ev);
+    const int w2 = quant_code(v2, pool.v_scale[c2], pool.v_zp[c2], 15, ev);
     const int pk1 = __shfl_xor(k1, 4, 64), pk2 = __shfl_xor(k2, 4, 64);
     const int pw1 = __shfl_xor(w1, 1, 64), pw2 = __shfl_xor(w2, 1, 64);
     if (!act) continue;
@@ -310,9 +388,13 @@ __global__ __launch_bounds__(256) void rmsnorm_splits_kernel(const float* __rest
 }
 
 // ---------------------------------------------------- cache writes
+// One workgroup per row.  Per-block x per-channel caches take two launches,
+// as for the RoPE kernel: mode 1, the row at slot 0 of a block sets the
+// block's exponents from the rows this call writes into it; mode 0, every
+// row quantises with its block's exponents.
 __global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ k,
                                                        const void* __restrict__ v, int src_f32,
-                                                       int Hkv, int D, SeqInfo seq, KvPool pool) {
+                                                       int Hkv, int D, SeqInfo seq, KvPool pool, int mode) {
   const int row = blockIdx.x;
   const int sidx = find_seq(seq, row);
   const int pos = row_position(seq, sidx, row);
@@ -321,10 +403,35 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ 
   auto ld = [&](const void* p, size_t i) {
     return src_f32 ? ((const float*)p)[i] : (float)((const bf16*)p)[i];
   };
+  if (mode == 1) {
+    if (slot != 0) return;
+    const int nr = min(kBlockTokens, min(seq_end_row(seq, sidx, row), (int)gridDim.x) - row);
+    const int top = pool.fmt == kKvU8 ? 255 : 15;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int g = wave; g < Hkv; g += blockDim.x / 64) {  // one wave per KV head
+      int ek = 0, ev = 0;
+      for (int i = 0; i < nr; ++i)
+        for (int d = lane; d < D; d += 64) {
+          const size_t idx = (size_t)(row + i) * Hkv * D + (size_t)g * D + d;
+          const int ch = g * D + d;
+          ek = max(ek, exp_needed(ld(k, idx), pool.k_scale[ch], pool.k_zp[ch], top));
+          ev = max(ev, exp_needed(ld(v, idx), pool.v_scale[ch], pool.v_zp[ch], top));
+        }
+      ek = wave_max_i(ek);
+      ev = wave_max_i(ev);
+      if (lane == 0) {
+        pool.exps[((size_t)blk * Hkv + g) * 2] = (int8_t)ek;
+        pool.exps[((size_t)blk * Hkv + g) * 2 + 1] = (int8_t)ev;
+      }
+    }
+    return;
+  }
   if (pool.fmt != kKvU4) {
     for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
       const size_t idx = (size_t)row * Hkv * D + e;
-      store_kv(pool, blk, e / D, Hkv, D, slot, e % D, ld(k, idx), ld(v, idx));
+      const int g = e / D;
+      store_kv(pool, blk, g, Hkv, D, slot, e % D, ld(k, idx), ld(v, idx), pool_exp(pool, blk, g, Hkv, 0),
+               pool_exp(pool, blk, g, Hkv, 1));
     }
     return;
   }
@@ -335,10 +442,11 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ 
     const int dk = 8 * (i >> 2) + (i & 3), dv = 2 * i;  // low-nibble channels
     const size_t src = (size_t)row * Hkv * D + (size_t)g * D;
     const int ck = g * D + dk, cv = g * D + dv;
-    const int klo = quant_code(ld(k, src + dk), pool.k_scale[ck], pool.k_zp[ck], 15);
-    const int khi = quant_code(ld(k, src + dk + 4), pool.k_scale[ck + 4], pool.k_zp[ck + 4], 15);
-    const int vlo = quant_code(ld(v, src + dv), pool.v_scale[cv], pool.v_zp[cv], 15);
-    const int vhi = quant_code(ld(v, src + dv + 1), pool.v_scale[cv + 1], pool.v_zp[cv + 1], 15);
+    const int ek = pool_exp(pool, blk, g, Hkv, 0), ev = pool_exp(pool, blk, g, Hkv, 1);
+    const int klo = quant_code(ld(k, src + dk), pool.k_scale[ck], pool.k_zp[ck], 15, ek);
+    const int khi = quant_code(ld(k, src + dk + 4), pool.k_scale[ck + 4], pool.k_zp[ck + 4], 15, ek);
+    const int vlo = quant_code(ld(v, src + dv), pool.v_scale[cv], pool.v_zp[cv], 15, ev);
+    const int vhi = quant_code(ld(v, src + dv + 1), pool.v_scale[cv + 1], pool.v_zp[cv + 1], 15, ev);
     const size_t hb = u4_head(blk, g, Hkv, D);
     ((uint8_t*)pool.k)[hb + u4_kbyte(slot, dk, D)] = (uint8_t)(klo | (khi << 4));
     ((uint8_t*)pool.v)[hb + u4_vbyte(slot, dv)] = (uint8_t)(vlo | (vhi << 4));
@@ -553,16 +661,27 @@ hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, cons
   // few rows (decode): four heads per workgroup for parallelism; many rows
   // (prefill): all heads of a row in one workgroup
   const int hpw = rows >= 1024 ? Hq + Hkv : 4;
-  rope_kv_kernel<<<dim3(rows, cdiv(Hq + Hkv, hpw)), 256, 0, s>>>(
-      (const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps, (float*)q_out, seq, pool, stage, splits,
-      bias, hpw);
+  const dim3 grid(rows, cdiv(Hq + Hkv, hpw));
+  if (pool.exps && pool.fmt != kKvBf16) {  // the blocks' exponents first
+    rope_kv_kernel<<<grid, 256, 0, s>>>((const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps,
+                                        (float*)q_out, seq, pool, stage, splits, bias, hpw, 1);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  rope_kv_kernel<<<grid, 256, 0, s>>>((const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps,
+                                      (float*)q_out, seq, pool, stage, splits, bias, hpw, 0);
   return hipGetLastError();
 }
 
 hipError_t kv_write_rows(const void* k, const void* v, int src_f32, int rows, int Hkv, int D,
                          SeqInfo seq, KvPool pool, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  kv_write_kernel<<<rows, 256, 0, s>>>(k, v, src_f32, Hkv, D, seq, pool);
+  if (pool.exps && pool.fmt != kKvBf16) {  // the blocks' exponents first
+    kv_write_kernel<<<rows, 256, 0, s>>>(k, v, src_f32, Hkv, D, seq, pool, 1);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  kv_write_kernel<<<rows, 256, 0, s>>>(k, v, src_f32, Hkv, D, seq, pool, 0);
   return hipGetLastError();
 }
 
