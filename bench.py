@@ -459,10 +459,11 @@ def main():
                        "p10": round(pcall[len(pcall) // 10], 4),
                        "p90": round(pcall[(9 * len(pcall)) // 10], 4)}
     log(f"prefill: {ms_step:.4f} ms/step wall, per call {prefill_call_ms}")
-    # per-kernel durations from the library's HIP events (a separate pass: the
-    # event records are kept out of the timed steps)
+    # per-kernel durations from the library's HIP events, in a separate pass
+    # of as many calls as the timed steps (the event records are kept out of
+    # the timed steps)
     layer.profile_enable(True)
-    for _ in range(max(3, args.steps // 4)):
+    for _ in range(args.steps):
         layer.prefill(x, y, 0, kv, table)
     torch.cuda.synchronize()
     prof = layer.profile_read()

@@ -192,7 +192,14 @@ typedef struct {
  * output); a [rows, I] bf16 (silu(gate) * up).
  * The projections take fp16 operands where their input is bounded (xn, o,
  * hn: weights converted to fp16 at layer_create, which refuses weights
- * beyond +-65504) and bf16 for the down projection (a is unbounded). */
+ * beyond +-65504) and bf16 for the down projection (a is unbounded).
+ * Ranges: xn and hn are fp16, |x * g / rms(x)| <= sqrt(H) * max|g|, so they
+ * saturate (at +-65504, finite) only for a norm gain above 65504/sqrt(H).
+ * Prefill attention computes on fp16 copies of K and V (exactly the values
+ * the cache holds while they lie in the fp16 range) and writes o in fp16:
+ * |K| and |V| above 65504 saturate there, finite but not the bf16 value.
+ * Decode attention reads a bf16 cache as bf16 (hi + lo pairs of q and P)
+ * and u8 / u4 codes within their calibrated range, with no such limit. */
 typedef struct {
   const void *xn, *qkv, *q, *o, *h, *hn, *a;
 } tdl_workspace_view;
@@ -270,7 +277,9 @@ tdl_status layer_workspace_view(const tdl_layer* layer, tdl_workspace_view* out)
 
 /* Per-stage timing.  While enabled, every call records a pair of hipEvents
  * around each of its kernels on the call's stream (a few microseconds per
- * call).  layer_profile_read synchronises those events, adds their elapsed
+ * call; timing-only events, created without the system-scope fence, so that
+ * recording one does not write back and invalidate the caches between
+ * stages).  layer_profile_read synchronises those events, adds their elapsed
  * times to the totals and returns the totals since the last enable. */
 enum {
   TDL_STAGE_RMSNORM1 = 0,  /* x -> xn                         */

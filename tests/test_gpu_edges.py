@@ -7,6 +7,8 @@ weight copies), and the rejection of misaligned activation pointers.  Same
 tolerance as the other layer tests (stage by stage, cache rows checked)."""
 import dataclasses
 
+import numpy as np
+
 import pytest
 
 import synth
@@ -124,12 +126,48 @@ def test_misaligned_activations_rejected():
     torch.cuda.synchronize()
 
 
-def test_q80_over_128_rows_expanded_weights():
-    # more than 128 rows: the Q8_0 layer's GEMMs run on its fp16/bf16
-    # expanded copies (codes x scales rounded once) instead of the codes
+def test_q80_over_128_rows_codes():
+    # more than 128 rows: the Q8_0 layer's GEMMs take its packed codes and
+    # block scales through the direct-load tiles (no expanded weight copy)
     wl = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=TINY_Q80)
     ctx = [5, 130, 301]
     inp = synth.make_inputs(wl, seed=31, prefill_len=200, prefill_start=40, decode_batch=len(ctx),
                             decode_ctx=ctx)
     layer, kv, t, cache, rows = check_layer(inp, what="mixed q80 203 rows")
     check_cache_rows(inp, kv, cache, range(1 + len(ctx)))
+
+
+def _scaled_kv_inputs(scale, seed):
+    # the tiny fp32 layer with Wk and Wv multiplied by `scale`: K / V values
+    # of about 16 * 0.02 * scale (xn ~ N(0, 1) over 256 inputs)
+    inp = synth.make_inputs(synth.WORKLOADS["tiny_prefill_32"], seed=seed, random_gains=True)
+    w = dict(inp.weights)
+    for name in ("wk", "wv", "bk", "bv"):
+        w[name] = (w[name].astype(np.float64) * scale).astype(np.float32)
+    return dataclasses.replace(inp, weights=w)
+
+
+def test_prefill_attention_near_fp16_limit():
+    # prefill attention computes on fp16 copies of K and V: values up to a
+    # few 10^4 (max |V| below 65504) keep the bf16 tolerance
+    inp = _scaled_kv_inputs(25000.0, 91)
+    layer, kv, t, cache, rows = check_layer(inp, what="prefill, |K|, |V| up to ~3e4")
+    from harness import run_oracle
+    _, (ref, st), _ = run_oracle(inp, want_stages=True)
+    vmax = float(np.abs(st["v"]).max())
+    print(f"max |V| {vmax:.0f}", flush=True)
+    assert 2e4 < vmax < 65504
+
+
+def test_prefill_attention_beyond_fp16_limit_saturates():
+    # beyond 65504 the fp16 copies saturate (documented in include/tdl.h):
+    # the output stays finite
+    import torch
+    from harness import gpu_call, gpu_setup, run_oracle
+    inp = _scaled_kv_inputs(100000.0, 92)
+    _, (ref, st), _ = run_oracle(inp, want_stages=True)
+    assert float(np.abs(st["v"]).max()) > 65504
+    layer, kv, t = gpu_setup(inp)
+    gpu_call(inp, layer, kv, t)
+    torch.cuda.synchronize()
+    assert torch.isfinite(t["y"].float()).all()

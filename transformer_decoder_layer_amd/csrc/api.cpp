@@ -357,8 +357,11 @@ hipEvent_t take_event(tdl_layer* L) {
     L->prof_free.pop_back();
     return e;
   }
+  // timing-only events: without the system-scope fence a recorded event
+  // does not write back and invalidate the caches, which would start every
+  // following stage cold and inflate its time
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 int prof_begin(tdl_layer* L, int stage, hipStream_t st) {
@@ -1024,6 +1027,15 @@ extern "C" tdl_status layer_profile_enable(tdl_layer* L, int enable) {
     L->prof_n[i] = 0;
   }
   L->prof_on = enable != 0;
+  // events for a few calls made up front: creating them inside a profiled
+  // call would hold up its launches
+  if (L->prof_on) {
+    for (size_t n = L->prof_free.size(); n < 8 * 2 * TDL_N_STAGES; ++n) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) break;
+      L->prof_free.push_back(e);
+    }
+  }
   return TDL_OK;
 }
 
