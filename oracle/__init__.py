@@ -16,7 +16,8 @@ Every step is written from the definition it cites.  Where the pages are
 silent or garbled the plainest reading is taken and named in the docstring.
 
 Parity status of each function (what pins it, see tests/test_oracle_*.py):
-  round_bf16, rms_norm, rope_neox, linear, silu, q80_expand, q80_from_gguf, iq8_expand, a8w8_gemm, kv_levels,
+  round_bf16, rms_norm, rope_neox, linear (+ A8W8Weight, quantize_rows_int8), silu, q80_expand,
+  q80_from_gguf, iq8_expand, a8w8_gemm, kv_levels,
   kv_calibrate, kv_quantize, kv_dequantize, kv_block_exponent, kv_quantize_block,
   attention, attention_online, PagedCache (per-channel and per-block x per-channel),
   layer_forward -- all pinned (worked examples, closed forms, brute force,
@@ -155,11 +156,51 @@ def rope_interleaved(x, pos, theta: float) -> np.ndarray:
     return out
 
 
+class A8W8Weight:
+    """A projection on the A8W8 path ([HET] section 4.5): int8 weight codes
+    [N, K] (Linear layout) and a float32 scale per output row (the listing's
+    b_scale[n]; no zero point).  ``act`` is the type ("f16" or "bf16") in
+    which the layer holds the activation this projection multiplies: the
+    activation's int8 codes are decided from those values
+    (quantize_rows_int8)."""
+
+    def __init__(self, codes, scale, act: str):
+        assert codes.dtype == np.int8 and act in ("f16", "bf16")
+        self.codes = codes
+        self.scale = np.asarray(scale, np.float32)
+        self.act = act
+
+
+def quantize_rows_int8(x, act: str):
+    """Per-row symmetric int8 activation quantisation for the A8W8 path.
+
+    [HET] section 4.5 stores activations as int8 with a scale per row
+    (a_scale[m]) but does not say how the scale is chosen.  Reading taken:
+    the row as the layer holds it (rounded to fp16 or bf16, ``act``), s =
+    max|x| / 127 in float32 (1 for an all-zero row), codes round-half-even(x
+    / s) in float32, clipped to [-127, 127].  Returns (codes int8, s float32).
+    """
+    x = np.asarray(x, np.float64)
+    xs = (x.astype(np.float16) if act == "f16" else round_bf16(x)).astype(np.float32)
+    s = (np.abs(xs).max(axis=-1) / np.float32(127)).astype(np.float32)
+    s = np.where(s == 0, np.float32(1), s).astype(np.float32)
+    q = np.rint(xs / s[..., None]).astype(np.int64)  # float32 divide
+    return np.clip(q, -127, 127).astype(np.int8), s
+
+
 def linear(x, w, b=None) -> np.ndarray:
     """Y = X W^T (+ b) with W in [out, in] row-major layout.
 
     [QWEN] section "4. cuBLAS Row-Major 陷阱": out[M,N] = input[M,K] @ W[N,K]^T.
+    An A8W8Weight multiplies the int8 codes of X (quantize_rows_int8) with its
+    own in int8 and dequantises with both scales (a8w8_gemm).
     """
+    if isinstance(w, A8W8Weight):
+        x2 = np.asarray(x, np.float64).reshape(-1, np.shape(x)[-1])
+        codes, s = quantize_rows_int8(x2, w.act)
+        _, y = a8w8_gemm(codes, w.codes, s, w.scale)
+        y = y.reshape(np.shape(x)[:-1] + (w.codes.shape[0],))
+        return y + np.asarray(b, np.float64) if b is not None else y
     y = np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
     if b is not None:
         y = y + np.asarray(b, np.float64)
@@ -473,14 +514,22 @@ def attention_online(q, q_pos, K, V, tile: int) -> np.ndarray:
 # The layer
 # --------------------------------------------------------------------------
 
+# the activation each projection multiplies, as the layer stores it: xn, o
+# and hn in fp16, the SwiGLU product a in bf16
+A8W8_ACT = {"wq": "f16", "wk": "f16", "wv": "f16", "wo": "f16", "wg": "f16", "wu": "f16", "wd": "bf16"}
+
+
 def expand_weights(shape, w: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
     """float64 copies of the weights; Q8_0 and per-channel int8 matrices
-    expanded exactly."""
+    expanded exactly; A8W8 projections kept as codes and scales
+    (A8W8Weight)."""
     out = {}
     for name, a in w.items():
         if name.endswith("_scale") or name.endswith("_zp"):
             continue
-        if shape.weight_dtype == "q80" and name + "_scale" in w:
+        if shape.weight_dtype == "a8w8" and name + "_scale" in w:
+            out[name] = A8W8Weight(a, w[name + "_scale"], A8W8_ACT[name])
+        elif shape.weight_dtype == "q80" and name + "_scale" in w:
             out[name] = q80_expand(a, w[name + "_scale"])
         elif shape.weight_dtype == "iq8" and name + "_scale" in w:
             out[name] = iq8_expand(a, w[name + "_scale"], w[name + "_zp"])

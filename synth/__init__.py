@@ -43,7 +43,7 @@ class LayerShape:
     rope_theta: float
     qkv_bias: bool
     qk_norm: bool
-    weight_dtype: str  # "f32" | "bf16" | "q80" | "iq8"
+    weight_dtype: str  # "f32" | "bf16" | "q80" | "iq8" | "a8w8"
 
     @property
     def n_rep(self) -> int:
@@ -59,6 +59,7 @@ QWEN25_7B = LayerShape("qwen2.5-7b", 3584, 28, 4, 128, 18944, 1e-6, 1e6, True, F
 QWEN3_8B = LayerShape("qwen3-8b", 4096, 32, 8, 128, 12288, 1e-6, 1e6, False, True, "bf16")
 QWEN3_8B_Q80 = dataclasses.replace(QWEN3_8B, name="qwen3-8b-q8_0", weight_dtype="q80")
 QWEN25_7B_IQ8 = dataclasses.replace(QWEN25_7B, name="qwen2.5-7b-iq8", weight_dtype="iq8")
+QWEN25_7B_A8W8 = dataclasses.replace(QWEN25_7B, name="qwen2.5-7b-a8w8", weight_dtype="a8w8")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -136,6 +137,12 @@ def make_weights(shape: LayerShape, seed: int = 0, random_gains: bool = False,
             assert inp % 32 == 0
             codes = rng.integers(-127, 128, size=(out, inp), dtype=np.int8)
             scales = np.abs(_normal(rng, (out, inp // 32), 0.002)).astype(np.float16)
+            return {name: codes, name + "_scale": scales}
+        if shape.weight_dtype == "a8w8":
+            # int8 codes and a float32 scale per output row (symmetric);
+            # code * scale has a spread like N(0, 0.02)
+            codes = rng.integers(-127, 128, size=(out, inp), dtype=np.int8)
+            scales = (np.abs(_normal(rng, (out,), 2.7e-4)) + 1e-5).astype(np.float32)
             return {name: codes, name + "_scale": scales}
         if shape.weight_dtype == "iq8":
             # int8 codes, an int8 zero point and a float32 scale per output
@@ -324,7 +331,8 @@ def make_inputs(wl: Workload, seed: int = 0, shape: Optional[LayerShape] = None,
 def torch_weights(shape: LayerShape, seed: int = 0, device: str = "cuda"):
     """Weights as device tensors in the dtypes the C ABI takes: linear weights
     bf16 (or Q8_0 int8 codes + fp16 scales, or per-row int8 codes + fp32
-    scale + int8 zero point), biases and gains float32."""
+    scale + int8 zero point, or A8W8 int8 codes + fp32 scale per row),
+    biases and gains float32."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(seed)
@@ -337,6 +345,9 @@ def torch_weights(shape: LayerShape, seed: int = 0, device: str = "cuda"):
         if shape.weight_dtype == "q80":
             w[name] = torch.randint(-127, 128, (o, i), generator=g, device=device, dtype=torch.int8)
             w[name + "_scale"] = (torch.randn(o, i // 32, generator=g, device=device).abs() * 0.002).half()
+        elif shape.weight_dtype == "a8w8":
+            w[name] = torch.randint(-127, 128, (o, i), generator=g, device=device, dtype=torch.int8)
+            w[name + "_scale"] = torch.randn(o, generator=g, device=device).abs() * 2.7e-4 + 1e-5
         elif shape.weight_dtype == "iq8":
             w[name] = torch.randint(-128, 128, (o, i), generator=g, device=device, dtype=torch.int8)
             w[name + "_zp"] = torch.randint(-20, 21, (o,), generator=g, device=device, dtype=torch.int8)

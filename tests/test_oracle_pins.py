@@ -4,6 +4,7 @@ routines for special cases, and brute force on tiny inputs.
 
 Each test names the plausible mistake it would catch."""
 import json
+import dataclasses
 import math
 import os
 
@@ -165,6 +166,66 @@ def test_q80_from_gguf_hand_blocks():
     codes, scales = oracle.q80_from_gguf(raw, 1, 256)
     assert codes.view(np.uint8).tolist()[0] == list(range(256))
     assert (scales == 1.0).all()
+
+
+# ------------------------------------------------------ A8W8 projections ---
+
+def test_quantize_rows_int8_worked_example():
+    """Row 0 (exact in fp16): s = 127 / 127 = 1, codes 127, round(-63.5) =
+    -64 and round(0.5) = 0 (ties to even), 0.25 -> 0; row 1 all zero: s = 1,
+    codes 0; a bf16 row: 300 is exact in bf16, its code is 127 and 1 rounds to
+    0 at s = 300/127."""
+    x = np.array([[127.0, -63.5, 0.5, 0.25, 0.0], [0.0, 0.0, 0.0, 0.0, 0.0]])
+    codes, s = oracle.quantize_rows_int8(x, "f16")
+    assert codes.tolist() == [[127, -64, 0, 0, 0], [0, 0, 0, 0, 0]]
+    assert s.tolist() == [1.0, 1.0]
+    codes, s = oracle.quantize_rows_int8(np.array([[300.0, 1.0, -300.0]]), "bf16")
+    assert codes.tolist() == [[127, 0, -127]]
+    assert s[0] == np.float32(np.float32(300.0) / np.float32(127.0))
+    # the row is rounded to its storage type first: 1 + 2^-9 is 1 in bf16
+    # (8 significant bits) but not in fp16 (11): it sets the scale only there
+    x = np.array([[1.0 + 2.0 ** -9, 0.5]])
+    assert oracle.quantize_rows_int8(x, "bf16")[1][0] == np.float32(1.0) / np.float32(127.0)
+    assert oracle.quantize_rows_int8(x, "f16")[1][0] == np.float32(1.0 + 2.0 ** -9) / np.float32(127.0)
+
+
+def test_a8w8_linear_exact_on_grid_and_orientation():
+    """Activations on their own int8 grid (each row's largest entry 127 s_m)
+    quantise exactly, so the A8W8 product equals X (codes x row scale)^T; the
+    activation scale runs over rows of X and the weight scale over rows of W
+    (catches a transposed scale)."""
+    rng = np.random.default_rng(23)
+    M, N, K = 5, 7, 64
+    qa = rng.integers(-127, 128, (M, K))
+    qa[:, 3] = 127
+    sa = np.array([0.5, 0.25, 1.0, 2.0, 0.125])  # powers of two: exact in fp16
+    x = qa * sa[:, None]
+    wc = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    ws = (rng.random(N) * 0.01 + 0.001).astype(np.float32)
+    W = oracle.A8W8Weight(wc, ws, "f16")
+    y = oracle.linear(x, W)
+    ref = x @ (wc.astype(np.float64) * ws.astype(np.float64)[:, None]).T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    b = rng.standard_normal(N)
+    np.testing.assert_allclose(oracle.linear(x, W, b), ref + b, rtol=1e-12, atol=1e-12)
+
+
+def test_a8w8_layer_close_to_expanded_weights():
+    """A tiny layer on the A8W8 path stays within the int8 activation
+    quantisation's error of the same layer with the weights expanded
+    (codes x scale) in float64: a few tenths of a percent."""
+    shape = dataclasses.replace(synth.TINY, weight_dtype="a8w8")
+    inp = synth.make_inputs(synth.Workload("tiny_a8w8", shape, "prefill", prefill_len=24, kv_dtype="none"),
+                            seed=5, random_gains=True)
+    W = oracle.expand_weights(shape, inp.weights)
+    E = {k: (np.asarray(v.codes, np.float64) * v.scale.astype(np.float64)[:, None]
+             if isinstance(v, oracle.A8W8Weight) else v) for k, v in W.items()}
+    q0, ql, ctx = np.array([0]), np.array([24]), np.array([0])
+    y = oracle.layer_forward(shape, W, inp.x, q0, ql, ctx, None, None)
+    ye = oracle.layer_forward(shape, E, inp.x, q0, ql, ctx, None, None)
+    x = inp.x.astype(np.float64)
+    rel = np.abs((y - x) - (ye - x)).sum() / np.abs(ye - x).sum()
+    assert 1e-4 < rel < 2e-2
 
 
 # ------------------------------------------- per-channel int8 weights ---
