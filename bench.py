@@ -345,6 +345,43 @@ def other_workloads(args, torch, synth, tdl, stream, layer512):
     log(f"a8w8 gemm: {ms * 1e3:.1f} us, {tops:.0f} TOP/s")
     del A8, B8, o8
 
+    # ---- the Qwen2.5-7B layer on the A8W8 path (int8 weights with a scale
+    # per output row, every projection's input quantised per row to int8):
+    # causal prefill of 4096 tokens into a bf16 paged cache, as the headline
+    shape = synth.QWEN25_7B_A8W8
+    T, H, D, Hq, Hkv = 4096, shape.hidden, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    log("qwen2.5 a8w8 prefill 4096: weights")
+    layer = tdl.Layer(tdl.make_config(shape, max_tokens=T, max_seqs=1, max_position=T),
+                      synth.torch_weights(shape, seed=90))
+    kv = tdl.KvCache(T // 16, Hkv, D, "bf16")
+    table = torch.arange(T // 16, dtype=torch.int32, device="cuda").view(1, -1)
+    x = synth.torch_normal((T, H), seed=91, dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    step = lambda: layer.prefill(x, y, 0, kv, table)
+    for _ in range(3):
+        step()
+    times = timed_steps(torch, stream, step, n_steps)
+    ms = float(np.median(times))
+    lin = linear_flops_per_token(shape) * T
+    fl = lin + attention_flops(D, Hq, T * (T + 1) // 2)
+    assert torch.isfinite(y.float()).all(), "non-finite a8w8 prefill output"
+    stages = stage_profile(layer, step, 5)
+    gu_ms = stages.get("gate_up", 0.0)
+    out["qwen25_a8w8_prefill_4096"] = {
+        "workload": "qwen2.5-7b-shaped layer on the A8W8 path (int8 weights, fp32 scale per output row; each "
+                    "projection's input rows quantised to int8 with a scale per row; int8 MFMAs with int32 "
+                    "sums), causal prefill of 4096 tokens into a bf16 paged cache; attention on fp16 MFMAs",
+        "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "linear_ops_per_step": lin,
+        "gate_up": {"bound": "mfma", "ms_per_launch": gu_ms,
+                    "achieved": round(2 * T * 2 * shape.intermediate * H / (gu_ms * 1e-3) / 1e12, 1) if gu_ms else None,
+                    "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "note": "quantisation of hn + int8 GEMM + SiLU-gate pass"},
+        "stages_ms": stages}
+    log(f"qwen2.5 a8w8 prefill: {ms:.3f} ms/step")
+    layer.close()
+    kv.close()
+    del x, y, kv, table
+
     # ---- a 28-layer stack of Qwen2.5-7B-shaped layers (each with its own
     # weights and bf16 cache), decode batch 64: one token of every sequence
     # through every layer per step, eager and as a replayed HIP graph

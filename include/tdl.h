@@ -65,7 +65,8 @@ typedef enum {
   TDL_Q8_0 = 2,    /* 32 int8 codes + one fp16 scale per block along K          */
   TDL_U8_ASYM = 3, /* uint8 codes + per-channel fp32 scale and int32 zero point */
   TDL_U4_ASYM = 4, /* uint4 codes, two per byte, + the same per-channel parameters */
-  TDL_I8_ROW = 5   /* weight-only int8: codes + per-output-row fp32 scale and int8 zero point */
+  TDL_I8_ROW = 5,  /* weight-only int8: codes + per-output-row fp32 scale and int8 zero point */
+  TDL_A8W8 = 6     /* int8 weights + per-output-row fp32 scale, int8 activations ([HET] 4.5) */
 } tdl_dtype;
 
 typedef void* tdl_stream; /* hipStream_t */
@@ -85,7 +86,7 @@ typedef struct {
   float rope_theta;       /* RoPE base; half-split pairs (i, i + D/2)       */
   int32_t qkv_bias;       /* 1: Q/K/V projections have a bias               */
   int32_t qk_norm;        /* 1: per-head RMSNorm on q and k before RoPE     */
-  int32_t weight_dtype;   /* TDL_F32, TDL_BF16, TDL_Q8_0 or TDL_I8_ROW       */
+  int32_t weight_dtype;   /* TDL_F32, TDL_BF16, TDL_Q8_0, TDL_I8_ROW or TDL_A8W8 */
   int32_t max_tokens;     /* most rows (new tokens) in one call             */
   int32_t max_seqs;       /* most sequences in one call                     */
   int32_t max_position;   /* positions 0 .. max_position-1 can be rotated   */
@@ -98,7 +99,15 @@ typedef struct {
  * (weight-only per-channel int8, [HET] 4.4): int8 codes, w*_scale float32
  * [out] and w*_zp int8 [out], W[n][k] = (code[n][k] - zp[n]) * scale[n];
  * decode-sized calls (<= 128 rows) stream the codes, larger ones use fp16 /
- * bf16 copies expanded at create time (when max_tokens > 128).  Biases bq/bk/bv
+ * bf16 copies expanded at create time (when max_tokens > 128).  TDL_A8W8
+ * (int8 activations x int8 weights, [HET] 4.5): int8 codes and w*_scale
+ * float32 [out] (symmetric, W[n][k] = code[n][k] * scale[n]); every
+ * projection quantises its input rows to int8 with a float32 scale per row
+ * (s = max|x| / 127 of the row as the layer holds it: xn, o, hn in fp16, the
+ * SwiGLU product in bf16; codes round-half-even(x / s), clipped to +-127),
+ * multiplies on the int8 matrix units with int32 sums and dequantises with
+ * both scales in fp32 before the usual bias / residual / SiLU-gate.
+ * Needs every input dimension a multiple of 16.  Biases bq/bk/bv
  * (if qkv_bias) and gains ln1/ln2 [H], q_norm/k_norm [D] (if qk_norm) are
  * float32.  Unused pointers may be NULL.  layer_create copies (and repacks)
  * everything into library-owned memory; the caller may free its copies once

@@ -22,9 +22,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 TDL_OK, TDL_E_INVALID, TDL_E_UNSUPPORTED, TDL_E_CAPACITY, TDL_E_NOMEM, TDL_E_HIP = range(6)
-TDL_BF16, TDL_F32, TDL_Q8_0, TDL_U8_ASYM, TDL_U4_ASYM, TDL_I8_ROW = range(6)
+TDL_BF16, TDL_F32, TDL_Q8_0, TDL_U8_ASYM, TDL_U4_ASYM, TDL_I8_ROW, TDL_A8W8 = range(7)
 _DTYPES = {"bf16": TDL_BF16, "f32": TDL_F32, "q80": TDL_Q8_0, "u8": TDL_U8_ASYM, "u4": TDL_U4_ASYM,
-           "iq8": TDL_I8_ROW}
+           "iq8": TDL_I8_ROW, "a8w8": TDL_A8W8}
 
 c_i32, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 P_i32 = ctypes.POINTER(ctypes.c_int32)

@@ -120,6 +120,9 @@ struct tdl_layer {
   tdl_layer_config cfg;
   bool q80 = false;
   bool iq8 = false;  // per-row int8 codes (TDL_I8_ROW)
+  bool a8w8 = false;  // int8 weights and activations (TDL_A8W8), scales in w*_rs
+  int8_t* aq = nullptr;  // A8W8: int8 codes of a projection's input rows
+  float* as = nullptr;   //       and their per-row scales
   // per-row int8: scale and zero point (as floats) of every stored row, in
   // the stored row order (QKV rows concatenated, gate/up interleaved)
   float *wqkv_rs = nullptr, *wqkv_rz = nullptr, *wo_rs = nullptr, *wo_rz = nullptr;
@@ -218,8 +221,8 @@ tdl_status check_config(const tdl_layer_config* c) {
   if (c->intermediate % 16)
     return fail(TDL_E_UNSUPPORTED, "intermediate must be a multiple of 16 (got %d)", c->intermediate);
   if (c->weight_dtype != TDL_F32 && c->weight_dtype != TDL_BF16 && c->weight_dtype != TDL_Q8_0 &&
-      c->weight_dtype != TDL_I8_ROW)
-    return fail(TDL_E_INVALID, "weight_dtype must be TDL_F32, TDL_BF16, TDL_Q8_0 or TDL_I8_ROW");
+      c->weight_dtype != TDL_I8_ROW && c->weight_dtype != TDL_A8W8)
+    return fail(TDL_E_INVALID, "weight_dtype must be TDL_F32, TDL_BF16, TDL_Q8_0, TDL_I8_ROW or TDL_A8W8");
   if ((c->weight_dtype == TDL_Q8_0 || c->weight_dtype == TDL_I8_ROW) &&
       (c->hidden % 32 || c->intermediate % 32 || (c->n_q_heads * c->head_dim) % 32))
     return fail(TDL_E_INVALID, "int8 weights need every input dimension to be a multiple of 32");
@@ -383,6 +386,21 @@ struct StageTimer {
   }
 };
 
+// A8W8 projection `mat` (0 QKV, 1 output, 2 gate/up, 3 down) over M rows:
+// the input rows A (fp16, or bf16 for the down projection) to int8 with a
+// scale per row, then the int8 GEMM, dequantised with both scales into out
+// (fp32 [M][N]).
+tdl_status a8w8_project(tdl_layer* L, const Scratch& sc, hipStream_t st, int mat, int M, int N, int K,
+                        const void* A, float* out) {
+  if (out == sc.gemm_ws && (size_t)M * N > sc.gemm_floats)
+    return fail(TDL_E_CAPACITY, "GEMM workspace too small for the int8 GEMM's result (M=%d N=%d)", M, N);
+  HIP_TRY(quant_rows_i8(A, mat == 3, M, K, L->aq, L->as, st));
+  const void* B = mat == 0 ? L->wqkv : mat == 1 ? L->wo : mat == 2 ? L->wgu : L->wd;
+  const float* bs = mat == 0 ? L->wqkv_rs : mat == 1 ? L->wo_rs : mat == 2 ? L->wgu_rs : L->wd_rs;
+  HIP_TRY(a8w8_gemm(L->aq, B, L->as, bs, nullptr, out, M, N, K, st));
+  return TDL_OK;
+}
+
 // The whole layer over `rows` rows.  Sequences 0..n_prefill-1 of `seq` use the
 // prefill attention kernel, decode sequences dec_first .. dec_first+n_dec-1
 // the paged decode kernel.
@@ -411,15 +429,18 @@ tdl_status run_layer(tdl_layer* L, const Scratch& sc, hipStream_t st, const void
   PrefillStage stage{L->stage_k, L->stage_v, L->stage_rows, std::min(n_prefill, kStagedSeqs)};
   {
     StageTimer t(L, TDL_STAGE_QKV, st, sc.timed);
-    TRY(run_gemm(L, sc, st, 0, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->wqkv_rs, L->wqkv_rz, L->wexp[0], EPI_BIAS_F32, L->bqkv, nullptr,
-                 0, L->qkv, L->Nqkv, true, &qkv_splits));
+    if (L->a8w8)  // (its bias is added by the RoPE kernel)
+      TRY(a8w8_project(L, sc, st, 0, rows, L->Nqkv, H, L->xn, (float*)L->qkv));
+    else
+      TRY(run_gemm(L, sc, st, 0, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->wqkv_rs, L->wqkv_rz, L->wexp[0], EPI_BIAS_F32, L->bqkv, nullptr,
+                   0, L->qkv, L->Nqkv, true, &qkv_splits));
   }
   {
     StageTimer t(L, TDL_STAGE_ROPE_KV, st, sc.timed);
     HIP_TRY(rope_kv_write(qkv_splits > 1 ? (const void*)sc.gemm_ws : (const void*)L->qkv, rows, Hq, Hkv,
                           D, L->rope, c.qk_norm ? L->qn : nullptr, c.qk_norm ? L->kn : nullptr,
                           c.rms_eps, L->q, seq, pool, stage, st, qkv_splits,
-                          qkv_splits > 1 ? L->bqkv : nullptr));
+                          qkv_splits > 1 || L->a8w8 ? L->bqkv : nullptr));
   }
   if (n_prefill) {
     StageTimer t(L, TDL_STAGE_ATTN_PREFILL, st, sc.timed);
@@ -428,6 +449,43 @@ tdl_status run_layer(tdl_layer* L, const Scratch& sc, hipStream_t st, const void
   if (n_dec) {
     StageTimer t(L, TDL_STAGE_ATTN_DECODE, st, sc.timed);
     HIP_TRY(attn_decode(dp, L->q, pool, seq, dec_first, n_dec, Hq, Hkv, D, L->o, sc.dec_part, st));
+  }
+  if (L->a8w8) {
+    // each projection's fp32 result goes through the GEMM workspace as one
+    // slice of the split-K form, whose consumers add the residual (RMSNorm-2)
+    // or run the SiLU-gate / residual epilogue (the reduction kernel)
+    if (H > kFusedNormMaxH) return fail(TDL_E_UNSUPPORTED, "A8W8 layers need hidden <= %d", kFusedNormMaxH);
+    {
+      StageTimer t(L, TDL_STAGE_O_PROJ, st, sc.timed);
+      TRY(a8w8_project(L, sc, st, 1, rows, H, Hq * D, L->o, sc.gemm_ws));
+    }
+    {
+      StageTimer t(L, TDL_STAGE_RMSNORM2, st, sc.timed);
+      HIP_TRY(rmsnorm_splits_resid(sc.gemm_ws, 1, x, L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
+    }
+    GemmArgs ep{};
+    ep.ws = sc.gemm_ws;
+    ep.splits = 1;
+    ep.M = rows;
+    {
+      StageTimer t(L, TDL_STAGE_GATE_UP, st, sc.timed);
+      TRY(a8w8_project(L, sc, st, 2, rows, 2 * I, H, L->hn, sc.gemm_ws));
+      ep.N = 2 * I;
+      ep.C = L->a;
+      ep.ldc = I;
+      HIP_TRY(gemm_epilogue(ep, EPI_SILU_GATE, st));
+    }
+    {
+      StageTimer t(L, TDL_STAGE_DOWN, st, sc.timed);
+      TRY(a8w8_project(L, sc, st, 3, rows, H, I, L->a, sc.gemm_ws));
+      ep.N = H;
+      ep.C = y;
+      ep.ldc = H;
+      ep.resid = L->h;
+      ep.ldr = H;
+      HIP_TRY(gemm_epilogue(ep, EPI_RESID_BF16, st));
+    }
+    return TDL_OK;
   }
   int o_splits = 1;
   {
@@ -504,7 +562,8 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   const tdl_layer_config& c = *cfg;
   const bool q80 = c.weight_dtype == TDL_Q8_0;
   const bool iq8 = c.weight_dtype == TDL_I8_ROW;
-  const bool codes = q80 || iq8;  // 1-byte codes stored as given
+  const bool a8w8 = c.weight_dtype == TDL_A8W8;
+  const bool codes = q80 || iq8 || a8w8;  // 1-byte codes stored as given
   if (!w->ln1 || !w->wq || !w->wk || !w->wv || !w->wo || !w->ln2 || !w->wg || !w->wu || !w->wd)
     return fail(TDL_E_INVALID, "a required weight pointer is NULL");
   if (c.qkv_bias && (!w->bq || !w->bk || !w->bv))
@@ -518,6 +577,9 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
               !w->wu_scale || !w->wd_scale || !w->wq_zp || !w->wk_zp || !w->wv_zp || !w->wo_zp ||
               !w->wg_zp || !w->wu_zp || !w->wd_zp))
     return fail(TDL_E_INVALID, "per-row int8 weights need every *_scale and *_zp pointer");
+  if (a8w8 && (!w->wq_scale || !w->wk_scale || !w->wv_scale || !w->wo_scale || !w->wg_scale ||
+               !w->wu_scale || !w->wd_scale))
+    return fail(TDL_E_INVALID, "A8W8 weights need every *_scale pointer");
 
   hipStream_t st = (hipStream_t)stream;
   {
@@ -530,6 +592,7 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   L->cfg = c;
   L->q80 = q80;
   L->iq8 = iq8;
+  L->a8w8 = a8w8;
   const int H = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads, I = c.intermediate;
   const int QD = Hq * D, KD = Hkv * D;
   L->Nqkv = QD + 2 * KD;
@@ -625,6 +688,23 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
     CHIP(interleave_gate_up(w->wg_scale, w->wu_scale, (int)rs, I, L->wgu_s, st));
     CHIP(hipStreamSynchronize(st));
   }
+  if (a8w8) {
+    // per-row scales (float32, copied) in the stored row order; gate/up rows
+    // interleaved like the codes (which stay row-major: the int8 GEMM reads
+    // them so)
+    auto rows_f32 = [&](float** dst, int n) { return dalloc(L, dst, (size_t)n * 4); };
+    CTRY(rows_f32(&L->wqkv_rs, L->Nqkv));
+    CTRY(rows_f32(&L->wo_rs, H));
+    CTRY(rows_f32(&L->wgu_rs, 2 * I));
+    CTRY(rows_f32(&L->wd_rs, H));
+    CHIP(copy_f32((const float*)w->wq_scale, L->wqkv_rs, QD, st));
+    CHIP(copy_f32((const float*)w->wk_scale, L->wqkv_rs + QD, KD, st));
+    CHIP(copy_f32((const float*)w->wv_scale, L->wqkv_rs + QD + KD, KD, st));
+    CHIP(copy_f32((const float*)w->wo_scale, L->wo_rs, H, st));
+    CHIP(copy_f32((const float*)w->wd_scale, L->wd_rs, H, st));
+    CHIP(interleave_gate_up(w->wg_scale, w->wu_scale, 4, I, L->wgu_rs, st));
+    CHIP(hipStreamSynchronize(st));
+  }
   if (iq8) {
     // per-row scales (float32, copied) and zero points (int8 -> float), in
     // the stored row order; gate/up rows interleaved like the codes
@@ -684,7 +764,7 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
       (void)hipFree(tmp);
     }
   }
-  if (codes) {
+  if (q80 || iq8) {
     // the codes themselves in the packed code layout where the shape allows
     // (the stream kernel: one contiguous 1 KB read per wave and stage; the
     // large-M Q8_0 kernel: one direct 1 KB copy per 16 rows and 64 k); after
@@ -734,6 +814,13 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   CTRY(dalloc(L, &L->a, (size_t)T * I * 2));
   gemm_ws_need(c, L->Nqkv, q80 ? kWQ80 : iq8 ? kWIQ8 : kWDense, L->wexp[0] != nullptr,
                &L->gemm_ws_floats);
+  if (a8w8) {
+    // the int8 GEMM's fp32 result of the widest projection, and the int8
+    // codes and scales of the widest input
+    L->gemm_ws_floats = std::max(L->gemm_ws_floats, (size_t)T * std::max({L->Nqkv, H, 2 * I}));
+    CTRY(dalloc(L, &L->aq, (size_t)T * std::max({H, QD, I})));
+    CTRY(dalloc(L, &L->as, (size_t)T * 4));
+  }
   CTRY(dalloc(L, &L->gemm_ws, L->gemm_ws_floats * 4));
   const int max_dec = std::min(c.max_seqs, c.max_tokens);
   L->dec_part_floats = decode_part_need(c, max_dec);
@@ -876,6 +963,7 @@ extern "C" tdl_status layer_decode_paged_noalloc(tdl_layer* L, tdl_stream stream
       g = std::max(g, gemm_plan(batch, shapes[m][0], shapes[m][1], f, shapes[m][2],
                                 f != kWDense && L->packed[m]).ws_floats);
     }
+  if (L->a8w8) g = std::max(g, (size_t)batch * std::max({L->Nqkv, H, 2 * I}));
   const DecodePlan dp = decode_plan(batch, c.n_q_heads, c.n_kv_heads, c.head_dim, max_ctx_len,
                                     pool_of(L, kv).fmt);
   const size_t g_al = (g + 63) & ~size_t(63);  // partition results start 256-byte aligned

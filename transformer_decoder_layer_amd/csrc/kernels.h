@@ -236,6 +236,14 @@ hipError_t expand_iq8(const void* codes, const float* scale, const float* zp, in
 // out = C * a_scale[m] * b_scale[n] in fp32.  K % 16 == 0.
 hipError_t a8w8_gemm(const void* A, const void* B, const float* a_scale, const float* b_scale,
                      int32_t* C, float* out, int M, int N, int K, hipStream_t s);
+// Per-row symmetric int8 quantisation of an fp16 (x_bf16 = 0) or bf16 row
+// [rows][K]: s[r] = max|x| / 127 (1 for a zero row), q = rint(x / s)
+// clipped to +-127.  K % 16 == 0.
+hipError_t quant_rows_i8(const void* x, int x_bf16, int rows, int K, int8_t* q, float* s, hipStream_t st);
+// The epilogue of a GEMM whose fp32 result sits in a.ws as a.splits slices
+// [splits][M][N]: the slices summed in order, then bias / residual /
+// SiLU-gate into a.C (the split-K reduction kernel).
+hipError_t gemm_epilogue(const GemmArgs& a, int epi, hipStream_t s);
 // int8 [n] -> float [n]
 hipError_t i8_to_f32(const void* src, float* dst, int64_t n, hipStream_t s);
 hipError_t pack_weights(const void* src, void* dst, int N, int K, hipStream_t s);

@@ -720,6 +720,51 @@ hipError_t expand_q80(const void* codes, const void* scales, int N, int K, void*
   return hipGetLastError();
 }
 
+// Per-row symmetric int8 quantisation (the A8W8 path's activations): one
+// workgroup per row, the row's absolute maximum by a block reduction, then
+// codes round-half-even(x / s) with a correctly rounded fp32 divide, eight
+// per thread and store.
+template <typename T>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ x, int K, int8_t* __restrict__ q,
+                                                         float* __restrict__ s) {
+  const int row = blockIdx.x;
+  const T* xr = x + (size_t)row * K;
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int k = threadIdx.x * 8; k < K; k += 256 * 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)xr[k + e]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = m == 0.f ? 1.f : __fdiv_rn(m, 127.f);
+  if (threadIdx.x == 0) s[row] = sc;
+  int8_t* qr = q + (size_t)row * K;
+  for (int k = threadIdx.x * 8; k < K; k += 256 * 8) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float c = __builtin_rintf(__fdiv_rn((float)xr[k + e], sc));
+      c = fminf(fmaxf(c, -127.f), 127.f);
+      w[e >> 2] |= ((uint32_t)(int)c & 0xffu) << (8 * (e & 3));
+    }
+    *(uint2*)(qr + k) = make_uint2(w[0], w[1]);
+  }
+}
+
+hipError_t quant_rows_i8(const void* x, int x_bf16, int rows, int K, int8_t* q, float* s, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (K % 16) return hipErrorInvalidValue;
+  if (x_bf16)
+    quant_rows_kernel<bf16><<<rows, 256, 0, st>>>((const bf16*)x, K, q, s);
+  else
+    quant_rows_kernel<f16><<<rows, 256, 0, st>>>((const f16*)x, K, q, s);
+  return hipGetLastError();
+}
+
 // GGUF Q8_0 blocks (34 bytes: binary16 scale, then 32 int8 codes) to split
 // codes and scales; one thread per block, blocks in row-major order map to
 // codes at 32 i and scales at i.  Reads in 2-byte words (the blocks are only
