@@ -53,6 +53,9 @@ def parse():
                     help="prompt tokens the oracle runs for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--rope-unfused", action="store_true",
+                    help="the RoPE kernel rotates the prefill queries too (instead of the prefill "
+                         "attention kernel as it loads them)")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the other workloads (512-token prefill, Qwen3 u8 / u4 decode, Q8_0 mixed step, layer stack)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -461,7 +464,7 @@ def main():
 
     log("generating weights")
     w = synth.torch_weights(shape, seed=0)
-    cfg = tdl.make_config(shape, max_tokens=T, max_seqs=64, max_position=8192)
+    cfg = tdl.make_config(shape, max_tokens=T, max_seqs=64, max_position=8192, rope_fused=not args.rope_unfused)
     layer = tdl.Layer(cfg, w)
 
     # ------------------------------------------------------------ prefill

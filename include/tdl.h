@@ -90,6 +90,14 @@ typedef struct {
   int32_t max_tokens;     /* most rows (new tokens) in one call             */
   int32_t max_seqs;       /* most sequences in one call                     */
   int32_t max_position;   /* positions 0 .. max_position-1 can be rotated   */
+  int32_t rope_fused;     /* 1: prefill rows' queries are normalised (Qwen3
+                             Q-norm), given their bias and rotated by the
+                             prefill attention kernel as it loads them from
+                             the QKV projection ([TFF] 3.7.2 item 4, RoPE
+                             applied while Q is loaded); the RoPE kernel then
+                             handles only their K and V.  0: the RoPE kernel
+                             writes every row's rotated q.  Same results
+                             either way up to the rounding of q.             */
 } tdl_layer_config;
 
 /* Weights, device pointers in PyTorch Linear layout ([out, in], row-major).
@@ -196,7 +204,8 @@ typedef struct {
  * (Hq+2Hkv)*D] float32 (projections + bias, before RoPE; not written when a
  * decode-sized projection is split over K: the RoPE kernel then sums the
  * split partial products itself); q [rows, Hq, D]
- * float32 (after Q-norm and RoPE); o [rows, Hq*D] fp16 (attention output);
+ * float32 (after Q-norm and RoPE; with rope_fused, written for decode rows
+ * only); o [rows, Hq*D] fp16 (attention output);
  * h [rows, H] float32 (first residual); hn [rows, H] fp16 (RMSNorm-2
  * output); a [rows, I] bf16 (silu(gate) * up).
  * The projections take fp16 operands where their input is bounded (xn, o,

@@ -158,7 +158,8 @@ class GpuRun:
     tensors: dict
 
 
-def gpu_setup(inp: synth.LayerInputs, max_tokens: Optional[int] = None, max_position: int = 16384):
+def gpu_setup(inp: synth.LayerInputs, max_tokens: Optional[int] = None, max_position: int = 16384,
+              rope_fused: bool = False):
     """Creates the layer and the cache (filled with the cached tokens) and
     uploads x and the batch arrays."""
     import torch
@@ -166,7 +167,7 @@ def gpu_setup(inp: synth.LayerInputs, max_tokens: Optional[int] = None, max_posi
     wl, shape, b = inp.workload, inp.workload.shape, inp.batch
     n_rows = b.n_rows
     cfg = tdl.make_config(shape, max_tokens=max_tokens or max(n_rows, 1), max_seqs=max(b.n_seqs, 1),
-                          max_position=max_position)
+                          max_position=max_position, rope_fused=rope_fused)
     layer = tdl.Layer(cfg, device_weights(shape, inp.weights))
     kv = None
     t = {}

@@ -66,7 +66,8 @@ def check_layer(inp, seqs=None, what="", stages=True, **setup):
     if stages:
         g = gpu_stages(layer, t, rows, shape)
         errs["xn"] = compare(g["xn"], st["xn"])
-        errs["q"] = compare(g["q"], st["q"].reshape(len(rows), -1))
+        if not setup.get("rope_fused"):  # (fused: prefill rows' q never reaches the workspace)
+            errs["q"] = compare(g["q"], st["q"].reshape(len(rows), -1))
         errs["o"] = compare(g["o"], st["o"])
         errs["h-x"] = compare(g["h"] - x_gpu, st["h"] - x)
         errs["a"] = compare(g["a"], st["a"])

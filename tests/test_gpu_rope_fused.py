@@ -1,0 +1,57 @@
+"""rope_fused layers: the prefill rows' queries go from the QKV projection
+into the prefill attention kernel, which adds the bias (A8W8 layers), the
+Qwen3 Q-norm and RoPE as it loads them ([TFF] 3.7.2 item 4: RoPE applied
+while Q is loaded).  Against the oracle, stage by stage (the attention
+output checks the fused query path): bf16 prefill with a QKV bias (no cache,
+paged, a chunk after cached tokens), a Qwen3-shaped prefill and mixed step
+(Q-norm; the decode rows keep the RoPE kernel's q), a u8 cache, Q8_0 and
+A8W8 layers."""
+import dataclasses
+
+import pytest
+
+import synth
+from test_gpu_a8w8_layer import TINY_A8
+from test_gpu_layer import TINY_Q3, TINY_Q80, check_cache_rows, check_layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_decoder_layer_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+@pytest.mark.parametrize("T", [1, 45, 150])
+def test_fused_prefill_bias(T):
+    inp = synth.make_inputs(synth.WORKLOADS["tiny_prefill_32"], seed=120 + T, prefill_len=T, random_gains=True)
+    check_layer(inp, what=f"fused prefill {T}, no cache", rope_fused=True)
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], kv_dtype="bf16")
+    inp = synth.make_inputs(wl, seed=130 + T, prefill_len=T, prefill_start=37, spare_blocks=1,
+                            random_gains=True)
+    layer, kv, t, cache, rows = check_layer(inp, what=f"fused chunk {T} at 37", rope_fused=True)
+    check_cache_rows(inp, kv, cache, [0])
+
+
+def test_fused_qwen3_prefill_mixed_u8():
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=TINY_Q3, kv_dtype="bf16")
+    inp = synth.make_inputs(wl, seed=140, prefill_len=100, spare_blocks=1, random_gains=True)
+    check_layer(inp, what="fused qwen3 prefill 100", rope_fused=True)
+    wm = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=TINY_Q3, kv_dtype="u8")
+    inp = synth.make_inputs(wm, seed=141, prefill_len=70, decode_batch=4, decode_ctx=[3, 16, 40, 129],
+                            random_gains=True)
+    layer, kv, t, cache, rows = check_layer(inp, what="fused qwen3 mixed u8", rope_fused=True)
+    check_cache_rows(inp, kv, cache, range(5))
+
+
+def test_fused_q80_and_a8w8():
+    wm = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=TINY_Q80)
+    inp = synth.make_inputs(wm, seed=142, prefill_len=160, decode_batch=3, decode_ctx=[5, 16, 77],
+                            random_gains=True)
+    check_layer(inp, what="fused q80 mixed", rope_fused=True)
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=TINY_A8, kv_dtype="bf16")
+    inp = synth.make_inputs(wl, seed=143, prefill_len=150, spare_blocks=1, random_gains=True)
+    check_layer(inp, what="fused a8w8 prefill 150", rope_fused=True)

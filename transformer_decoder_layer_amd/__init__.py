@@ -44,7 +44,7 @@ class LayerConfig(ctypes.Structure):
                 ("head_dim", c_i32), ("intermediate", c_i32), ("rms_eps", c_f32),
                 ("rope_theta", c_f32), ("qkv_bias", c_i32), ("qk_norm", c_i32),
                 ("weight_dtype", c_i32), ("max_tokens", c_i32), ("max_seqs", c_i32),
-                ("max_position", c_i32)]
+                ("max_position", c_i32), ("rope_fused", c_i32)]
 
 
 _WEIGHT_FIELDS = ["ln1", "wq", "bq", "wk", "bk", "wv", "bv", "wo", "ln2", "wg", "wu", "wd",
@@ -367,14 +367,15 @@ def q80_import_gguf(blocks, rows: int, cols: int, codes, scales, stream=None):
     _check("q80_import_gguf", _q80_gguf(_stream(stream), _ptr(blocks), rows, cols, _ptr(codes), _ptr(scales)))
 
 
-def make_config(shape, max_tokens: int, max_seqs: int = 1, max_position: int = 8192) -> LayerConfig:
+def make_config(shape, max_tokens: int, max_seqs: int = 1, max_position: int = 8192,
+                rope_fused: bool = False) -> LayerConfig:
     """LayerConfig from any object with the layer-shape attributes (hidden,
     n_q_heads, n_kv_heads, head_dim, intermediate, rms_eps, rope_theta,
-    qkv_bias, qk_norm, weight_dtype in {"f32", "bf16", "q80", "iq8"})."""
+    qkv_bias, qk_norm, weight_dtype in {"f32", "bf16", "q80", "iq8", "a8w8"})."""
     return LayerConfig(shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                        shape.intermediate, shape.rms_eps, shape.rope_theta, int(shape.qkv_bias),
                        int(shape.qk_norm), _DTYPES[shape.weight_dtype], max_tokens, max_seqs,
-                       max_position)
+                       max_position, int(rope_fused))
 
 
 class Layer:

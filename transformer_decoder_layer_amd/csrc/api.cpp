@@ -233,6 +233,7 @@ tdl_status check_config(const tdl_layer_config* c) {
                 kMaxDecodeSeqs, kMaxDecodePosition);
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f))
     return fail(TDL_E_INVALID, "rms_eps must be >= 0 and rope_theta > 0");
+  if (c->rope_fused != 0 && c->rope_fused != 1) return fail(TDL_E_INVALID, "rope_fused must be 0 or 1");
   return TDL_OK;
 }
 
@@ -435,16 +436,24 @@ tdl_status run_layer(tdl_layer* L, const Scratch& sc, hipStream_t st, const void
       TRY(run_gemm(L, sc, st, 0, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->wqkv_rs, L->wqkv_rz, L->wexp[0], EPI_BIAS_F32, L->bqkv, nullptr,
                    0, L->qkv, L->Nqkv, true, &qkv_splits));
   }
+  // rope_fused: the prefill rows' queries go from the (whole, unsplit) QKV
+  // projection straight into the prefill attention kernel, which adds the
+  // bias still missing (A8W8), applies the Q-norm and RoPE as it loads them
+  const bool q_fused = c.rope_fused && n_prefill > 0 && qkv_splits == 1;
+  PrefillQ qsrc{};
+  if (q_fused)
+    qsrc = PrefillQ{(const float*)L->qkv, L->Nqkv, L->a8w8 ? L->bqkv : nullptr, c.qk_norm ? L->qn : nullptr,
+                    c.rms_eps, L->rope};
   {
     StageTimer t(L, TDL_STAGE_ROPE_KV, st, sc.timed);
     HIP_TRY(rope_kv_write(qkv_splits > 1 ? (const void*)sc.gemm_ws : (const void*)L->qkv, rows, Hq, Hkv,
                           D, L->rope, c.qk_norm ? L->qn : nullptr, c.qk_norm ? L->kn : nullptr,
                           c.rms_eps, L->q, seq, pool, stage, st, qkv_splits,
-                          qkv_splits > 1 || L->a8w8 ? L->bqkv : nullptr));
+                          qkv_splits > 1 || L->a8w8 ? L->bqkv : nullptr, q_fused ? n_prefill : 0));
   }
   if (n_prefill) {
     StageTimer t(L, TDL_STAGE_ATTN_PREFILL, st, sc.timed);
-    HIP_TRY(attn_prefill(L->q, pool, seq, stage, n_prefill, max_q_len, Hq, Hkv, D, L->o, st));
+    HIP_TRY(attn_prefill(L->q, qsrc, pool, seq, stage, n_prefill, max_q_len, Hq, Hkv, D, L->o, st));
   }
   if (n_dec) {
     StageTimer t(L, TDL_STAGE_ATTN_DECODE, st, sc.timed);

@@ -192,7 +192,7 @@ __device__ __forceinline__ int prefill_v_index(int r, int d, int D) {
 hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, const float2* tab,
                          const float* q_norm, const float* k_norm, float eps, void* q_out,
                          SeqInfo seq, KvPool pool, PrefillStage stage, hipStream_t s, int splits = 1,
-                         const float* bias = nullptr);
+                         const float* bias = nullptr, int q_skip = 0);
 
 // Writes caller K/V rows into the pool (kv_cache_write).
 hipError_t kv_write_rows(const void* k, const void* v, int src_f32, int rows, int Hkv, int D,
@@ -263,8 +263,19 @@ __host__ __device__ inline size_t packed_offset(int n, int k, int N) {
 // before each chunk from the pool (bf16, u8 or u4) through the tables, the
 // chunk's own keys from `st` (sequences < st.n_seqs) or from the pool.  q
 // [rows][Hq][D] f32; o [rows][Hq*D] fp16 (saturating).
-hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, PrefillStage st, int n_prefill,
-                        int max_q_len, int Hq, int Hkv, int D, void* o, hipStream_t s);
+// Prefill queries taken straight from the QKV projection (rope_fused): the
+// attention kernel adds the bias (if not null), applies the Q-norm (gain not
+// null) and RoPE as it loads them.  qkv == null: q holds rotated queries.
+struct PrefillQ {
+  const float* qkv;  // [rows][ldq] fp32, the q heads first
+  int ldq;
+  const float* bias;  // [Hq * D] or null
+  const float* norm;  // [D] or null
+  float eps;
+  const float2* rope;  // [max_pos][D/2] (cos, sin)
+};
+hipError_t attn_prefill(const void* q, const PrefillQ& qsrc, KvPool pool, SeqInfo seq, PrefillStage st,
+                        int n_prefill, int max_q_len, int Hq, int Hkv, int D, void* o, hipStream_t s);
 
 // Paged decode attention for decode sequences first_seq .. first_seq+batch-1
 // (one query row each).  Each sequence's context is cut into partitions of

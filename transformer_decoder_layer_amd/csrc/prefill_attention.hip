@@ -76,7 +76,8 @@ __device__ __forceinline__ int p_qlen(const SeqInfo& s, int i) { return s.q_star
 __device__ __forceinline__ int p_ctx(const SeqInfo& s, int i) { return s.q_start ? s.ctx_len[i] : s.ctx0; }
 
 struct PrefillArgs {
-  const float* q;  // [rows][Hq][D] fp32, after RoPE
+  const float* q;  // [rows][Hq][D] fp32, after RoPE (unless qs.qkv)
+  PrefillQ qs;     // queries from the QKV projection, finished on load
   KvPool pool;
   SeqInfo seq;
   PrefillStage st;
@@ -168,7 +169,59 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
 
     // Q fragments (B operand of S^T = K Q^T): q[my_q][16s + 8G .. +7] * sc
     f16x8 qf[D / 16];
-    {
+    if (a.qs.qkv) {
+      // from the QKV projection: bias, Q-norm over the head (this lane holds
+      // half its channels, lane ^ 32 the other half) and RoPE, whose pairs
+      // (c, c + D/2) sit in steps s and s + D/32 of the same lane
+      const bool valid = my_q < q_len;
+      float xv[D / 16][8];
+      const float* src = a.qs.qkv + (size_t)(row0 + ql) * a.qs.ldq + (size_t)h * D + 8 * G;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        if (valid) {
+          const float4 x0 = *(const float4*)(src + 16 * s), x1 = *(const float4*)(src + 16 * s + 4);
+          xv[s][0] = x0.x; xv[s][1] = x0.y; xv[s][2] = x0.z; xv[s][3] = x0.w;
+          xv[s][4] = x1.x; xv[s][5] = x1.y; xv[s][6] = x1.z; xv[s][7] = x1.w;
+          if (a.qs.bias) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[s][e] += a.qs.bias[h * D + 16 * s + 8 * G + e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xv[s][e] = 0.f;
+        }
+      }
+      if (a.qs.norm) {
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += xv[s][e] * xv[s][e];
+        ss += __shfl_xor(ss, 32, 64);
+        const float inv = rsqrtf(ss / (float)D + a.qs.eps);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xv[s][e] = xv[s][e] * inv * a.qs.norm[16 * s + 8 * G + e];
+      }
+      const float2* cs = a.qs.rope + (size_t)(ctx + min(my_q, q_len - 1)) * (D / 2) + 8 * G;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 c = cs[16 * s + e];
+          const float x1 = xv[s][e], x2 = xv[s + D / 32][e];
+          xv[s][e] = x1 * c.x - x2 * c.y;
+          xv[s + D / 32][e] = x1 * c.y + x2 * c.x;
+        }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = f32_to_f16_sat(xv[s][e] * sc);
+        qf[s] = v;
+      }
+    } else {
       const bool valid = my_q < q_len;
       const float* qp = a.q + ((size_t)(row0 + ql) * a.Hq + h) * D + 8 * G;
 #pragma unroll
@@ -609,11 +662,12 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
 
 }  // namespace
 
-hipError_t attn_prefill(const void* q, KvPool pool, SeqInfo seq, PrefillStage st, int n_prefill,
-                        int max_q_len, int Hq, int Hkv, int D, void* o, hipStream_t s) {
+hipError_t attn_prefill(const void* q, const PrefillQ& qsrc, KvPool pool, SeqInfo seq, PrefillStage st,
+                        int n_prefill, int max_q_len, int Hq, int Hkv, int D, void* o, hipStream_t s) {
   if (n_prefill == 0 || max_q_len == 0) return hipSuccess;
   PrefillArgs a{};
   a.q = (const float*)q;
+  a.qs = qsrc;
   a.pool = pool;
   a.seq = seq;
   a.st = st;

@@ -166,7 +166,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
                                                       const float* __restrict__ kn, float eps,
                                                       float* __restrict__ q_out, SeqInfo seq,
                                                       KvPool pool, PrefillStage stage, int splits,
-                                                      const float* __restrict__ bias, int hpw, int mode) {
+                                                      const float* __restrict__ bias, int hpw, int mode,
+                                                      int q_skip) {
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = D >> 1;
@@ -253,6 +254,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
       }
       continue;
     }
+    if (is_q && sidx < q_skip) continue;  // rotated by prefill attention as it loads q
     float r1, r2;
     rotated(0, h, r1, r2);
     if (is_q) {  // wave-uniform
@@ -656,7 +658,7 @@ hipError_t rmsnorm_f32in(const float* x, const float* g, void* y, int rows, int 
 hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, const float2* tab,
                          const float* q_norm, const float* k_norm, float eps, void* q_out,
                          SeqInfo seq, KvPool pool, PrefillStage stage, hipStream_t s, int splits,
-                         const float* bias) {
+                         const float* bias, int q_skip) {
   if (rows == 0) return hipSuccess;
   // few rows (decode): four heads per workgroup for parallelism; many rows
   // (prefill): all heads of a row in one workgroup
@@ -664,12 +666,12 @@ hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, cons
   const dim3 grid(rows, cdiv(Hq + Hkv, hpw));
   if (pool.exps && pool.fmt != kKvBf16) {  // the blocks' exponents first
     rope_kv_kernel<<<grid, 256, 0, s>>>((const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps,
-                                        (float*)q_out, seq, pool, stage, splits, bias, hpw, 1);
+                                        (float*)q_out, seq, pool, stage, splits, bias, hpw, 1, q_skip);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   rope_kv_kernel<<<grid, 256, 0, s>>>((const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps,
-                                      (float*)q_out, seq, pool, stage, splits, bias, hpw, 0);
+                                      (float*)q_out, seq, pool, stage, splits, bias, hpw, 0, q_skip);
   return hipGetLastError();
 }
 
