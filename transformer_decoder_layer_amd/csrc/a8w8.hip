@@ -30,11 +30,72 @@ constexpr int kStep = 64;   // k per step (bytes per row and step)
 
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kStep + 16 * (c ^ ((r >> 2) & 3)); }
 
+// The epilogue of one wave's 64 x 64 quarter at (mw, nw): v = C a_scale[m]
+// b_scale[n] in fp32, then by e.epi: fp32 out (and the int32 sums to C);
+// + bias[n] (fp32 out); + bf16 residual (fp32 out); + fp32 residual (bf16
+// out); or SiLU(gate) * up, the gate and up columns interleaved in groups of
+// 16 (columns 32g .. 32g+15 gate, 32g+16 .. +31 up: fragments j and j + 1
+// of a lane pair them) into bf16 column 16g + c.
+template <typename Acc>
+__device__ __forceinline__ void a8w8_store(const Acc& acc, const A8Epi& e, const float* __restrict__ a_scale,
+                                           const float* __restrict__ b_scale, int32_t* __restrict__ C, int M,
+                                           int N, int mw, int nw, int lane) {
+  const int rq = 4 * (lane >> 4), cq = lane & 15;
+  if (e.epi == kA8SiluGate) {
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      const int ng = nw + 16 * j + cq, nu = ng + 16;
+      if (nu >= N) continue;
+      const float sg = b_scale[ng], su = b_scale[nu];
+      const int oc = (nw + 16 * j) / 2 + cq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mw + 16 * i + rq + r;
+          if (m >= M) continue;
+          const float sa = a_scale[m];
+          const float g = (float)acc[i][j][r] * sa * sg, u = (float)acc[i][j + 1][r] * sa * su;
+          ((bf16*)e.out)[(size_t)m * e.ldo + oc] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+        }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = nw + 16 * j + cq;
+    if (n >= N) continue;
+    const float sb = b_scale[n];
+    const float bias = e.epi == kA8Bias && e.bias ? e.bias[n] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mw + 16 * i + rq + r;
+        if (m >= M) continue;
+        const int32_t c = acc[i][j][r];
+        const float v = (float)c * a_scale[m] * sb;
+        const size_t o = (size_t)m * e.ldo + n;
+        switch (e.epi) {
+          case kA8ResidF32:
+            ((float*)e.out)[o] = v + (float)((const bf16*)e.resid)[(size_t)m * e.ldr + n];
+            break;
+          case kA8ResidBf16:
+            ((bf16*)e.out)[o] = f32_to_bf16(v + ((const float*)e.resid)[(size_t)m * e.ldr + n]);
+            break;
+          default:  // kA8Out, kA8Bias
+            if (C) C[(size_t)m * N + n] = c;
+            ((float*)e.out)[o] = v + bias;
+        }
+      }
+  }
+}
+
 __global__ __launch_bounds__(256) void a8w8_gemm_kernel(const int8_t* __restrict__ A,
                                                         const int8_t* __restrict__ B,
                                                         const float* __restrict__ a_scale,
                                                         const float* __restrict__ b_scale,
-                                                        int32_t* __restrict__ C, float* __restrict__ out,
+                                                        int32_t* __restrict__ C, A8Epi e,
                                                         int M, int N, int K) {
   __shared__ __attribute__((aligned(16))) int8_t As[2][kTile * kStep];
   __shared__ __attribute__((aligned(16))) int8_t Bs[2][kTile * kStep];
@@ -102,23 +163,7 @@ __global__ __launch_bounds__(256) void a8w8_gemm_kernel(const int8_t* __restrict
   }
 
   // acc[i][j][r] = C[row 16i + 4(lane/16) + r][col 16j + lane%16] of the wave's quarter
-  const int rq = 4 * (lane >> 4), cq = lane & 15;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 64 + 16 * j + cq;
-    if (n >= N) continue;
-    const float sb = b_scale[n];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 64 + 16 * i + rq + r;
-        if (m >= M) continue;
-        const int32_t c = acc[i][j][r];
-        if (C) C[(size_t)m * N + n] = c;
-        out[(size_t)m * N + n] = (float)c * a_scale[m] * sb;
-      }
-  }
+  a8w8_store(acc, e, a_scale, b_scale, C, M, N, m0 + wm * 64, n0 + wn * 64, lane);
 }
 
 // Direct-to-LDS variant (K % 64 == 0).  Each wave issues 2 copies of A
@@ -134,9 +179,8 @@ __global__ __launch_bounds__(512) void a8w8_gemm_direct_kernel(const int8_t* __r
                                                                const int8_t* __restrict__ B,
                                                                const float* __restrict__ a_scale,
                                                                const float* __restrict__ b_scale,
-                                                               int32_t* __restrict__ C,
-                                                               float* __restrict__ out, int M, int N,
-                                                               int K) {
+                                                               int32_t* __restrict__ C, A8Epi e, int M,
+                                                               int N, int K) {
   __shared__ __attribute__((aligned(16))) int8_t A0[kTileM * kStep];
   __shared__ __attribute__((aligned(16))) int8_t A1[kTileM * kStep];
   __shared__ __attribute__((aligned(16))) int8_t A2[kTileM * kStep];
@@ -208,41 +252,34 @@ __global__ __launch_bounds__(512) void a8w8_gemm_direct_kernel(const int8_t* __r
   }
   __builtin_amdgcn_s_waitcnt(vm_wait(0));  // the last (unused) copies land before the workgroup ends
 
-  const int rq = 4 * (lane >> 4), cq = lane & 15;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 64 + 16 * j + cq;
-    if (n >= N) continue;
-    const float sb = b_scale[n];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 64 + 16 * i + rq + r;
-        if (m >= M) continue;
-        const int32_t c = acc[i][j][r];
-        if (C) C[(size_t)m * N + n] = c;
-        out[(size_t)m * N + n] = (float)c * a_scale[m] * sb;
-      }
-  }
+  a8w8_store(acc, e, a_scale, b_scale, C, M, N, m0 + wm * 64, n0 + wn * 64, lane);
 }
 
 }  // namespace
 
-hipError_t a8w8_gemm(const void* A, const void* B, const float* a_scale, const float* b_scale,
-                     int32_t* C, float* out, int M, int N, int K, hipStream_t s) {
+hipError_t a8w8_gemm_epi(const void* A, const void* B, const float* a_scale, const float* b_scale,
+                         int32_t* C, const A8Epi& e, int M, int N, int K, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   if (M < 0 || N < 0 || K < 16 || K % 16 != 0) return hipErrorInvalidValue;
+  if (e.epi == kA8SiluGate && N % 32 != 0) return hipErrorInvalidValue;
   if (K % kStep == 0) {
     dim3 grid((N + kTile - 1) / kTile, (M + kTileM - 1) / kTileM);
-    a8w8_gemm_direct_kernel<<<grid, 512, 0, s>>>((const int8_t*)A, (const int8_t*)B, a_scale, b_scale, C, out,
+    a8w8_gemm_direct_kernel<<<grid, 512, 0, s>>>((const int8_t*)A, (const int8_t*)B, a_scale, b_scale, C, e,
                                                  M, N, K);
     return hipGetLastError();
   }
   dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
-  a8w8_gemm_kernel<<<grid, 256, 0, s>>>((const int8_t*)A, (const int8_t*)B, a_scale, b_scale, C, out, M, N,
-                                        K);
+  a8w8_gemm_kernel<<<grid, 256, 0, s>>>((const int8_t*)A, (const int8_t*)B, a_scale, b_scale, C, e, M, N, K);
   return hipGetLastError();
+}
+
+hipError_t a8w8_gemm(const void* A, const void* B, const float* a_scale, const float* b_scale,
+                     int32_t* C, float* out, int M, int N, int K, hipStream_t s) {
+  A8Epi e{};
+  e.epi = kA8Out;
+  e.out = out;
+  e.ldo = N;
+  return a8w8_gemm_epi(A, B, a_scale, b_scale, C, e, M, N, K, s);
 }
 
 }  // namespace tdl

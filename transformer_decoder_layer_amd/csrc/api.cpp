@@ -389,16 +389,22 @@ struct StageTimer {
 
 // A8W8 projection `mat` (0 QKV, 1 output, 2 gate/up, 3 down) over M rows:
 // the input rows A (fp16, or bf16 for the down projection) to int8 with a
-// scale per row, then the int8 GEMM, dequantised with both scales into out
-// (fp32 [M][N]).
-tdl_status a8w8_project(tdl_layer* L, const Scratch& sc, hipStream_t st, int mat, int M, int N, int K,
-                        const void* A, float* out) {
-  if (out == sc.gemm_ws && (size_t)M * N > sc.gemm_floats)
-    return fail(TDL_E_CAPACITY, "GEMM workspace too small for the int8 GEMM's result (M=%d N=%d)", M, N);
+// scale per row, then the int8 GEMM, dequantised with both scales and
+// finished by the projection's epilogue in the GEMM kernel (QKV + bias ->
+// qkv; + x -> h; SiLU(gate) * up -> a; + h -> y).
+tdl_status a8w8_project(tdl_layer* L, hipStream_t st, int mat, int M, int N, int K, const void* A,
+                        const void* resid, void* out) {
   HIP_TRY(quant_rows_i8(A, mat == 3, M, K, L->aq, L->as, st));
   const void* B = mat == 0 ? L->wqkv : mat == 1 ? L->wo : mat == 2 ? L->wgu : L->wd;
   const float* bs = mat == 0 ? L->wqkv_rs : mat == 1 ? L->wo_rs : mat == 2 ? L->wgu_rs : L->wd_rs;
-  HIP_TRY(a8w8_gemm(L->aq, B, L->as, bs, nullptr, out, M, N, K, st));
+  A8Epi e{};
+  e.epi = mat == 0 ? kA8Bias : mat == 1 ? kA8ResidF32 : mat == 2 ? kA8SiluGate : kA8ResidBf16;
+  e.bias = mat == 0 ? L->bqkv : nullptr;
+  e.resid = resid;
+  e.ldr = L->cfg.hidden;
+  e.out = out;
+  e.ldo = mat == 2 ? N / 2 : N;
+  HIP_TRY(a8w8_gemm_epi(L->aq, B, L->as, bs, nullptr, e, M, N, K, st));
   return TDL_OK;
 }
 
@@ -430,26 +436,25 @@ tdl_status run_layer(tdl_layer* L, const Scratch& sc, hipStream_t st, const void
   PrefillStage stage{L->stage_k, L->stage_v, L->stage_rows, std::min(n_prefill, kStagedSeqs)};
   {
     StageTimer t(L, TDL_STAGE_QKV, st, sc.timed);
-    if (L->a8w8)  // (its bias is added by the RoPE kernel)
-      TRY(a8w8_project(L, sc, st, 0, rows, L->Nqkv, H, L->xn, (float*)L->qkv));
+    if (L->a8w8)
+      TRY(a8w8_project(L, st, 0, rows, L->Nqkv, H, L->xn, nullptr, L->qkv));
     else
       TRY(run_gemm(L, sc, st, 0, rows, L->Nqkv, H, L->xn, L->wqkv, L->wqkv_s, L->wqkv_rs, L->wqkv_rz, L->wexp[0], EPI_BIAS_F32, L->bqkv, nullptr,
                    0, L->qkv, L->Nqkv, true, &qkv_splits));
   }
   // rope_fused: the prefill rows' queries go from the (whole, unsplit) QKV
-  // projection straight into the prefill attention kernel, which adds the
-  // bias still missing (A8W8), applies the Q-norm and RoPE as it loads them
+  // projection, bias included, straight into the prefill attention kernel,
+  // which applies the Q-norm and RoPE as it loads them
   const bool q_fused = c.rope_fused && n_prefill > 0 && qkv_splits == 1;
   PrefillQ qsrc{};
   if (q_fused)
-    qsrc = PrefillQ{(const float*)L->qkv, L->Nqkv, L->a8w8 ? L->bqkv : nullptr, c.qk_norm ? L->qn : nullptr,
-                    c.rms_eps, L->rope};
+    qsrc = PrefillQ{(const float*)L->qkv, L->Nqkv, nullptr, c.qk_norm ? L->qn : nullptr, c.rms_eps, L->rope};
   {
     StageTimer t(L, TDL_STAGE_ROPE_KV, st, sc.timed);
     HIP_TRY(rope_kv_write(qkv_splits > 1 ? (const void*)sc.gemm_ws : (const void*)L->qkv, rows, Hq, Hkv,
                           D, L->rope, c.qk_norm ? L->qn : nullptr, c.qk_norm ? L->kn : nullptr,
                           c.rms_eps, L->q, seq, pool, stage, st, qkv_splits,
-                          qkv_splits > 1 || L->a8w8 ? L->bqkv : nullptr, q_fused ? n_prefill : 0));
+                          qkv_splits > 1 ? L->bqkv : nullptr, q_fused ? n_prefill : 0));
   }
   if (n_prefill) {
     StageTimer t(L, TDL_STAGE_ATTN_PREFILL, st, sc.timed);
@@ -460,39 +465,21 @@ tdl_status run_layer(tdl_layer* L, const Scratch& sc, hipStream_t st, const void
     HIP_TRY(attn_decode(dp, L->q, pool, seq, dec_first, n_dec, Hq, Hkv, D, L->o, sc.dec_part, st));
   }
   if (L->a8w8) {
-    // each projection's fp32 result goes through the GEMM workspace as one
-    // slice of the split-K form, whose consumers add the residual (RMSNorm-2)
-    // or run the SiLU-gate / residual epilogue (the reduction kernel)
-    if (H > kFusedNormMaxH) return fail(TDL_E_UNSUPPORTED, "A8W8 layers need hidden <= %d", kFusedNormMaxH);
     {
       StageTimer t(L, TDL_STAGE_O_PROJ, st, sc.timed);
-      TRY(a8w8_project(L, sc, st, 1, rows, H, Hq * D, L->o, sc.gemm_ws));
+      TRY(a8w8_project(L, st, 1, rows, H, Hq * D, L->o, x, L->h));
     }
     {
       StageTimer t(L, TDL_STAGE_RMSNORM2, st, sc.timed);
-      HIP_TRY(rmsnorm_splits_resid(sc.gemm_ws, 1, x, L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
+      HIP_TRY(rmsnorm_f32in(L->h, L->ln2, L->hn, rows, H, c.rms_eps, st));
     }
-    GemmArgs ep{};
-    ep.ws = sc.gemm_ws;
-    ep.splits = 1;
-    ep.M = rows;
     {
       StageTimer t(L, TDL_STAGE_GATE_UP, st, sc.timed);
-      TRY(a8w8_project(L, sc, st, 2, rows, 2 * I, H, L->hn, sc.gemm_ws));
-      ep.N = 2 * I;
-      ep.C = L->a;
-      ep.ldc = I;
-      HIP_TRY(gemm_epilogue(ep, EPI_SILU_GATE, st));
+      TRY(a8w8_project(L, st, 2, rows, 2 * I, H, L->hn, nullptr, L->a));
     }
     {
       StageTimer t(L, TDL_STAGE_DOWN, st, sc.timed);
-      TRY(a8w8_project(L, sc, st, 3, rows, H, I, L->a, sc.gemm_ws));
-      ep.N = H;
-      ep.C = y;
-      ep.ldc = H;
-      ep.resid = L->h;
-      ep.ldr = H;
-      HIP_TRY(gemm_epilogue(ep, EPI_RESID_BF16, st));
+      TRY(a8w8_project(L, st, 3, rows, H, I, L->a, L->h, y));
     }
     return TDL_OK;
   }
@@ -824,9 +811,7 @@ extern "C" tdl_status layer_create(const tdl_layer_config* cfg, const tdl_layer_
   gemm_ws_need(c, L->Nqkv, q80 ? kWQ80 : iq8 ? kWIQ8 : kWDense, L->wexp[0] != nullptr,
                &L->gemm_ws_floats);
   if (a8w8) {
-    // the int8 GEMM's fp32 result of the widest projection, and the int8
-    // codes and scales of the widest input
-    L->gemm_ws_floats = std::max(L->gemm_ws_floats, (size_t)T * std::max({L->Nqkv, H, 2 * I}));
+    // the int8 codes and scales of the widest projection input
     CTRY(dalloc(L, &L->aq, (size_t)T * std::max({H, QD, I})));
     CTRY(dalloc(L, &L->as, (size_t)T * 4));
   }
@@ -972,7 +957,6 @@ extern "C" tdl_status layer_decode_paged_noalloc(tdl_layer* L, tdl_stream stream
       g = std::max(g, gemm_plan(batch, shapes[m][0], shapes[m][1], f, shapes[m][2],
                                 f != kWDense && L->packed[m]).ws_floats);
     }
-  if (L->a8w8) g = std::max(g, (size_t)batch * std::max({L->Nqkv, H, 2 * I}));
   const DecodePlan dp = decode_plan(batch, c.n_q_heads, c.n_kv_heads, c.head_dim, max_ctx_len,
                                     pool_of(L, kv).fmt);
   const size_t g_al = (g + 63) & ~size_t(63);  // partition results start 256-byte aligned

@@ -922,21 +922,6 @@ GemmPlan gemm_plan(int M, int N, int K, int wf, int epi, bool packed) {
   return best;
 }
 
-hipError_t gemm_epilogue(const GemmArgs& a, int epi, hipStream_t s) {
-  const int Nout = epi == EPI_SILU_GATE ? a.N / 2 : a.N;
-  if (a.M == 0 || Nout == 0) return hipSuccess;
-  if (a.splits < 1 || Nout % 4 || (epi == EPI_SILU_GATE && a.N % 32)) return hipErrorInvalidValue;
-  const int64_t threads = (int64_t)a.M * (Nout / 4);
-  const int blocks = (int)((threads + 255) / 256);
-  switch (epi) {
-    case EPI_BIAS_F32: splitk_reduce_kernel<EPI_BIAS_F32><<<blocks, 256, 0, s>>>(a); break;
-    case EPI_RESID_F32: splitk_reduce_kernel<EPI_RESID_F32><<<blocks, 256, 0, s>>>(a); break;
-    case EPI_RESID_BF16: splitk_reduce_kernel<EPI_RESID_BF16><<<blocks, 256, 0, s>>>(a); break;
-    default: splitk_reduce_kernel<EPI_SILU_GATE><<<blocks, 256, 0, s>>>(a); break;
-  }
-  return hipGetLastError();
-}
-
 hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, int wf, int epi, hipStream_t s, bool reduce) {
   a.splits = pl.splits;
   a.k_tiles_per_split = pl.k_tiles_per_split;

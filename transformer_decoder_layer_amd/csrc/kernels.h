@@ -232,6 +232,22 @@ hipError_t q80_from_gguf(const void* blocks, int64_t n_blocks, void* codes, void
 // dst [N][K] fp16 (saturating) or bf16: (code - zp) * scale rounded once.
 hipError_t expand_iq8(const void* codes, const float* scale, const float* zp, int N, int K, void* dst,
                       int dst_f16, hipStream_t s);
+// Epilogues of the int8 x int8 GEMM (v = C a_scale[m] b_scale[n]):
+// kA8Out: fp32 out = v (and the int32 sums to C if not null); kA8Bias:
+// fp32 out = v + bias[n]; kA8ResidF32: fp32 out = v + bf16 resid[m][n];
+// kA8ResidBf16: bf16 out = v + fp32 resid[m][n]; kA8SiluGate: bf16
+// out[m][16g + c] = silu(v[m][32g + c]) * v[m][32g + 16 + c] (N % 32 == 0).
+enum A8EpiKind : int { kA8Out = 0, kA8Bias = 1, kA8ResidF32 = 2, kA8ResidBf16 = 3, kA8SiluGate = 4 };
+struct A8Epi {
+  int epi;
+  const float* bias;
+  const void* resid;
+  int ldr;
+  void* out;
+  int ldo;
+};
+hipError_t a8w8_gemm_epi(const void* A, const void* B, const float* a_scale, const float* b_scale,
+                         int32_t* C, const A8Epi& e, int M, int N, int K, hipStream_t s);
 // int8 x int8 GEMM: C = A[M,K] B[N,K]^T in int32 (written if C != null),
 // out = C * a_scale[m] * b_scale[n] in fp32.  K % 16 == 0.
 hipError_t a8w8_gemm(const void* A, const void* B, const float* a_scale, const float* b_scale,
@@ -240,10 +256,6 @@ hipError_t a8w8_gemm(const void* A, const void* B, const float* a_scale, const f
 // [rows][K]: s[r] = max|x| / 127 (1 for a zero row), q = rint(x / s)
 // clipped to +-127.  K % 16 == 0.
 hipError_t quant_rows_i8(const void* x, int x_bf16, int rows, int K, int8_t* q, float* s, hipStream_t st);
-// The epilogue of a GEMM whose fp32 result sits in a.ws as a.splits slices
-// [splits][M][N]: the slices summed in order, then bias / residual /
-// SiLU-gate into a.C (the split-K reduction kernel).
-hipError_t gemm_epilogue(const GemmArgs& a, int epi, hipStream_t s);
 // int8 [n] -> float [n]
 hipError_t i8_to_f32(const void* src, float* dst, int64_t n, hipStream_t s);
 hipError_t pack_weights(const void* src, void* dst, int N, int K, hipStream_t s);
