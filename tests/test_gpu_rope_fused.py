@@ -5,7 +5,9 @@ while Q is loaded).  Against the oracle, stage by stage (the attention
 output checks the fused query path): bf16 prefill with a QKV bias (no cache,
 paged, a chunk after cached tokens), a Qwen3-shaped prefill and mixed step
 (Q-norm; the decode rows keep the RoPE kernel's q), a u8 cache, Q8_0 and
-A8W8 layers."""
+A8W8 layers, and mid-sized layers whose QKV projection is split along K
+(their prefill queries take the RoPE kernel's path, which sums the slices in
+order and adds the bias)."""
 import dataclasses
 
 import pytest
@@ -55,3 +57,21 @@ def test_fused_q80_and_a8w8():
     wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=TINY_A8, kv_dtype="bf16")
     inp = synth.make_inputs(wl, seed=143, prefill_len=150, spare_blocks=1, random_gains=True)
     check_layer(inp, what="fused a8w8 prefill 150", rope_fused=True)
+
+
+# hidden 1024 (8 / 2 heads, QKV bias) and 2048 (16 / 4 heads, Q/K-norm): at
+# 150 and 300 rows their QKV projections run as 4, 4 and 5 split-K slices
+MID_Q25 = dataclasses.replace(synth.QWEN25_7B, name="mid-qwen2.5", hidden=1024, n_q_heads=8,
+                              n_kv_heads=2, intermediate=2816)
+MID_Q3 = dataclasses.replace(synth.QWEN3_8B, name="mid-qwen3", hidden=2048, n_q_heads=16,
+                             n_kv_heads=4, intermediate=5632)
+
+
+@pytest.mark.parametrize("shape,T", [(MID_Q25, 150), (MID_Q25, 300), (MID_Q3, 150)])
+def test_fused_split_qkv(shape, T):
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=shape, kv_dtype="bf16")
+    inp = synth.make_inputs(wl, seed=150 + T, prefill_len=T, prefill_start=20, spare_blocks=1,
+                            random_gains=True)
+    layer, kv, t, cache, rows = check_layer(inp, what=f"fused {shape.name} split QKV, chunk {T} at 20",
+                                            rope_fused=True)
+    check_cache_rows(inp, kv, cache, [0])

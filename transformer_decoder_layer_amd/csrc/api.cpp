@@ -444,7 +444,10 @@ tdl_status run_layer(tdl_layer* L, const Scratch& sc, hipStream_t st, const void
   }
   // rope_fused: the prefill rows' queries go from the (whole, unsplit) QKV
   // projection, bias included, straight into the prefill attention kernel,
-  // which applies the Q-norm and RoPE as it loads them
+  // which applies the Q-norm and RoPE as it loads them.  A projection split
+  // along K keeps the RoPE kernel's q: summing the slices in the attention
+  // kernel's prologue cost it more than the RoPE kernel saved (512 tokens:
+  // attention +9 us, RoPE -7 us).
   const bool q_fused = c.rope_fused && n_prefill > 0 && qkv_splits == 1;
   PrefillQ qsrc{};
   if (q_fused)

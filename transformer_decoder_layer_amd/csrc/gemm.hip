@@ -653,7 +653,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
 
 // Sum of the split-K slices in slice order, then the epilogue; one thread per
 // 4 consecutive output columns (per gate/up pair for the SiLU-gate form).
-template <int EPI>
+// The slices are read SB at a time, every load of a batch issued before the
+// first add (slice indices past the last repeat it and add nothing).
+template <int EPI, int SB>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   const int Nout = EPI == EPI_SILU_GATE ? p.N / 2 : p.N;
   const int cols4 = Nout / 4;
@@ -666,19 +668,21 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
     // output column j -> gate column 32*(j/16) + j%16, up column +16
     const int ng = 32 * (c / 16) + (c % 16);
     float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < p.splits; s0 += 4) {  // four slices of independent loads per batch
-      float4 a[4], b[4];
+    for (int s0 = 0; s0 < p.splits; s0 += SB) {
+      float4 a[SB], b[SB];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < SB; ++q) {
         const float* src = p.ws + min(s0 + q, p.splits - 1) * slice + (size_t)m * p.N + ng;
         a[q] = *(const float4*)src;
         b[q] = *(const float4*)(src + 16);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (s0 + q >= p.splits) break;
-        g[0] += a[q].x; g[1] += a[q].y; g[2] += a[q].z; g[3] += a[q].w;
-        u[0] += b[q].x; u[1] += b[q].y; u[2] += b[q].z; u[3] += b[q].w;
+      for (int q = 0; q < SB; ++q) {  // a select, not a branch: the loads stay unconditional
+        const bool live = s0 + q < p.splits;
+        g[0] += live ? a[q].x : 0.f; g[1] += live ? a[q].y : 0.f;
+        g[2] += live ? a[q].z : 0.f; g[3] += live ? a[q].w : 0.f;
+        u[0] += live ? b[q].x : 0.f; u[1] += live ? b[q].y : 0.f;
+        u[2] += live ? b[q].z : 0.f; u[3] += live ? b[q].w : 0.f;
       }
     }
 #pragma unroll
@@ -688,14 +692,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
     for (int e = 0; e < 4; ++e) C[e] = f32_to_bf16(out[e]);
   } else {
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < p.splits; s0 += 4) {  // four slices of independent loads per batch
-      float4 a[4];
+    for (int s0 = 0; s0 < p.splits; s0 += SB) {
+      float4 a[SB];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) a[q] = *(const float4*)(p.ws + min(s0 + q, p.splits - 1) * slice + (size_t)m * p.N + c);
+      for (int q = 0; q < SB; ++q) a[q] = *(const float4*)(p.ws + min(s0 + q, p.splits - 1) * slice + (size_t)m * p.N + c);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (s0 + q >= p.splits) break;
-        v[0] += a[q].x; v[1] += a[q].y; v[2] += a[q].z; v[3] += a[q].w;
+      for (int q = 0; q < SB; ++q) {  // a select, not a branch: the loads stay unconditional
+        const bool live = s0 + q < p.splits;
+        v[0] += live ? a[q].x : 0.f; v[1] += live ? a[q].y : 0.f;
+        v[2] += live ? a[q].z : 0.f; v[3] += live ? a[q].w : 0.f;
       }
     }
     // the residual is never the output: its loads all issue before the stores
@@ -842,6 +847,17 @@ hipError_t tail_reduce(const GemmPlan& pl, const GemmArgs& a, int epi, hipStream
   return hipErrorInvalidValue;
 }
 
+template <int SB>
+hipError_t splitk_reduce(const GemmArgs& a, int epi, int blocks, hipStream_t s) {
+  switch (epi) {
+    case EPI_BIAS_F32: splitk_reduce_kernel<EPI_BIAS_F32, SB><<<blocks, 256, 0, s>>>(a); break;
+    case EPI_RESID_F32: splitk_reduce_kernel<EPI_RESID_F32, SB><<<blocks, 256, 0, s>>>(a); break;
+    case EPI_RESID_BF16: splitk_reduce_kernel<EPI_RESID_BF16, SB><<<blocks, 256, 0, s>>>(a); break;
+    default: splitk_reduce_kernel<EPI_SILU_GATE, SB><<<blocks, 256, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Chooses the tile configuration and split-K factor with the lowest estimated
@@ -941,13 +957,9 @@ hipError_t gemm_launch(const GemmPlan& pl, GemmArgs a, int wf, int epi, hipStrea
   const int Nout = epi == EPI_SILU_GATE ? a.N / 2 : a.N;
   const int64_t threads = (int64_t)a.M * (Nout / 4);
   const int blocks = (int)((threads + 255) / 256);
-  switch (epi) {
-    case EPI_BIAS_F32: splitk_reduce_kernel<EPI_BIAS_F32><<<blocks, 256, 0, s>>>(a); break;
-    case EPI_RESID_F32: splitk_reduce_kernel<EPI_RESID_F32><<<blocks, 256, 0, s>>>(a); break;
-    case EPI_RESID_BF16: splitk_reduce_kernel<EPI_RESID_BF16><<<blocks, 256, 0, s>>>(a); break;
-    default: splitk_reduce_kernel<EPI_SILU_GATE><<<blocks, 256, 0, s>>>(a); break;
-  }
-  return hipGetLastError();
+  if (a.splits <= 4) return splitk_reduce<4>(a, epi, blocks, s);
+  if (a.splits <= 8) return splitk_reduce<8>(a, epi, blocks, s);
+  return splitk_reduce<16>(a, epi, blocks, s);
 }
 
 }  // namespace tdl

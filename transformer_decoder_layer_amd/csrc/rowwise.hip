@@ -10,9 +10,10 @@ namespace {
 
 // ------------------------------------------------------------- RMSNorm
 // One workgroup per row (the "one block per row" layout of the RMSNorm kernel
-// on the Qwen2.5-7B single-layer page, section 2): fp32 sum of squares over
-// 16-byte vector loads, reduced within each wave by lane shuffles and across
-// the four waves through LDS; y = x * rsqrt(sum/H + eps) * g.
+// on the Qwen2.5-7B single-layer page, section 2), one thread per CH chunks of
+// 8 columns: the row is read once with 16-byte vector loads and kept in
+// registers; fp32 sum of squares reduced within each wave by lane shuffles
+// and across the waves through LDS; y = x * rsqrt(sum/H + eps) * g.
 
 __device__ __forceinline__ void load8(const bf16* p, float* v) {
   const bf16x8 t = *(const bf16x8*)p;
@@ -25,34 +26,61 @@ __device__ __forceinline__ void load8(const float* p, float* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-template <typename TIn>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const TIn* __restrict__ x,
-                                                      const float* __restrict__ g,
-                                                      f16* __restrict__ y, int H, float eps) {
-  __shared__ float red[4];
-  const int row = blockIdx.x;
+// Sum over the workgroup (at most 16 waves) of one value per thread.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  return t;
+}
+
+// Threads (a multiple of 64, at most 1024) and chunks of 8 per thread for a
+// row of H columns (H % 64 == 0); false if H is too long.
+bool row_shape(int H, int* threads, int* ch) {
+  const int chunks = H / 8;
+  for (int c = 1; c <= 4; c *= 2) {
+    const int t = (cdiv(chunks, c) + 63) / 64 * 64;
+    if (t <= 1024) {
+      *threads = t;
+      *ch = c;
+      return true;
+    }
+  }
+  return false;
+}
+
+template <typename TIn, int CH>
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(const TIn* __restrict__ x,
+                                                       const float* __restrict__ g,
+                                                       f16* __restrict__ y, int H, float eps) {
+  __shared__ float red[16];
+  const int row = blockIdx.x, nt = blockDim.x;
   const TIn* xr = x + (size_t)row * H;
   f16* yr = y + (size_t)row * H;
+  float v[CH][8], gg[CH][8];
   float ss = 0.f;
-  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-    float v[8];
-    load8(xr + c, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+  for (int j = 0; j < CH; ++j) {
+    const int c = (threadIdx.x + nt * j) * 8;
+    const bool ok = c < H;
+    load8(xr + (ok ? c : 0), v[j]);
+    load8(g + (ok ? c : 0), gg[j]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[j][e] = ok ? v[j][e] : 0.f;
+      ss += v[j][e] * v[j][e];
+    }
   }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
-  const float inv = rsqrtf(tot / (float)H + eps);
-  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-    float v[8];
-    load8(xr + c, v);
-    const float4 g0 = *(const float4*)(g + c), g1 = *(const float4*)(g + c + 4);
-    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  const float inv = rsqrtf(block_sum(ss, red) / (float)H + eps);
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = (threadIdx.x + nt * j) * 8;
+    if (c >= H) break;
     f16x8 o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = f32_to_f16_sat(v[e] * inv * gg[e]);
+    for (int e = 0; e < 8; ++e) o[e] = f32_to_f16_sat(v[j][e] * inv * gg[j][e]);
     *(f16x8*)(yr + c) = o;
   }
 }
@@ -160,6 +188,9 @@ __device__ __forceinline__ int u4_vbyte(int slot, int d) { return (d >> 1) * kBl
 // clamped, per KV head, K and V separately); every other row does nothing.
 // mode 0: every row quantises with its block's exponents (set by this call's
 // mode-1 launch, or by the call that wrote the block's first slot).
+// SB: split-K slices read per batch of loads (1, 4 or 8 by the slice count;
+// a larger batch costs registers and occupancy).
+template <int SB>
 __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ qkv, int Hq, int Hkv,
                                                       int D, const float2* __restrict__ tab,
                                                       const float* __restrict__ qn,
@@ -183,29 +214,39 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     if (slot != 0) return;
     n_blk_rows = min(kBlockTokens, min(seq_end_row(seq, sidx, row), (int)gridDim.x) - row);
   }
-  // element c of row row+i's projection: the partial slices in order (+
-  // bias).  Four slices per batch of independent loads (slice indices past
-  // the last repeat it and add nothing): a load per round trip otherwise.
-  auto val = [&](int i, int c) {
+  // elements c[0..NC) of row row+i's projection: the partial slices in order
+  // (+ bias), read SB slices at a time with every load of a batch issued
+  // before the first add (slice indices past the last repeat it and add
+  // nothing)
+  auto vals = [&](int i, auto& c, auto& out) {
+    constexpr int NC = sizeof(out) / sizeof(float);
     const float* src = qkv + (size_t)(row + i) * ldq;
-    if (splits == 1) return bias ? src[c] + bias[c] : src[c];
-    float v = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += 4) {
-      float t[4];
+    for (int s0 = 0; s0 < splits; s0 += SB) {
+      float t[SB][NC];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) t[u] = src[(size_t)min(s0 + u, splits - 1) * slice + c];
+      for (int u = 0; u < SB; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v += s0 + u < splits ? t[u] : 0.f;
+        for (int k = 0; k < NC; ++k) t[u][k] = src[(size_t)min(s0 + u, splits - 1) * slice + c[k]];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {  // a select, not a branch: the loads stay unconditional
+        const bool live = s0 + u < splits;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) out[k] = s0 + u == 0 ? t[u][k] : out[k] + (live ? t[u][k] : 0.f);
+      }
     }
-    return bias ? v + bias[c] : v;
+    if (bias) {
+#pragma unroll
+      for (int k = 0; k < NC; ++k) out[k] += bias[c[k]];
+    }
   };
   const bool act = lane < half;
   const int ln = act ? lane : 0;  // lanes past D/2 load a valid element and store nothing
   // head h of row row+i, normalised (Q/K) and rotated: channels ln, ln + D/2
-  auto rotated = [&](int i, int h, float& r1, float& r2) {
+  // (x holds their projections)
+  auto rotate = [&](int i, int h, float x1, float x2, float& r1, float& r2) {
     const bool is_q = h < Hq;
-    const int hc = h * D;  // q heads then k heads are contiguous
-    float x1 = val(i, hc + ln), x2 = val(i, hc + ln + half);
+    float2 cs = make_float2(1.f, 0.f);
+    if (act) cs = tab[(size_t)(pos + i) * half + lane];
     if (!act) x1 = x2 = 0.f;
     const float* gn = is_q ? qn : kn;
     if (gn) {  // per-head RMSNorm over D
@@ -216,8 +257,6 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
         x2 = x2 * inv * gn[lane + half];
       }
     }
-    float2 cs = make_float2(1.f, 0.f);
-    if (act) cs = tab[(size_t)(pos + i) * half + lane];
     r1 = x1 * cs.x - x2 * cs.y;
     r2 = x1 * cs.y + x2 * cs.x;
   };
@@ -236,9 +275,12 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
       const int c1 = g * D + ln, c2 = c1 + half;
       int ek = 0, ev = 0;
       for (int i = 0; i < n_blk_rows; ++i) {
+        const int cols[4] = {h * D + ln, h * D + ln + half, vc + ln, vc + ln + half};
+        float x[4];
+        vals(i, cols, x);
         float r1, r2;
-        rotated(i, h, r1, r2);
-        const float v1 = val(i, vc + ln), v2 = val(i, vc + ln + half);
+        rotate(i, h, x[0], x[1], r1, r2);
+        const float v1 = x[2], v2 = x[3];
         if (act) {
           ek = max(ek, max(exp_needed(r1, pool.k_scale[c1], pool.k_zp[c1], top),
                            exp_needed(r2, pool.k_scale[c2], pool.k_zp[c2], top)));
@@ -256,8 +298,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     }
     if (is_q && sidx < q_skip) continue;  // rotated by prefill attention as it loads q
     float r1, r2;
-    rotated(0, h, r1, r2);
     if (is_q) {  // wave-uniform
+      const int cols[2] = {h * D + ln, h * D + ln + half};
+      float x[2];
+      vals(0, cols, x);
+      rotate(0, h, x[0], x[1], r1, r2);
       if (act) {
         float* qo = q_out + ((size_t)row * Hq + h) * D;
         qo[lane] = r1;
@@ -267,7 +312,11 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     }
     const int g = h - Hq;
     const int vc = (Hq + Hkv + g) * D;
-    const float v1 = val(0, vc + ln), v2 = val(0, vc + ln + half);
+    const int cols[4] = {h * D + ln, h * D + ln + half, vc + ln, vc + ln + half};
+    float x[4];
+    vals(0, cols, x);
+    rotate(0, h, x[0], x[1], r1, r2);
+    const float v1 = x[2], v2 = x[3];
     const int ek = pool_exp(pool, blk, g, Hkv, 0), ev = pool_exp(pool, blk, g, Hkv, 1);
     if (staged && act) {
       // fp16 copy of what the cache holds (bf16-rounded, or the dequantised
@@ -323,70 +372,57 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
   }
 }
 
-// h = sum of the split slices (in order) + residual, kept in registers (up to
-// 256 * 8 * kSplitRowChunks columns), written once; then y = RMSNorm(h) * g.
-constexpr int kSplitRowChunks = 4;
-__global__ __launch_bounds__(256) void rmsnorm_splits_kernel(const float* __restrict__ ws, int splits,
-                                                             const bf16* __restrict__ resid,
-                                                             float* __restrict__ h,
-                                                             const float* __restrict__ g,
-                                                             f16* __restrict__ y, int H, float eps) {
-  __shared__ float red[4];
+// h = sum of the split slices (in order) + residual, one chunk of 8 columns
+// per thread (H <= 8192), written once; then y = RMSNorm(h) * g.  The slices
+// are read SB at a time, every load of a batch issued before the first add.
+constexpr int kSplitNormMaxH = 8192;
+template <int SB>
+__global__ __launch_bounds__(1024) void rmsnorm_splits_kernel(const float* __restrict__ ws, int splits,
+                                                              const bf16* __restrict__ resid,
+                                                              float* __restrict__ h,
+                                                              const float* __restrict__ g,
+                                                              f16* __restrict__ y, int H, float eps) {
+  __shared__ float red[16];
   const int row = blockIdx.x;
   const size_t slice = (size_t)gridDim.x * H;
-  // first pass: loads only (slices four at a time, chunks past H clamped to
-  // a valid address and zeroed), so that they all pipeline; second pass:
-  // the stores of h and y
-  float v[kSplitRowChunks][8], gg[kSplitRowChunks][8];
-  float ss = 0.f;
+  const int c = threadIdx.x * 8;
+  const bool ok = c < H;
+  const size_t o = (size_t)row * H + (ok ? c : 0);
+  const bf16x8 r = *(const bf16x8*)(resid + o);
+  float gg[8];
+  load8(g + (ok ? c : 0), gg);
+  float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += SB) {
+    float4 a[SB], b[SB];
 #pragma unroll
-  for (int j = 0; j < kSplitRowChunks; ++j) {
-    if (256 * 8 * j >= H) break;  // uniform: chunks wholly past the row
-    const int c = (threadIdx.x + 256 * j) * 8;
-    const bool ok = c < H;
-    const size_t o = (size_t)row * H + (ok ? c : 0);
-    const bf16x8 r = *(const bf16x8*)(resid + o);
-    const float4 g0 = *(const float4*)(g + (ok ? c : 0)), g1 = *(const float4*)(g + (ok ? c : 0) + 4);
-    gg[j][0] = g0.x; gg[j][1] = g0.y; gg[j][2] = g0.z; gg[j][3] = g0.w;
-    gg[j][4] = g1.x; gg[j][5] = g1.y; gg[j][6] = g1.z; gg[j][7] = g1.w;
-    float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < splits; s0 += 4) {
-      float4 a[4], b[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float* src = ws + (size_t)min(s0 + u, splits - 1) * slice + o;
-        a[u] = *(const float4*)src;
-        b[u] = *(const float4*)(src + 4);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (s0 + u >= splits) break;
-        p[0] += a[u].x; p[1] += a[u].y; p[2] += a[u].z; p[3] += a[u].w;
-        p[4] += b[u].x; p[5] += b[u].y; p[6] += b[u].z; p[7] += b[u].w;
-      }
+    for (int u = 0; u < SB; ++u) {  // slices past the last repeat it and add nothing
+      const float* src = ws + (size_t)min(s0 + u, splits - 1) * slice + o;
+      a[u] = *(const float4*)src;
+      b[u] = *(const float4*)(src + 4);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[j][e] = ok ? p[e] + (float)r[e] : 0.f;
-      ss += v[j][e] * v[j][e];
+    for (int u = 0; u < SB; ++u) {  // a select, not a branch: the loads stay unconditional
+      const bool live = s0 + u < splits;
+      p[0] += live ? a[u].x : 0.f; p[1] += live ? a[u].y : 0.f;
+      p[2] += live ? a[u].z : 0.f; p[3] += live ? a[u].w : 0.f;
+      p[4] += live ? b[u].x : 0.f; p[5] += live ? b[u].y : 0.f;
+      p[6] += live ? b[u].z : 0.f; p[7] += live ? b[u].w : 0.f;
     }
   }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  float v[8], ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kSplitRowChunks; ++j) {
-    const int c = (threadIdx.x + 256 * j) * 8;
-    if (c >= H) break;
-    const size_t o = (size_t)row * H + c;
-    *(float4*)(h + o) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
-    *(float4*)(h + o + 4) = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
-    f16x8 o8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o8[e] = f32_to_f16_sat(v[j][e] * inv * gg[j][e]);
-    *(f16x8*)(y + o) = o8;
+  for (int e = 0; e < 8; ++e) {
+    v[e] = ok ? p[e] + (float)r[e] : 0.f;
+    ss += v[e] * v[e];
   }
+  const float inv = rsqrtf(block_sum(ss, red) / (float)H + eps);
+  if (!ok) return;
+  *(float4*)(h + o) = make_float4(v[0], v[1], v[2], v[3]);
+  *(float4*)(h + o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  f16x8 o8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o8[e] = f32_to_f16_sat(v[e] * inv * gg[e]);
+  *(f16x8*)(y + o) = o8;
 }
 
 // ---------------------------------------------------- cache writes
@@ -637,22 +673,36 @@ __global__ void rope_table_kernel(float2* tab, int max_pos, int D, double theta)
 hipError_t rmsnorm_splits_resid(const float* ws, int splits, const void* resid, float* h,
                                 const float* g, void* y, int rows, int H, float eps, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (H % 8 != 0 || H > 256 * 8 * kSplitRowChunks) return hipErrorInvalidValue;
-  rmsnorm_splits_kernel<<<rows, 256, 0, s>>>(ws, splits, (const bf16*)resid, h, g, (f16*)y, H, eps);
+  if (H % 64 != 0 || H > kSplitNormMaxH || splits < 1) return hipErrorInvalidValue;
+  const int nt = (H / 8 + 63) / 64 * 64;
+  if (splits <= 4)
+    rmsnorm_splits_kernel<4><<<rows, nt, 0, s>>>(ws, splits, (const bf16*)resid, h, g, (f16*)y, H, eps);
+  else
+    rmsnorm_splits_kernel<8><<<rows, nt, 0, s>>>(ws, splits, (const bf16*)resid, h, g, (f16*)y, H, eps);
+  return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t rmsnorm_launch(const TIn* x, const float* g, void* y, int rows, int H, float eps,
+                          hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  int nt, ch;
+  if (H % 64 != 0 || !row_shape(H, &nt, &ch)) return hipErrorInvalidValue;
+  switch (ch) {
+    case 1: rmsnorm_kernel<TIn, 1><<<rows, nt, 0, s>>>(x, g, (f16*)y, H, eps); break;
+    case 2: rmsnorm_kernel<TIn, 2><<<rows, nt, 0, s>>>(x, g, (f16*)y, H, eps); break;
+    default: rmsnorm_kernel<TIn, 4><<<rows, nt, 0, s>>>(x, g, (f16*)y, H, eps); break;
+  }
   return hipGetLastError();
 }
 
 hipError_t rmsnorm_bf16in(const void* x, const float* g, void* y, int rows, int H, float eps,
                           hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  rmsnorm_kernel<bf16><<<rows, 256, 0, s>>>((const bf16*)x, g, (f16*)y, H, eps);
-  return hipGetLastError();
+  return rmsnorm_launch((const bf16*)x, g, y, rows, H, eps, s);
 }
 hipError_t rmsnorm_f32in(const float* x, const float* g, void* y, int rows, int H, float eps,
                          hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  rmsnorm_kernel<float><<<rows, 256, 0, s>>>(x, g, (f16*)y, H, eps);
-  return hipGetLastError();
+  return rmsnorm_launch(x, g, y, rows, H, eps, s);
 }
 
 hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, const float2* tab,
@@ -664,15 +714,22 @@ hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, cons
   // (prefill): all heads of a row in one workgroup
   const int hpw = rows >= 1024 ? Hq + Hkv : 4;
   const dim3 grid(rows, cdiv(Hq + Hkv, hpw));
+  if (splits < 1) return hipErrorInvalidValue;
+  auto launch = [&](int mode) {
+#define TDL_ROPE_KV(SB)                                                                           \
+  rope_kv_kernel<SB><<<grid, 256, 0, s>>>((const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps, \
+                                          (float*)q_out, seq, pool, stage, splits, bias, hpw, mode, q_skip)
+    if (splits == 1) TDL_ROPE_KV(1);
+    else if (splits <= 4) TDL_ROPE_KV(4);
+    else TDL_ROPE_KV(8);
+#undef TDL_ROPE_KV
+    return hipGetLastError();
+  };
   if (pool.exps && pool.fmt != kKvBf16) {  // the blocks' exponents first
-    rope_kv_kernel<<<grid, 256, 0, s>>>((const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps,
-                                        (float*)q_out, seq, pool, stage, splits, bias, hpw, 1, q_skip);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch(1);
     if (e != hipSuccess) return e;
   }
-  rope_kv_kernel<<<grid, 256, 0, s>>>((const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps,
-                                      (float*)q_out, seq, pool, stage, splits, bias, hpw, 0, q_skip);
-  return hipGetLastError();
+  return launch(0);
 }
 
 hipError_t kv_write_rows(const void* k, const void* v, int src_f32, int rows, int Hkv, int D,
