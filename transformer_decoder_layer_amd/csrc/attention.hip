@@ -153,10 +153,12 @@ struct DecStage {
   }
 };
 constexpr int kDecStages = 3;  // blocks per wave in rotation (one read, two in flight)
-template <int D, int F>
+// Each of the three stage arrays holds one stage of every wave; after the
+// loop the first two hold the waves' O^T tiles (half the waves each).
+template <int D, int F, int NW>
 constexpr int dec_stage_array_bytes() {
-  constexpr int o = 2 * D * 16 * 4;  // two waves' O^T tiles
-  constexpr int st = 4 * DecStage<D, F>::kBytes;
+  constexpr int o = NW / 2 * D * 16 * 4;
+  constexpr int st = NW * DecStage<D, F>::kBytes;
   return o > st ? o : st;
 }
 
@@ -213,23 +215,24 @@ __device__ __forceinline__ f16x4 u4x4_to_f16_biased(uint32_t w, int n) {
   return __builtin_bit_cast(f16x4, r);
 }
 
-template <int D, int F>
-__global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
+template <int D, int F, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(DecArgs a) {
   constexpr bool Q = F != kKvBf16;  // codes with per-channel scale / zero point
   constexpr bool U4 = F == kKvU4;
   constexpr float kBias = U4 ? kU4Bias : kU8Bias;
   constexpr int NT = D / 16;  // 16-channel tiles of the output
-  __shared__ float sm_m[4][16], sm_l[4][16], sm_lv[4][16];
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  __shared__ float sm_m[NW][16], sm_l[NW][16], sm_lv[NW][16];
   // Stage j of every wave's block rotation lives in its own array, so
   // the compiler can tell a wave's reads of one stage from the copies still
   // landing in the others (one array would make every read wait for all
-  // copies).  After the loop st0 / st1 hold the four waves' accumulators.
-  constexpr int SZ = dec_stage_array_bytes<D, F>();
+  // copies).  After the loop st0 / st1 hold the waves' accumulators.
+  constexpr int SZ = dec_stage_array_bytes<D, F, NW>();
   __shared__ __attribute__((aligned(16))) uint8_t st0[SZ];
   __shared__ __attribute__((aligned(16))) uint8_t st1[SZ];
   __shared__ __attribute__((aligned(16))) uint8_t st2[SZ];
   // wave w's O^T tile [D][16] floats, columns XOR-swizzled by row
-  auto o_tile = [&](int w) { return (float*)(w < 2 ? st0 : st1) + (w & 1) * D * 16; };
+  auto o_tile = [&](int w) { return (float*)(w < NW / 2 ? st0 : st1) + (w % (NW / 2)) * D * 16; };
   auto o_idx = [](int d, int hh) { return d * 16 + (hh ^ (d & 15)); };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -335,19 +338,19 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   // point, P entering the V product scaled by its block's factor)
   float lv_run = 0.f;
 
-  // this wave's blocks: blk0 + wave + 4i, i < cnt <= 128; the table
+  // this wave's blocks: blk0 + wave + NW i, i < cnt <= 128; the table
   // entries come in two loads (entry i in lane i % 64 of my_phys[i / 64])
-  const int cnt = blk1 - blk0 > wave ? cdiv(blk1 - blk0 - wave, 4) : 0;
+  const int cnt = blk1 - blk0 > wave ? cdiv(blk1 - blk0 - wave, NW) : 0;
   int my_phys[2] = {0, 0};
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    if (64 * h + lane < cnt) my_phys[h] = seq_block(a.seq, sidx, blk0 + wave + 4 * (64 * h + lane));
+    if (64 * h + lane < cnt) my_phys[h] = seq_block(a.seq, sidx, blk0 + wave + NW * (64 * h + lane));
 
   // ex: the block's factor exponents (eK in the low byte, eV in the high;
   // 0 without block scales), P <= 2^kLazy times 2^eV <= 2^7 stays in the fp16
   // range
   auto compute = [&](const DecFrags<D, F>& f, int i, int ex) {
-    const int blk = blk0 + wave + 4 * i;
+    const int blk = blk0 + wave + NW * i;
     const float sck = Q ? ldexpf(sc, (int8_t)(ex & 0xff)) : sc;
     const float fvb = Q ? ldexpf(1.f, (int8_t)(ex >> 8)) : 1.f;
     // S^T[key][head]: A = K rows (key = lane%16), B = Q^T (hi + lo, two
@@ -529,7 +532,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
     __syncthreads();  // every wave is done with its stages before they take the accumulators
   }
 
-  // ---- merge the four waves: acc[t][r] = O^T[dec_vchan(t, 4grp + r)][head col]
+  // ---- merge the waves: acc[t][r] = O^T[dec_vchan(t, 4grp + r)][head col]
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   lv_run += __shfl_xor(lv_run, 16, 64);
@@ -546,15 +549,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   __syncthreads();
 
   float* pp = a.part + (((size_t)b * a.Hkv + g) * a.max_parts + p) * kPartStride(D);
-  for (int e = tid; e < 16 * D; e += 256) {
+  for (int e = tid; e < 16 * D; e += NW * 64) {
     const int hh = e / D, d = e % D;
     if (hh >= n_rep) continue;
     float M = sm_m[0][hh];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][hh]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][hh]);
     float O = 0.f, L = 0.f, Lv = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = exp2f(sm_m[w][hh] - M);  // 0 for a wave with no blocks
       O += o_tile(w)[o_idx(d, hh)] * f;
       L += sm_l[w][hh] * f;
@@ -665,8 +668,15 @@ hipError_t attn_decode(const DecodePlan& pl, const void* q, KvPool pool, SeqInfo
   DecArgs a{(const float*)q, pool, seq, first_seq, Hq, Hkv, pl.part_blocks, pl.max_parts, part,
             (f16*)o};
   dim3 grid(Hkv, batch, pl.max_parts);
-#define TDL_DECODE_CASE(DD, FF) \
-  if (D == DD && pool.fmt == FF) attn_decode_kernel<DD, FF><<<grid, 256, 0, s>>>(a);
+  // at most one workgroup per CU: eight waves per workgroup (twice the
+  // blocks in flight for each (sequence, KV head); the longest sequence sets
+  // the time); otherwise four (two workgroups per CU)
+  const bool wide = (size_t)Hkv * batch * pl.max_parts <= 256;
+#define TDL_DECODE_CASE(DD, FF)                                                   \
+  if (D == DD && pool.fmt == FF) {                                                \
+    if (wide) attn_decode_kernel<DD, FF, 8><<<grid, 512, 0, s>>>(a);              \
+    else attn_decode_kernel<DD, FF, 4><<<grid, 256, 0, s>>>(a);                   \
+  }
   TDL_DECODE_CASE(128, kKvBf16) TDL_DECODE_CASE(128, kKvU8) TDL_DECODE_CASE(128, kKvU4)
   TDL_DECODE_CASE(64, kKvBf16) TDL_DECODE_CASE(64, kKvU8) TDL_DECODE_CASE(64, kKvU4)
 #undef TDL_DECODE_CASE
