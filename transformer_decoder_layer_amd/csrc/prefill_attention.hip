@@ -94,21 +94,36 @@ struct PrefillArgs {
 // When the group is split over n_split workgroups, the last one may have
 // fewer heads than waves; its spare waves repeat its last head (computed,
 // never stored) and still share the copies.
-template <int D, int NH, int F>
-__global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
+//
+// KS = 2 (short prompts, where the grid leaves CUs idle and the longest
+// query tile's key loop sets the time): two key groups of NH waves each take
+// half of the staged key tiles of the same query tile and heads, in
+// lockstep (the workgroup's barriers are shared; the group with fewer tiles
+// repeats a copy and skips the products), and group 1's running maximum,
+// denominator and accumulators are merged into group 0's through LDS at the
+// end.  Keys from the paged cache are converted by all threads and taken by
+// group 0 alone.
+template <int D, int NH, int F, int KS>
+__global__ __launch_bounds__(NH * KS * 64) void attn_prefill_kernel(PrefillArgs a) {
   using T = Tile<D>;
-  constexpr int NW = NH;
-  constexpr int NT = NW * 64;
+  static_assert(KS == 1 || KS == 2, "key groups");
+  constexpr int NW = NH;  // waves per key group
+  constexpr int NT = NH * KS * 64;
   // four stages, each its own array so that the compiler can tell a copy
-  // landing in one stage from reads of another
-  __shared__ __attribute__((aligned(16))) f16 s0[T::kElems];
-  __shared__ __attribute__((aligned(16))) f16 s1[T::kElems];
-  __shared__ __attribute__((aligned(16))) f16 s2[T::kElems];
-  __shared__ __attribute__((aligned(16))) f16 s3[T::kElems];
+  // landing in one stage from reads of another (key group k uses elements
+  // k * kElems of each)
+  __shared__ __attribute__((aligned(16))) f16 s0[KS * T::kElems];
+  __shared__ __attribute__((aligned(16))) f16 s1[KS * T::kElems];
+  __shared__ __attribute__((aligned(16))) f16 s2[KS * T::kElems];
+  __shared__ __attribute__((aligned(16))) f16 s3[KS * T::kElems];
   // u8 / u4 caches: this KV head's per-channel scale and zero point of K and V
   __shared__ float dq[4][D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // key group and head wave within it (compile-time 0 and tid / 64 for one
+  // key group, so that each stage pointer stays a known array)
+  const int kg = KS == 1 ? 0 : (tid >> 6) / NH;
+  const int wave = KS == 1 ? tid >> 6 : (tid >> 6) % NH;
   // (query tile slot x, KV head g) from the flat workgroup index.  The
   // dispatcher deals workgroups round-robin to the 8 XCDs (each with its own
   // L2): when the head count divides 8, each XCD takes whole heads, so an
@@ -478,6 +493,7 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
       // one pool tile: mask past this lane's query position and past the
       // pool's keys, then the softmax update and P V
       auto pool_tile = [&](int t, const f16* tile) {
+        if (kg != 0) return;  // wave-uniform
         const int key_base = t * PK;
         const bool masked = key_base + PK - 1 > ctx + q_lo || key_base + PK > n_pool_keys;
         plain_tile(tile, masked, min(ctx + my_q, n_pool_keys - 1) - key_base);
@@ -512,20 +528,32 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
 
     // ----------------------------------------------- the staged chunk keys
     if (staged) {
-      const int n_st = cdiv(q_hi + 1, PK);  // chunk tiles this query tile sees
+      const int n_all = cdiv(q_hi + 1, PK);  // chunk tiles this query tile sees
+      // this key group's tiles: tb .. tb + n_st - 1 (every group steps
+      // through n_steps tiles; copies past its last tile repeat a valid one)
+      const int n_steps = cdiv(n_all, KS);
+      const int tb = kg * n_steps;
+      const int n_st = min(n_all - tb, n_steps);  // may be 0 for group 1
+      const int t_last = max(min(tb + n_st, n_all) - 1, 0);
       const size_t base = (size_t)g * a.st.rows + prefill_stage_base(a.seq, sidx);
       const f16* ksrc = a.st.k + base * D;
       const f16* vsrc = a.st.v + base * D;
+      f16* const g0 = s0 + kg * T::kElems;
+      f16* const g1 = s1 + kg * T::kElems;
+      f16* const g2 = s2 + kg * T::kElems;
+      f16* const g3 = s3 + kg * T::kElems;
       constexpr int L = (T::kInst + NW - 1) / NW;  // copies per wave and tile
       // copy i of a tile: K (first half) or V (second half), 1 KB each;
       // waves past the last copy repeat it (the same bytes to the same place)
+      // (t: this group's tile index, 0-based)
       auto issue = [&](int t, f16* tile) {
+        const int ta = min(tb + t, t_last);
 #pragma unroll
         for (int j = 0; j < L; ++j) {
           const int i = min(wave + NW * j, T::kInst - 1);
           const bool isk = i < T::kInst / 2;
           const int off = (isk ? i : i - T::kInst / 2) * 512;  // fp16 elements
-          const f16* src = (isk ? ksrc : vsrc) + (size_t)t * PK * D + off + lane * 8;
+          const f16* src = (isk ? ksrc : vsrc) + (size_t)ta * PK * D + off + lane * 8;
           __builtin_amdgcn_global_load_lds((const void*)src,
                                            (lds_void*)(tile + (isk ? 0 : T::kK) + off), 16, 0, 0);
         }
@@ -542,22 +570,22 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
       };
-      auto masked_at = [&](int t) { return t * PK + PK - 1 > q_lo || t * PK + PK > q_len; };
-      auto lim_at = [&](int t) { return min(my_q, q_len - 1) - t * PK; };
+      auto masked_at = [&](int t) { return (tb + t) * PK + PK - 1 > q_lo || (tb + t) * PK + PK > q_len; };
+      auto lim_at = [&](int t) { return min(my_q, q_len - 1) - (tb + t) * PK; };
 
       // Every step issues the same copies (past the last tile they repeat it,
       // into a stage no step reads again), so every wait counts the same
       // number of copies on every path.
       __builtin_amdgcn_sched_barrier(0);
-      issue(0, s0);
-      issue(min(1, n_st - 1), s1);
-      issue(min(2, n_st - 1), s2);
+      issue(0, g0);
+      issue(1, g1);
+      issue(2, g2);
       __builtin_amdgcn_sched_barrier(0);
       wait_one_tile();
       __builtin_amdgcn_sched_barrier(0);
       barrier();
       __builtin_amdgcn_sched_barrier(0);
-      f32x16 sa = qk(s0), sb;
+      f32x16 sa = qk(g0), sb;
       // step t: tiles t and t+1 are in LDS, S(t) in registers.  Issue tile
       // t+3; read K(t+1)'s fragments; the row maxima of S(t) and the lazy
       // reference update; then S(t+1) = Q K(t+1)^T one MFMA at a time, each
@@ -568,7 +596,7 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
       // first.  The fences keep this order: every LDS read is issued well
       // before the MFMA that takes it.
       auto step = [&](int t, f16* cur, f16* nxt, f16* fill, f32x16& scur, f32x16& snxt) {
-        issue(min(t + 3, n_st - 1), fill);
+        issue(t + 3, fill);
         if (t < n_st) {
           constexpr int NS = D / 16;       // MFMAs of Q K^T
           constexpr int EPS = 16 / NS;     // exponentials per MFMA
@@ -633,18 +661,56 @@ __global__ __launch_bounds__(NH * 64) void attn_prefill_kernel(PrefillArgs a) {
       };
       // whole groups of four steps (steps past the last tile only copy and
       // wait), so that each of the four keeps its own stage arrays
-      for (int t = 0; t < n_st; t += 4) {
-        step(t, s0, s1, s3, sa, sb);
-        step(t + 1, s1, s2, s0, sb, sa);
-        step(t + 2, s2, s3, s1, sa, sb);
-        step(t + 3, s3, s0, s2, sb, sa);
+      for (int t = 0; t < n_steps; t += 4) {
+        step(t, g0, g1, g3, sa, sb);
+        step(t + 1, g1, g2, g0, sb, sa);
+        step(t + 2, g2, g3, g1, sa, sb);
+        step(t + 3, g3, g0, g2, sb, sa);
       }
       __builtin_amdgcn_s_waitcnt(0);  // the repeated copies past the last tile
     }
 
+    // ---------------------------------------- key group 1 into key group 0
+    if constexpr (KS == 2) {
+      __syncthreads();  // every wave is done with the stage arrays
+      // wave w of group 1 leaves its state in the stage memory of group 0's
+      // wave w: D/2 accumulator floats, m and l per lane
+      constexpr int PER = D / 32 * 16 + 2;
+      static_assert(NH * PER * 64 * 4 <= 4 * KS * T::kBytes, "merge buffer");
+      auto slot = [&](int i) -> float& {  // element i of this lane's record, spread over s0..s3
+        const int flat = (wave * PER + i) * 64 + lane;
+        constexpr int per_arr = KS * T::kElems / 2;  // floats per stage array
+        const int arr = flat / per_arr, off = flat % per_arr;
+        float* base = (float*)(arr == 0 ? s0 : arr == 1 ? s1 : arr == 2 ? s2 : s3);
+        return base[off];
+      };
+      if (kg == 1) {
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) slot(16 * t + r) = acc[t][r];
+        slot(PER - 2) = m_run;
+        slot(PER - 1) = l_run;
+      }
+      __syncthreads();
+      if (kg == 0) {
+        const float m1 = slot(PER - 2), l1 = slot(PER - 1);
+        const float m = fmaxf(m_run, m1);
+        // a group without keys has m = -inf: its weight is 0
+        const float f0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+        const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[t][r] = acc[t][r] * f0 + slot(16 * t + r) * f1;
+        l_run = l_run * f0 + l1 * f1;
+        m_run = m;
+      }
+    }
+
     // ------------------------------------------------------------ output
     const float l = l_run + __shfl_xor(l_run, 32, 64);
-    if (own && my_q < q_len) {
+    if (own && kg == 0 && my_q < q_len) {
       const float inv = 1.f / l;
       f16* op = a.o + (size_t)(row0 + ql) * a.Hq * D + (size_t)h * D;
 #pragma unroll
@@ -682,18 +748,32 @@ hipError_t attn_prefill(const void* q, const PrefillQ& qsrc, KvPool pool, SeqInf
   const long whole = (long)a.n_qtiles * Hkv * n_prefill;
   int nh = a.n_rep;
   if (whole < 256 && nh > 4) nh = 4;
+  // still fewer workgroups than CUs (short prompts, where the last query
+  // tile's key loop sets the time): groups of at most two heads, each with
+  // two key groups that take half of the key tiles (four waves of up to 512
+  // registers; four heads x two key groups in eight waves would spill)
+  const bool ks2 = a.n_qtiles > 1 && whole * cdiv(a.n_rep, nh) < 256;
+  if (ks2) nh = nh < 2 ? nh : 2;
   a.n_split = cdiv(a.n_rep, nh);
   // pair query tiles (x, n-1-x) when that still leaves a workgroup per CU
   a.paired = (long)cdiv(a.n_qtiles, 2) * Hkv * a.n_split * n_prefill >= 256 ? 1 : 0;
   const dim3 grid((a.paired ? cdiv(a.n_qtiles, 2) : a.n_qtiles) * Hkv * a.n_split, 1, n_prefill);
+#define TDL_PREFILL_FMT(DD, NH, KS)                                                \
+  if (pool.fmt == kKvU8)                                                           \
+    attn_prefill_kernel<DD, NH, kKvU8, KS><<<grid, NH * KS * 64, 0, s>>>(a);       \
+  else if (pool.fmt == kKvU4)                                                      \
+    attn_prefill_kernel<DD, NH, kKvU4, KS><<<grid, NH * KS * 64, 0, s>>>(a);       \
+  else                                                                             \
+    attn_prefill_kernel<DD, NH, kKvBf16, KS><<<grid, NH * KS * 64, 0, s>>>(a);
 #define TDL_PREFILL_CASE(DD, NH)                                                   \
   if (D == DD && nh == NH) {                                                       \
-    if (pool.fmt == kKvU8)                                                         \
-      attn_prefill_kernel<DD, NH, kKvU8><<<grid, NH * 64, 0, s>>>(a);              \
-    else if (pool.fmt == kKvU4)                                                    \
-      attn_prefill_kernel<DD, NH, kKvU4><<<grid, NH * 64, 0, s>>>(a);              \
-    else                                                                           \
-      attn_prefill_kernel<DD, NH, kKvBf16><<<grid, NH * 64, 0, s>>>(a);            \
+    if constexpr (NH <= 2) {                                                       \
+      if (ks2) {                                                                   \
+        TDL_PREFILL_FMT(DD, NH, 2)                                                 \
+        return hipGetLastError();                                                  \
+      }                                                                            \
+    }                                                                              \
+    TDL_PREFILL_FMT(DD, NH, 1)                                                     \
     return hipGetLastError();                                                      \
   }
   TDL_PREFILL_CASE(128, 1) TDL_PREFILL_CASE(128, 2) TDL_PREFILL_CASE(128, 4)
@@ -701,6 +781,7 @@ hipError_t attn_prefill(const void* q, const PrefillQ& qsrc, KvPool pool, SeqInf
   TDL_PREFILL_CASE(64, 1) TDL_PREFILL_CASE(64, 2) TDL_PREFILL_CASE(64, 4)
   TDL_PREFILL_CASE(64, 7) TDL_PREFILL_CASE(64, 8)
 #undef TDL_PREFILL_CASE
+#undef TDL_PREFILL_FMT
   return hipErrorInvalidValue;
 }
 
