@@ -405,22 +405,26 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] *= alpha;
     }
-    // P as a pair hi + lo (bf16 or fp16, the operand type of V): the
-    // weights keep fp32 precision
+    // bf16 cache: P as a pair hi + lo of bf16 (the weights keep fp32
+    // precision).  Code caches: P rounded once to fp16 (2^-12 relative), and
+    // the denominators summed from the same rounded values, so that the
+    // bias + zero point taken out at the end cancels what the products put
+    // in up to fp32 rounding (one MFMA per tile instead of two: these
+    // kernels are bound by the per-block chain, not by bytes)
     PT pf, pl;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float pv = exp2f(sv[r] - m_run);
       if constexpr (Q) {
-        const float pw = pv * fvb;  // exact: a power of two
-        pf[r] = (_Float16)pw;
-        pl[r] = (_Float16)(pw - (float)pf[r]);
+        const _Float16 ph = (_Float16)pv;
+        pf[r] = (_Float16)((float)ph * fvb);  // exact: a power of two (P <= 2^8, 2^eV <= 2^7)
+        psum += (float)ph;
       } else {
         pf[r] = f32_to_bf16(pv);
         pl[r] = f32_to_bf16(pv - (float)pf[r]);
+        psum += pv;
       }
-      psum += pv;
     }
     l_run += psum;
     lv_run += psum * fvb;
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(DecArgs a) {
         }
       }
       acc[t] = mfma16x16x16(vf, pf, acc[t]);
-      acc[t] = mfma16x16x16(vf, pl, acc[t]);
+      if constexpr (!Q) acc[t] = mfma16x16x16(vf, pl, acc[t]);
     }
   };
 
