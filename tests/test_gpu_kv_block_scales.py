@@ -139,7 +139,9 @@ def test_prefill_over_block_scaled_cache(kvd):
     # the block-scaled values) and after cached tokens (gathered and
     # dequantised with their blocks' factors)
     wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=TINY_Q3, kv_dtype=kvd)
-    for P, T in ((0, 77), (0, 150), (83, 37), (16, 100)):
+    # (1030 and 1100 rows: the RoPE/KV kernel's four rows per workgroup,
+    # after the one-row exponent pass)
+    for P, T in ((0, 77), (0, 150), (83, 37), (16, 100), (0, 1030), (83, 1100)):
         inp = synth.make_inputs(wl, seed=50 + P + T, prefill_len=T, prefill_start=P, spare_blocks=2,
                                 random_gains=True)
         inp = _narrow_calibration(inp, 51 + P + T)

@@ -156,3 +156,35 @@ def test_more_prefill_sequences_than_staged(kvd):
     e = harness.compare(t["y"].float().cpu().numpy()[rows], ref)
     print(f"[{n_pre} prefill seqs, {kvd}] {e}", flush=True)
     assert e.ok, e
+
+
+# 1024 rows and more: the RoPE/KV kernel takes four rows per workgroup (the
+# loads of all four issued before any is rotated or stored); rows of a group
+# may belong to different sequences (the mixed step: the chunk's last rows
+# and the first decode rows)
+@pytest.mark.parametrize("kvd", ["u8", "u4"])
+def test_long_prefill_coded_cache_four_rows_per_workgroup(kvd):
+    import torch
+    from harness import unpack_u4
+    import oracle
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=TINY_Q3, kv_dtype=kvd)
+    T = 1030
+    inp = synth.make_inputs(wl, seed=130, prefill_len=T, spare_blocks=2, random_gains=True)
+    inp = _calibration(_one_hot_rows(inp, 230), 330)
+    layer, kv, t, cache, rows = check_layer(inp, what=f"prefill {T} from 0, {kvd} exact")
+    kt, vt = kv.tensors()[:2]
+    if kvd == "u4":
+        kt, vt = map(torch.from_numpy, unpack_u4(kt, vt))
+    for p in range(T):
+        blk, off = oracle.PagedCache.location(inp.batch.table[0], p)
+        assert np.array_equal(kt[blk, :, off, :].cpu().numpy(), cache.k[blk, :, off, :]), (p, "K")
+        assert np.array_equal(vt[blk, :, :, off].cpu().numpy(), cache.v[blk, :, off, :]), (p, "V")
+
+
+@pytest.mark.parametrize("kvd", ["bf16", "u8"])
+def test_long_mixed_step_four_rows_per_workgroup(kvd):
+    wl = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=TINY_Q3, kv_dtype=kvd)
+    inp = synth.make_inputs(wl, seed=140, prefill_len=1041, decode_batch=6,
+                            decode_ctx=[3, 16, 40, 129, 500, 7], random_gains=True)
+    layer, kv, t, cache, rows = check_layer(inp, what=f"mixed 1041 + 6, {kvd}")
+    check_cache_rows(inp, kv, cache, range(7))

@@ -148,12 +148,13 @@ __device__ __forceinline__ int wave_max_i(int v) {
 
 // bf16 / u8 pools: one element per (slot, d); u8 codes in a block with
 // factors 2^ek (K) and 2^ev (V)
+template <int F>
 __device__ __forceinline__ void store_kv(const KvPool& pool, int blk, int g, int Hkv, int D, int slot,
                                          int d, float kval, float vval, int ek = 0, int ev = 0) {
   const size_t head = ((size_t)blk * Hkv + g) * kBlockTokens * D;
   const size_t kidx = head + (size_t)slot * D + d;   // K: [blk][g][slot][d]
   const size_t vidx = head + (size_t)d * kBlockTokens + slot;  // V: [blk][g][d][slot]
-  if (pool.fmt == kKvU8) {
+  if constexpr (F == kKvU8) {
     const int ch = g * D + d;
     ((uint8_t*)pool.k)[kidx] = (uint8_t)quant_code(kval, pool.k_scale[ch], pool.k_zp[ch], 255, ek);
     ((uint8_t*)pool.v)[vidx] = (uint8_t)quant_code(vval, pool.v_scale[ch], pool.v_zp[ch], 255, ev);
@@ -189,38 +190,59 @@ __device__ __forceinline__ int u4_vbyte(int slot, int d) { return (d >> 1) * kBl
 // mode 0: every row quantises with its block's exponents (set by this call's
 // mode-1 launch, or by the call that wrote the block's first slot).
 // SB: split-K slices read per batch of loads (1, 4 or 8 by the slice count;
-// a larger batch costs registers and occupancy).
-template <int SB>
-__global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ qkv, int Hq, int Hkv,
-                                                      int D, const float2* __restrict__ tab,
+// a larger batch costs registers and occupancy); F: the pool's format; RPW:
+// rows per workgroup (mode 0 only): each wave issues the loads of all its
+// rows' inputs before it rotates and stores any of them, one chain of
+// dependent loads for RPW rows instead of one per row.
+template <int SB, int F, int RPW>
+__global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ qkv, int rows, int Hq,
+                                                      int Hkv, int D, const float2* __restrict__ tab,
                                                       const float* __restrict__ qn,
                                                       const float* __restrict__ kn, float eps,
                                                       float* __restrict__ q_out, SeqInfo seq,
                                                       KvPool pool, PrefillStage stage, int splits,
                                                       const float* __restrict__ bias, int hpw, int mode,
                                                       int q_skip) {
-  const int row = blockIdx.x;
+  static_assert(RPW >= 1, "rows per workgroup");
+  const int row0 = blockIdx.x * RPW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = D >> 1;
-  const int sidx = find_seq(seq, row);
-  const int pos = row_position(seq, sidx, row);
   const int ldq = (Hq + 2 * Hkv) * D;
-  const size_t slice = (size_t)gridDim.x * ldq;
-  const int blk = block_of(seq, sidx, pos);
-  const int slot = pos % kBlockTokens;
-  // mode 1: only the rows at slot 0, for the rows of this call in the block
+  const size_t slice = (size_t)rows * ldq;
+  // the rows' sequences, positions and cache slots
+  int r_sidx[RPW], r_pos[RPW], r_blk[RPW], r_slot[RPW], r_srow[RPW];
+  bool r_ok[RPW], r_staged[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int row = min(row0 + rr, rows - 1);
+    r_ok[rr] = row0 + rr < rows;
+    r_sidx[rr] = find_seq(seq, row);
+    r_pos[rr] = row_position(seq, r_sidx[rr], row);
+    r_blk[rr] = block_of(seq, r_sidx[rr], r_pos[rr]);
+    r_slot[rr] = r_pos[rr] % kBlockTokens;
+    // the row of the prefill staging copy (sequences < stage.n_seqs)
+    r_staged[rr] = mode == 0 && !seq.rows_are_seqs && r_sidx[rr] < stage.n_seqs;
+    r_srow[rr] = r_staged[rr] ? prefill_stage_base(seq, r_sidx[rr]) + row -
+                                    (seq.q_start ? seq.q_start[r_sidx[rr]] : 0)
+                              : 0;
+  }
+  // mode 1 (RPW = 1): only the rows at slot 0, for the rows of this call in the block
   int n_blk_rows = 1;
   if (mode == 1) {
-    if (slot != 0) return;
-    n_blk_rows = min(kBlockTokens, min(seq_end_row(seq, sidx, row), (int)gridDim.x) - row);
+    if (r_slot[0] != 0) return;
+    n_blk_rows = min(kBlockTokens, min(seq_end_row(seq, r_sidx[0], row0), rows) - row0);
   }
-  // elements c[0..NC) of row row+i's projection: the partial slices in order
-  // (+ bias), read SB slices at a time with every load of a batch issued
-  // before the first add (slice indices past the last repeat it and add
-  // nothing)
+  // elements c[0..NC) of row row0+i's projection: the partial slices in
+  // order (+ bias), read SB slices at a time with every load of a batch
+  // issued before the first add (slice indices past the last repeat it and
+  // add nothing)
   auto vals = [&](int i, auto& c, auto& out) {
     constexpr int NC = sizeof(out) / sizeof(float);
-    const float* src = qkv + (size_t)(row + i) * ldq;
+    const float* src = qkv + (size_t)min(row0 + i, rows - 1) * ldq;
+    if constexpr (SB == 1) {  // one slice (splits == 1): plain loads, nothing waits for them here
+#pragma unroll
+      for (int k = 0; k < NC; ++k) out[k] = src[c[k]];
+    } else
     for (int s0 = 0; s0 < splits; s0 += SB) {
       float t[SB][NC];
 #pragma unroll
@@ -241,12 +263,12 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
   };
   const bool act = lane < half;
   const int ln = act ? lane : 0;  // lanes past D/2 load a valid element and store nothing
-  // head h of row row+i, normalised (Q/K) and rotated: channels ln, ln + D/2
-  // (x holds their projections)
-  auto rotate = [&](int i, int h, float x1, float x2, float& r1, float& r2) {
+  // the (cos, sin) pair of channel pair `lane` at position p
+  auto rope_cs = [&](int p) { return act ? tab[(size_t)p * half + lane] : make_float2(1.f, 0.f); };
+  // head h normalised (Q/K) and rotated: channels ln, ln + D/2 (x holds
+  // their projections)
+  auto rotate = [&](int h, float x1, float x2, float2 cs, float& r1, float& r2) {
     const bool is_q = h < Hq;
-    float2 cs = make_float2(1.f, 0.f);
-    if (act) cs = tab[(size_t)(pos + i) * half + lane];
     if (!act) x1 = x2 = 0.f;
     const float* gn = is_q ? qn : kn;
     if (gn) {  // per-head RMSNorm over D
@@ -260,12 +282,9 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
     r1 = x1 * cs.x - x2 * cs.y;
     r2 = x1 * cs.y + x2 * cs.x;
   };
-  // the row of the prefill staging copy (sequences < stage.n_seqs)
-  const bool staged = mode == 0 && !seq.rows_are_seqs && sidx < stage.n_seqs;
-  const int srow = staged ? prefill_stage_base(seq, sidx) + row - (seq.q_start ? seq.q_start[sidx] : 0) : 0;
-  const int top = pool.fmt == kKvU8 ? 255 : 15;
+  constexpr int top = F == kKvU8 ? 255 : 15;
 
-  // one wave per head: workgroup (row, y) takes heads hpw*y .. hpw*y + hpw-1
+  // one wave per head: workgroup (rows, y) takes heads hpw*y .. hpw*y + hpw-1
   for (int h = hpw * blockIdx.y + wave; h < min(Hq + Hkv, hpw * ((int)blockIdx.y + 1)); h += 4) {
     const bool is_q = h < Hq;
     if (mode == 1) {  // wave-uniform
@@ -279,7 +298,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
         float x[4];
         vals(i, cols, x);
         float r1, r2;
-        rotate(i, h, x[0], x[1], r1, r2);
+        rotate(h, x[0], x[1], rope_cs(r_pos[0] + i), r1, r2);
         const float v1 = x[2], v2 = x[3];
         if (act) {
           ek = max(ek, max(exp_needed(r1, pool.k_scale[c1], pool.k_zp[c1], top),
@@ -291,83 +310,115 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
       ek = wave_max_i(ek);
       ev = wave_max_i(ev);
       if (lane == 0) {
-        pool.exps[((size_t)blk * Hkv + g) * 2] = (int8_t)ek;
-        pool.exps[((size_t)blk * Hkv + g) * 2 + 1] = (int8_t)ev;
+        pool.exps[((size_t)r_blk[0] * Hkv + g) * 2] = (int8_t)ek;
+        pool.exps[((size_t)r_blk[0] * Hkv + g) * 2 + 1] = (int8_t)ev;
       }
       continue;
     }
-    if (is_q && sidx < q_skip) continue;  // rotated by prefill attention as it loads q
-    float r1, r2;
+    // rows whose queries the prefill attention rotates as it loads them
+    bool live[RPW], any = false;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      live[rr] = r_ok[rr] && !(is_q && r_sidx[rr] < q_skip);
+      any = any || live[rr];
+    }
+    if (!any) continue;  // wave-uniform: e.g. every row's queries rotated by prefill attention
     if (is_q) {  // wave-uniform
       const int cols[2] = {h * D + ln, h * D + ln + half};
-      float x[2];
-      vals(0, cols, x);
-      rotate(0, h, x[0], x[1], r1, r2);
-      if (act) {
-        float* qo = q_out + ((size_t)row * Hq + h) * D;
-        qo[lane] = r1;
-        qo[lane + half] = r2;
+      float x[RPW][2];
+      float2 cs[RPW];
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        vals(rr, cols, x[rr]);
+        cs[rr] = rope_cs(r_pos[rr]);
+      }
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        if (!live[rr]) continue;  // wave-uniform
+        float r1, r2;
+        rotate(h, x[rr][0], x[rr][1], cs[rr], r1, r2);
+        if (act) {
+          float* qo = q_out + ((size_t)(row0 + rr) * Hq + h) * D;
+          qo[lane] = r1;
+          qo[lane + half] = r2;
+        }
       }
       continue;
     }
     const int g = h - Hq;
     const int vc = (Hq + Hkv + g) * D;
     const int cols[4] = {h * D + ln, h * D + ln + half, vc + ln, vc + ln + half};
-    float x[4];
-    vals(0, cols, x);
-    rotate(0, h, x[0], x[1], r1, r2);
-    const float v1 = x[2], v2 = x[3];
-    const int ek = pool_exp(pool, blk, g, Hkv, 0), ev = pool_exp(pool, blk, g, Hkv, 1);
-    if (staged && act) {
-      // fp16 copy of what the cache holds (bf16-rounded, or the dequantised
-      // code) for prefill attention
-      const int c1 = g * D + lane, c2 = c1 + half;
-      float sk1, sk2, sv1, sv2;
-      if (pool.fmt == kKvBf16) {
-        sk1 = (float)f32_to_bf16(r1); sk2 = (float)f32_to_bf16(r2);
-        sv1 = (float)f32_to_bf16(v1); sv2 = (float)f32_to_bf16(v2);
+    float x[RPW][4];
+    float2 cs[RPW];
+    int ekr[RPW], evr[RPW];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      vals(rr, cols, x[rr]);
+      cs[rr] = rope_cs(r_pos[rr]);
+      ekr[rr] = pool_exp(pool, r_blk[rr], g, Hkv, 0);
+      evr[rr] = pool_exp(pool, r_blk[rr], g, Hkv, 1);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      if (!live[rr]) continue;  // wave-uniform
+      float r1, r2;
+      rotate(h, x[rr][0], x[rr][1], cs[rr], r1, r2);
+      const float v1 = x[rr][2], v2 = x[rr][3];
+      const int ek = ekr[rr], ev = evr[rr];
+      const int blk = r_blk[rr], slot = r_slot[rr];
+      if (r_staged[rr] && act) {
+        // fp16 copy of what the cache holds (bf16-rounded, or the dequantised
+        // code) for prefill attention
+        const int c1 = g * D + lane, c2 = c1 + half;
+        float sk1, sk2, sv1, sv2;
+        if constexpr (F == kKvBf16) {
+          sk1 = (float)f32_to_bf16(r1); sk2 = (float)f32_to_bf16(r2);
+          sv1 = (float)f32_to_bf16(v1); sv2 = (float)f32_to_bf16(v2);
+        } else {
+          const float fk = ldexpf(1.f, ek), fv = ldexpf(1.f, ev);
+          sk1 = (float)(quant_code(r1, pool.k_scale[c1], pool.k_zp[c1], top, ek) - pool.k_zp[c1]) * (pool.k_scale[c1] * fk);
+          sk2 = (float)(quant_code(r2, pool.k_scale[c2], pool.k_zp[c2], top, ek) - pool.k_zp[c2]) * (pool.k_scale[c2] * fk);
+          sv1 = (float)(quant_code(v1, pool.v_scale[c1], pool.v_zp[c1], top, ev) - pool.v_zp[c1]) * (pool.v_scale[c1] * fv);
+          sv2 = (float)(quant_code(v2, pool.v_scale[c2], pool.v_zp[c2], top, ev) - pool.v_zp[c2]) * (pool.v_scale[c2] * fv);
+        }
+        const int srow = r_srow[rr];
+        const size_t hb = (size_t)g * stage.rows * D;
+        stage.k[hb + prefill_k_index(srow, lane, D)] = f32_to_f16_sat(sk1);
+        stage.k[hb + prefill_k_index(srow, lane + half, D)] = f32_to_f16_sat(sk2);
+        stage.v[hb + prefill_v_index(srow, lane, D)] = f32_to_f16_sat(sv1);
+        stage.v[hb + prefill_v_index(srow, lane + half, D)] = f32_to_f16_sat(sv2);
+      }
+      if constexpr (F != kKvU4) {
+        if (act) {
+          store_kv<F>(pool, blk, g, Hkv, D, slot, lane, r1, v1, ek, ev);
+          store_kv<F>(pool, blk, g, Hkv, D, slot, lane + half, r2, v2, ek, ev);
+        }
       } else {
-        const float fk = ldexpf(1.f, ek), fv = ldexpf(1.f, ev);
-        sk1 = (float)(quant_code(r1, pool.k_scale[c1], pool.k_zp[c1], top, ek) - pool.k_zp[c1]) * (pool.k_scale[c1] * fk);
-        sk2 = (float)(quant_code(r2, pool.k_scale[c2], pool.k_zp[c2], top, ek) - pool.k_zp[c2]) * (pool.k_scale[c2] * fk);
-        sv1 = (float)(quant_code(v1, pool.v_scale[c1], pool.v_zp[c1], top, ev) - pool.v_zp[c1]) * (pool.v_scale[c1] * fv);
-        sv2 = (float)(quant_code(v2, pool.v_scale[c2], pool.v_zp[c2], top, ev) - pool.v_zp[c2]) * (pool.v_scale[c2] * fv);
+        // u4: lane i holds channels i and i + D/2; a byte pairs channels d,
+        // d + 4 (K) or d, d + 1 (V), whose codes sit in lanes i ^ 4 / i ^ 1
+        // (D/2 is a multiple of 8, so partners of active lanes are active).
+        // Every lane takes part in the exchange.
+        const int c1 = g * D + ln, c2 = c1 + half;
+        const int k1 = quant_code(r1, pool.k_scale[c1], pool.k_zp[c1], 15, ek);
+        const int k2 = quant_code(r2, pool.k_scale[c2], pool.k_zp[c2], 15, ek);
+        const int w1 = quant_code(v1, pool.v_scale[c1], pool.v_zp[c1], 15, ev);
+        const int w2 = quant_code(v2, pool.v_scale[c2], pool.v_zp[c2], 15, ev);
+        const int pk1 = __shfl_xor(k1, 4, 64), pk2 = __shfl_xor(k2, 4, 64);
+        const int pw1 = __shfl_xor(w1, 1, 64), pw2 = __shfl_xor(w2, 1, 64);
+        if (act) {
+          const size_t hb = u4_head(blk, g, Hkv, D);
+          uint8_t* kp = (uint8_t*)pool.k + hb;
+          uint8_t* vp = (uint8_t*)pool.v + hb;
+          if (!(lane & 4)) {
+            kp[u4_kbyte(slot, lane, D)] = (uint8_t)(k1 | (pk1 << 4));
+            kp[u4_kbyte(slot, lane + half, D)] = (uint8_t)(k2 | (pk2 << 4));
+          }
+          if (!(lane & 1)) {
+            vp[u4_vbyte(slot, lane)] = (uint8_t)(w1 | (pw1 << 4));
+            vp[u4_vbyte(slot, lane + half)] = (uint8_t)(w2 | (pw2 << 4));
+          }
+        }
       }
-      const size_t hb = (size_t)g * stage.rows * D;
-      stage.k[hb + prefill_k_index(srow, lane, D)] = f32_to_f16_sat(sk1);
-      stage.k[hb + prefill_k_index(srow, lane + half, D)] = f32_to_f16_sat(sk2);
-      stage.v[hb + prefill_v_index(srow, lane, D)] = f32_to_f16_sat(sv1);
-      stage.v[hb + prefill_v_index(srow, lane + half, D)] = f32_to_f16_sat(sv2);
-    }
-    if (pool.fmt != kKvU4) {
-      if (act) {
-        store_kv(pool, blk, g, Hkv, D, slot, lane, r1, v1, ek, ev);
-        store_kv(pool, blk, g, Hkv, D, slot, lane + half, r2, v2, ek, ev);
-      }
-      continue;
-    }
-    // u4: lane i holds channels i and i + D/2; a byte pairs channels d, d + 4
-    // (K) or d, d + 1 (V), whose codes sit in lanes i ^ 4 / i ^ 1 (D/2 is a
-    // multiple of 8, so partners of active lanes are active).  Every lane
-    // takes part in the exchange.
-    const int c1 = g * D + ln, c2 = c1 + half;
-    const int k1 = quant_code(r1, pool.k_scale[c1], pool.k_zp[c1], 15, ek);
-    const int k2 = quant_code(r2, pool.k_scale[c2], pool.k_zp[c2], 15, ek);
-    const int w1 = quant_code(v1, pool.v_scale[c1], pool.v_zp[c1], 15, ev);
-    const int w2 = quant_code(v2, pool.v_scale[c2], pool.v_zp[c2], 15, ev);
-    const int pk1 = __shfl_xor(k1, 4, 64), pk2 = __shfl_xor(k2, 4, 64);
-    const int pw1 = __shfl_xor(w1, 1, 64), pw2 = __shfl_xor(w2, 1, 64);
-    if (!act) continue;
-    const size_t hb = u4_head(blk, g, Hkv, D);
-    uint8_t* kp = (uint8_t*)pool.k + hb;
-    uint8_t* vp = (uint8_t*)pool.v + hb;
-    if (!(lane & 4)) {
-      kp[u4_kbyte(slot, lane, D)] = (uint8_t)(k1 | (pk1 << 4));
-      kp[u4_kbyte(slot, lane + half, D)] = (uint8_t)(k2 | (pk2 << 4));
-    }
-    if (!(lane & 1)) {
-      vp[u4_vbyte(slot, lane)] = (uint8_t)(w1 | (pw1 << 4));
-      vp[u4_vbyte(slot, lane + half)] = (uint8_t)(w2 | (pw2 << 4));
     }
   }
 }
@@ -468,8 +519,11 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ 
     for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
       const size_t idx = (size_t)row * Hkv * D + e;
       const int g = e / D;
-      store_kv(pool, blk, g, Hkv, D, slot, e % D, ld(k, idx), ld(v, idx), pool_exp(pool, blk, g, Hkv, 0),
-               pool_exp(pool, blk, g, Hkv, 1));
+      const int ek = pool_exp(pool, blk, g, Hkv, 0), ev = pool_exp(pool, blk, g, Hkv, 1);
+      if (pool.fmt == kKvU8)
+        store_kv<kKvU8>(pool, blk, g, Hkv, D, slot, e % D, ld(k, idx), ld(v, idx), ek, ev);
+      else
+        store_kv<kKvBf16>(pool, blk, g, Hkv, D, slot, e % D, ld(k, idx), ld(v, idx), ek, ev);
     }
     return;
   }
@@ -711,17 +765,29 @@ hipError_t rope_kv_write(const void* qkv, int rows, int Hq, int Hkv, int D, cons
                          const float* bias, int q_skip) {
   if (rows == 0) return hipSuccess;
   // few rows (decode): four heads per workgroup for parallelism; many rows
-  // (prefill): all heads of a row in one workgroup
+  // (prefill): all heads of four rows in one workgroup (the exponent pass:
+  // one row per workgroup)
   const int hpw = rows >= 1024 ? Hq + Hkv : 4;
-  const dim3 grid(rows, cdiv(Hq + Hkv, hpw));
   if (splits < 1) return hipErrorInvalidValue;
   auto launch = [&](int mode) {
-#define TDL_ROPE_KV(SB)                                                                           \
-  rope_kv_kernel<SB><<<grid, 256, 0, s>>>((const float*)qkv, Hq, Hkv, D, tab, q_norm, k_norm, eps, \
-                                          (float*)q_out, seq, pool, stage, splits, bias, hpw, mode, q_skip)
-    if (splits == 1) TDL_ROPE_KV(1);
-    else if (splits <= 4) TDL_ROPE_KV(4);
-    else TDL_ROPE_KV(8);
+    const int rpw = rows >= 1024 && mode == 0 ? 4 : 1;
+    const dim3 grid(cdiv(rows, rpw), cdiv(Hq + Hkv, hpw));
+#define TDL_ROPE_KV(SB, F, R)                                                                            \
+  rope_kv_kernel<SB, F, R><<<grid, 256, 0, s>>>((const float*)qkv, rows, Hq, Hkv, D, tab, q_norm, k_norm, \
+                                                eps, (float*)q_out, seq, pool, stage, splits, bias, hpw,   \
+                                                mode, q_skip)
+#define TDL_ROPE_KV_R(SB, F)              \
+  if (rpw == 4) TDL_ROPE_KV(SB, F, 4);    \
+  else TDL_ROPE_KV(SB, F, 1);
+#define TDL_ROPE_KV_SB(F)                   \
+  if (splits == 1) { TDL_ROPE_KV_R(1, F) }  \
+  else if (splits <= 4) { TDL_ROPE_KV_R(4, F) } \
+  else { TDL_ROPE_KV_R(8, F) }
+    if (pool.fmt == kKvU8) { TDL_ROPE_KV_SB(kKvU8) }
+    else if (pool.fmt == kKvU4) { TDL_ROPE_KV_SB(kKvU4) }
+    else { TDL_ROPE_KV_SB(kKvBf16) }
+#undef TDL_ROPE_KV_SB
+#undef TDL_ROPE_KV_R
 #undef TDL_ROPE_KV
     return hipGetLastError();
   };
