@@ -103,8 +103,12 @@ struct PrefillArgs {
 // denominator and accumulators are merged into group 0's through LDS at the
 // end.  Keys from the paged cache are converted by all threads and taken by
 // group 0 alone.
+// (Four waves of one key group: at most 256 registers each, so that two
+// workgroups share a CU and each SIMD has two waves to switch between --
+// Qwen3-8B's 2048-token chunk 67 -> 63 us, against a few spills; two key
+// groups of two heads need more registers than that.)
 template <int D, int NH, int F, int KS>
-__global__ __launch_bounds__(NH * KS * 64) void attn_prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn_prefill_kernel(PrefillArgs a) {
   using T = Tile<D>;
   static_assert(KS == 1 || KS == 2, "key groups");
   constexpr int NW = NH;  // waves per key group
