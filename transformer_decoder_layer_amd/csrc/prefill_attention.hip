@@ -677,8 +677,9 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
     // ---------------------------------------- key group 1 into key group 0
     if constexpr (KS == 2) {
       __syncthreads();  // every wave is done with the stage arrays
-      // wave w of group 1 leaves its state in the stage memory of group 0's
-      // wave w: D/2 accumulator floats, m and l per lane
+      // wave w of group 1 writes its state -- D/2 accumulator floats, m and
+      // l per lane -- to record w of the (now free) stage arrays, where wave
+      // w of group 0, the same head, reads it
       constexpr int PER = D / 32 * 16 + 2;
       static_assert(NH * PER * 64 * 4 <= 4 * KS * T::kBytes, "merge buffer");
       auto slot = [&](int i) -> float& {  // element i of this lane's record, spread over s0..s3
