@@ -37,10 +37,12 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // Threads (a multiple of 64, at most 1024) and chunks of 8 per thread for a
-// row of H columns (H % 64 == 0); false if H is too long.
-bool row_shape(int H, int* threads, int* ch) {
+// row of H columns (H % 64 == 0); false if H is too long.  Many rows: at
+// least two chunks per thread (more loads in flight per resident thread);
+// few rows (decode): one, for parallelism.
+bool row_shape(int H, int rows, int* threads, int* ch) {
   const int chunks = H / 8;
-  for (int c = 1; c <= 4; c *= 2) {
+  for (int c = rows >= 1024 ? 2 : 1; c <= 4; c *= 2) {
     const int t = (cdiv(chunks, c) + 63) / 64 * 64;
     if (t <= 1024) {
       *threads = t;
@@ -741,7 +743,7 @@ hipError_t rmsnorm_launch(const TIn* x, const float* g, void* y, int rows, int H
                           hipStream_t s) {
   if (rows == 0) return hipSuccess;
   int nt, ch;
-  if (H % 64 != 0 || !row_shape(H, &nt, &ch)) return hipErrorInvalidValue;
+  if (H % 64 != 0 || !row_shape(H, rows, &nt, &ch)) return hipErrorInvalidValue;
   switch (ch) {
     case 1: rmsnorm_kernel<TIn, 1><<<rows, nt, 0, s>>>(x, g, (f16*)y, H, eps); break;
     case 2: rmsnorm_kernel<TIn, 2><<<rows, nt, 0, s>>>(x, g, (f16*)y, H, eps); break;
