@@ -63,11 +63,12 @@ template <typename T> struct BFrag<kWIQ8, T> { uint2 codes; };
 
 // (at most 128 registers up to 64 rows of A: four waves per SIMD, i.e. two
 // 8-wave workgroups per CU, so that every workgroup of a launch is resident
-// at once; 128 rows of A need more and run two waves per SIMD)
+// at once; 128 rows of A need more and run two waves per SIMD; the 7-stage
+// ring of the int8-code variants holds twice the LDS and halves both)
 // RW row waves per k-slice (64 * RW / 4 ... 16 * RW weight rows per
 // workgroup), NS pipeline stages (= LDS ring buffers = register sets).
 template <typename T, int WF, int MT, int KW, int RW, int NS, int EPI, bool PACKED = false>
-__global__ __launch_bounds__(64 * RW * KW) __attribute__((amdgpu_waves_per_eu(MT == 8 ? 2 : 4)))
+__global__ __launch_bounds__(64 * RW * KW) __attribute__((amdgpu_waves_per_eu((MT == 8 ? 2 : 4) / (NS > 4 ? 2 : 1))))
 void gemm_stream_kernel(GemmArgs p) {
   constexpr bool Q80 = WF == kWQ80, IQ8 = WF == kWIQ8;
   constexpr int kRowWaves = RW, kStages = NS;
