@@ -111,12 +111,13 @@ def oracle_cache(inp: synth.LayerInputs, seqs=None) -> Optional[oracle.PagedCach
 
 
 def run_oracle(inp: synth.LayerInputs, seqs: Optional[List[int]] = None, want_stages=False,
-               rows_out=None):
+               rows_out=None, weights=None):
     """Oracle output rows of the chosen sequences (all by default), in row
     order, with their row indices.  ``rows_out`` (absolute row indices within
-    the chosen sequences) restricts the outputs to a sample of rows."""
+    the chosen sequences) restricts the outputs to a sample of rows;
+    ``weights`` replaces the expanded weights (oracle.expand_weights)."""
     shape, b = inp.workload.shape, inp.batch
-    W = oracle.expand_weights(shape, inp.weights)
+    W = oracle.expand_weights(shape, inp.weights) if weights is None else weights
     seqs = list(range(b.n_seqs)) if seqs is None else list(seqs)
     cache = oracle_cache(inp, seqs)
     rows = np.concatenate([np.arange(b.q_start[i], b.q_start[i] + b.q_len[i]) for i in seqs])

@@ -1,7 +1,9 @@
-"""GPU parity at the full sizes of the five workloads, in the launch
+"""GPU parity at the full sizes of the workloads, in the launch
 configuration the benchmark uses.  Where the oracle would take minutes the
 check runs on a sample of rows or sequences (the oracle still writes every
 row's K/V into its cache and calibrates u8 / u4 on every cached token)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -18,10 +20,10 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _check(inp, seqs=None, rows_out=None, what=""):
+def _check(inp, seqs=None, rows_out=None, what="", **setup):
     import torch
     print(f"[{what}] gpu", flush=True)
-    layer, kv, t = gpu_setup(inp)
+    layer, kv, t = gpu_setup(inp, **setup)
     gpu_call(inp, layer, kv, t)
     torch.cuda.synchronize()
     y = t["y"].float().cpu().numpy()
@@ -40,6 +42,79 @@ def test_qwen25_prefill_4096_sampled_rows():
     inp = synth.make_inputs(synth.WORKLOADS["qwen25_prefill_4096"])
     rows = [0, 1, 31, 32, 63, 64, 1000, 2047, 2048, 3001, 4064, 4094, 4095]
     _check(inp, [0], rows_out=rows, what="qwen2.5 prefill 4096")
+
+
+def test_qwen25_prefill_4096_fused_query_sampled_rows():
+    # the benchmark's layer: queries rotated inside the prefill attention kernel
+    inp = synth.make_inputs(synth.WORKLOADS["qwen25_prefill_4096"], seed=3)
+    rows = [0, 5, 32, 127, 128, 1023, 1024, 2500, 4000, 4095]
+    _check(inp, [0], rows_out=rows, what="qwen2.5 prefill 4096, fused query RoPE",
+           rope_fused=True, max_tokens=4096, max_position=8192)
+
+
+def test_qwen25_prefill_512_fused_query_full():
+    # the 512-token prefill the benchmark times on its 4096-row layer
+    inp = synth.make_inputs(synth.WORKLOADS["qwen25_prefill_512"], seed=4)
+    _check(inp, what="qwen2.5 prefill 512, fused query RoPE", rope_fused=True, max_tokens=4096,
+           max_position=8192)
+
+
+def test_qwen25_a8w8_prefill_4096_sampled_rows():
+    """The A8W8 layer at 4096 tokens, as the benchmark runs it.
+
+    Each projection on its own: the oracle's A8W8 projection of the stage
+    input the GPU holds (xn, o, hn in fp16, a in bf16, so both sides decide
+    the same int8 codes) against the GPU's stage output, at the bf16 bar.
+
+    End to end, an int8 code decided from a value a rounding step away on
+    either side moves by a whole step (max |row| / 127), and the steps are
+    coarse here: the SwiGLU product is heavy-tailed (max / rms ~ 12 over
+    18944 columns), so a 1e-2 difference in it moves the down projection's
+    output by ~2e-2, beyond the bf16 bar.  The bar for y is then the A8W8
+    method's own error: y may not be further from the oracle's A8W8 layer
+    than that layer is from the same layer in exact arithmetic (weights
+    dequantised, activations unquantised)."""
+    import torch
+    import oracle
+    from harness import compare_branch_bf16
+    from test_gpu_layer import gpu_stages
+    shape = synth.QWEN25_7B_A8W8
+    wl = dataclasses.replace(synth.WORKLOADS["qwen25_prefill_4096"], shape=shape)
+    inp = synth.make_inputs(wl, seed=5)
+    rows = np.array([0, 1, 63, 64, 777, 2048, 3333, 4064, 4095])
+    what = "qwen2.5 a8w8 prefill 4096"
+    print(f"[{what}] gpu", flush=True)
+    layer, kv, t = gpu_setup(inp, max_position=4096)
+    gpu_call(inp, layer, kv, t)
+    torch.cuda.synchronize()
+    y = t["y"].float().cpu().numpy()[rows]
+    x = t["x"].float().cpu().numpy()[rows].astype(np.float64)
+    g = gpu_stages(layer, t, rows, shape)
+    import transformer_decoder_layer_amd as tdl
+    hn = tdl.device_tensor(layer.workspace().hn, (4096, shape.hidden), torch.float16)[rows].float().cpu().numpy()
+    W = oracle.expand_weights(shape, inp.weights)
+    Hq, D = shape.n_q_heads, shape.head_dim
+    q_ref = oracle.rope_neox(oracle.linear(g["xn"], W["wq"], W["bq"]).reshape(len(rows), Hq, D),
+                             rows[:, None], shape.rope_theta).reshape(len(rows), -1)
+    h_ref = x + oracle.linear(g["o"], W["wo"])
+    a_ref = oracle.swiglu(oracle.linear(hn, W["wg"]), oracle.linear(hn, W["wu"]))
+    errs = {"q | xn": compare(g["q"], q_ref),
+            "h-x | o": compare(g["h"] - x, h_ref - x),
+            "hn | h": compare(hn, oracle.rms_norm(g["h"], W["ln2"], shape.rms_eps)),
+            "a | hn": compare(g["a"], a_ref),
+            "y-h | a": compare_branch_bf16(y, g["h"], g["h"] + oracle.linear(g["a"], W["wd"]), g["h"])}
+    for k, e in errs.items():
+        print(f"[{what}] {k}: {e}", flush=True)
+    print(f"[{what}] oracle", flush=True)
+    _, ref, _ = run_oracle(inp, [0], rows_out=rows)
+    W_exact = {k: (v.codes.astype(np.float64) * v.scale.astype(np.float64)[:, None]
+                   if isinstance(v, oracle.A8W8Weight) else v) for k, v in W.items()}
+    _, ref_exact, _ = run_oracle(inp, [0], rows_out=rows, weights=W_exact)
+    e, e_method = compare(y, ref), compare(ref, ref_exact)
+    print(f"[{what}] y: {e}; A8W8 oracle vs exact arithmetic: {e_method}", flush=True)
+    bad = [k for k, v in errs.items() if not v.ok]
+    assert not bad, f"{what}: projections out of tolerance: {bad}"
+    assert e.max_abs <= e_method.max_abs and e.mean_rel <= e_method.mean_rel, f"{what}: y {e} vs {e_method}"
 
 
 def test_qwen25_decode_b64_full():
