@@ -50,6 +50,38 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Lanes l and l ^ 32 combined on the VALU (no LDS permute, whose wait would
+// also wait for every LDS read issued before it): given the same register
+// twice, v_permlane32_swap leaves each lane the pair {x[l], x[l ^ 32]}, so
+// the max or the sum of the pair is the same on both halves.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// max and sum of a lane's 16 values as trees: the max in three-input steps
+// (v_max3, 3 dependent instructions, not 8), the sum in 4 dependent adds
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+__device__ __forceinline__ float max16(const float (&v)[16]) {
+  float m[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) m[i] = max3f(v[3 * i], v[3 * i + 1], v[3 * i + 2]);
+  return fmaxf(max3f(m[0], m[1], m[2]), max3f(m[3], m[4], v[15]));
+}
+__device__ __forceinline__ float sum16(const float (&v)[16]) {
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m[i] = v[2 * i] + v[2 * i + 1];
+#pragma unroll
+  for (int w = 4; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) m[i] += m[i + w];
+  return m[0];
+}
+
 // ------------------------------------------------------------ tile layout
 // One LDS tile: K [PK keys][D] fp16 at prefill_k_index, then V at kK +
 // prefill_v_index: the staging copy's layout, so that a tile is a straight
@@ -216,7 +248,7 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
         for (int s = 0; s < D / 16; ++s)
 #pragma unroll
           for (int e = 0; e < 8; ++e) ss += xv[s][e] * xv[s][e];
-        ss += __shfl_xor(ss, 32, 64);
+        ss = halves_sum(ss);
         const float inv = rsqrtf(ss / (float)D + a.qs.eps);
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
@@ -287,22 +319,21 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
     // moved (wave-uniform) and P (fp16) in the B-operand layout of
     // O^T += V^T P^T.
     auto softmax = [&](const f32x16& st, f16x8 (&pb)[2], float& alpha) {
-      float mt = st[0];
+      float sv[16];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, st[r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      for (int r = 0; r < 16; ++r) sv[r] = st[r];
+      const float mt = halves_max(max16(sv));
       const bool mv = __builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0;
       const float m_new = mv ? fmaxf(m_run, mt) : m_run;
       alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 if unmoved, 0 on the first tile
       m_run = m_new;
-      float psum = 0.f;
+      float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(st[r] - m_new);  // 0 where masked
-        psum += pv;
-        pb[r >> 3][r & 7] = (f16)pv;
+        pv[r] = __builtin_amdgcn_exp2f(sv[r] - m_new);  // 0 where masked
+        pb[r >> 3][r & 7] = (f16)pv[r];
       }
-      l_run = l_run * alpha + psum;
+      l_run = l_run * alpha + sum16(pv);
       return mv;
     };
     auto rescale = [&](bool moved, float alpha) {
@@ -612,10 +643,10 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
             mask(scur, lim_at(t));
             __builtin_amdgcn_sched_barrier(0);
           }
-          float mt = scur[0];
+          float sv[16];
 #pragma unroll
-          for (int r = 1; r < 16; ++r) mt = fmaxf(mt, scur[r]);
-          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+          for (int r = 0; r < 16; ++r) sv[r] = scur[r];
+          const float mt = halves_max(max16(sv));
           const bool mv = __builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0;
           const float m_new = mv ? fmaxf(m_run, mt) : m_run;
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -644,13 +675,9 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
           }
           snxt = e;
           f16x8 pb[2];
-          float psum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            psum += pv16[r];
-            pb[r >> 3][r & 7] = (f16)pv16[r];
-          }
-          l_run = l_run * alpha + psum;
+          for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (f16)pv16[r];
+          l_run = l_run * alpha + sum16(pv16);
           rescale(mv, alpha);
 #pragma unroll
           for (int kc = 0; kc < NB; ++kc)
@@ -714,7 +741,7 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
     }
 
     // ------------------------------------------------------------ output
-    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    const float l = halves_sum(l_run);
     if (own && kg == 0 && my_q < q_len) {
       const float inv = 1.f / l;
       f16* op = a.o + (size_t)(row0 + ql) * a.Hq * D + (size_t)h * D;
