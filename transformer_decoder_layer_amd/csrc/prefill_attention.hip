@@ -626,7 +626,8 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
       // reference update; then S(t+1) = Q K(t+1)^T one MFMA at a time, each
       // followed by its share of P(t) = 2^(S(t) - m) (the VALU and TRANS work
       // runs while the MFMA does; past the last tile the scores of a repeated
-      // tile are computed and never used); read V(t)'s fragments half way;
+      // tile are computed and never used), at a raised wave priority, which
+      // lets the SIMD's other wave fill the gaps; read V(t)'s fragments half way;
       // O += P(t) V(t); wait for tile t+2.  Tiles that need a mask take it
       // first.  The fences keep this order: every LDS read is issued well
       // before the MFMA that takes it.
@@ -655,6 +656,7 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
           f32x16 e{};
           f16x8 vf[NB][D / 32];
           float pv16[16];
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
             e = mfma32(kf[s], qf[s], e);
@@ -673,6 +675,7 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
             }
             __builtin_amdgcn_sched_barrier(0);
           }
+          __builtin_amdgcn_s_setprio(0);
           snxt = e;
           f16x8 pb[2];
 #pragma unroll
