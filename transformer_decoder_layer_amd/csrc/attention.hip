@@ -286,8 +286,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(DecArgs a) {
     }
     float qscale = 1.f;
     if constexpr (Q) {
-      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      amax = max_xor32(max_xor16(amax));
       int ex = 0;
       frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1); ex = 0 for amax 0
       const int sh = min(100, max(-100, 8 - ex));
@@ -313,8 +312,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(DecArgs a) {
       qlo[s] = lo;
     }
     if constexpr (Q) {
-      corr += __shfl_xor(corr, 16, 64);
-      corr += __shfl_xor(corr, 32, 64);
+      corr = sum_xor32(sum_xor16(corr));
     }
   }
 
@@ -390,8 +388,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(DecArgs a) {
         mb = fmaxf(mb, sv[r]);
       }
     }
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    mb = max_xor32(max_xor16(mb));
     // the reference point of the exponentials moves (and the accumulators
     // are rescaled) only when a block's maximum exceeds it by more than
     // kLazy: P <= 2^kLazy keeps its hi + lo pair exact enough, softmax
@@ -537,10 +534,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(DecArgs a) {
   }
 
   // ---- merge the waves: acc[t][r] = O^T[dec_vchan(t, 4grp + r)][head col]
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  lv_run += __shfl_xor(lv_run, 16, 64);
-  lv_run += __shfl_xor(lv_run, 32, 64);
+  l_run = sum_xor32(sum_xor16(l_run));
+  lv_run = sum_xor32(sum_xor16(lv_run));
   if (lane < 16) {
     sm_m[wave][lane] = m_run;
     sm_l[wave][lane] = l_run;

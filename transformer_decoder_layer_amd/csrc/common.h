@@ -55,6 +55,29 @@ __device__ __forceinline__ bf16 f32_to_bf16(float v) { return (bf16)v; }
 __device__ __forceinline__ uint16_t bf16_bits(bf16 v) { return __builtin_bit_cast(uint16_t, v); }
 __device__ __forceinline__ bf16 bits_bf16(uint16_t v) { return __builtin_bit_cast(bf16, v); }
 
+// Lanes l and l ^ 32 (l ^ 16) combined on the VALU, without the LDS
+// permute (whose wait also waits for every LDS access issued before it):
+// given the same register twice, v_permlane32_swap (v_permlane16_swap, over
+// rows of 16 lanes) leaves each lane the pair {x[l], x[l ^ 32]} ({x[l],
+// x[l ^ 16]}), so the max or the sum of the pair is the same on both lanes.
+// The whole wave must be active.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);

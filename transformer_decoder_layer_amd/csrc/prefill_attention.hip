@@ -50,18 +50,6 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Lanes l and l ^ 32 combined on the VALU (no LDS permute, whose wait would
-// also wait for every LDS read issued before it): given the same register
-// twice, v_permlane32_swap leaves each lane the pair {x[l], x[l ^ 32]}, so
-// the max or the sum of the pair is the same on both halves.
-__device__ __forceinline__ float halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 // max and sum of a lane's 16 values as trees: the max in three-input steps
 // (v_max3, 3 dependent instructions, not 8), the sum in 4 dependent adds
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -248,7 +236,7 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
         for (int s = 0; s < D / 16; ++s)
 #pragma unroll
           for (int e = 0; e < 8; ++e) ss += xv[s][e] * xv[s][e];
-        ss = halves_sum(ss);
+        ss = sum_xor32(ss);
         const float inv = rsqrtf(ss / (float)D + a.qs.eps);
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
@@ -322,7 +310,7 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
       float sv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = st[r];
-      const float mt = halves_max(max16(sv));
+      const float mt = max_xor32(max16(sv));
       const bool mv = __builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0;
       const float m_new = mv ? fmaxf(m_run, mt) : m_run;
       alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 if unmoved, 0 on the first tile
@@ -647,7 +635,7 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
           float sv[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) sv[r] = scur[r];
-          const float mt = halves_max(max16(sv));
+          const float mt = max_xor32(max16(sv));
           const bool mv = __builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0;
           const float m_new = mv ? fmaxf(m_run, mt) : m_run;
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -744,7 +732,7 @@ __global__ __launch_bounds__(NH * KS * 64, KS == 1 && NH == 4 ? 2 : 1) void attn
     }
 
     // ------------------------------------------------------------ output
-    const float l = halves_sum(l_run);
+    const float l = sum_xor32(l_run);
     if (own && kg == 0 && my_q < q_len) {
       const float inv = 1.f / l;
       f16* op = a.o + (size_t)(row0 + ql) * a.Hq * D + (size_t)h * D;
