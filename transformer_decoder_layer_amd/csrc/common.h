@@ -78,10 +78,22 @@ __device__ __forceinline__ float sum_xor16(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// DPP move within rows of 16 lanes (quad_perm, row_mirror, row_half_mirror)
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the wave, the same value on every lane, all on the VALU: lanes
+// l ^ 1 and l ^ 2 by quad permutations; then the half-row and row mirrors
+// (lane i with 7 - i, then with 15 - i), which pair lanes whose groups
+// already agree; then lanes l ^ 16 and l ^ 32.  The whole wave must be
+// active.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_move<0x141>(v);  // row_half_mirror
+  v += dpp_move<0x140>(v);  // row_mirror
+  return sum_xor32(sum_xor16(v));
 }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
