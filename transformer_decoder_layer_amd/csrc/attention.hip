@@ -215,8 +215,12 @@ __device__ __forceinline__ f16x4 u4x4_to_f16_biased(uint32_t w, int n) {
   return __builtin_bit_cast(f16x4, r);
 }
 
+// Four-wave workgroups (several per CU) are held to at least three waves
+// per SIMD: left to itself the compiler gives them up to 220 registers,
+// which caps every format at two waves per SIMD however many workgroups
+// there are.
 template <int D, int F, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 2) void attn_decode_kernel(DecArgs a) {
   constexpr bool Q = F != kKvBf16;  // codes with per-channel scale / zero point
   constexpr bool U4 = F == kKvU4;
   constexpr float kBias = U4 ? kU4Bias : kU8Bias;
