@@ -206,7 +206,17 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* __restrict__ 
                                                       const float* __restrict__ bias, int hpw, int mode,
                                                       int q_skip) {
   static_assert(RPW >= 1, "rows per workgroup");
-  const int row0 = blockIdx.x * RPW;
+  // Several rows per workgroup (long prompts): consecutive row groups, which
+  // write the same V^T lines of their cache blocks (one 2-byte slot per
+  // token and channel), go to one XCD, whose L2 then merges those partial
+  // line writes; workgroups are dealt to the 8 XCDs round-robin, so XCD x
+  // takes the x-th contiguous range of row groups (a bijection on the grid)
+  int bid = blockIdx.x;
+  if constexpr (RPW > 1) {
+    const int G = gridDim.x, per = G / 8, rem = G % 8, x = bid % 8, slot = bid / 8;
+    bid = x * per + min(x, rem) + slot;
+  }
+  const int row0 = bid * RPW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = D >> 1;
   const int ldq = (Hq + 2 * Hkv) * D;
