@@ -5,9 +5,9 @@ while Q is loaded).  Against the oracle, stage by stage (the attention
 output checks the fused query path): bf16 prefill with a QKV bias (no cache,
 paged, a chunk after cached tokens), a Qwen3-shaped prefill and mixed step
 (Q-norm; the decode rows keep the RoPE kernel's q), a u8 cache, Q8_0 and
-A8W8 layers, and mid-sized layers whose QKV projection is split along K
+A8W8 layers, mid-sized layers whose QKV projection is split along K
 (their prefill queries take the RoPE kernel's path, which sums the slices in
-order and adds the bias)."""
+order and adds the bias), and u4 and per-block-scaled u8 / u4 caches."""
 import dataclasses
 
 import pytest
@@ -74,4 +74,31 @@ def test_fused_split_qkv(shape, T):
                             random_gains=True)
     layer, kv, t, cache, rows = check_layer(inp, what=f"fused {shape.name} split QKV, chunk {T} at 20",
                                             rope_fused=True)
+    check_cache_rows(inp, kv, cache, [0])
+
+
+# the fused query path over coded caches: u4, and per-block x per-channel
+# u8 / u4 (the chunk's own keys come from the staging copy, which holds the
+# block-scaled values; the cached ones are dequantised with their blocks'
+# factors).  u4 checks y and the cache (its quantisation noise in o is above
+# the stage bar), as the other u4 tests do.
+@pytest.mark.parametrize("kvd,bs", [("u4", False), ("u8", True), ("u4", True)])
+def test_fused_mixed_step_over_coded_caches(kvd, bs):
+    from test_gpu_kv_block_scales import _check_exponents, _narrow_calibration
+    wl = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=TINY_Q3, kv_dtype=kvd)
+    inp = synth.make_inputs(wl, seed=170 + 2 * bs + (kvd == "u4"), prefill_len=90, decode_batch=4,
+                            decode_ctx=[3, 16, 40, 129], random_gains=True)
+    if bs:
+        inp = _narrow_calibration(inp, 175)
+    what = f"fused mixed {kvd}{' block scales' if bs else ''}"
+    layer, kv, t, cache, rows = check_layer(inp, what=what, rope_fused=True, stages=kvd == "u8")
+    check_cache_rows(inp, kv, cache, range(5))
+    if bs:
+        _check_exponents(inp, kv, cache, range(5))
+
+
+def test_fused_u4_chunk_after_cached_tokens():
+    wl = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=TINY_Q3, kv_dtype="u4")
+    inp = synth.make_inputs(wl, seed=178, prefill_len=100, prefill_start=37, spare_blocks=1, random_gains=True)
+    layer, kv, t, cache, rows = check_layer(inp, what="fused u4 chunk 100 at 37", rope_fused=True, stages=False)
     check_cache_rows(inp, kv, cache, [0])
