@@ -63,7 +63,7 @@ template <typename T> struct BFrag<kWIQ8, T> { uint2 codes; };
 
 // (at most 128 registers up to 64 rows of A: four waves per SIMD, i.e. two
 // 8-wave workgroups per CU, so that every workgroup of a launch is resident
-// at once; 128 rows of A need more and run two waves per SIMD; the 7-stage
+// at once; 128 rows of A need more and run two waves per SIMD; the 8-stage
 // ring of the int8-code variants holds twice the LDS and halves both)
 // RW row waves per k-slice (64 * RW / 4 ... 16 * RW weight rows per
 // workgroup), NS pipeline stages (= LDS ring buffers = register sets).
@@ -82,6 +82,11 @@ void gemm_stream_kernel(GemmArgs p) {
   // two block scales for Q8_0
   constexpr bool IQ8P = IQ8 && PACKED, Q80P = Q80 && PACKED;
   constexpr int LOADS = A_PER_WAVE + FN * (IQ8P ? 1 : Q80P ? 3 : 2 * (Q80 ? 2 : 1));  // vector-memory ops per stage
+  // stages per barrier: the 1 KB stages of the 8-deep int8-code ring are
+  // waited for and synchronised two at a time (the same bytes per barrier as
+  // a 2 KB stage), keeping 6 stages in flight
+  constexpr int SPB = IQ8 && NS == 8 ? 2 : 1;
+  static_assert(NS % SPB == 0 && NS - 2 * SPB >= 1 && SPB <= 2, "stages per barrier");
   // separate arrays (not one indexed array): the compiler can then tell that
   // reading one buffer does not depend on the loads still filling another
   // (arrays past NS are never referenced and take no LDS)
@@ -114,7 +119,11 @@ void gemm_stream_kernel(GemmArgs p) {
   const int my0 = ks0 + wk * per_slice;               // this slice's stages: [my0, my1)
   const int my1 = min(my0 + per_slice, ks1);
   const int last = max(my1 - 1, 0);                   // loads past the end repeat the last stage
-  const int n_iter = cdiv(per_slice, kStages) * kStages;
+  // the single-stage ring runs whole turns (an exit test per step measured
+  // slower for it); the paired ring's last turn stops after the slice's last
+  // stage (the same count for every wave of the workgroup), and what it
+  // issued past that point is drained after the loop
+  const int n_iter = SPB > 1 ? per_slice : cdiv(per_slice, kStages) * kStages;
 
   const T* __restrict__ A = (const T*)p.A;
   const int r16 = lane & 15, g8 = (lane >> 4) * 8;
@@ -253,20 +262,42 @@ void gemm_stream_kernel(GemmArgs p) {
   // every wave is done with the buffer refilled next), refill, compute.
   // Scheduling barriers keep the compiler from moving register reads of a
   // stage's loads, or the loads themselves, across these points: the wait
-  // counts assume program order.
+  // counts assume program order.  The paired ring's step does the same for
+  // two stages (kStages - 4 later ones in flight).
+  if constexpr (SPB == 1) {
 #pragma unroll
-  for (int j = 0; j < kStages - 1; ++j) issue(j, rings[j], breg[j]);
-  for (int it = 0; it < n_iter; it += kStages) {
+    for (int j = 0; j < kStages - 1; ++j) issue(j, rings[j], breg[j]);
+    for (int it = 0; it < n_iter; it += kStages) {
 #pragma unroll
-    for (int j = 0; j < kStages; ++j) {
-      const int jn = (j + kStages - 1) % kStages;
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * LOADS));
-      asm volatile("s_barrier" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      issue(it + j + kStages - 1, rings[jn], breg[jn]);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(it + j, rings[j], breg[j]);
+      for (int j = 0; j < kStages; ++j) {
+        const int jn = (j + kStages - 1) % kStages;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * LOADS));
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        issue(it + j + kStages - 1, rings[jn], breg[jn]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(it + j, rings[j], breg[j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kStages - 2; ++j) issue(j, rings[j], breg[j]);
+    for (int it = 0; it < n_iter; it += kStages) {
+#pragma unroll
+      for (int j = 0; j < kStages; j += 2) {
+        if (it + j >= per_slice) break;
+        const int jn = (j + kStages - 2) % kStages;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 4) * LOADS));
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        issue(it + j + kStages - 2, rings[jn], breg[jn]);
+        issue(it + j + kStages - 1, rings[jn + 1], breg[jn + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(it + j, rings[j], breg[j]);
+        compute(it + j + 1, rings[j + 1], breg[j + 1]);
+      }
     }
   }
   // the last refills are still landing in the ring: drain them before the
@@ -411,14 +442,16 @@ int stream_cfg(int MT, int RW, int NS, int KW) { return 10000 + 1000 * MT + 100 
 
 // Row waves per workgroup that are built (RW), and the pipeline depth: 4
 // stages of 2 KB per wave (bf16/fp16, Q8_0); per-row int8 stages carry 1 KB
-// (64 k of 16 rows), so 7 stages keep as many bytes in flight.
+// (64 k of 16 rows): an 8-buffer ring, waited for and synchronised two
+// stages at a time, keeps 6 of them in flight, twice the stages of bf16's
+// 3 and as many bytes, at the same bytes per barrier.
 constexpr int kStreamRW[3] = {4, 8, 10};
 constexpr int kStreamNS = 4;
-constexpr int kStreamNSIQ8 = 7;
+constexpr int kStreamNSIQ8 = 8;
 
 // Chooses (RW, row ranges, K splits) by a model of the decode-sized stream,
 // fitted to measurements on the Qwen2.5-7B decode shapes: a CU streams its
-// weight bytes at ~1.5 us latency with (NS-1) stages of 2 KB in flight per
+// weight bytes at ~1.5 us latency with its stages in flight (2 KB each) per
 // live row wave, up to ~22 GB/s, and the GPU at ~5.5 TB/s; the busiest CU
 // sets the time.  K splits add streams (and fp32 partials that are written
 // and read once more).
@@ -444,6 +477,7 @@ bool skinny_plan(int M, int N, int K, int wf, int epi, GemmPlan* pl) {
   const double wave_lat = big ? 2.3e-6 : 1.5e-6;
   const int NS = wf == kWIQ8 ? kStreamNSIQ8 : kStreamNS;
   const double stage_bytes = wf == kWIQ8 ? 1024.0 : 2048.0;  // per live row wave
+  const int in_flight = wf == kWIQ8 ? NS - 2 : NS - 1;  // stages in flight during a compute
   double best = 1e300;
   for (int RW : kStreamRW) {
     if (RW < 8 && units > 16) continue;  // (tiny N: too few row groups for 8 waves)
@@ -451,7 +485,7 @@ bool skinny_plan(int M, int N, int K, int wf, int epi, GemmPlan* pl) {
     const int rmin = cdiv(units, per);
     for (int s = 1; s <= 16; ++s) {
       const int kps = cdiv(KS, s), sp = cdiv(KS, kps);
-      if (sp != s || (sp > 1 && kps < 2 * NS)) continue;
+      if (sp != s || (sp > 1 && kps < 2 * (in_flight + 1))) continue;
       const int cands[3] = {rmin, kCUs / sp, 2 * kCUs / sp};
       for (int R : cands) {
         if (R < rmin || R > units || R < 1) continue;
@@ -459,7 +493,7 @@ bool skinny_plan(int M, int N, int K, int wf, int epi, GemmPlan* pl) {
         const int wg_per_cu = cdiv(W, kCUs);
         const int groups = cdiv(units, R) * PG;          // live row waves of the largest range
         const double wg_bytes = (double)groups * 16 * kps * 64 * wb;
-        double rate = std::min(22e9, wg_per_cu * groups * (NS - 1) * stage_bytes / wave_lat);
+        double rate = std::min(22e9, wg_per_cu * groups * in_flight * stage_bytes / wave_lat);
         rate *= (double)groups / RW;
         double t = std::max(wg_per_cu * wg_bytes / rate, total / 5.5e12);
         if (sp > 1) t += 2.0 * sp * (double)M * N * 4.0 / 5.0e12;
@@ -494,9 +528,9 @@ hipError_t gemm_skinny_launch(const GemmPlan& pl, const GemmArgs& a, int wf, int
 #define TDL_STREAM_CFG_IQ8(MT, RW, NS, KW)                                                  \
   if (pl.cfg == stream_cfg(MT, RW, NS, KW) && wf == kWIQ8)                                  \
     return launch_stream<kWIQ8, MT, KW, RW, NS>(pl.grid, epi, a, s);
-  TDL_STREAM_CFG_IQ8(2, 4, 7, 1) TDL_STREAM_CFG_IQ8(2, 8, 7, 1) TDL_STREAM_CFG_IQ8(2, 10, 7, 1)
-  TDL_STREAM_CFG_IQ8(4, 4, 7, 1) TDL_STREAM_CFG_IQ8(4, 8, 7, 1) TDL_STREAM_CFG_IQ8(4, 10, 7, 1)
-  TDL_STREAM_CFG_IQ8(8, 4, 7, 1) TDL_STREAM_CFG_IQ8(8, 8, 7, 1) TDL_STREAM_CFG_IQ8(8, 10, 7, 1)
+  TDL_STREAM_CFG_IQ8(2, 4, 8, 1) TDL_STREAM_CFG_IQ8(2, 8, 8, 1) TDL_STREAM_CFG_IQ8(2, 10, 8, 1)
+  TDL_STREAM_CFG_IQ8(4, 4, 8, 1) TDL_STREAM_CFG_IQ8(4, 8, 8, 1) TDL_STREAM_CFG_IQ8(4, 10, 8, 1)
+  TDL_STREAM_CFG_IQ8(8, 4, 8, 1) TDL_STREAM_CFG_IQ8(8, 8, 8, 1) TDL_STREAM_CFG_IQ8(8, 10, 8, 1)
 #undef TDL_STREAM_CFG_IQ8
   return hipErrorInvalidValue;
 }
