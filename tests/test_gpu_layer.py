@@ -185,14 +185,15 @@ def test_tiny_decode_u4(shape):
 
 @pytest.mark.parametrize("shape", [TINY_IQ8, TINY_IQ8_736], ids=lambda s: s.name)
 def test_tiny_iq8_decode_prefill_mixed(shape):
-    # decode rows stream the int8 codes; 45 rows too; 150 rows (> 128) take
-    # the expanded fp16/bf16 copies, in the mixed step as well
+    # decode rows stream the int8 codes; 45 and 100 rows too (100: the
+    # 128-row tiles, whose 8-stage ring fills 128 KB of LDS); 150 rows (> 128)
+    # take the expanded fp16/bf16 copies, in the mixed step as well
     wl = dataclasses.replace(synth.WORKLOADS["qwen25_iq8_decode_b64"], shape=shape)
     ctx = [0, 1, 16, 47, 300, 1023]
     inp = synth.make_inputs(wl, seed=61, decode_batch=len(ctx), decode_ctx=ctx)
     layer, kv, t, cache, rows = check_layer(inp, what=f"decode {shape.name}")
     check_cache_rows(inp, kv, cache, range(len(ctx)))
-    for T in (45, 150):
+    for T in (45, 100, 150):
         wp = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=shape, kv_dtype="bf16")
         inp = synth.make_inputs(wp, seed=62 + T, prefill_len=T, prefill_start=20, spare_blocks=1)
         check_layer(inp, what=f"prefill {T} {shape.name}")
