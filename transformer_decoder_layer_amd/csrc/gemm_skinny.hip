@@ -44,6 +44,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace tdl {
 
@@ -51,6 +52,25 @@ namespace {
 
 constexpr int kStageK = 64;  // k per stage (two 32-k MFMA steps)
 constexpr int kMaxStages = 8;
+
+// Eight int8 codes (two words) as fp16 values c - off, for an integer off
+// with |c - off| < 1024: the byte c ^ 0x80 = c + 128 under the exponent byte
+// 0x64 is the fp16 number 1024 + c + 128 (one byte permute per two codes),
+// and one packed subtract of 1152 + off leaves c - off exactly.
+__device__ __forceinline__ f16x8 codes_to_f16(uint2 c, _Float16 off1152) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const uint32_t w[2] = {c.x ^ 0x80808080u, c.y ^ 0x80808080u};
+  f16x8 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // bytes (u0, 0x64, u1, 0x64) from (w, 0x64646464)
+    const uint32_t bits = __builtin_amdgcn_perm(0x64646464u, w[q >> 1], (q & 1) ? 0x04030402u : 0x04010400u);
+    const h2 v = __builtin_bit_cast(h2, bits) - h2{off1152, off1152};
+    o[2 * q] = v.x;
+    o[2 * q + 1] = v.y;
+  }
+  return o;
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding and leaves the other counters alone.
@@ -152,10 +172,12 @@ void gemm_stream_kernel(GemmArgs p) {
   BFrag<WF, T> breg[kStages][FN][2];
   // per-row int8: this lane's row scale and zero point
   float rsc[FN], rzp[FN];
+  _Float16 zp1152[FN];  // 1152 + zero point, exact in fp16 (|zp| <= 128)
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
     rsc[f] = IQ8 ? p.B_rscale[b_row[f]] : 1.f;
     rzp[f] = IQ8 ? p.B_rzp[b_row[f]] : 0.f;
+    zp1152[f] = (_Float16)(1152.f + rzp[f]);
   }
   f32x4 acc[MT][FN];
 #pragma unroll
@@ -218,7 +240,10 @@ void gemm_stream_kernel(GemmArgs p) {
       float sc[FN];
 #pragma unroll
       for (int f = 0; f < FN; ++f) {
-        if constexpr (Q80) {
+        if constexpr (Q80 && std::is_same<T, f16>::value) {
+          bv[f] = codes_to_f16(b[f][u].codes, (_Float16)1152.f);
+          sc[f] = valid ? __half2float(__ushort_as_half((unsigned short)b[f][u].scale)) : 0.f;
+        } else if constexpr (Q80) {
           T8 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -227,6 +252,8 @@ void gemm_stream_kernel(GemmArgs p) {
           }
           bv[f] = v;
           sc[f] = valid ? __half2float(__ushort_as_half((unsigned short)b[f][u].scale)) : 0.f;
+        } else if constexpr (IQ8 && std::is_same<T, f16>::value) {
+          bv[f] = valid ? codes_to_f16(b[f][u].codes, zp1152[f]) : T8{};
         } else if constexpr (IQ8) {
           T8 v;
 #pragma unroll
