@@ -202,6 +202,19 @@ def test_tiny_iq8_decode_prefill_mixed(shape):
     check_layer(inp, what=f"mixed {shape.name}")
 
 
+@pytest.mark.parametrize("shape", [TINY_IQ8, TINY_Q80], ids=lambda s: s.name)
+def test_tiny_code_weights_row_count_edges(shape):
+    # the stream kernels' smallest and largest row tiles: one decode row (the
+    # 32-row tile), exactly 128 prompt rows (the last that stream the codes)
+    wl = dataclasses.replace(synth.WORKLOADS["qwen25_iq8_decode_b64"], shape=shape)
+    inp = synth.make_inputs(wl, seed=71, decode_batch=1, decode_ctx=[37], random_gains=True)
+    layer, kv, t, cache, rows = check_layer(inp, what=f"decode 1 row {shape.name}")
+    check_cache_rows(inp, kv, cache, range(1))
+    wp = dataclasses.replace(synth.WORKLOADS["tiny_prefill_32"], shape=shape, kv_dtype="bf16")
+    inp = synth.make_inputs(wp, seed=72, prefill_len=128, prefill_start=5, spare_blocks=1, random_gains=True)
+    check_layer(inp, what=f"prefill 128 {shape.name}")
+
+
 def test_tiny_mixed_q80():
     wl = dataclasses.replace(synth.WORKLOADS["qwen3_q80_mixed"], shape=TINY_Q80)
     inp = synth.make_inputs(wl, seed=6, prefill_len=77, decode_batch=5, decode_ctx=[3, 16, 40, 129, 500],
