@@ -290,7 +290,9 @@ void gemm_stream_kernel(GemmArgs p) {
   // Scheduling barriers keep the compiler from moving register reads of a
   // stage's loads, or the loads themselves, across these points: the wait
   // counts assume program order.  The paired ring's step does the same for
-  // two stages (kStages - 4 later ones in flight).
+  // two stages (kStages - 4 later ones in flight), the second refill issued
+  // between the two computes (the loads keep their order, so the counts
+  // hold; both buffers were freed before the barrier).
   if constexpr (SPB == 1) {
 #pragma unroll
     for (int j = 0; j < kStages - 1; ++j) issue(j, rings[j], breg[j]);
@@ -320,9 +322,11 @@ void gemm_stream_kernel(GemmArgs p) {
         asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         issue(it + j + kStages - 2, rings[jn], breg[jn]);
-        issue(it + j + kStages - 1, rings[jn + 1], breg[jn + 1]);
         __builtin_amdgcn_sched_barrier(0);
         compute(it + j, rings[j], breg[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(it + j + kStages - 1, rings[jn + 1], breg[jn + 1]);
+        __builtin_amdgcn_sched_barrier(0);
         compute(it + j + 1, rings[j + 1], breg[j + 1]);
       }
     }
